@@ -1,0 +1,534 @@
+/*
+ * tmv_oracle.c -- plain, slow CPU oracle for the teacher's tree-verification step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or call this
+ * file: only the test suite, the smoke check and the benchmark's CPU-baseline leg do.
+ * It shares no source, header, table or helper with the HIP library.
+ *
+ * Arithmetic: fp64 for every floating-point quantity (bf16 inputs are widened exactly),
+ * exact integers (64/128-bit) everywhere else.  Loops follow the definitions directly;
+ * nothing is blocked, fused or reordered.
+ *
+ * Sources (pages of the reference set):
+ *   [EP-pt]  "EAGLE-Pangu: Accelerator-Safe Tree Speculative Decoding on Ascend NPUs",
+ *            Portuguese technical summary, section 2 (methodology and architecture).
+ *   [EP-zh]  the independently written Chinese technical summary of the same paper,
+ *            section 2.1 (branchable KV cache, commit modes), 2.2 (accelerator-safe tree
+ *            tensors: virtual root row 0, ancestor table, invariant checks), 2.3 (fused
+ *            tree-masked teacher pass, a node sees its ancestors and itself).
+ *   [SDH]    "Speculative Decoding Hierarquico: Medusa, EAGLE-2 e Multi-Token Prediction",
+ *            sections on modified rejection sampling (acceptance min(1,p/q), residual
+ *            max(0,p-q) normalised, the identity min(q,p)+max(0,p-q)=p), on Medusa trees
+ *            (tree attention mask; the longest valid path is kept) and its FAQ (a
+ *            correction token is drawn when every guess is refused).
+ *
+ * Readings where the pages are silent (each is also listed in the design notes):
+ *   - ancestor table orientation: anc[i][k] = parent^k(i), saturating at the root 0,
+ *     width D_max+1; depth(i) = number of hops from i to 0.
+ *   - "validity closure": a valid node's parent is valid (or is the root).
+ *   - error precedence: the smallest nonzero code over the nodes of a sequence wins and
+ *     the whole sequence becomes inert (all-zero rows).
+ *   - argmax ties go to the smallest token; among equally deep matched nodes the
+ *     smallest node id wins; the bonus token after a full accept is the teacher's
+ *     choice at the last accepted node.
+ *   - sampling on a tree: children of a node are tried in ascending id, each by the
+ *     chain rule against the current residual; exact integer fixed point (below).
+ *   - RNG: Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11), key {seed, (step<<32)|b},
+ *     block n uses counter {n+1,0,0,0}; draw n is 64-bit word n%4 of block n/4.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <math.h>
+
+enum {
+    REF_OK = 0, REF_ERR_ARG = 1, REF_ERR_RANGE = 2, REF_ERR_CYCLE = 3, REF_ERR_DEPTH = 4,
+    REF_ERR_CLOSURE = 5, REF_ERR_INPUT = 6
+};
+enum { REF_PARENTS_VROOT = 0, REF_PARENTS_NEG1 = 1 };
+enum { REF_F32 = 0, REF_BF16 = 1 };
+
+typedef unsigned __int128 u128;
+
+/* smallest nonzero code wins */
+static int merge_code(int a, int b)
+{
+    if (a == REF_OK) return b;
+    if (b == REF_OK) return a;
+    return a < b ? a : b;
+}
+
+/* exact widening of one element of a f32 or bf16 array */
+static double load_elem(const void *base, int dtype, int64_t idx)
+{
+    if (dtype == REF_F32) return (double)((const float *)base)[idx];
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* ------------------------------------------------------------------------------------
+ * Tree tensors [EP-zh §2.2, EP-pt §2]: parents remapped onto the virtual root row 0,
+ * ancestor table whose entries all lie in [0, M_b], range / acyclicity / depth /
+ * validity-closure checks, per-sequence status.
+ *
+ *   parents  VROOT: [B][M_max+1], column 0 ignored, node i's parent in [0, M_b]
+ *            NEG1 : [B][M_max], node r (0-based) has parent -1 (the root) or 0..M_b-1;
+ *                   remapped here: node r -> r+1, parent -1 -> 0, parent v -> v+1
+ *   valid    [B][M_max+1] or NULL (all of 1..M_b valid)
+ *   anc      [B][M_max+1][D_max+1]   depth [B][M_max+1]   status [B]
+ * ---------------------------------------------------------------------------------- */
+int tmvref_build_ancestors(int B, int M_max, int D_max, int parent_format,
+                           const int32_t *parents, const uint8_t *valid,
+                           const int32_t *n_nodes,
+                           int32_t *anc, int32_t *depth, int32_t *status)
+{
+    if (B < 0 || M_max < 0 || D_max < 0) return REF_ERR_ARG;
+    const int W = D_max + 1, R = M_max + 1;
+    int32_t *par = (int32_t *)malloc(sizeof(int32_t) * (size_t)R);
+    uint8_t *ok = (uint8_t *)malloc((size_t)R);
+    if (!par || !ok) { free(par); free(ok); return REF_ERR_ARG; }
+
+    for (int b = 0; b < B; ++b) {
+        int32_t *A = anc + (int64_t)b * R * W;
+        int32_t *Dp = depth + (int64_t)b * R;
+        for (int64_t e = 0; e < (int64_t)R * W; ++e) A[e] = 0;
+        for (int i = 0; i < R; ++i) Dp[i] = 0;
+
+        const int M = n_nodes[b];
+        if (M < 0 || M > M_max) { status[b] = REF_ERR_RANGE; continue; }
+
+        /* parent of every node in virtual-root form; -1 marks a value that cannot be
+         * remapped (a NEG1 entry below -1), which the walk reports as RANGE */
+        for (int i = 1; i <= M; ++i) {
+            if (parent_format == REF_PARENTS_VROOT) {
+                par[i] = parents[(int64_t)b * R + i];
+            } else {
+                int32_t raw = parents[(int64_t)b * M_max + (i - 1)];
+                par[i] = raw == -1 ? 0 : (raw < -1 ? -1 : raw + 1);
+            }
+            ok[i] = valid ? (valid[(int64_t)b * R + i] != 0) : 1;
+        }
+
+        int st = REF_OK;
+        for (int i = 1; i <= M; ++i) {
+            if (!ok[i]) continue;
+            int code = REF_OK, d = 0, h = i, k = 0;
+            for (;;) {
+                if (k <= D_max) A[(int64_t)i * W + k] = h;
+                int p = par[h];
+                if (p < 0 || p > M) { code = REF_ERR_RANGE; break; }
+                if (p == 0) { d = k + 1; break; }
+                if (!ok[p]) { code = REF_ERR_CLOSURE; break; }
+                h = p;
+                ++k;
+                /* M hops without reaching the root revisit a node: a cycle */
+                if (k >= M) { code = REF_ERR_CYCLE; break; }
+            }
+            if (code == REF_OK && d > D_max) code = REF_ERR_DEPTH;
+            Dp[i] = d;
+            st = merge_code(st, code);
+        }
+        if (st != REF_OK) {
+            for (int64_t e = 0; e < (int64_t)R * W; ++e) A[e] = 0;
+            for (int i = 0; i < R; ++i) Dp[i] = 0;
+        }
+        status[b] = st;
+    }
+    free(par);
+    free(ok);
+    return REF_OK;
+}
+
+/* ------------------------------------------------------------------------------------
+ * Tree-masked attention [EP-zh §2.3, EP-pt §2, SDH Medusa section]: node i, query
+ * head h attends to the committed prefix [0,P_b) plus the cache slots of its own
+ * ancestor path including itself; node j's K/V live at slot P_b + j - 1.
+ * GQA: kv head = h / (Hq/Hkv).  Scores, softmax and the weighted sum in fp64.
+ *
+ *   q        [B][M_max][Hq][d] (element strides q_stride[0..2], d contiguous); row r = node r+1
+ *   k, v     [B][Hkv][L_cap][d] (element strides kv_stride[0..2], d contiguous)
+ *   out      dense fp64 [B][M_max][Hq][d]; rows of inert nodes are 0
+ *   row_select [B][M_max] or NULL: rows with 0 are skipped (left 0) -- a filter only
+ *   status   in/out: a prefix that does not fit (P_b<0 or P_b+M_b>L_cap) sets INPUT
+ * ---------------------------------------------------------------------------------- */
+int tmvref_tree_attention(int B, int M_max, int D_max, int Hq, int Hkv, int d, int dtype,
+                          const void *q, const int64_t *q_stride,
+                          const void *k, const void *v, const int64_t *kv_stride, int L_cap,
+                          const int32_t *prefix_len, const int32_t *n_nodes,
+                          const int32_t *anc, const int32_t *depth, int32_t *status,
+                          double scale, const uint8_t *row_select, double *out)
+{
+    if (B < 0 || M_max < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || d <= 0) return REF_ERR_ARG;
+    const int g = Hq / Hkv, W = D_max + 1, R = M_max + 1;
+    const int64_t out_elems = (int64_t)B * M_max * Hq * d;
+    for (int64_t e = 0; e < out_elems; ++e) out[e] = 0.0;
+
+    int64_t *cols = (int64_t *)malloc(sizeof(int64_t) * ((size_t)L_cap + 1));
+    double *s = (double *)malloc(sizeof(double) * ((size_t)L_cap + 1));
+    if (!cols || !s) { free(cols); free(s); return REF_ERR_ARG; }
+
+    for (int b = 0; b < B; ++b) {
+        if (status[b] != REF_OK) continue;
+        const int P = prefix_len[b], M = n_nodes[b];
+        if (P < 0 || (int64_t)P + M > L_cap) { status[b] = REF_ERR_INPUT; continue; }
+        for (int j = 1; j <= M; ++j) {
+            const int dep = depth[(int64_t)b * R + j];
+            if (dep < 1) continue;                      /* inert row */
+            if (row_select && !row_select[(int64_t)b * M_max + (j - 1)]) continue;
+
+            /* visible columns: the whole prefix, then the path j -> ... -> depth-1 node */
+            int64_t nc = 0;
+            for (int t = 0; t < P; ++t) cols[nc++] = t;
+            for (int kk = 0; kk < dep; ++kk) {
+                int node = anc[((int64_t)b * R + j) * W + kk];
+                cols[nc++] = (int64_t)P + node - 1;
+            }
+
+            for (int h = 0; h < Hq; ++h) {
+                const int kvh = h / g;
+                const int64_t qoff = b * q_stride[0] + (int64_t)(j - 1) * q_stride[1] + h * q_stride[2];
+                double mx = -INFINITY;
+                for (int64_t c = 0; c < nc; ++c) {
+                    const int64_t koff = b * kv_stride[0] + kvh * kv_stride[1] + cols[c] * kv_stride[2];
+                    double dot = 0.0;
+                    for (int e = 0; e < d; ++e)
+                        dot += load_elem(q, dtype, qoff + e) * load_elem(k, dtype, koff + e);
+                    s[c] = scale * dot;
+                    if (s[c] > mx) mx = s[c];
+                }
+                double den = 0.0;
+                for (int64_t c = 0; c < nc; ++c) { s[c] = exp(s[c] - mx); den += s[c]; }
+                double *o = out + (((int64_t)b * M_max + (j - 1)) * Hq + h) * d;
+                for (int64_t c = 0; c < nc; ++c) {
+                    const int64_t voff = b * kv_stride[0] + kvh * kv_stride[1] + cols[c] * kv_stride[2];
+                    const double w = s[c] / den;
+                    for (int e = 0; e < d; ++e) o[e] += w * load_elem(v, dtype, voff + e);
+                }
+            }
+        }
+    }
+    free(cols);
+    free(s);
+    return REF_OK;
+}
+
+/* ------------------------------------------------------------------------------------
+ * Greedy acceptance [SDH Medusa section: the longest valid path is kept; greedy-only
+ * teacher decoding is the baseline of EP-pt §4].
+ *   t(u) = argmax_x logits[b][u][x] (smallest x on ties) for u = 0 and every live node;
+ *   node i matches iff every edge on its path matches: tokens[c] == t(parent(c));
+ *   a* = deepest matching node (smallest id on ties; 0 if none);
+ *   accept_len = depth(a*), path = ids root->leaf, next_token = t(a*).
+ * NaN in a scanned row, or a live node's token outside [0,V), sets INPUT.
+ *   tokens  [B][M_max+1] (column 0 ignored);  logits row (b,u) at b*stride_b + u*stride_row
+ * ---------------------------------------------------------------------------------- */
+int tmvref_accept_greedy(int B, int M_max, int D_max, int V, const int32_t *tokens,
+                         int row_dtype, const void *logits, int64_t stride_b, int64_t stride_row,
+                         const int32_t *n_nodes, const int32_t *anc, const int32_t *depth,
+                         int32_t *status, int32_t *accept_len, int32_t *path, int32_t *next_token)
+{
+    if (B < 0 || M_max < 0 || D_max < 0 || V <= 0) return REF_ERR_ARG;
+    const int W = D_max + 1, R = M_max + 1;
+    int32_t *t = (int32_t *)malloc(sizeof(int32_t) * (size_t)R);
+    if (!t) return REF_ERR_ARG;
+
+    for (int b = 0; b < B; ++b) {
+        accept_len[b] = 0;
+        next_token[b] = 0;
+        for (int j = 0; j < D_max; ++j) path[(int64_t)b * D_max + j] = 0;
+        if (status[b] != REF_OK) continue;
+        const int M = n_nodes[b];
+        const int32_t *Dp = depth + (int64_t)b * R;
+        const int32_t *A = anc + (int64_t)b * R * W;
+        const int32_t *tok = tokens + (int64_t)b * R;
+
+        int bad = 0;
+        for (int u = 0; u <= M && !bad; ++u) {
+            if (u > 0 && Dp[u] < 1) continue;
+            if (u > 0 && (tok[u] < 0 || tok[u] >= V)) { bad = 1; break; }
+            const int64_t base = b * stride_b + u * stride_row;
+            double best = 0.0;
+            int arg = -1;
+            for (int x = 0; x < V; ++x) {
+                double val = load_elem(logits, row_dtype, base + x);
+                if (isnan(val)) { bad = 1; break; }
+                if (arg < 0 || val > best) { best = val; arg = x; }
+            }
+            t[u] = arg;
+        }
+        if (bad) { status[b] = REF_ERR_INPUT; continue; }
+
+        int star = 0, star_depth = 0;
+        for (int i = 1; i <= M; ++i) {
+            const int dep = Dp[i];
+            if (dep < 1) continue;
+            int match = 1;
+            for (int kk = 0; kk < dep; ++kk) {
+                int child = A[(int64_t)i * W + kk], par = A[(int64_t)i * W + kk + 1];
+                if (tok[child] != t[par]) { match = 0; break; }
+            }
+            if (match && dep > star_depth) { star = i; star_depth = dep; }
+        }
+        accept_len[b] = star_depth;
+        for (int j = 0; j < star_depth; ++j)
+            path[(int64_t)b * D_max + j] = A[(int64_t)star * W + (star_depth - 1 - j)];
+        next_token[b] = t[star];
+    }
+    free(t);
+    return REF_OK;
+}
+
+/* ------------------------------------------------------------------------------------
+ * Philox4x64-10 (Salmon et al., "Parallel random numbers: as easy as 1, 2, 3", SC'11):
+ * 10 rounds of two 64x64->128 multiplies with the published multipliers and Weyl key
+ * increments.
+ * ---------------------------------------------------------------------------------- */
+static void philox4x64_10(const uint64_t ctr_in[4], const uint64_t key_in[2], uint64_t out[4])
+{
+    uint64_t x0 = ctr_in[0], x1 = ctr_in[1], x2 = ctr_in[2], x3 = ctr_in[3];
+    uint64_t k0 = key_in[0], k1 = key_in[1];
+    for (int r = 0; r < 10; ++r) {
+        u128 p0 = (u128)0xD2E7470EE14C6C93ULL * x0;
+        u128 p1 = (u128)0xCA5A826395121157ULL * x2;
+        uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0;
+        uint64_t hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
+        x0 = hi1 ^ x1 ^ k0;
+        x1 = lo1;
+        x2 = hi0 ^ x3 ^ k1;
+        x3 = lo0;
+        k0 += 0x9E3779B97F4A7C15ULL;
+        k1 += 0xBB67AE8584CAA73BULL;
+    }
+    out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;
+}
+
+/* the n-th 64-bit word of the stream with the given key */
+static uint64_t philox_word(uint64_t seed, uint64_t stream, uint64_t n)
+{
+    uint64_t ctr[4] = { n / 4 + 1, 0, 0, 0 }, key[2] = { seed, stream }, out[4];
+    philox4x64_10(ctr, key, out);
+    return out[n % 4];
+}
+
+/* exported for the RNG pin: n words of stream {seed, stream} from word 0 */
+void tmvref_philox_words(uint64_t seed, uint64_t stream, int64_t n, uint64_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = philox_word(seed, stream, (uint64_t)i);
+}
+
+/* ------------------------------------------------------------------------------------
+ * Sampling acceptance [SDH, modified rejection sampling and its FAQ], extended to trees
+ * by trying a node's children one after another against the current residual.
+ *
+ * Exact integer fixed point (our reading; the pages give real-valued formulas):
+ *   WP_u(x) = floor(p[u][x] * 2^32), WQ_u(x) = floor(q[u][x] * 2^32); SP, SQ exact sums.
+ *   The working distribution is (W, S) with S = sum W.  After loading or updating it,
+ *   if bitlen(S) > 48 every W is shifted right by bitlen(S) - 48 and S recomputed.
+ *   Child c with token x, draw U = word >> 40 (24 bits):
+ *     accept  iff  U * WQ_u(x) * S < W(x) * SQ_u * 2^24     (i.e. u*q(x) < p_cur(x))
+ *     reject  ->   W(y) = max(0, W(y)*SQ_u - WQ_u(y)*S), S = sum, renormalise
+ *                  (kept unchanged if the residual is empty)
+ *   Draw from (W,S) with word: t = floor((word >> 32) * S / 2^32), token = min x with
+ *   sum_{y<=x} W(y) > t.  Stop at the first node whose children are all rejected
+ *   (correction) or at a node without children (bonus), drawing next_token there.
+ * Rows visited with entries outside [0,1] / non-finite, a zero p row, a zero q row
+ * under a node with children, or a live token outside [0,V) set INPUT.
+ *   p, q  [B][M_max+1][V] fp32 (row u = distribution after node u; row 0 after the prefix)
+ * ---------------------------------------------------------------------------------- */
+static int bitlen128(u128 x)
+{
+    int n = 0;
+    while (x) { ++n; x >>= 1; }
+    return n;
+}
+
+/* quantise row u of a distribution tensor; returns 0 on a malformed entry */
+static int quantise_row(const float *row, int V, u128 *w, u128 *sum)
+{
+    u128 s = 0;
+    for (int x = 0; x < V; ++x) {
+        double val = (double)row[x];
+        if (!(val >= 0.0 && val <= 1.0)) return 0;      /* also rejects NaN */
+        w[x] = (u128)(uint64_t)floor(val * 4294967296.0);
+        s += w[x];
+    }
+    *sum = s;
+    return 1;
+}
+
+static void renormalise(u128 *w, int V, u128 *sum)
+{
+    int bl = bitlen128(*sum);
+    if (bl <= 48) return;
+    int sh = bl - 48;
+    u128 s = 0;
+    for (int x = 0; x < V; ++x) { w[x] >>= sh; s += w[x]; }
+    *sum = s;
+}
+
+static int draw_token(const u128 *w, int V, u128 S, uint64_t word)
+{
+    u128 t = (((u128)(word >> 32)) * S) >> 32;
+    u128 c = 0;
+    for (int x = 0; x < V; ++x) {
+        c += w[x];
+        if (c > t) return x;
+    }
+    return V - 1;   /* unreachable: t < S */
+}
+
+/* exported for pins: the integer accept test and the inverse-CDF draw on one element */
+int tmvref_sample_accept_test(uint64_t u24, uint64_t wq_x, uint64_t S, uint64_t w_x, uint64_t SQ)
+{
+    return (u128)u24 * wq_x * S < ((u128)w_x * SQ) << 24;
+}
+
+int tmvref_sample_draw(const uint64_t *w, int V, uint64_t word)
+{
+    u128 *ww = (u128 *)malloc(sizeof(u128) * (size_t)V);
+    u128 S = 0;
+    for (int x = 0; x < V; ++x) { ww[x] = w[x]; S += w[x]; }
+    int r = draw_token(ww, V, S, word);
+    free(ww);
+    return r;
+}
+
+int tmvref_accept_sample(int B, int M_max, int D_max, int V, const int32_t *tokens,
+                         const float *p, const float *q, uint64_t seed, uint64_t step,
+                         const int32_t *n_nodes, const int32_t *anc, const int32_t *depth,
+                         int32_t *status, int32_t *accept_len, int32_t *path, int32_t *next_token)
+{
+    if (B < 0 || M_max < 0 || D_max < 0 || V <= 0) return REF_ERR_ARG;
+    const int W = D_max + 1, R = M_max + 1;
+    u128 *w = (u128 *)malloc(sizeof(u128) * (size_t)V);
+    u128 *wq = (u128 *)malloc(sizeof(u128) * (size_t)V);
+    u128 *wn = (u128 *)malloc(sizeof(u128) * (size_t)V);
+    int32_t *kids = (int32_t *)malloc(sizeof(int32_t) * (size_t)R);
+    if (!w || !wq || !wn || !kids) { free(w); free(wq); free(wn); free(kids); return REF_ERR_ARG; }
+
+    for (int b = 0; b < B; ++b) {
+        accept_len[b] = 0;
+        next_token[b] = 0;
+        for (int j = 0; j < D_max; ++j) path[(int64_t)b * D_max + j] = 0;
+        if (status[b] != REF_OK) continue;
+        const int M = n_nodes[b];
+        const int32_t *Dp = depth + (int64_t)b * R;
+        const int32_t *A = anc + (int64_t)b * R * W;
+        const int32_t *tok = tokens + (int64_t)b * R;
+        const uint64_t stream = (step << 32) | (uint64_t)(uint32_t)b;
+        const float *pb = p + (int64_t)b * R * V, *qb = q + (int64_t)b * R * V;
+
+        int bad = 0;
+        for (int i = 1; i <= M; ++i)
+            if (Dp[i] >= 1 && (tok[i] < 0 || tok[i] >= V)) bad = 1;
+
+        uint64_t n = 0;
+        int u = 0, acc = 0, out_tok = 0;
+        u128 S = 0;
+        if (!bad && !(quantise_row(pb, V, w, &S) && S > 0)) bad = 1;
+        if (!bad) renormalise(w, V, &S);
+        while (!bad) {
+            int nk = 0;
+            for (int c = 1; c <= M; ++c)
+                if (Dp[c] >= 1 && A[(int64_t)c * W + 1] == u) kids[nk++] = c;
+            if (nk == 0) { out_tok = draw_token(w, V, S, philox_word(seed, stream, n++)); break; }
+
+            u128 SQ = 0;
+            if (!(quantise_row(qb + (int64_t)u * V, V, wq, &SQ) && SQ > 0)) { bad = 1; break; }
+            int moved = 0;
+            for (int ci = 0; ci < nk; ++ci) {
+                const int c = kids[ci], x = tok[c];
+                const uint64_t U = philox_word(seed, stream, n++) >> 40;
+                if ((u128)U * wq[x] * S < (w[x] * SQ) << 24) {
+                    path[(int64_t)b * D_max + acc] = c;
+                    ++acc;
+                    u = c;
+                    if (!(quantise_row(pb + (int64_t)c * V, V, w, &S) && S > 0)) { bad = 1; break; }
+                    renormalise(w, V, &S);
+                    moved = 1;
+                    break;
+                }
+                u128 Sn = 0;
+                for (int y = 0; y < V; ++y) {
+                    u128 a = w[y] * SQ, c2 = wq[y] * S;
+                    wn[y] = a > c2 ? a - c2 : 0;
+                    Sn += wn[y];
+                }
+                if (Sn > 0) {
+                    for (int y = 0; y < V; ++y) w[y] = wn[y];
+                    S = Sn;
+                    renormalise(w, V, &S);
+                }
+            }
+            if (bad) break;
+            if (!moved) { out_tok = draw_token(w, V, S, philox_word(seed, stream, n++)); break; }
+        }
+        if (bad) {
+            status[b] = REF_ERR_INPUT;
+            for (int j = 0; j < D_max; ++j) path[(int64_t)b * D_max + j] = 0;
+            continue;
+        }
+        accept_len[b] = acc;
+        next_token[b] = out_tok;
+    }
+    free(w); free(wq); free(wn); free(kids);
+    return REF_OK;
+}
+
+/* ------------------------------------------------------------------------------------
+ * Path-index commit with prefix sharing [EP-zh §2.1, EP-pt §2]: the committed prefix
+ * is left untouched; for j < A_b the row at slot P_b + path[j] - 1 is copied to slot
+ * P_b + j (all sources are read before any destination is written), for every layer,
+ * KV head, and both K and V.  new_len = P_b + A_b.  A sequence whose status is not OK,
+ * or whose lengths / path do not fit, moves nothing and keeps new_len = P_b (a fit
+ * problem also sets INPUT).
+ *   caches [n_layers][B][Hkv][L_cap][d], element strides stride[0..3], d contiguous
+ * ---------------------------------------------------------------------------------- */
+int tmvref_commit(int n_layers, int B, int Hkv, int d, int L_cap, int M_max, int D_max,
+                  int elem_bytes, void *k_cache, void *v_cache, const int64_t *stride,
+                  const int32_t *prefix_len, const int32_t *n_nodes,
+                  const int32_t *accept_len, const int32_t *path,
+                  int32_t *status, int32_t *new_len)
+{
+    if (n_layers < 0 || B < 0 || Hkv <= 0 || d <= 0 || D_max < 0 || (elem_bytes != 2 && elem_bytes != 4))
+        return REF_ERR_ARG;
+    (void)M_max;    /* kept for symmetry with the device entry point */
+    const size_t row_bytes = (size_t)d * elem_bytes;
+    uint8_t *snap = (uint8_t *)malloc(row_bytes * ((size_t)D_max + 1));
+    if (!snap) return REF_ERR_ARG;
+
+    for (int b = 0; b < B; ++b) {
+        const int P = prefix_len[b];
+        new_len[b] = P;
+        if (status[b] != REF_OK) continue;
+        const int M = n_nodes[b], A = accept_len[b];
+        int fits = P >= 0 && (int64_t)P + M <= L_cap && A >= 0 && A <= D_max && A <= M;
+        for (int j = 0; fits && j < A; ++j) {
+            int node = path[(int64_t)b * D_max + j];
+            if (node < 1 || node > M) fits = 0;
+        }
+        if (!fits) { status[b] = REF_ERR_INPUT; continue; }
+        new_len[b] = P + A;
+
+        for (int layer = 0; layer < n_layers; ++layer)
+            for (int h = 0; h < Hkv; ++h)
+                for (int which = 0; which < 2; ++which) {
+                    uint8_t *base = (uint8_t *)(which == 0 ? k_cache : v_cache);
+                    const int64_t head_off = layer * stride[0] + b * stride[1] + h * stride[2];
+                    for (int j = 0; j < A; ++j) {
+                        int64_t src = (int64_t)P + path[(int64_t)b * D_max + j] - 1;
+                        memcpy(snap + (size_t)j * row_bytes,
+                               base + (head_off + src * stride[3]) * elem_bytes, row_bytes);
+                    }
+                    for (int j = 0; j < A; ++j) {
+                        int64_t dst = (int64_t)P + j;
+                        memcpy(base + (head_off + dst * stride[3]) * elem_bytes,
+                               snap + (size_t)j * row_bytes, row_bytes);
+                    }
+                }
+    }
+    free(snap);
+    return REF_OK;
+}

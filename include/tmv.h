@@ -1,0 +1,219 @@
+/*
+ * tmv.h -- C ABI of libtmv.so: the teacher's tree-verification step of tree speculative
+ * decoding, on AMD Instinct MI355X (gfx950).
+ *
+ * Four calls, one per stage of a verify step, all enqueued on the caller's HIP stream:
+ *
+ *   tmv_tree_build_ancestors   parents -> virtual-root ancestor table + invariant checks
+ *   tmv_tree_verify_attention  tree-masked attention of every draft node over the
+ *                              committed prefix plus its own ancestor path
+ *   tmv_tree_accept            greedy longest matching path, or modified rejection
+ *                              sampling with a max(0, p - q) residual
+ *   tmv_kv_commit_path         prefix-sharing compaction of the accepted path's K/V rows
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument is DEVICE memory owned by the caller (for example a torch
+ *     tensor's data_ptr), except the small int64 stride arrays, which are HOST arrays read
+ *     during the call.  The library keeps no global state and allocates nothing; scratch
+ *     memory comes from a caller workspace whose size the *_workspace call returns.  A
+ *     workspace must be zero-filled once before its first use; every call leaves it in
+ *     that state again, so it can be reused by the next call on the same stream (calls that
+ *     overlap in time must not share a workspace).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are asynchronous; none
+ *     synchronises the host.
+ *   - The return value reports problems the host can see (TMV_ERR_ARG: bad sizes, null
+ *     pointers, unsupported shapes; nothing was launched) or a failed launch
+ *     (TMV_ERR_DEVICE).  Problems in the data (a malformed tree, a NaN logit, a prefix that
+ *     does not fit) are reported per sequence in the caller's device array status[B]: a
+ *     stage only ever moves a sequence from TMV_OK to an error, and a failed sequence is
+ *     inert downstream (zero outputs, accept length 0, nothing committed).
+ *   - No stage ever reads or writes outside the buffers described below, and no output
+ *     ever holds a negative or out-of-range index.
+ *
+ * Node numbering (virtual root): row 0 is a virtual root that carries no K/V; draft nodes
+ * are 1..M_b.  This and the ancestor table follow section 2.2 of the Chinese technical
+ * summary of "EAGLE-Pangu: Accelerator-Safe Tree Speculative Decoding on Ascend NPUs"
+ * (parent pointers remapped onto a root row 0 so every gather index lies in [0, M]).
+ *
+ * Limits (host-checked): 0 <= M_max <= 128, 0 <= D_max <= 128, B >= 0, V >= 1.
+ */
+#ifndef TMV_H
+#define TMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes (return values and per-sequence status words) */
+enum {
+    TMV_OK = 0,
+    TMV_ERR_ARG = 1,      /* host-visible bad argument; nothing launched               */
+    TMV_ERR_RANGE = 2,    /* a parent index outside [0, M_b] (incl. a -1 sentinel), or
+                             M_b outside [0, M_max]                                     */
+    TMV_ERR_CYCLE = 3,    /* a parent chain never reaches the root                      */
+    TMV_ERR_DEPTH = 4,    /* a node deeper than D_max                                   */
+    TMV_ERR_CLOSURE = 5,  /* a valid node under an invalid one                          */
+    TMV_ERR_INPUT = 6,    /* malformed data: NaN / out-of-range probabilities, a token
+                             outside [0,V), a prefix or path that does not fit the cache */
+    TMV_ERR_DEVICE = 7    /* a kernel launch failed                                     */
+};
+
+enum { TMV_F32 = 0, TMV_BF16 = 1 };                       /* element types           */
+enum { TMV_PARENTS_VROOT = 0, TMV_PARENTS_NEG1 = 1 };     /* parent table formats    */
+enum { TMV_ACCEPT_GREEDY = 0, TMV_ACCEPT_SAMPLE = 1 };    /* acceptance rules        */
+
+/* Human-readable name of a status code (static string). */
+const char *tmv_status_string(int code);
+
+/* ABI version of this library (increments on any signature change). */
+int tmv_abi_version(void);
+
+/*
+ * tmv_tree_build_ancestors -- accelerator-safe tree tensors.
+ * Defined by section 2.2 of the Chinese EAGLE-Pangu technical summary (virtual root 0,
+ * precomputed ancestor table, range / acyclicity / validity-closure checks before any
+ * fused kernel) and section 2 of the Portuguese one (negative sentinels replaced by a
+ * valid root index).
+ *
+ *   parents   VROOT: int32 [B][M_max+1]; column 0 is ignored; node i in 1..M_b has parent
+ *                    parents[b][i] in [0, M_b] (0 = the virtual root).
+ *             NEG1 : int32 [B][M_max]; node r in 0..M_b-1 (0-based) has parent -1 (the
+ *                    original root) or 0..M_b-1; remapped here to node r+1 with parent
+ *                    -1 -> 0 and v -> v+1.  Values below -1 are RANGE errors.
+ *   valid     uint8 [B][M_max+1] or NULL (NULL: nodes 1..M_b are all valid).  Invalid
+ *             nodes are inert; a valid node whose parent is invalid is a CLOSURE error.
+ *   n_nodes   int32 [B]: M_b.
+ *   anc       out int32 [B][M_max+1][D_max+1]: anc[b][i][k] = parent^k(i), saturating at
+ *             0; anc[b][i][depth(i)] = 0.  Row 0, rows > M_b and invalid rows are all 0.
+ *   depth     out int32 [B][M_max+1]: hops from node i to the root (0 for inert rows).
+ *   status    out int32 [B]: written (not merged) by this stage: TMV_OK or the smallest
+ *             error code found among the sequence's nodes; a failed sequence's anc/depth
+ *             rows are all 0.
+ */
+int tmv_tree_build_ancestors(int B, int M_max, int D_max, int parent_format,
+                             const int32_t *parents, const uint8_t *valid,
+                             const int32_t *n_nodes,
+                             int32_t *anc, int32_t *depth, int32_t *status,
+                             void *stream);
+
+/*
+ * tmv_tree_verify_attention -- tree-masked attention of the flattened draft tree.
+ * Defined by section 2.3 of the Chinese EAGLE-Pangu technical summary (all speculative
+ * nodes evaluated in one teacher pass; node k attends only to its ancestor path,
+ * itself included) and the Medusa section of "Speculative Decoding Hierarquico: Medusa,
+ * EAGLE-2 e Multi-Token Prediction" (parallel nodes see only their direct ancestors).
+ * Equivalently: node i's output equals causal attention over the linear sequence
+ * prefix + path(i).  The 4D mask of the pages is never materialised: each row's
+ * ancestor set is a bitmask built in registers from `anc`.
+ *
+ *   dtype     TMV_F32 or TMV_BF16 for q, k_cache, v_cache and out (fp32 accumulation).
+ *   q         [B][M_max][Hq][d] with element strides q_stride = {batch, node, head}; d is
+ *             contiguous; row r holds node r+1.
+ *   k_cache,
+ *   v_cache   [B][Hkv][L_cap][d] with element strides kv_stride = {batch, head, slot}; d is
+ *             contiguous.  Slots [0, P_b) hold the committed prefix; node j's K/V (written
+ *             by the caller's teacher layer) live at slot P_b + j - 1.
+ *   prefix_len int32 [B]: P_b.  A sequence with P_b < 0 or P_b + M_b > L_cap gets status
+ *             TMV_ERR_INPUT and zero outputs.
+ *   anc, depth, n_nodes, status: from tmv_tree_build_ancestors (status in/out).
+ *   scale     softmax scale (typically 1/sqrt(d)).
+ *   out       [B][M_max][Hq][d] with element strides o_stride = {batch, node, head}: one
+ *             row per node and query head; rows of inert nodes (beyond M_b, invalid, or
+ *             in a failed sequence) are written as 0.
+ *   GQA: query head h reads KV head h / (Hq/Hkv).  Requires Hq % Hkv == 0, d in {64,128},
+ *        Hq/Hkv <= 16, 1 <= L_cap.
+ *   workspace: tmv_tree_verify_attention_workspace() bytes (split-KV partials and
+ *        combine counters), zero-filled before first use.
+ */
+size_t tmv_tree_verify_attention_workspace(int dtype, int B, int M_max, int Hq, int Hkv,
+                                           int d, int L_cap);
+int tmv_tree_verify_attention(int dtype, int B, int M_max, int D_max, int Hq, int Hkv, int d,
+                              const void *q, const int64_t *q_stride,
+                              const void *k_cache, const void *v_cache,
+                              const int64_t *kv_stride, int L_cap,
+                              const int32_t *prefix_len, const int32_t *n_nodes,
+                              const int32_t *anc, const int32_t *depth, int32_t *status,
+                              float scale, void *out, const int64_t *o_stride,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * tmv_tree_accept -- choose the accepted path and the next token.
+ *
+ * GREEDY (Medusa section of the hierarchical speculative decoding blog: the longest
+ * valid branch is kept; teacher-greedy decoding is the baseline of section 4 of the
+ * Portuguese EAGLE-Pangu summary):
+ *   t(u) = argmax_x teacher[b][u][x] (smallest x on ties) for u = 0 and every live node;
+ *   node i matches iff every node c on its path has tokens[c] == t(parent(c));
+ *   the deepest matching node a* (smallest id on ties; 0 if none) gives
+ *   accept_len = depth(a*), path = its ancestors root->leaf, next_token = t(a*).
+ *   teacher: logits, f32 or bf16 (row_dtype).  NaN in a scanned row -> TMV_ERR_INPUT.
+ *
+ * SAMPLE (modified rejection sampling section of the same blog: a draft token x is kept
+ *   with probability min(1, p(x)/q(x)); on refusal the rest is dropped and a correction
+ *   is drawn from max(0, p - q) renormalised; its FAQ: a correction is emitted when all
+ *   guesses are refused).  On a tree, the children of the current node are tried in
+ *   ascending id, each against the residual left by the refused siblings; a walk that
+ *   reaches a node without children draws a bonus token from that node's p.
+ *   teacher = p, draft_q = q: f32 probabilities; row u is the distribution after node u
+ *   (row 0 after the prefix); children of u must have been drawn from q row u.
+ *   Arithmetic is exact integer fixed point: W(x) = floor(p(x) 2^32) (and q alike),
+ *   working sums renormalised to <= 48 bits by right shifts, the accept test
+ *   U24 * Wq(x) * S < W(x) * Sq * 2^24 in 128-bit integers, the residual
+ *   max(0, W(y) Sq - Wq(y) S), and draws by inverse CDF over floor((word>>32) S / 2^32).
+ *   Random words: Philox4x64-10, key {seed, (step << 32) | b}, block n at counter
+ *   {n+1, 0, 0, 0}, word n = 64-bit lane n % 4 of block n / 4 (numpy's Philox stream);
+ *   one word per tried child, one per final draw, in walk order.
+ *   Visited rows with entries outside [0,1] or NaN, a zero p row, or a zero q row under a
+ *   node with children -> TMV_ERR_INPUT.
+ *
+ *   tokens     int32 [B][M_max+1] draft tokens (column 0 ignored); a live node's token
+ *              outside [0, V) -> TMV_ERR_INPUT.
+ *   teacher    [B][M_max+1][V] rows at teacher + b*t_stride_b + u*t_stride_row (elements).
+ *   draft_q    SAMPLE only: f32 rows at draft_q + b*q_stride_b + u*q_stride_row; NULL for
+ *              GREEDY.
+ *   accept_len out int32 [B]; path out int32 [B][D_max] (node ids root->leaf, then 0);
+ *   next_token out int32 [B].  All 0 for a failed sequence.
+ *   workspace: tmv_tree_accept_workspace() bytes, zero-filled before first use.
+ */
+size_t tmv_tree_accept_workspace(int mode, int B, int M_max, int V);
+int tmv_tree_accept(int mode, int B, int M_max, int D_max, int V,
+                    const int32_t *tokens, int row_dtype, const void *teacher,
+                    int64_t t_stride_b, int64_t t_stride_row,
+                    const float *draft_q, int64_t q_stride_b, int64_t q_stride_row,
+                    uint64_t seed, uint64_t step,
+                    const int32_t *n_nodes, const int32_t *anc, const int32_t *depth,
+                    int32_t *status, int32_t *accept_len, int32_t *path, int32_t *next_token,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * tmv_kv_commit_path -- prefix-sharing path-index commit, in place.
+ * Defined by section 2.1 of the Chinese EAGLE-Pangu technical summary (commit by
+ * accepted length or by path index; a prefix-sharing fast reorder moves only the newly
+ * accepted segment) and section 2 of the Portuguese one.
+ * For every layer, KV head and both caches: the rows at slots P_b + path[b][j] - 1,
+ * j < accept_len[b], are read first and then written to slots P_b + j; rows whose source
+ * equals their destination are not touched; the prefix [0, P_b) and every other slot are
+ * left unchanged.  new_len[b] = P_b + accept_len[b].
+ *   dtype      TMV_F32 or TMV_BF16 (rows are moved as bytes).
+ *   k_cache,
+ *   v_cache    [n_layers][B][Hkv][L_cap][d] with element strides
+ *              kv_stride = {layer, batch, head, slot}; d contiguous.
+ *   A sequence whose status is not OK moves nothing (new_len = P_b).  A sequence whose
+ *   P_b, M_b, accept_len or path entries do not fit (P_b < 0, P_b + M_b > L_cap,
+ *   accept_len outside [0, min(D_max, M_b)], a path entry outside [1, M_b]) moves nothing
+ *   and gets TMV_ERR_INPUT.  Requires d * element size <= 512 bytes and a multiple of 16.
+ */
+int tmv_kv_commit_path(int dtype, int n_layers, int B, int Hkv, int d, int L_cap,
+                       int M_max, int D_max,
+                       void *k_cache, void *v_cache, const int64_t *kv_stride,
+                       const int32_t *prefix_len, const int32_t *n_nodes,
+                       const int32_t *accept_len, const int32_t *path,
+                       int32_t *status, int32_t *new_len, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TMV_H */

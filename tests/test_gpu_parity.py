@@ -1,0 +1,178 @@
+"""Device parity: the HIP path through the C ABI against the oracle on the same seeded
+inputs.  Bit-exact for ancestor tables, statuses, accepted lengths, paths and next
+tokens; attention within 2e-2 absolute (bf16) / 1e-5 (fp32), plus a relative-L2
+diagnostic and mask-sensitive variants (empty prefix, sharpened queries) that a wrong
+mask cannot pass."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import tmv_inputs as ti
+from tests.harness import DeviceStep, attention_error, host_bits, oracle_attention, oracle_tables
+from tests.test_oracle_build import random_labelled_tree
+
+pytestmark = pytest.mark.gpu
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _case(name):
+    print("\n[gpu case] %s" % name, flush=True)
+
+
+def small_attention_workload(seed, B, Hq, Hkv, d, M_max, prefixes, n_nodes, dtype=ti.BF16, q_scale=1.0,
+                             sigma=0.5, max_depth=6, labelled=True):
+    rng = np.random.default_rng(seed)
+    parents = np.zeros((B, M_max + 1), np.int32)
+    for b in range(B):
+        m = int(n_nodes[b])
+        parents[b, : m + 1] = random_labelled_tree(rng, m, max_depth) if labelled else ti.tree_random(rng, m, max_depth)
+    L_cap = int(max(np.asarray(prefixes) + np.asarray(n_nodes))) + 5
+    mk = lambda shape, s: rng.standard_normal(shape).astype(np.float32) * np.float32(s)
+    q = mk((B, M_max, Hq, d), sigma * q_scale)
+    k = mk((B, Hkv, L_cap, d), sigma)
+    v = mk((B, Hkv, L_cap, d), sigma)
+    if dtype == ti.BF16:
+        q, k, v = ti.bf16_bits(q), ti.bf16_bits(k), ti.bf16_bits(v)
+    return ti.Workload("small", dtype, B, Hq, Hkv, d, M_max, max(max_depth, 1), L_cap, 16, "greedy", parents,
+                       np.asarray(n_nodes, np.int32), np.asarray(prefixes, np.int32),
+                       np.zeros((B, M_max + 1), np.int32), q, k, v)
+
+
+# ------------------------------------------------------------------ stage 1
+def test_build_ancestors_random_trees(ref):
+    _case("build: random labelled trees")
+    rng = np.random.default_rng(101)
+    for M_max, D_max in [(8, 8), (60, 6), (128, 8), (128, 128)]:
+        B = 40
+        n = rng.integers(0, M_max + 1, size=B).astype(np.int32)
+        parents = np.zeros((B, M_max + 1), np.int32)
+        for b in range(B):
+            parents[b, : n[b] + 1] = random_labelled_tree(rng, int(n[b]), min(D_max + (b % 3 == 0), 12))
+        w = ti.Workload("build", ti.F32, B, 1, 1, 64, M_max, D_max, 1, 1, "greedy", parents, n, n * 0, n * 0)
+        dev = DeviceStep(w)
+        dev.build()
+        a, d, s = dev.tables()
+        ra, rd, rs = oracle_tables(ref, w)
+        assert np.array_equal(s, rs) and np.array_equal(a, ra) and np.array_equal(d, rd)
+
+
+def test_build_ancestors_malformed_and_formats(ref):
+    _case("build: malformed fixtures, NEG1, valid masks")
+    cases = []
+    for line in open(os.path.join(GOLD, "malformed_trees.txt")):
+        if line.strip() and line[0] != "#":
+            cases.append([f.strip() for f in line.split("|")])
+    M_max, D_max = 6, 4
+    B = len(cases)
+    parents = np.zeros((B, M_max + 1), np.int32)
+    valid = np.ones((B, M_max + 1), np.uint8)
+    n = np.zeros(B, np.int32)
+    for b, (name, M, D, pars, vmask, want) in enumerate(cases):
+        n[b] = int(M)
+        if int(M):
+            parents[b, 1:int(M) + 1] = [int(x) for x in pars.split()]
+        if vmask != "-":
+            valid[b, 1:int(M) + 1] = [int(x) for x in vmask.split()]
+    for D in (3, 4):
+        w = ti.Workload("bad", ti.F32, B, 1, 1, 64, M_max, D, 1, 1, "greedy", parents, n, n * 0, n * 0)
+        dev = DeviceStep(w)
+        dev.build(valid=torch.from_numpy(valid).cuda())
+        a, d, s = dev.tables()
+        ra, rd, rs = ref.build_ancestors(parents, n, M_max, D, valid=valid)
+        assert np.array_equal(s, rs) and np.array_equal(a, ra) and np.array_equal(d, rd)
+    # NEG1 form and out-of-range node counts
+    rng = np.random.default_rng(102)
+    B, M_max = 12, 20
+    n = rng.integers(0, M_max + 1, size=B).astype(np.int32)
+    n[0], n[1] = -1, M_max + 1
+    neg1 = np.zeros((B, M_max), np.int32)
+    for b in range(2, B):
+        par = ti.tree_random(rng, int(n[b]), 5)
+        neg1[b, : n[b]] = par[1:] - 1
+    neg1[5, 0] = -3
+    w = ti.Workload("neg1", ti.F32, B, 1, 1, 64, M_max, 5, 1, 1, "greedy", neg1, n, n * 0, n * 0)
+    dev = DeviceStep(w)
+    dev.build(parent_format=1)
+    a, d, s = dev.tables()
+    ra, rd, rs = ref.build_ancestors(neg1, n, M_max, 5, parent_format=ref.PARENTS_NEG1)
+    assert np.array_equal(s, rs) and np.array_equal(a, ra) and np.array_equal(d, rd)
+
+
+# ------------------------------------------------------------------ stage 2
+def _attention_parity(ref, w, tol, rel_tol, rows=None):
+    dev = DeviceStep(w)
+    dev.build()
+    dev.attention()
+    a, d, s = dev.tables()
+    ra, rd, rs = oracle_tables(ref, w)
+    assert np.array_equal(s, rs) and np.array_equal(a, ra)
+    ref_out, ref_st = oracle_attention(ref, w, ra, rd, rs, row_select=rows)
+    out = host_bits(dev.out)
+    assert np.array_equal(host_bits(dev.status), ref_st)
+    mask = None
+    if rows is not None:
+        mask = np.zeros(out.shape, bool)
+        mask[rows.astype(bool)] = True
+    err, rel = attention_error(out, ref_out, w.dtype, mask)
+    print("    max|err| %.3g  relL2 %.3g" % (err, rel), flush=True)
+    assert err <= tol and rel <= rel_tol
+    if rows is None:
+        assert not np.any(np.isnan(out.astype(np.float64) if w.dtype == ti.F32 else ti.bf16_to_f32(out)))
+    return dev
+
+
+def test_attention_tiny_fp32_workload(ref):
+    _case("attention: tiny fp32 workload (config 1)")
+    _attention_parity(ref, ti.workload(1), 1e-5, 1e-6)
+
+
+@pytest.mark.parametrize("variant", ["plain", "empty_prefix", "sharpened", "tiny_prefix_sharp"])
+def test_attention_bf16_small_ragged(ref, variant):
+    _case("attention: bf16 ragged small, %s" % variant)
+    B, Hq, Hkv, d, M_max = 3, 8, 2, 128, 37
+    n_nodes = [37, 20, 1]
+    prefixes = {"plain": [700, 33, 5], "empty_prefix": [0, 0, 0], "sharpened": [300, 64, 1],
+                "tiny_prefix_sharp": [1, 2, 0]}[variant]
+    q_scale = 8.0 if "sharp" in variant else 1.0
+    w = small_attention_workload(200, B, Hq, Hkv, d, M_max, prefixes, n_nodes, q_scale=q_scale)
+    _attention_parity(ref, w, 2e-2, 1e-2)
+
+
+@pytest.mark.parametrize("Hq,Hkv,d", [(4, 4, 128), (16, 2, 64), (12, 4, 64), (64, 8, 128)])
+def test_attention_bf16_head_shapes(ref, Hq, Hkv, d):
+    _case("attention: bf16 Hq=%d Hkv=%d d=%d" % (Hq, Hkv, d))
+    w = small_attention_workload(201 + Hq, 2, Hq, Hkv, d, 24, [129, 0], [24, 17], q_scale=4.0)
+    _attention_parity(ref, w, 2e-2, 1e-2)
+
+
+def test_attention_fp32_general(ref):
+    _case("attention: fp32 general shapes")
+    w = small_attention_workload(205, 3, 6, 2, 128, 30, [90, 0, 257], [30, 11, 4], dtype=ti.F32, sigma=1.0)
+    _attention_parity(ref, w, 1e-5, 1e-6)
+
+
+def test_attention_llama8b_layer_full(ref):
+    _case("attention: 8B-shaped layer, every row (config 2)")
+    w = ti.workload(2)
+    _attention_parity(ref, w, 2e-2, 1e-2)
+    # the same tree with an empty prefix and sharpened queries: mask errors become O(1)
+    w2 = ti.workload(2)
+    w2.prefix = np.array([0], np.int32)
+    w2.q = ti.bf16_bits(ti.bf16_to_f32(w2.q) * 8.0)
+    _attention_parity(ref, w2, 2e-2, 1e-2)
+
+
+def test_attention_determinism():
+    _case("attention: bit-identical reruns")
+    w = ti.workload(2)
+    dev = DeviceStep(w)
+    dev.build()
+    dev.attention()
+    first = host_bits(dev.out).copy()
+    for _ in range(3):
+        dev.out.fill_(float("nan"))
+        dev.attention()
+        assert np.array_equal(host_bits(dev.out), first)

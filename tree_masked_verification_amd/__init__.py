@@ -1,0 +1,212 @@
+"""tree_masked_verification_amd -- MI355X (gfx950) tree-verification step.
+
+Thin ctypes binding of libtmv.so (see include/tmv.h for the C ABI).  Every function
+only marshals torch tensors into pointers, strides and the current HIP stream; all
+work runs in the library's HIP kernels.  If the library is not built, importing this
+package raises ImportError -- there is no fallback.
+
+Stages of one verify step, in order:
+  tree_build_ancestors   parents -> (anc, depth, status)
+  tree_verify_attention  tree-masked attention of all draft nodes
+  tree_accept            greedy longest matching path, or modified rejection sampling
+  kv_commit_path         prefix-sharing in-place compaction of the accepted K/V rows
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtmv.so")
+
+OK, ERR_ARG, ERR_RANGE, ERR_CYCLE, ERR_DEPTH, ERR_CLOSURE, ERR_INPUT, ERR_DEVICE = range(8)
+F32, BF16 = 0, 1
+PARENTS_VROOT, PARENTS_NEG1 = 0, 1
+ACCEPT_GREEDY, ACCEPT_SAMPLE = 0, 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libtmv.so is not built (run `python -m tree_masked_verification_amd.build`); "
+                      "the tree-verification path has no CPU fallback")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P, _I, _I64, _U64, _F, _SZ = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float,
+                               ctypes.c_size_t)
+_lib.tmv_status_string.argtypes = [_I]
+_lib.tmv_status_string.restype = ctypes.c_char_p
+_lib.tmv_abi_version.restype = _I
+_lib.tmv_tree_build_ancestors.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]
+_lib.tmv_tree_verify_attention_workspace.argtypes = [_I, _I, _I, _I, _I, _I, _I]
+_lib.tmv_tree_verify_attention_workspace.restype = _SZ
+_lib.tmv_tree_verify_attention.argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P,
+                                           _F, _P, _P, _P, _SZ, _P]
+_lib.tmv_tree_accept_workspace.argtypes = [_I, _I, _I, _I]
+_lib.tmv_tree_accept_workspace.restype = _SZ
+_lib.tmv_tree_accept.argtypes = [_I, _I, _I, _I, _I, _P, _I, _P, _I64, _I64, _P, _I64, _I64, _U64, _U64,
+                                 _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+_lib.tmv_kv_commit_path.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+
+EXPORTED = ("tmv_status_string", "tmv_abi_version", "tmv_tree_build_ancestors",
+            "tmv_tree_verify_attention_workspace", "tmv_tree_verify_attention", "tmv_tree_accept_workspace",
+            "tmv_tree_accept", "tmv_kv_commit_path")
+
+
+class TmvError(RuntimeError):
+    def __init__(self, code, what):
+        super().__init__("%s: %s (code %d)" % (what, status_string(code), code))
+        self.code = code
+
+
+def status_string(code: int) -> str:
+    return _lib.tmv_status_string(int(code)).decode()
+
+
+def abi_version() -> int:
+    return int(_lib.tmv_abi_version())
+
+
+def library():
+    """The loaded ctypes handle (for callers that need the raw ABI)."""
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _strides(t, dims):
+    return (ctypes.c_int64 * len(dims))(*[t.stride(i) for i in dims])
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("unsupported dtype %s" % t.dtype)
+
+
+def _check(rc, what):
+    if rc != OK:
+        raise TmvError(rc, what)
+
+
+def _i32(*ts):
+    for t in ts:
+        if t is not None and (t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous()):
+            raise TypeError("expected contiguous int32 device tensors")
+
+
+# ------------------------------------------------------------------------ stage 1
+def tree_build_ancestors(parents, n_nodes, anc, depth, status, parent_format=PARENTS_VROOT, valid=None,
+                         stream=None):
+    """parents int32 [B][M_max+1] (VROOT) or [B][M_max] (NEG1); anc [B][M_max+1][D_max+1],
+    depth [B][M_max+1], status [B] (outputs); valid uint8 [B][M_max+1] or None."""
+    _i32(parents, n_nodes, anc, depth, status)
+    B, R, W = anc.shape
+    if valid is not None and (valid.dtype != torch.uint8 or not valid.is_contiguous()):
+        raise TypeError("valid must be contiguous uint8")
+    _check(_lib.tmv_tree_build_ancestors(B, R - 1, W - 1, parent_format, _ptr(parents), _ptr(valid), _ptr(n_nodes),
+                                         _ptr(anc), _ptr(depth), _ptr(status), _stream(stream)),
+           "tree_build_ancestors")
+
+
+# ------------------------------------------------------------------------ stage 2
+def tree_verify_attention_workspace(dtype, B, M_max, Hq, Hkv, d, L_cap) -> int:
+    return int(_lib.tmv_tree_verify_attention_workspace(dtype, B, M_max, Hq, Hkv, d, L_cap))
+
+
+def tree_verify_attention(q, k_cache, v_cache, prefix_len, n_nodes, anc, depth, status, out, scale=None,
+                          workspace=None, stream=None):
+    """q, out [B][M_max][Hq][d]; k_cache, v_cache [B][Hkv][L_cap][d] (same dtype, d contiguous)."""
+    _i32(prefix_len, n_nodes, anc, depth, status)
+    dt = _dtype_code(q)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype or out.dtype != q.dtype:
+        raise TypeError("q, k_cache, v_cache and out must share a dtype")
+    if k_cache.shape != v_cache.shape or k_cache.stride() != v_cache.stride():
+        raise ValueError("k_cache and v_cache must have the same shape and strides")
+    B, M_max, Hq, d = q.shape
+    Hkv, L_cap = k_cache.shape[1], k_cache.shape[2]
+    if tuple(out.shape) != tuple(q.shape) or q.stride(3) != 1 or k_cache.stride(3) != 1 or out.stride(3) != 1:
+        raise ValueError("bad q / out / cache layout")
+    D_max = anc.shape[2] - 1
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    if workspace is None:
+        workspace = torch.zeros(tree_verify_attention_workspace(dt, B, M_max, Hq, Hkv, d, L_cap),
+                                dtype=torch.uint8, device=q.device)
+    _check(_lib.tmv_tree_verify_attention(dt, B, M_max, D_max, Hq, Hkv, d, _ptr(q), _strides(q, (0, 1, 2)),
+                                          _ptr(k_cache), _ptr(v_cache), _strides(k_cache, (0, 1, 2)), L_cap,
+                                          _ptr(prefix_len), _ptr(n_nodes), _ptr(anc), _ptr(depth), _ptr(status),
+                                          float(scale), _ptr(out), _strides(out, (0, 1, 2)), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(), _stream(stream)),
+           "tree_verify_attention")
+
+
+# ------------------------------------------------------------------------ stage 3
+def tree_accept_workspace(mode, B, M_max, V) -> int:
+    return int(_lib.tmv_tree_accept_workspace(mode, B, M_max, V))
+
+
+def tree_accept(mode, tokens, teacher, n_nodes, anc, depth, status, accept_len, path, next_token, draft_q=None,
+                seed=0, step=0, workspace=None, stream=None):
+    """teacher [B][M_max+1][V]: logits (GREEDY, f32/bf16) or p (SAMPLE, f32); draft_q the
+    same shape (SAMPLE).  Outputs accept_len [B], path [B][D_max], next_token [B]."""
+    _i32(tokens, n_nodes, anc, depth, status, accept_len, path, next_token)
+    B, R, V = teacher.shape
+    D_max = anc.shape[2] - 1
+    if teacher.stride(2) != 1:
+        raise ValueError("teacher rows must be contiguous")
+    if mode == ACCEPT_SAMPLE:
+        if draft_q is None or draft_q.dtype != torch.float32 or draft_q.shape != teacher.shape or draft_q.stride(2) != 1:
+            raise ValueError("sampling needs a float32 draft_q shaped like teacher")
+        qs = (draft_q.stride(0), draft_q.stride(1))
+    else:
+        qs = (0, 0)
+    if workspace is None:
+        workspace = torch.zeros(tree_accept_workspace(mode, B, R - 1, V), dtype=torch.uint8, device=teacher.device)
+    _check(_lib.tmv_tree_accept(mode, B, R - 1, D_max, V, _ptr(tokens), _dtype_code(teacher), _ptr(teacher),
+                                teacher.stride(0), teacher.stride(1), _ptr(draft_q), qs[0], qs[1],
+                                ctypes.c_uint64(seed), ctypes.c_uint64(step), _ptr(n_nodes), _ptr(anc), _ptr(depth),
+                                _ptr(status), _ptr(accept_len), _ptr(path), _ptr(next_token), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream)),
+           "tree_accept")
+
+
+# ------------------------------------------------------------------------ stage 4
+def kv_commit_path(k_cache, v_cache, prefix_len, n_nodes, accept_len, path, status, new_len, M_max, stream=None):
+    """In place on k_cache / v_cache [n_layers][B][Hkv][L_cap][d]."""
+    _i32(prefix_len, n_nodes, accept_len, path, status, new_len)
+    if k_cache.dim() == 4:
+        k_cache, v_cache = k_cache.unsqueeze(0), v_cache.unsqueeze(0)
+    if k_cache.shape != v_cache.shape or k_cache.stride() != v_cache.stride() or k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache must match")
+    nl, B, Hkv, L_cap, d = k_cache.shape
+    if k_cache.stride(4) != 1:
+        raise ValueError("d must be contiguous")
+    _check(_lib.tmv_kv_commit_path(_dtype_code(k_cache), nl, B, Hkv, d, L_cap, int(M_max), path.shape[1],
+                                   _ptr(k_cache), _ptr(v_cache), _strides(k_cache, (0, 1, 2, 3)), _ptr(prefix_len),
+                                   _ptr(n_nodes), _ptr(accept_len), _ptr(path), _ptr(status), _ptr(new_len),
+                                   _stream(stream)),
+           "kv_commit_path")
+
+
+class Workspaces:
+    """Zero-filled workspaces cached by size and device (each call leaves them zeroed)."""
+
+    def __init__(self):
+        self._cache = {}
+
+    def get(self, nbytes, device):
+        key = (int(nbytes), str(device))
+        ws = self._cache.get(key)
+        if ws is None:
+            ws = torch.zeros(max(256, int(nbytes)), dtype=torch.uint8, device=device)
+            self._cache[key] = ws
+        return ws

@@ -1,0 +1,122 @@
+// commit.hip -- prefix-sharing path-index commit of the accepted K/V rows (gfx950).
+//
+// After acceptance the cache holds [prefix | tree rows in node-id order].  The accepted
+// path's rows are compacted right behind the prefix, in depth order, in place; the
+// prefix itself is never touched and rows that are already in place are not moved
+// (EAGLE-Pangu, Chinese technical summary section 2.1: commit by path index with a
+// prefix-sharing fast reorder that only moves the newly accepted segment).
+//
+// One workgroup per (layer, sequence) handles every KV head and both caches.  A source
+// row can be another row's destination (ids need not be topological), so each pass
+// first copies all moving source rows into LDS, waits at a barrier, then writes them to
+// their destinations -- no row is read after it has been overwritten.  Rows move as
+// 16-byte vectors.
+#include "tmv_device.hpp"
+
+namespace {
+
+constexpr int kCommitThreads = 256;
+constexpr int kCommitLds = 64 * 1024;     // >= D_max * row bytes (host-checked)
+
+__global__ void __launch_bounds__(kCommitThreads)
+commit_kernel(int n_layers, int B, int Hkv, int row_bytes, int L_cap, int D_max,
+              uint8_t *__restrict__ kc, uint8_t *__restrict__ vc,
+              int64_t s_layer, int64_t s_b, int64_t s_h, int64_t s_t,      // bytes
+              const int32_t *__restrict__ prefix_len, const int32_t *__restrict__ n_nodes,
+              const int32_t *__restrict__ accept_len, const int32_t *__restrict__ path,
+              int32_t *__restrict__ status, int32_t *__restrict__ new_len)
+{
+    __shared__ uint4 snap[kCommitLds / 16];
+    __shared__ int src_row[128];
+    __shared__ int nmove, fits;
+
+    const int layer = blockIdx.x / B, b = blockIdx.x % B;
+    const int tid = threadIdx.x;
+    const int P = prefix_len[b], M = n_nodes[b], A = accept_len[b];
+    const int st = status[b];
+    const int32_t *pth = path + static_cast<int64_t>(b) * D_max;
+
+    if (tid == 0) {
+        int ok = st == TMV_OK && P >= 0 && static_cast<int64_t>(P) + M <= L_cap && A >= 0 && A <= D_max && A <= M;
+        for (int j = 0; ok && j < A; ++j) {
+            const int node = pth[j];
+            if (node < 1 || node > M) ok = 0;
+        }
+        fits = ok;
+        // rows that actually move: destination P + j, source P + path[j] - 1
+        int k = 0;
+        if (ok)
+            for (int j = 0; j < A; ++j)
+                if (pth[j] - 1 != j) src_row[k++] = j;
+        nmove = k;
+        if (layer == 0) {
+            new_len[b] = ok ? P + A : P;
+            if (!ok && st == TMV_OK) status[b] = TMV_ERR_INPUT;
+        }
+    }
+    __syncthreads();
+    if (!fits || nmove == 0) return;
+
+    const int n = nmove;
+    const int segs = row_bytes / 16;
+    const int units = 2 * Hkv;                               // (head, K|V)
+    const int per_pass = max(1, (kCommitLds / 16) / (n * segs));
+    for (int u0 = 0; u0 < units; u0 += per_pass) {
+        const int u1 = min(units, u0 + per_pass);
+        const int work = (u1 - u0) * n * segs;
+        for (int e = tid; e < work; e += kCommitThreads) {
+            const int uu = e / (n * segs), rem = e % (n * segs);
+            const int r = rem / segs, sg = rem % segs;
+            const int unit = u0 + uu, h = unit >> 1;
+            const uint8_t *base = ((unit & 1) ? vc : kc) + layer * s_layer + b * s_b + h * s_h;
+            const int j = src_row[r];
+            const int64_t src = static_cast<int64_t>(P) + pth[j] - 1;
+            snap[e] = *reinterpret_cast<const uint4 *>(base + src * s_t + sg * 16);
+        }
+        __syncthreads();
+        for (int e = tid; e < work; e += kCommitThreads) {
+            const int uu = e / (n * segs), rem = e % (n * segs);
+            const int r = rem / segs, sg = rem % segs;
+            const int unit = u0 + uu, h = unit >> 1;
+            uint8_t *base = ((unit & 1) ? vc : kc) + layer * s_layer + b * s_b + h * s_h;
+            const int64_t dst = static_cast<int64_t>(P) + src_row[r];
+            *reinterpret_cast<uint4 *>(base + dst * s_t + sg * 16) = snap[e];
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+extern "C" int tmv_kv_commit_path(int dtype, int n_layers, int B, int Hkv, int d, int L_cap,
+                                  int M_max, int D_max,
+                                  void *k_cache, void *v_cache, const int64_t *kv_stride,
+                                  const int32_t *prefix_len, const int32_t *n_nodes,
+                                  const int32_t *accept_len, const int32_t *path,
+                                  int32_t *status, int32_t *new_len, void *stream)
+{
+    if (dtype != TMV_F32 && dtype != TMV_BF16) return TMV_ERR_ARG;
+    const int es = dtype == TMV_F32 ? 4 : 2;
+    if (n_layers < 0 || B < 0 || Hkv <= 0 || d <= 0 || L_cap < 0) return TMV_ERR_ARG;
+    if (M_max < 0 || M_max > 128 || D_max < 0 || D_max > 128) return TMV_ERR_ARG;
+    const int row_bytes = d * es;
+    if (row_bytes % 16 != 0 || row_bytes > 512) return TMV_ERR_ARG;
+    if (!kv_stride) return TMV_ERR_ARG;
+    if (B == 0) return TMV_OK;
+    if (!prefix_len || !n_nodes || !accept_len || !status || !new_len || (D_max > 0 && !path)) return TMV_ERR_ARG;
+    if (n_layers > 0 && (!k_cache || !v_cache)) return TMV_ERR_ARG;
+    for (int i = 0; i < 4; ++i)
+        if (kv_stride[i] < 0 || (kv_stride[i] * es) % 16 != 0) return TMV_ERR_ARG;
+    if ((reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache)) & 15u) return TMV_ERR_ARG;
+    // new_len and the status checks are written by the layer-0 workgroups: with no
+    // layers, one pass over the sequences still publishes them (and moves no rows)
+    const int layers = n_layers > 0 ? n_layers : 1;
+    const int64_t blocks = static_cast<int64_t>(layers) * B;
+    if (blocks > 0x7fffffff) return TMV_ERR_ARG;
+    hipLaunchKernelGGL(commit_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kCommitThreads), 0,
+                       static_cast<hipStream_t>(stream), layers, B, n_layers > 0 ? Hkv : 0, row_bytes, L_cap, D_max,
+                       static_cast<uint8_t *>(k_cache), static_cast<uint8_t *>(v_cache),
+                       kv_stride[0] * es, kv_stride[1] * es, kv_stride[2] * es, kv_stride[3] * es,
+                       prefix_len, n_nodes, accept_len, path, status, new_len);
+    return tmv_host::launch_status(hipGetLastError());
+}

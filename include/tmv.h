@@ -16,9 +16,8 @@
  *     tensor's data_ptr), except the small int64 stride arrays, which are HOST arrays read
  *     during the call.  The library keeps no global state and allocates nothing; scratch
  *     memory comes from a caller workspace whose size the *_workspace call returns.  A
- *     workspace must be zero-filled once before its first use; every call leaves it in
- *     that state again, so it can be reused by the next call on the same stream (calls that
- *     overlap in time must not share a workspace).
+ *     workspace needs no initialisation and holds nothing between calls; calls that may
+ *     run at the same time (different streams) must not share one.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are asynchronous; none
  *     synchronises the host.
  *   - The return value reports problems the host can see (TMV_ERR_ARG: bad sizes, null
@@ -125,8 +124,8 @@ int tmv_tree_build_ancestors(int B, int M_max, int D_max, int parent_format,
  *             in a failed sequence) are written as 0.
  *   GQA: query head h reads KV head h / (Hq/Hkv).  Requires Hq % Hkv == 0, d in {64,128},
  *        Hq/Hkv <= 16, 1 <= L_cap.
- *   workspace: tmv_tree_verify_attention_workspace() bytes (split-KV partials and
- *        combine counters), zero-filled before first use.
+ *   workspace: tmv_tree_verify_attention_workspace() bytes (split-KV partials), 16-byte
+ *        aligned.
  */
 size_t tmv_tree_verify_attention_workspace(int dtype, int B, int M_max, int Hq, int Hkv,
                                            int d, int L_cap);
@@ -176,7 +175,7 @@ int tmv_tree_verify_attention(int dtype, int B, int M_max, int D_max, int Hq, in
  *              GREEDY.
  *   accept_len out int32 [B]; path out int32 [B][D_max] (node ids root->leaf, then 0);
  *   next_token out int32 [B].  All 0 for a failed sequence.
- *   workspace: tmv_tree_accept_workspace() bytes, zero-filled before first use.
+ *   workspace: tmv_tree_accept_workspace() bytes, 16-byte aligned.
  */
 size_t tmv_tree_accept_workspace(int mode, int B, int M_max, int V);
 int tmv_tree_accept(int mode, int B, int M_max, int D_max, int V,

@@ -1,0 +1,48 @@
+"""Known-answer checks of the benchmark's roofline arithmetic against the worked H100
+example printed in the roofline section of the hierarchical speculative decoding blog,
+and of its algorithmic-work accounting against a direct count."""
+import os
+
+import numpy as np
+
+import bench
+import tmv_inputs as ti
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden():
+    vals = {}
+    for line in open(os.path.join(GOLD, "h100_roofline.txt")):
+        if line.strip() and line[0] != "#":
+            k, v, _ = line.split()
+            vals[k] = float(v)
+    return vals
+
+
+def test_h100_worked_example():
+    g = golden()
+    ridge = bench.ridge_point(g["peak_bf16"] * 1e12, g["hbm_bw"] * 1e12)
+    assert round(ridge, 1) == g["ridge"]
+    assert round(100 * 1.0 / ridge, 2) == g["decode_util"]          # 1 FLOP/B at B=1
+    t = bench.read_time_s(g["weights_70b"] * 1e9, g["hbm_bw"] * 1e12)
+    assert round(t * 1e3, 1) == g["read_time"]
+    assert round(1.0 / t, 1) == g["tokens_per_s"]
+
+
+def test_attention_work_matches_direct_count():
+    w = ti.workload(2, with_rows=False)
+    par = w.parents[0]
+    depths = []
+    for i in range(1, 61):
+        d, h = 0, i
+        while h:
+            h = par[h]
+            d += 1
+        depths.append(d)
+    nbytes, flops = bench.attention_work(depths, 2048, 32, 8, 128)
+    # K and V rows of 8 heads over prefix + 60 tree slots, plus Q and O (bf16)
+    assert nbytes == 2 * 8 * (2048 + 60) * 128 * 2 + 2 * 60 * 32 * 128 * 2
+    # QK^T and PV over visible keys only: each (node, head) sees 2048 + depth keys
+    assert flops == sum(4 * 128 * 32 * (2048 + d) for d in depths)
+    assert sum(depths) == 242

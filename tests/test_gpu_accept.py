@@ -1,0 +1,200 @@
+"""Device parity of tree_accept (greedy and sampling) against the oracle: accepted length,
+path, next token and status must be bit-identical."""
+import numpy as np
+import pytest
+import torch
+
+import tmv_inputs as ti
+from tests.harness import DeviceStep, dev_tensor, host_bits, oracle_tables
+from tests.test_oracle_build import random_labelled_tree
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(name):
+    print("\n[gpu case] %s" % name, flush=True)
+
+
+def _greedy_parity(ref, w, logits_dev=None, row_dtype=0, logits_host=None):
+    dev = DeviceStep(w)
+    dev.build()
+    if logits_dev is not None:
+        dev.logits = logits_dev
+    dev.accept()
+    torch.cuda.synchronize()
+    ra, rd, rs = oracle_tables(ref, w)
+    lh = w.logits if logits_host is None else logits_host
+    A, path, nxt, st = ref.accept_greedy(w.tokens, lh, w.n_nodes, ra, rd, rs, row_dtype=row_dtype)
+    got = [host_bits(t) for t in (dev.accept_len, dev.path, dev.next_token, dev.status)]
+    for g, e, name in zip(got, (A, path, nxt, st), ("accept_len", "path", "next_token", "status")):
+        assert np.array_equal(g, e), (name, g, e)
+    return A, st
+
+
+def small_greedy(seed, B, M_max, D_max, V, tie_levels=None, alpha=0.8):
+    rng = np.random.default_rng(seed)
+    n = rng.integers(0, M_max + 1, size=B).astype(np.int32)
+    parents = np.zeros((B, M_max + 1), np.int32)
+    for b in range(B):
+        parents[b, : n[b] + 1] = random_labelled_tree(rng, int(n[b]), D_max)
+    if tie_levels:
+        # integer logits: every row has many tied maxima; most children carry the first
+        # maximum of their parent's row (numpy argmax), so accepted paths go through ties
+        logits = rng.integers(0, tie_levels, size=(B, M_max + 1, V)).astype(np.float32)
+        tokens = rng.integers(0, V, size=(B, M_max + 1)).astype(np.int32)
+        for b in range(B):
+            for c in range(1, int(n[b]) + 1):
+                if rng.random() < 0.7:
+                    tokens[b, c] = int(np.argmax(logits[b, parents[b, c]]))
+    else:
+        logits = rng.standard_normal((B, M_max + 1, V)).astype(np.float32)
+        tokens = np.zeros((B, M_max + 1), np.int32)
+        for b in range(B):
+            ti.plant_greedy(rng, parents[b], int(n[b]), V, logits[b], tokens[b], alpha)
+    return ti.Workload("greedy-small", ti.F32, B, 0, 1, 64, M_max, D_max, 1, V, "greedy", parents, n,
+                       np.zeros(B, np.int32), tokens, logits=logits)
+
+
+@pytest.mark.parametrize("V,ties", [(5, 3), (37, None), (8192, None), (20000, 4), (128256, None)])
+def test_greedy_small_trees(ref, V, ties):
+    _case("greedy: random trees V=%d ties=%s" % (V, ties))
+    w = small_greedy(300 + V, 24 if V < 100000 else 6, 20, 8, V, ties)
+    A, st = _greedy_parity(ref, w)
+    assert np.all(st == 0) and np.any(A > 0)
+
+
+def test_greedy_bf16_rows_and_strided_rows(ref):
+    _case("greedy: bf16 logits; padded row stride")
+    w = small_greedy(310, 16, 12, 6, 1000)
+    lb = ti.bf16_bits(w.logits)
+    _greedy_parity(ref, w, logits_dev=dev_tensor(lb, bf16=True), row_dtype=1, logits_host=lb)
+    # rows 3 elements apart from the vocabulary size (unaligned row starts)
+    pad = np.zeros((w.B, w.M_max + 1, w.V + 3), np.float32)
+    pad[:, :, : w.V] = w.logits
+    view = dev_tensor(pad)[:, :, : w.V]
+    _greedy_parity(ref, w, logits_dev=view)
+
+
+def test_greedy_errors_and_degenerate(ref):
+    _case("greedy: NaN rows, bad tokens, failed sequences, empty trees")
+    w = small_greedy(311, 8, 10, 6, 300)
+    w.n_nodes[:] = 10
+    parents = np.zeros((8, 11), np.int32)
+    rng = np.random.default_rng(5)
+    for b in range(8):
+        parents[b] = ti.tree_random(rng, 10, 6)
+    w.parents = parents
+    w.logits[1, 0, 17] = np.nan                       # root row
+    w.logits[2, 4, 3] = np.nan                        # a live node's row
+    w.tokens[3, 2] = 300                              # token == V
+    w.tokens[4, 7] = -1
+    w.parents[5, 3] = 3                               # cycle -> failed sequence upstream
+    w.n_nodes[6] = 0                                  # empty tree
+    A, st = _greedy_parity(ref, w)
+    assert st[1] == ref.ERR_INPUT and st[2] == ref.ERR_INPUT and st[3] == ref.ERR_INPUT
+    assert st[4] == ref.ERR_INPUT and st[5] == ref.ERR_CYCLE and st[6] == 0 and A[6] == 0
+    # M_max = 0: only the root row
+    w0 = ti.Workload("m0", ti.F32, 2, 0, 1, 64, 0, 0, 1, 7, "greedy", np.zeros((2, 1), np.int32),
+                     np.zeros(2, np.int32), np.zeros(2, np.int32), np.zeros((2, 1), np.int32),
+                     logits=np.array([[[0, 1, 5, 5, 2, 0, 0]], [[9, 1, 5, 5, 2, 0, 9]]], np.float32))
+    _greedy_parity(ref, w0)
+
+
+@pytest.mark.parametrize("c", [1, 2, 4])
+def test_greedy_workloads(ref, c):
+    _case("greedy: workload %d" % c)
+    A, st = _greedy_parity(ref, ti.workload(c))
+    assert np.all(st == 0)
+    print("    accept lengths", A.tolist(), flush=True)
+
+
+def test_greedy_determinism_and_workspace_reuse():
+    _case("greedy: repeated calls on one workspace")
+    import tree_masked_verification_amd as tmv
+    w = ti.workload(2)
+    dev = DeviceStep(w)
+    dev.build()
+    ws = torch.zeros(tmv.tree_accept_workspace(tmv.ACCEPT_GREEDY, 1, w.M_max, w.V), dtype=torch.uint8, device="cuda")
+    dev.accept(workspace=ws)
+    first = [host_bits(t).copy() for t in (dev.accept_len, dev.path, dev.next_token)]
+    for _ in range(5):
+        dev.accept(workspace=ws)
+        assert all(np.array_equal(host_bits(t), f) for t, f in zip((dev.accept_len, dev.path, dev.next_token), first))
+
+
+# ------------------------------------------------------------------ sampling
+def _sample_parity(ref, parents, n, tokens, p, q, seed, step, D_max, status_override=None):
+    B, R, V = p.shape
+    w = ti.Workload("sample", ti.F32, B, 0, 1, 64, R - 1, D_max, 1, V, "sample", parents, n,
+                    np.zeros(B, np.int32), tokens, p=p, qd=q, seed=seed, step=step)
+    dev = DeviceStep(w)
+    dev.build()
+    if status_override is not None:
+        dev.status.copy_(torch.from_numpy(status_override).cuda())
+    dev.accept()
+    torch.cuda.synchronize()
+    ra, rd, rs = oracle_tables(ref, w)
+    if status_override is not None:
+        rs = status_override.copy()
+    A, path, nxt, st = ref.accept_sample(tokens, p, q, seed, step, n, ra, rd, rs)
+    got = [host_bits(t) for t in (dev.accept_len, dev.path, dev.next_token, dev.status)]
+    for g, e, name in zip(got, (A, path, nxt, st), ("accept_len", "path", "next_token", "status")):
+        assert np.array_equal(g, e), (name, g, e)
+    return A, st
+
+
+@pytest.mark.parametrize("V,overlap", [(6, 0.9), (50, 0.95), (1000, 0.9), (5000, None), (128256, 0.97)])
+def test_sampling_small(ref, V, overlap):
+    _case("sampling: V=%d overlap=%s" % (V, overlap))
+    rng = np.random.default_rng(400 + V)
+    B = 64 if V <= 1000 else 8
+    parents, n, tokens, p, q = ti.small_sampling_case(rng, B, 12, V, 5, overlap=overlap)
+    for step in (0, 1):
+        A, st = _sample_parity(ref, parents, n, tokens, p, q, 77, step, 5)
+        assert np.all(st == 0)
+    if V <= 1000:
+        assert np.any(A >= 2)
+
+
+def test_sampling_unnormalised_and_edge_rows(ref):
+    """Rows that do not sum to 1 (the integer rule renormalises), rows with zeros,
+    a p row equal to q (empty residual), exact 0/1 probabilities."""
+    _case("sampling: unnormalised and degenerate rows")
+    rng = np.random.default_rng(410)
+    V = 40
+    parents, n, tokens, p, q = ti.small_sampling_case(rng, 48, 9, V, 4, overlap=0.8)
+    p = p.copy()
+    q = q.copy()
+    p[0:8] *= 0.37                                   # unnormalised
+    q[8:16, :, ::2] = 0.0                            # zeros in the draft rows
+    p[16:24] = q[16:24]                              # p == q: residual may vanish
+    p[24:32] = 0.0
+    p[24:32, :, 5] = 1.0                             # one-hot teacher
+    p[32:40] = np.minimum(1.0, p[32:40] * 40.0)      # rows summing to far above 1
+    A, st = _sample_parity(ref, parents, n, tokens, p, q, 3, 0, 4)
+    assert np.all(st == 0)
+
+
+def test_sampling_errors(ref):
+    _case("sampling: malformed rows and failed sequences")
+    rng = np.random.default_rng(411)
+    V = 64
+    parents, n, tokens, p, q = ti.small_sampling_case(rng, 8, 6, V, 3, overlap=0.9)
+    p = p.copy(); q = q.copy(); tokens = tokens.copy()
+    p[0, 0, 1] = -0.01
+    p[1, 0, 2] = np.nan
+    q[2, 0] = 0.0
+    tokens[3, 1] = V
+    p[4, 0, 0] = 1.5
+    st_in = np.zeros(8, np.int32)
+    st_in[5] = 3
+    A, st = _sample_parity(ref, parents, n, tokens, p, q, 9, 0, 3, status_override=st_in)
+    assert st[:6].tolist() == [ref.ERR_INPUT] * 5 + [3] and st[6] == 0 and st[7] == 0
+
+
+def test_sampling_workload5(ref):
+    _case("sampling: workload 5 (B32, V128256)")
+    w = ti.workload(5)
+    A, st = _sample_parity(ref, w.parents, w.n_nodes, w.tokens, w.p, w.qd, w.seed, w.step, w.D_max)
+    assert np.all(st == 0)
+    print("    accept lengths", A.tolist(), flush=True)

@@ -176,3 +176,25 @@ def test_attention_determinism():
         dev.out.fill_(float("nan"))
         dev.attention()
         assert np.array_equal(host_bits(dev.out), first)
+
+
+def test_workspace_contents_do_not_matter():
+    _case("attention + greedy: workspaces full of garbage")
+    import tree_masked_verification_amd as tmv
+    w = ti.workload(2)
+    dev = DeviceStep(w)
+    dev.build()
+    dev.attention()
+    dev.accept()
+    ref_out = host_bits(dev.out).copy()
+    ref_acc = [host_bits(t).copy() for t in (dev.accept_len, dev.path, dev.next_token)]
+    n_attn = tmv.tree_verify_attention_workspace(tmv.BF16, w.B, w.M_max, w.Hq, w.Hkv, w.d, w.L_cap)
+    n_acc = tmv.tree_accept_workspace(tmv.ACCEPT_GREEDY, w.B, w.M_max, w.V)
+    for fill in (0xFF, 0x7F, 0x00):
+        wa = torch.full((n_attn,), fill, dtype=torch.uint8, device="cuda")
+        wc = torch.full((n_acc,), fill, dtype=torch.uint8, device="cuda")
+        dev.out.fill_(float("nan"))
+        dev.attention(workspace=wa)
+        dev.accept(workspace=wc)
+        assert np.array_equal(host_bits(dev.out), ref_out)
+        assert all(np.array_equal(host_bits(t), r) for t, r in zip((dev.accept_len, dev.path, dev.next_token), ref_acc))

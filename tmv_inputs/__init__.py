@@ -35,11 +35,11 @@ F32, BF16 = 0, 1
 def bf16_bits(x) -> np.ndarray:
     """fp32 -> bf16 bit pattern (uint16), round to nearest even; NaN stays NaN."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    nan = np.isnan(x)
+    u = x.view(np.uint32)
+    # finite values cannot overflow 32 bits here (largest is 0xFF7FFFFF + 0x8000)
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     out = rounded.astype(np.uint16)
-    out[nan] = 0x7FC0
+    out[np.isnan(x)] = 0x7FC0
     return out
 
 

@@ -198,7 +198,7 @@ def kv_commit_path(k_cache, v_cache, prefix_len, n_nodes, accept_len, path, stat
 
 
 class Workspaces:
-    """Zero-filled workspaces cached by size and device (each call leaves them zeroed)."""
+    """Workspaces cached by size and device (their contents never matter between calls)."""
 
     def __init__(self):
         self._cache = {}

@@ -5,8 +5,9 @@
 //   the longest valid branch is kept).  The row scans are the HBM-bound part: one
 //   workgroup per (sequence, row, vocabulary chunk) reads its chunk with 16-byte loads
 //   and reduces a 64-bit key (order-preserving value bits << 32 | ~index), so max() gives
-//   the largest value and, on ties, the smallest index.  The last workgroup of a
-//   sequence (atomic ticket) merges the chunk keys and picks the path.
+//   the largest value and, on ties, the smallest index.  A second kernel (one
+//   workgroup per sequence, ordered after the scan on the stream) merges the chunk keys
+//   and picks the path -- no cross-workgroup synchronisation inside a kernel.
 // SAMPLE: modified rejection sampling (same page, its rejection-sampling section and
 //   FAQ), children of the current node tried in ascending id against the running
 //   residual.  Exact integer fixed point, so the result is bit-identical to any correct
@@ -37,101 +38,113 @@ __device__ __forceinline__ void scan_one(float v, int idx, uint64_t &best, bool 
 
 template <int DT>
 __global__ void __launch_bounds__(kScanThreads)
-greedy_scan_kernel(int M_max, int D_max, int V, int nchunk,
-                   const int32_t *__restrict__ tokens, const void *__restrict__ teacher,
-                   int64_t sb, int64_t sr,
-                   const int32_t *__restrict__ n_nodes, const int32_t *__restrict__ anc,
-                   const int32_t *__restrict__ depth, int32_t *__restrict__ status,
-                   int32_t *__restrict__ accept_len, int32_t *__restrict__ path,
-                   int32_t *__restrict__ next_token,
-                   uint64_t *__restrict__ keys, uint32_t *__restrict__ tickets)
+greedy_scan_kernel(int M_max, int V, int nchunk, const void *__restrict__ teacher, int64_t sb, int64_t sr,
+                   const int32_t *__restrict__ n_nodes, const int32_t *__restrict__ depth,
+                   const int32_t *__restrict__ status, uint64_t *__restrict__ keys)
 {
     __shared__ uint64_t red[kScanThreads / kWave];
-    __shared__ int last;
-    const int R = M_max + 1, W = D_max + 1;
+    const int R = M_max + 1;
     const int chunk = blockIdx.x % nchunk;
     const int u = (blockIdx.x / nchunk) % R;
     const int b = blockIdx.x / (nchunk * R);
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+    // the three words that decide whether this row is scanned are fetched together
     const int M = n_nodes[b];
-    // a node count outside [0, M_max] cannot come with an OK status from the build stage;
-    // it is rejected here so that no row beyond the tables is ever addressed
-    const int st = (status[b] == TMV_OK && (M < 0 || M > M_max)) ? TMV_ERR_INPUT : status[b];
-    const bool live = st == TMV_OK && u <= M && (u == 0 || depth[static_cast<int64_t>(b) * R + u] >= 1);
+    const int st = status[b];
+    const int dp = u > 0 ? depth[static_cast<int64_t>(b) * R + u] : 1;
+    if (st != TMV_OK || M < 0 || M > M_max || u > M || dp < 1) return;
 
-    if (live) {
-        const int x0 = chunk * kScanChunk;
-        const int x1 = min(V, x0 + kScanChunk);
-        uint64_t best = 0;
-        bool nan = false;
-        if constexpr (DT == TMV_F32) {
-            const float *row = static_cast<const float *>(teacher) + b * sb + static_cast<int64_t>(u) * sr;
-            // 16-byte loads when the row segment is aligned, scalar otherwise
-            const bool vec = ((reinterpret_cast<uintptr_t>(row + x0) & 15u) == 0);
-            if (vec) {
-                const int n4 = (x1 - x0) / 4;
-                const float4 *r4 = reinterpret_cast<const float4 *>(row + x0);
-                for (int i = tid; i < n4; i += kScanThreads) {
-                    const float4 f = r4[i];
-                    const int x = x0 + 4 * i;
-                    scan_one(f.x, x, best, nan);
-                    scan_one(f.y, x + 1, best, nan);
-                    scan_one(f.z, x + 2, best, nan);
-                    scan_one(f.w, x + 3, best, nan);
-                }
-                for (int x = x0 + 4 * n4 + tid; x < x1; x += kScanThreads) scan_one(row[x], x, best, nan);
-            } else {
-                for (int x = x0 + tid; x < x1; x += kScanThreads) scan_one(row[x], x, best, nan);
+    const int x0 = chunk * kScanChunk;
+    const int x1 = min(V, x0 + kScanChunk);
+    uint64_t best = 0;
+    bool nan = false;
+    if constexpr (DT == TMV_F32) {
+        const float *row = static_cast<const float *>(teacher) + b * sb + static_cast<int64_t>(u) * sr;
+        constexpr int kPer = kScanChunk / (4 * kScanThreads);        // float4 per thread
+        if (x1 - x0 == kScanChunk && ((reinterpret_cast<uintptr_t>(row + x0) & 15u) == 0)) {
+            // full aligned chunk: issue every 16-byte load before consuming any
+            const float4 *r4 = reinterpret_cast<const float4 *>(row + x0);
+            float4 f[kPer];
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) f[i] = r4[tid + i * kScanThreads];
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int x = x0 + 4 * (tid + i * kScanThreads);
+                scan_one(f[i].x, x, best, nan);
+                scan_one(f[i].y, x + 1, best, nan);
+                scan_one(f[i].z, x + 2, best, nan);
+                scan_one(f[i].w, x + 3, best, nan);
             }
         } else {
-            const uint16_t *row = static_cast<const uint16_t *>(teacher) + b * sb + static_cast<int64_t>(u) * sr;
-            for (int x = x0 + tid; x < x1; x += kScanThreads) scan_one(tmv::bf16_to_f32(row[x]), x, best, nan);
+            for (int x = x0 + tid; x < x1; x += kScanThreads) scan_one(row[x], x, best, nan);
         }
-        if (nan) best = kNanKey;
-        best = tmv::wave_max_u64(best);
-        if (lane == 0) red[wv] = best;
-        __syncthreads();
-        if (tid == 0) {
-            uint64_t k = red[0];
-            for (int w = 1; w < kScanThreads / kWave; ++w) k = red[w] > k ? red[w] : k;
-            keys[(static_cast<int64_t>(b) * R + u) * nchunk + chunk] = k;
-        }
+    } else {
+        const uint16_t *row = static_cast<const uint16_t *>(teacher) + b * sb + static_cast<int64_t>(u) * sr;
+        for (int x = x0 + tid; x < x1; x += kScanThreads) scan_one(tmv::bf16_to_f32(row[x]), x, best, nan);
     }
-
-    // ticket: the last workgroup of the sequence selects the path
-    __threadfence();
+    if (nan) best = kNanKey;
+    best = tmv::wave_max_u64(best);
+    if (lane == 0) red[wv] = best;
     __syncthreads();
     if (tid == 0) {
-        const uint32_t prev = atomicAdd(&tickets[b], 1u);
-        last = prev == static_cast<uint32_t>(R * nchunk - 1);
-        if (last) atomicExch(&tickets[b], 0u);
+        uint64_t k = red[0];
+        for (int w = 1; w < kScanThreads / kWave; ++w) k = red[w] > k ? red[w] : k;
+        keys[(static_cast<int64_t>(b) * R + u) * nchunk + chunk] = k;
     }
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
+}
 
-    __shared__ int32_t tsel[129];
+// One workgroup per sequence, after the scan: merge the chunk keys of every live row into
+// t(u), check the draft tokens, mark matching nodes and pick the deepest (smallest id).
+__global__ void __launch_bounds__(kScanThreads)
+greedy_select_kernel(int M_max, int D_max, int V, int nchunk, const int32_t *__restrict__ tokens,
+                     const int32_t *__restrict__ n_nodes, const int32_t *__restrict__ anc,
+                     const int32_t *__restrict__ depth, int32_t *__restrict__ status,
+                     int32_t *__restrict__ accept_len, int32_t *__restrict__ path,
+                     int32_t *__restrict__ next_token, const uint64_t *__restrict__ keys)
+{
+    constexpr int kKeyBatch = 16;                  // chunk keys per row fetched at once
+    constexpr int kAncBatch = 8;                   // ancestor entries per node fetched at once
+    __shared__ int32_t tsel[129], tok_sh[129];
     __shared__ int bad;
     __shared__ uint64_t best_node[kScanThreads / kWave];
+    const int R = M_max + 1, W = D_max + 1;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+
+    // one round trip: sequence scalars, this thread's row of keys, token, depth and
+    // first ancestor entries (indices clamped into the tables)
+    const int M = n_nodes[b];
+    const int st_in = status[b];
+    const int row = tid < R ? tid : R - 1;
+    const int64_t rb = static_cast<int64_t>(b) * R + row;
+    uint64_t kb[kKeyBatch];
+#pragma unroll
+    for (int c = 0; c < kKeyBatch; ++c) kb[c] = c < nchunk ? keys[rb * nchunk + c] : 0;
+    const int tok = tokens[rb];
+    const int dep = row > 0 ? depth[rb] : 0;
+    int a8[kAncBatch];
+    const int32_t *arow = anc + rb * W;
+#pragma unroll
+    for (int k = 0; k < kAncBatch; ++k) a8[k] = arow[k < W ? k : W - 1];
+
+    // a node count outside [0, M_max] cannot come with an OK status from the build stage;
+    // it is rejected here so that no row beyond the tables is ever addressed
+    const int st = (st_in == TMV_OK && (M < 0 || M > M_max)) ? TMV_ERR_INPUT : st_in;
     int32_t *pth = path + static_cast<int64_t>(b) * D_max;
     if (tid == 0) bad = st != TMV_OK;
+    if (tid < R) tok_sh[tid] = tok;
     __syncthreads();
-    const int st_in = status[b];
-    if (st == TMV_OK && tid < R && tid <= M) {
-        const bool row_live = tid == 0 || depth[static_cast<int64_t>(b) * R + tid] >= 1;
-        if (row_live) {
-            uint64_t k = 0;
-            for (int c = 0; c < nchunk; ++c) {
-                const uint64_t kc = keys[(static_cast<int64_t>(b) * R + tid) * nchunk + c];
-                k = kc > k ? kc : k;
-            }
-            if (k == kNanKey) bad = 1;
-            tsel[tid] = static_cast<int32_t>(0xffffffffu - static_cast<uint32_t>(k & 0xffffffffu));
-            if (tid > 0) {
-                const int tok = tokens[static_cast<int64_t>(b) * R + tid];
-                if (tok < 0 || tok >= V) bad = 1;
-            }
+    const bool row_live = st == TMV_OK && tid < R && tid <= M && (tid == 0 || dep >= 1);
+    if (row_live) {
+        uint64_t k = 0;
+#pragma unroll
+        for (int c = 0; c < kKeyBatch; ++c) k = kb[c] > k ? kb[c] : k;
+        for (int c = kKeyBatch; c < nchunk; ++c) {
+            const uint64_t kc = keys[rb * nchunk + c];
+            k = kc > k ? kc : k;
         }
+        if (k == kNanKey) bad = 1;
+        tsel[tid] = static_cast<int32_t>(0xffffffffu - static_cast<uint32_t>(k & 0xffffffffu));
+        if (tid > 0 && (tok < 0 || tok >= V)) bad = 1;
     }
     __syncthreads();
     if (bad) {
@@ -146,15 +159,18 @@ greedy_scan_kernel(int M_max, int D_max, int V, int nchunk,
     // node i matches iff every node c on its path has token == t(parent(c)); the chosen
     // node maximises (depth, -id): key = depth << 8 | (255 - id)
     uint64_t key = 0;
-    if (tid >= 1 && tid <= M) {
-        const int dep = depth[static_cast<int64_t>(b) * R + tid];
-        if (dep >= 1) {
-            const int32_t *arow = anc + (static_cast<int64_t>(b) * R + tid) * W;
-            bool ok = true;
-            for (int k = 0; k < dep && ok; ++k)
-                ok = tokens[static_cast<int64_t>(b) * R + arow[k]] == tsel[arow[k + 1]];
-            if (ok) key = (static_cast<uint64_t>(dep) << 8) | static_cast<uint64_t>(255 - tid);
+    if (tid >= 1 && tid <= M && dep >= 1) {
+        bool ok = true;
+#pragma unroll
+        for (int k = 0; k < kAncBatch; ++k) {
+            if (k < dep) {
+                const int parent = k + 1 < kAncBatch ? a8[k + 1] : arow[k + 1];
+                ok = ok && tok_sh[a8[k]] == tsel[k + 1 < dep ? parent : 0];
+            }
         }
+        for (int k = kAncBatch; k < dep && ok; ++k)
+            ok = tok_sh[arow[k]] == tsel[arow[k + 1]];
+        if (ok) key = (static_cast<uint64_t>(dep) << 8) | static_cast<uint64_t>(255 - tid);
     }
     key = tmv::wave_max_u64(key);
     if (lane == 0) best_node[wv] = key;
@@ -163,15 +179,15 @@ greedy_scan_kernel(int M_max, int D_max, int V, int nchunk,
         uint64_t k = best_node[0];
         for (int w = 1; w < kScanThreads / kWave; ++w) k = best_node[w] > k ? best_node[w] : k;
         const int star = k ? 255 - static_cast<int>(k & 255u) : 0;
-        const int dep = static_cast<int>(k >> 8);
-        best_node[0] = (static_cast<uint64_t>(dep) << 32) | static_cast<uint32_t>(star);
-        accept_len[b] = dep;
+        const int dstar = static_cast<int>(k >> 8);
+        best_node[0] = (static_cast<uint64_t>(dstar) << 32) | static_cast<uint32_t>(star);
+        accept_len[b] = dstar;
         next_token[b] = tsel[star];
     }
     __syncthreads();
-    const int dep = static_cast<int>(best_node[0] >> 32), star = static_cast<int>(best_node[0] & 0xffffffffu);
+    const int dstar = static_cast<int>(best_node[0] >> 32), star = static_cast<int>(best_node[0] & 0xffffffffu);
     for (int j = tid; j < D_max; j += kScanThreads)
-        pth[j] = j < dep ? anc[(static_cast<int64_t>(b) * R + star) * W + (dep - 1 - j)] : 0;
+        pth[j] = j < dstar ? anc[(static_cast<int64_t>(b) * R + star) * W + (dstar - 1 - j)] : 0;
 }
 
 // ============================================================== sampling
@@ -410,9 +426,7 @@ extern "C" size_t tmv_tree_accept_workspace(int mode, int B, int M_max, int V)
     if (B <= 0 || M_max < 0 || V <= 0) return 256;
     if (mode == TMV_ACCEPT_GREEDY) {
         const int nchunk = (V + kScanChunk - 1) / kScanChunk;
-        size_t t = static_cast<size_t>(B) * sizeof(uint32_t);
-        t = (t + 255) / 256 * 256;
-        return t + static_cast<size_t>(B) * (M_max + 1) * nchunk * sizeof(uint64_t);
+        return static_cast<size_t>(B) * (M_max + 1) * nchunk * sizeof(uint64_t) + 256;
     }
     return static_cast<size_t>(B) * V * sizeof(uint64_t) + 256;
 }
@@ -443,18 +457,15 @@ extern "C" int tmv_tree_accept(int mode, int B, int M_max, int D_max, int V,
         const int nchunk = (V + kScanChunk - 1) / kScanChunk;
         const int64_t blocks = static_cast<int64_t>(B) * (M_max + 1) * nchunk;
         if (blocks > 0x7fffffff) return TMV_ERR_ARG;
-        size_t off = static_cast<size_t>(B) * sizeof(uint32_t);
-        off = (off + 255) / 256 * 256;
-        uint32_t *tickets = reinterpret_cast<uint32_t *>(ws);
-        uint64_t *keys = reinterpret_cast<uint64_t *>(ws + off);
+        uint64_t *keys = reinterpret_cast<uint64_t *>(ws);
         if (row_dtype == TMV_F32)
             hipLaunchKernelGGL(greedy_scan_kernel<TMV_F32>, dim3(static_cast<unsigned>(blocks)), dim3(kScanThreads), 0, s,
-                               M_max, D_max, V, nchunk, tokens, teacher, t_stride_b, t_stride_row, n_nodes, anc, depth,
-                               status, accept_len, path, next_token, keys, tickets);
+                               M_max, V, nchunk, teacher, t_stride_b, t_stride_row, n_nodes, depth, status, keys);
         else
             hipLaunchKernelGGL(greedy_scan_kernel<TMV_BF16>, dim3(static_cast<unsigned>(blocks)), dim3(kScanThreads), 0, s,
-                               M_max, D_max, V, nchunk, tokens, teacher, t_stride_b, t_stride_row, n_nodes, anc, depth,
-                               status, accept_len, path, next_token, keys, tickets);
+                               M_max, V, nchunk, teacher, t_stride_b, t_stride_row, n_nodes, depth, status, keys);
+        hipLaunchKernelGGL(greedy_select_kernel, dim3(B), dim3(kScanThreads), 0, s, M_max, D_max, V, nchunk, tokens,
+                           n_nodes, anc, depth, status, accept_len, path, next_token, keys);
         return tmv_host::launch_status(hipGetLastError());
     }
     if (row_dtype != TMV_F32 || !draft_q || q_stride_b < 0 || q_stride_row < 0) return TMV_ERR_ARG;

@@ -27,7 +27,7 @@ commit_kernel(int n_layers, int B, int Hkv, int row_bytes, int L_cap, int D_max,
               int32_t *__restrict__ status, int32_t *__restrict__ new_len)
 {
     __shared__ uint4 snap[kCommitLds / 16];
-    __shared__ int src_row[128];
+    __shared__ int src_row[128], path_sh[128];
     __shared__ int nmove, fits;
 
     const int layer = blockIdx.x / B, b = blockIdx.x % B;
@@ -35,11 +35,13 @@ commit_kernel(int n_layers, int B, int Hkv, int row_bytes, int L_cap, int D_max,
     const int P = prefix_len[b], M = n_nodes[b], A = accept_len[b];
     const int st = status[b];
     const int32_t *pth = path + static_cast<int64_t>(b) * D_max;
+    if (tid < D_max) path_sh[tid] = pth[tid];            // the whole path in one round trip
+    __syncthreads();
 
     if (tid == 0) {
         int ok = st == TMV_OK && P >= 0 && static_cast<int64_t>(P) + M <= L_cap && A >= 0 && A <= D_max && A <= M;
         for (int j = 0; ok && j < A; ++j) {
-            const int node = pth[j];
+            const int node = path_sh[j];
             if (node < 1 || node > M) ok = 0;
         }
         fits = ok;
@@ -47,7 +49,7 @@ commit_kernel(int n_layers, int B, int Hkv, int row_bytes, int L_cap, int D_max,
         int k = 0;
         if (ok)
             for (int j = 0; j < A; ++j)
-                if (pth[j] - 1 != j) src_row[k++] = j;
+                if (path_sh[j] - 1 != j) src_row[k++] = j;
         nmove = k;
         if (layer == 0) {
             new_len[b] = ok ? P + A : P;
@@ -70,7 +72,7 @@ commit_kernel(int n_layers, int B, int Hkv, int row_bytes, int L_cap, int D_max,
             const int unit = u0 + uu, h = unit >> 1;
             const uint8_t *base = ((unit & 1) ? vc : kc) + layer * s_layer + b * s_b + h * s_h;
             const int j = src_row[r];
-            const int64_t src = static_cast<int64_t>(P) + pth[j] - 1;
+            const int64_t src = static_cast<int64_t>(P) + path_sh[j] - 1;
             snap[e] = *reinterpret_cast<const uint4 *>(base + src * s_t + sg * 16);
         }
         __syncthreads();

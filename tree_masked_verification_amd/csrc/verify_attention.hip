@@ -23,11 +23,13 @@
 //   * a workgroup has 4 waves: either all on the same 32 rows splitting the chunks
 //     (WR = 1, combined in LDS) or on 4 different row tiles sharing the chunks through
 //     the cache (WR = 4).  Token ranges are further split across workgroups (split-KV);
-//     the last workgroup of a split group, found with an atomic ticket, merges the
-//     partials in a fixed order (deterministic) -- one launch per call.
+//     a small second kernel merges the split partials in a fixed order (deterministic).
+//     No workgroup ever waits on another inside a kernel: on this GPU an agent-scope
+//     fence writes back and invalidates the whole XCD L2, which costs far more than the
+//     work it would protect.
 //   * workgroup ids are laid out so that every workgroup of one (sequence, KV head)
-//     lands on the same XCD: the head's K/V goes from HBM into that XCD's L2 once and
-//     its partials stay in the same L2.
+//     lands on the same XCD: the head's K/V goes from HBM into that XCD's L2 once and is
+//     re-read by the head's other row blocks from there.
 // fp32 kernel: one wave per (node, query head), plain FMA; used for fp32 caches.
 #include <cstdlib>
 #include <cstdio>
@@ -41,6 +43,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kOverflow = 32.0f;  // largest score excess over a row's reference, base 2
+constexpr int kBufferFlags = 0x00020000;   // raw buffer descriptor word 3 (gfx9 family)
 constexpr int kChunk = 32;          // tokens per chunk (two 16-token MFMA tiles)
 constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;    // two 16-row tiles
@@ -81,19 +85,14 @@ AttnPlan make_plan(int B, int M_max, int Hq, int Hkv, int L_cap) {
     return p;
 }
 
-// workspace layout: [counters: pairs*nb u32, padded to 256 B][stats: pairs*nb*S*rb*2 f32]
-//                   [partial O: pairs*nb*S*rb*d f32]
-size_t plan_bytes(const AttnPlan &p, int d, size_t *off_stats, size_t *off_o) {
-    size_t cnt = static_cast<size_t>(p.pairs) * p.nb * sizeof(uint32_t);
-    cnt = (cnt + 255) / 256 * 256;
-    if (cnt == 0) cnt = 256;
+// workspace layout (split-KV only): [stats: pairs*nb*S*rb*2 f32][partial O: pairs*nb*S*rb*d f32]
+size_t plan_bytes(const AttnPlan &p, int d, size_t *off_o) {
     const size_t units = static_cast<size_t>(p.pairs) * p.nb * p.splits * p.rb;
     size_t st = p.splits > 1 ? units * 2 * sizeof(float) : 0;
     st = (st + 255) / 256 * 256;
     const size_t o = p.splits > 1 ? units * d * sizeof(float) : 0;
-    if (off_stats) *off_stats = cnt;
-    if (off_o) *off_o = cnt + st;
-    return cnt + st + o;
+    if (off_o) *off_o = st;
+    return st + o < 256 ? 256 : st + o;
 }
 
 __device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t *p) {
@@ -114,8 +113,7 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
                       const int32_t *__restrict__ anc, const int32_t *__restrict__ depth,
                       int32_t *__restrict__ status, float qk_scale_log2,
                       uint16_t *__restrict__ out, int64_t os0, int64_t os1, int64_t os2,
-                      uint32_t *__restrict__ counters, float *__restrict__ ws_stats,
-                      float *__restrict__ ws_o,
+                      float *__restrict__ ws_stats, float *__restrict__ ws_o,
                       int pairs, int nb, int splits, int per_pair)
 {
     constexpr int KS = D / 32;           // k-steps of the QK^T contraction
@@ -135,14 +133,36 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
     const int g = Hq / Hkv;
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);     // wave-uniform
     const int wr = wave / WT, wt = wave % WT;
     const int c16 = lane & 15, G = lane >> 4;
+    auto row0_of = [&](int rb_, int wr_) { return rb_ * RB + wr_ * kRowsPerWave; };
 
+    const int R = 1 + M_max, W = D_max + 1;
+    constexpr int kAncBatch = 8;                           // ancestor entries fetched up front
+
+    // ---- one round trip for everything the prologue needs: the sequence's scalars and,
+    // independently of them, this lane's query fragments, node depths and first ancestor
+    // entries (row indices are clamped into the tables, so no load waits on another)
     const int M = n_nodes[b];
     const int P = prefix_len[b];
-    const int R = 1 + M_max, W = D_max + 1;
     int st = status[b];
+    bf16x8_t qf[2][KS];
+    int dep[2], anc8[2][kAncBatch];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        int r = row0_of(rbk, wr) + rt * 16 + c16;
+        if (r > M_max * g - 1) r = M_max * g - 1;
+        const int j = r / g + 1, gi = r % g;
+        const uint16_t *qp = q + b * qs0 + static_cast<int64_t>(j - 1) * qs1 + static_cast<int64_t>(kvh * g + gi) * qs2 + G * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = load_bf16x8(qp + ks * 32);
+        dep[rt] = depth[static_cast<int64_t>(b) * R + j];
+        const int32_t *arow = anc + (static_cast<int64_t>(b) * R + j) * W;
+#pragma unroll
+        for (int k = 0; k < kAncBatch; ++k) anc8[rt][k] = arow[k < W ? k : W - 1];
+    }
+
     if (st == TMV_OK && (M < 0 || M > M_max || P < 0 || static_cast<int64_t>(P) + M > L_cap)) {
         st = TMV_ERR_INPUT;
         if (threadIdx.x == 0 && rbk == 0 && split == 0) status[b] = TMV_ERR_INPUT;
@@ -165,29 +185,44 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
     };
 
     if (row0_wg >= Rh) {
-        // no live row in this workgroup: the first split clears the block's output rows
-        if (split == 0 && wt == 0) write_zero_rows(row0);
+        // no live row in this workgroup: clear the block's output rows (with split-KV the
+        // merge kernel writes every row instead)
+        if (splits == 1 && wt == 0) write_zero_rows(row0);
         return;
     }
     const bool wave_live = row0 < Rh;
 
-    // ---- per-lane query fragments and ancestor masks for its two rows
-    bf16x8_t qf[2][KS];
+    // query fragments live in LDS (one copy per row group) rather than in 2*KS*4 VGPRs;
+    // each chunk reads them back with 16-byte LDS loads in lane order (conflict-free)
+    __shared__ uint4 q_lds[WR][2][KS][kWave];
+    if (wt == 0) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) q_lds[wr][rt][ks][lane] = __builtin_bit_cast(uint4, qf[rt][ks]);
+    }
+    __syncthreads();
+
+    // ---- ancestor-or-self masks of the lane's two rows (bit a <-> tree slot P + a);
+    // rows beyond the live ones are padding whose results are never written
     uint64_t mlo[2] = {0, 0}, mhi[2] = {0, 0};
     const int T = P + M;                                  // tokens visible to someone
-    if (wave_live) {
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            int r = row0 + rt * 16 + c16;
-            if (r >= Rh) r = Rh - 1;                      // padding row: any live row
-            const int j = r / g + 1, gi = r % g;
-            const uint16_t *qp = q + b * qs0 + static_cast<int64_t>(j - 1) * qs1 + static_cast<int64_t>(kvh * g + gi) * qs2 + G * (8 * KS);
+    for (int rt = 0; rt < 2; ++rt) {
+        const int r = row0 + rt * 16 + c16;
+        if (r >= Rh) continue;
+        const int dp = dep[rt];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = load_bf16x8(qp + ks * 8);
+        for (int k = 0; k < kAncBatch; ++k)
+            if (k < dp) {
+                const int a = anc8[rt][k] - 1;
+                if (a < 64) mlo[rt] |= 1ull << a; else mhi[rt] |= 1ull << (a - 64);
+            }
+        if (dp > kAncBatch) {
+            const int j = r / g + 1;
             const int32_t *arow = anc + (static_cast<int64_t>(b) * R + j) * W;
-            const int dep = depth[static_cast<int64_t>(b) * R + j];
-            for (int k = 0; k < dep; ++k) {
-                const int a = arow[k] - 1;                // bit a <-> tree slot P + a
+            for (int k = kAncBatch; k < dp; ++k) {
+                const int a = arow[k] - 1;
                 if (a < 64) mlo[rt] |= 1ull << a; else mhi[rt] |= 1ull << (a - 64);
             }
         }
@@ -198,111 +233,135 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
     const int c_begin = static_cast<int>(static_cast<int64_t>(nchunks) * split / splits);
     const int c_end = static_cast<int>(static_cast<int64_t>(nchunks) * (split + 1) / splits);
 
-    const uint16_t *kbase = kc + b * ks0 + kvh * ks1;
-    const uint16_t *vbase = vc + b * ks0 + kvh * ks1;
+    // chunk addressing: buffer loads through a wave-uniform resource descriptor rebuilt
+    // per chunk (scalar ALU only) plus per-lane byte offsets that never change.  The
+    // descriptor's record count stops at token T, so loads past the sequence return 0
+    // and never touch memory outside it.  K fragment (tt, ks) of a lane: token
+    // tt*16 + c16, dims ks*32 + G*8 .. +8 (the four lane groups of one instruction cover
+    // 64 contiguous bytes of a row); V row jj of a lane: token pi(G*8 + jj), dims
+    // c16*NT .. +NT (16 lanes cover a whole row).
+    const char *kbase = reinterpret_cast<const char *>(kc + b * ks0 + kvh * ks1);
+    const char *vbase = reinterpret_cast<const char *>(vc + b * ks0 + kvh * ks1);
+    const int64_t row_bytes = ks2 * 2;
+    uint32_t offk[2], offv[8];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) offk[tt] = static_cast<uint32_t>((tt * 16 + c16) * row_bytes + G * 16);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+        offv[jj] = static_cast<uint32_t>((jj < 4 ? G * 4 + jj : 16 + G * 4 + (jj - 4)) * row_bytes + c16 * NT * 2);
 
     f32x4_t oacc[2][NT];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) oacc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
+    float mref[2], mtrue[2], lrow[2];
+    const float cs = qk_scale_log2;
 
-    // registers of one chunk: K fragments (token t0 + tt*16 + c16, dims G*8*KS + ks*8 .. +8)
-    // and V rows (tokens pi(G*8 + j), dims c16*NT .. +NT)
     struct Chunk {
         bf16x8_t kf[2][KS];
-        uint32_t vr[8][NT / 2];
+        uint4 vr[8];
     };
     auto load_chunk = [&](Chunk &ch, int c) {
         const int t0 = c * kChunk;
+        const int64_t left = static_cast<int64_t>(T - t0) * row_bytes;
+        const int records = static_cast<int>(left < 0 ? 0 : (left > kChunk * row_bytes ? kChunk * row_bytes : left));
+        __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(kbase + t0 * row_bytes), 0, records, kBufferFlags);
+        __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(vbase + t0 * row_bytes), 0, records, kBufferFlags);
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            int t = t0 + tt * 16 + c16;
-            if (t > T - 1) t = T - 1;
-            const uint16_t *kp = kbase + static_cast<int64_t>(t) * ks2 + G * (8 * KS);
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) ch.kf[tt][ks] = load_bf16x8(kp + ks * 8);
-        }
+            for (int ks = 0; ks < KS; ++ks)
+                ch.kf[tt][ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(kr, offk[tt] + ks * 64, 0, 0));
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-            int t = t0 + (jj < 4 ? G * 4 + jj : 16 + G * 4 + (jj - 4));
-            if (t > T - 1) t = T - 1;
-            const uint16_t *vp = vbase + static_cast<int64_t>(t) * ks2 + c16 * NT;
             if constexpr (NT == 8) {
-                const uint4 u = *reinterpret_cast<const uint4 *>(vp);
-                ch.vr[jj][0] = u.x; ch.vr[jj][1] = u.y; ch.vr[jj][2] = u.z; ch.vr[jj][3] = u.w;
+                ch.vr[jj] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, offv[jj], 0, 0));
             } else {
-                const uint2 u = *reinterpret_cast<const uint2 *>(vp);
-                ch.vr[jj][0] = u.x; ch.vr[jj][1] = u.y;
+                const auto u = __builtin_amdgcn_raw_buffer_load_b64(vrs, offv[jj], 0, 0);
+                ch.vr[jj] = make_uint4(u[0], u[1], 0, 0);
             }
         }
     };
+    auto xor16_max = [](float x) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    };
+    auto xor32_max = [](float x) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    };
+    // first pass: each row's reference is the first finite chunk maximum (O and l are
+    // still exactly zero then, so adopting it rescales nothing); later maxima are only
+    // tracked.  p = 2^(s*cs - ref) stays finite unless a score exceeds the reference by
+    // more than kOverflow in base 2, in which case the whole split is recomputed against
+    // the exact maximum -- the accumulators never need rescaling inside the loop.
+    bool first_pass = true, overflow = false;
     auto compute_chunk = [&](const Chunk &ch, int c) {
         const int t0 = c * kChunk;
-        // S^T tiles: [token][row]
+        // S^T tiles: [token][row]; lane holds row c16 of tile rt, tokens t0 + tt*16 + G*4 + i
         f32x4_t s[2][2];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < 2; ++rt) {
+            bf16x8_t qr[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qr[ks] = __builtin_bit_cast(bf16x8_t, q_lds[wr][rt][ks][lane]);
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ch.kf[tt][ks], qf[rt][ks], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ch.kf[tt][ks], qr[ks], acc, 0, 0, 0);
                 s[rt][tt] = acc;
             }
-        // scale, mask, online softmax; lane holds row c16 of tile rt, tokens
-        // t0 + tt*16 + G*4 + i
-        const bool needs_mask = t0 + kChunk > P;
+        }
+        if (t0 + kChunk > P) {
+            // chunk reaches the tree slots: a token is visible if it is in the prefix or
+            // is an ancestor-or-self of the row's node (bit t - P of the row's mask)
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int a = t0 + tt * 16 + G * 4 + i - P;
+                        const uint64_t word = a >= 64 ? mhi[rt] : mlo[rt];
+                        const bool bit = (word >> (a & 63)) & 1ull;
+                        const bool vis = a < 0 || (a < M && bit);
+                        s[rt][tt][i] = vis ? s[rt][tt][i] : -INFINITY;
+                    }
+        }
         bf16x8_t pb[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-            float v[8];
+            if (first_pass) {
+                float cm = fmaxf(fmaxf(fmaxf(s[rt][0][0], s[rt][0][1]), fmaxf(s[rt][0][2], s[rt][0][3])),
+                                 fmaxf(fmaxf(s[rt][1][0], s[rt][1][1]), fmaxf(s[rt][1][2], s[rt][1][3])));
+                cm = xor32_max(xor16_max(cm));
+                mtrue[rt] = fmaxf(mtrue[rt], cm);
+                if (mref[rt] == -INFINITY) mref[rt] = cm;
+                overflow |= (cm - mref[rt]) * cs > kOverflow;
+            }
+            const float mr = mref[rt] == -INFINITY ? 0.f : mref[rt] * cs;
+            float lsum = 0.f;
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    float x = s[rt][tt][i] * qk_scale_log2;
-                    if (needs_mask) {
-                        const int t = t0 + tt * 16 + G * 4 + i;
-                        bool vis = t < P;
-                        if (!vis && t < T) {
-                            const int a = t - P;
-                            vis = a < 64 ? ((mlo[rt] >> a) & 1ull) : ((mhi[rt] >> (a - 64)) & 1ull);
-                        }
-                        if (!vis) x = -INFINITY;
-                    }
-                    v[tt * 4 + i] = x;
+                    const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rt][tt][i], cs, -mr));
+                    pb[rt][tt * 4 + i] = static_cast<__bf16>(pe);
+                    lsum += pe;
                 }
-            float cm = v[0];
-#pragma unroll
-            for (int e = 1; e < 8; ++e) cm = fmaxf(cm, v[e]);
-            cm = fmaxf(cm, __shfl_xor(cm, 16, kWave));
-            cm = fmaxf(cm, __shfl_xor(cm, 32, kWave));
-            const float mnew = fmaxf(mrow[rt], cm);
-            const float mref = mnew == -INFINITY ? 0.f : mnew;
-            const float alpha = __builtin_amdgcn_exp2f(mrow[rt] - mref);
-            float lsum = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const __bf16 pe = static_cast<__bf16>(__builtin_amdgcn_exp2f(v[e] - mref));
-                pb[rt][e] = pe;
-                lsum += static_cast<float>(pe);
-            }
-            lrow[rt] = lrow[rt] * alpha + lsum;
-            mrow[rt] = mnew;
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) oacc[rt][nt] *= alpha;
+            lrow[rt] += lsum;
         }
         // O^T += V^T P^T; A operand of dim tile nt = (vr[0][nt], ..., vr[7][nt])
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             uint32_t a4[4];
+            const uint32_t sel = (nt & 1) ? 0x07060302u : 0x05040100u;
 #pragma unroll
             for (int f = 0; f < 4; ++f) {
-                const uint32_t x = ch.vr[2 * f][nt >> 1], y = ch.vr[2 * f + 1][nt >> 1];
-                a4[f] = (nt & 1) ? hi_pair(x, y) : lo_pair(x, y);
+                const uint4 x4 = ch.vr[2 * f], y4 = ch.vr[2 * f + 1];
+                const int e = nt >> 1;
+                const uint32_t x = e == 0 ? x4.x : e == 1 ? x4.y : e == 2 ? x4.z : x4.w;
+                const uint32_t y = e == 0 ? y4.x : e == 1 ? y4.y : e == 2 ? y4.z : y4.w;
+                a4[f] = __builtin_amdgcn_perm(y, x, sel);
             }
             const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(a4[0], a4[1], a4[2], a4[3]));
 #pragma unroll
@@ -311,28 +370,52 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
         }
     };
 
-    if (wave_live) {
-        // ping-pong register buffers: the next chunk's loads are in flight while the
-        // current chunk is computed (the prefetch index is clamped, never out of range)
-        Chunk bufA, bufB;
-        int c = c_begin + wt;
-        if (c < c_end) load_chunk(bufA, c);
-        while (c < c_end) {
-            const int c1 = c + WT;
-            load_chunk(bufB, c1 < c_end ? c1 : c);
-            compute_chunk(bufA, c);
-            if (c1 >= c_end) break;
-            const int c2 = c1 + WT;
-            load_chunk(bufA, c2 < c_end ? c2 : c1);
-            compute_chunk(bufB, c1);
-            c = c2;
-        }
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) { mref[rt] = -INFINITY; mtrue[rt] = -INFINITY; }
+    for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-            lrow[rt] += __shfl_xor(lrow[rt], 16, kWave);
-            lrow[rt] += __shfl_xor(lrow[rt], 32, kWave);
+            lrow[rt] = 0.f;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) oacc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
+        if (wave_live) {
+            // ping-pong register buffers: the next chunk's loads are in flight while the
+            // current chunk is computed (the prefetch index is clamped into the range)
+            Chunk bufA, bufB;
+            int c = c_begin + wt;
+            if (c < c_end) load_chunk(bufA, c);
+            while (c < c_end) {
+                const int c1 = c + WT;
+                load_chunk(bufB, c1 < c_end ? c1 : c);
+                compute_chunk(bufA, c);
+                if (c1 >= c_end) break;
+                const int c2 = c1 + WT;
+                load_chunk(bufA, c2 < c_end ? c2 : c1);
+                compute_chunk(bufB, c1);
+                c = c2;
+            }
+        }
+        if (!__any(overflow)) break;
+        // rare: some score outgrew its reference; redo the split against the exact maxima
+        first_pass = false;
+        overflow = false;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) mref[rt] = mtrue[rt];
     }
+    float mrow[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        mrow[rt] = mref[rt];
+        // row sums: each of the four lanes of a row holds a partial sum
+        auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(lrow[rt]), __float_as_uint(lrow[rt]), false, false);
+        const float l16 = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+        auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(l16), __float_as_uint(l16), false, false);
+        lrow[rt] = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+    }
+    // from here on the running maxima are in base-2 units, as the merge steps expect
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) mrow[rt] = mrow[rt] == -INFINITY ? -INFINITY : mrow[rt] * cs;
 
     // ---- merge the WT waves that share rows (LDS), fixed order
     // lane's output element (rt, nt, i) is row row0 + rt*16 + c16, dim (G*4 + i)*NT + nt
@@ -388,75 +471,30 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
         }
     }
 
-    // ---- split-KV: publish partials, last workgroup of the group merges
-    const int64_t unit = (static_cast<int64_t>(pair) * nb + rbk);          // (pair, row block)
-    bool finalize = true;
+    // ---- split-KV: publish this split's partial (m, l, unnormalised O) and stop; the
+    // merge kernel that follows on the stream combines the splits in a fixed order
     if (splits > 1) {
-        __shared__ int is_last;
-        if (wt == 0) {
-            const int64_t base = (unit * splits + split) * RB + wr * kRowsPerWave;
+        if (wt != 0) return;
+        const int64_t unit = static_cast<int64_t>(pair) * nb + rbk;          // (pair, row block)
+        const int64_t base = (unit * splits + split) * RB + wr * kRowsPerWave;
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const int rr = rt * 16 + c16;
-                float *o = ws_o + (base + rr) * D + G * DG;
+        for (int rt = 0; rt < 2; ++rt) {
+            const int rr = rt * 16 + c16;
+            float *o = ws_o + (base + rr) * D + G * DG;
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) o[i * NT + nt] = oacc[rt][nt][i];
-                if (G == 0) {
-                    ws_stats[(base + rr) * 2 + 0] = mrow[rt];
-                    ws_stats[(base + rr) * 2 + 1] = lrow[rt];
-                }
+            for (int e = 0; e < DG; e += 4) {
+                float4 v4;
+                v4.x = oacc[rt][(e + 0) % NT][(e + 0) / NT];
+                v4.y = oacc[rt][(e + 1) % NT][(e + 1) / NT];
+                v4.z = oacc[rt][(e + 2) % NT][(e + 2) / NT];
+                v4.w = oacc[rt][(e + 3) % NT][(e + 3) / NT];
+                *reinterpret_cast<float4 *>(o + e) = v4;
             }
+            if (G == 0) *reinterpret_cast<float2 *>(ws_stats + (base + rr) * 2) = make_float2(mrow[rt], lrow[rt]);
         }
-        __threadfence();
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const uint32_t prev = atomicAdd(&counters[unit], 1u);
-            is_last = prev == static_cast<uint32_t>(splits - 1);
-            if (is_last) atomicExch(&counters[unit], 0u);
-        }
-        __syncthreads();
-        finalize = is_last != 0;
-        if (finalize && wt == 0) {
-            __threadfence();
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const int rr = rt * 16 + c16;
-                float mo[16], mt = -INFINITY;
-                for (int s2 = 0; s2 < splits; ++s2) {
-                    const int64_t base = (unit * splits + s2) * RB + wr * kRowsPerWave;
-                    mo[s2 & 15] = s2 == split ? mrow[rt] : ws_stats[(base + rr) * 2];
-                    mt = fmaxf(mt, mo[s2 & 15]);
-                }
-                const float mref = mt == -INFINITY ? 0.f : mt;
-                f32x4_t acc[NT];
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                float lt = 0.f;
-                for (int s2 = 0; s2 < splits; ++s2) {
-                    const int64_t base = (unit * splits + s2) * RB + wr * kRowsPerWave;
-                    const float sc = __builtin_amdgcn_exp2f(mo[s2 & 15] - mref);
-                    if (s2 == split) {
-                        lt += sc * lrow[rt];
-#pragma unroll
-                        for (int nt = 0; nt < NT; ++nt) acc[nt] += sc * oacc[rt][nt];
-                    } else {
-                        lt += sc * ws_stats[(base + rr) * 2 + 1];
-                        const float *o = ws_o + (base + rr) * D + G * DG;
-#pragma unroll
-                        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) acc[nt][i] += sc * o[i * NT + nt];
-                    }
-                }
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) oacc[rt][nt] = acc[nt];
-                lrow[rt] = lt;
-            }
-        }
+        return;
     }
-    if (!finalize || wt != 0) return;
+    if (wt != 0) return;
 
     // ---- write the final rows: lane writes dims G*DG .. +DG of its row in each tile
 #pragma unroll
@@ -481,6 +519,79 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
             *reinterpret_cast<uint4 *>(o + e) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
         }
     }
+}
+
+// --------------------------------------------------------------------------- split merge
+// One thread per (row, 8 head dims) of every live row block: reads the S partials of its
+// row in split order, rescales them to the common maximum and writes the bf16 row; rows
+// of inert nodes (and whole failed sequences) are written as 0.
+template <int D, int RB>
+__global__ void __launch_bounds__(256)
+tree_attn_merge_kernel(int M_max, int D_max, int Hq, int Hkv, int L_cap,
+                       const int32_t *__restrict__ prefix_len, const int32_t *__restrict__ n_nodes,
+                       const int32_t *__restrict__ depth, const int32_t *__restrict__ status,
+                       uint16_t *__restrict__ out, int64_t os0, int64_t os1, int64_t os2,
+                       const float *__restrict__ ws_stats, const float *__restrict__ ws_o,
+                       int pairs, int nb, int splits)
+{
+    constexpr int TPR = D / 8;                         // threads per row
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t row_global = t / TPR;                // over pairs * nb * RB
+    const int part = static_cast<int>(t % TPR);
+    if (row_global >= static_cast<int64_t>(pairs) * nb * RB) return;
+    const int64_t unit = row_global / RB;
+    const int rr = static_cast<int>(row_global % RB);
+    const int pair = static_cast<int>(unit / nb), rbk = static_cast<int>(unit % nb);
+    const int b = pair / Hkv, kvh = pair % Hkv, g = Hq / Hkv;
+    const int r = rbk * RB + rr;
+    if (r >= M_max * g) return;
+    const int j = r / g + 1, gi = r % g;
+    const int M = n_nodes[b], P = prefix_len[b], st = status[b];
+    const int dp = depth[static_cast<int64_t>(b) * (M_max + 1) + j];
+    // every split's (m, l) and O slice are fetched before any is consumed
+    constexpr int kMaxSplits = 16;
+    float2 ml[kMaxSplits];
+    float4 oa[kMaxSplits], ob[kMaxSplits];
+#pragma unroll
+    for (int s2 = 0; s2 < kMaxSplits; ++s2) {
+        if (s2 < splits) {
+            const int64_t base = (unit * splits + s2) * RB + rr;
+            ml[s2] = *reinterpret_cast<const float2 *>(ws_stats + base * 2);
+            const float4 *o = reinterpret_cast<const float4 *>(ws_o + base * D + part * 8);
+            oa[s2] = o[0];
+            ob[s2] = o[1];
+        }
+    }
+    const bool seq_ok = st == TMV_OK && M >= 0 && M <= M_max && P >= 0 && static_cast<int64_t>(P) + M <= L_cap;
+    const bool live = seq_ok && r < M * g && dp >= 1;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (live) {
+        float mt = -INFINITY;
+#pragma unroll
+        for (int s2 = 0; s2 < kMaxSplits; ++s2)
+            if (s2 < splits) mt = fmaxf(mt, ml[s2].x);
+        const float mref = mt == -INFINITY ? 0.f : mt;
+        float lt = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < kMaxSplits; ++s2) {
+            if (s2 < splits) {
+                const float sc = __builtin_amdgcn_exp2f(ml[s2].x - mref);
+                lt += sc * ml[s2].y;
+                acc[0] += sc * oa[s2].x; acc[1] += sc * oa[s2].y; acc[2] += sc * oa[s2].z; acc[3] += sc * oa[s2].w;
+                acc[4] += sc * ob[s2].x; acc[5] += sc * ob[s2].y; acc[6] += sc * ob[s2].z; acc[7] += sc * ob[s2].w;
+            }
+        }
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] *= inv;
+    }
+    uint32_t w4[4];
+#pragma unroll
+    for (int h2 = 0; h2 < 4; ++h2)
+        w4[h2] = static_cast<uint32_t>(tmv::f32_to_bf16(acc[2 * h2])) |
+                 (static_cast<uint32_t>(tmv::f32_to_bf16(acc[2 * h2 + 1])) << 16);
+    uint16_t *o = out + b * os0 + static_cast<int64_t>(j - 1) * os1 + static_cast<int64_t>(kvh * g + gi) * os2 + part * 8;
+    *reinterpret_cast<uint4 *>(o) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
 }
 
 // --------------------------------------------------------------------------- fp32 kernel
@@ -561,16 +672,22 @@ template <int D, int WR>
 void launch_bf16(const AttnPlan &p, hipStream_t s, int M_max, int D_max, int Hq, int Hkv,
                  const void *q, const int64_t *qs, const void *k, const void *v, const int64_t *kvs,
                  int L_cap, const int32_t *P, const int32_t *n, const int32_t *anc, const int32_t *dep,
-                 int32_t *status, float scale, void *out, const int64_t *os, void *ws, size_t off_st,
-                 size_t off_o)
+                 int32_t *status, float scale, void *out, const int64_t *os, void *ws, size_t off_o)
 {
     char *w = static_cast<char *>(ws);
+    float *stats = reinterpret_cast<float *>(w), *part = reinterpret_cast<float *>(w + off_o);
     hipLaunchKernelGGL((tree_attn_bf16_kernel<D, WR>), dim3(p.slots * tmv::kXcds), dim3(kWaves * kWave), 0, s,
                        M_max, D_max, Hq, Hkv, static_cast<const uint16_t *>(q), qs[0], qs[1], qs[2],
                        static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), kvs[0], kvs[1], kvs[2],
                        L_cap, P, n, anc, dep, status, scale * kLog2e, static_cast<uint16_t *>(out), os[0], os[1],
-                       os[2], reinterpret_cast<uint32_t *>(w), reinterpret_cast<float *>(w + off_st),
-                       reinterpret_cast<float *>(w + off_o), p.pairs, p.nb, p.splits, p.per_pair);
+                       os[2], stats, part, p.pairs, p.nb, p.splits, p.per_pair);
+    if (p.splits > 1) {
+        constexpr int RB = WR * kRowsPerWave;
+        const int64_t threads = static_cast<int64_t>(p.pairs) * p.nb * RB * (D / 8);
+        hipLaunchKernelGGL((tree_attn_merge_kernel<D, RB>), dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256),
+                           0, s, M_max, D_max, Hq, Hkv, L_cap, P, n, dep, status, static_cast<uint16_t *>(out),
+                           os[0], os[1], os[2], stats, part, p.pairs, p.nb, p.splits);
+    }
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -582,7 +699,7 @@ extern "C" size_t tmv_tree_verify_attention_workspace(int dtype, int B, int M_ma
 {
     if (dtype != TMV_BF16 || B <= 0 || Hkv <= 0 || Hq <= 0 || Hq % Hkv) return 256;
     const AttnPlan p = make_plan(B, M_max, Hq, Hkv, L_cap);
-    return plan_bytes(p, d, nullptr, nullptr);
+    return plan_bytes(p, d, nullptr);
 }
 
 extern "C" int tmv_tree_verify_attention(int dtype, int B, int M_max, int D_max, int Hq, int Hkv, int d,
@@ -624,21 +741,21 @@ extern "C" int tmv_tree_verify_attention(int dtype, int B, int M_max, int D_max,
     for (int i = 0; i < 3; ++i)
         if ((q_stride[i] | kv_stride[i] | o_stride[i]) & 7) return TMV_ERR_ARG;
     const AttnPlan p = make_plan(B, M_max, Hq, Hkv, L_cap);
-    size_t off_st = 0, off_o = 0;
-    const size_t need = plan_bytes(p, d, &off_st, &off_o);
+    size_t off_o = 0;
+    const size_t need = plan_bytes(p, d, &off_o);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return TMV_ERR_ARG;
     if (static_cast<int64_t>(p.slots) * tmv::kXcds > 0x7fffffff) return TMV_ERR_ARG;
 
     if (d == 128) {
         if (p.wr == 4) launch_bf16<128, 4>(p, s, M_max, D_max, Hq, Hkv, q, q_stride, k_cache, v_cache, kv_stride, L_cap,
-                                           prefix_len, n_nodes, anc, depth, status, scale, out, o_stride, workspace, off_st, off_o);
+                                           prefix_len, n_nodes, anc, depth, status, scale, out, o_stride, workspace, off_o);
         else launch_bf16<128, 1>(p, s, M_max, D_max, Hq, Hkv, q, q_stride, k_cache, v_cache, kv_stride, L_cap,
-                                 prefix_len, n_nodes, anc, depth, status, scale, out, o_stride, workspace, off_st, off_o);
+                                 prefix_len, n_nodes, anc, depth, status, scale, out, o_stride, workspace, off_o);
     } else {
         if (p.wr == 4) launch_bf16<64, 4>(p, s, M_max, D_max, Hq, Hkv, q, q_stride, k_cache, v_cache, kv_stride, L_cap,
-                                          prefix_len, n_nodes, anc, depth, status, scale, out, o_stride, workspace, off_st, off_o);
+                                          prefix_len, n_nodes, anc, depth, status, scale, out, o_stride, workspace, off_o);
         else launch_bf16<64, 1>(p, s, M_max, D_max, Hq, Hkv, q, q_stride, k_cache, v_cache, kv_stride, L_cap,
-                                prefix_len, n_nodes, anc, depth, status, scale, out, o_stride, workspace, off_st, off_o);
+                                prefix_len, n_nodes, anc, depth, status, scale, out, o_stride, workspace, off_o);
     }
     return tmv_host::launch_status(hipGetLastError());
 }

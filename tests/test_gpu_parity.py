@@ -141,6 +141,18 @@ def test_attention_bf16_small_ragged(ref, variant):
     _attention_parity(ref, w, 2e-2, 1e-2)
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_attention_bf16_deep_paths(ref, d):
+    # ancestor paths longer than the entries a row fetches up front (the kernels' deep-row
+    # branch): chains and deep random trees, with and without a prefix
+    _case("attention: bf16 deep paths d=%d" % d)
+    w = small_attention_workload(206 + d, 3, 8, 2, d, 70, [0, 45, 3], [70, 52, 33], q_scale=6.0, max_depth=70,
+                                 labelled=False)
+    w.parents[0, :71] = ti.tree_chain(70)
+    assert int(oracle_tables(ref, w)[1].max()) > 16
+    _attention_parity(ref, w, 2e-2, 1e-2)
+
+
 @pytest.mark.parametrize("Hq,Hkv,d", [(4, 4, 128), (16, 2, 64), (12, 4, 64), (64, 8, 128)])
 def test_attention_bf16_head_shapes(ref, Hq, Hkv, d):
     _case("attention: bf16 Hq=%d Hkv=%d d=%d" % (Hq, Hkv, d))

@@ -46,7 +46,8 @@ def build(verbose: bool = False) -> str:
     if failed:
         raise RuntimeError("libtmv build failed")
     tmp = LIB + ".tmp%d" % os.getpid()
-    subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs)
+    # -z defs: an unresolved symbol (e.g. a kernel stub that was not emitted) fails the link
+    subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp] + objs)
     os.replace(tmp, LIB)
     return LIB
 

@@ -45,6 +45,62 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kOverflow = 32.0f;  // largest score excess over a row's reference, base 2
 constexpr int kBufferFlags = 0x00020000;   // raw buffer descriptor word 3 (gfx9 family)
+
+// s_waitcnt immediate that waits for vector-memory count <= N only (gfx9 encoding:
+// vmcnt[3:0] and vmcnt[5:4] at bits 15:14, expcnt and lgkmcnt left at their maxima)
+template <int N>
+constexpr int kVmcntRound() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    return (N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14);
+}
+constexpr int kVmcntZero = kVmcntRound<0>();
+// s_waitcnt immediate that waits for LDS / scalar-memory count 0 only
+constexpr int kLgkmcntZero = 0xF | (0x7 << 4) | (0x3 << 14);
+
+// LDS operand reads of the attention loop.  The compiler cannot tell the two halves of
+// the DMA ring apart inside the loop, so for any LDS load it writes itself it would first
+// wait for all buffer->LDS DMA in flight, including the next round's.  These reads are
+// therefore inline assembly, each block self-contained: it issues its reads and waits for
+// them before its outputs exist, so no register is ever seen before its data has landed
+// (outputs are early-clobber: a returning read must not overwrite a later read's address).
+// The loop's own waits and barriers order the blocks against the DMA (the memory clobber
+// keeps the compiler from moving them across those).
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void lds_read_b128_x4(u32x4_t (&v)[4], const uint32_t (&a)[4]) {
+    asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+                 : "memory");
+}
+__device__ __forceinline__ void lds_read_b128_x8(u32x4_t (&v)[8], const uint32_t (&a)[8]) {
+    asm volatile("ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\tds_read_b128 %3, %11\n\t"
+                 "ds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\tds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]),
+                   "=&v"(v[7])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+                 : "memory");
+}
+__device__ __forceinline__ void lds_read_b64_x8(u32x2_t (&v)[8], const uint32_t (&a)[8]) {
+    asm volatile("ds_read_b64 %0, %8\n\tds_read_b64 %1, %9\n\tds_read_b64 %2, %10\n\tds_read_b64 %3, %11\n\t"
+                 "ds_read_b64 %4, %12\n\tds_read_b64 %5, %13\n\tds_read_b64 %6, %14\n\tds_read_b64 %7, %15\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]),
+                   "=&v"(v[7])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+                 : "memory");
+}
+// buffer -> LDS copy of 16 bytes per lane: lane l's bytes land at lds + 16*l; a voffset
+// past the descriptor's records writes zeros and reads nothing
+__device__ __forceinline__ void dma_to_lds16(__amdgpu_buffer_rsrc_t r, char *lds, uint32_t voffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voffset, 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t lds_addr(const char *p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char *)p));
+}
 constexpr int kChunk = 32;          // tokens per chunk (two 16-token MFMA tiles)
 constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;    // two 16-row tiles
@@ -102,10 +158,12 @@ __device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t *p) {
 __device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
 __device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
 
-// --------------------------------------------------------------------------- bf16 MFMA kernel
+// ------------------------------------------------ bf16 MFMA kernel, register streaming (d64)
+// Each wave streams its own chunks straight from memory into registers; used for head
+// dimension 64, where the LDS-ring kernel below is switched off.
 template <int D, int WR>
 __global__ void __launch_bounds__(kWaves * kWave)
-tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
+tree_attn_bf16_stream_kernel(int M_max, int D_max, int Hq, int Hkv,
                       const uint16_t *__restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
                       const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
                       int64_t ks0, int64_t ks1, int64_t ks2, int L_cap,
@@ -521,6 +579,550 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
     }
 }
 
+// --------------------------------------------------------------------------- bf16 MFMA kernel
+// LDS ring of chunk slots: 128 KiB, two halves of kRound chunks each (double buffered).
+constexpr int kRingBytes = 128 * 1024;
+
+template <int D>
+struct RingShape {
+    static constexpr int kRowBytes = D * 2;                 // one K (or V) row in LDS
+    static constexpr int kPieces = D / 8;                   // 16-byte pieces per row
+    static constexpr int kMatBytes = kChunk * kRowBytes;    // K (or V) part of one chunk
+    static constexpr int kSlotBytes = 2 * kMatBytes;        // K then V
+    static constexpr int kSlots = kRingBytes / kSlotBytes;  // 8 (d128) or 16 (d64)
+    static constexpr int kRound = kSlots / 2;               // chunks per half
+    static constexpr int kDmaPerChunk = kSlotBytes / 1024;  // 1 KiB per DMA instruction
+    static constexpr int kDmaPerWave = kDmaPerChunk / kWaves;
+    static_assert(kDmaPerWave * kWaves == kDmaPerChunk, "chunk DMA must split evenly over the waves");
+};
+
+// ancestor entries of a row fetched in the prologue; deeper rows (DEEP kernels only)
+// fetch the rest in further batches
+constexpr int kAncBatch = 16;
+
+template <int D, int WR, bool DEEP>
+__global__ void __launch_bounds__(kWaves * kWave)
+tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
+                      const uint16_t *__restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
+                      const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
+                      int64_t ks0, int64_t ks1, int64_t ks2, int L_cap,
+                      const int32_t *__restrict__ prefix_len, const int32_t *__restrict__ n_nodes,
+                      const int32_t *__restrict__ anc, const int32_t *__restrict__ depth,
+                      int32_t *__restrict__ status, float qk_scale_log2,
+                      uint16_t *__restrict__ out, int64_t os0, int64_t os1, int64_t os2,
+                      float *__restrict__ ws_stats, float *__restrict__ ws_o,
+                      int pairs, int nb, int splits, int per_pair)
+{
+    using RS = RingShape<D>;
+    constexpr int KS = D / 32;           // k-steps of the QK^T contraction
+    constexpr int NT = D / 16;           // 16-dim output tiles
+    constexpr int WT = kWaves / WR;      // waves sharing rows (they split the chunks)
+    constexpr int RB = WR * kRowsPerWave;
+    constexpr int DG = D / 4;            // dims per lane of an output row
+    constexpr int PP = RS::kPieces;
+
+    // two halves of the ring as distinct objects, so LDS reads of one half need not wait
+    // for DMA still landing in the other
+    __shared__ __attribute__((aligned(16))) char ring0[RS::kRound * RS::kSlotBytes];
+    __shared__ __attribute__((aligned(16))) char ring1[RS::kRound * RS::kSlotBytes];
+
+    // ---- decode the workgroup: XCD-major so one (sequence, kv head) stays on one XCD
+    const int wg = blockIdx.x;
+    const int xcd = wg % tmv::kXcds, slot = wg / tmv::kXcds;
+    const int pair = (slot / per_pair) * tmv::kXcds + xcd;
+    if (pair >= pairs) return;
+    const int within = slot % per_pair;
+    const int rbk = within / splits, split = within % splits;
+    const int b = pair / Hkv, kvh = pair % Hkv;
+    const int g = Hq / Hkv;
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);     // wave-uniform
+    const int wr = wave / WT, wt = wave % WT;
+    const int c16 = lane & 15, G = lane >> 4;
+    const int R = 1 + M_max, W = D_max + 1;
+    const int row0_wg = rbk * RB;
+    const int row0 = row0_wg + wr * kRowsPerWave;         // first row of this wave
+
+    // ---- one round trip for the prologue: the sequence's scalars and, independently of
+    // them, this lane's query fragments, node depths and first ancestor entries (row
+    // indices are clamped into the tables, so no load waits on another)
+    // (values are wave-uniform; readfirstlane keeps the chunk descriptors in scalar registers)
+    const int M = __builtin_amdgcn_readfirstlane(n_nodes[b]);
+    const int P = __builtin_amdgcn_readfirstlane(prefix_len[b]);
+    int st = __builtin_amdgcn_readfirstlane(status[b]);
+    bf16x8_t qf[2][KS];
+    int dep[2], anc8[2][kAncBatch];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        int r = row0 + rt * 16 + c16;
+        if (r > M_max * g - 1) r = M_max * g - 1;
+        const int j = r / g + 1, gi = r % g;
+        const uint16_t *qp = q + b * qs0 + static_cast<int64_t>(j - 1) * qs1 + static_cast<int64_t>(kvh * g + gi) * qs2 + G * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = load_bf16x8(qp + ks * 32);
+        dep[rt] = depth[static_cast<int64_t>(b) * R + j];
+        const int32_t *arow = anc + (static_cast<int64_t>(b) * R + j) * W;
+#pragma unroll
+        for (int k = 0; k < kAncBatch; ++k) anc8[rt][k] = arow[k < W ? k : W - 1];
+    }
+
+    if (st == TMV_OK && (M < 0 || M > M_max || P < 0 || static_cast<int64_t>(P) + M > L_cap)) {
+        st = TMV_ERR_INPUT;
+        if (threadIdx.x == 0 && rbk == 0 && split == 0) status[b] = TMV_ERR_INPUT;
+    }
+    const int Rh = (st == TMV_OK) ? M * g : 0;           // live rows of this kv head
+
+    if (row0_wg >= Rh) {
+        // no live row in this workgroup: clear the block's output rows (with split-KV the
+        // merge kernel writes every row instead)
+        if (splits == 1 && wt == 0) {
+            for (int rt = 0; rt < 2; ++rt) {
+                const int r = row0 + rt * 16 + c16;
+                if (r >= M_max * g) continue;
+                const int j = r / g + 1, gi = r % g;
+                uint16_t *o = out + b * os0 + static_cast<int64_t>(j - 1) * os1 + static_cast<int64_t>(kvh * g + gi) * os2 + G * DG;
+#pragma unroll
+                for (int e = 0; e < DG; e += 8) *reinterpret_cast<uint4 *>(o + e) = make_uint4(0, 0, 0, 0);
+            }
+        }
+        return;
+    }
+
+    // ---- token range of this split, in 32-token chunks; local chunk k of this
+    // workgroup sits in slot k % kSlots (half (k / kRound) % 2)
+    const int T = P + M;                                  // tokens visible to someone
+    const int nchunks = (T + kChunk - 1) / kChunk;
+    // (nchunks * splits stays far below 2^31: nchunks <= 2^26 and splits <= 16)
+    const int c_begin = __builtin_amdgcn_readfirstlane(nchunks * split / splits);
+    const int c_end = __builtin_amdgcn_readfirstlane(nchunks * (split + 1) / splits);
+    const int nk = c_end - c_begin;
+    const int nrounds = (nk + RS::kRound - 1) / RS::kRound;
+
+    // DMA lane mapping: instruction i of a chunk covers LDS bytes [i*1 KiB, +1 KiB) of the
+    // slot; lane l writes 16 bytes at 16*l.  Within K (or V) the LDS holds row t at
+    // t*kRowBytes with its 16-byte pieces XOR-swizzled by (t mod kPieces), so the lane
+    // that fills LDS piece (t, pp) reads global piece pp ^ (t mod kPieces) of row t.
+    const char *kbase = reinterpret_cast<const char *>(kc + b * ks0 + kvh * ks1);
+    const char *vbase = reinterpret_cast<const char *>(vc + b * ks0 + kvh * ks1);
+    const int64_t row_bytes = ks2 * 2;
+    // each wave moves whole 1 KiB pieces of either K or V (waves 0-1 K, 2-3 V)
+    static_assert((RS::kDmaPerChunk / 2) % RS::kDmaPerWave == 0, "a wave must stay within K or V");
+    const bool wave_v = wave * RS::kDmaPerWave >= RS::kDmaPerChunk / 2;
+    const char *mbase = wave_v ? vbase : kbase;
+    uint32_t dma_off[RS::kDmaPerWave];
+    int dma_lds[RS::kDmaPerWave];
+#pragma unroll
+    for (int jd = 0; jd < RS::kDmaPerWave; ++jd) {
+        const int i = wave * RS::kDmaPerWave + jd;             // instruction within the chunk
+        const int ii = wave_v ? i - RS::kDmaPerChunk / 2 : i;
+        const int qpos = ii * 64 + lane;                       // 16-byte LDS piece index
+        const int t = qpos / PP, pp = qpos % PP;
+        dma_off[jd] = static_cast<uint32_t>(t * row_bytes + ((pp ^ (t % PP)) * 16));
+        dma_lds[jd] = (wave_v ? RS::kMatBytes : 0) + ii * 1024;
+    }
+    // issue this wave's share of local chunk k into the slot at `slot` (records stop at T,
+    // so loads past it write zeros and touch no memory; chunks past the split load nothing)
+    auto issue_chunk = [&](int k, char *slot) {
+        const int t0 = (c_begin + k) * kChunk;
+        int recs = (k < nk) ? T - t0 : 0;
+        recs = recs < 0 ? 0 : (recs > kChunk ? kChunk : recs);
+        const int nbytes = __builtin_amdgcn_readfirstlane(static_cast<int>(recs * row_bytes));
+        const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char *>(mbase + static_cast<int64_t>(k < nk ? t0 : 0) * row_bytes), 0, nbytes, kBufferFlags);
+#pragma unroll
+        for (int jd = 0; jd < RS::kDmaPerWave; ++jd)
+            dma_to_lds16(mr, slot + dma_lds[jd], dma_off[jd]);
+    };
+    // round r fills half r % 2 of the ring with local chunks r*kRound .. +kRound
+    auto issue_round = [&](int r, char *half) {
+#pragma unroll
+        for (int j = 0; j < RS::kRound; ++j) issue_chunk(r * RS::kRound + j, half + j * RS::kSlotBytes);
+    };
+    // the first two rounds go out before anything waits
+    // (round 1 is issued even when empty -- it then loads nothing -- so the number of DMA
+    // operations in flight is the same on every path)
+    issue_round(0, ring0);
+    issue_round(1, ring1);
+
+    const bool wave_live = row0 < Rh;
+
+    // ---- ancestor-or-self masks of the lane's two rows (bit a <-> tree slot P + a);
+    // rows beyond the live ones are padding whose results are never written
+    uint64_t mlo[2] = {0, 0}, mhi[2] = {0, 0};
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        const int r = row0 + rt * 16 + c16;
+        if (r >= Rh) continue;
+        const int dp = dep[rt];
+#pragma unroll
+        for (int k = 0; k < kAncBatch; ++k)
+            if (k < dp) {
+                const int a = anc8[rt][k] - 1;
+                if (a < 64) mlo[rt] |= 1ull << a; else mhi[rt] |= 1ull << (a - 64);
+            }
+        if (DEEP && dp > kAncBatch) {
+            // deep rows: the rest of the path, one batch of loads per round trip
+            const int j = r / g + 1;
+            const int32_t *arow = anc + (static_cast<int64_t>(b) * R + j) * W;
+            for (int k0 = kAncBatch; k0 < dp; k0 += kAncBatch) {
+                int e[kAncBatch];
+#pragma unroll
+                for (int k = 0; k < kAncBatch; ++k) e[k] = arow[k0 + k < W ? k0 + k : W - 1];
+#pragma unroll
+                for (int k = 0; k < kAncBatch; ++k)
+                    if (k0 + k < dp) {
+                        const int a = e[k] - 1;
+                        if (a < 64) mlo[rt] |= 1ull << a; else mhi[rt] |= 1ull << (a - 64);
+                    }
+            }
+        }
+    }
+
+    // LDS read offsets of the MFMA operands inside a slot (constant per lane).  K
+    // fragment (tt, ks): row tt*16 + c16, logical piece ks*4 + G; V row jj: row
+    // pi(G*8 + jj), logical piece c16 (d128) or c16/2 + half (d64).
+    uint32_t lk[2][KS], lv[8];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        const int t = tt * 16 + c16;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) lk[tt][ks] = t * RS::kRowBytes + (((ks * 4 + G) ^ (t % PP)) * 16);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+        const int t = jj < 4 ? G * 4 + jj : 16 + G * 4 + (jj - 4);
+        if constexpr (NT == 8)
+            lv[jj] = RS::kMatBytes + t * RS::kRowBytes + ((c16 ^ (t % PP)) * 16);
+        else
+            lv[jj] = RS::kMatBytes + t * RS::kRowBytes + ((((c16 >> 1) ^ (t % PP)) * 16) + (c16 & 1) * 8);
+    }
+
+    f32x4_t oacc[2][NT];
+    float mref[2], mtrue[2], lrow[2];
+    const float cs = qk_scale_log2;
+    auto xor16_max = [](float x) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    };
+    auto xor32_max = [](float x) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    };
+    // first pass: each row's reference is the first finite chunk maximum (O and l are
+    // still exactly zero then, so adopting it rescales nothing); later maxima are only
+    // tracked.  p = 2^(s*cs - ref) stays finite unless a score exceeds the reference by
+    // more than kOverflow in base 2, in which case the whole split is recomputed against
+    // the exact maximum -- the accumulators never need rescaling inside the loop.
+    bool first_pass = true, overflow = false;
+    auto compute_chunk = [&](uint32_t sp, int c) {
+        const int t0 = c * kChunk;
+        // S^T tiles: [token][row]; lane holds row c16 of tile rt, tokens t0 + tt*16 + G*4 + i
+        constexpr int NK = 2 * KS;                   // K fragments of the chunk per lane
+        u32x4_t kraw[NK];
+        {
+            uint32_t ka[NK];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) ka[tt * KS + ks] = sp + lk[tt][ks];
+            if constexpr (NK == 8) lds_read_b128_x8(kraw, ka);
+            else lds_read_b128_x4(kraw, ka);
+        }
+        bf16x8_t kf[2][KS];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) kf[tt][ks] = __builtin_bit_cast(bf16x8_t, kraw[tt * KS + ks]);
+        f32x4_t s[2][2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[tt][ks], qf[rt][ks], acc, 0, 0, 0);
+                s[rt][tt] = acc;
+            }
+        // V reads go out while the score MFMAs run
+        uint4 vr[8];
+        {
+            uint32_t va[8];
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) va[jj] = sp + lv[jj];
+            if constexpr (NT == 8) {
+                u32x4_t t4[8];
+                lds_read_b128_x8(t4, va);
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) vr[jj] = make_uint4(t4[jj].x, t4[jj].y, t4[jj].z, t4[jj].w);
+            } else {
+                u32x2_t t2[8];
+                lds_read_b64_x8(t2, va);
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) vr[jj] = make_uint4(t2[jj].x, t2[jj].y, 0u, 0u);
+            }
+        }
+        if (t0 + kChunk > P) {
+            // chunk reaches the tree slots: a token is visible if it is in the prefix or is
+            // an ancestor-or-self of the row's node.  Over the sequence of 32-bit words
+            // (all ones, mask bits 0-31, 32-63, 64-95, 96-127) -- i.e. prefix tokens read as
+            // visible -- the chunk's 32 visibility bits start at bit e = t0 - P + 32 (>= 1).
+            const int e = t0 - P + 32;
+            const int qw = e >> 5, sh = e & 31;                       // wave-uniform
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                const uint32_t w0 = static_cast<uint32_t>(mlo[rt]), w1 = static_cast<uint32_t>(mlo[rt] >> 32);
+                const uint32_t w2 = static_cast<uint32_t>(mhi[rt]), w3 = static_cast<uint32_t>(mhi[rt] >> 32);
+                const uint32_t lo = qw == 0 ? 0xFFFFFFFFu : qw == 1 ? w0 : qw == 2 ? w1 : qw == 3 ? w2 : w3;
+                const uint32_t hi = qw == 0 ? w0 : qw == 1 ? w1 : qw == 2 ? w2 : qw == 3 ? w3 : 0u;
+                const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, sh) >> (G * 4);
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        s[rt][tt][i] = ((win >> (tt * 16 + i)) & 1u) ? s[rt][tt][i] : -INFINITY;
+            }
+        }
+        bf16x8_t pb[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            if (first_pass) {
+                float cm = fmaxf(fmaxf(fmaxf(s[rt][0][0], s[rt][0][1]), fmaxf(s[rt][0][2], s[rt][0][3])),
+                                 fmaxf(fmaxf(s[rt][1][0], s[rt][1][1]), fmaxf(s[rt][1][2], s[rt][1][3])));
+                cm = xor32_max(xor16_max(cm));
+                mtrue[rt] = fmaxf(mtrue[rt], cm);
+                if (mref[rt] == -INFINITY) mref[rt] = cm;
+                overflow |= (cm - mref[rt]) * cs > kOverflow;
+            }
+            const float mr = mref[rt] == -INFINITY ? 0.f : mref[rt] * cs;
+            float lsum = 0.f;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rt][tt][i], cs, -mr));
+                    pb[rt][tt * 4 + i] = static_cast<__bf16>(pe);
+                    lsum += pe;
+                }
+            lrow[rt] += lsum;
+        }
+        // O^T += V^T P^T; A operand of dim tile nt = (vr[0][nt], ..., vr[7][nt])
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            uint32_t a4[4];
+            const uint32_t sel = (nt & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                const uint4 x4 = vr[2 * f], y4 = vr[2 * f + 1];
+                const int e = nt >> 1;
+                const uint32_t x = e == 0 ? x4.x : e == 1 ? x4.y : e == 2 ? x4.z : x4.w;
+                const uint32_t y = e == 0 ? y4.x : e == 1 ? y4.y : e == 2 ? y4.z : y4.w;
+                a4[f] = __builtin_amdgcn_perm(y, x, sel);
+            }
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(a4[0], a4[1], a4[2], a4[3]));
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+                oacc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rt], oacc[rt][nt], 0, 0, 0);
+        }
+    };
+
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) { mref[rt] = -INFINITY; mtrue[rt] = -INFINITY; }
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            lrow[rt] = 0.f;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) oacc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        if (pass > 0) {
+            issue_round(0, ring0);
+            issue_round(1, ring1);
+        }
+        // Round r: wait until this wave's DMA of round r has landed (round r + 1 may still
+        // be in flight), barrier so every wave's share is visible, compute, barrier so no
+        // wave still reads the half, then refill it with round r + 2.  The barriers carry
+        // no memory fence on purpose: a fence would wait for all DMA in flight.
+        auto run_round = [&](int r, char *half) {
+            if (r + 1 < nrounds) __builtin_amdgcn_s_waitcnt(kVmcntRound<RS::kRound * RS::kDmaPerWave>());
+            else __builtin_amdgcn_s_waitcnt(kVmcntZero);
+            __builtin_amdgcn_s_barrier();
+            if (wave_live) {
+#pragma unroll
+                for (int j = 0; j < RS::kRound; ++j) {
+                    const int k = r * RS::kRound + j;
+                    if (k < nk && (k % WT) == wt) compute_chunk(lds_addr(half) + j * RS::kSlotBytes, c_begin + k);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
+            __builtin_amdgcn_s_barrier();
+            if (r + 2 < nrounds) issue_round(r + 2, half);
+        };
+        for (int r = 0; r < nrounds; r += 2) {
+            run_round(r, ring0);
+            if (r + 1 < nrounds) run_round(r + 1, ring1);
+        }
+        __builtin_amdgcn_s_waitcnt(kVmcntZero);   // nothing may land in LDS after this
+        // the decision is the workgroup's: every wave must take the same number of passes,
+        // since the passes contain barriers
+        if (!__syncthreads_or(overflow ? 1 : 0)) break;
+        // rare: some score outgrew its reference; redo the split against the exact maxima
+        first_pass = false;
+        overflow = false;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) mref[rt] = mtrue[rt];
+    }
+    __syncthreads();
+    float mrow[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        mrow[rt] = mref[rt];
+        // row sums: each of the four lanes of a row holds a partial sum
+        auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(lrow[rt]), __float_as_uint(lrow[rt]), false, false);
+        const float l16 = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+        auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(l16), __float_as_uint(l16), false, false);
+        lrow[rt] = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+    }
+    // from here on the running maxima are in base-2 units, as the merge steps expect
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) mrow[rt] = mrow[rt] == -INFINITY ? -INFINITY : mrow[rt] * cs;
+
+    if constexpr (WT > 1) {
+        // ---- the WT waves share the same 32 rows: every wave parks its (m, l, O) in the
+        // idle ring, then wave wt combines rows wt*8 .. wt*8+7 of all four in a fixed order
+        // and writes them (lane: row wt*8 + lane/8, dims (lane%8)*D/8 .. +D/8).  O rows sit
+        // kOS floats apart so the parked writes are free of bank conflicts.
+        static_assert(WT == kWaves && WR == 1, "one row group per workgroup");
+        constexpr int kOS = D + 4;
+        constexpr int kPark = kRowsPerWave * kOS;                  // floats per parked wave
+        static_assert(2 * kPark * 4 + WT * kRowsPerWave * 2 * 4 <= (int)sizeof(ring1), "park area");
+        auto parked = [&](int w) { return reinterpret_cast<float *>(w < 2 ? ring0 : ring1) + (w & 1) * kPark; };
+        float *ml = reinterpret_cast<float *>(ring1) + 2 * kPark;    // [WT][32 rows][m, l]
+        {
+            float *o = parked(wt);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                const int rr = rt * 16 + c16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float4 x0, x1;
+                    x0.x = oacc[rt][0][i]; x0.y = oacc[rt][1 % NT][i]; x0.z = oacc[rt][2 % NT][i]; x0.w = oacc[rt][3 % NT][i];
+                    *reinterpret_cast<float4 *>(o + rr * kOS + (G * 4 + i) * NT) = x0;
+                    if constexpr (NT == 8) {
+                        x1.x = oacc[rt][4][i]; x1.y = oacc[rt][5][i]; x1.z = oacc[rt][6][i]; x1.w = oacc[rt][7][i];
+                        *reinterpret_cast<float4 *>(o + rr * kOS + (G * 4 + i) * NT + 4) = x1;
+                    }
+                }
+                if (G == 0) *reinterpret_cast<float2 *>(ml + (wt * kRowsPerWave + rr) * 2) = make_float2(mrow[rt], lrow[rt]);
+            }
+        }
+        __syncthreads();
+        constexpr int DL = D / 8;                                  // dims per lane
+        const int rr = wt * 8 + (lane >> 3), d0 = (lane & 7) * DL;
+        float mw[WT], lw[WT], mt = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < WT; ++w) {
+            const float2 x = *reinterpret_cast<const float2 *>(ml + (w * kRowsPerWave + rr) * 2);
+            mw[w] = x.x; lw[w] = x.y;
+            mt = fmaxf(mt, x.x);
+        }
+        const float mref2 = mt == -INFINITY ? 0.f : mt;
+        float sc[WT], lt = 0.f;
+#pragma unroll
+        for (int w = 0; w < WT; ++w) { sc[w] = __builtin_amdgcn_exp2f(mw[w] - mref2); lt += sc[w] * lw[w]; }
+        float acc[DL];
+#pragma unroll
+        for (int e = 0; e < DL; ++e) acc[e] = 0.f;
+#pragma unroll
+        for (int w = 0; w < WT; ++w) {
+            const float *src = parked(w) + rr * kOS + d0;
+#pragma unroll
+            for (int e = 0; e < DL; e += 4) {
+                const float4 x = *reinterpret_cast<const float4 *>(src + e);
+                acc[e] += sc[w] * x.x; acc[e + 1] += sc[w] * x.y; acc[e + 2] += sc[w] * x.z; acc[e + 3] += sc[w] * x.w;
+            }
+        }
+        if (splits > 1) {
+            // ---- split-KV: publish this split's partial (m, l, unnormalised O); the merge
+            // kernel that follows on the stream combines the splits in a fixed order
+            const int64_t unit = static_cast<int64_t>(pair) * nb + rbk;
+            const int64_t base = (unit * splits + split) * RB;
+            float *o = ws_o + (base + rr) * D + d0;
+#pragma unroll
+            for (int e = 0; e < DL; e += 4) *reinterpret_cast<float4 *>(o + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+            if ((lane & 7) == 0) *reinterpret_cast<float2 *>(ws_stats + (base + rr) * 2) = make_float2(mt, lt);
+            return;
+        }
+        const int r = row0 + rr;
+        if (r >= M_max * g) return;
+        const int j = r / g + 1, gi = r % g;
+        const bool live = r < Rh && depth[static_cast<int64_t>(b) * R + j] >= 1;
+        const float inv = live && lt > 0.f ? 1.f / lt : 0.f;
+        uint16_t *o = out + b * os0 + static_cast<int64_t>(j - 1) * os1 + static_cast<int64_t>(kvh * g + gi) * os2 + d0;
+#pragma unroll
+        for (int e = 0; e < DL; e += 8) {
+            uint32_t w4[4];
+#pragma unroll
+            for (int h2 = 0; h2 < 4; ++h2) {
+                const float x0 = live ? acc[e + 2 * h2] * inv : 0.f, x1 = live ? acc[e + 2 * h2 + 1] * inv : 0.f;
+                w4[h2] = static_cast<uint32_t>(tmv::f32_to_bf16(x0)) | (static_cast<uint32_t>(tmv::f32_to_bf16(x1)) << 16);
+            }
+            *reinterpret_cast<uint4 *>(o + e) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        }
+        return;
+    } else {
+    // ---- split-KV: publish this split's partial (m, l, unnormalised O) and stop; the
+    // merge kernel that follows on the stream combines the splits in a fixed order
+    if (splits > 1) {
+        if (wt != 0) return;
+        const int64_t unit = static_cast<int64_t>(pair) * nb + rbk;          // (pair, row block)
+        const int64_t base = (unit * splits + split) * RB + wr * kRowsPerWave;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const int rr = rt * 16 + c16;
+            float *o = ws_o + (base + rr) * D + G * DG;
+#pragma unroll
+            for (int e = 0; e < DG; e += 4) {
+                float4 v4;
+                v4.x = oacc[rt][(e + 0) % NT][(e + 0) / NT];
+                v4.y = oacc[rt][(e + 1) % NT][(e + 1) / NT];
+                v4.z = oacc[rt][(e + 2) % NT][(e + 2) / NT];
+                v4.w = oacc[rt][(e + 3) % NT][(e + 3) / NT];
+                *reinterpret_cast<float4 *>(o + e) = v4;
+            }
+            if (G == 0) *reinterpret_cast<float2 *>(ws_stats + (base + rr) * 2) = make_float2(mrow[rt], lrow[rt]);
+        }
+        return;
+    }
+    if (wt != 0) return;
+
+    // ---- write the final rows: lane writes dims G*DG .. +DG of its row in each tile
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        const int r = row0 + rt * 16 + c16;
+        if (r >= M_max * g) continue;
+        const int j = r / g + 1, gi = r % g;
+        const bool live = r < Rh && depth[static_cast<int64_t>(b) * R + j] >= 1;
+        const float inv = live && lrow[rt] > 0.f ? 1.f / lrow[rt] : 0.f;
+        uint16_t *o = out + b * os0 + static_cast<int64_t>(j - 1) * os1 + static_cast<int64_t>(kvh * g + gi) * os2 + G * DG;
+#pragma unroll
+        for (int e = 0; e < DG; e += 8) {
+            uint32_t w4[4];
+#pragma unroll
+            for (int h2 = 0; h2 < 4; ++h2) {
+                // dims e + 2*h2, e + 2*h2 + 1 of this lane's slice: (i, nt) = (dim / NT, dim % NT)
+                const int d0 = e + 2 * h2, d1 = d0 + 1;
+                const float x0 = live ? oacc[rt][d0 % NT][d0 / NT] * inv : 0.f;
+                const float x1 = live ? oacc[rt][d1 % NT][d1 / NT] * inv : 0.f;
+                w4[h2] = static_cast<uint32_t>(tmv::f32_to_bf16(x0)) | (static_cast<uint32_t>(tmv::f32_to_bf16(x1)) << 16);
+            }
+            *reinterpret_cast<uint4 *>(o + e) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        }
+    }
+    }
+}
+
 // --------------------------------------------------------------------------- split merge
 // One thread per (row, 8 head dims) of every live row block: reads the S partials of its
 // row in split order, rescales them to the common maximum and writes the bf16 row; rows
@@ -676,11 +1278,23 @@ void launch_bf16(const AttnPlan &p, hipStream_t s, int M_max, int D_max, int Hq,
 {
     char *w = static_cast<char *>(ws);
     float *stats = reinterpret_cast<float *>(w), *part = reinterpret_cast<float *>(w + off_o);
-    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, WR>), dim3(p.slots * tmv::kXcds), dim3(kWaves * kWave), 0, s,
-                       M_max, D_max, Hq, Hkv, static_cast<const uint16_t *>(q), qs[0], qs[1], qs[2],
-                       static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), kvs[0], kvs[1], kvs[2],
-                       L_cap, P, n, anc, dep, status, scale * kLog2e, static_cast<uint16_t *>(out), os[0], os[1],
-                       os[2], stats, part, p.pairs, p.nb, p.splits, p.per_pair);
+#define TMV_LAUNCH_ATTN(DEEP)                                                                              \
+    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, WR, DEEP>), dim3(p.slots * tmv::kXcds), dim3(kWaves * kWave), 0, s, \
+                       M_max, D_max, Hq, Hkv, static_cast<const uint16_t *>(q), qs[0], qs[1], qs[2],             \
+                       static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), kvs[0], kvs[1], kvs[2], \
+                       L_cap, P, n, anc, dep, status, scale * kLog2e, static_cast<uint16_t *>(out), os[0], os[1], \
+                       os[2], stats, part, p.pairs, p.nb, p.splits, p.per_pair)
+    if constexpr (D == 64) {
+        hipLaunchKernelGGL((tree_attn_bf16_stream_kernel<D, WR>), dim3(p.slots * tmv::kXcds), dim3(kWaves * kWave), 0,
+                           s, M_max, D_max, Hq, Hkv, static_cast<const uint16_t *>(q), qs[0], qs[1], qs[2],
+                           static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), kvs[0], kvs[1],
+                           kvs[2], L_cap, P, n, anc, dep, status, scale * kLog2e, static_cast<uint16_t *>(out),
+                           os[0], os[1], os[2], stats, part, p.pairs, p.nb, p.splits, p.per_pair);
+    } else {
+        if (D_max + 1 > kAncBatch) TMV_LAUNCH_ATTN(true);
+        else TMV_LAUNCH_ATTN(false);
+    }
+#undef TMV_LAUNCH_ATTN
     if (p.splits > 1) {
         constexpr int RB = WR * kRowsPerWave;
         const int64_t threads = static_cast<int64_t>(p.pairs) * p.nb * RB * (D / 8);

@@ -21,6 +21,8 @@ def flags():
             "-Wall", "-Wno-unused-function",
             # packed fp32 arithmetic stays off (hipcc -O3 would form v_pk_* from plain code)
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # the first kernel arguments arrive in SGPRs instead of through a dependent load
+            "-mllvm", "-amdgpu-kernarg-preload-count=16",
             "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
 
 

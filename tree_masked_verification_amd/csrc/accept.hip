@@ -22,7 +22,7 @@ using tmv::u128;
 
 // ============================================================== greedy
 constexpr int kScanThreads = 256;
-constexpr int kScanChunk = 8192;          // vocabulary entries per workgroup
+constexpr int kScanChunk = 4096;          // vocabulary entries per workgroup (four 16-byte loads per thread)
 constexpr uint64_t kNanKey = ~0ull;       // a chunk with a NaN reports the all-ones key
 
 __device__ __forceinline__ uint32_t order_bits(float v) {
@@ -48,11 +48,12 @@ greedy_scan_kernel(int M_max, int V, int nchunk, const void *__restrict__ teache
     const int u = (blockIdx.x / nchunk) % R;
     const int b = blockIdx.x / (nchunk * R);
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
-    // the three words that decide whether this row is scanned are fetched together
+    // The row's loads go out before the words that decide whether the row is live have
+    // returned: every (b, u, chunk) of the grid addresses the teacher tensor in bounds, so
+    // a dead row only costs bandwidth, and a live one saves a round trip.
     const int M = n_nodes[b];
     const int st = status[b];
     const int dp = u > 0 ? depth[static_cast<int64_t>(b) * R + u] : 1;
-    if (st != TMV_OK || M < 0 || M > M_max || u > M || dp < 1) return;
 
     const int x0 = chunk * kScanChunk;
     const int x1 = min(V, x0 + kScanChunk);
@@ -62,11 +63,11 @@ greedy_scan_kernel(int M_max, int V, int nchunk, const void *__restrict__ teache
         const float *row = static_cast<const float *>(teacher) + b * sb + static_cast<int64_t>(u) * sr;
         constexpr int kPer = kScanChunk / (4 * kScanThreads);        // float4 per thread
         if (x1 - x0 == kScanChunk && ((reinterpret_cast<uintptr_t>(row + x0) & 15u) == 0)) {
-            // full aligned chunk: issue every 16-byte load before consuming any
             const float4 *r4 = reinterpret_cast<const float4 *>(row + x0);
             float4 f[kPer];
 #pragma unroll
             for (int i = 0; i < kPer; ++i) f[i] = r4[tid + i * kScanThreads];
+            if (st != TMV_OK || M < 0 || M > M_max || u > M || dp < 1) return;
 #pragma unroll
             for (int i = 0; i < kPer; ++i) {
                 const int x = x0 + 4 * (tid + i * kScanThreads);
@@ -76,11 +77,32 @@ greedy_scan_kernel(int M_max, int V, int nchunk, const void *__restrict__ teache
                 scan_one(f[i].w, x + 3, best, nan);
             }
         } else {
+            if (st != TMV_OK || M < 0 || M > M_max || u > M || dp < 1) return;
             for (int x = x0 + tid; x < x1; x += kScanThreads) scan_one(row[x], x, best, nan);
         }
     } else {
         const uint16_t *row = static_cast<const uint16_t *>(teacher) + b * sb + static_cast<int64_t>(u) * sr;
-        for (int x = x0 + tid; x < x1; x += kScanThreads) scan_one(tmv::bf16_to_f32(row[x]), x, best, nan);
+        constexpr int kPer = kScanChunk / (8 * kScanThreads);        // 8 bf16 per thread and load
+        if (x1 - x0 == kScanChunk && ((reinterpret_cast<uintptr_t>(row + x0) & 15u) == 0)) {
+            const uint4 *r8 = reinterpret_cast<const uint4 *>(row + x0);
+            uint4 h[kPer];
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) h[i] = r8[tid + i * kScanThreads];
+            if (st != TMV_OK || M < 0 || M > M_max || u > M || dp < 1) return;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int x = x0 + 8 * (tid + i * kScanThreads);
+                const uint32_t w[4] = {h[i].x, h[i].y, h[i].z, h[i].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    scan_one(__uint_as_float(w[e] << 16), x + 2 * e, best, nan);
+                    scan_one(__uint_as_float(w[e] & 0xffff0000u), x + 2 * e + 1, best, nan);
+                }
+            }
+        } else {
+            if (st != TMV_OK || M < 0 || M > M_max || u > M || dp < 1) return;
+            for (int x = x0 + tid; x < x1; x += kScanThreads) scan_one(tmv::bf16_to_f32(row[x]), x, best, nan);
+        }
     }
     if (nan) best = kNanKey;
     best = tmv::wave_max_u64(best);
@@ -102,7 +124,7 @@ greedy_select_kernel(int M_max, int D_max, int V, int nchunk, const int32_t *__r
                      int32_t *__restrict__ accept_len, int32_t *__restrict__ path,
                      int32_t *__restrict__ next_token, const uint64_t *__restrict__ keys)
 {
-    constexpr int kKeyBatch = 16;                  // chunk keys per row fetched at once
+    constexpr int kKeyBatch = 32;                  // chunk keys per row fetched at once
     constexpr int kAncBatch = 8;                   // ancestor entries per node fetched at once
     __shared__ int32_t tsel[129], tok_sh[129];
     __shared__ int bad;

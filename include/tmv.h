@@ -15,9 +15,11 @@
  *   - Every pointer argument is DEVICE memory owned by the caller (for example a torch
  *     tensor's data_ptr), except the small int64 stride arrays, which are HOST arrays read
  *     during the call.  The library keeps no global state and allocates nothing; scratch
- *     memory comes from a caller workspace whose size the *_workspace call returns.  A
- *     workspace needs no initialisation and holds nothing between calls; calls that may
- *     run at the same time (different streams) must not share one.
+ *     memory comes from a caller workspace whose size the *_workspace call returns.  The
+ *     accept workspace needs no initialisation; the attention workspace must be
+ *     zero-filled once before its first use and every call leaves it ready for the next
+ *     (see tmv_tree_verify_attention).  Calls that may run at the same time (different
+ *     streams) must not share a workspace.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are asynchronous; none
  *     synchronises the host.
  *   - The return value reports problems the host can see (TMV_ERR_ARG: bad sizes, null
@@ -124,8 +126,12 @@ int tmv_tree_build_ancestors(int B, int M_max, int D_max, int parent_format,
  *             in a failed sequence) are written as 0.
  *   GQA: query head h reads KV head h / (Hq/Hkv).  Requires Hq % Hkv == 0, d in {64,128},
  *        Hq/Hkv <= 16, 1 <= L_cap.
- *   workspace: tmv_tree_verify_attention_workspace() bytes (split-KV partials), 16-byte
- *        aligned.
+ *   workspace: tmv_tree_verify_attention_workspace() bytes, 16-byte aligned.  It opens
+ *        with a fixed 1 KiB block of arrival counters (one per split row block; the last
+ *        split of a block to finish merges it) followed by the split-KV partials, which
+ *        every call rewrites.  The counter block must be zero before the first call and
+ *        every completed call leaves it zero, so zero-fill a new workspace once; it then
+ *        stays valid for calls of any shape whose size it covers.
  */
 size_t tmv_tree_verify_attention_workspace(int dtype, int B, int M_max, int Hq, int Hkv,
                                            int d, int L_cap);

@@ -190,23 +190,49 @@ def test_attention_determinism():
         assert np.array_equal(host_bits(dev.out), first)
 
 
-def test_workspace_contents_do_not_matter():
-    _case("attention + greedy: workspaces full of garbage")
+def test_workspace_reuse_across_calls_and_shapes():
+    _case("attention: zero-filled workspace reused across shapes; greedy: garbage workspace")
     import tree_masked_verification_amd as tmv
     w = ti.workload(2)
     dev = DeviceStep(w)
     dev.build()
-    dev.attention()
+    n_attn = tmv.tree_verify_attention_workspace(tmv.BF16, w.B, w.M_max, w.Hq, w.Hkv, w.d, w.L_cap)
+    small = small_attention_workload(207, 3, 8, 2, 128, 37, [700, 33, 5], [37, 20, 1], q_scale=4.0)
+    n_small = tmv.tree_verify_attention_workspace(tmv.BF16, small.B, small.M_max, small.Hq, small.Hkv, small.d,
+                                                  small.L_cap)
+    wa = torch.zeros(max(n_attn, n_small), dtype=torch.uint8, device="cuda")
+    dev.attention(workspace=wa)
     dev.accept()
     ref_out = host_bits(dev.out).copy()
     ref_acc = [host_bits(t).copy() for t in (dev.accept_len, dev.path, dev.next_token)]
-    n_attn = tmv.tree_verify_attention_workspace(tmv.BF16, w.B, w.M_max, w.Hq, w.Hkv, w.d, w.L_cap)
+    # a different split plan on the same workspace, then the first shape again: the
+    # arrival counters must have come back to zero after every call
+    ds = DeviceStep(small)
+    ds.build()
+    for _ in range(2):
+        ds.attention(workspace=wa)
+    torch.cuda.synchronize()
+    s1 = host_bits(ds.out).copy()
     n_acc = tmv.tree_accept_workspace(tmv.ACCEPT_GREEDY, w.B, w.M_max, w.V)
     for fill in (0xFF, 0x7F, 0x00):
-        wa = torch.full((n_attn,), fill, dtype=torch.uint8, device="cuda")
         wc = torch.full((n_acc,), fill, dtype=torch.uint8, device="cuda")
         dev.out.fill_(float("nan"))
         dev.attention(workspace=wa)
         dev.accept(workspace=wc)
         assert np.array_equal(host_bits(dev.out), ref_out)
         assert all(np.array_equal(host_bits(t), r) for t, r in zip((dev.accept_len, dev.path, dev.next_token), ref_acc))
+        ds.out.fill_(float("nan"))
+        ds.attention(workspace=wa)
+        assert np.array_equal(host_bits(ds.out), s1)
+
+
+@pytest.mark.parametrize("plan", ["1:1", "1:3", "2:1", "2:4", "2:8", "4:1", "4:6"])
+def test_attention_launch_plans(ref, plan, monkeypatch):
+    # every launch plan (row-group width : token splits) must give the same rows: the
+    # split merge, the row-group combine and the per-wave chunk assignment all change
+    _case("attention: 8B-shaped layer under plan %s" % plan)
+    monkeypatch.setenv("TMV_ATTN_PLAN", plan)
+    w = ti.workload(2)
+    _attention_parity(ref, w, 2e-2, 1e-2)
+    w3 = small_attention_workload(208, 3, 8, 2, 128, 37, [700, 33, 5], [37, 20, 1], q_scale=4.0)
+    _attention_parity(ref, w3, 2e-2, 1e-2)

@@ -198,7 +198,8 @@ def kv_commit_path(k_cache, v_cache, prefix_len, n_nodes, accept_len, path, stat
 
 
 class Workspaces:
-    """Workspaces cached by size and device (their contents never matter between calls)."""
+    """Workspaces cached by size and device, zero-filled when created (the attention
+    workspace's arrival counters must start at zero; every call leaves them at zero)."""
 
     def __init__(self):
         self._cache = {}

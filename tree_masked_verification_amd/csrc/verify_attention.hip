@@ -54,6 +54,8 @@ constexpr int kVmcntRound() {
     return (N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14);
 }
 constexpr int kVmcntZero = kVmcntRound<0>();
+// s_getreg operand for bits 3:0 of HW_REG_XCC_ID (register 20): the XCD running the wave
+constexpr int kHwRegXccId = 20 | (0 << 6) | (3 << 11);
 // s_waitcnt immediate that waits for LDS / scalar-memory count 0 only
 constexpr int kLgkmcntZero = 0xF | (0x7 << 4) | (0x3 << 14);
 
@@ -84,15 +86,57 @@ __device__ __forceinline__ void lds_read_b128_x8(u32x4_t (&v)[8], const uint32_t
                  : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
                  : "memory");
 }
-__device__ __forceinline__ void lds_read_b64_x8(u32x2_t (&v)[8], const uint32_t (&a)[8]) {
-    asm volatile("ds_read_b64 %0, %8\n\tds_read_b64 %1, %9\n\tds_read_b64 %2, %10\n\tds_read_b64 %3, %11\n\t"
-                 "ds_read_b64 %4, %12\n\tds_read_b64 %5, %13\n\tds_read_b64 %6, %14\n\tds_read_b64 %7, %15\n\t"
+// V^T operand reads with the gfx950 transposing LDS load: within each 16-lane group, lane
+// s supplies 4 consecutive bf16 at its address and receives element s%4 of the groups
+// supplied by lanes s/4, s/4 + 4, s/4 + 8, s/4 + 12.  With lane s reading row T[s/4] at
+// dims 4*(s%4) .. +3 of a 16-dim tile, lane s ends up with dim s of rows T[0..3] -- one
+// column of V, as the MFMA A operand wants.  v[2*nt + h]: dim tile nt, token half h; the
+// tile's address is the lane's half base z_h with 32*nt XORed in (the swizzle of the V
+// rows only permutes 32-byte dim groups, so tiles stay XOR-addressable).
+__device__ __forceinline__ void lds_read_vt(u32x2_t (&v)[16], uint32_t z0, uint32_t z1) {
+    uint32_t t0, t1;
+    asm volatile("ds_read_b64_tr_b16 %0, %18\n\t"
+                 "ds_read_b64_tr_b16 %1, %19\n\t"
+                 "v_xor_b32 %16, 0x20, %18\n\t"
+                 "ds_read_b64_tr_b16 %2, %16\n\t"
+                 "v_xor_b32 %17, 0x20, %19\n\t"
+                 "ds_read_b64_tr_b16 %3, %17\n\t"
+                 "v_xor_b32 %16, 0x40, %18\n\t"
+                 "ds_read_b64_tr_b16 %4, %16\n\t"
+                 "v_xor_b32 %17, 0x40, %19\n\t"
+                 "ds_read_b64_tr_b16 %5, %17\n\t"
+                 "v_xor_b32 %16, 0x60, %18\n\t"
+                 "ds_read_b64_tr_b16 %6, %16\n\t"
+                 "v_xor_b32 %17, 0x60, %19\n\t"
+                 "ds_read_b64_tr_b16 %7, %17\n\t"
+                 "v_xor_b32 %16, 0x80, %18\n\t"
+                 "ds_read_b64_tr_b16 %8, %16\n\t"
+                 "v_xor_b32 %17, 0x80, %19\n\t"
+                 "ds_read_b64_tr_b16 %9, %17\n\t"
+                 "v_xor_b32 %16, 0xa0, %18\n\t"
+                 "ds_read_b64_tr_b16 %10, %16\n\t"
+                 "v_xor_b32 %17, 0xa0, %19\n\t"
+                 "ds_read_b64_tr_b16 %11, %17\n\t"
+                 "v_xor_b32 %16, 0xc0, %18\n\t"
+                 "ds_read_b64_tr_b16 %12, %16\n\t"
+                 "v_xor_b32 %17, 0xc0, %19\n\t"
+                 "ds_read_b64_tr_b16 %13, %17\n\t"
+                 "v_xor_b32 %16, 0xe0, %18\n\t"
+                 "ds_read_b64_tr_b16 %14, %16\n\t"
+                 "v_xor_b32 %17, 0xe0, %19\n\t"
+                 "ds_read_b64_tr_b16 %15, %17\n\t"
                  "s_waitcnt lgkmcnt(0)"
                  : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]),
-                   "=&v"(v[7])
-                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+                   "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]),
+                   "=&v"(v[14]), "=&v"(v[15]), "=&v"(t0), "=&v"(t1)
+                 : "v"(z0), "v"(z1)
                  : "memory");
 }
+// the XCD (accelerator complex die) this wave runs on
+__device__ __forceinline__ int xcc_id() { return __builtin_amdgcn_s_getreg(kHwRegXccId) & 0xf; }
+// drop this CU's vector L1 lines so later loads read the XCD's L2
+__device__ __forceinline__ void l1_invalidate() { asm volatile("buffer_inv sc0" ::: "memory"); }
+
 // buffer -> LDS copy of 16 bytes per lane: lane l's bytes land at lds + 16*l; a voffset
 // past the descriptor's records writes zeros and reads nothing
 __device__ __forceinline__ void dma_to_lds16(__amdgpu_buffer_rsrc_t r, char *lds, uint32_t voffset) {
@@ -116,14 +160,18 @@ struct AttnPlan {
     int slots;     // workgroups per XCD (ceil(pairs / 8) * per_pair)
 };
 
-AttnPlan make_plan(int B, int M_max, int Hq, int Hkv, int L_cap) {
+// split-KV row blocks (pairs x row blocks) are limited to the counter block's size
+constexpr int kMaxSplitUnits = 256;
+constexpr size_t kCounterBytes = kMaxSplitUnits * sizeof(int32_t);
+
+AttnPlan make_plan(int B, int M_max, int Hq, int Hkv, int L_cap, int d) {
     AttnPlan p;
     const int g = Hq / Hkv;
     const int rows = M_max * g;
     p.wr = rows >= 256 ? 4 : 1;
     int forced_wr = 0, forced_s = 0;
     if (const char *e = std::getenv("TMV_ATTN_PLAN")) std::sscanf(e, "%d:%d", &forced_wr, &forced_s);
-    if (forced_wr == 1 || forced_wr == 4) p.wr = forced_wr;
+    if (forced_wr == 1 || forced_wr == 4 || (forced_wr == 2 && d == 128)) p.wr = forced_wr;
     p.rb = p.wr * kRowsPerWave;
     p.nb = rows > 0 ? (rows + p.rb - 1) / p.rb : 0;
     p.pairs = B * Hkv;
@@ -135,20 +183,28 @@ AttnPlan make_plan(int B, int M_max, int Hq, int Hkv, int L_cap) {
     if (s > 16) s = 16;
     if (s < 1) s = 1;
     if (forced_s >= 1 && forced_s <= 16) s = forced_s;
+    if (base >= kMaxSplitUnits) s = 1;
     p.splits = s;
     p.per_pair = p.nb * p.splits;
     p.slots = ((p.pairs + tmv::kXcds - 1) / tmv::kXcds) * p.per_pair;
     return p;
 }
 
-// workspace layout (split-KV only): [stats: pairs*nb*S*rb*2 f32][partial O: pairs*nb*S*rb*d f32]
-size_t plan_bytes(const AttnPlan &p, int d, size_t *off_o) {
+// workspace layout: [arrival counters: kMaxSplitUnits int32][stats: pairs*nb*S*rb*2 f32]
+// [partial O: pairs*nb*S*rb*d f32] (the last two only with split-KV).  The counter block
+// sits at the same place for every shape and nothing else is ever written there: it must
+// be zero before the first call, and every call leaves the counters it used at zero, so a
+// zero-filled workspace stays valid across calls of any shape it is large enough for.
+// Split-KV is only planned for fewer than kMaxSplitUnits row blocks (with that many, one
+// split per block already fills the chip).
+size_t plan_bytes(const AttnPlan &p, int d, size_t *off_o, size_t *off_stats = nullptr) {
     const size_t units = static_cast<size_t>(p.pairs) * p.nb * p.splits * p.rb;
     size_t st = p.splits > 1 ? units * 2 * sizeof(float) : 0;
     st = (st + 255) / 256 * 256;
     const size_t o = p.splits > 1 ? units * d * sizeof(float) : 0;
-    if (off_o) *off_o = st;
-    return st + o < 256 ? 256 : st + o;
+    if (off_stats) *off_stats = kCounterBytes;
+    if (off_o) *off_o = kCounterBytes + st;
+    return kCounterBytes + st + o;
 }
 
 __device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t *p) {
@@ -157,6 +213,90 @@ __device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t *p) {
 
 __device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
 __device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+
+// --------------------------------------------------------------------------- split merge
+// Row rr, dims part*8 .. +8 of split-KV unit `unit`: the S partials (m, l, unnormalised O)
+// are read in split order, rescaled to the common maximum and written as the bf16 row;
+// rows of inert nodes (and whole failed sequences) are written as 0.
+template <int D, int RB>
+__device__ __forceinline__ void merge_row_part(int64_t unit, int rr, int part, int splits, int b, int kvh, int g,
+                                               int r, int M_max, int L_cap, int M, int P, int st,
+                                               const int32_t *__restrict__ depth, uint16_t *__restrict__ out,
+                                               int64_t os0, int64_t os1, int64_t os2,
+                                               const float *__restrict__ ws_stats, const float *__restrict__ ws_o)
+{
+    if (r >= M_max * g) return;
+    const int j = r / g + 1, gi = r % g;
+    const int dp = depth[static_cast<int64_t>(b) * (M_max + 1) + j];
+    // every split's (m, l) and O slice are fetched before any is consumed
+    constexpr int kMaxSplits = 16;
+    float2 ml[kMaxSplits];
+    float4 oa[kMaxSplits], ob[kMaxSplits];
+#pragma unroll
+    for (int s2 = 0; s2 < kMaxSplits; ++s2) {
+        if (s2 < splits) {
+            const int64_t base = (unit * splits + s2) * RB + rr;
+            ml[s2] = *reinterpret_cast<const float2 *>(ws_stats + base * 2);
+            const float4 *o = reinterpret_cast<const float4 *>(ws_o + base * D + part * 8);
+            oa[s2] = o[0];
+            ob[s2] = o[1];
+        }
+    }
+    const bool seq_ok = st == TMV_OK && M >= 0 && M <= M_max && P >= 0 && static_cast<int64_t>(P) + M <= L_cap;
+    const bool live = seq_ok && r < M * g && dp >= 1;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (live) {
+        float mt = -INFINITY;
+#pragma unroll
+        for (int s2 = 0; s2 < kMaxSplits; ++s2)
+            if (s2 < splits) mt = fmaxf(mt, ml[s2].x);
+        const float mref = mt == -INFINITY ? 0.f : mt;
+        float lt = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < kMaxSplits; ++s2) {
+            if (s2 < splits) {
+                const float sc = __builtin_amdgcn_exp2f(ml[s2].x - mref);
+                lt += sc * ml[s2].y;
+                acc[0] += sc * oa[s2].x; acc[1] += sc * oa[s2].y; acc[2] += sc * oa[s2].z; acc[3] += sc * oa[s2].w;
+                acc[4] += sc * ob[s2].x; acc[5] += sc * ob[s2].y; acc[6] += sc * ob[s2].z; acc[7] += sc * ob[s2].w;
+            }
+        }
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] *= inv;
+    }
+    uint32_t w4[4];
+#pragma unroll
+    for (int h2 = 0; h2 < 4; ++h2)
+        w4[h2] = static_cast<uint32_t>(tmv::f32_to_bf16(acc[2 * h2])) |
+                 (static_cast<uint32_t>(tmv::f32_to_bf16(acc[2 * h2 + 1])) << 16);
+    uint16_t *o = out + b * os0 + static_cast<int64_t>(j - 1) * os1 + static_cast<int64_t>(kvh * g + gi) * os2 + part * 8;
+    *reinterpret_cast<uint4 *>(o) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+}
+
+// One thread per (row, 8 head dims) of every live row block (the register-streaming
+// kernel's split-KV merge, ordered after it on the stream).
+template <int D, int RB>
+__global__ void __launch_bounds__(256)
+tree_attn_merge_kernel(int M_max, int D_max, int Hq, int Hkv, int L_cap,
+                       const int32_t *__restrict__ prefix_len, const int32_t *__restrict__ n_nodes,
+                       const int32_t *__restrict__ depth, const int32_t *__restrict__ status,
+                       uint16_t *__restrict__ out, int64_t os0, int64_t os1, int64_t os2,
+                       const float *__restrict__ ws_stats, const float *__restrict__ ws_o,
+                       int pairs, int nb, int splits)
+{
+    constexpr int TPR = D / 8;                         // threads per row
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t row_global = t / TPR;                // over pairs * nb * RB
+    const int part = static_cast<int>(t % TPR);
+    if (row_global >= static_cast<int64_t>(pairs) * nb * RB) return;
+    const int64_t unit = row_global / RB;
+    const int rr = static_cast<int>(row_global % RB);
+    const int pair = static_cast<int>(unit / nb), rbk = static_cast<int>(unit % nb);
+    const int b = pair / Hkv, kvh = pair % Hkv, g = Hq / Hkv;
+    merge_row_part<D, RB>(unit, rr, part, splits, b, kvh, g, rbk * RB + rr, M_max, L_cap, n_nodes[b], prefix_len[b],
+                          status[b], depth, out, os0, os1, os2, ws_stats, ws_o);
+}
 
 // ------------------------------------------------ bf16 MFMA kernel, register streaming (d64)
 // Each wave streams its own chunks straight from memory into registers; used for head
@@ -610,10 +750,11 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
                       const int32_t *__restrict__ anc, const int32_t *__restrict__ depth,
                       int32_t *__restrict__ status, float qk_scale_log2,
                       uint16_t *__restrict__ out, int64_t os0, int64_t os1, int64_t os2,
-                      float *__restrict__ ws_stats, float *__restrict__ ws_o,
+                      float *__restrict__ ws_stats, float *__restrict__ ws_o, int32_t *__restrict__ ws_cnt,
                       int pairs, int nb, int splits, int per_pair)
 {
     using RS = RingShape<D>;
+    static_assert(D == 128, "the LDS-ring kernel is written for head dimension 128");
     constexpr int KS = D / 32;           // k-steps of the QK^T contraction
     constexpr int NT = D / 16;           // 16-dim output tiles
     constexpr int WT = kWaves / WR;      // waves sharing rows (they split the chunks)
@@ -625,6 +766,7 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
     // for DMA still landing in the other
     __shared__ __attribute__((aligned(16))) char ring0[RS::kRound * RS::kSlotBytes];
     __shared__ __attribute__((aligned(16))) char ring1[RS::kRound * RS::kSlotBytes];
+    __shared__ int s_last;
 
     // ---- decode the workgroup: XCD-major so one (sequence, kv head) stays on one XCD
     const int wg = blockIdx.x;
@@ -674,9 +816,9 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
     const int Rh = (st == TMV_OK) ? M * g : 0;           // live rows of this kv head
 
     if (row0_wg >= Rh) {
-        // no live row in this workgroup: clear the block's output rows (with split-KV the
-        // merge kernel writes every row instead)
-        if (splits == 1 && wt == 0) {
+        // no live row in this workgroup (nor in the other splits of its row block, which
+        // see the same rows): split 0 clears the block's output rows
+        if (split == 0 && wt == 0) {
             for (int rt = 0; rt < 2; ++rt) {
                 const int r = row0 + rt * 16 + c16;
                 if (r >= M_max * g) continue;
@@ -718,7 +860,10 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
         const int ii = wave_v ? i - RS::kDmaPerChunk / 2 : i;
         const int qpos = ii * 64 + lane;                       // 16-byte LDS piece index
         const int t = qpos / PP, pp = qpos % PP;
-        dma_off[jd] = static_cast<uint32_t>(t * row_bytes + ((pp ^ (t % PP)) * 16));
+        // K rows swizzle their 16-byte pieces by t mod 16, V rows by 2t mod 16 (the V^T reads
+        // take four consecutive rows at once; see lds_read_vt)
+        const int sw = wave_v ? (2 * t) % PP : t % PP;
+        dma_off[jd] = static_cast<uint32_t>(t * row_bytes + ((pp ^ sw) * 16));
         dma_lds[jd] = (wave_v ? RS::kMatBytes : 0) + ii * 1024;
     }
     // issue this wave's share of local chunk k into the slot at `slot` (records stop at T,
@@ -780,9 +925,9 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
     }
 
     // LDS read offsets of the MFMA operands inside a slot (constant per lane).  K
-    // fragment (tt, ks): row tt*16 + c16, logical piece ks*4 + G; V row jj: row
-    // pi(G*8 + jj), logical piece c16 (d128) or c16/2 + half (d64).
-    uint32_t lk[2][KS], lv[8];
+    // fragment (tt, ks): row tt*16 + c16, logical piece ks*4 + G.  V^T: lane reads row
+    // h*16 + 4G + c16/4 at dims 4*(c16%4) of each 16-dim tile (base zv[h], see lds_read_vt).
+    uint32_t lk[2][KS], zv[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
         const int t = tt * 16 + c16;
@@ -790,12 +935,9 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
         for (int ks = 0; ks < KS; ++ks) lk[tt][ks] = t * RS::kRowBytes + (((ks * 4 + G) ^ (t % PP)) * 16);
     }
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-        const int t = jj < 4 ? G * 4 + jj : 16 + G * 4 + (jj - 4);
-        if constexpr (NT == 8)
-            lv[jj] = RS::kMatBytes + t * RS::kRowBytes + ((c16 ^ (t % PP)) * 16);
-        else
-            lv[jj] = RS::kMatBytes + t * RS::kRowBytes + ((((c16 >> 1) ^ (t % PP)) * 16) + (c16 & 1) * 8);
+    for (int h = 0; h < 2; ++h) {
+        const int t = h * 16 + 4 * G + (c16 >> 2);
+        zv[h] = RS::kMatBytes + t * RS::kRowBytes + (((c16 & 3) >> 1) * 16) + (c16 & 1) * 8 + ((2 * t) % PP) * 16;
     }
 
     f32x4_t oacc[2][NT];
@@ -845,24 +987,9 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[tt][ks], qf[rt][ks], acc, 0, 0, 0);
                 s[rt][tt] = acc;
             }
-        // V reads go out while the score MFMAs run
-        uint4 vr[8];
-        {
-            uint32_t va[8];
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) va[jj] = sp + lv[jj];
-            if constexpr (NT == 8) {
-                u32x4_t t4[8];
-                lds_read_b128_x8(t4, va);
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) vr[jj] = make_uint4(t4[jj].x, t4[jj].y, t4[jj].z, t4[jj].w);
-            } else {
-                u32x2_t t2[8];
-                lds_read_b64_x8(t2, va);
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) vr[jj] = make_uint4(t2[jj].x, t2[jj].y, 0u, 0u);
-            }
-        }
+        // V^T fragments go out while the score MFMAs run
+        u32x2_t vt[16];
+        lds_read_vt(vt, sp + zv[0], sp + zv[1]);
         if (t0 + kChunk > P) {
             // chunk reaches the tree slots: a token is visible if it is in the prefix or is
             // an ancestor-or-self of the row's node.  Over the sequence of 32-bit words
@@ -907,20 +1034,11 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
                 }
             lrow[rt] += lsum;
         }
-        // O^T += V^T P^T; A operand of dim tile nt = (vr[0][nt], ..., vr[7][nt])
+        // O^T += V^T P^T over dim tiles of 16: A operand of tile nt = (tokens pi(8G + j)) at
+        // dim nt*16 + c16; the accumulator lane holds dims nt*16 + 4G + i of row c16
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            uint32_t a4[4];
-            const uint32_t sel = (nt & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                const uint4 x4 = vr[2 * f], y4 = vr[2 * f + 1];
-                const int e = nt >> 1;
-                const uint32_t x = e == 0 ? x4.x : e == 1 ? x4.y : e == 2 ? x4.z : x4.w;
-                const uint32_t y = e == 0 ? y4.x : e == 1 ? y4.y : e == 2 ? y4.z : y4.w;
-                a4[f] = __builtin_amdgcn_perm(y, x, sel);
-            }
-            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(a4[0], a4[1], a4[2], a4[3]));
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(vt[2 * nt].x, vt[2 * nt].y, vt[2 * nt + 1].x, vt[2 * nt + 1].y));
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
                 oacc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rt], oacc[rt][nt], 0, 0, 0);
@@ -988,42 +1106,69 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) mrow[rt] = mrow[rt] == -INFINITY ? -INFINITY : mrow[rt] * cs;
 
+    // ---- split-KV completion: the last split of a row block to arrive merges the block.
+    // Every split of the block runs on this workgroup's XCD (blockIdx % 8, the dispatch
+    // order), whose L2 all of them write: a split's partial stores are complete once its
+    // vector-memory count drains, after which it counts itself in with a device-scope
+    // atomic; the last arrival then only needs a fresh L1.  A split that finds itself on
+    // another XCD releases its stores device-wide first and flags the counter, and a last
+    // arrival that sees the flag acquires device-wide before reading.
+    auto finish_split = [&]() {
+        const int64_t unit = static_cast<int64_t>(pair) * nb + rbk;
+        __builtin_amdgcn_s_waitcnt(kVmcntZero);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const bool local = xcc_id() == xcd;
+            if (!local) __threadfence();
+            const int old = __hip_atomic_fetch_add(ws_cnt + unit, local ? 1 : 0x10001, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+            s_last = (old & 0xffff) == splits - 1 ? ((old >> 16) != 0 || !local ? 2 : 1) : 0;
+        }
+        __syncthreads();
+        const int last = s_last;
+        if (last == 0) return;
+        if (last == 2) __threadfence();
+        else l1_invalidate();
+        if (threadIdx.x == 0) __hip_atomic_store(ws_cnt + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int item = threadIdx.x; item < RB * (D / 8); item += kWaves * kWave) {
+            const int rr = item / (D / 8), part = item % (D / 8);
+            merge_row_part<D, RB>(unit, rr, part, splits, b, kvh, g, row0_wg + rr, M_max, L_cap, M, P, st, depth, out,
+                                  os0, os1, os2, ws_stats, ws_o);
+        }
+    };
+
     if constexpr (WT > 1) {
-        // ---- the WT waves share the same 32 rows: every wave parks its (m, l, O) in the
-        // idle ring, then wave wt combines rows wt*8 .. wt*8+7 of all four in a fixed order
-        // and writes them (lane: row wt*8 + lane/8, dims (lane%8)*D/8 .. +D/8).  O rows sit
-        // kOS floats apart so the parked writes are free of bank conflicts.
-        static_assert(WT == kWaves && WR == 1, "one row group per workgroup");
+        // ---- the WT waves of a row group share its 32 rows: every wave parks its (m, l, O)
+        // in the idle ring, then each wave combines its share of its group's rows over the
+        // group's WT waves in a fixed order and writes them.  O rows sit kOS floats apart so
+        // the parked writes are free of bank conflicts.
+        static_assert(WR * WT == kWaves && (WR == 1 || WR == 2), "row groups of 32 rows shared by WT waves");
         constexpr int kOS = D + 4;
         constexpr int kPark = kRowsPerWave * kOS;                  // floats per parked wave
-        static_assert(2 * kPark * 4 + WT * kRowsPerWave * 2 * 4 <= (int)sizeof(ring1), "park area");
+        static_assert(2 * kPark * 4 + kWaves * kRowsPerWave * 2 * 4 <= (int)sizeof(ring1), "park area");
         auto parked = [&](int w) { return reinterpret_cast<float *>(w < 2 ? ring0 : ring1) + (w & 1) * kPark; };
-        float *ml = reinterpret_cast<float *>(ring1) + 2 * kPark;    // [WT][32 rows][m, l]
+        float *ml = reinterpret_cast<float *>(ring1) + 2 * kPark;    // [wave][32 rows][m, l]
         {
-            float *o = parked(wt);
+            float *o = parked(wave);
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
                 const int rr = rt * 16 + c16;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float4 x0, x1;
-                    x0.x = oacc[rt][0][i]; x0.y = oacc[rt][1 % NT][i]; x0.z = oacc[rt][2 % NT][i]; x0.w = oacc[rt][3 % NT][i];
-                    *reinterpret_cast<float4 *>(o + rr * kOS + (G * 4 + i) * NT) = x0;
-                    if constexpr (NT == 8) {
-                        x1.x = oacc[rt][4][i]; x1.y = oacc[rt][5][i]; x1.z = oacc[rt][6][i]; x1.w = oacc[rt][7][i];
-                        *reinterpret_cast<float4 *>(o + rr * kOS + (G * 4 + i) * NT + 4) = x1;
-                    }
-                }
-                if (G == 0) *reinterpret_cast<float2 *>(ml + (wt * kRowsPerWave + rr) * 2) = make_float2(mrow[rt], lrow[rt]);
+                for (int nt = 0; nt < NT; ++nt)
+                    *reinterpret_cast<f32x4_t *>(o + rr * kOS + nt * 16 + 4 * G) = oacc[rt][nt];
+                if (G == 0) *reinterpret_cast<float2 *>(ml + (wave * kRowsPerWave + rr) * 2) = make_float2(mrow[rt], lrow[rt]);
             }
         }
         __syncthreads();
-        constexpr int DL = D / 8;                                  // dims per lane
-        const int rr = wt * 8 + (lane >> 3), d0 = (lane & 7) * DL;
+        // wave (wr, wt) combines rows wt*RPW .. +RPW of its row group; LPR lanes per row,
+        // DL dims per lane
+        constexpr int RPW = kRowsPerWave / WT, LPR = kWave / RPW, DL = D / LPR;
+        const int rg = wt * RPW + lane / LPR, d0 = (lane % LPR) * DL;
+        const int rr = wr * kRowsPerWave + rg;                      // row within the workgroup
         float mw[WT], lw[WT], mt = -INFINITY;
 #pragma unroll
         for (int w = 0; w < WT; ++w) {
-            const float2 x = *reinterpret_cast<const float2 *>(ml + (w * kRowsPerWave + rr) * 2);
+            const float2 x = *reinterpret_cast<const float2 *>(ml + ((wr * WT + w) * kRowsPerWave + rg) * 2);
             mw[w] = x.x; lw[w] = x.y;
             mt = fmaxf(mt, x.x);
         }
@@ -1036,7 +1181,7 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
         for (int e = 0; e < DL; ++e) acc[e] = 0.f;
 #pragma unroll
         for (int w = 0; w < WT; ++w) {
-            const float *src = parked(w) + rr * kOS + d0;
+            const float *src = parked(wr * WT + w) + rg * kOS + d0;
 #pragma unroll
             for (int e = 0; e < DL; e += 4) {
                 const float4 x = *reinterpret_cast<const float4 *>(src + e);
@@ -1044,17 +1189,18 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
             }
         }
         if (splits > 1) {
-            // ---- split-KV: publish this split's partial (m, l, unnormalised O); the merge
-            // kernel that follows on the stream combines the splits in a fixed order
+            // ---- split-KV: publish this split's partial (m, l, unnormalised O); the last
+            // split of the row block to arrive merges them (finish_split)
             const int64_t unit = static_cast<int64_t>(pair) * nb + rbk;
             const int64_t base = (unit * splits + split) * RB;
             float *o = ws_o + (base + rr) * D + d0;
 #pragma unroll
             for (int e = 0; e < DL; e += 4) *reinterpret_cast<float4 *>(o + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
-            if ((lane & 7) == 0) *reinterpret_cast<float2 *>(ws_stats + (base + rr) * 2) = make_float2(mt, lt);
+            if ((lane % LPR) == 0) *reinterpret_cast<float2 *>(ws_stats + (base + rr) * 2) = make_float2(mt, lt);
+            finish_split();
             return;
         }
-        const int r = row0 + rr;
+        const int r = row0_wg + rr;
         if (r >= M_max * g) return;
         const int j = r / g + 1, gi = r % g;
         const bool live = r < Rh && depth[static_cast<int64_t>(b) * R + j] >= 1;
@@ -1072,32 +1218,25 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
         }
         return;
     } else {
-    // ---- split-KV: publish this split's partial (m, l, unnormalised O) and stop; the
-    // merge kernel that follows on the stream combines the splits in a fixed order
+    // ---- split-KV: publish this split's partial (m, l, unnormalised O); the last split
+    // of the row block to arrive merges them (finish_split)
     if (splits > 1) {
-        if (wt != 0) return;
         const int64_t unit = static_cast<int64_t>(pair) * nb + rbk;          // (pair, row block)
         const int64_t base = (unit * splits + split) * RB + wr * kRowsPerWave;
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             const int rr = rt * 16 + c16;
-            float *o = ws_o + (base + rr) * D + G * DG;
+            float *o = ws_o + (base + rr) * D + 4 * G;
 #pragma unroll
-            for (int e = 0; e < DG; e += 4) {
-                float4 v4;
-                v4.x = oacc[rt][(e + 0) % NT][(e + 0) / NT];
-                v4.y = oacc[rt][(e + 1) % NT][(e + 1) / NT];
-                v4.z = oacc[rt][(e + 2) % NT][(e + 2) / NT];
-                v4.w = oacc[rt][(e + 3) % NT][(e + 3) / NT];
-                *reinterpret_cast<float4 *>(o + e) = v4;
-            }
+            for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f32x4_t *>(o + nt * 16) = oacc[rt][nt];
             if (G == 0) *reinterpret_cast<float2 *>(ws_stats + (base + rr) * 2) = make_float2(mrow[rt], lrow[rt]);
         }
+        finish_split();
         return;
     }
     if (wt != 0) return;
 
-    // ---- write the final rows: lane writes dims G*DG .. +DG of its row in each tile
+    // ---- write the final rows: lane writes dims nt*16 + 4G .. +3 of its row in each tile
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
         const int r = row0 + rt * 16 + c16;
@@ -1105,95 +1244,17 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
         const int j = r / g + 1, gi = r % g;
         const bool live = r < Rh && depth[static_cast<int64_t>(b) * R + j] >= 1;
         const float inv = live && lrow[rt] > 0.f ? 1.f / lrow[rt] : 0.f;
-        uint16_t *o = out + b * os0 + static_cast<int64_t>(j - 1) * os1 + static_cast<int64_t>(kvh * g + gi) * os2 + G * DG;
+        uint16_t *o = out + b * os0 + static_cast<int64_t>(j - 1) * os1 + static_cast<int64_t>(kvh * g + gi) * os2 + 4 * G;
 #pragma unroll
-        for (int e = 0; e < DG; e += 8) {
-            uint32_t w4[4];
-#pragma unroll
-            for (int h2 = 0; h2 < 4; ++h2) {
-                // dims e + 2*h2, e + 2*h2 + 1 of this lane's slice: (i, nt) = (dim / NT, dim % NT)
-                const int d0 = e + 2 * h2, d1 = d0 + 1;
-                const float x0 = live ? oacc[rt][d0 % NT][d0 / NT] * inv : 0.f;
-                const float x1 = live ? oacc[rt][d1 % NT][d1 / NT] * inv : 0.f;
-                w4[h2] = static_cast<uint32_t>(tmv::f32_to_bf16(x0)) | (static_cast<uint32_t>(tmv::f32_to_bf16(x1)) << 16);
-            }
-            *reinterpret_cast<uint4 *>(o + e) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        for (int nt = 0; nt < NT; ++nt) {
+            const float x0 = live ? oacc[rt][nt][0] * inv : 0.f, x1 = live ? oacc[rt][nt][1] * inv : 0.f;
+            const float x2 = live ? oacc[rt][nt][2] * inv : 0.f, x3 = live ? oacc[rt][nt][3] * inv : 0.f;
+            *reinterpret_cast<uint2 *>(o + nt * 16) =
+                make_uint2(static_cast<uint32_t>(tmv::f32_to_bf16(x0)) | (static_cast<uint32_t>(tmv::f32_to_bf16(x1)) << 16),
+                           static_cast<uint32_t>(tmv::f32_to_bf16(x2)) | (static_cast<uint32_t>(tmv::f32_to_bf16(x3)) << 16));
         }
     }
     }
-}
-
-// --------------------------------------------------------------------------- split merge
-// One thread per (row, 8 head dims) of every live row block: reads the S partials of its
-// row in split order, rescales them to the common maximum and writes the bf16 row; rows
-// of inert nodes (and whole failed sequences) are written as 0.
-template <int D, int RB>
-__global__ void __launch_bounds__(256)
-tree_attn_merge_kernel(int M_max, int D_max, int Hq, int Hkv, int L_cap,
-                       const int32_t *__restrict__ prefix_len, const int32_t *__restrict__ n_nodes,
-                       const int32_t *__restrict__ depth, const int32_t *__restrict__ status,
-                       uint16_t *__restrict__ out, int64_t os0, int64_t os1, int64_t os2,
-                       const float *__restrict__ ws_stats, const float *__restrict__ ws_o,
-                       int pairs, int nb, int splits)
-{
-    constexpr int TPR = D / 8;                         // threads per row
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    const int64_t row_global = t / TPR;                // over pairs * nb * RB
-    const int part = static_cast<int>(t % TPR);
-    if (row_global >= static_cast<int64_t>(pairs) * nb * RB) return;
-    const int64_t unit = row_global / RB;
-    const int rr = static_cast<int>(row_global % RB);
-    const int pair = static_cast<int>(unit / nb), rbk = static_cast<int>(unit % nb);
-    const int b = pair / Hkv, kvh = pair % Hkv, g = Hq / Hkv;
-    const int r = rbk * RB + rr;
-    if (r >= M_max * g) return;
-    const int j = r / g + 1, gi = r % g;
-    const int M = n_nodes[b], P = prefix_len[b], st = status[b];
-    const int dp = depth[static_cast<int64_t>(b) * (M_max + 1) + j];
-    // every split's (m, l) and O slice are fetched before any is consumed
-    constexpr int kMaxSplits = 16;
-    float2 ml[kMaxSplits];
-    float4 oa[kMaxSplits], ob[kMaxSplits];
-#pragma unroll
-    for (int s2 = 0; s2 < kMaxSplits; ++s2) {
-        if (s2 < splits) {
-            const int64_t base = (unit * splits + s2) * RB + rr;
-            ml[s2] = *reinterpret_cast<const float2 *>(ws_stats + base * 2);
-            const float4 *o = reinterpret_cast<const float4 *>(ws_o + base * D + part * 8);
-            oa[s2] = o[0];
-            ob[s2] = o[1];
-        }
-    }
-    const bool seq_ok = st == TMV_OK && M >= 0 && M <= M_max && P >= 0 && static_cast<int64_t>(P) + M <= L_cap;
-    const bool live = seq_ok && r < M * g && dp >= 1;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (live) {
-        float mt = -INFINITY;
-#pragma unroll
-        for (int s2 = 0; s2 < kMaxSplits; ++s2)
-            if (s2 < splits) mt = fmaxf(mt, ml[s2].x);
-        const float mref = mt == -INFINITY ? 0.f : mt;
-        float lt = 0.f;
-#pragma unroll
-        for (int s2 = 0; s2 < kMaxSplits; ++s2) {
-            if (s2 < splits) {
-                const float sc = __builtin_amdgcn_exp2f(ml[s2].x - mref);
-                lt += sc * ml[s2].y;
-                acc[0] += sc * oa[s2].x; acc[1] += sc * oa[s2].y; acc[2] += sc * oa[s2].z; acc[3] += sc * oa[s2].w;
-                acc[4] += sc * ob[s2].x; acc[5] += sc * ob[s2].y; acc[6] += sc * ob[s2].z; acc[7] += sc * ob[s2].w;
-            }
-        }
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] *= inv;
-    }
-    uint32_t w4[4];
-#pragma unroll
-    for (int h2 = 0; h2 < 4; ++h2)
-        w4[h2] = static_cast<uint32_t>(tmv::f32_to_bf16(acc[2 * h2])) |
-                 (static_cast<uint32_t>(tmv::f32_to_bf16(acc[2 * h2 + 1])) << 16);
-    uint16_t *o = out + b * os0 + static_cast<int64_t>(j - 1) * os1 + static_cast<int64_t>(kvh * g + gi) * os2 + part * 8;
-    *reinterpret_cast<uint4 *>(o) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
 }
 
 // --------------------------------------------------------------------------- fp32 kernel
@@ -1274,16 +1335,17 @@ template <int D, int WR>
 void launch_bf16(const AttnPlan &p, hipStream_t s, int M_max, int D_max, int Hq, int Hkv,
                  const void *q, const int64_t *qs, const void *k, const void *v, const int64_t *kvs,
                  int L_cap, const int32_t *P, const int32_t *n, const int32_t *anc, const int32_t *dep,
-                 int32_t *status, float scale, void *out, const int64_t *os, void *ws, size_t off_o)
+                 int32_t *status, float scale, void *out, const int64_t *os, void *ws, size_t off_o, size_t off_stats)
 {
     char *w = static_cast<char *>(ws);
-    float *stats = reinterpret_cast<float *>(w), *part = reinterpret_cast<float *>(w + off_o);
+    int32_t *cnt = reinterpret_cast<int32_t *>(w);
+    float *stats = reinterpret_cast<float *>(w + off_stats), *part = reinterpret_cast<float *>(w + off_o);
 #define TMV_LAUNCH_ATTN(DEEP)                                                                              \
     hipLaunchKernelGGL((tree_attn_bf16_kernel<D, WR, DEEP>), dim3(p.slots * tmv::kXcds), dim3(kWaves * kWave), 0, s, \
                        M_max, D_max, Hq, Hkv, static_cast<const uint16_t *>(q), qs[0], qs[1], qs[2],             \
                        static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), kvs[0], kvs[1], kvs[2], \
                        L_cap, P, n, anc, dep, status, scale * kLog2e, static_cast<uint16_t *>(out), os[0], os[1], \
-                       os[2], stats, part, p.pairs, p.nb, p.splits, p.per_pair)
+                       os[2], stats, part, cnt, p.pairs, p.nb, p.splits, p.per_pair)
     if constexpr (D == 64) {
         hipLaunchKernelGGL((tree_attn_bf16_stream_kernel<D, WR>), dim3(p.slots * tmv::kXcds), dim3(kWaves * kWave), 0,
                            s, M_max, D_max, Hq, Hkv, static_cast<const uint16_t *>(q), qs[0], qs[1], qs[2],
@@ -1295,7 +1357,9 @@ void launch_bf16(const AttnPlan &p, hipStream_t s, int M_max, int D_max, int Hq,
         else TMV_LAUNCH_ATTN(false);
     }
 #undef TMV_LAUNCH_ATTN
-    if (p.splits > 1) {
+    // the LDS-ring kernel (d128) merges its splits itself; the streaming kernel needs the
+    // merge kernel after it
+    if (D == 64 && p.splits > 1) {
         constexpr int RB = WR * kRowsPerWave;
         const int64_t threads = static_cast<int64_t>(p.pairs) * p.nb * RB * (D / 8);
         hipLaunchKernelGGL((tree_attn_merge_kernel<D, RB>), dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256),
@@ -1312,7 +1376,7 @@ extern "C" size_t tmv_tree_verify_attention_workspace(int dtype, int B, int M_ma
                                                       int L_cap)
 {
     if (dtype != TMV_BF16 || B <= 0 || Hkv <= 0 || Hq <= 0 || Hq % Hkv) return 256;
-    const AttnPlan p = make_plan(B, M_max, Hq, Hkv, L_cap);
+    const AttnPlan p = make_plan(B, M_max, Hq, Hkv, L_cap, d);
     return plan_bytes(p, d, nullptr);
 }
 
@@ -1354,22 +1418,24 @@ extern "C" int tmv_tree_verify_attention(int dtype, int B, int M_max, int D_max,
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return TMV_ERR_ARG;
     for (int i = 0; i < 3; ++i)
         if ((q_stride[i] | kv_stride[i] | o_stride[i]) & 7) return TMV_ERR_ARG;
-    const AttnPlan p = make_plan(B, M_max, Hq, Hkv, L_cap);
-    size_t off_o = 0;
-    const size_t need = plan_bytes(p, d, &off_o);
+    const AttnPlan p = make_plan(B, M_max, Hq, Hkv, L_cap, d);
+    size_t off_o = 0, off_stats = 0;
+    const size_t need = plan_bytes(p, d, &off_o, &off_stats);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return TMV_ERR_ARG;
     if (static_cast<int64_t>(p.slots) * tmv::kXcds > 0x7fffffff) return TMV_ERR_ARG;
 
     if (d == 128) {
         if (p.wr == 4) launch_bf16<128, 4>(p, s, M_max, D_max, Hq, Hkv, q, q_stride, k_cache, v_cache, kv_stride, L_cap,
-                                           prefix_len, n_nodes, anc, depth, status, scale, out, o_stride, workspace, off_o);
+                                           prefix_len, n_nodes, anc, depth, status, scale, out, o_stride, workspace, off_o, off_stats);
+        else if (p.wr == 2) launch_bf16<128, 2>(p, s, M_max, D_max, Hq, Hkv, q, q_stride, k_cache, v_cache, kv_stride, L_cap,
+                                 prefix_len, n_nodes, anc, depth, status, scale, out, o_stride, workspace, off_o, off_stats);
         else launch_bf16<128, 1>(p, s, M_max, D_max, Hq, Hkv, q, q_stride, k_cache, v_cache, kv_stride, L_cap,
-                                 prefix_len, n_nodes, anc, depth, status, scale, out, o_stride, workspace, off_o);
+                                 prefix_len, n_nodes, anc, depth, status, scale, out, o_stride, workspace, off_o, off_stats);
     } else {
         if (p.wr == 4) launch_bf16<64, 4>(p, s, M_max, D_max, Hq, Hkv, q, q_stride, k_cache, v_cache, kv_stride, L_cap,
-                                          prefix_len, n_nodes, anc, depth, status, scale, out, o_stride, workspace, off_o);
+                                          prefix_len, n_nodes, anc, depth, status, scale, out, o_stride, workspace, off_o, off_stats);
         else launch_bf16<64, 1>(p, s, M_max, D_max, Hq, Hkv, q, q_stride, k_cache, v_cache, kv_stride, L_cap,
-                                prefix_len, n_nodes, anc, depth, status, scale, out, o_stride, workspace, off_o);
+                                prefix_len, n_nodes, anc, depth, status, scale, out, o_stride, workspace, off_o, off_stats);
     }
     return tmv_host::launch_status(hipGetLastError());
 }

@@ -27,7 +27,7 @@ PARENTS_VROOT, PARENTS_NEG1 = 0, 1
 ACCEPT_GREEDY, ACCEPT_SAMPLE = 0, 1
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError("libtmv.so is not built (run `python -m tree_masked_verification_amd.build`); "
+    raise ImportError("libtmv.so is not built (run `python tree_masked_verification_amd/build.py`); "
                       "the tree-verification path has no CPU fallback")
 
 _lib = ctypes.CDLL(LIB_PATH)

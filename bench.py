@@ -9,8 +9,9 @@ single-layer workload (bf16, 32 query / 8 KV heads, head_dim 128, batch 1, prefi
 reads miss the 256 MB Infinity Cache.
 
 Timed regions (both after --warmup untimed steps):
-  1. throughput: --steps steps, each one HIP-graph replay of the four stages on its input
-     set, bracketed by torch.cuda.synchronize(); value = verified node-tokens per second.
+  1. throughput: --steps steps, bracketed by torch.cuda.synchronize(); the steps run as
+     replays of one HIP graph that holds a step on every input set in turn (plus one graph
+     for the remainder); value = verified node-tokens per second.
   2. kernel durations: for each stage, one HIP graph of back-to-back launches over the
      rotating sets, timed with HIP events recorded on the stream the kernels run on;
      the average launch duration feeds the roofline figures.
@@ -209,24 +210,33 @@ def main():
         raise RuntimeError("a verify step reported a non-OK status: %s" % st.flatten().tolist())
     mean_accept = float(torch.stack([s.accept_len for s in sets]).float().mean())
 
-    # ---- one graph per input set for the step
+    # ---- the step loop as HIP graphs: one graph runs a step on each input set in turn
+    # (n_sets steps back to back), a second one the first `rem` of them, so that exactly
+    # --steps steps are timed with one replay per n_sets steps
     stream = torch.cuda.Stream()
-    graphs = []
+
+    def capture(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                sets[i].step()
+        return g
+
+    full_reps, rem = divmod(args.steps, n_sets)
     with torch.cuda.stream(stream):
-        for s in sets:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                s.step()
-            graphs.append(g)
+        g_all = capture(n_sets)
+        g_rem = capture(rem) if rem else None
     torch.cuda.synchronize()
-    for i in range(args.warmup):
-        graphs[i % n_sets].replay()
+    for _ in range(max(1, args.warmup // n_sets)):
+        g_all.replay()
     torch.cuda.synchronize()
 
     # ---- timed region 1: throughput
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        graphs[i % n_sets].replay()
+    for _ in range(full_reps):
+        g_all.replay()
+    if g_rem is not None:
+        g_rem.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     sec_per_step = (t1 - t0) / args.steps

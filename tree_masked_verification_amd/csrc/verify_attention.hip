@@ -132,6 +132,12 @@ __device__ __forceinline__ void lds_read_vt(u32x2_t (&v)[16], uint32_t z0, uint3
                  : "v"(z0), "v"(z1)
                  : "memory");
 }
+// zero 16 bytes of LDS (inline assembly, like the operand reads: a compiler-written LDS
+// store would first wait for every buffer->LDS copy in flight)
+__device__ __forceinline__ void lds_zero16(uint32_t addr) {
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(z) : "memory");
+}
 // the XCD (accelerator complex die) this wave runs on
 __device__ __forceinline__ int xcc_id() { return __builtin_amdgcn_s_getreg(kHwRegXccId) & 0xf; }
 // drop this CU's vector L1 lines so later loads read the XCD's L2
@@ -742,16 +748,18 @@ constexpr int kAncBatch = 16;
 
 template <int D, int WR, bool DEEP>
 __global__ void __launch_bounds__(kWaves * kWave)
-tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
-                      const uint16_t *__restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
-                      const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
-                      int64_t ks0, int64_t ks1, int64_t ks2, int L_cap,
+tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
                       const int32_t *__restrict__ prefix_len, const int32_t *__restrict__ n_nodes,
+                      uint32_t ks0_16, uint32_t ks1_16, uint32_t ks2_16, int L_cap, int pairs, uint32_t geom,
+                      // (the arguments above fill the 14 SGPRs the hardware preloads: everything
+                      // the first K/V copies need, cache strides in 16-byte units; the rest
+                      // arrive through the kernel-argument segment)
+                      int M_max, int D_max, int Hq, int nb,
+                      const uint16_t *__restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
                       const int32_t *__restrict__ anc, const int32_t *__restrict__ depth,
                       int32_t *__restrict__ status, float qk_scale_log2,
                       uint16_t *__restrict__ out, int64_t os0, int64_t os1, int64_t os2,
-                      float *__restrict__ ws_stats, float *__restrict__ ws_o, int32_t *__restrict__ ws_cnt,
-                      int pairs, int nb, int splits, int per_pair)
+                      float *__restrict__ ws_stats, float *__restrict__ ws_o, int32_t *__restrict__ ws_cnt)
 {
     using RS = RingShape<D>;
     static_assert(D == 128, "the LDS-ring kernel is written for head dimension 128");
@@ -769,6 +777,9 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
     __shared__ int s_last;
 
     // ---- decode the workgroup: XCD-major so one (sequence, kv head) stays on one XCD
+    // geom = splits | workgroups per pair << 5 | Hkv << 16
+    const int splits = static_cast<int>(geom & 31u), per_pair = static_cast<int>((geom >> 5) & 2047u);
+    const int Hkv = static_cast<int>(geom >> 16);
     const int wg = blockIdx.x;
     const int xcd = wg % tmv::kXcds, slot = wg / tmv::kXcds;
     const int pair = (slot / per_pair) * tmv::kXcds + xcd;
@@ -776,7 +787,6 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
     const int within = slot % per_pair;
     const int rbk = within / splits, split = within % splits;
     const int b = pair / Hkv, kvh = pair % Hkv;
-    const int g = Hq / Hkv;
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);     // wave-uniform
@@ -786,13 +796,76 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
     const int row0_wg = rbk * RB;
     const int row0 = row0_wg + wr * kRowsPerWave;         // first row of this wave
 
-    // ---- one round trip for the prologue: the sequence's scalars and, independently of
-    // them, this lane's query fragments, node depths and first ancestor entries (row
+    // ---- K/V copies.  Split s takes the global 32-token chunks s, s + S, s + 2S, ... (local
+    // chunk k = global chunk s + k*S), so the chunks of a split are known before the
+    // sequence's length is: the first two rounds go out at once, bounded by the cache
+    // capacity L_cap (every slot below it is the caller's memory); later rounds stop at the
+    // visible length T.  Rows in [T, L_cap) of a speculatively copied chunk are never
+    // visible (their mask bits are clear); V rows among them are zeroed in LDS before use
+    // (0 * garbage could be NaN), and chunks entirely beyond T are never computed.
+    // Local chunk k sits in slot k % kSlots (half (k / kRound) % 2).
+    const int ncap = (L_cap + kChunk - 1) / kChunk;
+    const int nk_cap = ncap > split ? (ncap - split + splits - 1) / splits : 0;
+    int t_lim = L_cap, nk_lim = nk_cap;       // copy bounds: capacity until T is known
+
+    // DMA lane mapping: instruction i of a chunk covers LDS bytes [i*1 KiB, +1 KiB) of the
+    // slot; lane l writes 16 bytes at 16*l.  Within K (or V) the LDS holds row t at
+    // t*kRowBytes with its 16-byte pieces XOR-swizzled by (t mod kPieces), so the lane
+    // that fills LDS piece (t, pp) reads global piece pp ^ (t mod kPieces) of row t.
+    const int64_t head_off = (static_cast<int64_t>(b) * ks0_16 + static_cast<int64_t>(kvh) * ks1_16) * 16;
+    const char *kbase = reinterpret_cast<const char *>(kc) + head_off;
+    const char *vbase = reinterpret_cast<const char *>(vc) + head_off;
+    const int64_t row_bytes = static_cast<int64_t>(ks2_16) * 16;
+    // each wave moves whole 1 KiB pieces of either K or V (waves 0-1 K, 2-3 V)
+    static_assert((RS::kDmaPerChunk / 2) % RS::kDmaPerWave == 0, "a wave must stay within K or V");
+    const bool wave_v = wave * RS::kDmaPerWave >= RS::kDmaPerChunk / 2;
+    const char *mbase = wave_v ? vbase : kbase;
+    uint32_t dma_off[RS::kDmaPerWave];
+    int dma_lds[RS::kDmaPerWave];
+#pragma unroll
+    for (int jd = 0; jd < RS::kDmaPerWave; ++jd) {
+        const int i = wave * RS::kDmaPerWave + jd;             // instruction within the chunk
+        const int ii = wave_v ? i - RS::kDmaPerChunk / 2 : i;
+        const int qpos = ii * 64 + lane;                       // 16-byte LDS piece index
+        const int t = qpos / PP, pp = qpos % PP;
+        // K rows swizzle their 16-byte pieces by t mod 16, V rows by 2t mod 16 (the V^T reads
+        // take four consecutive rows at once; see lds_read_vt)
+        const int sw = wave_v ? (2 * t) % PP : t % PP;
+        dma_off[jd] = static_cast<uint32_t>(t * row_bytes + ((pp ^ sw) * 16));
+        dma_lds[jd] = (wave_v ? RS::kMatBytes : 0) + ii * 1024;
+    }
+    // issue this wave's share of local chunk k into the slot at `slot` (records stop at
+    // t_lim, so loads past it write zeros and touch no memory; chunks past nk_lim load nothing)
+    auto issue_chunk = [&](int k, char *slot) {
+        const int t0 = (split + k * splits) * kChunk;
+        int recs = (k < nk_lim) ? t_lim - t0 : 0;
+        recs = recs < 0 ? 0 : (recs > kChunk ? kChunk : recs);
+        const int nbytes = __builtin_amdgcn_readfirstlane(static_cast<int>(recs * row_bytes));
+        const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char *>(mbase + static_cast<int64_t>(k < nk_lim ? t0 : 0) * row_bytes), 0, nbytes, kBufferFlags);
+#pragma unroll
+        for (int jd = 0; jd < RS::kDmaPerWave; ++jd)
+            dma_to_lds16(mr, slot + dma_lds[jd], dma_off[jd]);
+    };
+    // round r fills half r % 2 of the ring with local chunks r*kRound .. +kRound
+    auto issue_round = [&](int r, char *half) {
+#pragma unroll
+        for (int j = 0; j < RS::kRound; ++j) issue_chunk(r * RS::kRound + j, half + j * RS::kSlotBytes);
+    };
+    // the first two rounds go out before anything is loaded or waited for
+    // (both are issued even when empty -- they then load nothing -- so the number of DMA
+    // operations in flight is the same on every path)
+    issue_round(0, ring0);
+    issue_round(1, ring1);
+
+    // ---- one round trip for the prologue, under the first copies: the sequence's scalars and,
+    // independently of them, this lane's query fragments, node depths and first ancestor entries (row
     // indices are clamped into the tables, so no load waits on another)
     // (values are wave-uniform; readfirstlane keeps the chunk descriptors in scalar registers)
     const int M = __builtin_amdgcn_readfirstlane(n_nodes[b]);
     const int P = __builtin_amdgcn_readfirstlane(prefix_len[b]);
     int st = __builtin_amdgcn_readfirstlane(status[b]);
+    const int g = Hq / Hkv;
     bf16x8_t qf[2][KS];
     int dep[2], anc8[2][kAncBatch];
 #pragma unroll
@@ -828,67 +901,23 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
                 for (int e = 0; e < DG; e += 8) *reinterpret_cast<uint4 *>(o + e) = make_uint4(0, 0, 0, 0);
             }
         }
+        __builtin_amdgcn_s_waitcnt(kVmcntZero);   // no copy may land in LDS after the exit
         return;
     }
 
-    // ---- token range of this split, in 32-token chunks; local chunk k of this
-    // workgroup sits in slot k % kSlots (half (k / kRound) % 2)
+    // ---- this split's chunks of the visible range [0, T); later copies stop at T
     const int T = P + M;                                  // tokens visible to someone
     const int nchunks = (T + kChunk - 1) / kChunk;
-    // (nchunks * splits stays far below 2^31: nchunks <= 2^26 and splits <= 16)
-    const int c_begin = __builtin_amdgcn_readfirstlane(nchunks * split / splits);
-    const int c_end = __builtin_amdgcn_readfirstlane(nchunks * (split + 1) / splits);
-    const int nk = c_end - c_begin;
+    const int nk = __builtin_amdgcn_readfirstlane(nchunks > split ? (nchunks - split + splits - 1) / splits : 0);
     const int nrounds = (nk + RS::kRound - 1) / RS::kRound;
+    t_lim = T;
+    nk_lim = nk;
+    // the chunk holding T when T is not a chunk boundary: its rows >= T may hold anything
+    // if it was copied before T was known (first two rounds of the first pass)
+    const int cb = T / kChunk;
+    const int kb_loc = (T % kChunk != 0 && cb >= split && (cb - split) % splits == 0) ? (cb - split) / splits : -1;
+    const int kb_round = kb_loc >= 0 && kb_loc < 2 * RS::kRound ? kb_loc / RS::kRound : -1;
 
-    // DMA lane mapping: instruction i of a chunk covers LDS bytes [i*1 KiB, +1 KiB) of the
-    // slot; lane l writes 16 bytes at 16*l.  Within K (or V) the LDS holds row t at
-    // t*kRowBytes with its 16-byte pieces XOR-swizzled by (t mod kPieces), so the lane
-    // that fills LDS piece (t, pp) reads global piece pp ^ (t mod kPieces) of row t.
-    const char *kbase = reinterpret_cast<const char *>(kc + b * ks0 + kvh * ks1);
-    const char *vbase = reinterpret_cast<const char *>(vc + b * ks0 + kvh * ks1);
-    const int64_t row_bytes = ks2 * 2;
-    // each wave moves whole 1 KiB pieces of either K or V (waves 0-1 K, 2-3 V)
-    static_assert((RS::kDmaPerChunk / 2) % RS::kDmaPerWave == 0, "a wave must stay within K or V");
-    const bool wave_v = wave * RS::kDmaPerWave >= RS::kDmaPerChunk / 2;
-    const char *mbase = wave_v ? vbase : kbase;
-    uint32_t dma_off[RS::kDmaPerWave];
-    int dma_lds[RS::kDmaPerWave];
-#pragma unroll
-    for (int jd = 0; jd < RS::kDmaPerWave; ++jd) {
-        const int i = wave * RS::kDmaPerWave + jd;             // instruction within the chunk
-        const int ii = wave_v ? i - RS::kDmaPerChunk / 2 : i;
-        const int qpos = ii * 64 + lane;                       // 16-byte LDS piece index
-        const int t = qpos / PP, pp = qpos % PP;
-        // K rows swizzle their 16-byte pieces by t mod 16, V rows by 2t mod 16 (the V^T reads
-        // take four consecutive rows at once; see lds_read_vt)
-        const int sw = wave_v ? (2 * t) % PP : t % PP;
-        dma_off[jd] = static_cast<uint32_t>(t * row_bytes + ((pp ^ sw) * 16));
-        dma_lds[jd] = (wave_v ? RS::kMatBytes : 0) + ii * 1024;
-    }
-    // issue this wave's share of local chunk k into the slot at `slot` (records stop at T,
-    // so loads past it write zeros and touch no memory; chunks past the split load nothing)
-    auto issue_chunk = [&](int k, char *slot) {
-        const int t0 = (c_begin + k) * kChunk;
-        int recs = (k < nk) ? T - t0 : 0;
-        recs = recs < 0 ? 0 : (recs > kChunk ? kChunk : recs);
-        const int nbytes = __builtin_amdgcn_readfirstlane(static_cast<int>(recs * row_bytes));
-        const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<char *>(mbase + static_cast<int64_t>(k < nk ? t0 : 0) * row_bytes), 0, nbytes, kBufferFlags);
-#pragma unroll
-        for (int jd = 0; jd < RS::kDmaPerWave; ++jd)
-            dma_to_lds16(mr, slot + dma_lds[jd], dma_off[jd]);
-    };
-    // round r fills half r % 2 of the ring with local chunks r*kRound .. +kRound
-    auto issue_round = [&](int r, char *half) {
-#pragma unroll
-        for (int j = 0; j < RS::kRound; ++j) issue_chunk(r * RS::kRound + j, half + j * RS::kSlotBytes);
-    };
-    // the first two rounds go out before anything waits
-    // (round 1 is issued even when empty -- it then loads nothing -- so the number of DMA
-    // operations in flight is the same on every path)
-    issue_round(0, ring0);
-    issue_round(1, ring1);
 
     const bool wave_live = row0 < Rh;
 
@@ -1066,11 +1095,19 @@ tree_attn_bf16_kernel(int M_max, int D_max, int Hq, int Hkv,
             if (r + 1 < nrounds) __builtin_amdgcn_s_waitcnt(kVmcntRound<RS::kRound * RS::kDmaPerWave>());
             else __builtin_amdgcn_s_waitcnt(kVmcntZero);
             __builtin_amdgcn_s_barrier();
+            if (pass == 0 && r == kb_round) {
+                // the chunk holding T was copied before T was known: zero its V rows >= T
+                const int r0 = T - (split + kb_loc * splits) * kChunk;
+                const uint32_t vb = lds_addr(half) + (kb_loc % RS::kRound) * RS::kSlotBytes + RS::kMatBytes + r0 * RS::kRowBytes;
+                for (int i = threadIdx.x; i < (kChunk - r0) * PP; i += kWaves * kWave) lds_zero16(vb + i * 16);
+                __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
+                __builtin_amdgcn_s_barrier();
+            }
             if (wave_live) {
 #pragma unroll
                 for (int j = 0; j < RS::kRound; ++j) {
                     const int k = r * RS::kRound + j;
-                    if (k < nk && (k % WT) == wt) compute_chunk(lds_addr(half) + j * RS::kSlotBytes, c_begin + k);
+                    if (k < nk && (k % WT) == wt) compute_chunk(lds_addr(half) + j * RS::kSlotBytes, split + k * splits);
                 }
             }
             __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
@@ -1340,12 +1377,15 @@ void launch_bf16(const AttnPlan &p, hipStream_t s, int M_max, int D_max, int Hq,
     char *w = static_cast<char *>(ws);
     int32_t *cnt = reinterpret_cast<int32_t *>(w);
     float *stats = reinterpret_cast<float *>(w + off_stats), *part = reinterpret_cast<float *>(w + off_o);
+    const uint32_t geom = static_cast<uint32_t>(p.splits) | (static_cast<uint32_t>(p.per_pair) << 5) |
+                          (static_cast<uint32_t>(Hkv) << 16);
 #define TMV_LAUNCH_ATTN(DEEP)                                                                              \
     hipLaunchKernelGGL((tree_attn_bf16_kernel<D, WR, DEEP>), dim3(p.slots * tmv::kXcds), dim3(kWaves * kWave), 0, s, \
-                       M_max, D_max, Hq, Hkv, static_cast<const uint16_t *>(q), qs[0], qs[1], qs[2],             \
-                       static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), kvs[0], kvs[1], kvs[2], \
-                       L_cap, P, n, anc, dep, status, scale * kLog2e, static_cast<uint16_t *>(out), os[0], os[1], \
-                       os[2], stats, part, cnt, p.pairs, p.nb, p.splits, p.per_pair)
+                       static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), P, n,                 \
+                       static_cast<uint32_t>(kvs[0] / 8), static_cast<uint32_t>(kvs[1] / 8),                    \
+                       static_cast<uint32_t>(kvs[2] / 8), L_cap, p.pairs, geom, M_max, D_max, Hq, p.nb,         \
+                       static_cast<const uint16_t *>(q), qs[0], qs[1], qs[2], anc, dep, status, scale * kLog2e,  \
+                       static_cast<uint16_t *>(out), os[0], os[1], os[2], stats, part, cnt)
     if constexpr (D == 64) {
         hipLaunchKernelGGL((tree_attn_bf16_stream_kernel<D, WR>), dim3(p.slots * tmv::kXcds), dim3(kWaves * kWave), 0,
                            s, M_max, D_max, Hq, Hkv, static_cast<const uint16_t *>(q), qs[0], qs[1], qs[2],
@@ -1418,6 +1458,11 @@ extern "C" int tmv_tree_verify_attention(int dtype, int B, int M_max, int D_max,
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return TMV_ERR_ARG;
     for (int i = 0; i < 3; ++i)
         if ((q_stride[i] | kv_stride[i] | o_stride[i]) & 7) return TMV_ERR_ARG;
+    // the d128 kernel takes the cache strides as 32-bit counts of 16-byte units (they are
+    // multiples of 8 elements, checked above) and packs the launch geometry
+    for (int i = 0; i < 3; ++i)
+        if (kv_stride[i] / 8 > 0xffffffffll) return TMV_ERR_ARG;
+    if (Hkv > 0xffff) return TMV_ERR_ARG;
     const AttnPlan p = make_plan(B, M_max, Hq, Hkv, L_cap, d);
     size_t off_o = 0, off_stats = 0;
     const size_t need = plan_bytes(p, d, &off_o, &off_stats);

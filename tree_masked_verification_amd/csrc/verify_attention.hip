@@ -140,8 +140,6 @@ __device__ __forceinline__ void lds_zero16(uint32_t addr) {
 }
 // the XCD (accelerator complex die) this wave runs on
 __device__ __forceinline__ int xcc_id() { return __builtin_amdgcn_s_getreg(kHwRegXccId) & 0xf; }
-// drop this CU's vector L1 lines so later loads read the XCD's L2
-__device__ __forceinline__ void l1_invalidate() { asm volatile("buffer_inv sc0" ::: "memory"); }
 
 // buffer -> LDS copy of 16 bytes per lane: lane l's bytes land at lds + 16*l; a voffset
 // past the descriptor's records writes zeros and reads nothing
@@ -302,6 +300,85 @@ tree_attn_merge_kernel(int M_max, int D_max, int Hq, int Hkv, int L_cap,
     const int b = pair / Hkv, kvh = pair % Hkv, g = Hq / Hkv;
     merge_row_part<D, RB>(unit, rr, part, splits, b, kvh, g, rbk * RB + rr, M_max, L_cap, n_nodes[b], prefix_len[b],
                           status[b], depth, out, os0, os1, os2, ws_stats, ws_o);
+}
+
+// The merging workgroup of a split-KV row block (LDS-ring kernel): IPB items (row rr,
+// dims part*8 .. +8) per thread and batch.  Every split's (m, l) and O slice of the
+// batch's items are loaded at once, through the L2 (sc0: the partials were written by
+// other CUs of this XCD, so this CU's L1 must not serve them), then merged in split order.
+template <int D, int RB, int IPB, int SMAX>
+__device__ __forceinline__ void merge_block(int64_t unit, int splits, int b, int kvh, int g, int row0_wg, int M_max,
+                                            int L_cap, int M, int P, int st, const int32_t *__restrict__ depth,
+                                            uint16_t *__restrict__ out, int64_t os0, int64_t os1, int64_t os2,
+                                            const float *__restrict__ ws_stats, const float *__restrict__ ws_o)
+{
+    constexpr int kItems = RB * (D / 8);
+    constexpr int kThreads = kWaves * kWave;
+    const __amdgpu_buffer_rsrc_t rst = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(ws_stats + unit * splits * RB * 2), 0, splits * RB * 2 * 4, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(ws_o + unit * splits * RB * D), 0, splits * RB * D * 4, kBufferFlags);
+    const bool seq_ok = st == TMV_OK && M >= 0 && M <= M_max && P >= 0 && static_cast<int64_t>(P) + M <= L_cap;
+    for (int i0 = threadIdx.x; i0 < kItems; i0 += kThreads * IPB) {
+        u32x2_t ml[IPB][SMAX];
+        u32x4_t oa[IPB][SMAX], ob[IPB][SMAX];
+#pragma unroll
+        for (int k = 0; k < IPB; ++k) {
+            const int item = i0 + k * kThreads;
+            const int rr = item / (D / 8), part = item % (D / 8);
+#pragma unroll
+            for (int s2 = 0; s2 < SMAX; ++s2) {
+                if (s2 < splits && item < kItems) {
+                    const int row = s2 * RB + rr;
+                    ml[k][s2] = __builtin_amdgcn_raw_buffer_load_b64(rst, row * 8, 0, 1);
+                    oa[k][s2] = __builtin_amdgcn_raw_buffer_load_b128(ro, (row * D + part * 8) * 4, 0, 1);
+                    ob[k][s2] = __builtin_amdgcn_raw_buffer_load_b128(ro, (row * D + part * 8 + 4) * 4, 0, 1);
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < IPB; ++k) {
+            const int item = i0 + k * kThreads;
+            if (item >= kItems) break;
+            const int rr = item / (D / 8), part = item % (D / 8);
+            const int r = row0_wg + rr;
+            if (r >= M_max * g) continue;
+            const int j = r / g + 1, gi = r % g;
+            const int dp = depth[static_cast<int64_t>(b) * (M_max + 1) + j];
+            const bool live = seq_ok && r < M * g && dp >= 1;
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            if (live) {
+                float mt = -INFINITY;
+#pragma unroll
+                for (int s2 = 0; s2 < SMAX; ++s2)
+                    if (s2 < splits) mt = fmaxf(mt, __uint_as_float(ml[k][s2][0]));
+                const float mref = mt == -INFINITY ? 0.f : mt;
+                float lt = 0.f;
+#pragma unroll
+                for (int s2 = 0; s2 < SMAX; ++s2) {
+                    if (s2 < splits) {
+                        const float sc = __builtin_amdgcn_exp2f(__uint_as_float(ml[k][s2][0]) - mref);
+                        lt += sc * __uint_as_float(ml[k][s2][1]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            acc[e] += sc * __uint_as_float(oa[k][s2][e]);
+                            acc[4 + e] += sc * __uint_as_float(ob[k][s2][e]);
+                        }
+                    }
+                }
+                const float inv = lt > 0.f ? 1.f / lt : 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] *= inv;
+            }
+            uint32_t w4[4];
+#pragma unroll
+            for (int h2 = 0; h2 < 4; ++h2)
+                w4[h2] = static_cast<uint32_t>(tmv::f32_to_bf16(acc[2 * h2])) |
+                         (static_cast<uint32_t>(tmv::f32_to_bf16(acc[2 * h2 + 1])) << 16);
+            uint16_t *o = out + b * os0 + static_cast<int64_t>(j - 1) * os1 + static_cast<int64_t>(kvh * g + gi) * os2 + part * 8;
+            *reinterpret_cast<uint4 *>(o) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        }
+    }
 }
 
 // ------------------------------------------------ bf16 MFMA kernel, register streaming (d64)
@@ -1147,7 +1224,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     // Every split of the block runs on this workgroup's XCD (blockIdx % 8, the dispatch
     // order), whose L2 all of them write: a split's partial stores are complete once its
     // vector-memory count drains, after which it counts itself in with a device-scope
-    // atomic; the last arrival then only needs a fresh L1.  A split that finds itself on
+    // atomic; the last arrival then reads the partials past its L1.  A split that finds itself on
     // another XCD releases its stores device-wide first and flags the counter, and a last
     // arrival that sees the flag acquires device-wide before reading.
     auto finish_split = [&]() {
@@ -1165,13 +1242,14 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         const int last = s_last;
         if (last == 0) return;
         if (last == 2) __threadfence();
-        else l1_invalidate();
         if (threadIdx.x == 0) __hip_atomic_store(ws_cnt + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (int item = threadIdx.x; item < RB * (D / 8); item += kWaves * kWave) {
-            const int rr = item / (D / 8), part = item % (D / 8);
-            merge_row_part<D, RB>(unit, rr, part, splits, b, kvh, g, row0_wg + rr, M_max, L_cap, M, P, st, depth, out,
-                                  os0, os1, os2, ws_stats, ws_o);
-        }
+        // one round trip for the partials of up to 8 splits and 2 items per thread
+        if (splits <= 8)
+            merge_block<D, RB, 2, 8>(unit, splits, b, kvh, g, row0_wg, M_max, L_cap, M, P, st, depth, out, os0, os1,
+                                     os2, ws_stats, ws_o);
+        else
+            merge_block<D, RB, 1, 16>(unit, splits, b, kvh, g, row0_wg, M_max, L_cap, M, P, st, depth, out, os0, os1,
+                                      os2, ws_stats, ws_o);
     };
 
     if constexpr (WT > 1) {

@@ -1,12 +1,18 @@
 #!/usr/bin/env python3
 """Benchmark of the tree-verification step on one MI355X.
 
-A step is one pass of the whole verify path over one batch: tree_build_ancestors,
-tree_verify_attention, tree_accept (greedy) and kv_commit_path, on the Llama-3-8B-shaped
-single-layer workload (bf16, 32 query / 8 KV heads, head_dim 128, batch 1, prefix 2048,
-60-node static tree of depth 6, vocabulary 128256).  Inputs are synthetic and seeded
-(tmv_inputs), resident in HBM before timing, and rotated over enough distinct sets that
-reads miss the 256 MB Infinity Cache.
+A step is one pass of the whole verify path over one batch of synthetic, seeded input:
+tree_build_ancestors, tree_verify_attention, tree_accept and kv_commit_path.  The default
+workload (the one the headline metric is quoted on) is the Llama-3-8B-shaped single layer:
+bf16, 32 query / 8 KV heads, head_dim 128, batch 1, prefix 2048, 60-node static tree of
+depth 6, vocabulary 128256, greedy acceptance.  `--workload N` measures the others:
+  1  tiny fp32 step (1 head, d64, prefix 128, 7-node tree, vocabulary 32)
+  3  batch 16 of ragged prefixes (512..4096) and best-first trees of 16..128 nodes
+  4  70B-shaped layer: 64 / 8 heads, batch 4, prefix 32768, 64-node random trees
+  5  sampling acceptance (batch 32, 32-node trees, p and q over 128256 tokens) and the
+     commit of the accepted paths over 32 layers of 8 KV heads x d128 (no attention)
+Inputs are resident in HBM before timing and rotated over enough distinct sets that
+reads miss the 256 MB Infinity Cache (each set of workloads 3-5 is larger than it).
 
 Timed regions (both after --warmup untimed steps):
   1. throughput: --steps steps, bracketed by torch.cuda.synchronize(); the steps run as
@@ -15,7 +21,7 @@ Timed regions (both after --warmup untimed steps):
   2. kernel durations: for each stage, one HIP graph of back-to-back launches over the
      rotating sets, timed with HIP events recorded on the stream the kernels run on;
      the average launch duration feeds the roofline figures.
-The oracle (tests-only CPU implementation) is timed on a bounded sample of the same
+The oracle (tests-only CPU implementation) is timed on a bounded sample of the default
 workload for the cpu_baseline field.
 
 Prints one JSON line.
@@ -59,11 +65,35 @@ def attention_work(M_nodes_depths, P, Hq, Hkv, d, elem=2):
     return 2 * q_bytes + kv_bytes, flops
 
 
+def workload_work(w, depth, accept_len):
+    """Algorithmic bytes and flops per launch of every stage of one step of workload w,
+    given the device-built depths [B][M_max+1] and the accepted lengths [B]."""
+    elem = 4 if w.dtype == 0 else 2
+    nodes = [int(n) for n in w.n_nodes]
+    work = {"build": (w.B * (w.M_max + 1) * 4 * (w.D_max + 3), 0)}
+    if w.mode == "greedy":
+        ab, af = 0, 0
+        for b in range(w.B):
+            nb, fl = attention_work(depth[b, 1:nodes[b] + 1].tolist(), int(w.prefix[b]), w.Hq, w.Hkv, w.d, elem)
+            ab += nb + (w.M_max + 1) * (w.D_max + 2) * 4                 # ancestor table + depths
+            af += fl
+        work["attention"] = (ab, af)
+        # every live row of the teacher's logits once (row 0 plus the nodes)
+        work["accept"] = (sum(n + 1 for n in nodes) * w.V * 4 + w.B * (w.M_max + 1) * 4, 0)
+    else:
+        # the sampling walk reads the teacher's and the draft's row of every visited node
+        visited = int(np.sum(accept_len)) + w.B
+        work["accept"] = (visited * w.V * 4 * 2, 0)
+    # every accepted row of K and V read and written once, per layer and KV head
+    work["commit"] = (int(2 * 2 * w.n_layers * w.Hkv * w.d * elem * int(np.sum(accept_len))), 0)
+    return work
+
+
 # ---------------------------------------------------------------- workload sets
 class StepSet:
     """Device tensors of one input set and its stage outputs."""
 
-    def __init__(self, tmv, torch, w, ws_attn, ws_acc):
+    def __init__(self, tmv, torch, w, ws_attn, ws_acc, caches=None):
         dev = "cuda"
         t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
         self.tmv, self.torch = tmv, torch
@@ -72,16 +102,19 @@ class StepSet:
         self.n_nodes = t(w.n_nodes.astype(np.int32))
         self.prefix = t(w.prefix.astype(np.int32))
         self.tokens = t(w.tokens.astype(np.int32))
-        self.q = t(w.q).view(torch.bfloat16)
-        self.k = t(w.k).view(torch.bfloat16)
-        self.v = t(w.v).view(torch.bfloat16)
-        self.logits = t(w.logits)
+        if w.mode == "greedy":
+            bf = w.dtype == 1
+            self.q, self.k, self.v = (t(a).view(torch.bfloat16) if bf else t(a) for a in (w.q, w.k, w.v))
+            self.out = torch.zeros_like(self.q)
+            self.logits = t(w.logits)
+        else:
+            self.p, self.qd = t(w.p), t(w.qd)
+            self.k, self.v = caches
         B, M, D = w.B, w.M_max, w.D_max
         i32 = dict(dtype=torch.int32, device=dev)
         self.anc = torch.zeros((B, M + 1, D + 1), **i32)
         self.depth = torch.zeros((B, M + 1), **i32)
         self.status = torch.zeros((B,), **i32)
-        self.out = torch.zeros_like(self.q)
         self.accept_len = torch.zeros((B,), **i32)
         self.path = torch.zeros((B, D), **i32)
         self.next_token = torch.zeros((B,), **i32)
@@ -96,22 +129,31 @@ class StepSet:
                                        self.status, self.out, scale=self.w.scale, workspace=self.ws_attn)
 
     def accept(self):
-        self.tmv.tree_accept(self.tmv.ACCEPT_GREEDY, self.tokens, self.logits, self.n_nodes, self.anc, self.depth,
-                             self.status, self.accept_len, self.path, self.next_token, workspace=self.ws_acc)
+        if self.w.mode == "greedy":
+            self.tmv.tree_accept(self.tmv.ACCEPT_GREEDY, self.tokens, self.logits, self.n_nodes, self.anc, self.depth,
+                                 self.status, self.accept_len, self.path, self.next_token, workspace=self.ws_acc)
+        else:
+            self.tmv.tree_accept(self.tmv.ACCEPT_SAMPLE, self.tokens, self.p, self.n_nodes, self.anc, self.depth,
+                                 self.status, self.accept_len, self.path, self.next_token, draft_q=self.qd,
+                                 seed=self.w.seed, step=self.w.step, workspace=self.ws_acc)
 
     def commit(self):
         self.tmv.kv_commit_path(self.k, self.v, self.prefix, self.n_nodes, self.accept_len, self.path, self.status,
                                 self.new_len, self.w.M_max)
 
+    def stages(self):
+        names = ["build", "attention", "accept", "commit"] if self.w.mode == "greedy" else ["build", "accept", "commit"]
+        return {n: getattr(self, n) for n in names}
+
     def step(self):
-        self.build()
-        self.attention()
-        self.accept()
-        self.commit()
+        for fn in self.stages().values():
+            fn()
 
 
 def set_bytes(w):
-    return w.q.nbytes + w.k.nbytes + w.v.nbytes + w.logits.nbytes + w.q.nbytes
+    if w.mode == "greedy":
+        return w.q.nbytes + w.k.nbytes + w.v.nbytes + w.logits.nbytes + w.q.nbytes
+    return w.p.nbytes + w.qd.nbytes
 
 
 # ---------------------------------------------------------------- counters from profiles/
@@ -124,15 +166,15 @@ def kernel_source_digest():
     return h.hexdigest()
 
 
-def traffic_from_profiles(kernel_key):
-    """HBM bytes per launch from committed rocprofv3 counter runs, or None when the
-    kernels changed since the counters were taken."""
+def traffic_from_profiles(kernel_key, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs of this workload, or
+    None when the kernels changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "hbm_counters.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_sha256") != kernel_source_digest():
+    if rec.get("source_sha256") != kernel_source_digest() or rec.get("workload", 2) != workload:
         return None
     k = rec.get("kernels", {}).get(kernel_key)
     return None if k is None else k.get("hbm_bytes_per_launch")
@@ -158,19 +200,49 @@ def cpu_baseline(w, budget_s):
             break
     node_tokens = steps * int(w.n_nodes.sum())
     return {"value": node_tokens / el, "unit": "node-tokens/s", "cores": 1, "kind": "oracle",
-            "sample": "%d full verify steps of the same 8B-layer workload (build, attention over all 1920 "
-                      "query rows, greedy accept over 61 x 128256 logits, commit), single thread, %.1f s"
-                      % (steps, el),
+            "sample": "%d full verify steps of the same workload (build, attention over all %d query rows, "
+                      "greedy accept over %d x %d logits, commit), single thread, %.1f s"
+                      % (steps, int(w.n_nodes.sum()) * w.Hq, int(w.n_nodes.sum()) + w.B, w.V, el),
             "ms_per_step": 1e3 * el / steps}
 
 
 # ---------------------------------------------------------------- main
+def make_sets(c, ti, tmv, torch):
+    """The rotating input sets of workload c (and the workspaces and caches they share)."""
+    w0 = ti.workload(c)
+    per_set = set_bytes(w0)
+    if c == 5:
+        n_sets = 1                                           # p and q: 1.08 GB per set
+    else:
+        n_sets = min(64, max(2 if per_set > MALL_BYTES else 16, math.ceil(2.5 * MALL_BYTES / per_set)))
+    dt = tmv.BF16 if w0.dtype == 1 else tmv.F32
+    ws_attn = None
+    if w0.mode == "greedy":
+        ws_attn = torch.zeros(tmv.tree_verify_attention_workspace(dt, w0.B, w0.M_max, w0.Hq, w0.Hkv, w0.d, w0.L_cap),
+                              dtype=torch.uint8, device="cuda")
+    mode = tmv.ACCEPT_GREEDY if w0.mode == "greedy" else tmv.ACCEPT_SAMPLE
+    ws_acc = torch.zeros(tmv.tree_accept_workspace(mode, w0.B, w0.M_max, w0.V), dtype=torch.uint8, device="cuda")
+    caches = None
+    if c == 5:
+        # [layer][b][head][slot][d] bf16 K and V caches (8.66 GB each), made on the device
+        shape = (w0.n_layers, w0.B, w0.Hkv, w0.L_cap, w0.d)
+        caches = (torch.zeros(shape, dtype=torch.bfloat16, device="cuda"),
+                  torch.ones(shape, dtype=torch.bfloat16, device="cuda"))
+    print("bench: workload %d, %d input set(s) of %.1f MB (%.0f MB total)"
+          % (c, n_sets, per_set / 1e6, n_sets * per_set / 1e6), file=sys.stderr, flush=True)
+    sets = [StepSet(tmv, torch, w0, ws_attn, ws_acc, caches)]
+    for i in range(1, n_sets):
+        sets.append(StepSet(tmv, torch, ti.workload(c, seed=20000 + 100 * c + i), ws_attn, ws_acc, caches))
+    return w0, sets
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 2000; 200 for workloads 3-5)")
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--kernel-reps", type=int, default=400, help="launches per stage in the duration graphs")
+    ap.add_argument("--kernel-reps", type=int, default=None, help="launches per stage in the duration graphs")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -180,29 +252,22 @@ def main():
         print("bench.py: this build measures one GPU only; --gpus %d is not supported "
               "(the multi-GPU sharding is described in the design notes, not run)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    c = args.workload
+    big = c in (3, 4, 5)
+    steps = args.steps if args.steps is not None else (200 if big else 2000)
+    reps = args.kernel_reps if args.kernel_reps is not None else (40 if big else 400)
 
     import torch
     import tmv_inputs as ti
     import tree_masked_verification_amd as tmv
 
     torch.cuda.init()
-    w0 = ti.workload(2)
-    per_set = set_bytes(w0)
-    n_sets = max(16, math.ceil(2.5 * MALL_BYTES / per_set))
-    print("bench: %d input sets of %.1f MB (%.0f MB total)" % (n_sets, per_set / 1e6, n_sets * per_set / 1e6),
-          file=sys.stderr, flush=True)
-
-    ws_attn = torch.zeros(tmv.tree_verify_attention_workspace(tmv.BF16, w0.B, w0.M_max, w0.Hq, w0.Hkv, w0.d, w0.L_cap),
-                          dtype=torch.uint8, device="cuda")
-    ws_acc = torch.zeros(tmv.tree_accept_workspace(tmv.ACCEPT_GREEDY, w0.B, w0.M_max, w0.V), dtype=torch.uint8,
-                         device="cuda")
-    sets = [StepSet(tmv, torch, w0, ws_attn, ws_acc)]
-    for i in range(1, n_sets):
-        sets.append(StepSet(tmv, torch, ti.workload(2, seed=20000 + i), ws_attn, ws_acc))
+    w0, sets = make_sets(c, ti, tmv, torch)
+    n_sets = len(sets)
     torch.cuda.synchronize()
 
     # eager warm-up (also validates every stage once per set)
-    for i in range(max(args.warmup, n_sets)):
+    for i in range(max(min(args.warmup, 4 * n_sets), n_sets)):
         sets[i % n_sets].step()
     torch.cuda.synchronize()
     st = torch.stack([s.status for s in sets]).cpu()
@@ -212,7 +277,7 @@ def main():
 
     # ---- the step loop as HIP graphs: one graph runs a step on each input set in turn
     # (n_sets steps back to back), a second one the first `rem` of them, so that exactly
-    # --steps steps are timed with one replay per n_sets steps
+    # `steps` steps are timed with one replay per n_sets steps
     stream = torch.cuda.Stream()
 
     def capture(n):
@@ -222,7 +287,7 @@ def main():
                 sets[i].step()
         return g
 
-    full_reps, rem = divmod(args.steps, n_sets)
+    full_reps, rem = divmod(steps, n_sets)
     with torch.cuda.stream(stream):
         g_all = capture(n_sets)
         g_rem = capture(rem) if rem else None
@@ -239,23 +304,20 @@ def main():
         g_rem.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    sec_per_step = (t1 - t0) / args.steps
+    sec_per_step = (t1 - t0) / steps
     nodes = int(w0.n_nodes.sum())
     value = nodes / sec_per_step
-    print("bench: %.2f us/step, %.3g node-tokens/s, mean accept length %.2f"
+    print("bench: %.2f us/step, %.4g node-tokens/s, mean accept length %.2f"
           % (sec_per_step * 1e6, value, mean_accept), file=sys.stderr, flush=True)
 
     # ---- timed region 2: per-stage launch durations (HIP events on the launch stream)
-    reps = args.kernel_reps
-    stages = {"build": lambda s: s.build, "attention": lambda s: s.attention, "accept": lambda s: s.accept,
-              "commit": lambda s: s.commit}
     durations = {}
     with torch.cuda.stream(stream):
-        for name, fn in stages.items():
+        for name in sets[0].stages():
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=stream):
                 for r in range(reps):
-                    fn(sets[r % n_sets])()
+                    sets[r % n_sets].stages()[name]()
             g.replay()                      # warm
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
@@ -267,35 +329,36 @@ def main():
             del g
     torch.cuda.synchronize()
 
-    # ---- algorithmic work per launch
-    depth = sets[0].depth.cpu().numpy()[0, 1:nodes + 1].tolist()
-    attn_bytes, attn_flops = attention_work(depth, int(w0.prefix[0]), w0.Hq, w0.Hkv, w0.d)
-    attn_bytes += (w0.M_max + 1) * (w0.D_max + 2) * 4                  # ancestor table + depths
-    acc_bytes = (nodes + 1) * w0.V * 4 + (w0.M_max + 1) * 4
-    build_bytes = (w0.M_max + 1) * 4 * (w0.D_max + 3)
-    commit_bytes = int(round(2 * 2 * w0.Hkv * w0.d * 2 * mean_accept))   # rows read + written, K and V
-    work = {"build": (build_bytes, 0), "attention": (attn_bytes, attn_flops), "accept": (acc_bytes, 0),
-            "commit": (commit_bytes, 0)}
+    # ---- algorithmic work per launch (averaged over the input sets)
+    works = [workload_work(s.w, s.depth.cpu().numpy(), s.accept_len.cpu().numpy()) for s in sets]
+    work = {k: (sum(x[k][0] for x in works) / n_sets, sum(x[k][1] for x in works) / n_sets) for k in works[0]}
     kernels = {}
-    for name, (nb, fl) in work.items():
-        us = durations[name]
+    for name, us in durations.items():
+        nb, fl = work[name]
         gbs = nb / (us * 1e-6) / 1e9
-        kernels[name] = {"avg_us": round(us, 3), "bytes": nb, "GB/s": round(gbs, 1),
+        kernels[name] = {"avg_us": round(us, 3), "bytes": int(nb), "GB/s": round(gbs, 1),
                          "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
         if fl:
             tf = fl / (us * 1e-6) / 1e12
-            kernels[name]["flops"] = fl
+            kernels[name]["flops"] = int(fl)
             kernels[name]["TFLOP/s"] = round(tf, 1)
             kernels[name]["frac_mfma"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
-    dominant = max(("attention", "accept"), key=lambda k: durations[k])
-    nb = work[dominant][0]
-    achieved = nb / (durations[dominant] * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic_from_profiles(dominant)}
-    attention_roofline = {"bound": "hbm", "kernel": "attention",
-                          "achieved": kernels["attention"]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": kernels["attention"]["frac_hbm"], "traffic": traffic_from_profiles("attention")}
+
+    def roofline(name):
+        """The stage against the roof that bounds it: MFMA when its flops take longer at
+        peak than its bytes do, HBM otherwise."""
+        nb, fl = work[name]
+        us = durations[name]
+        if fl and fl / (MFMA_BF16_PEAK_TFLOPS * 1e12) > nb / (HBM_PEAK_GBS * 1e9):
+            ach = fl / (us * 1e-6) / 1e12
+            return {"bound": "mfma", "kernel": name, "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": traffic_from_profiles(name, c)}
+        ach = nb / (us * 1e-6) / 1e9
+        return {"bound": "hbm", "kernel": name, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(name, c)}
+
+    dominant = max((k for k in durations if k != "build"), key=lambda k: durations[k])
 
     if args.copy_probe:
         n = 256 << 20
@@ -308,18 +371,21 @@ def main():
               file=sys.stderr, flush=True)
 
     cpu = None
-    if not args.no_cpu:
+    if not args.no_cpu and c in (1, 2):
         cpu = cpu_baseline(w0, args.cpu_budget)
 
+    config = {"workload": w0.name, "batch": w0.B,
+              "prefix": int(w0.prefix[0]) if w0.B == 1 else [int(x) for x in w0.prefix],
+              "tree_nodes": nodes, "tree_depth": w0.D_max, "heads_q_kv": [w0.Hq, w0.Hkv], "head_dim": w0.d,
+              "vocab": w0.V, "accept": w0.mode, "layers": w0.n_layers, "input_sets": n_sets,
+              "mean_accept_len": round(mean_accept, 3)}
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "node-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC, "value": round(value, 1), "unit": "node-tokens/s", "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": round(sec_per_step * 1e3, 6), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w0.name, "batch": w0.B, "prefix": int(w0.prefix[0]), "tree_nodes": nodes,
-                   "tree_depth": w0.D_max, "heads_q_kv": [w0.Hq, w0.Hkv], "head_dim": w0.d, "vocab": w0.V,
-                   "accept": "greedy", "input_sets": n_sets, "mean_accept_len": round(mean_accept, 3)},
-        "roofline": roofline,
-        "attention_roofline": attention_roofline,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32" if w0.dtype == 0 else "bf16", "data": "synthetic",
+        "config": config,
+        "roofline": roofline(dominant),
+        "attention_roofline": roofline("attention") if "attention" in durations else None,
         "kernels": kernels,
         "cpu_baseline": cpu,
     }

@@ -125,7 +125,8 @@ int tmv_tree_build_ancestors(int B, int M_max, int D_max, int parent_format,
  *             row per node and query head; rows of inert nodes (beyond M_b, invalid, or
  *             in a failed sequence) are written as 0.
  *   GQA: query head h reads KV head h / (Hq/Hkv).  Requires Hq % Hkv == 0, d in {64,128},
- *        Hq/Hkv <= 16, 1 <= L_cap.
+ *        Hq/Hkv <= 16, 1 <= L_cap, q and the caches 16-byte aligned with strides that
+ *        are multiples of 16 bytes (bf16: out too; TMV_ERR_ARG otherwise).
  *   workspace: tmv_tree_verify_attention_workspace() bytes, 16-byte aligned.  It opens
  *        with a fixed 1 KiB block of arrival counters (one per split row block; the last
  *        split of a block to finish merges it) followed by the split-KV partials, which

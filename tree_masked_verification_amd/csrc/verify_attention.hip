@@ -1373,10 +1373,16 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
 }
 
 // --------------------------------------------------------------------------- fp32 kernel
-// One wave per (sequence, node, query head).  Tokens are visited in chunks of 64 (one per
-// lane for the scores); the output is accumulated with lanes over the head dims.
+// One wave per (sequence, node, query head).  Tokens are visited in chunks of 64, one per
+// lane for the scores: the lane's K row arrives as D/4 independent 16-byte loads against
+// the query held in registers, and the next chunk's rows are requested before this
+// chunk's V rows are consumed.  For P V the visible rows of the chunk are taken in
+// batches of 64 / (D/64), their addresses made wave-uniform with readlane, so every V load
+// is one coalesced row and a batch's loads are all in flight together; lanes hold dims
+// lane and lane + 64.
+template <int D>
 __global__ void __launch_bounds__(256)
-tree_attn_f32_kernel(int B, int M_max, int D_max, int Hq, int Hkv, int d,
+tree_attn_f32_kernel(int B, int M_max, int D_max, int Hq, int Hkv,
                      const float *__restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
                      const float *__restrict__ kc, const float *__restrict__ vc,
                      int64_t ks0, int64_t ks1, int64_t ks2, int L_cap,
@@ -1385,7 +1391,10 @@ tree_attn_f32_kernel(int B, int M_max, int D_max, int Hq, int Hkv, int d,
                      int32_t *__restrict__ status, float scale,
                      float *__restrict__ out, int64_t os0, int64_t os1, int64_t os2)
 {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    constexpr int DV = D / 64;                 // output dims per lane
+    constexpr int kBatch = 64 / DV;            // V rows in flight per batch
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + wv;
     if (item >= static_cast<int64_t>(B) * M_max * Hq) return;
     const int h = static_cast<int>(item % Hq);
@@ -1403,47 +1412,83 @@ tree_attn_f32_kernel(int B, int M_max, int D_max, int Hq, int Hkv, int d,
     }
     const int dep = (st == TMV_OK && j <= M) ? depth[static_cast<int64_t>(b) * R + j] : 0;
     if (dep < 1) {
-        for (int e = lane; e < d; e += 64) o[e] = 0.f;
+#pragma unroll
+        for (int e = 0; e < DV; ++e) o[lane + 64 * e] = 0.f;
         return;
     }
     const float *qp = q + b * qs0 + static_cast<int64_t>(j - 1) * qs1 + h * qs2;
+    float4 qv[D / 4];
+#pragma unroll
+    for (int e = 0; e < D / 4; ++e) qv[e] = reinterpret_cast<const float4 *>(qp)[e];
 
     const float *kb = kc + b * ks0 + kvh * ks1;
     const float *vb = vc + b * ks0 + kvh * ks1;
     const int32_t *arow = anc + (static_cast<int64_t>(b) * R + j) * W;
     const int total = P + dep;            // visible tokens: prefix then the path
-    float m = -INFINITY, l = 0.f, acc0 = 0.f, acc1 = 0.f;
-    for (int t0 = 0; t0 < total; t0 += 64) {
+    const int ks2_32 = static_cast<int>(ks2);
+    // slot of the lane's token in chunk t0 (-1 past the visible tokens) and its K row
+    auto slot_of = [&](int t0) {
         const int idx = t0 + lane;
-        int slot = -1;
-        if (idx < P) slot = idx;
-        else if (idx < total) slot = P + arow[idx - P] - 1;
+        return idx < P ? idx : (idx < total ? P + arow[idx - P] - 1 : -1);
+    };
+    auto load_k = [&](int slot, float4 (&kv)[D / 4]) {
+        const float4 *kr = reinterpret_cast<const float4 *>(kb + static_cast<int64_t>(slot < 0 ? 0 : slot) * ks2);
+#pragma unroll
+        for (int e = 0; e < D / 4; ++e) kv[e] = kr[e];
+    };
+    float m = -INFINITY, l = 0.f, acc[DV];
+#pragma unroll
+    for (int e = 0; e < DV; ++e) acc[e] = 0.f;
+    int slot = slot_of(0);
+    float4 kv[D / 4];
+    load_k(slot, kv);
+    for (int t0 = 0; t0 < total; t0 += 64) {
         float s = -INFINITY;
         if (slot >= 0) {
-            const float *kr = kb + static_cast<int64_t>(slot) * ks2;
             float dot = 0.f;
-            for (int e = 0; e < d; ++e) dot = fmaf(qp[e], kr[e], dot);
+#pragma unroll
+            for (int e = 0; e < D / 4; ++e) {
+                dot = fmaf(qv[e].x, kv[e].x, dot);
+                dot = fmaf(qv[e].y, kv[e].y, dot);
+                dot = fmaf(qv[e].z, kv[e].z, dot);
+                dot = fmaf(qv[e].w, kv[e].w, dot);
+            }
             s = dot * scale;
+        }
+        // the next chunk's K rows go out before this chunk's V rows are waited for
+        const int cur = slot;
+        if (t0 + 64 < total) {
+            slot = slot_of(t0 + 64);
+            load_k(slot, kv);
         }
         const float mnew = fmaxf(m, tmv::wave_max(s));
         const float alpha = expf(m - mnew);
-        const float p = slot >= 0 ? expf(s - mnew) : 0.f;
+        const float p = cur >= 0 ? expf(s - mnew) : 0.f;
         l = l * alpha + tmv::wave_sum(p);
-        acc0 *= alpha;
-        acc1 *= alpha;
+#pragma unroll
+        for (int e = 0; e < DV; ++e) acc[e] *= alpha;
         const int n = min(64, total - t0);
-        for (int t = 0; t < n; ++t) {
-            const float pt = __shfl(p, t, 64);
-            const int sl = __shfl(slot, t, 64);
-            const float *vr = vb + static_cast<int64_t>(sl) * ks2;
-            if (lane < d) acc0 = fmaf(pt, vr[lane], acc0);
-            if (lane + 64 < d) acc1 = fmaf(pt, vr[lane + 64], acc1);
+        for (int u0 = 0; u0 < n; u0 += kBatch) {
+            float vv[kBatch][DV], pv[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int t = u0 + u < n ? u0 + u : n - 1;         // padding lanes repeat a row, weight 0
+                const int sl = __builtin_amdgcn_readlane(cur, t);
+                pv[u] = u0 + u < n ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), t)) : 0.f;
+                const float *vr = vb + static_cast<uint32_t>(sl * ks2_32);     // slot * stride < 2^31 (host-checked)
+#pragma unroll
+                for (int e = 0; e < DV; ++e) vv[u][e] = vr[lane + 64 * e];
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+                for (int e = 0; e < DV; ++e) acc[e] = fmaf(pv[u], vv[u][e], acc[e]);
         }
         m = mnew;
     }
     const float inv = 1.f / l;
-    if (lane < d) o[lane] = acc0 * inv;
-    if (lane + 64 < d) o[lane + 64] = acc1 * inv;
+#pragma unroll
+    for (int e = 0; e < DV; ++e) o[lane + 64 * e] = acc[e] * inv;
 }
 
 template <int D, int WR>
@@ -1524,11 +1569,21 @@ extern "C" int tmv_tree_verify_attention(int dtype, int B, int M_max, int D_max,
         const int64_t items = static_cast<int64_t>(B) * M_max * Hq;
         const int64_t blocks = (items + 3) / 4;
         if (blocks > 0x7fffffff) return TMV_ERR_ARG;
-        hipLaunchKernelGGL(tree_attn_f32_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, B, M_max,
-                           D_max, Hq, Hkv, d, static_cast<const float *>(q), q_stride[0], q_stride[1], q_stride[2],
-                           static_cast<const float *>(k_cache), static_cast<const float *>(v_cache), kv_stride[0],
-                           kv_stride[1], kv_stride[2], L_cap, prefix_len, n_nodes, anc, depth, status, scale,
-                           static_cast<float *>(out), o_stride[0], o_stride[1], o_stride[2]);
+        // 16-byte loads of q and K rows need 16-byte aligned rows; slot offsets within a
+        // (sequence, head) are 32-bit
+        if (!aligned16(q) || !aligned16(k_cache) || ((q_stride[0] | q_stride[1] | q_stride[2] | kv_stride[0] |
+                                                       kv_stride[1] | kv_stride[2]) & 3))
+            return TMV_ERR_ARG;
+        if (static_cast<int64_t>(L_cap) * kv_stride[2] >= (int64_t(1) << 31)) return TMV_ERR_ARG;
+#define TMV_LAUNCH_F32(DD)                                                                                       \
+        hipLaunchKernelGGL(tree_attn_f32_kernel<DD>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, B, M_max, \
+                           D_max, Hq, Hkv, static_cast<const float *>(q), q_stride[0], q_stride[1], q_stride[2],  \
+                           static_cast<const float *>(k_cache), static_cast<const float *>(v_cache), kv_stride[0], \
+                           kv_stride[1], kv_stride[2], L_cap, prefix_len, n_nodes, anc, depth, status, scale,     \
+                           static_cast<float *>(out), o_stride[0], o_stride[1], o_stride[2])
+        if (d == 64) TMV_LAUNCH_F32(64);
+        else TMV_LAUNCH_F32(128);
+#undef TMV_LAUNCH_F32
         return tmv_host::launch_status(hipGetLastError());
     }
 

@@ -18,9 +18,9 @@ Timed regions (both after --warmup untimed steps):
   1. throughput: --steps steps, bracketed by torch.cuda.synchronize(); the steps run as
      replays of one HIP graph that holds a step on every input set in turn (plus one graph
      for the remainder); value = verified node-tokens per second.
-  2. kernel durations: for each stage, one HIP graph of back-to-back launches over the
-     rotating sets, timed with HIP events recorded on the stream the kernels run on;
-     the average launch duration feeds the roofline figures.
+  2. kernel durations: the step loop again, launched eagerly behind a short spin kernel
+     so that the launches queue up, with HIP events recorded on the launch stream between
+     stages; the average duration of each stage within the step feeds the roofline figures.
 The oracle (tests-only CPU implementation) is timed on a bounded sample of the default
 workload for the cpu_baseline field.
 
@@ -228,11 +228,11 @@ def make_sets(c, ti, tmv, torch):
         shape = (w0.n_layers, w0.B, w0.Hkv, w0.L_cap, w0.d)
         caches = (torch.zeros(shape, dtype=torch.bfloat16, device="cuda"),
                   torch.ones(shape, dtype=torch.bfloat16, device="cuda"))
-    print("bench: workload %d, %d input set(s) of %.1f MB (%.0f MB total)"
-          % (c, n_sets, per_set / 1e6, n_sets * per_set / 1e6), file=sys.stderr, flush=True)
     sets = [StepSet(tmv, torch, w0, ws_attn, ws_acc, caches)]
     for i in range(1, n_sets):
         sets.append(StepSet(tmv, torch, ti.workload(c, seed=20000 + 100 * c + i), ws_attn, ws_acc, caches))
+    print("bench: workload %d, %d input set(s) of %.1f MB (%.0f MB total)"
+          % (c, n_sets, per_set / 1e6, n_sets * per_set / 1e6), file=sys.stderr, flush=True)
     return w0, sets
 
 
@@ -242,7 +242,6 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default 2000; 200 for workloads 3-5)")
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--kernel-reps", type=int, default=None, help="launches per stage in the duration graphs")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -255,7 +254,6 @@ def main():
     c = args.workload
     big = c in (3, 4, 5)
     steps = args.steps if args.steps is not None else (200 if big else 2000)
-    reps = args.kernel_reps if args.kernel_reps is not None else (40 if big else 400)
 
     import torch
     import tmv_inputs as ti
@@ -310,23 +308,25 @@ def main():
     print("bench: %.2f us/step, %.4g node-tokens/s, mean accept length %.2f"
           % (sec_per_step * 1e6, value, mean_accept), file=sys.stderr, flush=True)
 
-    # ---- timed region 2: per-stage launch durations (HIP events on the launch stream)
-    durations = {}
+    # ---- timed region 2: per-stage durations inside the step sequence.  The steps are
+    # launched eagerly with a HIP event on the launch stream between stages; they queue up
+    # behind a short spin kernel, so the GPU never waits for the host between them and each
+    # interval is one stage's kernels in the context of a real step (a stage timed alone,
+    # back to back with itself, runs faster: the neighbouring stages' traffic is missing).
+    n_timed = min(steps, 40 if big else 200)
+    names = list(sets[0].stages())
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(n_timed)]
     with torch.cuda.stream(stream):
-        for name in sets[0].stages():
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                for r in range(reps):
-                    sets[r % n_sets].stages()[name]()
-            g.replay()                      # warm
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
-            e1.synchronize()
-            durations[name] = e0.elapsed_time(e1) * 1e3 / reps      # us per launch
-            del g
+        torch.cuda._sleep(30_000_000)          # tens of ms at the shader clock: the launches below queue up
+        for i in range(n_timed):
+            s = sets[i % n_sets]
+            evs[i][0].record(stream)
+            for k, name in enumerate(names):
+                s.stages()[name]()
+                evs[i][k + 1].record(stream)
+    stream.synchronize()
+    durations = {name: 1e3 * sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(n_timed)) / n_timed
+                 for k, name in enumerate(names)}
     torch.cuda.synchronize()
 
     # ---- algorithmic work per launch (averaged over the input sets)

@@ -18,9 +18,10 @@ Timed regions (both after --warmup untimed steps):
   1. throughput: --steps steps, bracketed by torch.cuda.synchronize(); the steps run as
      replays of one HIP graph that holds a step on every input set in turn (plus one graph
      for the remainder); value = verified node-tokens per second.
-  2. kernel durations: the step loop again, launched eagerly behind a short spin kernel
-     so that the launches queue up, with HIP events recorded on the launch stream between
-     stages; the average duration of each stage within the step feeds the roofline figures.
+  2. kernel durations: for each stage, one HIP graph of back-to-back launches over the
+     rotating sets (device copies added until the stage's own inputs exceed the Infinity
+     Cache 2.5 times), timed with HIP events recorded on the stream the kernels run on;
+     the average launch duration feeds the roofline figures.
 The oracle (tests-only CPU implementation) is timed on a bounded sample of the default
 workload for the cpu_baseline field.
 
@@ -141,6 +142,17 @@ class StepSet:
         self.tmv.kv_commit_path(self.k, self.v, self.prefix, self.n_nodes, self.accept_len, self.path, self.status,
                                 self.new_len, self.w.M_max)
 
+    def clone(self):
+        """A copy of this set at new device addresses (inputs copied, outputs fresh)."""
+        other = object.__new__(StepSet)
+        other.__dict__.update(self.__dict__)
+        names = ["parents", "n_nodes", "prefix", "tokens", "anc", "depth", "status", "accept_len", "path",
+                 "next_token", "new_len"]
+        names += ["q", "k", "v", "out", "logits"] if self.w.mode == "greedy" else ["p", "qd"]
+        for n in names:
+            setattr(other, n, getattr(self, n).clone())
+        return other
+
     def stages(self):
         names = ["build", "attention", "accept", "commit"] if self.w.mode == "greedy" else ["build", "accept", "commit"]
         return {n: getattr(self, n) for n in names}
@@ -231,8 +243,17 @@ def make_sets(c, ti, tmv, torch):
     sets = [StepSet(tmv, torch, w0, ws_attn, ws_acc, caches)]
     for i in range(1, n_sets):
         sets.append(StepSet(tmv, torch, ti.workload(c, seed=20000 + 100 * c + i), ws_attn, ws_acc, caches))
-    print("bench: workload %d, %d input set(s) of %.1f MB (%.0f MB total)"
-          % (c, n_sets, per_set / 1e6, n_sets * per_set / 1e6), file=sys.stderr, flush=True)
+    # a stage timed alone must also rotate its own inputs through more than the Infinity
+    # Cache holds: add device copies of the generated sets (the same values at new
+    # addresses) until the smallest stage's inputs do
+    n_gen = n_sets
+    if c != 5 and per_set <= MALL_BYTES:
+        stage_bytes = min(w0.q.nbytes * 2 + w0.k.nbytes + w0.v.nbytes, w0.logits.nbytes)
+        n_total = min(96, max(n_sets, math.ceil(2.5 * MALL_BYTES / stage_bytes)))
+        for i in range(n_sets, n_total):
+            sets.append(sets[i % n_gen].clone())
+    print("bench: workload %d, %d input set(s) of %.1f MB (%d generated, %.0f MB total)"
+          % (c, len(sets), per_set / 1e6, n_gen, len(sets) * per_set / 1e6), file=sys.stderr, flush=True)
     return w0, sets
 
 
@@ -290,16 +311,20 @@ def main():
         g_all = capture(n_sets)
         g_rem = capture(rem) if rem else None
     torch.cuda.synchronize()
-    for _ in range(max(1, args.warmup // n_sets)):
-        g_all.replay()
+    # replays go to the stream the graphs were captured on (a replay on another stream
+    # measured ~20 % slower per step)
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, args.warmup // n_sets)):
+            g_all.replay()
     torch.cuda.synchronize()
 
     # ---- timed region 1: throughput
     t0 = time.perf_counter()
-    for _ in range(full_reps):
-        g_all.replay()
-    if g_rem is not None:
-        g_rem.replay()
+    with torch.cuda.stream(stream):
+        for _ in range(full_reps):
+            g_all.replay()
+        if g_rem is not None:
+            g_rem.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     sec_per_step = (t1 - t0) / steps
@@ -308,25 +333,26 @@ def main():
     print("bench: %.2f us/step, %.4g node-tokens/s, mean accept length %.2f"
           % (sec_per_step * 1e6, value, mean_accept), file=sys.stderr, flush=True)
 
-    # ---- timed region 2: per-stage durations inside the step sequence.  The steps are
-    # launched eagerly with a HIP event on the launch stream between stages; they queue up
-    # behind a short spin kernel, so the GPU never waits for the host between them and each
-    # interval is one stage's kernels in the context of a real step (a stage timed alone,
-    # back to back with itself, runs faster: the neighbouring stages' traffic is missing).
-    n_timed = min(steps, 40 if big else 200)
-    names = list(sets[0].stages())
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(n_timed)]
+    # ---- timed region 2: per-stage launch durations.  For each stage, one HIP graph of
+    # back-to-back launches over the rotating sets, replayed on its capture stream and timed
+    # with HIP events recorded on that stream (the kernels' own stream).
+    reps = 40 if big else 400
+    durations = {}
     with torch.cuda.stream(stream):
-        torch.cuda._sleep(30_000_000)          # tens of ms at the shader clock: the launches below queue up
-        for i in range(n_timed):
-            s = sets[i % n_sets]
-            evs[i][0].record(stream)
-            for k, name in enumerate(names):
-                s.stages()[name]()
-                evs[i][k + 1].record(stream)
-    stream.synchronize()
-    durations = {name: 1e3 * sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(n_timed)) / n_timed
-                 for k, name in enumerate(names)}
+        for name in sets[0].stages():
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for r in range(reps):
+                    sets[r % n_sets].stages()[name]()
+            g.replay()                      # warm
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            e1.synchronize()
+            durations[name] = e0.elapsed_time(e1) * 1e3 / reps      # us per launch
+            del g
     torch.cuda.synchronize()
 
     # ---- algorithmic work per launch (averaged over the input sets)

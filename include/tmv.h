@@ -16,10 +16,11 @@
  *     tensor's data_ptr), except the small int64 stride arrays, which are HOST arrays read
  *     during the call.  The library keeps no global state and allocates nothing; scratch
  *     memory comes from a caller workspace whose size the *_workspace call returns.  The
- *     accept workspace needs no initialisation; the attention workspace must be
- *     zero-filled once before its first use and every call leaves it ready for the next
- *     (see tmv_tree_verify_attention).  Calls that may run at the same time (different
- *     streams) must not share a workspace.
+ *     attention and sampling workspaces hold counters: zero-fill them once before their
+ *     first use; every completed call leaves them ready for the next call of any shape
+ *     they are large enough for (after a TMV_ERR_DEVICE status, zero-fill again).  The
+ *     greedy-accept workspace needs no initialisation.  Calls that may run at the same
+ *     time (different streams) must not share a workspace.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are asynchronous; none
  *     synchronises the host.
  *   - The return value reports problems the host can see (TMV_ERR_ARG: bad sizes, null
@@ -182,7 +183,11 @@ int tmv_tree_verify_attention(int dtype, int B, int M_max, int D_max, int Hq, in
  *              GREEDY.
  *   accept_len out int32 [B]; path out int32 [B][D_max] (node ids root->leaf, then 0);
  *   next_token out int32 [B].  All 0 for a failed sequence.
- *   workspace: tmv_tree_accept_workspace() bytes, 16-byte aligned.
+ *   workspace: tmv_tree_accept_workspace() bytes, 16-byte aligned.  SAMPLE: a working
+ *              distribution per sequence, then per-sequence barrier counts -- K workgroups
+ *              (one vocabulary slice each) walk a sequence together and meet after every
+ *              full-row pass; zero-fill once.  A wait for the other slices that exceeds 2 ms
+ *              ends the walk with status TMV_ERR_DEVICE (never a hang).
  */
 size_t tmv_tree_accept_workspace(int mode, int B, int M_max, int V);
 int tmv_tree_accept(int mode, int B, int M_max, int D_max, int V,

@@ -63,8 +63,8 @@ def _load():
         lib.tmvref_commit.argtypes = [I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
         lib.tmvref_philox_words.argtypes = [U64, U64, I64, P]
         lib.tmvref_philox_words.restype = None
-        lib.tmvref_sample_accept_test.argtypes = [U64, U64, U64, U64, U64]
-        lib.tmvref_sample_draw.argtypes = [P, I, U64]
+        lib.tmvref_sample_accept_test.argtypes = [U64, U64, U64, U64, U64, U64, U64]
+        lib.tmvref_sample_draw.argtypes = [P, P, I, U64]
         _lib = lib
     return _lib
 
@@ -185,10 +185,16 @@ def philox_words(seed, stream, n):
     return out
 
 
-def sample_accept_test(u24, wq_x, S, w_x, SQ) -> bool:
-    return bool(_load().tmvref_sample_accept_test(int(u24), int(wq_x), int(S), int(w_x), int(SQ)))
+def sample_accept_test(u24, wq_x, T, r_x, SQ) -> bool:
+    """U * WQ(x) * T < R(x) * SQ * 2^24 on Python integers (T, r_x < 2^128)."""
+    m = (1 << 64) - 1
+    return bool(_load().tmvref_sample_accept_test(int(u24), int(wq_x), int(T) & m, int(T) >> 64, int(r_x) & m,
+                                                  int(r_x) >> 64, int(SQ)))
 
 
 def sample_draw(w, word) -> int:
-    w = _c(w, np.uint64)
-    return int(_load().tmvref_sample_draw(_p(w), w.shape[0], int(word)))
+    """Inverse-CDF draw over integer weights w (Python ints < 2^128)."""
+    m = (1 << 64) - 1
+    lo = np.array([int(x) & m for x in w], np.uint64)
+    hi = np.array([int(x) >> 64 for x in w], np.uint64)
+    return int(_load().tmvref_sample_draw(_p(lo), _p(hi), len(w), int(word)))

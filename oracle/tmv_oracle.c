@@ -32,7 +32,8 @@
  *     smallest node id wins; the bonus token after a full accept is the teacher's
  *     choice at the last accepted node.
  *   - sampling on a tree: children of a node are tried in ascending id, each by the
- *     chain rule against the current residual; exact integer fixed point (below).
+ *     chain rule against the current residual, kept in threshold form; exact integer
+ *     fixed point (below).
  *   - RNG: Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11), key {seed, (step<<32)|b},
  *     block n uses counter {n+1,0,0,0}; draw n is 64-bit word n%4 of block n/4.
  */
@@ -322,77 +323,95 @@ void tmvref_philox_words(uint64_t seed, uint64_t stream, int64_t n, uint64_t *ou
  * Sampling acceptance [SDH, modified rejection sampling and its FAQ], extended to trees
  * by trying a node's children one after another against the current residual.
  *
+ * Threshold form (mathematics; our reading of how the residual is iterated): at node u
+ * the teacher row p and the draft row q stay fixed, so the distribution left after j
+ * refusals is (p - c_j q)+ normalised, with c_0 = 0 and c_{j+1} = c_j + sum (p - c_j q)+.
+ * (One refusal maps r = (p - c q)+ / Z to (r - q)+ normalised, and where it is positive
+ * r - q equals (p - (c + Z) q) / Z.)
+ *
  * Exact integer fixed point (our reading; the pages give real-valued formulas):
- *   WP_u(x) = floor(p[u][x] * 2^32), WQ_u(x) = floor(q[u][x] * 2^32); SP, SQ exact sums.
- *   The working distribution is (W, S) with S = sum W.  After loading or updating it,
- *   if bitlen(S) > 48 every W is shifted right by bitlen(S) - 48 and S recomputed.
- *   Child c with token x, draw U = word >> 40 (24 bits):
- *     accept  iff  U * WQ_u(x) * S < W(x) * SQ_u * 2^24     (i.e. u*q(x) < p_cur(x))
- *     reject  ->   W(y) = max(0, W(y)*SQ_u - WQ_u(y)*S), S = sum, renormalise
- *                  (kept unchanged if the residual is empty)
- *   Draw from (W,S) with word: t = floor((word >> 32) * S / 2^32), token = min x with
- *   sum_{y<=x} W(y) > t.  Stop at the first node whose children are all rejected
+ *   WP(y) = floor(p[u][y] * 2^31), WQ(y) = floor(q[u][y] * 2^31); SP, SQ their exact
+ *   sums.  At a node without children q is not read and SQ = 1, WQ = 0.
+ *   State (M, T): R(y) = max(0, WP(y) * SQ - WQ(y) * M), T = sum R > 0; M = 0 on arrival
+ *   (R = WP * SQ, i.e. p itself; M / SP plays c_j).
+ *   Child c with token x, U = word >> 40 (24 bits):
+ *     accept  iff  U * WQ(x) * T < R(x) * SQ * 2^24     (i.e. u * q(x) < p_cur(x))
+ *     refuse  ->   M' = M + floor(T / SQ); the state becomes (M', sum R_M') unless that
+ *                  sum is 0 (empty residual: the state is kept)
+ *   Draw with word: t = floor((word >> 32) * T / 2^32), the token is the least x with
+ *   sum_{y<=x} R(y) > t.  Stop at the first node whose children are all refused
  *   (correction) or at a node without children (bonus), drawing next_token there.
+ *   Bounds: V <= 2^24 and M_max * V < 2^33 give SP, SQ < 2^55, M < 2^64, R < 2^87,
+ *   T < 2^111 and both sides of the accept test < 2^166.
  * Rows visited with entries outside [0,1] / non-finite, a zero p row, a zero q row
  * under a node with children, or a live token outside [0,V) set INPUT.
  *   p, q  [B][M_max+1][V] fp32 (row u = distribution after node u; row 0 after the prefix)
  * ---------------------------------------------------------------------------------- */
-static int bitlen128(u128 x)
-{
-    int n = 0;
-    while (x) { ++n; x >>= 1; }
-    return n;
-}
 
 /* quantise row u of a distribution tensor; returns 0 on a malformed entry */
-static int quantise_row(const float *row, int V, u128 *w, u128 *sum)
+static int quantise_row(const float *row, int V, uint64_t *w, uint64_t *sum)
 {
-    u128 s = 0;
+    uint64_t s = 0;
     for (int x = 0; x < V; ++x) {
         double val = (double)row[x];
         if (!(val >= 0.0 && val <= 1.0)) return 0;      /* also rejects NaN */
-        w[x] = (u128)(uint64_t)floor(val * 4294967296.0);
+        w[x] = (uint64_t)floor(val * 2147483648.0);
         s += w[x];
     }
     *sum = s;
     return 1;
 }
 
-static void renormalise(u128 *w, int V, u128 *sum)
+static u128 residual_at(uint64_t wp, uint64_t wq, uint64_t SQ, uint64_t M)
 {
-    int bl = bitlen128(*sum);
-    if (bl <= 48) return;
-    int sh = bl - 48;
-    u128 s = 0;
-    for (int x = 0; x < V; ++x) { w[x] >>= sh; s += w[x]; }
-    *sum = s;
+    u128 a = (u128)wp * SQ, c = (u128)wq * M;
+    return a > c ? a - c : 0;
 }
 
-static int draw_token(const u128 *w, int V, u128 S, uint64_t word)
+/* a * b as three little-endian 64-bit words */
+static void mul_u128_u64(u128 a, uint64_t b, uint64_t out[3])
 {
-    u128 t = (((u128)(word >> 32)) * S) >> 32;
-    u128 c = 0;
+    u128 lo = (u128)(uint64_t)a * b, hi = (u128)(uint64_t)(a >> 64) * b;
+    u128 mid = (lo >> 64) + (uint64_t)hi;
+    out[0] = (uint64_t)lo;
+    out[1] = (uint64_t)mid;
+    out[2] = (uint64_t)(hi >> 64) + (uint64_t)(mid >> 64);
+}
+
+static int accept_test(uint64_t u24, uint64_t wq_x, u128 T, u128 r_x, uint64_t SQ)
+{
+    uint64_t l[3], r[3];
+    mul_u128_u64(T, u24 * wq_x, l);
+    mul_u128_u64(r_x << 24, SQ, r);
+    for (int i = 2; i >= 0; --i)
+        if (l[i] != r[i]) return l[i] < r[i];
+    return 0;
+}
+
+/* floor(word_hi * T / 2^32) without overflow for T < 2^127 */
+static u128 draw_target(uint64_t word, u128 T)
+{
+    const uint64_t wh = word >> 32;
+    return (u128)wh * (T >> 32) + (((u128)wh * (uint64_t)(T & 0xffffffffu)) >> 32);
+}
+
+/* exported for pins: the integer accept test and the inverse-CDF draw on one row */
+int tmvref_sample_accept_test(uint64_t u24, uint64_t wq_x, uint64_t T_lo, uint64_t T_hi, uint64_t r_lo,
+                              uint64_t r_hi, uint64_t SQ)
+{
+    return accept_test(u24, wq_x, ((u128)T_hi << 64) | T_lo, ((u128)r_hi << 64) | r_lo, SQ);
+}
+
+int tmvref_sample_draw(const uint64_t *w_lo, const uint64_t *w_hi, int V, uint64_t word)
+{
+    u128 T = 0, c = 0;
+    for (int x = 0; x < V; ++x) T += ((u128)w_hi[x] << 64) | w_lo[x];
+    const u128 t = draw_target(word, T);
     for (int x = 0; x < V; ++x) {
-        c += w[x];
+        c += ((u128)w_hi[x] << 64) | w_lo[x];
         if (c > t) return x;
     }
-    return V - 1;   /* unreachable: t < S */
-}
-
-/* exported for pins: the integer accept test and the inverse-CDF draw on one element */
-int tmvref_sample_accept_test(uint64_t u24, uint64_t wq_x, uint64_t S, uint64_t w_x, uint64_t SQ)
-{
-    return (u128)u24 * wq_x * S < ((u128)w_x * SQ) << 24;
-}
-
-int tmvref_sample_draw(const uint64_t *w, int V, uint64_t word)
-{
-    u128 *ww = (u128 *)malloc(sizeof(u128) * (size_t)V);
-    u128 S = 0;
-    for (int x = 0; x < V; ++x) { ww[x] = w[x]; S += w[x]; }
-    int r = draw_token(ww, V, S, word);
-    free(ww);
-    return r;
+    return V - 1;   /* unreachable: t < T */
 }
 
 int tmvref_accept_sample(int B, int M_max, int D_max, int V, const int32_t *tokens,
@@ -400,13 +419,13 @@ int tmvref_accept_sample(int B, int M_max, int D_max, int V, const int32_t *toke
                          const int32_t *n_nodes, const int32_t *anc, const int32_t *depth,
                          int32_t *status, int32_t *accept_len, int32_t *path, int32_t *next_token)
 {
-    if (B < 0 || M_max < 0 || D_max < 0 || V <= 0) return REF_ERR_ARG;
+    if (B < 0 || M_max < 0 || D_max < 0 || V <= 0 || V > (1 << 24)) return REF_ERR_ARG;
+    if ((uint64_t)M_max * (uint64_t)V >= (1ull << 33)) return REF_ERR_ARG;
     const int W = D_max + 1, R = M_max + 1;
-    u128 *w = (u128 *)malloc(sizeof(u128) * (size_t)V);
-    u128 *wq = (u128 *)malloc(sizeof(u128) * (size_t)V);
-    u128 *wn = (u128 *)malloc(sizeof(u128) * (size_t)V);
+    uint64_t *wp = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)V);
+    uint64_t *wq = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)V);
     int32_t *kids = (int32_t *)malloc(sizeof(int32_t) * (size_t)R);
-    if (!w || !wq || !wn || !kids) { free(w); free(wq); free(wn); free(kids); return REF_ERR_ARG; }
+    if (!wp || !wq || !kids) { free(wp); free(wq); free(kids); return REF_ERR_ARG; }
 
     for (int b = 0; b < B; ++b) {
         accept_len[b] = 0;
@@ -426,44 +445,43 @@ int tmvref_accept_sample(int B, int M_max, int D_max, int V, const int32_t *toke
 
         uint64_t n = 0;
         int u = 0, acc = 0, out_tok = 0;
-        u128 S = 0;
-        if (!bad && !(quantise_row(pb, V, w, &S) && S > 0)) bad = 1;
-        if (!bad) renormalise(w, V, &S);
         while (!bad) {
             int nk = 0;
             for (int c = 1; c <= M; ++c)
                 if (Dp[c] >= 1 && A[(int64_t)c * W + 1] == u) kids[nk++] = c;
-            if (nk == 0) { out_tok = draw_token(w, V, S, philox_word(seed, stream, n++)); break; }
-
-            u128 SQ = 0;
-            if (!(quantise_row(qb + (int64_t)u * V, V, wq, &SQ) && SQ > 0)) { bad = 1; break; }
+            uint64_t SP = 0, SQ = 1;
+            if (!(quantise_row(pb + (int64_t)u * V, V, wp, &SP) && SP > 0)) { bad = 1; break; }
+            if (nk > 0) {
+                if (!(quantise_row(qb + (int64_t)u * V, V, wq, &SQ) && SQ > 0)) { bad = 1; break; }
+            } else {
+                memset(wq, 0, sizeof(uint64_t) * (size_t)V);
+            }
+            uint64_t Mc = 0;
+            u128 T = (u128)SP * SQ;
             int moved = 0;
             for (int ci = 0; ci < nk; ++ci) {
                 const int c = kids[ci], x = tok[c];
                 const uint64_t U = philox_word(seed, stream, n++) >> 40;
-                if ((u128)U * wq[x] * S < (w[x] * SQ) << 24) {
+                if (accept_test(U, wq[x], T, residual_at(wp[x], wq[x], SQ, Mc), SQ)) {
                     path[(int64_t)b * D_max + acc] = c;
                     ++acc;
                     u = c;
-                    if (!(quantise_row(pb + (int64_t)c * V, V, w, &S) && S > 0)) { bad = 1; break; }
-                    renormalise(w, V, &S);
                     moved = 1;
                     break;
                 }
-                u128 Sn = 0;
-                for (int y = 0; y < V; ++y) {
-                    u128 a = w[y] * SQ, c2 = wq[y] * S;
-                    wn[y] = a > c2 ? a - c2 : 0;
-                    Sn += wn[y];
-                }
-                if (Sn > 0) {
-                    for (int y = 0; y < V; ++y) w[y] = wn[y];
-                    S = Sn;
-                    renormalise(w, V, &S);
-                }
+                const uint64_t Mn = Mc + (uint64_t)(T / SQ);
+                u128 Tn = 0;
+                for (int y = 0; y < V; ++y) Tn += residual_at(wp[y], wq[y], SQ, Mn);
+                if (Tn > 0) { Mc = Mn; T = Tn; }
             }
-            if (bad) break;
-            if (!moved) { out_tok = draw_token(w, V, S, philox_word(seed, stream, n++)); break; }
+            if (moved) continue;
+            const u128 t = draw_target(philox_word(seed, stream, n++), T);
+            u128 cum = 0;
+            for (int y = 0; y < V; ++y) {
+                cum += residual_at(wp[y], wq[y], SQ, Mc);
+                if (cum > t) { out_tok = y; break; }
+            }
+            break;
         }
         if (bad) {
             status[b] = REF_ERR_INPUT;
@@ -473,7 +491,7 @@ int tmvref_accept_sample(int B, int M_max, int D_max, int V, const int32_t *toke
         accept_len[b] = acc;
         next_token[b] = out_tok;
     }
-    free(w); free(wq); free(wn); free(kids);
+    free(wp); free(wq); free(kids);
     return REF_OK;
 }
 

@@ -4,9 +4,11 @@ Independent evidence:
   * Philox4x64-10 stream equals numpy.random.Philox (numpy's own implementation);
   * the integer accept test keeps exactly min(2^24, ceil(b/a)) of the 2^24 uniform codes,
     i.e. min(1, p/q) quantised to 2^-24 (modified rejection sampling section of the
-    hierarchical speculative decoding blog);
-  * the inverse-CDF draw gives token x to exactly the codes in [ceil(C_{x-1} 2^32 / S),
-    ceil(C_x 2^32 / S));
+    hierarchical speculative decoding blog), without wrapping at its full widths;
+  * the inverse-CDF draw gives token x to exactly the codes in [ceil(C_{x-1} 2^32 / T),
+    ceil(C_x 2^32 / T));
+  * iterated refusals against one draft row stay in the threshold form (p - c q)+ that
+    the oracle's integer state follows (exact rationals);
   * outcome frequencies over many streams match the exact rational outcome distribution
     (oracle/exact.py) -- chi-square;
   * the tree reading itself is lossless: with children drawn i.i.d. from q, the first
@@ -32,47 +34,87 @@ def test_philox_matches_numpy(ref):
 
 
 def test_accept_threshold_closed_form(ref):
+    """The integer test U * WQ(x) * T < R(x) * SQ * 2^24 keeps the codes U below
+    min(2^24, ceil(b / a)), a = WQ(x) T, b = R(x) SQ 2^24, at the full widths it is used
+    with (T < 2^111, R < 2^87, SQ < 2^55): no product may wrap."""
     rng = np.random.default_rng(31)
-    cases = [(0, 2**32, 5, 2**32), (0, 2**32, 0, 2**32), (2**32, 2**32, 2**32, 2**32)]
+    cases = [(0, 2**31, 5, 2**31), (0, 2**31, 0, 2**31), (2**31, 2**62, 2**62, 2**31),
+             (2**31, 2**110 - 1, 2**86, 2**55 - 1), (1, 2**110 - 1, 2**86, 1), (2**31, 1, 2**86, 2**55 - 1)]
     for _ in range(300):
-        S = int(rng.integers(1, 2**48))
-        SQ = int(rng.integers(1, 2**49))
-        cases.append((int(rng.integers(0, 2**32 + 1)), S, int(rng.integers(0, S + 1)), SQ))
-    for wq, S, w, SQ in cases:
-        a, b = wq * S, w * SQ * 2**24
-        thr = (2**24 if w > 0 else 0) if a == 0 else min(2**24, -(-b // a))
+        SQ = int(rng.integers(1, 2**55))
+        T = int(rng.integers(1, 2**55)) * SQ + int(rng.integers(0, SQ))
+        wq = int(rng.integers(0, 2**31 + 1))
+        r = int(rng.integers(0, 2**62)) << int(rng.integers(0, 25))
+        cases.append((wq, T, r, SQ))
+    for wq, T, r, SQ in cases:
+        a, b = wq * T, r * SQ * 2**24
+        thr = (2**24 if b > 0 else 0) if a == 0 else min(2**24, -(-b // a))
         lo, hi = 0, 2**24                     # smallest U that is refused, by bisection
         while lo < hi:
             mid = (lo + hi) // 2
-            if ref.sample_accept_test(mid, wq, S, w, SQ):
+            if ref.sample_accept_test(mid, wq, T, r, SQ):
                 lo = mid + 1
             else:
                 hi = mid
-        assert lo == thr, (wq, S, w, SQ)
+        assert lo == thr, (wq, T, r, SQ)
         if thr > 0:
-            assert ref.sample_accept_test(thr - 1, wq, S, w, SQ)
+            assert ref.sample_accept_test(thr - 1, wq, T, r, SQ)
         if thr < 2**24:
-            assert not ref.sample_accept_test(thr, wq, S, w, SQ)
+            assert not ref.sample_accept_test(thr, wq, T, r, SQ)
 
 
 def test_draw_boundaries_closed_form(ref):
+    """Word w (high half h) draws the least x with C_x > floor(h T / 2^32): token x owns
+    exactly the h in [ceil(C_{x-1} 2^32 / T), ceil(C_x 2^32 / T)), weights up to 2^100."""
     rng = np.random.default_rng(32)
     for _ in range(100):
         V = int(rng.integers(1, 7))
-        w = rng.integers(0, 2**40, size=V).astype(np.uint64)
-        w[rng.random(V) < 0.3] = 0
-        if w.sum() == 0:
+        scale = int(rng.integers(0, 61))
+        w = [int(rng.integers(0, 2**40)) << scale for _ in range(V)]
+        for i in range(V):
+            if rng.random() < 0.3:
+                w[i] = 0
+        if sum(w) == 0:
             w[0] = 1
-        S = int(sum(int(x) for x in w))
-        cum = np.cumsum([int(x) for x in w])
+        T = sum(w)
+        cum = np.cumsum(np.array(w, dtype=object))
         for x in range(V):
-            start = -(-(int(cum[x - 1]) if x else 0) * 2**32 // S)
-            end = -(-int(cum[x]) * 2**32 // S)
+            start = -(-(int(cum[x - 1]) if x else 0) * 2**32 // T)
+            end = -(-int(cum[x]) * 2**32 // T)
             if start == end:
                 continue
             low = int(rng.integers(0, 2**32))
             assert ref.sample_draw(w, (start << 32) | low) == x
             assert ref.sample_draw(w, ((end - 1) << 32) | low) == x
+
+
+def test_refusals_keep_the_threshold_form():
+    """Refusing again and again against one draft row q: the residual after j refusals,
+    iterated as max(0, r - q) normalised (exact rationals), equals (p - c_j q)+ normalised
+    with c_0 = 0, c_{j+1} = c_j + sum (p - c_j q)+ -- the form the oracle's integer state
+    (M, T) follows."""
+    checked = 0
+    for seed in range(40):
+        rng = np.random.default_rng(seed)
+        V = int(rng.integers(2, 8))
+        p = [Fraction(int(x)) for x in rng.integers(0, 9, size=V)]
+        q = [Fraction(int(x)) for x in rng.integers(0, 9, size=V)]
+        if sum(p) == 0 or sum(q) == 0:
+            continue
+        p = [x / sum(p) for x in p]
+        q = [x / sum(q) for x in q]
+        cur, c = p, Fraction(0)
+        for _ in range(6):
+            nxt = exact._residual(cur, q)
+            z = sum(max(Fraction(0), a - c * b) for a, b in zip(p, q))
+            form = [max(Fraction(0), a - (c + z) * b) for a, b in zip(p, q)]
+            if sum(form) == 0:                 # empty residual: the distribution is kept
+                assert nxt == cur
+                break
+            assert nxt == [f / sum(form) for f in form]
+            cur, c = nxt, c + z
+            checked += 1
+    assert checked > 60
 
 
 def _tiny_tree_case(rng, V, overlap):
@@ -113,6 +155,57 @@ def test_outcome_frequencies_match_exact_model(ref, overlap, seed):
     obs, exp_ = [], []
     rest_o, rest_e = 0, 0.0
     for kk in keys:
+        e = float(want[kk]) * total
+        if e >= 20:
+            obs.append(counts[kk])
+            exp_.append(e)
+        else:
+            rest_o += counts[kk]
+            rest_e += e
+    if rest_e > 0:
+        obs.append(rest_o)
+        exp_.append(rest_e)
+    chi2 = sum((o - e) ** 2 / e for o, e in zip(obs, exp_))
+    pval = stats.chi2.sf(chi2, len(obs) - 1)
+    assert pval > 1e-4, (chi2, len(obs), pval)
+
+
+@pytest.mark.parametrize("seed", [51, 52])
+def test_repeated_refusals_match_exact_model(ref, seed):
+    """A root with six children under a draft row far from the teacher's: most walks
+    refuse several children in a row, so every outcome after the second refusal depends
+    on how the residual state is carried from one refusal to the next."""
+    rng = np.random.default_rng(seed)
+    V, M = 4, 6
+    parents = np.zeros(M + 1, np.int32)
+    p = np.zeros((M + 1, V), np.float32)
+    q = np.zeros((M + 1, V), np.float32)
+    p[:] = rng.dirichlet(np.ones(V))
+    p[0] = [0.05, 0.15, 0.3, 0.5]
+    q[:] = 1.0 / V
+    q[0] = [0.55, 0.3, 0.1, 0.05]
+    tokens = np.array([0, 0, 1, 0, 1, 2, 0], np.int32)      # drafts mostly where q > p
+    kids = ti.children_lists(parents, M)
+    want = exact.outcome_distribution({u: p[u] for u in range(M + 1)}, {u: q[u] for u in range(M + 1)},
+                                      kids, [int(t) for t in tokens])
+    after_two = sum(v for (path, _), v in want.items() if not path or path[0] >= 3)
+    assert after_two > 0.3                     # mass of walks that get past two refusals
+    B, steps = 50_000, 4
+    P = np.repeat(parents[None], B, 0)
+    n = np.full(B, M, np.int32)
+    anc, depth, st = ref.build_ancestors(P, n, M, 2)
+    counts = Counter()
+    for step in range(steps):
+        A, path, nxt, st2 = ref.accept_sample(np.repeat(tokens[None], B, 0), np.repeat(p[None], B, 0),
+                                              np.repeat(q[None], B, 0), 4321 + seed, step, n, anc, depth, st)
+        assert np.all(st2 == 0)
+        for b in range(B):
+            counts[(tuple(path[b, : A[b]].tolist()), int(nxt[b]))] += 1
+    total = B * steps
+    assert set(counts) <= set(want), set(counts) - set(want)
+    obs, exp_ = [], []
+    rest_o, rest_e = 0, 0.0
+    for kk in sorted(want, key=lambda k: -want[k]):
         e = float(want[kk]) * total
         if e >= 20:
             obs.append(counts[kk])

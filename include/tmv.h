@@ -166,10 +166,15 @@ int tmv_tree_verify_attention(int dtype, int B, int M_max, int D_max, int Hq, in
  *   reaches a node without children draws a bonus token from that node's p.
  *   teacher = p, draft_q = q: f32 probabilities; row u is the distribution after node u
  *   (row 0 after the prefix); children of u must have been drawn from q row u.
- *   Arithmetic is exact integer fixed point: W(x) = floor(p(x) 2^32) (and q alike),
- *   working sums renormalised to <= 48 bits by right shifts, the accept test
- *   U24 * Wq(x) * S < W(x) * Sq * 2^24 in 128-bit integers, the residual
- *   max(0, W(y) Sq - Wq(y) S), and draws by inverse CDF over floor((word>>32) S / 2^32).
+ *   Arithmetic is exact integer fixed point.  WP(x) = floor(p(x) 2^31) and WQ(x) =
+ *   floor(q(x) 2^31) have exact sums SP and SQ; SQ = 1 at a node without children, whose
+ *   q row is not read.  Against one draft row, the residual left after j refusals is
+ *   (p - c_j q)+ renormalised.  It is held as M and T, with R(y) = max(0, WP(y) SQ -
+ *   WQ(y) M) and T = sum R; M = 0 on arrival at a node.
+ *     accept:  iff U24 * WQ(x) * T < R(x) * SQ * 2^24 (exact, 192-bit).
+ *     refusal: M += floor(T / SQ), unless the new residual sums to 0 (the state is kept).
+ *     draw:    the least x with sum_{y<=x} R(y) > floor((word >> 32) * T / 2^32).
+ *   Requires V <= 2^24.
  *   Random words: Philox4x64-10, key {seed, (step << 32) | b}, block n at counter
  *   {n+1, 0, 0, 0}, word n = 64-bit lane n % 4 of block n / 4 (numpy's Philox stream);
  *   one word per tried child, one per final draw, in walk order.
@@ -183,11 +188,16 @@ int tmv_tree_verify_attention(int dtype, int B, int M_max, int D_max, int Hq, in
  *              GREEDY.
  *   accept_len out int32 [B]; path out int32 [B][D_max] (node ids root->leaf, then 0);
  *   next_token out int32 [B].  All 0 for a failed sequence.
- *   workspace: tmv_tree_accept_workspace() bytes, 16-byte aligned.  SAMPLE: a working
- *              distribution per sequence, then per-sequence barrier counts -- K workgroups
- *              (one vocabulary slice each) walk a sequence together and meet after every
- *              full-row pass; zero-fill once.  A wait for the other slices that exceeds 2 ms
- *              ends the walk with status TMV_ERR_DEVICE (never a hang).
+ *   workspace: tmv_tree_accept_workspace() bytes, 16-byte aligned.
+ *     SAMPLE: one synchronisation block per sequence.  K workgroups walk a sequence
+ *     together, one per vocabulary slice (K = compute units / B, at most 64), and meet
+ *     after every row pass.
+ *     - Every completed call leaves the workspace zero; zero-fill it once before first use,
+ *       and again after a GREEDY call has used it.
+ *     - A wait for the other slices that exceeds 2 ms ends the walk with status
+ *       TMV_ERR_DEVICE (never a hang).  Zero-fill the workspace again after that status.
+ *     - All K workgroups of a sequence must be resident at once, which holds when no other
+ *       kernel occupies the device's compute units.
  */
 size_t tmv_tree_accept_workspace(int mode, int B, int M_max, int V);
 int tmv_tree_accept(int mode, int B, int M_max, int D_max, int V,

@@ -42,7 +42,8 @@ def test_workspace_sizes_are_host_only():
     assert tmv.tree_verify_attention_workspace(tmv.F32, 1, 7, 1, 1, 64, 135) == 256
     big = tmv.tree_accept_workspace(tmv.ACCEPT_GREEDY, 16, 128, 128256)
     assert big >= 16 * 129 * 16 * 8
-    assert tmv.tree_accept_workspace(tmv.ACCEPT_SAMPLE, 32, 32, 128256) >= 32 * 128256 * 8
+    # sampling: one synchronisation block (4224 bytes) per sequence, nothing per vocabulary entry
+    assert 32 * 4224 <= tmv.tree_accept_workspace(tmv.ACCEPT_SAMPLE, 32, 32, 128256) < 32 * 8192
 
 
 def test_argument_checks_return_before_launch():
@@ -72,6 +73,10 @@ def test_argument_checks_return_before_launch():
     assert lib.tmv_tree_accept(*acc(tmv.ACCEPT_SAMPLE, 0, None, 1 << 20)) == tmv.ERR_ARG
     assert lib.tmv_tree_accept(*acc(tmv.ACCEPT_GREEDY, 0, None, 8)) == tmv.ERR_ARG
     assert lib.tmv_tree_accept(*acc(tmv.ACCEPT_GREEDY, 4, None, 1 << 20)) == tmv.ERR_ARG
+    big_v = (tmv.ACCEPT_SAMPLE, 1, 8, 4, (1 << 24) + 1, fake, 0, fake, 9 * ((1 << 24) + 1), (1 << 24) + 1, fake,
+             9 * ((1 << 24) + 1), (1 << 24) + 1, ctypes.c_uint64(1), ctypes.c_uint64(0), fake, fake, fake, fake, fake,
+             fake, fake, fake, 1 << 20, None)
+    assert lib.tmv_tree_accept(*big_v) == tmv.ERR_ARG                 # sampling vocabulary above 2^24
     # commit: row bytes not a multiple of 16 / too large, misaligned strides
     com = lambda dt, d, st: (dt, 2, 1, 8, d, 64, 8, 4, fake, fake, st, fake, fake, fake, fake, fake, fake, None)
     assert lib.tmv_kv_commit_path(*com(tmv.BF16, 4, s4)) == tmv.ERR_ARG

@@ -123,7 +123,7 @@ def test_greedy_determinism_and_workspace_reuse():
 
 
 # ------------------------------------------------------------------ sampling
-def _sample_parity(ref, parents, n, tokens, p, q, seed, step, D_max, status_override=None):
+def _sample_parity(ref, parents, n, tokens, p, q, seed, step, D_max, status_override=None, workspace=None):
     B, R, V = p.shape
     w = ti.Workload("sample", ti.F32, B, 0, 1, 64, R - 1, D_max, 1, V, "sample", parents, n,
                     np.zeros(B, np.int32), tokens, p=p, qd=q, seed=seed, step=step)
@@ -131,7 +131,7 @@ def _sample_parity(ref, parents, n, tokens, p, q, seed, step, D_max, status_over
     dev.build()
     if status_override is not None:
         dev.status.copy_(torch.from_numpy(status_override).cuda())
-    dev.accept()
+    dev.accept(workspace=workspace)
     torch.cuda.synchronize()
     ra, rd, rs = oracle_tables(ref, w)
     if status_override is not None:
@@ -198,3 +198,21 @@ def test_sampling_workload5(ref):
     A, st = _sample_parity(ref, w.parents, w.n_nodes, w.tokens, w.p, w.qd, w.seed, w.step, w.D_max)
     assert np.all(st == 0)
     print("    accept lengths", A.tolist(), flush=True)
+
+
+@pytest.mark.parametrize("B,seed", [(300, 420), (2, 421)])
+def test_sampling_slice_shapes_and_workspace(ref, B, seed):
+    """B = 300: one workgroup per sequence whose 20000-entry slice is longer than the
+    registers hold (the rest is re-read on every pass); B = 2: many slices per sequence
+    meeting at the barrier.  Both: parity on two calls sharing one workspace, which every
+    completed call leaves zero."""
+    import tree_masked_verification_amd as tmv
+    _case("sampling: B=%d V=20000 (slice shapes, workspace left zero)" % B)
+    rng = np.random.default_rng(seed)
+    V = 20000
+    parents, n, tokens, p, q = ti.small_sampling_case(rng, B, 10, V, 4, overlap=0.9)
+    ws = torch.zeros(tmv.tree_accept_workspace(tmv.ACCEPT_SAMPLE, B, 10, V), dtype=torch.uint8, device="cuda")
+    for step in (0, 1):
+        A, st = _sample_parity(ref, parents, n, tokens, p, q, 5, step, 4, workspace=ws)
+        assert np.all(st == 0)
+        assert int(torch.count_nonzero(ws)) == 0

@@ -10,9 +10,10 @@
 //   and picks the path -- no cross-workgroup synchronisation inside a kernel.
 // SAMPLE: modified rejection sampling (same page, its rejection-sampling section and
 //   FAQ), children of the current node tried in ascending id against the running
-//   residual.  Exact integer fixed point, so the result is bit-identical to any correct
-//   implementation: one workgroup walks one sequence; every full-row pass (row sums,
-//   residual update, inverse-CDF draw) is a block-wide integer reduction or scan.
+//   residual, which against one draft row keeps the form (p - c q)+.  Exact integer fixed
+//   point, so the result is bit-identical to any correct implementation.  K workgroups
+//   walk a sequence, one per vocabulary slice, holding their slices of the node's two rows
+//   in registers; every refusal is one exact sum over them, met at a bounded barrier.
 #include "tmv_device.hpp"
 
 namespace {
@@ -214,190 +215,302 @@ greedy_select_kernel(int M_max, int D_max, int V, int nchunk, const int32_t *__r
 
 // ============================================================== sampling
 // K workgroups walk each sequence together, each owning a contiguous slice of the
-// vocabulary: every full-row pass is split over the K slices, and the slices' exact
-// partial sums meet at a per-sequence barrier (device-scope atomics in the workspace,
-// bounded wait).  All K take the same decisions from the same sums and random words; the
-// stored residual of a slice is only ever read and written by its owner, and the owner
-// of the next child's token publishes that token's weight with its partial sum.
+// vocabulary; every thread owns a contiguous segment of its slice.  At node u the teacher
+// row p and the draft row q stay fixed while children are refused, and the residual left
+// after j refusals is (p - c_j q)+ renormalised (c_{j+1} = c_j + sum (p - c_j q)+).  In
+// integers the state is (M, T): R(y) = max(0, WP(y) SQ - WQ(y) M), T = sum R, and a
+// refusal adds floor(T / SQ) to M.  So each thread quantises its segment of both rows
+// once per node and keeps it in registers; a refusal is one pass of integer arithmetic
+// over registers and one exact sum, and the test of any child needs only WP and WQ at its
+// token.  The slices' partial sums meet at a per-sequence barrier of phase-tagged records
+// in the workspace (bounded wait).
 constexpr int kSampleThreads = 1024;
 constexpr int kSampleWaves = kSampleThreads / kWave;
-constexpr int kMaxSlices = 16;                 // workgroups per sequence
+constexpr int kMaxNodes = 128;                 // tree nodes per sequence (host-checked)
+constexpr int kMaxSlices = 64;                 // workgroups per sequence: one lane each at the barrier
+constexpr int kSeg = 16;                       // segment entries a thread keeps in registers
+constexpr int kTailBatch = 4;                  // loads in flight per thread beyond them
+constexpr int kSumGroup = 2;                   // register entries whose arithmetic may overlap
 constexpr uint64_t kSyncSpinTicks = 200000;    // 2 ms at the 100 MHz s_memrealtime clock
 constexpr int kFlagBad = 1;                    // an entry outside [0, 1] in a scanned row
 constexpr int kFlagTimeout = 2;                // a workgroup stopped waiting for the others
+constexpr int kTagShift = 48;                  // record words: 48-bit piece | phase << 48
+constexpr uint64_t kPieceMask = (1ull << kTagShift) - 1;
+constexpr int kRowBufferFlags = 0x00020000;     // raw buffer descriptor word 3 (gfx9 family)
 
-// block-wide exact sum of one u128 per thread (result broadcast to every thread)
-__device__ u128 block_sum_u128(u128 v, u128 *sh) {
-    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-    v = tmv::wave_sum_u128(v);
-    __syncthreads();
-    if (lane == 0) sh[wv] = v;
-    __syncthreads();
-    u128 t = 0;
-    for (int w = 0; w < kSampleWaves; ++w) t += sh[w];
-    return t;
+// a row as a buffer of `bytes` bytes: loads past the end return 0, so a segment's loads need
+// neither a guard nor an address of their own (zero bytes: no load touches memory)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_buffer(const float *row, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(row), 0, bytes, kRowBufferFlags);
 }
 
-__device__ int block_or(int v, int *sh) {
-    __syncthreads();
-    if (threadIdx.x == 0) *sh = 0;
-    __syncthreads();
-    if (v) atomicOr(sh, 1);
-    __syncthreads();
-    return *sh;
+__device__ __forceinline__ float row_load(__amdgpu_buffer_rsrc_t r, int x) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<uint32_t>(x) * 4u, 0, 0));
 }
 
-// floor(p * 2^32) for p in [0,1]; flags entries outside [0,1] (and NaN)
-__device__ __forceinline__ uint64_t quantise(float p, int &bad) {
-    // floor(p * 2^32) from the fp32 bits: p = m * 2^(e - 150) with m the 24-bit significand,
-    // so p * 2^32 = m * 2^(e - 118), exact in integers (the same value as in fp64)
+// Per-sequence synchronisation block of the workspace.  Record words carry the phase that
+// wrote them, so a reader knows a record is current without a separate arrival count; a
+// slot is rewritten two phases later only after every slice has read it.  Between calls
+// everything is zero: the last workgroup to leave clears the records and the count.
+struct SeqSync {
+    uint64_t leave;                          // workgroups done with this call
+    uint64_t pad[15];
+    uint64_t rec[2][kMaxSlices][4];          // [phase parity][slice]: sum bits 0-47, 48-95, 96-143; flags
+};
+
+struct SeqView {
+    u128 own;        // this slice's partial sum
+    u128 total;      // sum over the slices
+    u128 before;     // sum over the slices before this one
+    int flags;       // OR of the slices' flags, plus kFlagTimeout if this workgroup gave up
+};
+
+struct SyncLds {
+    u128 red[kSampleWaves];
+    int fl[kSampleWaves];
+    u128 res[3];         // total, before, own
+    int res_flags;
+};
+
+// wave-uniform copies in scalar registers (the values are equal in every lane)
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ u128 uniform_u128(u128 v) {
+    return (static_cast<u128>(uniform_u64(static_cast<uint64_t>(v >> 64))) << 64) | uniform_u64(static_cast<uint64_t>(v));
+}
+
+// floor(p * 2^31) for p in [0, 1] (at most 2^31); flags entries outside [0, 1] and NaN
+__device__ __forceinline__ uint32_t quantise31(float p, int &bad) {
+    // p = m * 2^(e - 150) with m the 24-bit significand, so p * 2^31 = m * 2^(e - 119):
+    // an exact integer operation on the fp32 bits
     const uint32_t u = __float_as_uint(p);
     if (u > 0x3F800000u) {                     // above 1, negative, infinite or NaN
         if (u != 0x80000000u) bad = 1;         // (-0 is zero)
         return 0;
     }
     const uint32_t e = u >> 23;
-    const uint64_t m = (u & 0x7FFFFFu) | 0x800000u;
-    if (e >= 118) return m << (e - 118);       // e <= 127: at most 2^32
-    const uint32_t sh = 118 - e;
-    return sh >= 24 ? 0 : m >> sh;             // zero and subnormals give 0
+    const uint32_t m = (u & 0x7FFFFFu) | 0x800000u;
+    if (e >= 119) return m << (e - 119);       // e <= 127: at most 2^31
+    const uint32_t sh = 119 - e;
+    return sh >= 24 ? 0u : m >> sh;            // zero and subnormals give 0
 }
 
-// Per-sequence synchronisation block of the workspace; arrival and leave counts are zero
-// between calls (the last workgroup to leave returns them to zero).
-struct SeqSync {
-    uint64_t arrive;                         // barrier arrivals in this call
-    uint64_t leave;                          // workgroups done with this call
-    uint64_t pad[14];
-    uint64_t rec[2][kMaxSlices][4];          // by phase parity and slice: sum lo, sum hi, extra, flags
+// R(y) = max(0, WP(y) SQ - WQ(y) M) < 2^96 from four 32 x 32 -> 64-bit products, as its low
+// 32 bits and the rest: R = lo + hi * 2^32
+struct R96 {
+    uint32_t lo;
+    uint64_t hi;
 };
 
-struct SeqView {
-    u128 own;        // this slice's sum
-    u128 total;      // sum over the slices
-    u128 before;     // sum over the slices before this one
-    uint64_t extra;  // the value published by the chosen owner slice
-    int flags;       // OR of the slices' flags, plus kFlagTimeout if this workgroup gave up
-};
+__device__ __forceinline__ R96 resid96(uint32_t wp, uint32_t wq, uint64_t SQ, uint64_t M) {
+    const uint64_t a_lo = static_cast<uint64_t>(wp) * static_cast<uint32_t>(SQ);
+    const uint64_t a_hi = static_cast<uint64_t>(wp) * static_cast<uint32_t>(SQ >> 32);
+    const uint64_t c_lo = static_cast<uint64_t>(wq) * static_cast<uint32_t>(M);
+    const uint64_t c_hi = static_cast<uint64_t>(wq) * static_cast<uint32_t>(M >> 32);
+    const uint64_t a12 = (a_lo >> 32) + a_hi, c12 = (c_lo >> 32) + c_hi;   // (neither sum wraps)
+    const uint32_t a0 = static_cast<uint32_t>(a_lo), c0 = static_cast<uint32_t>(c_lo);
+    // a - c as lo + d12 * 2^32 with a signed high part (a12 < 2^55, c12 < 2^63: no overflow);
+    // it is negative exactly when a < c, and its sign masks both parts
+    const int64_t d12 = static_cast<int64_t>(a12 - c12 - (a0 < c0 ? 1u : 0u));
+    const uint64_t keep = ~static_cast<uint64_t>(d12 >> 63);
+    R96 r;
+    r.lo = (a0 - c0) & static_cast<uint32_t>(keep);
+    r.hi = static_cast<uint64_t>(d12) & keep;
+    return r;
+}
 
-struct SyncLds {
-    u128 red[kSampleWaves];
-    int flag;
-    int res_flags;
-    uint64_t res[5];
-};
+__device__ __forceinline__ u128 resid(uint32_t wp, uint32_t wq, uint64_t SQ, uint64_t M) {
+    const R96 r = resid96(wp, wq, SQ, M);
+    return (static_cast<u128>(r.hi) << 32) | r.lo;
+}
+
+// a * b as three 64-bit words, least significant first
+__device__ __forceinline__ void mul_u128_u64(u128 a, uint64_t b, uint64_t w[3]) {
+    const u128 lo = static_cast<u128>(static_cast<uint64_t>(a)) * b;
+    const u128 hi = static_cast<u128>(static_cast<uint64_t>(a >> 64)) * b;
+    const u128 mid = (lo >> 64) + static_cast<uint64_t>(hi);
+    w[0] = static_cast<uint64_t>(lo);
+    w[1] = static_cast<uint64_t>(mid);
+    w[2] = static_cast<uint64_t>(hi >> 64) + static_cast<uint64_t>(mid >> 64);
+}
+
+// accept iff U * WQ(x) * T < R(x) * SQ * 2^24 (both sides below 2^166)
+__device__ __forceinline__ bool sample_accepts(uint64_t U, uint32_t wqx, u128 T, u128 rx, uint64_t SQ) {
+    uint64_t l[3], r[3];
+    mul_u128_u64(T, U * wqx, l);
+    mul_u128_u64(rx << 24, SQ, r);
+    if (l[2] != r[2]) return l[2] < r[2];
+    if (l[1] != r[1]) return l[1] < r[1];
+    return l[0] < r[0];
+}
+
+// floor(n / d) for d >= 1 and a quotient below 2^64: a double-precision estimate, then
+// exact corrections (the estimate is off by a few units at most)
+__device__ uint64_t udiv_u128_u64(u128 n, uint64_t d) {
+    const double est = (static_cast<double>(static_cast<uint64_t>(n >> 64)) * 18446744073709551616.0 +
+                        static_cast<double>(static_cast<uint64_t>(n))) / static_cast<double>(d);
+    uint64_t q = est >= 18446744073709549568.0 ? 0xFFFFFFFFFFFFF800ull : static_cast<uint64_t>(est);
+    u128 prod = static_cast<u128>(q) * d;
+    while (prod > n) { --q; prod -= d; }
+    while (n - prod >= d) { ++q; prod += d; }
+    return q;
+}
+
+// floor((word >> 32) * T / 2^32), split so that no product exceeds 128 bits
+__device__ __forceinline__ u128 draw_target(uint64_t word, u128 T) {
+    const uint64_t h = word >> 32;
+    return static_cast<u128>(h) * (T >> 32) + ((static_cast<u128>(h) * static_cast<uint32_t>(T)) >> 32);
+}
+
+__device__ __forceinline__ uint32_t shfl_u32(uint32_t v, int src) { return static_cast<uint32_t>(__shfl(static_cast<int>(v), src, kWave)); }
+
+__device__ __forceinline__ int wave_or(int v) {
+    for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// true in every thread if v is true in any thread of the block
+__device__ bool block_any(bool v, int *sh) {
+    __syncthreads();
+    if (threadIdx.x == 0) *sh = 0;
+    __syncthreads();
+    if (__ballot(v) != 0 && (threadIdx.x & (kWave - 1)) == 0) *sh = 1;
+    __syncthreads();
+    return *sh != 0;
+}
 
 // Sum `local` over the block and then over the K slices of the sequence.  Every thread
-// of the block calls it; `phase` counts the calls and must advance alike in all K.
-__device__ SeqView seq_reduce(SeqSync *ss, int K, int k, int &phase, u128 local, uint64_t extra, int owner,
-                              int flags, SyncLds &L)
-{
-    const u128 wg = block_sum_u128(local, L.red);
-    const int fl = block_or(flags, &L.flag);
-    const int slot = phase & 1;
-    ++phase;
-    if (threadIdx.x < kWave) {
-        const int lane = threadIdx.x;
+// of the block calls it; `phase` counts the calls and advances alike in all K.
+__device__ SeqView seq_reduce(SeqSync *ss, int K, int k, int &phase, u128 local, int flags, SyncLds &L) {
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+    const u128 v = tmv::wave_sum_u128(local);
+    const int f = wave_or(flags);
+    __syncthreads();                                  // the previous call's results are read
+    if (lane == 0) { L.red[wv] = v; L.fl[wv] = f; }
+    __syncthreads();
+    const uint64_t tag = static_cast<uint64_t>(++phase);
+    if (wv == 0) {
+        const u128 wg = tmv::wave_sum_u128(lane < kSampleWaves ? L.red[lane] : 0);
+        const int fl = wave_or(lane < kSampleWaves ? L.fl[lane] : 0);
+        const uint64_t own[4] = {static_cast<uint64_t>(wg) & kPieceMask, static_cast<uint64_t>(wg >> 48) & kPieceMask,
+                                 static_cast<uint64_t>(wg >> 96) & kPieceMask, static_cast<uint64_t>(fl)};
+        uint64_t *slot = &ss->rec[tag & 1][0][0];
+        if (lane < 4) {
+            const uint64_t word = (lane == 0 ? own[0] : lane == 1 ? own[1] : lane == 2 ? own[2] : own[3]) | (tag << kTagShift);
+            __hip_atomic_store(slot + 4 * k + lane, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // lane j < K collects slice j's record (its own from registers)
+        uint64_t w0 = own[0], w1 = own[1], w2 = own[2], w3 = own[3];
+        bool ok = lane >= K || lane == k;
         int timed_out = 0;
-        if (lane == 0) {
-            uint64_t *r = ss->rec[slot][k];
-            __hip_atomic_store(r + 0, static_cast<uint64_t>(wg), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(r + 1, static_cast<uint64_t>(wg >> 64), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(r + 2, extra, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(r + 3, static_cast<uint64_t>(fl), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __builtin_amdgcn_s_waitcnt(0);                 // the record is out before the count
-            __hip_atomic_fetch_add(&ss->arrive, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const uint64_t target = static_cast<uint64_t>(K) * phase;
-            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-            while (__hip_atomic_load(&ss->arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-                if (__builtin_amdgcn_s_memrealtime() - t0 > kSyncSpinTicks) { timed_out = 1; break; }
-                __builtin_amdgcn_s_sleep(2);
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        for (;;) {
+            if (!ok) {
+                const uint64_t *r = slot + 4 * lane;
+                w0 = __hip_atomic_load(r + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                w1 = __hip_atomic_load(r + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                w2 = __hip_atomic_load(r + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                w3 = __hip_atomic_load(r + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ok = (w0 >> kTagShift) == tag && (w1 >> kTagShift) == tag && (w2 >> kTagShift) == tag &&
+                     (w3 >> kTagShift) == tag;
             }
+            if (__ballot(!ok) == 0) break;
+            if (__builtin_amdgcn_s_memrealtime() - t0 > kSyncSpinTicks) { timed_out = 1; break; }
+            __builtin_amdgcn_s_sleep(1);
         }
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);          // the record reads stay after the wait
-        u128 v = 0;
-        uint64_t ex = 0;
-        int f = 0;
+        u128 vj = 0;
+        int fj = 0;
         if (lane < K) {
-            const uint64_t *rj = ss->rec[slot][lane];
-            const uint64_t lo = __hip_atomic_load(rj + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const uint64_t hi = __hip_atomic_load(rj + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            ex = __hip_atomic_load(rj + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            f = static_cast<int>(__hip_atomic_load(rj + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-            v = (static_cast<u128>(hi) << 64) | lo;
+            vj = (static_cast<u128>(w2 & kPieceMask) << 96) | (static_cast<u128>(w1 & kPieceMask) << 48) |
+                 (w0 & kPieceMask);
+            fj = static_cast<int>(w3 & kPieceMask);
         }
-        const u128 tot = tmv::wave_sum_u128(v);
-        const u128 bef = tmv::wave_sum_u128(lane < k ? v : 0);
-        const uint32_t ex_lo = __shfl(static_cast<uint32_t>(ex), owner, kWave);
-        const uint32_t ex_hi = __shfl(static_cast<uint32_t>(ex >> 32), owner, kWave);
-        for (int o = 32; o > 0; o >>= 1) f |= __shfl_xor(f, o, kWave);
+        const u128 tot = tmv::wave_sum_u128(vj);
+        const u128 bef = tmv::wave_sum_u128(lane < k ? vj : 0);
+        fj = wave_or(fj);
         if (lane == 0) {
-            L.res[0] = static_cast<uint64_t>(tot);
-            L.res[1] = static_cast<uint64_t>(tot >> 64);
-            L.res[2] = static_cast<uint64_t>(bef);
-            L.res[3] = static_cast<uint64_t>(bef >> 64);
-            L.res[4] = (static_cast<uint64_t>(ex_hi) << 32) | ex_lo;
-            L.res_flags = f | (timed_out ? kFlagTimeout : 0);
+            L.res[0] = tot;
+            L.res[1] = bef;
+            L.res[2] = wg;
+            L.res_flags = fj | (timed_out ? kFlagTimeout : 0);
         }
     }
     __syncthreads();
     SeqView r;
-    r.own = wg;
-    r.total = (static_cast<u128>(L.res[1]) << 64) | L.res[0];
-    r.before = (static_cast<u128>(L.res[3]) << 64) | L.res[2];
-    r.extra = L.res[4];
-    r.flags = L.res_flags;
+    r.total = uniform_u128(L.res[0]);
+    r.before = uniform_u128(L.res[1]);
+    r.own = uniform_u128(L.res[2]);
+    r.flags = __builtin_amdgcn_readfirstlane(L.res_flags);
     return r;
 }
 
-// the workgroup is done with the call; the last of the K returns the counts to zero
+// The workgroup is done with the call.  Its record stores are complete before it counts
+// itself out, so the last of the K can clear every record for the next call.
 __device__ void seq_leave(SeqSync *ss, int K) {
     __syncthreads();
-    if (threadIdx.x == 0) {
-        __builtin_amdgcn_s_waitcnt(0);
-        const uint64_t l = __hip_atomic_fetch_add(&ss->leave, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x < kWave) {
+        const int lane = threadIdx.x;
+        uint64_t l = 0;
+        if (lane == 0) {
+            __builtin_amdgcn_s_waitcnt(0);
+            l = __hip_atomic_fetch_add(&ss->leave, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        l = __shfl(l, 0, kWave);
         if (l == static_cast<uint64_t>(K) - 1) {
-            __hip_atomic_store(&ss->arrive, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&ss->leave, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int i = lane; i < 2 * K * 4; i += kWave) {
+                const int slot = i / (4 * K), j = i % (4 * K);
+                __hip_atomic_store(&ss->rec[slot][j / 4][j % 4], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if (lane == 0) __hip_atomic_store(&ss->leave, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
 
-struct Dist {       // the working distribution W of the walk
-    const float *row;    // W(x) = floor(row[x] * 2^32) >> shift when stored == false
-    int shift;
-    bool stored;         // W lives in the workspace array
-    uint64_t S;          // sum of W, renormalised to at most 48 bits
-};
-
-// A pass over the slice [x_lo, x_hi) strided over the block: x is visited by thread
-// (x - x_lo) mod kSampleThreads, and each thread has kPassBatch loads in flight --
-// load(x) for a whole batch goes out before body(x, value) runs on any of them.  (x and
-// its value stay in one thread, so a body may overwrite what its own load read.)
-constexpr int kPassBatch = 8;
-template <class Load, class Body>
-__device__ __forceinline__ void strided_pass(int x_lo, int x_hi, Load load, Body body) {
-    for (int x0 = x_lo + static_cast<int>(threadIdx.x); x0 < x_hi; x0 += kPassBatch * kSampleThreads) {
-        decltype(load(0)) v[kPassBatch];
+// Visit the entries of a thread's segment [s0, s1) beyond the kSeg held in registers
+// (only when a slice exceeds kSampleThreads * kSeg entries): f(x, WP(x), WQ(x)) in order,
+// read and quantised again.
+template <class F>
+__device__ __forceinline__ void visit_tail(int s0, int s1, __amdgpu_buffer_rsrc_t prs, __amdgpu_buffer_rsrc_t qrs, F f) {
+    for (int x0 = s0 + kSeg; x0 < s1; x0 += kTailBatch) {
+        float tp[kTailBatch], tq[kTailBatch];
 #pragma unroll
-        for (int j = 0; j < kPassBatch; ++j) {
-            const int x = x0 + j * kSampleThreads;
-            if (x < x_hi) v[j] = load(x);
+        for (int e = 0; e < kTailBatch; ++e) {
+            tp[e] = row_load(prs, x0 + e);
+            tq[e] = row_load(qrs, x0 + e);
         }
+        int unused = 0;
 #pragma unroll
-        for (int j = 0; j < kPassBatch; ++j) {
-            const int x = x0 + j * kSampleThreads;
-            if (x < x_hi) body(x, v[j]);
-        }
+        for (int e = 0; e < kTailBatch; ++e)
+            if (x0 + e < s1) f(x0 + e, quantise31(tp[e], unused), quantise31(tq[e], unused));
     }
 }
 
-// the working distribution's raw entry at x (a stored W, or the bits of the p value)
-// together with the draft's q(x)
-struct RowPair {
-    uint64_t a;
-    float q;
-};
+// sum of R over a thread's segment.  Register entries past the segment's end hold
+// WP = WQ = 0 (R = 0), so the register part runs unguarded; its 96-bit terms are summed in
+// two 64-bit halves (each below 2^59 over kSeg terms).
+__device__ __forceinline__ u128 segment_sum(int s0, int s1, const uint32_t (&rp)[kSeg], const uint32_t (&rq)[kSeg],
+                                            __amdgpu_buffer_rsrc_t prs, __amdgpu_buffer_rsrc_t qrs, uint64_t SQ,
+                                            uint64_t M) {
+    uint64_t lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < kSeg; ++e) {
+        // (opaque copies: the compiler would otherwise keep 64-bit widened copies of the
+        // cached rows alive across the refusal loop)
+        uint32_t wp = rp[e], wq = rq[e];
+        asm volatile("" : "+v"(wp), "+v"(wq));
+        const R96 r = resid96(wp, wq, SQ, M);
+        lo += r.lo;
+        hi += r.hi;
+        if (e % kSumGroup == kSumGroup - 1) __builtin_amdgcn_sched_barrier(0);   // bounds the overlap
+    }
+    u128 s = static_cast<u128>(lo) + (static_cast<u128>(hi) << 32);
+    visit_tail(s0, s1, prs, qrs, [&](int, uint32_t a, uint32_t c2) { s += resid(a, c2, SQ, M); });
+    return s;
+}
 
 __global__ void __launch_bounds__(kSampleThreads)
 sample_walk_kernel(int M_max, int D_max, int V, int K,
@@ -408,39 +521,39 @@ sample_walk_kernel(int M_max, int D_max, int V, int K,
                    const int32_t *__restrict__ n_nodes, const int32_t *__restrict__ anc,
                    const int32_t *__restrict__ depth, int32_t *__restrict__ status,
                    int32_t *__restrict__ accept_len, int32_t *__restrict__ path,
-                   int32_t *__restrict__ next_token, uint64_t *__restrict__ wsW, SeqSync *__restrict__ sync)
+                   int32_t *__restrict__ next_token, SeqSync *__restrict__ sync)
 {
     __shared__ SyncLds L;
-    __shared__ int kids[129];
-    __shared__ int nkids;
+    __shared__ int par[kMaxNodes + 1];         // parent of a live node, -1 otherwise
+    __shared__ int tok[kMaxNodes + 1];         // draft token of a live node
+    __shared__ int kids[kMaxNodes];
     __shared__ int kid_count[kSampleWaves];
+    __shared__ int nkids;
+    __shared__ uint32_t kwp[kMaxNodes], kwq[kMaxNodes];   // WP and WQ at the children's tokens
     __shared__ u128 scan_sh[kSampleWaves];
+    __shared__ int flag_sh;
     __shared__ int draw_tok;
 
     const int b = blockIdx.x / K, k = blockIdx.x % K, tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wv = tid / kWave;
     const int x_lo = static_cast<int>(static_cast<int64_t>(V) * k / K);
     const int x_hi = static_cast<int>(static_cast<int64_t>(V) * (k + 1) / K);
-    auto owner_of = [&](int x) {                 // the slice holding token x
-        int o = static_cast<int>(static_cast<int64_t>(x) * K / V);
-        while (o + 1 < K && static_cast<int64_t>(V) * (o + 1) / K <= x) ++o;
-        while (o > 0 && static_cast<int64_t>(V) * o / K > x) --o;
-        return o;
-    };
+    const int seg = (x_hi - x_lo + kSampleThreads - 1) / kSampleThreads;
+    const int s0 = min(x_hi, x_lo + tid * seg), s1 = min(x_hi, s0 + seg);
     SeqSync *ss = sync + b;
     int phase = 0;
     const int R = M_max + 1, W = D_max + 1;
     const int M = n_nodes[b];
     int32_t *pth = path + static_cast<int64_t>(b) * D_max;
-    uint64_t *w = wsW + static_cast<int64_t>(b) * V;
     const int st_in = status[b];
     const int st = (st_in == TMV_OK && (M < 0 || M > M_max)) ? TMV_ERR_INPUT : st_in;
     const uint64_t stream = (step << 32) | static_cast<uint32_t>(b);
 
     // outputs: slice 0 writes the path, the length and a data error; the slice holding the
     // final draw writes the token
-    auto finish = [&](int code, int acc, int tok, bool mine) {
+    auto finish = [&](int code, int acc, int tk, bool mine) {
         __syncthreads();
-        if (code != TMV_OK) { acc = 0; tok = 0; }
+        if (code != TMV_OK) { acc = 0; tk = 0; }
         if (k == 0)
             for (int j = tid; j < D_max; j += kSampleThreads)
                 if (code != TMV_OK || j >= acc) pth[j] = 0;
@@ -454,66 +567,39 @@ sample_walk_kernel(int M_max, int D_max, int V, int K,
                     if (st_in == TMV_OK) status[b] = code;
                 }
             }
-            if (code == TMV_OK && mine) next_token[b] = tok;
+            if (code == TMV_OK && mine) next_token[b] = tk;
         }
         seq_leave(ss, K);
     };
     if (st != TMV_OK) { finish(st, 0, 0, false); return; }
 
-    // live tokens in range (every slice checks all of them: the same answer everywhere)
-    int bad = 0;
-    for (int i = tid + 1; i <= M; i += kSampleThreads)
-        if (depth[static_cast<int64_t>(b) * R + i] >= 1) {
-            const int t = tokens[static_cast<int64_t>(b) * R + i];
-            if (t < 0 || t >= V) bad = 1;
+    // the live nodes' parents and tokens (every slice checks every token: one answer)
+    bool bad_tok = false;
+    for (int c = tid; c <= M_max; c += kSampleThreads) {
+        int pc = -1, t = 0;
+        if (c >= 1 && c <= M && W > 1 && depth[static_cast<int64_t>(b) * R + c] >= 1) {
+            pc = anc[(static_cast<int64_t>(b) * R + c) * W + 1];
+            t = tokens[static_cast<int64_t>(b) * R + c];
+            if (t < 0 || t >= V) bad_tok = true;
         }
-    if (block_or(bad, &L.flag)) { finish(TMV_ERR_INPUT, 0, 0, false); return; }
-
-    // load (W, S) = quantised p row `row`, renormalised to <= 48 bits; 1 on success,
-    // 0 on bad data, -1 when the other slices did not come
-    auto load_p = [&](int row, Dist &Dd) -> int {
-        const float *pr = p + b * psb + static_cast<int64_t>(row) * psr;
-        int bd = 0;
-        u128 s = 0;
-        strided_pass(x_lo, x_hi, [&](int x) { return pr[x]; }, [&](int, float v) { s += quantise(v, bd); });
-        SeqView v = seq_reduce(ss, K, k, phase, s, 0, 0, bd ? kFlagBad : 0, L);
-        if (v.flags & kFlagTimeout) return -1;
-        if ((v.flags & kFlagBad) || v.total == 0) return 0;
-        Dd.row = pr; Dd.shift = 0; Dd.stored = false;
-        const int bl = tmv::bitlen_u128(v.total);
-        if (bl > 48) {
-            Dd.shift = bl - 48;
-            u128 s2 = 0;
-            strided_pass(x_lo, x_hi, [&](int x) { return pr[x]; },
-                         [&](int, float v2) { s2 += quantise(v2, bd) >> Dd.shift; });
-            v = seq_reduce(ss, K, k, phase, s2, 0, 0, 0, L);
-            if (v.flags & kFlagTimeout) return -1;
-        }
-        Dd.S = static_cast<uint64_t>(v.total);
-        return 1;
-    };
-
-    Dist cur;
-    {
-        const int r = load_p(0, cur);
-        if (r <= 0) { finish(r < 0 ? TMV_ERR_DEVICE : TMV_ERR_INPUT, 0, 0, false); return; }
+        par[c] = pc;
+        tok[c] = t;
     }
-    uint64_t n = 0;           // draws consumed
+    if (block_any(bad_tok, &flag_sh)) { finish(TMV_ERR_INPUT, 0, 0, false); return; }
+
+    uint32_t rp[kSeg], rq[kSeg];
+    uint64_t n = 0;            // random words consumed
     int u = 0, acc = 0;
     for (;;) {
-        // children of u in ascending id: thread c-1 tests node c (one round trip), matches
-        // are compacted in order with ballots
-        __syncthreads();
+        // children of u in ascending id: thread c-1 tests node c, compacted with ballots
         {
             const int c = tid + 1;
-            const bool is_kid = c <= M && depth[static_cast<int64_t>(b) * R + c] >= 1 &&
-                                anc[(static_cast<int64_t>(b) * R + c) * W + 1] == u;
+            const bool is_kid = c <= M_max && par[c] == u;
             const uint64_t bal = __ballot(is_kid);
-            const int wv = tid / kWave;
-            if ((tid & (kWave - 1)) == 0) kid_count[wv] = __popcll(bal);
+            if (lane == 0) kid_count[wv] = __popcll(bal);
             __syncthreads();
             if (is_kid) {
-                int before = __popcll(bal & ((1ull << (tid & (kWave - 1))) - 1));
+                int before = __popcll(bal & ((1ull << lane) - 1));
                 for (int w2 = 0; w2 < wv; ++w2) before += kid_count[w2];
                 kids[before] = c;
             }
@@ -522,182 +608,161 @@ sample_walk_kernel(int M_max, int D_max, int V, int K,
                 for (int w2 = 0; w2 < kSampleWaves; ++w2) kk += kid_count[w2];
                 nkids = kk;
             }
+            __syncthreads();
         }
-        __syncthreads();
         const int nk = nkids;
-        bool moved = false;
-        if (nk > 0) {
-            const float *qr = q + b * qsb + static_cast<int64_t>(u) * qsr;
-            int bd = 0;
-            u128 sq = 0;
-            strided_pass(x_lo, x_hi, [&](int x) { return qr[x]; }, [&](int, float v) { sq += quantise(v, bd); });
-            SeqView vq = seq_reduce(ss, K, k, phase, sq, 0, 0, bd ? kFlagBad : 0, L);
-            if (vq.flags & kFlagTimeout) { finish(TMV_ERR_DEVICE, 0, 0, false); return; }
-            // sum of Wq: at most V * 2^32 < 2^64
-            const uint64_t SQ = static_cast<uint64_t>(vq.total);
-            if ((vq.flags & kFlagBad) || SQ == 0) { finish(TMV_ERR_INPUT, 0, 0, false); return; }
-            uint64_t w_next = 0;                   // W at the current child's token once W is stored
-            for (int ci = 0; ci < nk; ++ci) {
-                const int c = kids[ci];
-                const int x = tokens[static_cast<int64_t>(b) * R + c];
-                int bd2 = 0;
-                const uint64_t wx = cur.stored ? w_next : quantise(cur.row[x], bd2) >> cur.shift;
-                const uint64_t wqx = quantise(qr[x], bd2);
-                const uint64_t U = tmv::philox_word(seed, stream, n++) >> 40;
-                if (static_cast<u128>(U) * wqx * cur.S < (static_cast<u128>(wx) * SQ) << 24) {
-                    if (k == 0 && tid == 0) pth[acc] = c;
-                    ++acc;
-                    u = c;
-                    const int r = load_p(c, cur);
-                    if (r <= 0) { finish(r < 0 ? TMV_ERR_DEVICE : TMV_ERR_INPUT, 0, 0, false); return; }
-                    moved = true;
-                    break;
-                }
-                // residual: W(y) <- max(0, W(y) SQ - Wq(y) S), renormalised.  The owner of the
-                // next child's token publishes W there: first its current value (kept when the
-                // residual is empty), then its new one.
-                const int xn = ci + 1 < nk ? tokens[static_cast<int64_t>(b) * R + kids[ci + 1]] : 0;
-                const int own_n = owner_of(xn);
-                const bool have_xn = ci + 1 < nk && xn >= x_lo && xn < x_hi;
-                auto load_pair = [&](int y) {
-                    RowPair r;
-                    r.a = cur.stored ? w[y] : static_cast<uint64_t>(__float_as_uint(cur.row[y]));
-                    r.q = qr[y];
-                    return r;
-                };
-                auto w_of = [&](const RowPair &r) {
-                    int bd3 = 0;
-                    return cur.stored ? r.a : quantise(__uint_as_float(static_cast<uint32_t>(r.a)), bd3) >> cur.shift;
-                };
-                uint64_t pub = 0;
-                if (have_xn) {
-                    int bd3 = 0;
-                    pub = cur.stored ? w[xn] : quantise(cur.row[xn], bd3) >> cur.shift;
-                }
-                u128 sn = 0;
-                strided_pass(x_lo, x_hi, load_pair, [&](int, const RowPair &r) {
-                    int bd3 = 0;
-                    const u128 a = static_cast<u128>(w_of(r)) * SQ;
-                    const u128 c2 = static_cast<u128>(quantise(r.q, bd3)) * cur.S;
-                    sn += a > c2 ? a - c2 : 0;
-                });
-                SeqView vs = seq_reduce(ss, K, k, phase, sn, pub, own_n, 0, L);
-                if (vs.flags & kFlagTimeout) { finish(TMV_ERR_DEVICE, 0, 0, false); return; }
-                if (vs.total == 0) {                // empty residual: keep the distribution
-                    w_next = vs.extra;
-                    continue;
-                }
-                const int bl = tmv::bitlen_u128(vs.total);
-                const int sh = bl > 48 ? bl - 48 : 0;
-                // write the shifted residual; reading W(y) and writing w[y] happen in the
-                // same thread for the same y, so the update is safe in place
-                u128 s2 = 0;
-                uint64_t pub2 = 0;
-                strided_pass(x_lo, x_hi, load_pair, [&](int y, const RowPair &r) {
-                    int bd3 = 0;
-                    const u128 a = static_cast<u128>(w_of(r)) * SQ;
-                    const u128 c2 = static_cast<u128>(quantise(r.q, bd3)) * cur.S;
-                    const uint64_t nv = static_cast<uint64_t>((a > c2 ? a - c2 : 0) >> sh);
-                    w[y] = nv;
-                    s2 += nv;
-                    if (have_xn && y == xn) pub2 = nv;
-                });
-                // (the thread that wrote the token's weight holds it; pass it to the block)
-                if (have_xn) {
-                    __syncthreads();
-                    if (tid == (xn - x_lo) % kSampleThreads) L.res[0] = pub2;
-                    __syncthreads();
-                    pub2 = L.res[0];
-                }
-                SeqView vw = seq_reduce(ss, K, k, phase, s2, pub2, own_n, 0, L);
-                if (vw.flags & kFlagTimeout) { finish(TMV_ERR_DEVICE, 0, 0, false); return; }
-                cur.stored = true;
-                cur.S = static_cast<uint64_t>(vw.total);
-                w_next = vw.extra;
-            }
-            if (moved) continue;
-        }
-        // draw the bonus (no children) or the correction (all refused) from (W, S):
-        // t = floor(word_hi * S / 2^32), the token is the first x whose running sum of W
-        // exceeds t.  Slice sums locate the slice; inside it, contiguous segments per thread
-        // (a multiple of 4 entries) and an exclusive scan of their sums locate the token.
-        const uint64_t word = tmv::philox_word(seed, stream, n++);
-        const u128 t = (static_cast<u128>(word >> 32) * cur.S) >> 32;
-        const int len = x_hi - x_lo;
-        const int seg = ((len + kSampleThreads - 1) / kSampleThreads + 3) & ~3;
-        const int s0 = min(x_hi, x_lo + tid * seg), s1 = min(x_hi, s0 + seg);
-        u128 ssum = 0;
+        const bool have_q = nk > 0;          // a leaf's q row is never read
+        const __amdgpu_buffer_rsrc_t prs = row_buffer(p + b * psb + static_cast<int64_t>(u) * psr, V * 4);
+        const __amdgpu_buffer_rsrc_t qrs = row_buffer(q + b * qsb + static_cast<int64_t>(u) * qsr, have_q ? V * 4 : 0);
+
+        // arrival at u: quantise this thread's segment of both rows into registers, sum
+        // them, and fetch both rows at the children's tokens
         int bd = 0;
-        constexpr int kDrawBatch = 16;
-        for (int xb = s0; xb < s1; xb += kDrawBatch) {
-            uint64_t vals[kDrawBatch];
+        uint64_t sp = 0, sq = 0;
+        {
+            float fp[kSeg], fq[kSeg];
 #pragma unroll
-            for (int j = 0; j < kDrawBatch; ++j) {
-                const int x = xb + j;
-                vals[j] = x < s1 ? (cur.stored ? w[x] : static_cast<uint64_t>(__float_as_uint(cur.row[x]))) : 0;
+            for (int e = 0; e < kSeg; ++e) {
+                fp[e] = row_load(prs, s0 + e);
+                fq[e] = row_load(qrs, s0 + e);
             }
+            const int xc = tid < nk ? tok[kids[tid]] : 0;
+            const float cp = row_load(prs, xc), cq = row_load(qrs, xc);
 #pragma unroll
-            for (int j = 0; j < kDrawBatch; ++j)
-                if (xb + j < s1)
-                    ssum += cur.stored ? vals[j] : quantise(__uint_as_float(static_cast<uint32_t>(vals[j])), bd) >> cur.shift;
-        }
-        // inclusive scan of the segment sums inside the wave (shuffles up, 32-bit parts)
-        const int lane = tid & (kWave - 1), wv = tid / kWave;
-        u128 incl = ssum;
-        for (int o = 1; o < kWave; o <<= 1) {
-            u128 y = 0;
-#pragma unroll
-            for (int part = 0; part < 4; ++part) {
-                const uint32_t v32 = static_cast<uint32_t>(incl >> (32 * part));
-                y |= static_cast<u128>(static_cast<uint32_t>(__shfl_up(v32, o, kWave))) << (32 * part);
+            for (int e = 0; e < kSeg; ++e) {
+                const bool in = s0 + e < s1;
+                rp[e] = quantise31(in ? fp[e] : 0.f, bd);
+                rq[e] = quantise31(in ? fq[e] : 0.f, bd);
+                sp += rp[e];
+                sq += rq[e];
             }
-            if (lane >= o) incl += y;
-        }
-        __syncthreads();
-        if (lane == kWave - 1) scan_sh[wv] = incl;
-        if (tid == 0) draw_tok = -1;
-        __syncthreads();
-        u128 wbefore = 0;
-        for (int w2 = 0; w2 < wv; ++w2) wbefore += scan_sh[w2];
-        // the slice sums: the same values as S (the distribution is unchanged since)
-        const SeqView vd = seq_reduce(ss, K, k, phase, ssum, 0, 0, 0, L);
-        if (vd.flags & kFlagTimeout) { finish(TMV_ERR_DEVICE, 0, 0, false); return; }
-        const u128 excl = vd.before + wbefore + incl - ssum;
-        const bool mine = vd.before <= t && t < vd.before + vd.own;      // t lies in this slice
-        // the thread whose segment holds the crossing point finds the token
-        if (ssum > 0 && excl <= t && t < excl + ssum) {
-            u128 cacc = excl;
-            for (int x = s0; x < s1; ++x) {
-                cacc += cur.stored ? w[x] : quantise(cur.row[x], bd) >> cur.shift;
-                if (cacc > t) { draw_tok = x; break; }
+            for (int x0 = s0 + kSeg; x0 < s1; x0 += kTailBatch) {
+                float tp[kTailBatch], tq[kTailBatch];
+#pragma unroll
+                for (int e = 0; e < kTailBatch; ++e) {
+                    tp[e] = row_load(prs, x0 + e);
+                    tq[e] = row_load(qrs, x0 + e);
+                }
+#pragma unroll
+                for (int e = 0; e < kTailBatch; ++e)
+                    if (x0 + e < s1) {
+                        sp += quantise31(tp[e], bd);
+                        sq += quantise31(tq[e], bd);
+                    }
+            }
+            if (tid < nk) {
+                int unused = 0;
+                kwp[tid] = quantise31(cp, unused);
+                kwq[tid] = quantise31(cq, unused);
             }
         }
-        __syncthreads();
-        const int tok = draw_tok >= 0 ? draw_tok : x_hi - 1;
-        finish(TMV_OK, acc, tok, mine);
+        // (slice sums of WP and WQ stay below 2^55, so they share one 128-bit sum)
+        const SeqView va = seq_reduce(ss, K, k, phase, static_cast<u128>(sp) | (static_cast<u128>(sq) << 64),
+                                      bd ? kFlagBad : 0, L);
+        if (va.flags & kFlagTimeout) { finish(TMV_ERR_DEVICE, 0, 0, false); return; }
+        const uint64_t SP = static_cast<uint64_t>(va.total), SQt = static_cast<uint64_t>(va.total >> 64);
+        if ((va.flags & kFlagBad) || SP == 0 || (have_q && SQt == 0)) { finish(TMV_ERR_INPUT, 0, 0, false); return; }
+        const uint64_t SQ = have_q ? SQt : 1;
+
+        // state on arrival: M = 0, R = WP * SQ
+        uint64_t Mc = 0;
+        u128 T = static_cast<u128>(SP) * SQ;
+        u128 mine_sum = static_cast<u128>(sp) * SQ;                          // this thread's share of T
+        u128 own = static_cast<u128>(static_cast<uint64_t>(va.own)) * SQ;    // this slice's share
+        u128 before = static_cast<u128>(static_cast<uint64_t>(va.before)) * SQ;
+        bool moved = false;
+        for (int ci = 0; ci < nk; ++ci) {
+            const uint64_t U = tmv::philox_word(seed, stream, n++) >> 40;
+            const uint32_t wpx = __builtin_amdgcn_readfirstlane(kwp[ci]), wqx = __builtin_amdgcn_readfirstlane(kwq[ci]);
+            if (sample_accepts(U, wqx, T, resid(wpx, wqx, SQ, Mc), SQ)) {
+                if (k == 0 && tid == 0) pth[acc] = kids[ci];
+                ++acc;
+                u = kids[ci];
+                moved = true;
+                break;
+            }
+            // refusal: the residual against q is the state at M + T / SQ
+            const uint64_t Mn = Mc + udiv_u128_u64(T, SQ);
+            // (SQ is made opaque here so that the products WP * SQ are not hoisted out of
+            // the refusal loop: sixteen of them would not fit next to the cached rows)
+            uint64_t SQp = SQ;
+            asm volatile("" : "+s"(SQp));
+            const u128 s = segment_sum(s0, s1, rp, rq, prs, qrs, SQp, Mn);
+            const SeqView vr = seq_reduce(ss, K, k, phase, s, 0, L);
+            if (vr.flags & kFlagTimeout) { finish(TMV_ERR_DEVICE, 0, 0, false); return; }
+            if (vr.total != 0) {               // an empty residual keeps the state
+                Mc = Mn;
+                T = vr.total;
+                mine_sum = s;
+                own = vr.own;
+                before = vr.before;
+            }
+        }
+        if (moved) continue;
+
+        // draw the bonus (no children) or the correction (all refused): the token is the
+        // first x whose running sum of R exceeds t.  The slice sums of the state locate
+        // the slice; inside it an exclusive scan of the segment sums locates the thread.
+        const u128 t = draw_target(tmv::philox_word(seed, stream, n++), T);
+        const bool mine = before <= t && t < before + own;
+        int tk = 0;
+        if (mine) {
+            u128 incl = mine_sum;
+            for (int o = 1; o < kWave; o <<= 1) {
+                u128 y = 0;
+#pragma unroll
+                for (int part = 0; part < 4; ++part) {
+                    const uint32_t v32 = static_cast<uint32_t>(incl >> (32 * part));
+                    y |= static_cast<u128>(static_cast<uint32_t>(__shfl_up(static_cast<int>(v32), o, kWave))) << (32 * part);
+                }
+                if (lane >= o) incl += y;
+            }
+            if (lane == kWave - 1) scan_sh[wv] = incl;
+            if (tid == 0) draw_tok = x_hi - 1;
+            __syncthreads();
+            u128 excl = before + incl - mine_sum;
+            for (int w2 = 0; w2 < wv; ++w2) excl += scan_sh[w2];
+            if (mine_sum > 0 && excl <= t && t < excl + mine_sum) {
+                u128 cum = excl;
+                int found = -1;
+#pragma unroll
+                for (int e = 0; e < kSeg; ++e) {          // (entries past the end add 0)
+                    cum += resid(rp[e], rq[e], SQ, Mc);
+                    if (found < 0 && cum > t) found = s0 + e;
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                visit_tail(s0, s1, prs, qrs, [&](int x, uint32_t a, uint32_t c2) {
+                    if (found < 0) {
+                        cum += resid(a, c2, SQ, Mc);
+                        if (cum > t) found = x;
+                    }
+                });
+                draw_tok = found >= 0 ? found : s1 - 1;   // (found is always set: cum reaches excl + mine_sum > t)
+            }
+            __syncthreads();
+            tk = draw_tok;
+        }
+        finish(TMV_OK, acc, tk, mine);
         return;
     }
 }
 
 }  // namespace
 
-// sampling workspace: [B][V] u64 working distributions | [B] sequence synchronisation
-// blocks (their counts zero between calls)
-static size_t sample_ws_bytes(int B, int V, size_t *off_sync) {
-    const size_t dist = (static_cast<size_t>(B) * V * sizeof(uint64_t) + 255) / 256 * 256;
-    if (off_sync) *off_sync = dist;
-    return dist + static_cast<size_t>(B) * sizeof(SeqSync);
+// sampling workspace: one synchronisation block per sequence (all zero between calls)
+static size_t sample_ws_bytes(int B) {
+    return static_cast<size_t>(B) * sizeof(SeqSync) + 256;
 }
 
 // workgroups per sequence: at most one workgroup per compute unit in all (so every workgroup
-// a barrier waits for is resident), at most kMaxSlices, slices of >= 1024 entries
+// a barrier waits for is resident), at most kMaxSlices, slices of >= 2048 entries
 static int sample_slices(int B, int V) {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         cus = 1;
     int K = cus / (B > 0 ? B : 1);
     if (K > kMaxSlices) K = kMaxSlices;
-    if (K > V / 1024) K = V / 1024;
+    if (K > V / 2048) K = V / 2048;
     return K < 1 ? 1 : K;
 }
 
@@ -708,7 +773,7 @@ extern "C" size_t tmv_tree_accept_workspace(int mode, int B, int M_max, int V)
         const int nchunk = (V + kScanChunk - 1) / kScanChunk;
         return static_cast<size_t>(B) * (M_max + 1) * nchunk * sizeof(uint64_t) + 256;
     }
-    return sample_ws_bytes(B, V, nullptr);
+    return sample_ws_bytes(B);
 }
 
 extern "C" int tmv_tree_accept(int mode, int B, int M_max, int D_max, int V,
@@ -749,12 +814,11 @@ extern "C" int tmv_tree_accept(int mode, int B, int M_max, int D_max, int V,
         return tmv_host::launch_status(hipGetLastError());
     }
     if (row_dtype != TMV_F32 || !draft_q || q_stride_b < 0 || q_stride_row < 0) return TMV_ERR_ARG;
+    if (V > (1 << 24)) return TMV_ERR_ARG;
     const int K = sample_slices(B, V);
-    size_t off_sync = 0;
-    sample_ws_bytes(B, V, &off_sync);
     hipLaunchKernelGGL(sample_walk_kernel, dim3(static_cast<unsigned>(B) * K), dim3(kSampleThreads), 0, s, M_max,
                        D_max, V, K, tokens, static_cast<const float *>(teacher), t_stride_b, t_stride_row, draft_q,
                        q_stride_b, q_stride_row, seed, step, n_nodes, anc, depth, status, accept_len, path,
-                       next_token, reinterpret_cast<uint64_t *>(ws), reinterpret_cast<SeqSync *>(ws + off_sync));
+                       next_token, reinterpret_cast<SeqSync *>(ws));
     return tmv_host::launch_status(hipGetLastError());
 }

@@ -215,11 +215,11 @@ greedy_select_kernel(int M_max, int D_max, int V, int nchunk, const int32_t *__r
 
 // ============================================================== sampling
 // K workgroups walk each sequence together, each owning a contiguous slice of the
-// vocabulary; every thread owns a contiguous segment of its slice.  At node u the teacher
+// vocabulary.  At node u the teacher
 // row p and the draft row q stay fixed while children are refused, and the residual left
 // after j refusals is (p - c_j q)+ renormalised (c_{j+1} = c_j + sum (p - c_j q)+).  In
 // integers the state is (M, T): R(y) = max(0, WP(y) SQ - WQ(y) M), T = sum R, and a
-// refusal adds floor(T / SQ) to M.  So each thread quantises its segment of both rows
+// refusal adds floor(T / SQ) to M.  So each thread quantises its entries of both rows
 // once per node and keeps it in registers; a refusal is one pass of integer arithmetic
 // over registers and one exact sum, and the test of any child needs only WP and WQ at its
 // token.  The slices' partial sums meet at a per-sequence barrier of phase-tagged records
@@ -228,9 +228,9 @@ constexpr int kSampleThreads = 1024;
 constexpr int kSampleWaves = kSampleThreads / kWave;
 constexpr int kMaxNodes = 128;                 // tree nodes per sequence (host-checked)
 constexpr int kMaxSlices = 64;                 // workgroups per sequence: one lane each at the barrier
+constexpr int kMaxWords = 4 * ((kMaxNodes + 1 + 3) / 4);   // one per tried child, one draw
 constexpr int kSeg = 16;                       // segment entries a thread keeps in registers
 constexpr int kTailBatch = 4;                  // loads in flight per thread beyond them
-constexpr int kSumGroup = 2;                   // register entries whose arithmetic may overlap
 constexpr uint64_t kSyncSpinTicks = 200000;    // 2 ms at the 100 MHz s_memrealtime clock
 constexpr int kFlagBad = 1;                    // an entry outside [0, 1] in a scanned row
 constexpr int kFlagTimeout = 2;                // a workgroup stopped waiting for the others
@@ -266,10 +266,12 @@ struct SeqView {
 };
 
 struct SyncLds {
-    u128 red[kSampleWaves];
-    int fl[kSampleWaves];
+    u128 red[kSampleThreads];   // every thread's term of the block sum
+    int fl[kSampleWaves];       // per wave: any flag raised
     u128 res[3];         // total, before, own
     int res_flags;
+    uint64_t dec_m;      // decision for the next child (taken by wave 0): M after a refusal,
+    int dec_accept;      // and whether the child is accepted
 };
 
 // wave-uniform copies in scalar registers (the values are equal in every lane)
@@ -306,11 +308,14 @@ struct R96 {
     uint64_t hi;
 };
 
+// kWideSQ / kWideM: whether SQ / M may exceed 32 bits (when not, their high products vanish;
+// normalised rows give SQ < 2^32, and M < 2^32 until c_j reaches about 2)
+template <bool kWideSQ = true, bool kWideM = true>
 __device__ __forceinline__ R96 resid96(uint32_t wp, uint32_t wq, uint64_t SQ, uint64_t M) {
     const uint64_t a_lo = static_cast<uint64_t>(wp) * static_cast<uint32_t>(SQ);
-    const uint64_t a_hi = static_cast<uint64_t>(wp) * static_cast<uint32_t>(SQ >> 32);
+    const uint64_t a_hi = kWideSQ ? static_cast<uint64_t>(wp) * static_cast<uint32_t>(SQ >> 32) : 0;
     const uint64_t c_lo = static_cast<uint64_t>(wq) * static_cast<uint32_t>(M);
-    const uint64_t c_hi = static_cast<uint64_t>(wq) * static_cast<uint32_t>(M >> 32);
+    const uint64_t c_hi = kWideM ? static_cast<uint64_t>(wq) * static_cast<uint32_t>(M >> 32) : 0;
     const uint64_t a12 = (a_lo >> 32) + a_hi, c12 = (c_lo >> 32) + c_hi;   // (neither sum wraps)
     const uint32_t a0 = static_cast<uint32_t>(a_lo), c0 = static_cast<uint32_t>(c_lo);
     // a - c as lo + d12 * 2^32 with a signed high part (a12 < 2^55, c12 < 2^63: no overflow);
@@ -366,13 +371,6 @@ __device__ __forceinline__ u128 draw_target(uint64_t word, u128 T) {
     return static_cast<u128>(h) * (T >> 32) + ((static_cast<u128>(h) * static_cast<uint32_t>(T)) >> 32);
 }
 
-__device__ __forceinline__ uint32_t shfl_u32(uint32_t v, int src) { return static_cast<uint32_t>(__shfl(static_cast<int>(v), src, kWave)); }
-
-__device__ __forceinline__ int wave_or(int v) {
-    for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, kWave);
-    return v;
-}
-
 // true in every thread if v is true in any thread of the block
 __device__ bool block_any(bool v, int *sh) {
     __syncthreads();
@@ -384,18 +382,25 @@ __device__ bool block_any(bool v, int *sh) {
 }
 
 // Sum `local` over the block and then over the K slices of the sequence.  Every thread
-// of the block calls it; `phase` counts the calls and advances alike in all K.
-__device__ SeqView seq_reduce(SeqSync *ss, int K, int k, int &phase, u128 local, int flags, SyncLds &L) {
+// of the block calls it; `phase` counts the calls and advances alike in all K.  Wave 0,
+// which gathers the slices' sums, then runs post(view) -- the walk's scalar decisions are
+// taken there once, instead of in every wave -- before the block reads the results.
+template <class Post>
+__device__ SeqView seq_reduce(SeqSync *ss, int K, int k, int &phase, u128 local, int flags, SyncLds &L, Post post) {
     const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-    const u128 v = tmv::wave_sum_u128(local);
-    const int f = wave_or(flags);
+    const bool any_bad = __ballot(flags != 0) != 0;
     __syncthreads();                                  // the previous call's results are read
-    if (lane == 0) { L.red[wv] = v; L.fl[wv] = f; }
+    L.red[threadIdx.x] = local;
+    if (lane == 0) L.fl[wv] = any_bad ? 1 : 0;
     __syncthreads();
     const uint64_t tag = static_cast<uint64_t>(++phase);
     if (wv == 0) {
-        const u128 wg = tmv::wave_sum_u128(lane < kSampleWaves ? L.red[lane] : 0);
-        const int fl = wave_or(lane < kSampleWaves ? L.fl[lane] : 0);
+        // the block's sum: each lane adds sixteen staged terms, then one wave reduction
+        u128 part = 0;
+#pragma unroll
+        for (int j = 0; j < kSampleThreads / kWave; ++j) part += L.red[j * kWave + lane];
+        const u128 wg = tmv::wave_sum_u128(part);
+        const int fl = __ballot(lane < kSampleWaves && L.fl[lane] != 0) != 0 ? kFlagBad : 0;
         const uint64_t own[4] = {static_cast<uint64_t>(wg) & kPieceMask, static_cast<uint64_t>(wg >> 48) & kPieceMask,
                                  static_cast<uint64_t>(wg >> 96) & kPieceMask, static_cast<uint64_t>(fl)};
         uint64_t *slot = &ss->rec[tag & 1][0][0];
@@ -422,22 +427,35 @@ __device__ SeqView seq_reduce(SeqSync *ss, int K, int k, int &phase, u128 local,
             if (__builtin_amdgcn_s_memrealtime() - t0 > kSyncSpinTicks) { timed_out = 1; break; }
             __builtin_amdgcn_s_sleep(1);
         }
-        u128 vj = 0;
-        int fj = 0;
-        if (lane < K) {
-            vj = (static_cast<u128>(w2 & kPieceMask) << 96) | (static_cast<u128>(w1 & kPieceMask) << 48) |
-                 (w0 & kPieceMask);
-            fj = static_cast<int>(w3 & kPieceMask);
+        // the slices' sums in scalar registers, slice by slice (K is at most 64)
+        const bool rec_bad = __ballot(lane < K && (w3 & kPieceMask) != 0) != 0;
+        u128 tot = 0, bef = 0;
+        for (int j = 0; j < K; ++j) {
+            const uint32_t a0 = __builtin_amdgcn_readlane(static_cast<uint32_t>(w0), j);
+            const uint32_t a1 = __builtin_amdgcn_readlane(static_cast<uint32_t>(w0 >> 32), j);
+            const uint32_t b0 = __builtin_amdgcn_readlane(static_cast<uint32_t>(w1), j);
+            const uint32_t b1 = __builtin_amdgcn_readlane(static_cast<uint32_t>(w1 >> 32), j);
+            const uint32_t c0 = __builtin_amdgcn_readlane(static_cast<uint32_t>(w2), j);
+            const uint32_t c1 = __builtin_amdgcn_readlane(static_cast<uint32_t>(w2 >> 32), j);
+            const u128 vj = (static_cast<u128>(((static_cast<uint64_t>(c1) << 32) | c0) & kPieceMask) << 96) |
+                            (static_cast<u128>(((static_cast<uint64_t>(b1) << 32) | b0) & kPieceMask) << 48) |
+                            (((static_cast<uint64_t>(a1) << 32) | a0) & kPieceMask);
+            if (j < k) bef += vj;
+            tot += vj;
         }
-        const u128 tot = tmv::wave_sum_u128(vj);
-        const u128 bef = tmv::wave_sum_u128(lane < k ? vj : 0);
-        fj = wave_or(fj);
+        const int fj = (rec_bad ? kFlagBad : 0) | (timed_out ? kFlagTimeout : 0);
         if (lane == 0) {
             L.res[0] = tot;
             L.res[1] = bef;
             L.res[2] = wg;
-            L.res_flags = fj | (timed_out ? kFlagTimeout : 0);
+            L.res_flags = fj;
         }
+        SeqView w;
+        w.total = tot;
+        w.before = bef;
+        w.own = uniform_u128(wg);
+        w.flags = fj;
+        post(w);
     }
     __syncthreads();
     SeqView r;
@@ -470,45 +488,63 @@ __device__ void seq_leave(SeqSync *ss, int K) {
     }
 }
 
-// Visit the entries of a thread's segment [s0, s1) beyond the kSeg held in registers
-// (only when a slice exceeds kSampleThreads * kSeg entries): f(x, WP(x), WQ(x)) in order,
-// read and quantised again.
+// Slice layout: column c of a slice is the 1024 entries x_lo + c * kSampleThreads + [0,
+// kSampleThreads), so thread t holds entry t of every column and each column is read with
+// fully coalesced loads.  Columns 0 .. kSeg-1 live in registers; later ones (only when a
+// slice exceeds kSampleThreads * kSeg entries) are read and quantised again when needed.
+
+// f(c, WP, WQ) for this thread's entry of every column c >= kSeg (WP = WQ = 0 past the slice)
 template <class F>
-__device__ __forceinline__ void visit_tail(int s0, int s1, __amdgpu_buffer_rsrc_t prs, __amdgpu_buffer_rsrc_t qrs, F f) {
-    for (int x0 = s0 + kSeg; x0 < s1; x0 += kTailBatch) {
+__device__ __forceinline__ void visit_tail_columns(int x_lo, int x_hi, int ncol, __amdgpu_buffer_rsrc_t prs,
+                                                   __amdgpu_buffer_rsrc_t qrs, F f) {
+    for (int c0 = kSeg; c0 < ncol; c0 += kTailBatch) {
         float tp[kTailBatch], tq[kTailBatch];
 #pragma unroll
         for (int e = 0; e < kTailBatch; ++e) {
-            tp[e] = row_load(prs, x0 + e);
-            tq[e] = row_load(qrs, x0 + e);
+            const int x = x_lo + (c0 + e) * kSampleThreads + static_cast<int>(threadIdx.x);
+            tp[e] = row_load(prs, x);
+            tq[e] = row_load(qrs, x);
         }
         int unused = 0;
 #pragma unroll
-        for (int e = 0; e < kTailBatch; ++e)
-            if (x0 + e < s1) f(x0 + e, quantise31(tp[e], unused), quantise31(tq[e], unused));
+        for (int e = 0; e < kTailBatch; ++e) {
+            const bool in = c0 + e < ncol && x_lo + (c0 + e) * kSampleThreads + static_cast<int>(threadIdx.x) < x_hi;
+            f(c0 + e, quantise31(in ? tp[e] : 0.f, unused), quantise31(in ? tq[e] : 0.f, unused));
+        }
     }
 }
 
-// sum of R over a thread's segment.  Register entries past the segment's end hold
-// WP = WQ = 0 (R = 0), so the register part runs unguarded; its 96-bit terms are summed in
-// two 64-bit halves (each below 2^59 over kSeg terms).
-__device__ __forceinline__ u128 segment_sum(int s0, int s1, const uint32_t (&rp)[kSeg], const uint32_t (&rq)[kSeg],
-                                            __amdgpu_buffer_rsrc_t prs, __amdgpu_buffer_rsrc_t qrs, uint64_t SQ,
-                                            uint64_t M) {
-    uint64_t lo = 0, hi = 0;
+// this thread's sum of R over the register columns, in two 64-bit halves (each below 2^59)
+template <bool kWideSQ, bool kWideM>
+__device__ __forceinline__ void register_sum(const uint32_t (&rp)[kSeg], const uint32_t (&rq)[kSeg], uint64_t SQ,
+                                             uint64_t M, uint64_t &lo, uint64_t &hi) {
 #pragma unroll
     for (int e = 0; e < kSeg; ++e) {
         // (opaque copies: the compiler would otherwise keep 64-bit widened copies of the
         // cached rows alive across the refusal loop)
         uint32_t wp = rp[e], wq = rq[e];
         asm volatile("" : "+v"(wp), "+v"(wq));
-        const R96 r = resid96(wp, wq, SQ, M);
+        const R96 r = resid96<kWideSQ, kWideM>(wp, wq, SQ, M);
         lo += r.lo;
         hi += r.hi;
-        if (e % kSumGroup == kSumGroup - 1) __builtin_amdgcn_sched_barrier(0);   // bounds the overlap
+    }
+}
+
+// this thread's sum of R over its entries of the slice
+__device__ __forceinline__ u128 thread_sum(const uint32_t (&rp)[kSeg], const uint32_t (&rq)[kSeg], int x_lo,
+                                           int x_hi, int ncol, __amdgpu_buffer_rsrc_t prs,
+                                           __amdgpu_buffer_rsrc_t qrs, uint64_t SQ, uint64_t M) {
+    uint64_t lo = 0, hi = 0;
+    const bool wide_sq = (SQ >> 32) != 0, wide_m = (M >> 32) != 0;      // (wave-uniform)
+    if (wide_sq) {
+        if (wide_m) register_sum<true, true>(rp, rq, SQ, M, lo, hi);
+        else register_sum<true, false>(rp, rq, SQ, M, lo, hi);
+    } else {
+        if (wide_m) register_sum<false, true>(rp, rq, SQ, M, lo, hi);
+        else register_sum<false, false>(rp, rq, SQ, M, lo, hi);
     }
     u128 s = static_cast<u128>(lo) + (static_cast<u128>(hi) << 32);
-    visit_tail(s0, s1, prs, qrs, [&](int, uint32_t a, uint32_t c2) { s += resid(a, c2, SQ, M); });
+    visit_tail_columns(x_lo, x_hi, ncol, prs, qrs, [&](int, uint32_t a, uint32_t c2) { s += resid(a, c2, SQ, M); });
     return s;
 }
 
@@ -530,16 +566,17 @@ sample_walk_kernel(int M_max, int D_max, int V, int K,
     __shared__ int kid_count[kSampleWaves];
     __shared__ int nkids;
     __shared__ uint32_t kwp[kMaxNodes], kwq[kMaxNodes];   // WP and WQ at the children's tokens
+    __shared__ uint32_t rows_lds[2][kSeg * kSampleThreads]; // draw: one chunk of the slice, in x order
     __shared__ u128 scan_sh[kSampleWaves];
     __shared__ int flag_sh;
     __shared__ int draw_tok;
+    __shared__ uint64_t words[kMaxWords];                 // the walk's random words, in order
 
     const int b = blockIdx.x / K, k = blockIdx.x % K, tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wv = tid / kWave;
     const int x_lo = static_cast<int>(static_cast<int64_t>(V) * k / K);
     const int x_hi = static_cast<int>(static_cast<int64_t>(V) * (k + 1) / K);
-    const int seg = (x_hi - x_lo + kSampleThreads - 1) / kSampleThreads;
-    const int s0 = min(x_hi, x_lo + tid * seg), s1 = min(x_hi, s0 + seg);
+    const int ncol = (x_hi - x_lo + kSampleThreads - 1) / kSampleThreads;
     SeqSync *ss = sync + b;
     int phase = 0;
     const int R = M_max + 1, W = D_max + 1;
@@ -573,6 +610,16 @@ sample_walk_kernel(int M_max, int D_max, int V, int K,
     };
     if (st != TMV_OK) { finish(st, 0, 0, false); return; }
 
+    const float *p_b = p + b * psb, *q_b = q + b * qsb;
+
+    // the random words the walk can consume (one per tried child and one draw), computed
+    // once: Philox blocks at counters 1, 2, ... hold words 0-3, 4-7, ...
+    if (tid < kMaxWords / 4) {
+        uint64_t o[4];
+        tmv::philox4x64_10(static_cast<uint64_t>(tid) + 1, seed, stream, o);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) words[4 * tid + j] = o[j];
+    }
     // the live nodes' parents and tokens (every slice checks every token: one answer)
     bool bad_tok = false;
     for (int c = tid; c <= M_max; c += kSampleThreads) {
@@ -612,10 +659,10 @@ sample_walk_kernel(int M_max, int D_max, int V, int K,
         }
         const int nk = nkids;
         const bool have_q = nk > 0;          // a leaf's q row is never read
-        const __amdgpu_buffer_rsrc_t prs = row_buffer(p + b * psb + static_cast<int64_t>(u) * psr, V * 4);
-        const __amdgpu_buffer_rsrc_t qrs = row_buffer(q + b * qsb + static_cast<int64_t>(u) * qsr, have_q ? V * 4 : 0);
+        const __amdgpu_buffer_rsrc_t prs = row_buffer(p_b + static_cast<int64_t>(u) * psr, V * 4);
+        const __amdgpu_buffer_rsrc_t qrs = row_buffer(q_b + static_cast<int64_t>(u) * qsr, have_q ? V * 4 : 0);
 
-        // arrival at u: quantise this thread's segment of both rows into registers, sum
+        // arrival at u: quantise this thread's entries of both rows into registers, sum
         // them, and fetch both rows at the children's tokens
         int bd = 0;
         uint64_t sp = 0, sq = 0;
@@ -623,29 +670,31 @@ sample_walk_kernel(int M_max, int D_max, int V, int K,
             float fp[kSeg], fq[kSeg];
 #pragma unroll
             for (int e = 0; e < kSeg; ++e) {
-                fp[e] = row_load(prs, s0 + e);
-                fq[e] = row_load(qrs, s0 + e);
+                const int x = x_lo + e * kSampleThreads + tid;
+                fp[e] = row_load(prs, x);
+                fq[e] = row_load(qrs, x);
             }
             const int xc = tid < nk ? tok[kids[tid]] : 0;
             const float cp = row_load(prs, xc), cq = row_load(qrs, xc);
 #pragma unroll
             for (int e = 0; e < kSeg; ++e) {
-                const bool in = s0 + e < s1;
+                const bool in = x_lo + e * kSampleThreads + tid < x_hi;
                 rp[e] = quantise31(in ? fp[e] : 0.f, bd);
                 rq[e] = quantise31(in ? fq[e] : 0.f, bd);
                 sp += rp[e];
                 sq += rq[e];
             }
-            for (int x0 = s0 + kSeg; x0 < s1; x0 += kTailBatch) {
+            for (int c0 = kSeg; c0 < ncol; c0 += kTailBatch) {
                 float tp[kTailBatch], tq[kTailBatch];
 #pragma unroll
                 for (int e = 0; e < kTailBatch; ++e) {
-                    tp[e] = row_load(prs, x0 + e);
-                    tq[e] = row_load(qrs, x0 + e);
+                    const int x = x_lo + (c0 + e) * kSampleThreads + tid;
+                    tp[e] = row_load(prs, x);
+                    tq[e] = row_load(qrs, x);
                 }
 #pragma unroll
                 for (int e = 0; e < kTailBatch; ++e)
-                    if (x0 + e < s1) {
+                    if (c0 + e < ncol && x_lo + (c0 + e) * kSampleThreads + tid < x_hi) {
                         sp += quantise31(tp[e], bd);
                         sq += quantise31(tq[e], bd);
                     }
@@ -656,9 +705,32 @@ sample_walk_kernel(int M_max, int D_max, int V, int K,
                 kwq[tid] = quantise31(cq, unused);
             }
         }
+        // The decision on child ci against state (M, T): its random word, the accept test,
+        // and after a refusal the next threshold M + floor(T / SQ).  Taken by wave 0.
+        auto decide = [&](int ci, uint64_t Md, u128 Td, uint64_t SQd) {
+            int accept = 0;
+            uint64_t m_next = 0;
+            if (ci < nk) {
+                const uint64_t U = words[n + ci] >> 40;
+                const uint32_t wpx = __builtin_amdgcn_readfirstlane(kwp[ci]);
+                const uint32_t wqx = __builtin_amdgcn_readfirstlane(kwq[ci]);
+                accept = sample_accepts(U, wqx, Td, resid(wpx, wqx, SQd, Md), SQd) ? 1 : 0;
+                if (!accept) m_next = Md + udiv_u128_u64(Td, SQd);
+            }
+            if (lane == 0) {
+                L.dec_accept = accept;
+                L.dec_m = m_next;
+            }
+        };
         // (slice sums of WP and WQ stay below 2^55, so they share one 128-bit sum)
         const SeqView va = seq_reduce(ss, K, k, phase, static_cast<u128>(sp) | (static_cast<u128>(sq) << 64),
-                                      bd ? kFlagBad : 0, L);
+                                      bd ? kFlagBad : 0, L, [&](const SeqView &w) {
+            const uint64_t sp_w = static_cast<uint64_t>(w.total), sq_w = static_cast<uint64_t>(w.total >> 64);
+            if (!(w.flags & (kFlagBad | kFlagTimeout)) && sp_w != 0 && (!have_q || sq_w != 0)) {
+                const uint64_t sq1 = have_q ? sq_w : 1;
+                decide(0, 0, static_cast<u128>(sp_w) * sq1, sq1);
+            }
+        });
         if (va.flags & kFlagTimeout) { finish(TMV_ERR_DEVICE, 0, 0, false); return; }
         const uint64_t SP = static_cast<uint64_t>(va.total), SQt = static_cast<uint64_t>(va.total >> 64);
         if ((va.flags & kFlagBad) || SP == 0 || (have_q && SQt == 0)) { finish(TMV_ERR_INPUT, 0, 0, false); return; }
@@ -667,80 +739,111 @@ sample_walk_kernel(int M_max, int D_max, int V, int K,
         // state on arrival: M = 0, R = WP * SQ
         uint64_t Mc = 0;
         u128 T = static_cast<u128>(SP) * SQ;
-        u128 mine_sum = static_cast<u128>(sp) * SQ;                          // this thread's share of T
         u128 own = static_cast<u128>(static_cast<uint64_t>(va.own)) * SQ;    // this slice's share
         u128 before = static_cast<u128>(static_cast<uint64_t>(va.before)) * SQ;
         bool moved = false;
         for (int ci = 0; ci < nk; ++ci) {
-            const uint64_t U = tmv::philox_word(seed, stream, n++) >> 40;
-            const uint32_t wpx = __builtin_amdgcn_readfirstlane(kwp[ci]), wqx = __builtin_amdgcn_readfirstlane(kwq[ci]);
-            if (sample_accepts(U, wqx, T, resid(wpx, wqx, SQ, Mc), SQ)) {
+            if (__builtin_amdgcn_readfirstlane(L.dec_accept)) {
                 if (k == 0 && tid == 0) pth[acc] = kids[ci];
                 ++acc;
                 u = kids[ci];
+                n += ci + 1;
                 moved = true;
                 break;
             }
             // refusal: the residual against q is the state at M + T / SQ
-            const uint64_t Mn = Mc + udiv_u128_u64(T, SQ);
+            const uint64_t Mn = uniform_u64(L.dec_m);
             // (SQ is made opaque here so that the products WP * SQ are not hoisted out of
             // the refusal loop: sixteen of them would not fit next to the cached rows)
             uint64_t SQp = SQ;
             asm volatile("" : "+s"(SQp));
-            const u128 s = segment_sum(s0, s1, rp, rq, prs, qrs, SQp, Mn);
-            const SeqView vr = seq_reduce(ss, K, k, phase, s, 0, L);
+            const u128 s = thread_sum(rp, rq, x_lo, x_hi, ncol, prs, qrs, SQp, Mn);
+            const SeqView vr = seq_reduce(ss, K, k, phase, s, 0, L, [&](const SeqView &w) {
+                if (!(w.flags & kFlagTimeout)) {
+                    if (w.total != 0) decide(ci + 1, Mn, w.total, SQ);
+                    else decide(ci + 1, Mc, T, SQ);      // empty residual: the state is kept
+                }
+            });
             if (vr.flags & kFlagTimeout) { finish(TMV_ERR_DEVICE, 0, 0, false); return; }
             if (vr.total != 0) {               // an empty residual keeps the state
                 Mc = Mn;
                 T = vr.total;
-                mine_sum = s;
                 own = vr.own;
                 before = vr.before;
             }
         }
         if (moved) continue;
+        n += nk;
 
-        // draw the bonus (no children) or the correction (all refused): the token is the
-        // first x whose running sum of R exceeds t.  The slice sums of the state locate
-        // the slice; inside it an exclusive scan of the segment sums locates the thread.
-        const u128 t = draw_target(tmv::philox_word(seed, stream, n++), T);
+        // Draw the bonus (no children) or the correction (all refused): the token is the
+        // first x whose running sum of R exceeds t.  The slice sums locate the slice.
+        // Inside it, groups of kSeg columns are summed column by column until the group
+        // holding t is found; an exclusive scan over the threads of that column ends it.
+        const u128 t = draw_target(words[n], T);
         const bool mine = before <= t && t < before + own;
         int tk = 0;
         if (mine) {
-            u128 incl = mine_sum;
-            for (int o = 1; o < kWave; o <<= 1) {
-                u128 y = 0;
+            // The slice in chunks of kSeg columns (kSeg * kSampleThreads entries), each staged
+            // in LDS in x order -- the first from the registers, which makes them free for
+            // the draw -- so that thread i holds entries [kSeg i, kSeg i + kSeg) of the chunk.
+            u128 base = before;             // running sum before the current chunk
+            int found = -1;
 #pragma unroll
-                for (int part = 0; part < 4; ++part) {
-                    const uint32_t v32 = static_cast<uint32_t>(incl >> (32 * part));
-                    y |= static_cast<u128>(static_cast<uint32_t>(__shfl_up(static_cast<int>(v32), o, kWave))) << (32 * part);
-                }
-                if (lane >= o) incl += y;
+            for (int e = 0; e < kSeg; ++e) {
+                rows_lds[0][e * kSampleThreads + tid] = rp[e];
+                rows_lds[1][e * kSampleThreads + tid] = rq[e];
             }
-            if (lane == kWave - 1) scan_sh[wv] = incl;
-            if (tid == 0) draw_tok = x_hi - 1;
-            __syncthreads();
-            u128 excl = before + incl - mine_sum;
-            for (int w2 = 0; w2 < wv; ++w2) excl += scan_sh[w2];
-            if (mine_sum > 0 && excl <= t && t < excl + mine_sum) {
-                u128 cum = excl;
-                int found = -1;
+            for (int c0 = 0; c0 < ncol && found < 0; c0 += kSeg) {
+                if (c0 > 0) {
+                    __syncthreads();                      // (the previous chunk is read)
 #pragma unroll
-                for (int e = 0; e < kSeg; ++e) {          // (entries past the end add 0)
-                    cum += resid(rp[e], rq[e], SQ, Mc);
-                    if (found < 0 && cum > t) found = s0 + e;
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                visit_tail(s0, s1, prs, qrs, [&](int x, uint32_t a, uint32_t c2) {
-                    if (found < 0) {
-                        cum += resid(a, c2, SQ, Mc);
-                        if (cum > t) found = x;
+                    for (int e = 0; e < kSeg; ++e) {
+                        const int x = x_lo + (c0 + e) * kSampleThreads + tid;
+                        const bool in = c0 + e < ncol && x < x_hi;
+                        const float fpv = row_load(prs, x), fqv = row_load(qrs, x);
+                        int unused = 0;
+                        rows_lds[0][e * kSampleThreads + tid] = in ? quantise31(fpv, unused) : 0u;
+                        rows_lds[1][e * kSampleThreads + tid] = in ? quantise31(fqv, unused) : 0u;
                     }
-                });
-                draw_tok = found >= 0 ? found : s1 - 1;   // (found is always set: cum reaches excl + mine_sum > t)
+                }
+                __syncthreads();
+                u128 mine_sum = 0;
+#pragma unroll
+                for (int i = 0; i < kSeg; ++i)
+                    mine_sum += resid(rows_lds[0][kSeg * tid + i], rows_lds[1][kSeg * tid + i], SQ, Mc);
+                // exclusive scan of the threads' sums (the chunk total comes with it)
+                u128 incl = mine_sum;
+                for (int o = 1; o < kWave; o <<= 1) {
+                    u128 y = 0;
+#pragma unroll
+                    for (int part = 0; part < 4; ++part) {
+                        const uint32_t v32 = static_cast<uint32_t>(incl >> (32 * part));
+                        y |= static_cast<u128>(static_cast<uint32_t>(__shfl_up(static_cast<int>(v32), o, kWave))) << (32 * part);
+                    }
+                    if (lane >= o) incl += y;
+                }
+                if (lane == kWave - 1) scan_sh[wv] = incl;
+                if (tid == 0) draw_tok = -1;
+                __syncthreads();
+                u128 excl = base + incl - mine_sum, chunk = 0;
+                for (int w2 = 0; w2 < kSampleWaves; ++w2) {
+                    if (w2 < wv) excl += scan_sh[w2];
+                    chunk += scan_sh[w2];
+                }
+                if (mine_sum > 0 && excl <= t && t < excl + mine_sum) {
+                    u128 cum = excl;
+                    int f = -1;
+                    for (int i = 0; i < kSeg && f < 0; ++i) {
+                        cum += resid(rows_lds[0][kSeg * tid + i], rows_lds[1][kSeg * tid + i], SQ, Mc);
+                        if (cum > t) f = i;
+                    }
+                    draw_tok = x_lo + c0 * kSampleThreads + kSeg * tid + (f < 0 ? kSeg - 1 : f);
+                }
+                __syncthreads();
+                found = __builtin_amdgcn_readfirstlane(draw_tok);
+                base = uniform_u128(base + chunk);
             }
-            __syncthreads();
-            tk = draw_tok;
+            tk = found >= 0 ? found : x_hi - 1;   // (found is always set: t lies in this slice)
         }
         finish(TMV_OK, acc, tk, mine);
         return;

@@ -128,6 +128,7 @@ greedy_select_kernel(int M_max, int D_max, int V, int nchunk, const int32_t *__r
     constexpr int kKeyBatch = 32;                  // chunk keys per row fetched at once
     constexpr int kAncBatch = 8;                   // ancestor entries per node fetched at once
     __shared__ int32_t tsel[129], tok_sh[129];
+    __shared__ int32_t anc_sh[129][kAncBatch];     // every row's first ancestor entries
     __shared__ int bad;
     __shared__ uint64_t best_node[kScanThreads / kWave];
     const int R = M_max + 1, W = D_max + 1;
@@ -154,7 +155,11 @@ greedy_select_kernel(int M_max, int D_max, int V, int nchunk, const int32_t *__r
     const int st = (st_in == TMV_OK && (M < 0 || M > M_max)) ? TMV_ERR_INPUT : st_in;
     int32_t *pth = path + static_cast<int64_t>(b) * D_max;
     if (tid == 0) bad = st != TMV_OK;
-    if (tid < R) tok_sh[tid] = tok;
+    if (tid < R) {
+        tok_sh[tid] = tok;
+#pragma unroll
+        for (int k = 0; k < kAncBatch; ++k) anc_sh[tid][k] = a8[k];
+    }
     __syncthreads();
     const bool row_live = st == TMV_OK && tid < R && tid <= M && (tid == 0 || dep >= 1);
     if (row_live) {
@@ -209,8 +214,12 @@ greedy_select_kernel(int M_max, int D_max, int V, int nchunk, const int32_t *__r
     }
     __syncthreads();
     const int dstar = static_cast<int>(best_node[0] >> 32), star = static_cast<int>(best_node[0] & 0xffffffffu);
-    for (int j = tid; j < D_max; j += kScanThreads)
-        pth[j] = j < dstar ? anc[(static_cast<int64_t>(b) * R + star) * W + (dstar - 1 - j)] : 0;
+    // the path root -> leaf is the chosen node's ancestor row read backwards; its first
+    // kAncBatch entries are already in LDS
+    for (int j = tid; j < D_max; j += kScanThreads) {
+        const int e = dstar - 1 - j;
+        pth[j] = j >= dstar ? 0 : e < kAncBatch ? anc_sh[star][e] : anc[(static_cast<int64_t>(b) * R + star) * W + e];
+    }
 }
 
 // ============================================================== sampling

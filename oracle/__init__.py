@@ -17,6 +17,8 @@ Every function mirrors one entry point of the C ABI on host arrays:
 ``accept_sample``     modified rejection sampling with min(1,p/q) and the normalised
                       max(0,p-q) residual (blog, modified rejection sampling section)
 ``commit``            prefix-sharing path-index commit (Chinese summary, section 2.1)
+``tree_best_first``   best-first prefix tree from per-position draft marginals and the
+                      budget controller (BASTION summary, sections 1-3)
 """
 from __future__ import annotations
 
@@ -65,6 +67,7 @@ def _load():
         lib.tmvref_philox_words.restype = None
         lib.tmvref_sample_accept_test.argtypes = [U64, U64, U64, U64, U64, U64, U64]
         lib.tmvref_sample_draw.argtypes = [P, P, I, U64]
+        lib.tmvref_tree_best_first.argtypes = [I, I, I, I, P, P, D, P, P, P, P, P]
         _lib = lib
     return _lib
 
@@ -198,3 +201,20 @@ def sample_draw(w, word) -> int:
     lo = np.array([int(x) & m for x in w], np.uint64)
     hi = np.array([int(x) >> 64 for x in w], np.uint64)
     return int(_load().tmvref_sample_draw(_p(lo), _p(hi), len(w), int(word)))
+
+
+def tree_best_first(q, N_max, cost=None, l_ar=1.0, status=None):
+    """q float32 [B][D][V] (row k = marginal of position k+1); cost float64 [N_max] or None.
+    Returns (parents [B][N_max+1], tokens [B][N_max+1], n_nodes [B], rho [B][N_max+1], status)."""
+    q = _c(q, np.float32)
+    B, D, V = q.shape
+    R = N_max + 1
+    st = np.zeros((B,), np.int32) if status is None else _c(status, np.int32).copy()
+    parents = np.zeros((B, R), np.int32)
+    tokens = np.zeros((B, R), np.int32)
+    n = np.zeros((B,), np.int32)
+    rho = np.zeros((B, R), np.float64)
+    c = None if cost is None else _c(cost, np.float64)
+    _check(_load().tmvref_tree_best_first(B, D, V, int(N_max), _p(q), _p(c), float(l_ar), _p(parents), _p(tokens),
+                                          _p(n), _p(rho), _p(st)))
+    return parents, tokens, n, rho, st

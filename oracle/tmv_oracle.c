@@ -550,3 +550,133 @@ int tmvref_commit(int n_layers, int B, int Hkv, int d, int L_cap, int M_max, int
     free(snap);
     return REF_OK;
 }
+
+/* ------------------------------------------------------------------------------------
+ * Best-first prefix tree from per-position draft marginals [BAS, sections 1-3]
+ * (BAS = the BASTION technical summary: block-diffusion marginals, path scores,
+ * best-first expansion, budget controller).
+ *   q[b][k][x] = q_{k+1}(x), the drafter's marginal for position k+1 (k = 0..D-1).
+ *   A node at depth d is a token tuple (x_1..x_d) with path score
+ *   rho = q_1(x_1) * ... * q_d(x_d) (section 1).  Best-first expansion adds, again and
+ *   again, the node with the largest score among those whose parent is already in the
+ *   tree (section 2).  The surrogate of a tree is the sum of its scores (section 2); the
+ *   controller keeps growing the tree while S(n) = A(n) * L_AR / C(n) rises (section 3).
+ * Readings (ours; the pages give no tie rule, arithmetic or cost model):
+ *   - rho in fp64, in depth order: rho(child) = rho(parent) * (double)q.
+ *   - ranks per position by (q descending, token ascending); equal scores go to the
+ *     shallower node, then to the lexicographically smaller rank tuple.  Only the N_max
+ *     best tokens of a position can enter a tree of N_max nodes (any other token is
+ *     beaten by N_max siblings), so candidates are drawn from those ranks.
+ *   - node ids in the order the nodes are added (1..n); parents in virtual-root form.
+ *   - controller: A(n) = sum of the first n scores, S(n) = A(n) * l_ar / cost[n-1]; the
+ *     tree keeps n* nodes, the smallest n with S(n+1) < S(n) (all of them if S never
+ *     falls).  Without a cost table n* = N_max.
+ *   - a q row with an entry outside [0,1] or NaN sets status INPUT.
+ * ---------------------------------------------------------------------------------- */
+typedef struct { float v; int32_t tok; } ref_rank;
+
+static int ref_rank_cmp(const void *a, const void *b)
+{
+    const ref_rank *x = (const ref_rank *)a, *y = (const ref_rank *)b;
+    if (x->v != y->v) return x->v > y->v ? -1 : 1;
+    return (x->tok > y->tok) - (x->tok < y->tok);
+}
+
+/* does node (depth da, ranks ra) come before node (db, rb) at equal score? */
+static int ref_tuple_before(int da, const int *ra, int db, const int *rb)
+{
+    if (da != db) return da < db;
+    for (int k = 0; k < da; ++k)
+        if (ra[k] != rb[k]) return ra[k] < rb[k];
+    return 0;
+}
+
+int tmvref_tree_best_first(int B, int D, int V, int N_max, const float *q, const double *cost, double l_ar,
+                           int32_t *parents, int32_t *tokens, int32_t *n_nodes, double *rho, int32_t *status)
+{
+    if (B < 0 || D < 1 || D > 8 || V < 1 || N_max < 1 || N_max > 128) return REF_ERR_ARG;
+    const int R = N_max + 1;
+    const int K = V < N_max ? V : N_max;            /* ranks per position */
+    ref_rank *row = (ref_rank *)malloc(sizeof(ref_rank) * (size_t)V);
+    int32_t *rtok = (int32_t *)malloc(sizeof(int32_t) * (size_t)D * K);
+    float *rq = (float *)malloc(sizeof(float) * (size_t)D * K);
+    if (!row || !rtok || !rq) { free(row); free(rtok); free(rq); return REF_ERR_ARG; }
+    int depth[129], ranks[129][8];
+    double sc[129];
+    unsigned char child_in[129][128];
+
+    for (int b = 0; b < B; ++b) {
+        for (int j = 0; j < R; ++j) {
+            parents[(int64_t)b * R + j] = 0;
+            tokens[(int64_t)b * R + j] = 0;
+            rho[(int64_t)b * R + j] = j == 0 ? 1.0 : 0.0;
+        }
+        n_nodes[b] = 0;
+        if (status[b] != REF_OK) continue;
+        int bad = 0;
+        for (int k = 0; k < D && !bad; ++k) {
+            const float *qr = q + ((int64_t)b * D + k) * V;
+            for (int x = 0; x < V; ++x) {
+                if (!(qr[x] >= 0.0f && qr[x] <= 1.0f)) { bad = 1; break; }
+                row[x].v = qr[x];
+                row[x].tok = x;
+            }
+            if (bad) break;
+            qsort(row, (size_t)V, sizeof(ref_rank), ref_rank_cmp);
+            for (int r = 0; r < K; ++r) { rtok[k * K + r] = row[r].tok; rq[k * K + r] = row[r].v; }
+        }
+        if (bad) { status[b] = REF_ERR_INPUT; continue; }
+
+        /* best-first: node 0 is the root (depth 0, score 1) */
+        depth[0] = 0;
+        sc[0] = 1.0;
+        memset(child_in, 0, sizeof(child_in));
+        int n = 0;
+        while (n < N_max) {
+            int bp = -1, br = -1, bd = 0, bt[8] = {0};
+            double bs = 0.0;
+            for (int p = 0; p <= n; ++p) {
+                if (depth[p] >= D) continue;
+                for (int r = 0; r < K; ++r) {
+                    if (child_in[p][r]) continue;
+                    const double s = sc[p] * (double)rq[depth[p] * K + r];
+                    int t[8];
+                    for (int k = 0; k < depth[p]; ++k) t[k] = ranks[p][k];
+                    t[depth[p]] = r;
+                    const int d = depth[p] + 1;
+                    if (bp < 0 || s > bs || (s == bs && ref_tuple_before(d, t, bd, bt))) {
+                        bp = p; br = r; bs = s; bd = d;
+                        for (int k = 0; k < d; ++k) bt[k] = t[k];
+                    }
+                }
+            }
+            if (bp < 0) break;                      /* every possible node is in the tree */
+            ++n;
+            depth[n] = bd;
+            for (int k = 0; k < bd; ++k) ranks[n][k] = bt[k];
+            sc[n] = bs;
+            child_in[bp][br] = 1;
+            parents[(int64_t)b * R + n] = bp;
+            tokens[(int64_t)b * R + n] = rtok[(bd - 1) * K + br];
+            rho[(int64_t)b * R + n] = bs;
+        }
+        int keep = n;
+        if (cost) {
+            double A = 0.0, s_prev = 0.0;
+            for (int m = 1; m <= n; ++m) {
+                A += rho[(int64_t)b * R + m];
+                const double s = A * l_ar / cost[m - 1];
+                if (m > 1 && s < s_prev) { keep = m - 1; break; }
+                s_prev = s;
+            }
+        }
+        for (int j = keep + 1; j < R; ++j) {
+            parents[(int64_t)b * R + j] = 0;
+            tokens[(int64_t)b * R + j] = 0;
+            rho[(int64_t)b * R + j] = 0.0;
+        }
+        n_nodes[b] = keep;
+    }
+    free(row); free(rtok); free(rq);
+    return REF_OK;
+}

@@ -234,6 +234,43 @@ int tmv_kv_commit_path(int dtype, int n_layers, int B, int Hkv, int d, int L_cap
                        const int32_t *accept_len, const int32_t *path,
                        int32_t *status, int32_t *new_len, void *stream);
 
+/*
+ * tmv_tree_best_first -- a best-first prefix tree from per-position draft marginals, and
+ * the hardware-aware budget controller that chooses its size.
+ * Defined by sections 1-3 of the BASTION technical summary:
+ *   - a block-diffusion drafter gives one marginal q_k per future position;
+ *   - a node at depth d (tokens x_1..x_d) has path score rho = q_1(x_1) * ... * q_d(x_d);
+ *   - best-first expansion repeatedly adds the highest-scoring node whose parent is in the
+ *     tree, which is optimal for the surrogate A(T) = sum of its scores;
+ *   - the controller keeps growing the tree while S(n) = A(n) * L_AR / C(n) rises.
+ * Readings:
+ *   - rho is an fp64 product in depth order.
+ *   - Equal scores go to the shallower node, then to the smaller rank tuple, with ranks per
+ *     position by (q descending, token ascending).
+ *   - Nodes are numbered in the order they are added.
+ *   - The tree keeps the smallest n with S(n+1) < S(n), or every node if S never falls.
+ *   q          f32 [B][D][V] rows at q + b*q_stride_b + k*q_stride_k (elements),
+ *              vocabulary contiguous; row k is the marginal of position k+1.
+ *   N_max      budget, 1..128.  D in 1..8, V in 1..262144.
+ *   cost       f64 [N_max] device array, cost[n-1] = C(n), the caller's measured cost of
+ *              verifying an n-node tree (for example µs per verify step); NULL keeps N_max
+ *              nodes.  l_ar = L_AR (cost units per autoregressive token).
+ *   parents    out int32 [B][N_max+1], virtual-root form (parents[b][i] < i, column 0 = 0);
+ *   tokens     out int32 [B][N_max+1] (column 0 = 0);
+ *   n_nodes    out int32 [B];
+ *   rho        out f64 [B][N_max+1] (rho[b][0] = 1).  Entries past n_nodes are 0.
+ *   status     in/out int32 [B]: a sequence whose status is not OK is skipped (n_nodes 0);
+ *              a q row with an entry outside [0,1] or NaN sets TMV_ERR_INPUT.
+ *   workspace: tmv_tree_best_first_workspace() bytes, 16-byte aligned, no initialisation.
+ * Together, parents, n_nodes and tokens are the input of tmv_tree_build_ancestors
+ * (TMV_PARENTS_VROOT, M_max = N_max) and of the verify step.
+ */
+size_t tmv_tree_best_first_workspace(int B, int D, int V, int N_max);
+int tmv_tree_best_first(int B, int D, int V, int N_max, const float *q, int64_t q_stride_b,
+                        int64_t q_stride_k, const double *cost, double l_ar, int32_t *parents,
+                        int32_t *tokens, int32_t *n_nodes, double *rho, int32_t *status,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

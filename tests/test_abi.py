@@ -77,6 +77,15 @@ def test_argument_checks_return_before_launch():
              9 * ((1 << 24) + 1), (1 << 24) + 1, ctypes.c_uint64(1), ctypes.c_uint64(0), fake, fake, fake, fake, fake,
              fake, fake, fake, 1 << 20, None)
     assert lib.tmv_tree_accept(*big_v) == tmv.ERR_ARG                 # sampling vocabulary above 2^24
+    # best-first: depth, vocabulary and budget limits, workspace too small
+    bf = lambda D, V, N, wsb: (1, D, V, N, fake, 0, 0, None, ctypes.c_double(1.0), fake, fake, fake, fake, fake, fake,
+                                wsb, None)
+    assert lib.tmv_tree_best_first(*bf(0, 100, 8, 1 << 20)) == tmv.ERR_ARG
+    assert lib.tmv_tree_best_first(*bf(9, 100, 8, 1 << 20)) == tmv.ERR_ARG
+    assert lib.tmv_tree_best_first(*bf(4, 262145, 8, 1 << 30)) == tmv.ERR_ARG
+    assert lib.tmv_tree_best_first(*bf(4, 100, 129, 1 << 20)) == tmv.ERR_ARG
+    assert lib.tmv_tree_best_first(*bf(4, 100, 0, 1 << 20)) == tmv.ERR_ARG
+    assert lib.tmv_tree_best_first(*bf(4, 100, 8, 16)) == tmv.ERR_ARG
     # commit: row bytes not a multiple of 16 / too large, misaligned strides
     com = lambda dt, d, st: (dt, 2, 1, 8, d, 64, 8, 4, fake, fake, st, fake, fake, fake, fake, fake, fake, None)
     assert lib.tmv_kv_commit_path(*com(tmv.BF16, 4, s4)) == tmv.ERR_ARG

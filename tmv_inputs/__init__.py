@@ -138,6 +138,15 @@ def tree_best_first(marginals_sorted: np.ndarray, budget: int):
     return parents, order
 
 
+def draft_marginals(rng, B: int, D: int, V: int, sigma: float = 3.0, levels: int | None = None) -> np.ndarray:
+    """Per-position draft marginals of a block-diffusion drafter, float32 [B][D][V]:
+    softmax of N(0, sigma) logits per (sequence, position) -- workload 3's recipe.  With
+    `levels`, values are instead drawn from {0, 1/levels, ..., 1}, so many are equal."""
+    if levels:
+        return (rng.integers(0, levels + 1, size=(B, D, V)) / levels).astype(np.float32)
+    return _softmax_rows(rng.standard_normal(size=(B, D, V)) * sigma).astype(np.float32)
+
+
 def children_lists(parents: np.ndarray, M: int):
     kids = {u: [] for u in range(M + 1)}
     for i in range(1, M + 1):

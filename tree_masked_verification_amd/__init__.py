@@ -10,6 +10,9 @@ Stages of one verify step, in order:
   tree_verify_attention  tree-masked attention of all draft nodes
   tree_accept            greedy longest matching path, or modified rejection sampling
   kv_commit_path         prefix-sharing in-place compaction of the accepted K/V rows
+and, on the drafting side of a step:
+  tree_best_first        best-first prefix tree from per-position draft marginals, sized
+                         by the budget controller
 """
 from __future__ import annotations
 
@@ -46,10 +49,14 @@ _lib.tmv_tree_accept_workspace.restype = _SZ
 _lib.tmv_tree_accept.argtypes = [_I, _I, _I, _I, _I, _P, _I, _P, _I64, _I64, _P, _I64, _I64, _U64, _U64,
                                  _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
 _lib.tmv_kv_commit_path.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+_lib.tmv_tree_best_first_workspace.argtypes = [_I, _I, _I, _I]
+_lib.tmv_tree_best_first_workspace.restype = _SZ
+_lib.tmv_tree_best_first.argtypes = [_I, _I, _I, _I, _P, _I64, _I64, _P, ctypes.c_double, _P, _P, _P, _P, _P, _P,
+                                     _SZ, _P]
 
 EXPORTED = ("tmv_status_string", "tmv_abi_version", "tmv_tree_build_ancestors",
             "tmv_tree_verify_attention_workspace", "tmv_tree_verify_attention", "tmv_tree_accept_workspace",
-            "tmv_tree_accept", "tmv_kv_commit_path")
+            "tmv_tree_accept", "tmv_kv_commit_path", "tmv_tree_best_first_workspace", "tmv_tree_best_first")
 
 
 class TmvError(RuntimeError):
@@ -195,6 +202,36 @@ def kv_commit_path(k_cache, v_cache, prefix_len, n_nodes, accept_len, path, stat
                                    _ptr(n_nodes), _ptr(accept_len), _ptr(path), _ptr(status), _ptr(new_len),
                                    _stream(stream)),
            "kv_commit_path")
+
+
+# ------------------------------------------------------------------------ tree construction
+def tree_best_first_workspace(B, D, V, N_max) -> int:
+    return int(_lib.tmv_tree_best_first_workspace(B, D, V, N_max))
+
+
+def tree_best_first(q, N_max, parents, tokens, n_nodes, rho, status, cost=None, l_ar=1.0, workspace=None,
+                    stream=None):
+    """q float32 [B][D][V] (vocabulary contiguous); parents, tokens int32 [B][N_max+1], n_nodes
+    int32 [B], rho float64 [B][N_max+1] (outputs); status int32 [B] (in/out); cost float64
+    [N_max] device tensor or None."""
+    _i32(parents, tokens, n_nodes, status)
+    if q.dtype != torch.float32 or q.stride(2) != 1 or not q.is_cuda:
+        raise ValueError("q must be a float32 device tensor with a contiguous vocabulary")
+    if rho.dtype != torch.float64 or not rho.is_contiguous():
+        raise TypeError("rho must be contiguous float64")
+    if cost is not None and (cost.dtype != torch.float64 or not cost.is_contiguous() or cost.numel() < N_max):
+        raise ValueError("cost must be a contiguous float64 tensor of N_max entries")
+    B, D, V = q.shape
+    if tuple(parents.shape) != (B, N_max + 1) or tuple(tokens.shape) != (B, N_max + 1) or \
+            tuple(rho.shape) != (B, N_max + 1):
+        raise ValueError("outputs must be [B][N_max+1]")
+    if workspace is None:
+        workspace = torch.empty(tree_best_first_workspace(B, D, V, N_max), dtype=torch.uint8, device=q.device)
+    _check(_lib.tmv_tree_best_first(B, D, V, int(N_max), _ptr(q), q.stride(0), q.stride(1), _ptr(cost),
+                                    ctypes.c_double(l_ar), _ptr(parents), _ptr(tokens), _ptr(n_nodes), _ptr(rho),
+                                    _ptr(status), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(stream)),
+           "tree_best_first")
 
 
 class Workspaces:

@@ -1,0 +1,389 @@
+// best_first.hip -- best-first prefix trees from per-position draft marginals (gfx950).
+//
+// BASTION summary, sections 1-3: a block-diffusion drafter gives one marginal q_k per
+// future position; a node at depth d (tokens x_1..x_d) scores rho = q_1(x_1)...q_d(x_d);
+// best-first expansion adds, again and again, the highest-scoring node whose parent is in
+// the tree; a controller keeps growing the tree while S(n) = A(n) L_AR / C(n) rises, with
+// A(n) the sum of the first n scores.  Ties (our reading): the shallower node, then the
+// smaller rank tuple, ranks per position by (q descending, token ascending); scores are
+// fp64 products in depth order, so the result is exact and bit-identical to any correct
+// implementation.
+//
+// Three launches:
+//   1. every 16384-entry segment of every q row: its K best entries, K = min(V, N_max).
+//      Keys are (value bits << 32 | ~token), all distinct.  The K-th largest of the
+//      threads' maxima is a threshold below which no top-K entry lies, and at most K
+//      threads hold entries above it: at most 16 K candidates, sorted in LDS.
+//   2. every row: its segments' lists merged (sorted in LDS) into the row's ranks.
+//   3. every sequence, one wave: best-first over rank tuples.  A node's successors in the
+//      order are its next sibling and its first child, so a frontier of at most N + 1
+//      entries holds the next node at every step; it lives in registers, four slots per
+//      lane, and each step is one wave-wide argmax.
+#include "tmv_device.hpp"
+
+namespace {
+
+using tmv::kWave;
+
+constexpr int kBfMaxN = 128;                        // nodes per tree
+constexpr int kBfMaxD = 8;                          // positions (tree depth)
+constexpr int kSegThreads = 1024;
+constexpr int kSegPer = 16;                         // entries per thread of a segment
+constexpr int kSegLen = kSegThreads * kSegPer;      // entries per segment
+constexpr int kMaxSegs = 16;                        // segments per row: V <= 262144
+constexpr int kCand = kBfMaxN * kSegPer;            // candidates of a segment (at most)
+static_assert(kMaxSegs * kBfMaxN == kCand, "the row merge sorts as many keys as a segment");
+constexpr int kSlots = 4;                           // frontier slots per lane (4 * 64 >= kBfMaxN + 1)
+constexpr int kRankBits = 7;                        // rank < 128
+constexpr int kDepthShift = 56;                     // tuple key: depth << 56 | ranks, MSB first
+
+// larger key = earlier rank (value descending, token ascending); 0 = no entry
+__device__ __forceinline__ uint64_t rank_key(float v, int x) {
+    return (static_cast<uint64_t>(__float_as_uint(v)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(x));
+}
+
+// sort keys[0, n) in descending order (n a power of two); every thread of the block calls it
+__device__ void bitonic_desc(uint64_t *keys, int n) {
+    for (int k = 2; k <= n; k <<= 1)
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            __syncthreads();
+            for (int i = threadIdx.x; i < n; i += blockDim.x) {
+                const int l = i ^ j;
+                if (l > i) {
+                    const uint64_t a = keys[i], c = keys[l];
+                    if ((i & k) == 0 ? a < c : a > c) {
+                        keys[i] = c;
+                        keys[l] = a;
+                    }
+                }
+            }
+        }
+    __syncthreads();
+}
+
+// exclusive prefix sum over the block (kSegThreads threads); *total gets the sum
+__device__ int block_exclusive_scan(int v, int *wave_sums, int *total) {
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+    int incl = v;
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += y;
+    }
+    __syncthreads();
+    if (lane == kWave - 1) wave_sums[wv] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+    for (int w = 0; w < kSegThreads / kWave; ++w) {
+        if (w < wv) before += wave_sums[w];
+        all += wave_sums[w];
+    }
+    *total = all;
+    return before + incl - v;
+}
+
+__device__ __forceinline__ int pow2_at_least(int n) {
+    int p = 1;
+    while (p < n) p <<= 1;
+    return p;
+}
+
+// ---- 1. the K best entries of each segment of each q row
+__global__ void __launch_bounds__(kSegThreads)
+bf_segment_kernel(int D, int V, int K, int nseg, const float *__restrict__ q, int64_t qsb, int64_t qsk,
+                  uint64_t *__restrict__ seg_keys, int32_t *__restrict__ seg_bad)
+{
+    __shared__ uint64_t sh[kCand];
+    __shared__ int wave_sums[kSegThreads / kWave];
+    __shared__ int any_bad;
+    const int tid = threadIdx.x;
+    const int row = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+    const int b = row / D, k = row % D;
+    const float *qr = q + b * qsb + k * qsk;
+    const int x0 = seg * kSegLen;
+    if (tid == 0) any_bad = 0;
+
+    // this thread's entries x0 + e * kSegThreads + tid (each load instruction is coalesced)
+    uint64_t key[kSegPer];
+    uint64_t mx = 0;
+    bool bad = false;
+#pragma unroll
+    for (int e = 0; e < kSegPer; ++e) {
+        const int x = x0 + e * kSegThreads + tid;
+        key[e] = 0;
+        if (x < V) {
+            const float v = qr[x];
+            if (v >= 0.f && v <= 1.f) key[e] = rank_key(v, x);
+            else bad = true;                          // (also NaN)
+        }
+        mx = key[e] > mx ? key[e] : mx;
+    }
+    // the K-th largest thread maximum: no top-K entry lies below it
+    sh[tid] = mx;
+    bitonic_desc(sh, kSegThreads);
+    const uint64_t tau = sh[K - 1];
+    if (bad) any_bad = 1;
+    // candidates: entries >= tau (only the K threads whose maximum reaches tau hold any)
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < kSegPer; ++e) c += (key[e] != 0 && key[e] >= tau) ? 1 : 0;
+    int total = 0;
+    const int off = block_exclusive_scan(c, wave_sums, &total);   // (its barriers also end the reads of sh)
+    int o = off;
+#pragma unroll
+    for (int e = 0; e < kSegPer; ++e)
+        if (key[e] != 0 && key[e] >= tau && o < kCand) sh[o++] = key[e];
+    const int n = pow2_at_least(total > K ? total : K);
+    for (int i = total + tid; i < n; i += kSegThreads) sh[i] = 0;
+    bitonic_desc(sh, n);
+    uint64_t *out = seg_keys + (static_cast<int64_t>(row) * nseg + seg) * K;
+    for (int r = tid; r < K; r += kSegThreads) out[r] = sh[r];
+    if (tid == 0) seg_bad[static_cast<int64_t>(row) * nseg + seg] = any_bad;
+}
+
+// ---- 2. each row's ranks from its segments' lists
+__global__ void __launch_bounds__(kSegThreads)
+bf_row_kernel(int K, int nseg, const uint64_t *__restrict__ seg_keys, const int32_t *__restrict__ seg_bad,
+              int32_t *__restrict__ rank_tok, float *__restrict__ rank_val, int32_t *__restrict__ row_bad)
+{
+    __shared__ uint64_t sh[kCand];
+    const int tid = threadIdx.x, row = blockIdx.x;
+    const int m = nseg * K;                           // <= kMaxSegs * kBfMaxN = kCand
+    const int n = pow2_at_least(m);
+    for (int i = tid; i < n; i += kSegThreads) sh[i] = i < m ? seg_keys[static_cast<int64_t>(row) * m + i] : 0;
+    bitonic_desc(sh, n);
+    for (int r = tid; r < K; r += kSegThreads) {
+        const uint64_t key = sh[r];
+        rank_tok[static_cast<int64_t>(row) * K + r] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+        rank_val[static_cast<int64_t>(row) * K + r] = __uint_as_float(static_cast<uint32_t>(key >> 32));
+    }
+    if (tid == 0) {
+        int bad = 0;
+        for (int s = 0; s < nseg; ++s) bad |= seg_bad[static_cast<int64_t>(row) * nseg + s];
+        row_bad[row] = bad;
+    }
+}
+
+// ---- 3. best-first expansion and the budget controller, one wave per sequence
+struct Entry {
+    double rho;       // the node's score
+    double prho;      // its parent's score (a sibling's score is prho * q)
+    uint64_t key;     // depth << 56 | ranks (position 0 in the top 7 bits below the depth)
+    int par;          // parent id
+    int live;
+};
+
+// does a come before b (score descending, then depth and rank tuple ascending)?
+__device__ __forceinline__ bool before(double ra, uint64_t ka, double rb, uint64_t kb) {
+    return ra > rb || (ra == rb && ka < kb);
+}
+
+__global__ void __launch_bounds__(kWave)
+bf_expand_kernel(int D, int K, int N_max, const int32_t *__restrict__ rank_tok, const float *__restrict__ rank_val,
+                 const int32_t *__restrict__ row_bad, const double *__restrict__ cost, double l_ar,
+                 int32_t *__restrict__ parents, int32_t *__restrict__ tokens, int32_t *__restrict__ n_nodes,
+                 double *__restrict__ rho, int32_t *__restrict__ status)
+{
+    __shared__ float rv[kBfMaxD][kBfMaxN];
+    __shared__ int32_t rt[kBfMaxD][kBfMaxN];
+    __shared__ int32_t out_par[kBfMaxN + 1], out_tok[kBfMaxN + 1];
+    __shared__ double out_rho[kBfMaxN + 1];
+    const int b = blockIdx.x, lane = threadIdx.x;
+    const int R = N_max + 1;
+    int32_t *pb = parents + static_cast<int64_t>(b) * R;
+    int32_t *tb = tokens + static_cast<int64_t>(b) * R;
+    double *rb = rho + static_cast<int64_t>(b) * R;
+
+    const int st = status[b];
+    int bad = 0;
+    for (int k = 0; k < D; ++k) bad |= row_bad[static_cast<int64_t>(b) * D + k];
+    if (st != TMV_OK || bad) {
+        for (int j = lane; j < R; j += kWave) {
+            pb[j] = 0;
+            tb[j] = 0;
+            rb[j] = j == 0 ? 1.0 : 0.0;
+        }
+        if (lane == 0) {
+            n_nodes[b] = 0;
+            if (st == TMV_OK) status[b] = TMV_ERR_INPUT;
+        }
+        return;
+    }
+    for (int i = lane; i < D * K; i += kWave) {
+        rv[i / K][i % K] = rank_val[static_cast<int64_t>(b) * D * K + i];
+        rt[i / K][i % K] = rank_tok[static_cast<int64_t>(b) * D * K + i];
+    }
+    __syncthreads();
+
+    // frontier slot s lives in lane s % 64, register s / 64; slot 0 starts as the best
+    // child of the root
+    Entry f[kSlots];
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j) f[j].live = 0;
+    if (lane == 0) {
+        f[0].rho = static_cast<double>(rv[0][0]);
+        f[0].prho = 1.0;
+        f[0].key = 1ull << kDepthShift;
+        f[0].par = 0;
+        f[0].live = 1;
+    }
+    int used = 1;                                    // slots handed out so far (wave-uniform)
+    int n = 0;
+    while (n < N_max) {
+        // wave-wide argmax over the live slots
+        double br = -1.0;
+        uint64_t bk = ~0ull;
+        int bs = -1;
+#pragma unroll
+        for (int j = 0; j < kSlots; ++j)
+            if (f[j].live && (bs < 0 || before(f[j].rho, f[j].key, br, bk))) {
+                br = f[j].rho;
+                bk = f[j].key;
+                bs = j * kWave + lane;
+            }
+        for (int o = 32; o > 0; o >>= 1) {
+            const double orr = __shfl_xor(br, o, kWave);
+            const uint64_t ok = tmv::shfl_xor_u64(bk, o);
+            const int os = __shfl_xor(bs, o, kWave);
+            if (os >= 0 && (bs < 0 || before(orr, ok, br, bk))) {
+                br = orr;
+                bk = ok;
+                bs = os;
+            }
+        }
+        if (bs < 0) break;                           // every possible node is in the tree
+        // the popped entry, known to every lane
+        const int owner = bs % kWave, js = bs / kWave;
+        double prho = 0.0;
+        int par = 0;
+#pragma unroll
+        for (int j = 0; j < kSlots; ++j)
+            if (j == js) {
+                prho = f[j].prho;
+                par = f[j].par;
+            }
+        prho = __shfl(prho, owner, kWave);
+        par = __shfl(par, owner, kWave);
+        ++n;
+        const int d = static_cast<int>(bk >> kDepthShift);
+        const int sh_r = kDepthShift - kRankBits * d;    // bit offset of the last position's rank
+        const int r = static_cast<int>((bk >> sh_r) & ((1u << kRankBits) - 1));
+        if (lane == 0) {
+            out_par[n] = par;
+            out_tok[n] = rt[d - 1][r];
+            out_rho[n] = br;
+        }
+        // successors: the next sibling (same parent, next rank) and the first child
+        const bool has_sib = r + 1 < K, has_child = d < D;
+        Entry sib, child;
+        sib.rho = prho * static_cast<double>(rv[d - 1][has_sib ? r + 1 : r]);
+        sib.prho = prho;
+        sib.key = bk + (1ull << sh_r);
+        sib.par = par;
+        sib.live = 1;
+        child.rho = br * static_cast<double>(rv[has_child ? d : 0][0]);
+        child.prho = br;
+        child.key = (static_cast<uint64_t>(d + 1) << kDepthShift) | (bk & ((1ull << kDepthShift) - 1));
+        child.par = n;
+        child.live = 1;
+        // the popped slot takes the sibling (else the child, else it dies); a child next to
+        // a sibling takes a new slot
+        const int new_slot = used;
+        const bool use_new = has_sib && has_child;
+        if (use_new) ++used;
+#pragma unroll
+        for (int j = 0; j < kSlots; ++j) {
+            if (lane == owner && j == js) {
+                if (has_sib) f[j] = sib;
+                else if (has_child) f[j] = child;
+                else f[j].live = 0;
+            }
+            if (use_new && lane == new_slot % kWave && j == new_slot / kWave) f[j] = child;
+        }
+    }
+    __syncthreads();
+
+    // the controller: the first n whose successor lowers S(n) = A(n) L_AR / C(n)
+    int keep = n;
+    if (cost != nullptr && lane == 0) {
+        double a = 0.0, s_prev = 0.0;
+        for (int m = 1; m <= n; ++m) {
+            a += out_rho[m];
+            const double s = a * l_ar / cost[m - 1];
+            if (m > 1 && s < s_prev) {
+                keep = m - 1;
+                break;
+            }
+            s_prev = s;
+        }
+    }
+    keep = __shfl(keep, 0, kWave);
+    for (int j = lane; j < R; j += kWave) {
+        const bool in = j >= 1 && j <= keep;
+        pb[j] = in ? out_par[j] : 0;
+        tb[j] = in ? out_tok[j] : 0;
+        rb[j] = j == 0 ? 1.0 : in ? out_rho[j] : 0.0;
+    }
+    if (lane == 0) n_nodes[b] = keep;
+}
+
+// workspace: seg_keys [rows][nseg][K] u64 | seg_bad [rows][nseg] | rank_tok [rows][K] |
+// rank_val [rows][K] f32 | row_bad [rows]
+struct BfLayout {
+    size_t seg_keys, seg_bad, rank_tok, rank_val, row_bad, total;
+};
+
+size_t bf_align(size_t x) { return (x + 255) / 256 * 256; }
+
+BfLayout bf_layout(int B, int D, int V, int N_max) {
+    const size_t rows = static_cast<size_t>(B) * D;
+    const size_t K = static_cast<size_t>(V < N_max ? V : N_max);
+    const size_t nseg = (static_cast<size_t>(V) + kSegLen - 1) / kSegLen;
+    BfLayout l;
+    l.seg_keys = 0;
+    l.seg_bad = l.seg_keys + bf_align(rows * nseg * K * sizeof(uint64_t));
+    l.rank_tok = l.seg_bad + bf_align(rows * nseg * sizeof(int32_t));
+    l.rank_val = l.rank_tok + bf_align(rows * K * sizeof(int32_t));
+    l.row_bad = l.rank_val + bf_align(rows * K * sizeof(float));
+    l.total = l.row_bad + bf_align(rows * sizeof(int32_t));
+    return l;
+}
+
+}  // namespace
+
+extern "C" size_t tmv_tree_best_first_workspace(int B, int D, int V, int N_max)
+{
+    if (B <= 0 || D <= 0 || V <= 0 || N_max <= 0) return 256;
+    return bf_layout(B, D, V, N_max).total;
+}
+
+extern "C" int tmv_tree_best_first(int B, int D, int V, int N_max, const float *q, int64_t q_stride_b,
+                                   int64_t q_stride_k, const double *cost, double l_ar, int32_t *parents,
+                                   int32_t *tokens, int32_t *n_nodes, double *rho, int32_t *status,
+                                   void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (B < 0 || D < 1 || D > kBfMaxD || V < 1 || V > kMaxSegs * kSegLen || N_max < 1 || N_max > kBfMaxN)
+        return TMV_ERR_ARG;
+    if (q_stride_b < 0 || q_stride_k < 0) return TMV_ERR_ARG;
+    if (B == 0) return TMV_OK;
+    if (!q || !parents || !tokens || !n_nodes || !rho || !status || !workspace) return TMV_ERR_ARG;
+    const BfLayout l = bf_layout(B, D, V, N_max);
+    if (workspace_bytes < l.total || (reinterpret_cast<uintptr_t>(workspace) & 15u) != 0) return TMV_ERR_ARG;
+    const int K = V < N_max ? V : N_max;
+    const int nseg = (V + kSegLen - 1) / kSegLen;
+    const int64_t rows = static_cast<int64_t>(B) * D;
+    if (rows * nseg > 0x7fffffff) return TMV_ERR_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    uint64_t *seg_keys = reinterpret_cast<uint64_t *>(ws + l.seg_keys);
+    int32_t *seg_bad = reinterpret_cast<int32_t *>(ws + l.seg_bad);
+    int32_t *rank_tok = reinterpret_cast<int32_t *>(ws + l.rank_tok);
+    float *rank_val = reinterpret_cast<float *>(ws + l.rank_val);
+    int32_t *row_bad = reinterpret_cast<int32_t *>(ws + l.row_bad);
+    hipLaunchKernelGGL(bf_segment_kernel, dim3(static_cast<unsigned>(rows * nseg)), dim3(kSegThreads), 0, s, D, V, K,
+                       nseg, q, q_stride_b, q_stride_k, seg_keys, seg_bad);
+    hipLaunchKernelGGL(bf_row_kernel, dim3(static_cast<unsigned>(rows)), dim3(kSegThreads), 0, s, K, nseg, seg_keys,
+                       seg_bad, rank_tok, rank_val, row_bad);
+    hipLaunchKernelGGL(bf_expand_kernel, dim3(B), dim3(kWave), 0, s, D, K, N_max, rank_tok, rank_val, row_bad, cost,
+                       l_ar, parents, tokens, n_nodes, rho, status);
+    return tmv_host::launch_status(hipGetLastError());
+}

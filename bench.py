@@ -22,6 +22,9 @@ Timed regions (both after --warmup untimed steps):
      rotating sets (device copies added until the stage's own inputs exceed the Infinity
      Cache 2.5 times), timed with HIP events recorded on the stream the kernels run on;
      the average launch duration feeds the roofline figures.
+  3. workload 3 only: device best-first tree construction at its drafter shape (16
+     sequences, 8 positions, vocabulary 128256, budget 128), reported as "drafting" beside
+     the step (it builds the trees a step verifies; it is not part of the step).
 The oracle (tests-only CPU implementation) is timed on a bounded sample of the default
 workload for the cpu_baseline field.
 
@@ -219,6 +222,49 @@ def cpu_baseline(w, budget_s):
 
 
 # ---------------------------------------------------------------- main
+def time_best_first(torch, tmv, ti, stream, B=16, D=8, V=128256, N=128):
+    """Device best-first tree construction (drafting side, not part of the verify step) at
+    workload 3's drafter shape: per-position marginals softmax(N(0,3)) over the vocabulary,
+    sets rotated past the Infinity Cache, one HIP graph of back-to-back launches timed with
+    HIP events on its capture stream."""
+    set_bytes = B * D * V * 4
+    n_sets = max(2, math.ceil(2.5 * MALL_BYTES / set_bytes))
+    rng = np.random.default_rng(3300)
+    qs = [torch.from_numpy(ti.draft_marginals(rng, B, D, V)).cuda() for _ in range(n_sets)]
+    parents = torch.zeros((B, N + 1), dtype=torch.int32, device="cuda")
+    tokens = torch.zeros_like(parents)
+    n_nodes = torch.zeros((B,), dtype=torch.int32, device="cuda")
+    rho = torch.zeros((B, N + 1), dtype=torch.float64, device="cuda")
+    status = torch.zeros((B,), dtype=torch.int32, device="cuda")
+    ws = torch.empty(tmv.tree_best_first_workspace(B, D, V, N), dtype=torch.uint8, device="cuda")
+    run = lambda q: tmv.tree_best_first(q, N, parents, tokens, n_nodes, rho, status, workspace=ws, stream=stream)
+    reps = 40
+    with torch.cuda.stream(stream):
+        for q in qs:
+            run(q)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for r in range(reps):
+                run(qs[r % n_sets])
+        g.replay()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        e1.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    if int(status.abs().sum()) != 0 or int(n_nodes.min()) != N:
+        raise RuntimeError("tree_best_first: unexpected status or size")
+    nb = set_bytes + B * (N + 1) * (4 + 4 + 8) + B * 4
+    gbs = nb / (us * 1e-6) / 1e9
+    del g
+    return {"tree_best_first": {"avg_us": round(us, 3), "bytes": int(nb), "GB/s": round(gbs, 1),
+                                "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                                "shape": "B%d positions %d vocab %d budget %d" % (B, D, V, N),
+                                "input_sets": n_sets}}
+
+
 def make_sets(c, ti, tmv, torch):
     """The rotating input sets of workload c (and the workspaces and caches they share)."""
     w0 = ti.workload(c)
@@ -385,6 +431,11 @@ def main():
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(name, c)}
 
     dominant = max((k for k in durations if k != "build"), key=lambda k: durations[k])
+    drafting = time_best_first(torch, tmv, ti, stream) if c == 3 else None
+    if drafting:
+        print("bench: tree_best_first %.2f us per launch (%s)" % (drafting["tree_best_first"]["avg_us"],
+                                                                   drafting["tree_best_first"]["shape"]),
+              file=sys.stderr, flush=True)
 
     if args.copy_probe:
         n = 256 << 20
@@ -413,6 +464,7 @@ def main():
         "roofline": roofline(dominant),
         "attention_roofline": roofline("attention") if "attention" in durations else None,
         "kernels": kernels,
+        "drafting": drafting,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -164,17 +164,77 @@ bf_row_kernel(int K, int nseg, const uint64_t *__restrict__ seg_keys, const int3
 }
 
 // ---- 3. best-first expansion and the budget controller, one wave per sequence
-struct Entry {
-    double rho;       // the node's score
-    double prho;      // its parent's score (a sibling's score is prho * q)
-    uint64_t key;     // depth << 56 | ranks (position 0 in the top 7 bits below the depth)
-    int par;          // parent id
-    int live;
-};
-
 // does a come before b (score descending, then depth and rank tuple ascending)?
 __device__ __forceinline__ bool before(double ra, uint64_t ka, double rb, uint64_t kb) {
     return ra > rb || (ra == rb && ka < kb);
+}
+
+// keep (r2, k2, s2) if it comes first (slot -1: no candidate; keys are distinct, so every
+// lane makes the same choice)
+__device__ __forceinline__ void take(double &r, uint64_t &k, int &s, double r2, uint64_t k2, int s2) {
+    const bool t = s2 >= 0 && (s < 0 || before(r2, k2, r, k));
+    r = t ? r2 : r;
+    k = t ? k2 : k;
+    s = t ? s2 : s;
+}
+
+__device__ __forceinline__ uint32_t lo32(uint64_t v) { return static_cast<uint32_t>(v); }
+__device__ __forceinline__ uint32_t hi32(uint64_t v) { return static_cast<uint32_t>(v >> 32); }
+__device__ __forceinline__ uint64_t join(uint32_t h, uint32_t l) { return (static_cast<uint64_t>(h) << 32) | l; }
+__device__ __forceinline__ uint64_t dbits(double d) { return static_cast<uint64_t>(__double_as_longlong(d)); }
+__device__ __forceinline__ double from_bits(uint64_t b) { return __longlong_as_double(static_cast<long long>(b)); }
+
+// combine with the lane that DPP control CTRL reads from (within rows of 16 lanes)
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), CTRL, 0xf, 0xf, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ void dpp_take(double &r, uint64_t &k, int &s) {
+    const uint64_t rb = dbits(r);
+    const double r2 = from_bits(join(dpp32<CTRL>(hi32(rb)), dpp32<CTRL>(lo32(rb))));
+    const uint64_t k2 = join(dpp32<CTRL>(hi32(k)), dpp32<CTRL>(lo32(k)));
+    const int s2 = static_cast<int>(dpp32<CTRL>(static_cast<uint32_t>(s)));
+    take(r, k, s, r2, k2, s2);
+}
+
+// combine the pairs of rows (16-lane swap) or of half-waves (32-lane swap): each swap hands
+// every lane the values of both members of its pair
+template <bool kHalves>
+__device__ __forceinline__ void swap_take(double &r, uint64_t &k, int &s) {
+    const uint64_t rb = dbits(r);
+    uint32_t a0, a1, b0, b1, c0, c1, d0, d1, e0, e1;
+    if constexpr (kHalves) {
+        const auto a = __builtin_amdgcn_permlane32_swap(lo32(rb), lo32(rb), false, false);
+        const auto b = __builtin_amdgcn_permlane32_swap(hi32(rb), hi32(rb), false, false);
+        const auto c = __builtin_amdgcn_permlane32_swap(lo32(k), lo32(k), false, false);
+        const auto d = __builtin_amdgcn_permlane32_swap(hi32(k), hi32(k), false, false);
+        const auto e = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(s), static_cast<uint32_t>(s), false, false);
+        a0 = a[0]; a1 = a[1]; b0 = b[0]; b1 = b[1]; c0 = c[0]; c1 = c[1]; d0 = d[0]; d1 = d[1]; e0 = e[0]; e1 = e[1];
+    } else {
+        const auto a = __builtin_amdgcn_permlane16_swap(lo32(rb), lo32(rb), false, false);
+        const auto b = __builtin_amdgcn_permlane16_swap(hi32(rb), hi32(rb), false, false);
+        const auto c = __builtin_amdgcn_permlane16_swap(lo32(k), lo32(k), false, false);
+        const auto d = __builtin_amdgcn_permlane16_swap(hi32(k), hi32(k), false, false);
+        const auto e = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(s), static_cast<uint32_t>(s), false, false);
+        a0 = a[0]; a1 = a[1]; b0 = b[0]; b1 = b[1]; c0 = c[0]; c1 = c[1]; d0 = d[0]; d1 = d[1]; e0 = e[0]; e1 = e[1];
+    }
+    r = from_bits(join(b0, a0));
+    k = join(d0, c0);
+    s = static_cast<int>(e0);
+    take(r, k, s, from_bits(join(b1, a1)), join(d1, c1), static_cast<int>(e1));
+}
+
+// the earliest candidate of the wave, in every lane: xor 1 and xor 2 (quad permutes),
+// quads (row half-mirror), half-rows (row mirror), rows, half-waves
+__device__ __forceinline__ void wave_take(double &r, uint64_t &k, int &s) {
+    dpp_take<0xB1>(r, k, s);        // quad_perm [1,0,3,2]
+    dpp_take<0x4E>(r, k, s);        // quad_perm [2,3,0,1]
+    dpp_take<0x141>(r, k, s);       // row_half_mirror
+    dpp_take<0x140>(r, k, s);       // row_mirror
+    swap_take<false>(r, k, s);
+    swap_take<true>(r, k, s);
 }
 
 __global__ void __launch_bounds__(kWave)
@@ -214,55 +274,47 @@ bf_expand_kernel(int D, int K, int N_max, const int32_t *__restrict__ rank_tok, 
     }
     __syncthreads();
 
-    // frontier slot s lives in lane s % 64, register s / 64; slot 0 starts as the best
-    // child of the root
-    Entry f[kSlots];
+    // frontier slot s lives in lane s % 64, register s / 64 (one array per field); slot 0
+    // starts as the best child of the root
+    double f_rho[kSlots], f_prho[kSlots];
+    uint64_t f_key[kSlots];
+    int f_par[kSlots];
+    bool f_live[kSlots];
 #pragma unroll
-    for (int j = 0; j < kSlots; ++j) f[j].live = 0;
-    if (lane == 0) {
-        f[0].rho = static_cast<double>(rv[0][0]);
-        f[0].prho = 1.0;
-        f[0].key = 1ull << kDepthShift;
-        f[0].par = 0;
-        f[0].live = 1;
+    for (int j = 0; j < kSlots; ++j) {
+        const bool first = lane == 0 && j == 0;
+        f_rho[j] = first ? static_cast<double>(rv[0][0]) : 0.0;
+        f_prho[j] = 1.0;
+        f_key[j] = 1ull << kDepthShift;
+        f_par[j] = 0;
+        f_live[j] = first;
     }
     int used = 1;                                    // slots handed out so far (wave-uniform)
     int n = 0;
     while (n < N_max) {
-        // wave-wide argmax over the live slots
-        double br = -1.0;
-        uint64_t bk = ~0ull;
+        // this lane's earliest live slot, then the wave's
+        double br = 0.0;
+        uint64_t bk = 0;
         int bs = -1;
 #pragma unroll
         for (int j = 0; j < kSlots; ++j)
-            if (f[j].live && (bs < 0 || before(f[j].rho, f[j].key, br, bk))) {
-                br = f[j].rho;
-                bk = f[j].key;
-                bs = j * kWave + lane;
-            }
-        for (int o = 32; o > 0; o >>= 1) {
-            const double orr = __shfl_xor(br, o, kWave);
-            const uint64_t ok = tmv::shfl_xor_u64(bk, o);
-            const int os = __shfl_xor(bs, o, kWave);
-            if (os >= 0 && (bs < 0 || before(orr, ok, br, bk))) {
-                br = orr;
-                bk = ok;
-                bs = os;
-            }
-        }
+            if (f_live[j]) take(br, bk, bs, f_rho[j], f_key[j], j * kWave + lane);
+        wave_take(br, bk, bs);
+        bs = __builtin_amdgcn_readfirstlane(bs);
         if (bs < 0) break;                           // every possible node is in the tree
-        // the popped entry, known to every lane
         const int owner = bs % kWave, js = bs / kWave;
         double prho = 0.0;
         int par = 0;
 #pragma unroll
-        for (int j = 0; j < kSlots; ++j)
-            if (j == js) {
-                prho = f[j].prho;
-                par = f[j].par;
-            }
-        prho = __shfl(prho, owner, kWave);
-        par = __shfl(par, owner, kWave);
+        for (int j = 0; j < kSlots; ++j) {
+            prho = j == js ? f_prho[j] : prho;
+            par = j == js ? f_par[j] : par;
+        }
+        prho = from_bits(join(__builtin_amdgcn_readlane(hi32(dbits(prho)), owner),
+                              __builtin_amdgcn_readlane(lo32(dbits(prho)), owner)));
+        par = __builtin_amdgcn_readlane(par, owner);
+        br = from_bits(join(__builtin_amdgcn_readfirstlane(hi32(dbits(br))), __builtin_amdgcn_readfirstlane(lo32(dbits(br)))));
+        bk = join(__builtin_amdgcn_readfirstlane(hi32(bk)), __builtin_amdgcn_readfirstlane(lo32(bk)));
         ++n;
         const int d = static_cast<int>(bk >> kDepthShift);
         const int sh_r = kDepthShift - kRankBits * d;    // bit offset of the last position's rank
@@ -274,17 +326,10 @@ bf_expand_kernel(int D, int K, int N_max, const int32_t *__restrict__ rank_tok, 
         }
         // successors: the next sibling (same parent, next rank) and the first child
         const bool has_sib = r + 1 < K, has_child = d < D;
-        Entry sib, child;
-        sib.rho = prho * static_cast<double>(rv[d - 1][has_sib ? r + 1 : r]);
-        sib.prho = prho;
-        sib.key = bk + (1ull << sh_r);
-        sib.par = par;
-        sib.live = 1;
-        child.rho = br * static_cast<double>(rv[has_child ? d : 0][0]);
-        child.prho = br;
-        child.key = (static_cast<uint64_t>(d + 1) << kDepthShift) | (bk & ((1ull << kDepthShift) - 1));
-        child.par = n;
-        child.live = 1;
+        const double sib_rho = prho * static_cast<double>(rv[d - 1][has_sib ? r + 1 : r]);
+        const uint64_t sib_key = bk + (1ull << sh_r);
+        const double child_rho = br * static_cast<double>(rv[has_child ? d : 0][0]);
+        const uint64_t child_key = (static_cast<uint64_t>(d + 1) << kDepthShift) | (bk & ((1ull << kDepthShift) - 1));
         // the popped slot takes the sibling (else the child, else it dies); a child next to
         // a sibling takes a new slot
         const int new_slot = used;
@@ -292,12 +337,15 @@ bf_expand_kernel(int D, int K, int N_max, const int32_t *__restrict__ rank_tok, 
         if (use_new) ++used;
 #pragma unroll
         for (int j = 0; j < kSlots; ++j) {
-            if (lane == owner && j == js) {
-                if (has_sib) f[j] = sib;
-                else if (has_child) f[j] = child;
-                else f[j].live = 0;
-            }
-            if (use_new && lane == new_slot % kWave && j == new_slot / kWave) f[j] = child;
+            const bool here = lane == owner && j == js;
+            const bool fresh = use_new && lane == new_slot % kWave && j == new_slot / kWave;
+            const bool to_sib = here && has_sib;
+            const bool to_child = fresh || (here && !has_sib && has_child);
+            f_rho[j] = to_sib ? sib_rho : to_child ? child_rho : f_rho[j];
+            f_prho[j] = to_sib ? prho : to_child ? br : f_prho[j];
+            f_key[j] = to_sib ? sib_key : to_child ? child_key : f_key[j];
+            f_par[j] = to_sib ? par : to_child ? n : f_par[j];
+            f_live[j] = (to_sib || to_child) ? true : (here ? false : f_live[j]);
         }
     }
     __syncthreads();

@@ -267,12 +267,17 @@ def time_best_first(torch, tmv, ti, stream, B=16, D=8, V=128256, N=128):
 
 def make_sets(c, ti, tmv, torch):
     """The rotating input sets of workload c (and the workspaces and caches they share)."""
-    w0 = ti.workload(c)
+    return make_sets_from(ti.workload(c), lambda i: ti.workload(c, seed=20000 + 100 * c + i), c, tmv, torch)
+
+
+def make_sets_from(w0, gen, c, tmv, torch, quiet=False, max_gen=64):
+    """Rotating input sets: w0 and gen(1), gen(2), ... (same shape, at most max_gen
+    generated), then device copies."""
     per_set = set_bytes(w0)
     if c == 5:
         n_sets = 1                                           # p and q: 1.08 GB per set
     else:
-        n_sets = min(64, max(2 if per_set > MALL_BYTES else 16, math.ceil(2.5 * MALL_BYTES / per_set)))
+        n_sets = min(max_gen, max(2 if per_set > MALL_BYTES else 16, math.ceil(2.5 * MALL_BYTES / per_set)))
     dt = tmv.BF16 if w0.dtype == 1 else tmv.F32
     ws_attn = None
     if w0.mode == "greedy":
@@ -288,7 +293,7 @@ def make_sets(c, ti, tmv, torch):
                   torch.ones(shape, dtype=torch.bfloat16, device="cuda"))
     sets = [StepSet(tmv, torch, w0, ws_attn, ws_acc, caches)]
     for i in range(1, n_sets):
-        sets.append(StepSet(tmv, torch, ti.workload(c, seed=20000 + 100 * c + i), ws_attn, ws_acc, caches))
+        sets.append(StepSet(tmv, torch, gen(i), ws_attn, ws_acc, caches))
     # a stage timed alone must also rotate its own inputs through more than the Infinity
     # Cache holds: add device copies of the generated sets (the same values at new
     # addresses) until the smallest stage's inputs do
@@ -298,15 +303,97 @@ def make_sets(c, ti, tmv, torch):
         n_total = min(96, max(n_sets, math.ceil(2.5 * MALL_BYTES / stage_bytes)))
         for i in range(n_sets, n_total):
             sets.append(sets[i % n_gen].clone())
-    print("bench: workload %d, %d input set(s) of %.1f MB (%d generated, %.0f MB total)"
-          % (c, len(sets), per_set / 1e6, n_gen, len(sets) * per_set / 1e6), file=sys.stderr, flush=True)
+    if not quiet:
+        print("bench: workload %d, %d input set(s) of %.1f MB (%d generated, %.0f MB total)"
+              % (c, len(sets), per_set / 1e6, n_gen, len(sets) * per_set / 1e6), file=sys.stderr, flush=True)
     return w0, sets
+
+
+def time_steps(sets, steps, warmup, torch):
+    """us per verify step: graph replays of a step on every set in turn (as in the main loop)."""
+    n_sets = len(sets)
+    for i in range(max(min(warmup, 4 * n_sets), n_sets)):
+        sets[i % n_sets].step()
+    torch.cuda.synchronize()
+    st = torch.stack([s.status for s in sets]).cpu()
+    if int(st.abs().sum()) != 0:
+        raise RuntimeError("a verify step reported a non-OK status")
+    stream = torch.cuda.Stream()
+    reps, rem = divmod(steps, n_sets)
+    with torch.cuda.stream(stream):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for s in sets:
+                s.step()
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, reps)):
+            g.replay()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) / (max(1, reps) * n_sets) * 1e6
+    del g
+    return us
+
+
+def stage_durations(sets, stream, reps, torch):
+    """us per launch of each stage: one HIP graph of `reps` back-to-back launches over the
+    rotating sets per stage, replayed on its capture stream and timed with HIP events
+    recorded on that stream (the kernels' own stream)."""
+    durations = {}
+    with torch.cuda.stream(stream):
+        for name in sets[0].stages():
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for r in range(reps):
+                    sets[r % len(sets)].stages()[name]()
+            g.replay()                      # warm
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            e1.synchronize()
+            durations[name] = e0.elapsed_time(e1) * 1e3 / reps      # us per launch
+            del g
+    torch.cuda.synchronize()
+    return durations
+
+
+def budget_sweep(args, ti, tmv, torch):
+    """Verify-step cost over tree size M and depth limit D_max on workload 2's layer (the
+    pages' budget sweet-spot experiment, without a model): the cost table C(N) that the
+    best-first budget controller takes."""
+    out = []
+    for M in (8, 16, 32, 64, 96, 128):
+        for D in (2, 4, 8, 16):
+            w0, sets = make_sets_from(ti.budget_workload(M, D, 50000 + 97 * M + D),
+                                      lambda i: ti.budget_workload(M, D, 50000 + 97 * M + D + 7919 * i), 2, tmv, torch,
+                                      quiet=True, max_gen=6)
+            us = time_steps(sets, args.steps if args.steps is not None else 600, args.warmup, torch)
+            stages = stage_durations(sets, torch.cuda.Stream(), 200, torch)
+            depth = int(max(np.max(s.depth.cpu().numpy()) for s in sets[:4]))
+            out.append({"M": M, "D_max": D, "depth": depth, "us_per_step": round(us, 2),
+                        "stage_us": {k: round(v, 2) for k, v in stages.items()}, "input_sets": len(sets)})
+            print("bench: sweep M=%d D_max=%d (deepest %d): %.2f us/step (%s)"
+                  % (M, D, depth, us, ", ".join("%s %.2f" % kv for kv in stages.items())), file=sys.stderr, flush=True)
+            del sets
+            torch.cuda.empty_cache()
+    line = {"metric": "verify step us by tree size and depth (budget sweep)", "unit": "us/step", "n_gpus": 1,
+            "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "llama3-8b-layer bf16 B1 H32/8 d128 P2048 V128256, random trees (M nodes, depth "
+                                   "<= D_max), greedy"},
+            "sweep": out}
+    print(json.dumps(line), flush=True)
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the step line: verify-step cost over tree size and depth (one JSON line)")
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default 2000; 200 for workloads 3-5)")
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
@@ -327,6 +414,9 @@ def main():
     import tree_masked_verification_amd as tmv
 
     torch.cuda.init()
+    if args.sweep:
+        budget_sweep(args, ti, tmv, torch)
+        return
     w0, sets = make_sets(c, ti, tmv, torch)
     n_sets = len(sets)
     torch.cuda.synchronize()
@@ -382,24 +472,7 @@ def main():
     # ---- timed region 2: per-stage launch durations.  For each stage, one HIP graph of
     # back-to-back launches over the rotating sets, replayed on its capture stream and timed
     # with HIP events recorded on that stream (the kernels' own stream).
-    reps = 40 if big else 400
-    durations = {}
-    with torch.cuda.stream(stream):
-        for name in sets[0].stages():
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                for r in range(reps):
-                    sets[r % n_sets].stages()[name]()
-            g.replay()                      # warm
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
-            e1.synchronize()
-            durations[name] = e0.elapsed_time(e1) * 1e3 / reps      # us per launch
-            del g
-    torch.cuda.synchronize()
+    durations = stage_durations(sets, stream, 40 if big else 400, torch)
 
     # ---- algorithmic work per launch (averaged over the input sets)
     works = [workload_work(s.w, s.depth.cpu().numpy(), s.accept_len.cpu().numpy()) for s in sets]

@@ -46,3 +46,18 @@ def test_attention_work_matches_direct_count():
     # QK^T and PV over visible keys only: each (node, head) sees 2048 + depth keys
     assert flops == sum(4 * 128 * 32 * (2048 + d) for d in depths)
     assert sum(depths) == 242
+
+
+def test_budget_sweep_inputs():
+    """The sweep's trees hold M nodes no deeper than D_max, the cache has room for the
+    prefix and every tree slot, and the greedy rows are the layer's vocabulary."""
+    for M, D in ((8, 2), (64, 16), (128, 4)):
+        w = ti.budget_workload(M, D, 7)
+        par = w.parents[0]
+        assert par.shape == (M + 1,) and np.all(par[1:] < np.arange(1, M + 1))
+        depth = np.zeros(M + 1, np.int64)
+        for i in range(1, M + 1):
+            depth[i] = depth[par[i]] + 1
+        assert depth.max() <= D and w.D_max == D
+        assert w.L_cap >= w.prefix[0] + M and w.logits.shape == (1, M + 1, 128256)
+        assert (w.B, w.Hq, w.Hkv, w.d, w.mode) == (1, 32, 8, 128, "greedy")

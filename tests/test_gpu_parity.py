@@ -226,6 +226,23 @@ def test_workspace_reuse_across_calls_and_shapes():
         assert np.array_equal(host_bits(ds.out), s1)
 
 
+def test_attention_after_kernels_of_odd_grid_sizes(ref):
+    """The hardware deals a launch's workgroups to the XCDs round-robin, starting where the
+    previous launch stopped, so the XCD of a split-KV row block's splits depends on what ran
+    before.  After kernels of assorted grid sizes the rows must stay bit-identical."""
+    _case("attention: 8B-shaped layer after kernels of odd grid sizes")
+    w = ti.workload(2)
+    dev = _attention_parity(ref, w, 2e-2, 1e-2)
+    first = host_bits(dev.out).copy()
+    scratch = torch.empty(1 << 20, device="cuda")
+    for n in (1, 3, 70001, 5, 123457, 7, 9000, 333333):
+        dev.out.fill_(float("nan"))
+        scratch[:n].fill_(1.0)
+        dev.attention()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(dev.out), first), n
+
+
 @pytest.mark.parametrize("plan", ["1:1", "1:3", "2:1", "2:4", "2:8", "4:1", "4:6"])
 def test_attention_launch_plans(ref, plan, monkeypatch):
     # every launch plan (row-group width : token splits) must give the same rows: the

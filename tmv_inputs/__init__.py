@@ -244,6 +244,21 @@ def _softmax_rows(z):
     return e / e.sum(axis=-1, keepdims=True)
 
 
+def budget_workload(M: int, D_max: int, seed: int, alpha: float = 0.7) -> Workload:
+    """Workload 2's layer (bf16, 32/8 heads, d128, prefix 2048, vocabulary 128256, greedy)
+    with a random tree of M nodes and depth at most D_max (tree_random): the inputs of the
+    verify-cost sweep over tree size and depth."""
+    rng = np.random.default_rng(seed)
+    parents = tree_random(rng, M, D_max)
+    P = 2048
+    L_cap = P + (M + 63) // 64 * 64
+    q, k, v = _attention_tensors(rng, 1, 32, 8, 128, M, L_cap, 0.5, BF16)
+    logits, tokens = _greedy_rows(rng, [parents], [M], M, 128256, 2.0, alpha)
+    return Workload("budget-sweep bf16 B1 H32/8 d128 P2048 M%d D%d V128256" % (M, D_max), BF16, 1, 32, 8, 128, M,
+                    D_max, L_cap, 128256, "greedy", _pad_parents([parents], M), np.array([M], np.int32),
+                    np.array([P], np.int32), tokens, q, k, v, logits)
+
+
 def workload(c: int, seed: int | None = None, *, alpha: float = 0.7, with_rows: bool = True) -> Workload:
     """Workload number c (1..5).  `seed` overrides the default stream 1000 + c (used to
     make many distinct input sets of the same shape)."""

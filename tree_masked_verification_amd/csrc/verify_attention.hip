@@ -55,7 +55,9 @@ constexpr int kVmcntRound() {
 }
 constexpr int kVmcntZero = kVmcntRound<0>();
 // s_getreg operand for bits 3:0 of HW_REG_XCC_ID (register 20): the XCD running the wave
-constexpr int kHwRegXccId = 20 | (0 << 6) | (3 << 11);
+// buffer cache policy sc1: agent-scope coherent access (the form of a relaxed agent-scope
+// atomic load or store): stores write through to memory, loads are not served stale lines
+constexpr int kCoherent = 16;
 // s_waitcnt immediate that waits for LDS / scalar-memory count 0 only
 constexpr int kLgkmcntZero = 0xF | (0x7 << 4) | (0x3 << 14);
 
@@ -139,7 +141,6 @@ __device__ __forceinline__ void lds_zero16(uint32_t addr) {
     asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(z) : "memory");
 }
 // the XCD (accelerator complex die) this wave runs on
-__device__ __forceinline__ int xcc_id() { return __builtin_amdgcn_s_getreg(kHwRegXccId) & 0xf; }
 
 // buffer -> LDS copy of 16 bytes per lane: lane l's bytes land at lds + 16*l; a voffset
 // past the descriptor's records writes zeros and reads nothing
@@ -168,11 +169,35 @@ struct AttnPlan {
 constexpr int kMaxSplitUnits = 256;
 constexpr size_t kCounterBytes = kMaxSplitUnits * sizeof(int32_t);
 
+// An XCD's L2 (4 MB): a (sequence, kv head) pair's K and V rows up to this size stay in
+// L2 while the pair's row groups re-read them.
+constexpr long kL2Bytes = 4l << 20;
+
+// Launch plan.  d128 runs the LDS-ring kernel, whose ring takes 128 KB of a CU's 160 KB
+// LDS, so a CU holds one of its workgroups at a time: a grid of more than 256 workgroups
+// runs in several rounds, and the plan keeps the grid at one round where it can.
+//   * row-group width: 32-row groups when the 32-row blocks of an XCD's pairs fit one
+//     round on its 32 CUs and a pair's K/V fit an L2 (the re-reads by each row group then come from L2); 128-row
+//     groups when a pair's K/V are larger than an L2 (re-reads would come from HBM, so
+//     the rows that share a chunk load are maximised); 64-row groups otherwise;
+//   * token splits: the most that keep the grid within one round (at least 1, at most
+//     16, and at least two chunks per wave in each split).
+// d64 runs the streaming kernel (no ring) with 128-row groups from 256 rows on and
+// enough splits to reach 256 workgroups.
 AttnPlan make_plan(int B, int M_max, int Hq, int Hkv, int L_cap, int d) {
     AttnPlan p;
     const int g = Hq / Hkv;
     const int rows = M_max * g;
-    p.wr = rows >= 256 ? 4 : 1;
+    // pairs per XCD: workgroup i runs on XCD i % 8 and the grid gives each XCD its own pairs
+    const long xcd_pairs = (static_cast<long>(B) * Hkv + tmv::kXcds - 1) / tmv::kXcds;
+    const long cus_per_xcd = 256 / tmv::kXcds;
+    if (d == 128) {
+        const long kv_pair = static_cast<long>(L_cap) * d * 2 * 2;
+        const long blocks32 = xcd_pairs * ((rows + kRowsPerWave - 1) / kRowsPerWave);
+        p.wr = kv_pair > kL2Bytes ? 4 : blocks32 <= cus_per_xcd ? 1 : 2;
+    } else {
+        p.wr = rows >= 256 ? 4 : 1;
+    }
     int forced_wr = 0, forced_s = 0;
     if (const char *e = std::getenv("TMV_ATTN_PLAN")) std::sscanf(e, "%d:%d", &forced_wr, &forced_s);
     if (forced_wr == 1 || forced_wr == 4 || (forced_wr == 2 && d == 128)) p.wr = forced_wr;
@@ -181,7 +206,9 @@ AttnPlan make_plan(int B, int M_max, int Hq, int Hkv, int L_cap, int d) {
     p.pairs = B * Hkv;
     const int wt = kWaves / p.wr;
     const long base = static_cast<long>(p.pairs) * p.nb;
-    int s = base > 0 ? static_cast<int>((256 + base - 1) / base) : 1;
+    int s = base <= 0 ? 1
+          : d == 128 ? static_cast<int>(cus_per_xcd / (xcd_pairs * p.nb))
+                     : static_cast<int>((256 + base - 1) / base);
     const int s_tok = L_cap / (wt * 2 * kChunk);          // >= 2 chunks per wave per split
     if (s > s_tok) s = s_tok;
     if (s > 16) s = 16;
@@ -304,8 +331,8 @@ tree_attn_merge_kernel(int M_max, int D_max, int Hq, int Hkv, int L_cap,
 
 // The merging workgroup of a split-KV row block (LDS-ring kernel): IPB items (row rr,
 // dims part*8 .. +8) per thread and batch.  Every split's (m, l) and O slice of the
-// batch's items are loaded at once, through the L2 (sc0: the partials were written by
-// other CUs of this XCD, so this CU's L1 must not serve them), then merged in split order.
+// batch's items are loaded at once with agent-coherent loads (the partials were written
+// by other workgroups, on any XCD, with agent-coherent stores), then merged in split order.
 template <int D, int RB, int IPB, int SMAX>
 __device__ __forceinline__ void merge_block(int64_t unit, int splits, int b, int kvh, int g, int row0_wg, int M_max,
                                             int L_cap, int M, int P, int st, const int32_t *__restrict__ depth,
@@ -330,9 +357,9 @@ __device__ __forceinline__ void merge_block(int64_t unit, int splits, int b, int
             for (int s2 = 0; s2 < SMAX; ++s2) {
                 if (s2 < splits && item < kItems) {
                     const int row = s2 * RB + rr;
-                    ml[k][s2] = __builtin_amdgcn_raw_buffer_load_b64(rst, row * 8, 0, 1);
-                    oa[k][s2] = __builtin_amdgcn_raw_buffer_load_b128(ro, (row * D + part * 8) * 4, 0, 1);
-                    ob[k][s2] = __builtin_amdgcn_raw_buffer_load_b128(ro, (row * D + part * 8 + 4) * 4, 0, 1);
+                    ml[k][s2] = __builtin_amdgcn_raw_buffer_load_b64(rst, row * 8, 0, kCoherent);
+                    oa[k][s2] = __builtin_amdgcn_raw_buffer_load_b128(ro, (row * D + part * 8) * 4, 0, kCoherent);
+                    ob[k][s2] = __builtin_amdgcn_raw_buffer_load_b128(ro, (row * D + part * 8 + 4) * 4, 0, kCoherent);
                 }
             }
         }
@@ -1221,27 +1248,28 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     for (int rt = 0; rt < 2; ++rt) mrow[rt] = mrow[rt] == -INFINITY ? -INFINITY : mrow[rt] * cs;
 
     // ---- split-KV completion: the last split of a row block to arrive merges the block.
-    // Every split of the block runs on this workgroup's XCD (blockIdx % 8, the dispatch
-    // order), whose L2 all of them write: a split's partial stores are complete once its
-    // vector-memory count drains, after which it counts itself in with a device-scope
-    // atomic; the last arrival then reads the partials past its L1.  A split that finds itself on
-    // another XCD releases its stores device-wide first and flags the counter, and a last
-    // arrival that sees the flag acquires device-wide before reading.
+    // Splits publish their partials with agent-coherent stores (sc1: written through to
+    // memory, as the compiler writes a relaxed agent-scope atomic store) and the merging
+    // workgroup reads them with agent-coherent loads, so the splits of a block may run on
+    // any XCDs: no L2 write-back or invalidation is needed.  A split's stores are complete
+    // once its vector-memory count drains, after which it counts itself in with a
+    // device-scope atomic; the last arrival clears the counter and merges.
+    // this launch's split partials: [pairs * nb units][splits][RB rows] (m, l) and O rows
+    const int64_t part_rows = static_cast<int64_t>(pairs) * nb * splits * RB;
+    const __amdgpu_buffer_rsrc_t part_o =
+        __builtin_amdgcn_make_buffer_rsrc(ws_o, 0, static_cast<int>(part_rows * D * 4), kBufferFlags);
+    const __amdgpu_buffer_rsrc_t part_ml =
+        __builtin_amdgcn_make_buffer_rsrc(ws_stats, 0, static_cast<int>(part_rows * 8), kBufferFlags);
     auto finish_split = [&]() {
         const int64_t unit = static_cast<int64_t>(pair) * nb + rbk;
         __builtin_amdgcn_s_waitcnt(kVmcntZero);
         __syncthreads();
         if (threadIdx.x == 0) {
-            const bool local = xcc_id() == xcd;
-            if (!local) __threadfence();
-            const int old = __hip_atomic_fetch_add(ws_cnt + unit, local ? 1 : 0x10001, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-            s_last = (old & 0xffff) == splits - 1 ? ((old >> 16) != 0 || !local ? 2 : 1) : 0;
+            const int old = __hip_atomic_fetch_add(ws_cnt + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = old == splits - 1 ? 1 : 0;
         }
         __syncthreads();
-        const int last = s_last;
-        if (last == 0) return;
-        if (last == 2) __threadfence();
+        if (s_last == 0) return;
         if (threadIdx.x == 0) __hip_atomic_store(ws_cnt + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // one round trip for the partials of up to 8 splits and 2 items per thread
         if (splits <= 8)
@@ -1307,11 +1335,17 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
             // ---- split-KV: publish this split's partial (m, l, unnormalised O); the last
             // split of the row block to arrive merges them (finish_split)
             const int64_t unit = static_cast<int64_t>(pair) * nb + rbk;
-            const int64_t base = (unit * splits + split) * RB;
-            float *o = ws_o + (base + rr) * D + d0;
+            const int base = static_cast<int>((unit * splits + split) * RB);
 #pragma unroll
-            for (int e = 0; e < DL; e += 4) *reinterpret_cast<float4 *>(o + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
-            if ((lane % LPR) == 0) *reinterpret_cast<float2 *>(ws_stats + (base + rr) * 2) = make_float2(mt, lt);
+            for (int e = 0; e < DL; e += 4) {
+                const u32x4_t x = {__float_as_uint(acc[e]), __float_as_uint(acc[e + 1]), __float_as_uint(acc[e + 2]),
+                                   __float_as_uint(acc[e + 3])};
+                __builtin_amdgcn_raw_buffer_store_b128(x, part_o, ((base + rr) * D + d0 + e) * 4, 0, kCoherent);
+            }
+            if ((lane % LPR) == 0) {
+                const u32x2_t x = {__float_as_uint(mt), __float_as_uint(lt)};
+                __builtin_amdgcn_raw_buffer_store_b64(x, part_ml, (base + rr) * 8, 0, kCoherent);
+            }
             finish_split();
             return;
         }
@@ -1337,14 +1371,18 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     // of the row block to arrive merges them (finish_split)
     if (splits > 1) {
         const int64_t unit = static_cast<int64_t>(pair) * nb + rbk;          // (pair, row block)
-        const int64_t base = (unit * splits + split) * RB + wr * kRowsPerWave;
+        const int base = static_cast<int>((unit * splits + split) * RB + wr * kRowsPerWave);
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             const int rr = rt * 16 + c16;
-            float *o = ws_o + (base + rr) * D + 4 * G;
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f32x4_t *>(o + nt * 16) = oacc[rt][nt];
-            if (G == 0) *reinterpret_cast<float2 *>(ws_stats + (base + rr) * 2) = make_float2(mrow[rt], lrow[rt]);
+            for (int nt = 0; nt < NT; ++nt)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, oacc[rt][nt]), part_o,
+                                                       ((base + rr) * D + nt * 16 + 4 * G) * 4, 0, kCoherent);
+            if (G == 0) {
+                const u32x2_t x = {__float_as_uint(mrow[rt]), __float_as_uint(lrow[rt])};
+                __builtin_amdgcn_raw_buffer_store_b64(x, part_ml, (base + rr) * 8, 0, kCoherent);
+            }
         }
         finish_split();
         return;

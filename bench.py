@@ -361,6 +361,33 @@ def stage_durations(sets, stream, reps, torch):
     return durations
 
 
+def controller_from_sweep(out, ti, tmv, torch, B=16, D=8, V=128256, N=128):
+    """The budget controller fed by the measured cost: C(n) = verify-step us at n nodes,
+    interpolated linearly between the swept sizes (mean over the depth limits; flat below
+    the smallest), L_AR = the step at the smallest size.  Device best-first construction
+    over workload 3's drafter marginals then picks each sequence's budget."""
+    Ms = sorted({r["M"] for r in out})
+    t = [float(np.mean([r["us_per_step"] for r in out if r["M"] == m])) for m in Ms]
+    cost = np.interp(np.arange(1, N + 1), Ms, t)
+    q = torch.from_numpy(ti.draft_marginals(np.random.default_rng(3300), B, D, V)).cuda()
+    i32 = dict(dtype=torch.int32, device="cuda")
+    parents, tokens = torch.zeros((B, N + 1), **i32), torch.zeros((B, N + 1), **i32)
+    n_nodes, status = torch.zeros((B,), **i32), torch.zeros((B,), **i32)
+    rho = torch.zeros((B, N + 1), dtype=torch.float64, device="cuda")
+    tmv.tree_best_first(q, N, parents, tokens, n_nodes, rho, status, cost=torch.from_numpy(cost).cuda(), l_ar=t[0])
+    torch.cuda.synchronize()
+    if int(status.abs().sum()) != 0:
+        raise RuntimeError("tree_best_first reported a non-OK status")
+    n = n_nodes.cpu().numpy()
+    r = rho.cpu().numpy()
+    a_hat = [float(r[b, 1:n[b] + 1].sum()) for b in range(B)]
+    return {"cost_us_at": dict(zip(map(str, Ms), [round(x, 2) for x in t])), "l_ar_us": round(t[0], 2),
+            "drafter": "B%d positions %d vocab %d budget <= %d, marginals softmax(N(0,3))" % (B, D, V, N),
+            "chosen_n": n.tolist(), "mean_n": float(n.mean()),
+            "mean_expected_accepted": round(float(np.mean(a_hat)), 3),
+            "mean_S_at_chosen_n": round(float(np.mean([a * t[0] / cost[k - 1] for a, k in zip(a_hat, n)])), 3)}
+
+
 def budget_sweep(args, ti, tmv, torch):
     """Verify-step cost over tree size M and depth limit D_max on workload 2's layer (the
     pages' budget sweet-spot experiment, without a model): the cost table C(N) that the
@@ -384,7 +411,7 @@ def budget_sweep(args, ti, tmv, torch):
             "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": "llama3-8b-layer bf16 B1 H32/8 d128 P2048 V128256, random trees (M nodes, depth "
                                    "<= D_max), greedy"},
-            "sweep": out}
+            "sweep": out, "controller": controller_from_sweep(out, ti, tmv, torch)}
     print(json.dumps(line), flush=True)
 
 

@@ -11,6 +11,9 @@
  *                              sampling with a max(0, p - q) residual
  *   tmv_kv_commit_path         prefix-sharing compaction of the accepted path's K/V rows
  *
+ * Paged K/V caches (block tables) have their own attention and commit calls, and a
+ * best-first tree builder with a budget controller produces trees for the step.
+ *
  * Conventions shared by every call
  *   - Every pointer argument is DEVICE memory owned by the caller (for example a torch
  *     tensor's data_ptr), except the small int64 stride arrays, which are HOST arrays read
@@ -147,6 +150,41 @@ int tmv_tree_verify_attention(int dtype, int B, int M_max, int D_max, int Hq, in
                               void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * tmv_tree_verify_attention_paged -- the same attention over a paged K/V cache.
+ * Defined by the runtime-memory question of "Speculative Decoding Hierarquico: Medusa,
+ * EAGLE-2 e Multi-Token Prediction" (vLLM's PagedAttention keeps the cache in pages
+ * allocated on demand; during tree verification the ancestors' pages are shared, the
+ * pages of rejected branches are freed afterwards and only the accepted path stays).
+ * Results are those of tmv_tree_verify_attention over the cache the pages describe.
+ *   k_pages,
+ *   v_pages      [num_pages][Hkv][page_size][d] pools with element strides
+ *                page_stride = {page, head, slot}; d contiguous.
+ *   block_table  int32 [B][table_stride]: logical slot t of sequence b (prefix slots
+ *                [0, P_b), then node j at P_b + j - 1) lives in page
+ *                block_table[b][t / page_size] at row t % page_size.  Entries
+ *                [0, max_blocks) are read; every entry that holds a slot below P_b + M_b
+ *                must be in [0, num_pages), else the sequence gets TMV_ERR_INPUT and zero
+ *                outputs (other entries may hold anything).  Pages may be shared between
+ *                sequences (a common prefix).
+ *   The capacity is L_cap = max_blocks * page_size.  Requires dtype TMV_BF16, d = 128,
+ *   page_size a power of two in [16, 2^20], 1 <= max_blocks <= 4096, table_stride >=
+ *   max_blocks, page_size * page_stride[2] * 2 < 2^31 bytes, and the alignment rules of
+ *   tmv_tree_verify_attention (TMV_ERR_ARG otherwise).  Every other argument is as there.
+ *   workspace: tmv_tree_verify_attention_paged_workspace() bytes, same contract.
+ */
+size_t tmv_tree_verify_attention_paged_workspace(int B, int M_max, int Hq, int Hkv, int d, int page_size,
+                                                 int max_blocks);
+int tmv_tree_verify_attention_paged(int dtype, int B, int M_max, int D_max, int Hq, int Hkv, int d,
+                                    const void *q, const int64_t *q_stride,
+                                    const void *k_pages, const void *v_pages,
+                                    const int64_t *page_stride, int num_pages, int page_size,
+                                    const int32_t *block_table, int64_t table_stride, int max_blocks,
+                                    const int32_t *prefix_len, const int32_t *n_nodes,
+                                    const int32_t *anc, const int32_t *depth, int32_t *status,
+                                    float scale, void *out, const int64_t *o_stride,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * tmv_tree_accept -- choose the accepted path and the next token.
  *
  * GREEDY (Medusa section of the hierarchical speculative decoding blog: the longest
@@ -233,6 +271,31 @@ int tmv_kv_commit_path(int dtype, int n_layers, int B, int Hkv, int d, int L_cap
                        const int32_t *prefix_len, const int32_t *n_nodes,
                        const int32_t *accept_len, const int32_t *path,
                        int32_t *status, int32_t *new_len, void *stream);
+
+/*
+ * tmv_kv_commit_path_paged -- the same commit over paged K/V pools.
+ * Defined by the runtime-memory question of "Speculative Decoding Hierarquico: Medusa,
+ * EAGLE-2 e Multi-Token Prediction" (only the accepted path is integrated into the
+ * sequence; the pages of rejected branches are freed).  Moves exactly the rows
+ * tmv_kv_commit_path moves, with logical slot t of sequence b at page
+ * block_table[b][t / page_size], row t % page_size.  The table is not changed; after
+ * the call, pages that hold only slots >= new_len[b] carry nothing the sequence needs and
+ * the caller may free them.
+ *   k_pages,
+ *   v_pages      [n_layers][num_pages][Hkv][page_size][d] with element strides
+ *                page_stride = {layer, page, head, slot}; d contiguous.  One table serves
+ *                every layer.
+ *   L_cap = max_blocks * page_size.  A sequence whose moving rows touch a page entry
+ *   outside [0, num_pages) moves nothing and gets TMV_ERR_INPUT (new_len = P_b); the
+ *   other rules are those of tmv_kv_commit_path.  Requires page_size a power of two in
+ *   [1, 2^20], max_blocks >= 1, table_stride >= max_blocks.
+ */
+int tmv_kv_commit_path_paged(int dtype, int n_layers, int B, int Hkv, int d, int num_pages, int page_size,
+                             const int32_t *block_table, int64_t table_stride, int max_blocks,
+                             int M_max, int D_max, void *k_pages, void *v_pages,
+                             const int64_t *page_stride, const int32_t *prefix_len,
+                             const int32_t *n_nodes, const int32_t *accept_len, const int32_t *path,
+                             int32_t *status, int32_t *new_len, void *stream);
 
 /*
  * tmv_tree_best_first -- a best-first prefix tree from per-position draft marginals, and

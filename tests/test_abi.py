@@ -91,6 +91,29 @@ def test_argument_checks_return_before_launch():
     assert lib.tmv_kv_commit_path(*com(tmv.BF16, 4, s4)) == tmv.ERR_ARG
     assert lib.tmv_kv_commit_path(*com(tmv.F32, 256, s4)) == tmv.ERR_ARG
     assert lib.tmv_kv_commit_path(*com(tmv.BF16, 128, (ctypes.c_int64 * 4)(8, 8, 8, 3))) == tmv.ERR_ARG
+    # paged attention: bf16 d128 only; page size a power of two >= 16; table sizes
+    s3p = (ctypes.c_int64 * 3)(8 * 16 * 128, 16 * 128, 128)
+    pa = lambda dt, d, ps, nblk, ts, npg, wsb: (dt, 1, 8, 4, 8, 2, d, fake, s3, fake, fake, s3p, npg, ps, fake,
+                                                ctypes.c_int64(ts), nblk, fake, fake, fake, fake, fake,
+                                                ctypes.c_float(0.1), fake, s3, fake, wsb, None)
+    ok_ws = tmv.tree_verify_attention_paged_workspace(1, 8, 8, 2, 128, 16, 64)
+    assert ok_ws >= 1024
+    assert lib.tmv_tree_verify_attention_paged(*pa(tmv.F32, 128, 16, 64, 64, 100, ok_ws)) == tmv.ERR_ARG
+    assert lib.tmv_tree_verify_attention_paged(*pa(tmv.BF16, 64, 16, 64, 64, 100, ok_ws)) == tmv.ERR_ARG
+    assert lib.tmv_tree_verify_attention_paged(*pa(tmv.BF16, 128, 24, 64, 64, 100, ok_ws)) == tmv.ERR_ARG
+    assert lib.tmv_tree_verify_attention_paged(*pa(tmv.BF16, 128, 8, 64, 64, 100, ok_ws)) == tmv.ERR_ARG
+    assert lib.tmv_tree_verify_attention_paged(*pa(tmv.BF16, 128, 16, 4097, 4097, 100, 1 << 30)) == tmv.ERR_ARG
+    assert lib.tmv_tree_verify_attention_paged(*pa(tmv.BF16, 128, 16, 64, 63, 100, ok_ws)) == tmv.ERR_ARG
+    assert lib.tmv_tree_verify_attention_paged(*pa(tmv.BF16, 128, 16, 64, 64, 0, ok_ws)) == tmv.ERR_ARG
+    assert lib.tmv_tree_verify_attention_paged(*pa(tmv.BF16, 128, 16, 64, 64, 100, 16)) == tmv.ERR_ARG
+    # paged commit: page size, table width, row bytes
+    s4p = (ctypes.c_int64 * 4)(100 * 8 * 16 * 128, 8 * 16 * 128, 16 * 128, 128)
+    pc = lambda ps, nblk, ts, d: (tmv.BF16, 2, 1, 8, d, 100, ps, fake, ctypes.c_int64(ts), nblk, 8, 4, fake, fake, s4p,
+                                  fake, fake, fake, fake, fake, fake, None)
+    assert lib.tmv_kv_commit_path_paged(*pc(12, 8, 8, 128)) == tmv.ERR_ARG
+    assert lib.tmv_kv_commit_path_paged(*pc(16, 8, 7, 128)) == tmv.ERR_ARG
+    assert lib.tmv_kv_commit_path_paged(*pc(16, 0, 8, 128)) == tmv.ERR_ARG
+    assert lib.tmv_kv_commit_path_paged(*pc(16, 8, 8, 4)) == tmv.ERR_ARG
 
 
 def test_package_fails_loudly_without_library(tmp_path):

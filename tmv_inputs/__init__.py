@@ -244,6 +244,35 @@ def _softmax_rows(z):
     return e / e.sum(axis=-1, keepdims=True)
 
 
+def paged_layout(rng, caches, page_size: int, spare: int = 3, alias=()):
+    """Page pools holding contiguous caches [..., B, Hkv, L, d] (same shape, any element
+    dtype): every sequence's slots [0, L) go to max_blocks = ceil(L / page_size) pages at
+    random places of a pool of B * max_blocks + spare pages; slots past L and unused pages
+    hold random bits.  alias = ((b_src, b_dst, n), ...) points b_dst's first n table entries
+    at b_src's pages (the caller makes those slots' contents equal).  Returns the pools
+    [..., num_pages, Hkv, page_size, d] and the table int32 [B][max_blocks]."""
+    lead = caches[0].shape[:-4]
+    B, H, L, d = caches[0].shape[-4:]
+    nblk = -(-L // page_size)
+    num_pages = B * nblk + spare
+    table = rng.permutation(num_pages)[: B * nblk].reshape(B, nblk).astype(np.int32)
+    for bs, bd, n in alias:
+        table[bd, :n] = table[bs, :n]
+    pools = []
+    for c in caches:
+        bits = np.dtype(c.dtype).itemsize * 8
+        garbage = rng.integers(0, 1 << min(bits, 16), size=lead + (num_pages, H, page_size, d))
+        pool = garbage.astype(np.uint16).view(np.uint16).astype(c.dtype) if bits == 16 else \
+            rng.standard_normal(lead + (num_pages, H, page_size, d)).astype(c.dtype)
+        pad = np.zeros(lead + (B, H, nblk * page_size, d), c.dtype)
+        pad[..., :L, :] = c
+        for b in range(B):
+            for j in range(nblk):
+                pool[..., table[b, j], :, :, :] = pad[..., b, :, j * page_size:(j + 1) * page_size, :]
+        pools.append(pool)
+    return pools, table
+
+
 def budget_workload(M: int, D_max: int, seed: int, alpha: float = 0.7) -> Workload:
     """Workload 2's layer (bf16, 32/8 heads, d128, prefix 2048, vocabulary 128256, greedy)
     with a random tree of M nodes and depth at most D_max (tree_random): the inputs of the

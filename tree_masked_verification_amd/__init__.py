@@ -49,6 +49,12 @@ _lib.tmv_tree_accept_workspace.restype = _SZ
 _lib.tmv_tree_accept.argtypes = [_I, _I, _I, _I, _I, _P, _I, _P, _I64, _I64, _P, _I64, _I64, _U64, _U64,
                                  _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
 _lib.tmv_kv_commit_path.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+_lib.tmv_tree_verify_attention_paged_workspace.argtypes = [_I, _I, _I, _I, _I, _I, _I]
+_lib.tmv_tree_verify_attention_paged_workspace.restype = _SZ
+_lib.tmv_tree_verify_attention_paged.argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _I64, _I,
+                                                 _P, _P, _P, _P, _P, _F, _P, _P, _P, _SZ, _P]
+_lib.tmv_kv_commit_path_paged.argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _I64, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,
+                                          _P, _P, _P]
 _lib.tmv_tree_best_first_workspace.argtypes = [_I, _I, _I, _I]
 _lib.tmv_tree_best_first_workspace.restype = _SZ
 _lib.tmv_tree_best_first.argtypes = [_I, _I, _I, _I, _P, _I64, _I64, _P, ctypes.c_double, _P, _P, _P, _P, _P, _P,
@@ -56,7 +62,9 @@ _lib.tmv_tree_best_first.argtypes = [_I, _I, _I, _I, _P, _I64, _I64, _P, ctypes.
 
 EXPORTED = ("tmv_status_string", "tmv_abi_version", "tmv_tree_build_ancestors",
             "tmv_tree_verify_attention_workspace", "tmv_tree_verify_attention", "tmv_tree_accept_workspace",
-            "tmv_tree_accept", "tmv_kv_commit_path", "tmv_tree_best_first_workspace", "tmv_tree_best_first")
+            "tmv_tree_accept", "tmv_kv_commit_path", "tmv_tree_best_first_workspace", "tmv_tree_best_first",
+            "tmv_tree_verify_attention_paged_workspace", "tmv_tree_verify_attention_paged",
+            "tmv_kv_commit_path_paged")
 
 
 class TmvError(RuntimeError):
@@ -156,6 +164,41 @@ def tree_verify_attention(q, k_cache, v_cache, prefix_len, n_nodes, anc, depth, 
            "tree_verify_attention")
 
 
+def tree_verify_attention_paged_workspace(B, M_max, Hq, Hkv, d, page_size, max_blocks) -> int:
+    return int(_lib.tmv_tree_verify_attention_paged_workspace(B, M_max, Hq, Hkv, d, page_size, max_blocks))
+
+
+def tree_verify_attention_paged(q, k_pages, v_pages, block_table, prefix_len, n_nodes, anc, depth, status, out,
+                                scale=None, workspace=None, stream=None):
+    """q, out [B][M_max][Hq][d] bf16; k_pages, v_pages [num_pages][Hkv][page_size][d] bf16;
+    block_table int32 [B][max_blocks] (logical slot t of sequence b: page block_table[b][t //
+    page_size], row t % page_size)."""
+    _i32(block_table, prefix_len, n_nodes, anc, depth, status)
+    if k_pages.dtype != q.dtype or v_pages.dtype != q.dtype or out.dtype != q.dtype:
+        raise TypeError("q, k_pages, v_pages and out must share a dtype")
+    if k_pages.shape != v_pages.shape or k_pages.stride() != v_pages.stride():
+        raise ValueError("k_pages and v_pages must have the same shape and strides")
+    B, M_max, Hq, d = q.shape
+    num_pages, Hkv, page_size = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    max_blocks = block_table.shape[1]
+    if tuple(out.shape) != tuple(q.shape) or q.stride(3) != 1 or k_pages.stride(3) != 1 or out.stride(3) != 1:
+        raise ValueError("bad q / out / page layout")
+    D_max = anc.shape[2] - 1
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    if workspace is None:
+        workspace = torch.zeros(tree_verify_attention_paged_workspace(B, M_max, Hq, Hkv, d, page_size, max_blocks),
+                                dtype=torch.uint8, device=q.device)
+    _check(_lib.tmv_tree_verify_attention_paged(_dtype_code(q), B, M_max, D_max, Hq, Hkv, d, _ptr(q),
+                                                _strides(q, (0, 1, 2)), _ptr(k_pages), _ptr(v_pages),
+                                                _strides(k_pages, (0, 1, 2)), num_pages, page_size, _ptr(block_table),
+                                                block_table.stride(0), max_blocks, _ptr(prefix_len), _ptr(n_nodes),
+                                                _ptr(anc), _ptr(depth), _ptr(status), float(scale), _ptr(out),
+                                                _strides(out, (0, 1, 2)), _ptr(workspace),
+                                                workspace.numel() * workspace.element_size(), _stream(stream)),
+           "tree_verify_attention_paged")
+
+
 # ------------------------------------------------------------------------ stage 3
 def tree_accept_workspace(mode, B, M_max, V) -> int:
     return int(_lib.tmv_tree_accept_workspace(mode, B, M_max, V))
@@ -202,6 +245,26 @@ def kv_commit_path(k_cache, v_cache, prefix_len, n_nodes, accept_len, path, stat
                                    _ptr(n_nodes), _ptr(accept_len), _ptr(path), _ptr(status), _ptr(new_len),
                                    _stream(stream)),
            "kv_commit_path")
+
+
+def kv_commit_path_paged(k_pages, v_pages, block_table, prefix_len, n_nodes, accept_len, path, status, new_len, M_max,
+                         stream=None):
+    """In place on k_pages / v_pages [n_layers][num_pages][Hkv][page_size][d] (or without the
+    layer dimension); block_table int32 [B][max_blocks], shared by every layer."""
+    _i32(block_table, prefix_len, n_nodes, accept_len, path, status, new_len)
+    if k_pages.dim() == 4:
+        k_pages, v_pages = k_pages.unsqueeze(0), v_pages.unsqueeze(0)
+    if k_pages.shape != v_pages.shape or k_pages.stride() != v_pages.stride() or k_pages.dtype != v_pages.dtype:
+        raise ValueError("k_pages and v_pages must match")
+    nl, num_pages, Hkv, page_size, d = k_pages.shape
+    if k_pages.stride(4) != 1:
+        raise ValueError("d must be contiguous")
+    _check(_lib.tmv_kv_commit_path_paged(_dtype_code(k_pages), nl, prefix_len.shape[0], Hkv, d, num_pages, page_size,
+                                         _ptr(block_table), block_table.stride(0), block_table.shape[1], int(M_max),
+                                         path.shape[1], _ptr(k_pages), _ptr(v_pages), _strides(k_pages, (0, 1, 2, 3)),
+                                         _ptr(prefix_len), _ptr(n_nodes), _ptr(accept_len), _ptr(path), _ptr(status),
+                                         _ptr(new_len), _stream(stream)),
+           "kv_commit_path_paged")
 
 
 # ------------------------------------------------------------------------ tree construction

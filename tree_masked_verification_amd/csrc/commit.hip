@@ -11,6 +11,13 @@
 // first copies all moving source rows into LDS, waits at a barrier, then writes them to
 // their destinations -- no row is read after it has been overwritten.  Rows move as
 // 16-byte vectors.
+//
+// Paged caches (vLLM-style blocks, the PagedAttention-for-trees notes of the
+// speculative-decoding survey page): logical slot t of sequence b lives in page
+// table[b][t / page] at row t % page.  The same moves go through the block table; the
+// table itself is not rewritten (a commit moves at most D_max rows per layer and head,
+// which a page copy could only match for whole pages of an in-order path), and pages past
+// the new length hold nothing the sequence still needs, so the caller may free them.
 #include "tmv_device.hpp"
 
 namespace {
@@ -18,16 +25,28 @@ namespace {
 constexpr int kCommitThreads = 256;
 constexpr int kCommitLds = 64 * 1024;     // >= D_max * row bytes (host-checked)
 
+// block table of a paged cache: page of logical slot t of sequence b is
+// tab[b * stride + (t >> shift)], valid when in [0, npages)
+struct CommitPages {
+    const int32_t *tab;
+    int64_t stride;
+    int shift;
+    int npages;
+};
+
+// PAGED: s_b is the page stride
+template <bool PAGED>
 __global__ void __launch_bounds__(kCommitThreads)
 commit_kernel(int n_layers, int B, int Hkv, int row_bytes, int L_cap, int D_max,
               uint8_t *__restrict__ kc, uint8_t *__restrict__ vc,
               int64_t s_layer, int64_t s_b, int64_t s_h, int64_t s_t,      // bytes
               const int32_t *__restrict__ prefix_len, const int32_t *__restrict__ n_nodes,
               const int32_t *__restrict__ accept_len, const int32_t *__restrict__ path,
-              int32_t *__restrict__ status, int32_t *__restrict__ new_len)
+              int32_t *__restrict__ status, int32_t *__restrict__ new_len, CommitPages pg)
 {
     __shared__ uint4 snap[kCommitLds / 16];
     __shared__ int src_row[128], path_sh[128];
+    __shared__ int64_t src_off[128], dst_off[128];   // byte offsets of the moving rows' slots
     __shared__ int nmove, fits;
 
     const int layer = blockIdx.x / B, b = blockIdx.x % B;
@@ -51,13 +70,33 @@ commit_kernel(int n_layers, int B, int Hkv, int row_bytes, int L_cap, int D_max,
             for (int j = 0; j < A; ++j)
                 if (path_sh[j] - 1 != j) src_row[k++] = j;
         nmove = k;
-        if (layer == 0) {
-            new_len[b] = ok ? P + A : P;
-            if (!ok && st == TMV_OK) status[b] = TMV_ERR_INPUT;
-        }
     }
     __syncthreads();
-    if (!fits || nmove == 0) return;
+    // byte offsets of the moving rows' slots, one thread per row (paged: through the
+    // block table; every page involved must be valid)
+    bool bad_page = false;
+    if (fits && tid < nmove) {
+        const int j = src_row[tid];
+        const int64_t src = static_cast<int64_t>(P) + path_sh[j] - 1, dst = static_cast<int64_t>(P) + j;
+        if constexpr (PAGED) {
+            const int32_t *trow = pg.tab + static_cast<int64_t>(b) * pg.stride;
+            const int ps = trow[src >> pg.shift], pd = trow[dst >> pg.shift];
+            bad_page = ps < 0 || ps >= pg.npages || pd < 0 || pd >= pg.npages;
+            const int64_t mask = (int64_t(1) << pg.shift) - 1;
+            src_off[tid] = (bad_page ? 0 : ps) * s_b + (src & mask) * s_t;
+            dst_off[tid] = (bad_page ? 0 : pd) * s_b + (dst & mask) * s_t;
+        } else {
+            src_off[tid] = b * s_b + src * s_t;
+            dst_off[tid] = b * s_b + dst * s_t;
+        }
+    }
+    const bool rejected = __syncthreads_or(bad_page ? 1 : 0) != 0;
+    const bool ok = fits && !rejected;
+    if (tid == 0 && layer == 0) {
+        new_len[b] = ok ? P + A : P;
+        if (!ok && st == TMV_OK) status[b] = TMV_ERR_INPUT;
+    }
+    if (!ok || nmove == 0) return;
 
     const int n = nmove;
     const int segs = row_bytes / 16;
@@ -70,19 +109,16 @@ commit_kernel(int n_layers, int B, int Hkv, int row_bytes, int L_cap, int D_max,
             const int uu = e / (n * segs), rem = e % (n * segs);
             const int r = rem / segs, sg = rem % segs;
             const int unit = u0 + uu, h = unit >> 1;
-            const uint8_t *base = ((unit & 1) ? vc : kc) + layer * s_layer + b * s_b + h * s_h;
-            const int j = src_row[r];
-            const int64_t src = static_cast<int64_t>(P) + path_sh[j] - 1;
-            snap[e] = *reinterpret_cast<const uint4 *>(base + src * s_t + sg * 16);
+            const uint8_t *base = ((unit & 1) ? vc : kc) + layer * s_layer + h * s_h;
+            snap[e] = *reinterpret_cast<const uint4 *>(base + src_off[r] + sg * 16);
         }
         __syncthreads();
         for (int e = tid; e < work; e += kCommitThreads) {
             const int uu = e / (n * segs), rem = e % (n * segs);
             const int r = rem / segs, sg = rem % segs;
             const int unit = u0 + uu, h = unit >> 1;
-            uint8_t *base = ((unit & 1) ? vc : kc) + layer * s_layer + b * s_b + h * s_h;
-            const int64_t dst = static_cast<int64_t>(P) + src_row[r];
-            *reinterpret_cast<uint4 *>(base + dst * s_t + sg * 16) = snap[e];
+            uint8_t *base = ((unit & 1) ? vc : kc) + layer * s_layer + h * s_h;
+            *reinterpret_cast<uint4 *>(base + dst_off[r] + sg * 16) = snap[e];
         }
         __syncthreads();
     }
@@ -115,10 +151,49 @@ extern "C" int tmv_kv_commit_path(int dtype, int n_layers, int B, int Hkv, int d
     const int layers = n_layers > 0 ? n_layers : 1;
     const int64_t blocks = static_cast<int64_t>(layers) * B;
     if (blocks > 0x7fffffff) return TMV_ERR_ARG;
-    hipLaunchKernelGGL(commit_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kCommitThreads), 0,
+    hipLaunchKernelGGL(commit_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kCommitThreads), 0,
                        static_cast<hipStream_t>(stream), layers, B, n_layers > 0 ? Hkv : 0, row_bytes, L_cap, D_max,
                        static_cast<uint8_t *>(k_cache), static_cast<uint8_t *>(v_cache),
                        kv_stride[0] * es, kv_stride[1] * es, kv_stride[2] * es, kv_stride[3] * es,
-                       prefix_len, n_nodes, accept_len, path, status, new_len);
+                       prefix_len, n_nodes, accept_len, path, status, new_len, CommitPages{nullptr, 0, 0, 0});
+    return tmv_host::launch_status(hipGetLastError());
+}
+
+extern "C" int tmv_kv_commit_path_paged(int dtype, int n_layers, int B, int Hkv, int d, int num_pages, int page_size,
+                                        const int32_t *block_table, int64_t table_stride, int max_blocks,
+                                        int M_max, int D_max, void *k_pages, void *v_pages,
+                                        const int64_t *page_stride, const int32_t *prefix_len,
+                                        const int32_t *n_nodes, const int32_t *accept_len, const int32_t *path,
+                                        int32_t *status, int32_t *new_len, void *stream)
+{
+    if (dtype != TMV_F32 && dtype != TMV_BF16) return TMV_ERR_ARG;
+    const int es = dtype == TMV_F32 ? 4 : 2;
+    if (n_layers < 0 || B < 0 || Hkv <= 0 || d <= 0 || num_pages < 1) return TMV_ERR_ARG;
+    if (page_size < 1 || (page_size & (page_size - 1)) || page_size > (1 << 20)) return TMV_ERR_ARG;
+    if (max_blocks < 1 || table_stride < max_blocks) return TMV_ERR_ARG;
+    const int64_t L_cap = static_cast<int64_t>(page_size) * max_blocks;
+    if (L_cap > 0x7fffffff) return TMV_ERR_ARG;
+    if (M_max < 0 || M_max > 128 || D_max < 0 || D_max > 128) return TMV_ERR_ARG;
+    const int row_bytes = d * es;
+    if (row_bytes % 16 != 0 || row_bytes > 512) return TMV_ERR_ARG;
+    if (!page_stride) return TMV_ERR_ARG;
+    if (B == 0) return TMV_OK;
+    if (!block_table || !prefix_len || !n_nodes || !accept_len || !status || !new_len || (D_max > 0 && !path))
+        return TMV_ERR_ARG;
+    if (n_layers > 0 && (!k_pages || !v_pages)) return TMV_ERR_ARG;
+    for (int i = 0; i < 4; ++i)
+        if (page_stride[i] < 0 || (page_stride[i] * es) % 16 != 0) return TMV_ERR_ARG;
+    if ((reinterpret_cast<uintptr_t>(k_pages) | reinterpret_cast<uintptr_t>(v_pages)) & 15u) return TMV_ERR_ARG;
+    const int layers = n_layers > 0 ? n_layers : 1;
+    const int64_t blocks = static_cast<int64_t>(layers) * B;
+    if (blocks > 0x7fffffff) return TMV_ERR_ARG;
+    int shift = 0;
+    while ((1 << shift) < page_size) ++shift;
+    hipLaunchKernelGGL(commit_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kCommitThreads), 0,
+                       static_cast<hipStream_t>(stream), layers, B, n_layers > 0 ? Hkv : 0, row_bytes,
+                       static_cast<int>(L_cap), D_max, static_cast<uint8_t *>(k_pages), static_cast<uint8_t *>(v_pages),
+                       page_stride[0] * es, page_stride[1] * es, page_stride[2] * es, page_stride[3] * es,
+                       prefix_len, n_nodes, accept_len, path, status, new_len,
+                       CommitPages{block_table, table_stride, shift, num_pages});
     return tmv_host::launch_status(hipGetLastError());
 }

@@ -850,7 +850,19 @@ struct RingShape {
 // fetch the rest in further batches
 constexpr int kAncBatch = 16;
 
-template <int D, int WR, bool DEEP>
+// paged caches: block-table entries of one sequence staged in LDS (the ring leaves 32 KB)
+constexpr int kMaxPagesLds = 4096;
+
+// block table of a paged cache (PAGED kernels): page of logical token t of sequence b is
+// tab[b * stride + (t >> shift)], valid when in [0, npages)
+struct PagedArgs {
+    const int32_t *tab;
+    int64_t stride;
+    int shift;
+    int npages;
+};
+
+template <int D, int WR, bool DEEP, bool PAGED>
 __global__ void __launch_bounds__(kWaves * kWave)
 tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
                       const int32_t *__restrict__ prefix_len, const int32_t *__restrict__ n_nodes,
@@ -863,7 +875,8 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
                       const int32_t *__restrict__ anc, const int32_t *__restrict__ depth,
                       int32_t *__restrict__ status, float qk_scale_log2,
                       uint16_t *__restrict__ out, int64_t os0, int64_t os1, int64_t os2,
-                      float *__restrict__ ws_stats, float *__restrict__ ws_o, int32_t *__restrict__ ws_cnt)
+                      float *__restrict__ ws_stats, float *__restrict__ ws_o, int32_t *__restrict__ ws_cnt,
+                      PagedArgs pg)
 {
     using RS = RingShape<D>;
     static_assert(D == 128, "the LDS-ring kernel is written for head dimension 128");
@@ -879,6 +892,10 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     __shared__ __attribute__((aligned(16))) char ring0[RS::kRound * RS::kSlotBytes];
     __shared__ __attribute__((aligned(16))) char ring1[RS::kRound * RS::kSlotBytes];
     __shared__ int s_last;
+    // paged caches: this sequence's block-table entries (-1: invalid) and, per wave, the
+    // first invalid entry it staged
+    __shared__ int32_t pg_lds[PAGED ? kMaxPagesLds : 1];
+    __shared__ int pg_bad[kWaves];
 
     // ---- decode the workgroup: XCD-major so one (sequence, kv head) stays on one XCD
     // geom = splits | workgroups per pair << 5 | Hkv << 16
@@ -916,7 +933,9 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     // slot; lane l writes 16 bytes at 16*l.  Within K (or V) the LDS holds row t at
     // t*kRowBytes with its 16-byte pieces XOR-swizzled by (t mod kPieces), so the lane
     // that fills LDS piece (t, pp) reads global piece pp ^ (t mod kPieces) of row t.
-    const int64_t head_off = (static_cast<int64_t>(b) * ks0_16 + static_cast<int64_t>(kvh) * ks1_16) * 16;
+    // (paged: ks0_16 is the page stride; a chunk's page is added when it is issued)
+    const int64_t head_off = ((PAGED ? 0 : static_cast<int64_t>(b) * ks0_16) + static_cast<int64_t>(kvh) * ks1_16) * 16;
+    const int64_t page_bytes = static_cast<int64_t>(ks0_16) * 16;
     const char *kbase = reinterpret_cast<const char *>(kc) + head_off;
     const char *vbase = reinterpret_cast<const char *>(vc) + head_off;
     const int64_t row_bytes = static_cast<int64_t>(ks2_16) * 16;
@@ -926,6 +945,10 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     const char *mbase = wave_v ? vbase : kbase;
     uint32_t dma_off[RS::kDmaPerWave];
     int dma_lds[RS::kDmaPerWave];
+    // 16-token pages: rows 16-31 of a chunk lie on its second page; every DMA instruction
+    // covers 4 rows, all on one page (dma_hi), at offsets relative to that page
+    bool dma_hi[RS::kDmaPerWave];
+    const bool two_pages = PAGED && pg.shift == 4;
 #pragma unroll
     for (int jd = 0; jd < RS::kDmaPerWave; ++jd) {
         const int i = wave * RS::kDmaPerWave + jd;             // instruction within the chunk
@@ -935,7 +958,8 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         // K rows swizzle their 16-byte pieces by t mod 16, V rows by 2t mod 16 (the V^T reads
         // take four consecutive rows at once; see lds_read_vt)
         const int sw = wave_v ? (2 * t) % PP : t % PP;
-        dma_off[jd] = static_cast<uint32_t>(t * row_bytes + ((pp ^ sw) * 16));
+        dma_hi[jd] = two_pages && t >= 16;
+        dma_off[jd] = static_cast<uint32_t>((dma_hi[jd] ? t - 16 : t) * row_bytes + ((pp ^ sw) * 16));
         dma_lds[jd] = (wave_v ? RS::kMatBytes : 0) + ii * 1024;
     }
     // issue this wave's share of local chunk k into the slot at `slot` (records stop at
@@ -944,19 +968,60 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         const int t0 = (split + k * splits) * kChunk;
         int recs = (k < nk_lim) ? t_lim - t0 : 0;
         recs = recs < 0 ? 0 : (recs > kChunk ? kChunk : recs);
-        const int nbytes = __builtin_amdgcn_readfirstlane(static_cast<int>(recs * row_bytes));
-        const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<char *>(mbase + static_cast<int64_t>(k < nk_lim ? t0 : 0) * row_bytes), 0, nbytes, kBufferFlags);
+        if constexpr (PAGED) {
+            // the chunk's rows on its page(s); an invalid page loads nothing (the sequence
+            // is rejected in the prologue when such a page is visible)
+            const int recs0 = two_pages ? (recs < 16 ? recs : 16) : recs;
+            const int recs1 = two_pages ? (recs > 16 ? recs - 16 : 0) : 0;
+            // (indices clamped into the staged entries: a chunk with rows has them there)
+            const int n_pg = L_cap >> pg.shift;
+            const int p0 = (t0 >> pg.shift) < n_pg - 1 ? (t0 >> pg.shift) : n_pg - 1;
+            const int p1 = p0 + 1 < n_pg - 1 ? p0 + 1 : n_pg - 1;
+            const int pa = __builtin_amdgcn_readfirstlane(recs0 > 0 ? pg_lds[p0] : -1);
+            const int pb = __builtin_amdgcn_readfirstlane(recs1 > 0 ? pg_lds[p1] : -1);
+            const int64_t in_page = static_cast<int64_t>(t0 & ((1 << pg.shift) - 1)) * row_bytes;
+            const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<char *>(mbase + (pa >= 0 ? pa : 0) * page_bytes + in_page), 0,
+                pa >= 0 ? static_cast<int>(recs0 * row_bytes) : 0, kBufferFlags);
+            const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<char *>(mbase + (pb >= 0 ? pb : 0) * page_bytes), 0,
+                pb >= 0 ? static_cast<int>(recs1 * row_bytes) : 0, kBufferFlags);
 #pragma unroll
-        for (int jd = 0; jd < RS::kDmaPerWave; ++jd)
-            dma_to_lds16(mr, slot + dma_lds[jd], dma_off[jd]);
+            for (int jd = 0; jd < RS::kDmaPerWave; ++jd)
+                dma_to_lds16(dma_hi[jd] ? rb : ra, slot + dma_lds[jd], dma_off[jd]);
+        } else {
+            const int nbytes = __builtin_amdgcn_readfirstlane(static_cast<int>(recs * row_bytes));
+            const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<char *>(mbase + static_cast<int64_t>(k < nk_lim ? t0 : 0) * row_bytes), 0, nbytes, kBufferFlags);
+#pragma unroll
+            for (int jd = 0; jd < RS::kDmaPerWave; ++jd)
+                dma_to_lds16(mr, slot + dma_lds[jd], dma_off[jd]);
+        }
     };
     // round r fills half r % 2 of the ring with local chunks r*kRound .. +kRound
     auto issue_round = [&](int r, char *half) {
 #pragma unroll
         for (int j = 0; j < RS::kRound; ++j) issue_chunk(r * RS::kRound + j, half + j * RS::kSlotBytes);
     };
-    // the first two rounds go out before anything is loaded or waited for
+    // paged caches: stage the sequence's block-table entries first (L_cap = entries x page)
+    if constexpr (PAGED) {
+        const int n_pg = L_cap >> pg.shift;
+        const int32_t *trow = pg.tab + static_cast<int64_t>(b) * pg.stride;
+        int bad_min = 0x7fffffff;
+        for (int i = threadIdx.x; i < n_pg; i += kWaves * kWave) {
+            const int e = trow[i];
+            const bool ok = e >= 0 && e < pg.npages;
+            pg_lds[i] = ok ? e : -1;
+            bad_min = ok || i > bad_min ? bad_min : i;
+        }
+        for (int o = 32; o >= 1; o >>= 1) {
+            const int y = __shfl_xor(bad_min, o, kWave);
+            bad_min = y < bad_min ? y : bad_min;
+        }
+        if (lane == 0) pg_bad[wave] = bad_min;
+        __syncthreads();
+    }
+    // the first two rounds go out before anything else is loaded or waited for
     // (both are issued even when empty -- they then load nothing -- so the number of DMA
     // operations in flight is the same on every path)
     issue_round(0, ring0);
@@ -989,6 +1054,17 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     if (st == TMV_OK && (M < 0 || M > M_max || P < 0 || static_cast<int64_t>(P) + M > L_cap)) {
         st = TMV_ERR_INPUT;
         if (threadIdx.x == 0 && rbk == 0 && split == 0) status[b] = TMV_ERR_INPUT;
+    }
+    if constexpr (PAGED) {
+        // every page holding a visible token must be a valid page
+        int fb = pg_bad[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) fb = pg_bad[w] < fb ? pg_bad[w] : fb;
+        fb = __builtin_amdgcn_readfirstlane(fb);
+        if (st == TMV_OK && fb < ((P + M + (1 << pg.shift) - 1) >> pg.shift)) {
+            st = TMV_ERR_INPUT;
+            if (threadIdx.x == 0 && rbk == 0 && split == 0) status[b] = TMV_ERR_INPUT;
+        }
     }
     const int Rh = (st == TMV_OK) ? M * g : 0;           // live rows of this kv head
 
@@ -1533,20 +1609,21 @@ template <int D, int WR>
 void launch_bf16(const AttnPlan &p, hipStream_t s, int M_max, int D_max, int Hq, int Hkv,
                  const void *q, const int64_t *qs, const void *k, const void *v, const int64_t *kvs,
                  int L_cap, const int32_t *P, const int32_t *n, const int32_t *anc, const int32_t *dep,
-                 int32_t *status, float scale, void *out, const int64_t *os, void *ws, size_t off_o, size_t off_stats)
+                 int32_t *status, float scale, void *out, const int64_t *os, void *ws, size_t off_o, size_t off_stats,
+                 const PagedArgs *pg)
 {
     char *w = static_cast<char *>(ws);
     int32_t *cnt = reinterpret_cast<int32_t *>(w);
     float *stats = reinterpret_cast<float *>(w + off_stats), *part = reinterpret_cast<float *>(w + off_o);
     const uint32_t geom = static_cast<uint32_t>(p.splits) | (static_cast<uint32_t>(p.per_pair) << 5) |
                           (static_cast<uint32_t>(Hkv) << 16);
-#define TMV_LAUNCH_ATTN(DEEP)                                                                              \
-    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, WR, DEEP>), dim3(p.slots * tmv::kXcds), dim3(kWaves * kWave), 0, s, \
+#define TMV_LAUNCH_ATTN(DEEP, PAGED)                                                                       \
+    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, WR, DEEP, PAGED>), dim3(p.slots * tmv::kXcds), dim3(kWaves * kWave), 0, s, \
                        static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), P, n,                 \
                        static_cast<uint32_t>(kvs[0] / 8), static_cast<uint32_t>(kvs[1] / 8),                    \
                        static_cast<uint32_t>(kvs[2] / 8), L_cap, p.pairs, geom, M_max, D_max, Hq, p.nb,         \
                        static_cast<const uint16_t *>(q), qs[0], qs[1], qs[2], anc, dep, status, scale * kLog2e,  \
-                       static_cast<uint16_t *>(out), os[0], os[1], os[2], stats, part, cnt)
+                       static_cast<uint16_t *>(out), os[0], os[1], os[2], stats, part, cnt, pgv)
     if constexpr (D == 64) {
         hipLaunchKernelGGL((tree_attn_bf16_stream_kernel<D, WR>), dim3(p.slots * tmv::kXcds), dim3(kWaves * kWave), 0,
                            s, M_max, D_max, Hq, Hkv, static_cast<const uint16_t *>(q), qs[0], qs[1], qs[2],
@@ -1554,8 +1631,14 @@ void launch_bf16(const AttnPlan &p, hipStream_t s, int M_max, int D_max, int Hq,
                            kvs[2], L_cap, P, n, anc, dep, status, scale * kLog2e, static_cast<uint16_t *>(out),
                            os[0], os[1], os[2], stats, part, p.pairs, p.nb, p.splits, p.per_pair);
     } else {
-        if (D_max + 1 > kAncBatch) TMV_LAUNCH_ATTN(true);
-        else TMV_LAUNCH_ATTN(false);
+        const PagedArgs pgv = pg ? *pg : PagedArgs{nullptr, 0, 0, 0};
+        if (pg) {
+            if (D_max + 1 > kAncBatch) TMV_LAUNCH_ATTN(true, true);
+            else TMV_LAUNCH_ATTN(false, true);
+        } else {
+            if (D_max + 1 > kAncBatch) TMV_LAUNCH_ATTN(true, false);
+            else TMV_LAUNCH_ATTN(false, false);
+        }
     }
 #undef TMV_LAUNCH_ATTN
     // the LDS-ring kernel (d128) merges its splits itself; the streaming kernel needs the
@@ -1570,6 +1653,32 @@ void launch_bf16(const AttnPlan &p, hipStream_t s, int M_max, int D_max, int Hq,
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// the bf16 kernels for the plan's row-group width (pg: block table of a paged cache, d128 only)
+void dispatch_bf16(const AttnPlan &p, int d, hipStream_t s, int M_max, int D_max, int Hq, int Hkv, const void *q,
+                   const int64_t *qs, const void *k, const void *v, const int64_t *kvs, int L_cap, const int32_t *P,
+                   const int32_t *n, const int32_t *anc, const int32_t *dep, int32_t *status, float scale, void *out,
+                   const int64_t *os, void *ws, size_t off_o, size_t off_stats, const PagedArgs *pg)
+{
+    if (d == 128) {
+        if (p.wr == 4)
+            launch_bf16<128, 4>(p, s, M_max, D_max, Hq, Hkv, q, qs, k, v, kvs, L_cap, P, n, anc, dep, status, scale, out,
+                                os, ws, off_o, off_stats, pg);
+        else if (p.wr == 2)
+            launch_bf16<128, 2>(p, s, M_max, D_max, Hq, Hkv, q, qs, k, v, kvs, L_cap, P, n, anc, dep, status, scale, out,
+                                os, ws, off_o, off_stats, pg);
+        else
+            launch_bf16<128, 1>(p, s, M_max, D_max, Hq, Hkv, q, qs, k, v, kvs, L_cap, P, n, anc, dep, status, scale, out,
+                                os, ws, off_o, off_stats, pg);
+    } else {
+        if (p.wr == 4)
+            launch_bf16<64, 4>(p, s, M_max, D_max, Hq, Hkv, q, qs, k, v, kvs, L_cap, P, n, anc, dep, status, scale, out,
+                               os, ws, off_o, off_stats, nullptr);
+        else
+            launch_bf16<64, 1>(p, s, M_max, D_max, Hq, Hkv, q, qs, k, v, kvs, L_cap, P, n, anc, dep, status, scale, out,
+                               os, ws, off_o, off_stats, nullptr);
+    }
+}
 
 }  // namespace
 
@@ -1640,18 +1749,59 @@ extern "C" int tmv_tree_verify_attention(int dtype, int B, int M_max, int D_max,
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return TMV_ERR_ARG;
     if (static_cast<int64_t>(p.slots) * tmv::kXcds > 0x7fffffff) return TMV_ERR_ARG;
 
-    if (d == 128) {
-        if (p.wr == 4) launch_bf16<128, 4>(p, s, M_max, D_max, Hq, Hkv, q, q_stride, k_cache, v_cache, kv_stride, L_cap,
-                                           prefix_len, n_nodes, anc, depth, status, scale, out, o_stride, workspace, off_o, off_stats);
-        else if (p.wr == 2) launch_bf16<128, 2>(p, s, M_max, D_max, Hq, Hkv, q, q_stride, k_cache, v_cache, kv_stride, L_cap,
-                                 prefix_len, n_nodes, anc, depth, status, scale, out, o_stride, workspace, off_o, off_stats);
-        else launch_bf16<128, 1>(p, s, M_max, D_max, Hq, Hkv, q, q_stride, k_cache, v_cache, kv_stride, L_cap,
-                                 prefix_len, n_nodes, anc, depth, status, scale, out, o_stride, workspace, off_o, off_stats);
-    } else {
-        if (p.wr == 4) launch_bf16<64, 4>(p, s, M_max, D_max, Hq, Hkv, q, q_stride, k_cache, v_cache, kv_stride, L_cap,
-                                          prefix_len, n_nodes, anc, depth, status, scale, out, o_stride, workspace, off_o, off_stats);
-        else launch_bf16<64, 1>(p, s, M_max, D_max, Hq, Hkv, q, q_stride, k_cache, v_cache, kv_stride, L_cap,
-                                prefix_len, n_nodes, anc, depth, status, scale, out, o_stride, workspace, off_o, off_stats);
+    dispatch_bf16(p, d, s, M_max, D_max, Hq, Hkv, q, q_stride, k_cache, v_cache, kv_stride, L_cap, prefix_len, n_nodes,
+                  anc, depth, status, scale, out, o_stride, workspace, off_o, off_stats, nullptr);
+    return tmv_host::launch_status(hipGetLastError());
+}
+
+extern "C" size_t tmv_tree_verify_attention_paged_workspace(int B, int M_max, int Hq, int Hkv, int d, int page_size,
+                                                            int max_blocks)
+{
+    if (B <= 0 || Hkv <= 0 || Hq <= 0 || Hq % Hkv || page_size <= 0 || max_blocks <= 0) return 256;
+    const int64_t L_cap = static_cast<int64_t>(page_size) * max_blocks;
+    if (L_cap > 0x7fffffff) return 256;
+    return plan_bytes(make_plan(B, M_max, Hq, Hkv, static_cast<int>(L_cap), d), d, nullptr);
+}
+
+extern "C" int tmv_tree_verify_attention_paged(int dtype, int B, int M_max, int D_max, int Hq, int Hkv, int d,
+                                               const void *q, const int64_t *q_stride,
+                                               const void *k_pages, const void *v_pages,
+                                               const int64_t *page_stride, int num_pages, int page_size,
+                                               const int32_t *block_table, int64_t table_stride, int max_blocks,
+                                               const int32_t *prefix_len, const int32_t *n_nodes,
+                                               const int32_t *anc, const int32_t *depth, int32_t *status,
+                                               float scale, void *out, const int64_t *o_stride,
+                                               void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (dtype != TMV_BF16 || d != 128) return TMV_ERR_ARG;
+    if (B < 0 || M_max < 0 || M_max > 128 || D_max < 0 || D_max > 128) return TMV_ERR_ARG;
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Hq / Hkv > 16 || Hkv > 0xffff) return TMV_ERR_ARG;
+    if (page_size < 16 || (page_size & (page_size - 1)) || page_size > (1 << 20)) return TMV_ERR_ARG;
+    if (max_blocks < 1 || max_blocks > kMaxPagesLds || num_pages < 1 || table_stride < max_blocks) return TMV_ERR_ARG;
+    const int64_t L_cap = static_cast<int64_t>(page_size) * max_blocks;
+    if (L_cap > 0x7fffffff) return TMV_ERR_ARG;
+    if (!q_stride || !page_stride || !o_stride) return TMV_ERR_ARG;
+    if (B == 0 || M_max == 0) return TMV_OK;
+    if (!q || !k_pages || !v_pages || !block_table || !prefix_len || !n_nodes || !anc || !depth || !status || !out)
+        return TMV_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(out)) return TMV_ERR_ARG;
+    for (int i = 0; i < 3; ++i) {
+        if (q_stride[i] < 0 || page_stride[i] < 0 || o_stride[i] < 0) return TMV_ERR_ARG;
+        if ((q_stride[i] | page_stride[i] | o_stride[i]) & 7) return TMV_ERR_ARG;
+        if (page_stride[i] / 8 > 0xffffffffll) return TMV_ERR_ARG;
     }
+    // a chunk's rows are addressed by 32-bit offsets from their page's first row
+    if (static_cast<int64_t>(page_size) * page_stride[2] * 2 >= (int64_t(1) << 31)) return TMV_ERR_ARG;
+    const AttnPlan p = make_plan(B, M_max, Hq, Hkv, static_cast<int>(L_cap), d);
+    size_t off_o = 0, off_stats = 0;
+    const size_t need = plan_bytes(p, d, &off_o, &off_stats);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return TMV_ERR_ARG;
+    if (static_cast<int64_t>(p.slots) * tmv::kXcds > 0x7fffffff) return TMV_ERR_ARG;
+    int shift = 0;
+    while ((1 << shift) < page_size) ++shift;
+    const PagedArgs pg{block_table, table_stride, shift, num_pages};
+    dispatch_bf16(p, d, static_cast<hipStream_t>(stream), M_max, D_max, Hq, Hkv, q, q_stride, k_pages, v_pages,
+                  page_stride, static_cast<int>(L_cap), prefix_len, n_nodes, anc, depth, status, scale, out, o_stride,
+                  workspace, off_o, off_stats, &pg);
     return tmv_host::launch_status(hipGetLastError());
 }

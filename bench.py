@@ -25,6 +25,8 @@ Timed regions (both after --warmup untimed steps):
   3. workload 3 only: device best-first tree construction at its drafter shape (16
      sequences, 8 positions, vocabulary 128256, budget 128), reported as "drafting" beside
      the step (it builds the trees a step verifies; it is not part of the step).
+  4. workloads 2-4: the paged-cache attention and commit on the same sets (K/V in pools
+     of 16-token pages at random places), timed like region 2, reported as "paged".
 The oracle (tests-only CPU implementation) is timed on a bounded sample of the default
 workload for the cpu_baseline field.
 
@@ -263,6 +265,72 @@ def time_best_first(torch, tmv, ti, stream, B=16, D=8, V=128256, N=128):
                                 "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
                                 "shape": "B%d positions %d vocab %d budget %d" % (B, D, V, N),
                                 "input_sets": n_sets}}
+
+
+def time_paged(torch, tmv, sets, stream, durations, page_size=16, reps=None):
+    """The paged-cache calls on the same input sets: every set's K/V laid out in a pool of
+    page_size-token pages at a random permutation (made on the device), the attention and
+    commit timed like the contiguous stages (one HIP graph of back-to-back launches over
+    the rotating sets, HIP events on its capture stream)."""
+    g = torch.Generator(device="cpu").manual_seed(4242)
+    paged = []
+    w0 = sets[0].w
+    ws = torch.zeros(tmv.tree_verify_attention_paged_workspace(w0.B, w0.M_max, w0.Hq, w0.Hkv, w0.d, page_size,
+                                                               -(-w0.L_cap // page_size)),
+                     dtype=torch.uint8, device="cuda")
+    for s in sets:
+        B, H, L, d = s.k.shape
+        nblk = -(-L // page_size)
+        perm = torch.randperm(B * nblk + 3, generator=g)[: B * nblk].to(torch.int32)
+        table = perm.view(B, nblk).cuda()
+        pad = torch.zeros((B, H, nblk * page_size, d), dtype=s.k.dtype, device="cuda")
+        pools = []
+        for c in (s.k, s.v):
+            pad[:, :, :L] = c
+            pool = torch.zeros((B * nblk + 3, H, page_size, d), dtype=c.dtype, device="cuda")
+            pool[table.view(-1).long()] = pad.view(B, H, nblk, page_size, d).permute(0, 2, 1, 3, 4).reshape(
+                B * nblk, H, page_size, d)
+            pools.append(pool)
+        paged.append((s, pools[0], pools[1], table))
+    del pad
+
+    def attn(e):
+        s, kp, vp, tab = e
+        tmv.tree_verify_attention_paged(s.q, kp, vp, tab, s.prefix, s.n_nodes, s.anc, s.depth, s.status, s.out,
+                                        scale=s.w.scale, workspace=ws)
+
+    def commit(e):
+        s, kp, vp, tab = e
+        tmv.kv_commit_path_paged(kp, vp, tab, s.prefix, s.n_nodes, s.accept_len, s.path, s.status, s.new_len,
+                                 s.w.M_max)
+
+    reps = reps or (40 if w0.B * w0.L_cap > 100000 else 400)
+    out = {}
+    with torch.cuda.stream(stream):
+        for name, fn in (("attention", attn), ("commit", commit)):
+            for e in paged:
+                fn(e)
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=stream):
+                for r in range(reps):
+                    fn(paged[r % len(paged)])
+            gr.replay()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            gr.replay()
+            e1.record(stream)
+            e1.synchronize()
+            out[name] = e0.elapsed_time(e1) * 1e3 / reps
+            del gr
+    torch.cuda.synchronize()
+    if int(torch.stack([s.status for s in sets]).abs().sum()) != 0:
+        raise RuntimeError("a paged call reported a non-OK status")
+    return {"page_size": page_size, "input_sets": len(paged),
+            "tree_verify_attention_paged": {"avg_us": round(out["attention"], 3),
+                                            "vs_contiguous": round(out["attention"] / durations["attention"], 3)},
+            "kv_commit_path_paged": {"avg_us": round(out["commit"], 3),
+                                     "vs_contiguous": round(out["commit"] / durations["commit"], 3)}}
 
 
 def make_sets(c, ti, tmv, torch):
@@ -532,6 +600,12 @@ def main():
 
     dominant = max((k for k in durations if k != "build"), key=lambda k: durations[k])
     drafting = time_best_first(torch, tmv, ti, stream) if c == 3 else None
+    paged = time_paged(torch, tmv, sets, stream, durations) if c in (2, 3, 4) else None
+    if paged:
+        print("bench: paged (%d-token pages): attention %.2f us (x%.3f), commit %.2f us"
+              % (paged["page_size"], paged["tree_verify_attention_paged"]["avg_us"],
+                 paged["tree_verify_attention_paged"]["vs_contiguous"], paged["kv_commit_path_paged"]["avg_us"]),
+              file=sys.stderr, flush=True)
     if drafting:
         print("bench: tree_best_first %.2f us per launch (%s)" % (drafting["tree_best_first"]["avg_us"],
                                                                    drafting["tree_best_first"]["shape"]),
@@ -565,6 +639,7 @@ def main():
         "attention_roofline": roofline("attention") if "attention" in durations else None,
         "kernels": kernels,
         "drafting": drafting,
+        "paged": paged,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

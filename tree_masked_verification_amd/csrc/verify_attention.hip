@@ -958,13 +958,36 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         // K rows swizzle their 16-byte pieces by t mod 16, V rows by 2t mod 16 (the V^T reads
         // take four consecutive rows at once; see lds_read_vt)
         const int sw = wave_v ? (2 * t) % PP : t % PP;
-        dma_hi[jd] = two_pages && t >= 16;
+        // (from the wave-uniform instruction index: instruction ii covers rows 64*ii/PP ..
+        // +64/PP - 1, all on one side of row 16, so the page choice stays scalar)
+        static_assert((64 / PP) > 0 && 16 % (64 / PP) == 0, "a DMA instruction must not straddle row 16");
+        dma_hi[jd] = two_pages && ii * 64 / PP >= 16;
         dma_off[jd] = static_cast<uint32_t>((dma_hi[jd] ? t - 16 : t) * row_bytes + ((pp ^ sw) * 16));
         dma_lds[jd] = (wave_v ? RS::kMatBytes : 0) + ii * 1024;
     }
     // issue this wave's share of local chunk k into the slot at `slot` (records stop at
     // t_lim, so loads past it write zeros and touch no memory; chunks past nk_lim load nothing)
-    auto issue_chunk = [&](int k, char *slot) {
+    // rows of local chunk k to copy (records stop at t_lim, so loads past it write zeros and
+    // touch no memory; chunks past nk_lim load nothing)
+    auto chunk_recs = [&](int k) {
+        const int t0 = (split + k * splits) * kChunk;
+        const int recs = (k < nk_lim) ? t_lim - t0 : 0;
+        return recs < 0 ? 0 : (recs > kChunk ? kChunk : recs);
+    };
+    // paged: the staged table entry of local chunk k's first (which = 0) or second page,
+    // -1 when the chunk copies no rows there (indices clamped into the staged entries: a
+    // chunk with rows has them there)
+    auto page_of = [&](int k, int which) {
+        const int t0 = (split + k * splits) * kChunk;
+        const int recs = chunk_recs(k);
+        const int rows = which == 0 ? (two_pages ? (recs < 16 ? recs : 16) : recs) : (two_pages ? recs - 16 : 0);
+        const int n_pg = L_cap >> pg.shift;
+        const int p = (t0 >> pg.shift) + which;
+        return rows > 0 ? pg_lds[p < n_pg - 1 ? p : n_pg - 1] : -1;
+    };
+    // issue this wave's share of local chunk k into the slot at `slot` (paged: pa / pb are
+    // its page entries, wave-uniform)
+    auto issue_chunk = [&](int k, char *slot, int pa, int pb) {
         const int t0 = (split + k * splits) * kChunk;
         int recs = (k < nk_lim) ? t_lim - t0 : 0;
         recs = recs < 0 ? 0 : (recs > kChunk ? kChunk : recs);
@@ -973,12 +996,6 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
             // is rejected in the prologue when such a page is visible)
             const int recs0 = two_pages ? (recs < 16 ? recs : 16) : recs;
             const int recs1 = two_pages ? (recs > 16 ? recs - 16 : 0) : 0;
-            // (indices clamped into the staged entries: a chunk with rows has them there)
-            const int n_pg = L_cap >> pg.shift;
-            const int p0 = (t0 >> pg.shift) < n_pg - 1 ? (t0 >> pg.shift) : n_pg - 1;
-            const int p1 = p0 + 1 < n_pg - 1 ? p0 + 1 : n_pg - 1;
-            const int pa = __builtin_amdgcn_readfirstlane(recs0 > 0 ? pg_lds[p0] : -1);
-            const int pb = __builtin_amdgcn_readfirstlane(recs1 > 0 ? pg_lds[p1] : -1);
             const int64_t in_page = static_cast<int64_t>(t0 & ((1 << pg.shift) - 1)) * row_bytes;
             const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<char *>(mbase + (pa >= 0 ? pa : 0) * page_bytes + in_page), 0,
@@ -998,10 +1015,33 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
                 dma_to_lds16(mr, slot + dma_lds[jd], dma_off[jd]);
         }
     };
-    // round r fills half r % 2 of the ring with local chunks r*kRound .. +kRound
-    auto issue_round = [&](int r, char *half) {
+    // paged: page entries of the next round to issue, read from LDS a round ahead so the
+    // read's latency hides behind that round's wait and compute
+    int pf_a[RS::kRound], pf_b[RS::kRound];
+    auto prefetch_pages = [&](int r) {
+        if constexpr (PAGED) {
 #pragma unroll
-        for (int j = 0; j < RS::kRound; ++j) issue_chunk(r * RS::kRound + j, half + j * RS::kSlotBytes);
+            for (int j = 0; j < RS::kRound; ++j) {
+                pf_a[j] = page_of(r * RS::kRound + j, 0);
+                pf_b[j] = page_of(r * RS::kRound + j, 1);
+            }
+        }
+    };
+    // round r fills half r % 2 of the ring with local chunks r*kRound .. +kRound (paged:
+    // from the prefetched entries when `prefetched`)
+    auto issue_round = [&](int r, char *half, bool prefetched = false) {
+        if constexpr (PAGED) {
+#pragma unroll
+            for (int j = 0; j < RS::kRound; ++j) {
+                const int k = r * RS::kRound + j;
+                const int pa = __builtin_amdgcn_readfirstlane(prefetched ? pf_a[j] : page_of(k, 0));
+                const int pb = __builtin_amdgcn_readfirstlane(prefetched ? pf_b[j] : page_of(k, 1));
+                issue_chunk(k, half + j * RS::kSlotBytes, pa, pb);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < RS::kRound; ++j) issue_chunk(r * RS::kRound + j, half + j * RS::kSlotBytes, -1, -1);
+        }
     };
     // paged caches: stage the sequence's block-table entries first (L_cap = entries x page)
     if constexpr (PAGED) {
@@ -1272,6 +1312,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         // wave still reads the half, then refill it with round r + 2.  The barriers carry
         // no memory fence on purpose: a fence would wait for all DMA in flight.
         auto run_round = [&](int r, char *half) {
+            if (r + 2 < nrounds) prefetch_pages(r + 2);
             if (r + 1 < nrounds) __builtin_amdgcn_s_waitcnt(kVmcntRound<RS::kRound * RS::kDmaPerWave>());
             else __builtin_amdgcn_s_waitcnt(kVmcntZero);
             __builtin_amdgcn_s_barrier();
@@ -1292,7 +1333,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
             }
             __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
             __builtin_amdgcn_s_barrier();
-            if (r + 2 < nrounds) issue_round(r + 2, half);
+            if (r + 2 < nrounds) issue_round(r + 2, half, true);
         };
         for (int r = 0; r < nrounds; r += 2) {
             run_round(r, ring0);

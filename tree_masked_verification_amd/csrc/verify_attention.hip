@@ -993,9 +993,11 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         recs = recs < 0 ? 0 : (recs > kChunk ? kChunk : recs);
         if constexpr (PAGED) {
             // the chunk's rows on its page(s); an invalid page loads nothing (the sequence
-            // is rejected in the prologue when such a page is visible)
-            const int recs0 = two_pages ? (recs < 16 ? recs : 16) : recs;
-            const int recs1 = two_pages ? (recs > 16 ? recs - 16 : 0) : 0;
+            // is rejected in the prologue when such a page is visible).  (The row count is
+            // wave-uniform; readfirstlane keeps the descriptors in scalar registers.)
+            const int rs = __builtin_amdgcn_readfirstlane(recs);
+            const int recs0 = two_pages ? (rs < 16 ? rs : 16) : rs;
+            const int recs1 = two_pages ? (rs > 16 ? rs - 16 : 0) : 0;
             const int64_t in_page = static_cast<int64_t>(t0 & ((1 << pg.shift) - 1)) * row_bytes;
             const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<char *>(mbase + (pa >= 0 ? pa : 0) * page_bytes + in_page), 0,
@@ -1003,9 +1005,12 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
             const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<char *>(mbase + (pb >= 0 ? pb : 0) * page_bytes), 0,
                 pb >= 0 ? static_cast<int>(recs1 * row_bytes) : 0, kBufferFlags);
+            // (the page choice goes through readfirstlane as an integer: selected as a lane mask,
+            // the descriptor would land in vector registers and every copy would become a
+            // waterfall loop)
 #pragma unroll
             for (int jd = 0; jd < RS::kDmaPerWave; ++jd)
-                dma_to_lds16(dma_hi[jd] ? rb : ra, slot + dma_lds[jd], dma_off[jd]);
+                dma_to_lds16(__builtin_amdgcn_readfirstlane(dma_hi[jd] ? 1 : 0) ? rb : ra, slot + dma_lds[jd], dma_off[jd]);
         } else {
             const int nbytes = __builtin_amdgcn_readfirstlane(static_cast<int>(recs * row_bytes));
             const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc(
@@ -1043,29 +1048,25 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
             for (int j = 0; j < RS::kRound; ++j) issue_chunk(r * RS::kRound + j, half + j * RS::kSlotBytes, -1, -1);
         }
     };
-    // paged caches: stage the sequence's block-table entries first (L_cap = entries x page)
+    // paged caches: this thread's block-table entries are loaded first, together with the
+    // prologue's loads below, and staged in LDS before the first copies (L_cap = entries x page)
+    constexpr int kPgPer = kMaxPagesLds / (kWaves * kWave);
+    int pg_reg[PAGED ? kPgPer : 1];
     if constexpr (PAGED) {
         const int n_pg = L_cap >> pg.shift;
         const int32_t *trow = pg.tab + static_cast<int64_t>(b) * pg.stride;
-        int bad_min = 0x7fffffff;
-        for (int i = threadIdx.x; i < n_pg; i += kWaves * kWave) {
-            const int e = trow[i];
-            const bool ok = e >= 0 && e < pg.npages;
-            pg_lds[i] = ok ? e : -1;
-            bad_min = ok || i > bad_min ? bad_min : i;
+#pragma unroll
+        for (int u = 0; u < kPgPer; ++u) {
+            const int i = threadIdx.x + u * kWaves * kWave;
+            pg_reg[u] = i < n_pg ? trow[i] : -1;
         }
-        for (int o = 32; o >= 1; o >>= 1) {
-            const int y = __shfl_xor(bad_min, o, kWave);
-            bad_min = y < bad_min ? y : bad_min;
-        }
-        if (lane == 0) pg_bad[wave] = bad_min;
-        __syncthreads();
+    } else {
+        // the first two rounds go out before anything else is loaded or waited for
+        // (both are issued even when empty -- they then load nothing -- so the number of DMA
+        // operations in flight is the same on every path)
+        issue_round(0, ring0);
+        issue_round(1, ring1);
     }
-    // the first two rounds go out before anything else is loaded or waited for
-    // (both are issued even when empty -- they then load nothing -- so the number of DMA
-    // operations in flight is the same on every path)
-    issue_round(0, ring0);
-    issue_round(1, ring1);
 
     // ---- one round trip for the prologue, under the first copies: the sequence's scalars and,
     // independently of them, this lane's query fragments, node depths and first ancestor entries (row
@@ -1089,6 +1090,30 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         const int32_t *arow = anc + (static_cast<int64_t>(b) * R + j) * W;
 #pragma unroll
         for (int k = 0; k < kAncBatch; ++k) anc8[rt][k] = arow[k < W ? k : W - 1];
+    }
+    if constexpr (PAGED) {
+        // stage the entries (invalid ones as -1; each wave records the first invalid one),
+        // then issue the first two rounds from them
+        const int n_pg = L_cap >> pg.shift;
+        int bad_min = 0x7fffffff;
+#pragma unroll
+        for (int u = 0; u < kPgPer; ++u) {
+            const int i = threadIdx.x + u * kWaves * kWave;
+            if (i < n_pg) {
+                const int e = pg_reg[u];
+                const bool ok = e >= 0 && e < pg.npages;
+                pg_lds[i] = ok ? e : -1;
+                bad_min = ok || i > bad_min ? bad_min : i;
+            }
+        }
+        for (int o = 32; o >= 1; o >>= 1) {
+            const int y = __shfl_xor(bad_min, o, kWave);
+            bad_min = y < bad_min ? y : bad_min;
+        }
+        if (lane == 0) pg_bad[wave] = bad_min;
+        __syncthreads();
+        issue_round(0, ring0);
+        issue_round(1, ring1);
     }
 
     if (st == TMV_OK && (M < 0 || M > M_max || P < 0 || static_cast<int64_t>(P) + M > L_cap)) {

@@ -39,10 +39,13 @@ def _parity(ref, q, N, cost=None, l_ar=1.0, status=None):
 
 
 @pytest.mark.parametrize("D,V,N,levels", [(1, 5, 7, 4), (3, 100, 64, 6), (8, 20000, 128, None), (2, 50, 128, 3),
-                                          (4, 40000, 96, None), (8, 7, 128, 2)])
+                                          (4, 40000, 96, None), (8, 7, 128, 2), (3, 20000, 128, 3),
+                                          (2, 200000, 128, None), (1, 262144, 128, 5)])
 def test_random_marginals(ref, D, V, N, levels):
     """Shapes across the limits: fewer tokens than the budget (V = 5, 50, 7), several
-    16384-entry segments per row (V = 20000, 40000), coarse values with many equal scores."""
+    32768-entry segments per row (V = 40000, 200000, up to the 262144 maximum, whose rows
+    merge more keys than the merge holds one per thread), coarse values with many equal
+    scores (V = 20000 with 4 levels: more candidates per segment than one per thread)."""
     _case("best-first: D=%d V=%d N=%d levels=%s" % (D, V, N, levels))
     rng = np.random.default_rng(1200 + D * 7 + V)
     q = ti.draft_marginals(rng, 6, D, V, sigma=2.0, levels=levels)

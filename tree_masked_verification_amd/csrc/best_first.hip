@@ -10,11 +10,14 @@
 // implementation.
 //
 // Three launches:
-//   1. every 16384-entry segment of every q row: its K best entries, K = min(V, N_max).
-//      Keys are (value bits << 32 | ~token), all distinct.  The K-th largest of the
-//      threads' maxima is a threshold below which no top-K entry lies, and at most K
-//      threads hold entries above it: at most 16 K candidates, sorted in LDS.
-//   2. every row: its segments' lists merged (sorted in LDS) into the row's ranks.
+//   1. every 32768-entry segment of every q row (512 threads, 64 entries each): its K
+//      best entries, K = min(V, N_max).  Keys are (value bits << 32 | ~token), all
+//      distinct.  The K-th largest of the threads' maxima is a threshold below which no
+//      top-K entry lies, and at most K threads hold entries above it (at most 64 K
+//      candidates).  Sorts keep one key per thread: partners within a wave trade keys
+//      by lane shuffles, partners further apart through LDS.
+//   2. every row: its segments' lists merged (sorted, one key per thread when they fit)
+//      into the row's ranks.
 //   3. every sequence, one wave: best-first over rank tuples.  A node's successors in the
 //      order are its next sibling and its first child, so a frontier of at most N + 1
 //      entries holds the next node at every step; it lives in registers, four slots per
@@ -27,12 +30,14 @@ using tmv::kWave;
 
 constexpr int kBfMaxN = 128;                        // nodes per tree
 constexpr int kBfMaxD = 8;                          // positions (tree depth)
-constexpr int kSegThreads = 1024;
-constexpr int kSegPer = 16;                         // entries per thread of a segment
-constexpr int kSegLen = kSegThreads * kSegPer;      // entries per segment
-constexpr int kMaxSegs = 16;                        // segments per row: V <= 262144
+constexpr int kSegThreads = 512;
+constexpr int kSegPer = 64;                         // entries per thread of a segment
+constexpr int kSegLen = kSegThreads * kSegPer;      // entries per segment (32768)
+constexpr int kMaxSegs = 8;                         // segments per row: V <= 262144
 constexpr int kCand = kBfMaxN * kSegPer;            // candidates of a segment (at most)
-static_assert(kMaxSegs * kBfMaxN == kCand, "the row merge sorts as many keys as a segment");
+constexpr int kRowKeys = kMaxSegs * kBfMaxN;        // keys a row merge sorts (at most)
+constexpr int kBfBufferFlags = 0x00020000;          // raw buffer descriptor word 3 (gfx9 family)
+constexpr uint32_t kNoEntry = 0xFFFFFFFFu;          // value bits of a missing entry (q <= 1 has bits <= 0x3F800000)
 constexpr int kSlots = 4;                           // frontier slots per lane (4 * 64 >= kBfMaxN + 1)
 constexpr int kRankBits = 7;                        // rank < 128
 constexpr int kDepthShift = 56;                     // tuple key: depth << 56 | ranks, MSB first
@@ -81,6 +86,37 @@ __device__ int block_exclusive_scan(int v, int *wave_sums, int *total) {
     return before + incl - v;
 }
 
+// Sort the block's keys, one per thread (kSegThreads of them), in descending order; returns
+// the key that ends at position threadIdx.x.  Compare-exchange partners within a wave trade
+// keys by lane shuffles; partners kWave or more apart trade through LDS (xbuf: two buffers
+// of kSegThreads keys, alternated so each such stage needs one barrier).
+__device__ uint64_t block_bitonic_desc(uint64_t key, uint64_t *xbuf) {
+    const int i = threadIdx.x;
+    int buf = 0;
+    for (int k = 2; k <= kSegThreads; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            uint64_t other;
+            if (j >= kWave) {
+                uint64_t *x = xbuf + buf * kSegThreads;
+                x[i] = key;
+                __syncthreads();
+                other = x[i ^ j];
+                buf ^= 1;
+            } else {
+                const int lo = __shfl_xor(static_cast<int>(static_cast<uint32_t>(key)), j, kWave);
+                const int hi = __shfl_xor(static_cast<int>(static_cast<uint32_t>(key >> 32)), j, kWave);
+                other = (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+            }
+            // of the pair (i, i ^ j), the lower position keeps the larger key when the
+            // k-block runs descending ((i & k) == 0), the smaller one otherwise
+            const bool take_max = ((i & j) == 0) == ((i & k) == 0);
+            key = take_max ? (key > other ? key : other) : (key < other ? key : other);
+        }
+    }
+    __syncthreads();
+    return key;
+}
+
 __device__ __forceinline__ int pow2_at_least(int n) {
     int p = 1;
     while (p < n) p <<= 1;
@@ -93,6 +129,8 @@ bf_segment_kernel(int D, int V, int K, int nseg, const float *__restrict__ q, in
                   uint64_t *__restrict__ seg_keys, int32_t *__restrict__ seg_bad)
 {
     __shared__ uint64_t sh[kCand];
+    __shared__ uint64_t xbuf[2 * kSegThreads];
+    __shared__ uint64_t s_tau;
     __shared__ int wave_sums[kSegThreads / kWave];
     __shared__ int any_bad;
     const int tid = threadIdx.x;
@@ -102,41 +140,75 @@ bf_segment_kernel(int D, int V, int K, int nseg, const float *__restrict__ q, in
     const int x0 = seg * kSegLen;
     if (tid == 0) any_bad = 0;
 
-    // this thread's entries x0 + e * kSegThreads + tid (each load instruction is coalesced)
-    uint64_t key[kSegPer];
-    uint64_t mx = 0;
+    // this thread's entries x0 + e * kSegThreads + tid (each load instruction is coalesced),
+    // kept as value bits; an entry's key is rebuilt from its bits and position
+    // (buffer loads: one vector offset, the entry's 4 KiB step in a scalar offset)
+    const __amdgpu_buffer_rsrc_t qrs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(qr), 0, V * 4, kBfBufferFlags);
+    uint32_t vb[kSegPer];
     bool bad = false;
+#pragma unroll
+    for (int e = 0; e < kSegPer; ++e)
+        vb[e] = __builtin_amdgcn_raw_buffer_load_b32(qrs, (x0 + tid) * 4, e * kSegThreads * 4, 0);
 #pragma unroll
     for (int e = 0; e < kSegPer; ++e) {
         const int x = x0 + e * kSegThreads + tid;
-        key[e] = 0;
-        if (x < V) {
-            const float v = qr[x];
-            if (v >= 0.f && v <= 1.f) key[e] = rank_key(v, x);
-            else bad = true;                          // (also NaN)
-        }
-        mx = key[e] > mx ? key[e] : mx;
+        const float v = __uint_as_float(vb[e]);
+        const bool ok = v >= 0.f && v <= 1.f;         // (false for NaN)
+        bad = bad || (x < V && !ok);
+        vb[e] = x < V && ok ? vb[e] : kNoEntry;
     }
+    // the thread's largest key: largest value, then smallest token -- the first entry
+    // holding the largest value bits (entries are in token order)
+    uint32_t mv = kNoEntry;
+    int me = 0;
+#pragma unroll
+    for (int e = 0; e < kSegPer; ++e) {
+        const bool better = vb[e] != kNoEntry && (mv == kNoEntry || vb[e] > mv);
+        mv = better ? vb[e] : mv;
+        me = better ? e : me;
+    }
+    const uint64_t mx = mv == kNoEntry ? 0 : rank_key(__uint_as_float(mv), x0 + me * kSegThreads + tid);
+    // does entry e's key reach (th, tl), the two halves of a key?  (32-bit compares only)
+    auto reaches = [&](int e, uint32_t th, uint32_t tl) {
+        const uint32_t lo = 0xFFFFFFFFu - static_cast<uint32_t>(x0 + e * kSegThreads + tid);
+        return vb[e] != kNoEntry && (vb[e] > th || (vb[e] == th && lo >= tl));
+    };
     // the K-th largest thread maximum: no top-K entry lies below it
-    sh[tid] = mx;
-    bitonic_desc(sh, kSegThreads);
-    const uint64_t tau = sh[K - 1];
+    const uint64_t mx_sorted = block_bitonic_desc(mx, xbuf);
+    if (tid == K - 1) s_tau = mx_sorted;
     if (bad) any_bad = 1;
+    __syncthreads();
+    const uint64_t tau = s_tau;
+    // (tau = 0: fewer than K entries; every entry is a candidate)
+    const uint32_t tau_hi = static_cast<uint32_t>(tau >> 32), tau_lo = static_cast<uint32_t>(tau);
     // candidates: entries >= tau (only the K threads whose maximum reaches tau hold any)
     int c = 0;
+    uint32_t rm[kSegPer / 32] = {};              // bit e: entry e is a candidate
 #pragma unroll
-    for (int e = 0; e < kSegPer; ++e) c += (key[e] != 0 && key[e] >= tau) ? 1 : 0;
+    for (int e = 0; e < kSegPer; ++e) rm[e >> 5] |= (reaches(e, tau_hi, tau_lo) ? 1u : 0u) << (e & 31);
+#pragma unroll
+    for (int w = 0; w < kSegPer / 32; ++w) c += __popc(rm[w]);
     int total = 0;
     const int off = block_exclusive_scan(c, wave_sums, &total);   // (its barriers also end the reads of sh)
     int o = off;
 #pragma unroll
-    for (int e = 0; e < kSegPer; ++e)
-        if (key[e] != 0 && key[e] >= tau && o < kCand) sh[o++] = key[e];
-    const int n = pow2_at_least(total > K ? total : K);
-    for (int i = total + tid; i < n; i += kSegThreads) sh[i] = 0;
-    bitonic_desc(sh, n);
+    for (int e = 0; e < kSegPer; ++e) {
+        if (((rm[e >> 5] >> (e & 31)) & 1u) && o < kCand)
+            sh[o++] = rank_key(__uint_as_float(vb[e]), x0 + e * kSegThreads + tid);
+    }
     uint64_t *out = seg_keys + (static_cast<int64_t>(row) * nseg + seg) * K;
-    for (int r = tid; r < K; r += kSegThreads) out[r] = sh[r];
+    if (total <= kSegThreads) {
+        // (the usual case) one candidate per thread, the rest padded with 0
+        __syncthreads();
+        const uint64_t c = block_bitonic_desc(tid < total ? sh[tid] : 0, xbuf);
+        if (tid < K) out[tid] = c;
+    } else {
+        const int n = pow2_at_least(total);
+        for (int i = total + tid; i < n; i += kSegThreads) sh[i] = 0;
+        bitonic_desc(sh, n);
+        for (int r = tid; r < K; r += kSegThreads) out[r] = sh[r];
+    }
     if (tid == 0) seg_bad[static_cast<int64_t>(row) * nseg + seg] = any_bad;
 }
 
@@ -145,16 +217,24 @@ __global__ void __launch_bounds__(kSegThreads)
 bf_row_kernel(int K, int nseg, const uint64_t *__restrict__ seg_keys, const int32_t *__restrict__ seg_bad,
               int32_t *__restrict__ rank_tok, float *__restrict__ rank_val, int32_t *__restrict__ row_bad)
 {
-    __shared__ uint64_t sh[kCand];
+    __shared__ uint64_t xbuf[2 * kSegThreads];
+    __shared__ uint64_t sh[kRowKeys];
     const int tid = threadIdx.x, row = blockIdx.x;
-    const int m = nseg * K;                           // <= kMaxSegs * kBfMaxN = kCand
-    const int n = pow2_at_least(m);
-    for (int i = tid; i < n; i += kSegThreads) sh[i] = i < m ? seg_keys[static_cast<int64_t>(row) * m + i] : 0;
-    bitonic_desc(sh, n);
-    for (int r = tid; r < K; r += kSegThreads) {
-        const uint64_t key = sh[r];
+    const int m = nseg * K;                           // <= kRowKeys
+    const uint64_t *keys = seg_keys + static_cast<int64_t>(row) * m;
+    auto put = [&](int r, uint64_t key) {
         rank_tok[static_cast<int64_t>(row) * K + r] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key));
         rank_val[static_cast<int64_t>(row) * K + r] = __uint_as_float(static_cast<uint32_t>(key >> 32));
+    };
+    if (m <= kSegThreads) {
+        // one key per thread, the rest padded with 0
+        const uint64_t c = block_bitonic_desc(tid < m ? keys[tid] : 0, xbuf);
+        if (tid < K) put(tid, c);
+    } else {
+        const int n = pow2_at_least(m);
+        for (int i = tid; i < n; i += kSegThreads) sh[i] = i < m ? keys[i] : 0;
+        bitonic_desc(sh, n);
+        for (int r = tid; r < K; r += kSegThreads) put(r, sh[r]);
     }
     if (tid == 0) {
         int bad = 0;

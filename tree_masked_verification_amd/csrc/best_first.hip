@@ -317,6 +317,19 @@ __device__ __forceinline__ void wave_take(double &r, uint64_t &k, int &s) {
     swap_take<true>(r, k, s);
 }
 
+// the wave's largest value, in every lane (same exchange pattern as wave_take)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+    v = mx(v, dpp32<0xB1>(v));
+    v = mx(v, dpp32<0x4E>(v));
+    v = mx(v, dpp32<0x141>(v));
+    v = mx(v, dpp32<0x140>(v));
+    const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = mx(a[0], a[1]);
+    const auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return mx(c[0], c[1]);
+}
+
 __global__ void __launch_bounds__(kWave)
 bf_expand_kernel(int D, int K, int N_max, const int32_t *__restrict__ rank_tok, const float *__restrict__ rank_val,
                  const int32_t *__restrict__ row_bad, const double *__restrict__ cost, double l_ar,
@@ -372,29 +385,57 @@ bf_expand_kernel(int D, int K, int N_max, const int32_t *__restrict__ rank_tok, 
     int used = 1;                                    // slots handed out so far (wave-uniform)
     int n = 0;
     while (n < N_max) {
-        // this lane's earliest live slot, then the wave's
-        double br = 0.0;
-        uint64_t bk = 0;
-        int bs = -1;
+        // the earliest live slot.  Scores are positive doubles, so their upper 32 bits order
+        // them up to ties there: the wave's largest upper word (+1, 0 for a dead slot) picks
+        // the slot when one slot alone holds it; otherwise the exact comparison runs over
+        // the slots that hold it.
+        uint32_t top = 0;
 #pragma unroll
-        for (int j = 0; j < kSlots; ++j)
-            if (f_live[j]) take(br, bk, bs, f_rho[j], f_key[j], j * kWave + lane);
-        wave_take(br, bk, bs);
-        bs = __builtin_amdgcn_readfirstlane(bs);
-        if (bs < 0) break;                           // every possible node is in the tree
-        const int owner = bs % kWave, js = bs / kWave;
-        double prho = 0.0;
+        for (int j = 0; j < kSlots; ++j) {
+            const uint32_t h = f_live[j] ? hi32(dbits(f_rho[j])) + 1 : 0;
+            top = h > top ? h : top;
+        }
+        top = __builtin_amdgcn_readfirstlane(wave_max_u32(top));
+        if (top == 0) break;                         // every possible node is in the tree
+        uint64_t hold[kSlots];
+        int n_hold = 0, js = 0;
+#pragma unroll
+        for (int j = 0; j < kSlots; ++j) {
+            hold[j] = __ballot(f_live[j] && hi32(dbits(f_rho[j])) + 1 == top);
+            n_hold += __popcll(hold[j]);
+            js = hold[j] != 0 ? j : js;
+        }
+        int owner;
+        if (n_hold == 1) {
+            owner = __ffsll(static_cast<long long>(hold[js])) - 1;
+        } else {
+            double br = 0.0;
+            uint64_t bk = 0;
+            int bs = -1;
+#pragma unroll
+            for (int j = 0; j < kSlots; ++j)
+                if ((hold[j] >> lane) & 1ull) take(br, bk, bs, f_rho[j], f_key[j], j * kWave + lane);
+            wave_take(br, bk, bs);
+            bs = __builtin_amdgcn_readfirstlane(bs);
+            owner = bs % kWave;
+            js = bs / kWave;
+        }
+        double prho = 0.0, br = 0.0;
+        uint64_t bk = 0;
         int par = 0;
 #pragma unroll
         for (int j = 0; j < kSlots; ++j) {
             prho = j == js ? f_prho[j] : prho;
+            br = j == js ? f_rho[j] : br;
+            bk = j == js ? f_key[j] : bk;
             par = j == js ? f_par[j] : par;
         }
         prho = from_bits(join(__builtin_amdgcn_readlane(hi32(dbits(prho)), owner),
                               __builtin_amdgcn_readlane(lo32(dbits(prho)), owner)));
+        br = from_bits(join(__builtin_amdgcn_readlane(hi32(dbits(br)), owner),
+                            __builtin_amdgcn_readlane(lo32(dbits(br)), owner)));
+        bk = join(__builtin_amdgcn_readlane(hi32(bk), owner), __builtin_amdgcn_readlane(lo32(bk), owner));
         par = __builtin_amdgcn_readlane(par, owner);
-        br = from_bits(join(__builtin_amdgcn_readfirstlane(hi32(dbits(br))), __builtin_amdgcn_readfirstlane(lo32(dbits(br)))));
-        bk = join(__builtin_amdgcn_readfirstlane(hi32(bk)), __builtin_amdgcn_readfirstlane(lo32(bk)));
         ++n;
         const int d = static_cast<int>(bk >> kDepthShift);
         const int sh_r = kDepthShift - kRankBits * d;    // bit offset of the last position's rank

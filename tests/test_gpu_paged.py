@@ -168,3 +168,26 @@ def test_paged_commit(ref, page_size, nl):
             if pg < 0:
                 continue
             assert np.array_equal(kg[:, pg, :, r], kr[:, b, :, t]) and np.array_equal(vg[:, pg, :, r], vr[:, b, :, t])
+
+
+@pytest.mark.parametrize("plan", ["2:3", "4:1", "4:2", "1:5"])
+def test_paged_attention_launch_plans(ref, plan, monkeypatch):
+    """Every row-group width of the paged kernel (the plan override), against the oracle and
+    bit-identical to the contiguous kernel under the same plan."""
+    _case("paged attention: plan %s" % plan)
+    monkeypatch.setenv("TMV_ATTN_PLAN", plan)
+    w = small_attention_workload(290, 2, 16, 2, 128, 40, [600, 70], [40, 33], q_scale=3.0)
+    dev, out = _paged_attention(w, 16, np.random.default_rng(291))
+    _check_against_oracle(ref, w, dev, out)
+    L = -(-w.L_cap // 16) * 16
+    assert np.array_equal(out, _contiguous_bits(_padded(w, L)))
+
+
+def test_paged_attention_deep_trees(ref):
+    """Trees deeper than the ancestor entries fetched in the prologue (the deep kernels)."""
+    _case("paged attention: a 48-deep chain and a random tree, 32-token pages")
+    w = small_attention_workload(295, 2, 8, 2, 128, 48, [300, 45], [48, 30], q_scale=3.0, max_depth=48)
+    w.parents[0] = ti.tree_chain(48)
+    dev, out = _paged_attention(w, 32, np.random.default_rng(296))
+    _check_against_oracle(ref, w, dev, out)
+    assert int(dev.tables()[1].max()) > 16

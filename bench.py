@@ -27,6 +27,9 @@ Timed regions (both after --warmup untimed steps):
      the step (it builds the trees a step verifies; it is not part of the step).
   4. workloads 2-4: the paged-cache attention and commit on the same sets (K/V in pools
      of 16-token pages at random places), timed like region 2, reported as "paged".
+  5. a streaming ceiling of the device (the better of torch.amax over 4 GiB and a 2 GiB
+     device copy), reported as "stream_read_ceiling"; every kernel's GB/s is also given as
+     a fraction of it.
 The oracle (tests-only CPU implementation) is timed on a bounded sample of the default
 workload for the cpu_baseline field.
 
@@ -198,6 +201,16 @@ def traffic_from_profiles(kernel_key, workload):
 
 
 # ---------------------------------------------------------------- CPU baseline
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return "%s (%d logical CPUs)" % (line.split(":", 1)[1].strip(), os.cpu_count() or 0)
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, budget_s):
     """The oracle, as it stands, on whole verify steps of the same workload."""
     import oracle
@@ -216,7 +229,7 @@ def cpu_baseline(w, budget_s):
         if el >= budget_s or steps >= 1000:
             break
     node_tokens = steps * int(w.n_nodes.sum())
-    return {"value": node_tokens / el, "unit": "node-tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": node_tokens / el, "unit": "node-tokens/s", "cores": 1, "kind": "oracle", "cpu": cpu_model(),
             "sample": "%d full verify steps of the same workload (build, attention over all %d query rows, "
                       "greedy accept over %d x %d logits, commit), single thread, %.1f s"
                       % (steps, int(w.n_nodes.sum()) * w.Hq, int(w.n_nodes.sum()) + w.B, w.V, el),
@@ -265,6 +278,36 @@ def time_best_first(torch, tmv, ti, stream, B=16, D=8, V=128256, N=128):
                                 "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
                                 "shape": "B%d positions %d vocab %d budget %d" % (B, D, V, N),
                                 "input_sets": n_sets}}
+
+
+def stream_read_ceiling(torch, stream, nbytes=4 << 30, reps=5):
+    """A measured streaming ceiling of this device, the better of two plain library kernels,
+    best of `reps` each, HIP events on the launch stream: the maximum over a 4 GiB fp32 tensor
+    (every byte read once) and a 2 GiB device-to-device copy (bytes read + bytes written)."""
+    def best_ms(fn):
+        best = None
+        with torch.cuda.stream(stream):
+            fn()
+            for _ in range(reps):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                e1.synchronize()
+                ms = e0.elapsed_time(e1)
+                best = ms if best is None else min(best, ms)
+        return best
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    read = nbytes / (best_ms(lambda: torch.amax(x)) * 1e-3) / 1e9
+    half = x[: x.numel() // 2]
+    y = torch.empty_like(half)
+    copy = nbytes / (best_ms(lambda: y.copy_(half)) * 1e-3) / 1e9
+    del x, y, half
+    torch.cuda.empty_cache()
+    return {"GB/s": round(max(read, copy), 1), "read_GB/s": round(read, 1), "copy_GB/s": round(copy, 1),
+            "how": "max of torch.amax over 4 GiB fp32 (bytes read) and a 2 GiB device copy (bytes read + written), "
+                   "best of %d each" % reps}
 
 
 def time_paged(torch, tmv, sets, stream, durations, page_size=16, reps=None):
@@ -599,6 +642,9 @@ def main():
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(name, c)}
 
     dominant = max((k for k in durations if k != "build"), key=lambda k: durations[k])
+    ceiling = stream_read_ceiling(torch, stream)
+    for k in kernels.values():
+        k["frac_stream_ceiling"] = round(k["GB/s"] / ceiling["GB/s"], 4)
     drafting = time_best_first(torch, tmv, ti, stream) if c == 3 else None
     paged = time_paged(torch, tmv, sets, stream, durations) if c in (2, 3, 4) else None
     if paged:
@@ -637,6 +683,7 @@ def main():
         "config": config,
         "roofline": roofline(dominant),
         "attention_roofline": roofline("attention") if "attention" in durations else None,
+        "stream_read_ceiling": ceiling,
         "kernels": kernels,
         "drafting": drafting,
         "paged": paged,

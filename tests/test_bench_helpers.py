@@ -61,3 +61,23 @@ def test_budget_sweep_inputs():
         assert depth.max() <= D and w.D_max == D
         assert w.L_cap >= w.prefix[0] + M and w.logits.shape == (1, M + 1, 128256)
         assert (w.B, w.Hq, w.Hkv, w.d, w.mode) == (1, 32, 8, 128, "greedy")
+
+
+def test_paged_layout_places_every_slot():
+    """The page pools hold each sequence's slot t at page table[b][t // page], row t % page,
+    for every layer and head; aliased table entries point at the source sequence's pages;
+    the table is a permutation of distinct pages apart from the aliases."""
+    rng = np.random.default_rng(11)
+    k = rng.integers(0, 65536, size=(2, 3, 2, 70, 8)).astype(np.uint16)       # [layer][B][H][L][d]
+    v = rng.integers(0, 65536, size=(2, 3, 2, 70, 8)).astype(np.uint16)
+    k[:, 2, :, :32] = k[:, 0, :, :32]
+    v[:, 2, :, :32] = v[:, 0, :, :32]
+    (kp, vp), table = ti.paged_layout(rng, [k, v], 16, spare=2, alias=((0, 2, 2),))
+    assert kp.shape == (2, 3 * 5 + 2, 2, 16, 8) and table.shape == (3, 5)
+    for b in range(3):
+        for t in range(70):
+            pg, r = table[b, t // 16], t % 16
+            assert np.array_equal(kp[:, pg, :, r], k[:, b, :, t]) and np.array_equal(vp[:, pg, :, r], v[:, b, :, t])
+    assert np.array_equal(table[2, :2], table[0, :2])
+    rest = np.concatenate([table[0], table[1], table[2, 2:]])
+    assert len(set(rest.tolist())) == rest.size and rest.max() < kp.shape[1]

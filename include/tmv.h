@@ -150,6 +150,30 @@ int tmv_tree_verify_attention(int dtype, int B, int M_max, int D_max, int Hq, in
                               void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * tmv_tree_verify_attention_plan -- tmv_tree_verify_attention with its launch plan pinned
+ * (for tuning sweeps and tests that must exercise every plan; results agree with the
+ * library's own choice within the attention tolerance, and are bit-identical across
+ * reruns of one plan).  The plan of the bf16 kernels is (rows sharing each staged K/V
+ * chunk, token splits per row block):
+ *   rows_per_group  d = 128: 64, 128 or 256; d = 64: 32 or 128; 0 = the library's choice.
+ *   splits          1 .. 16; 0 = the library's choice.  (Split-KV is dropped when the
+ *                   call has 256 or more row blocks.)
+ * Other values are ignored (the library's choice).  fp32 calls have no plan.  The
+ * workspace must hold tmv_tree_verify_attention_plan_workspace() bytes for the same plan.
+ */
+size_t tmv_tree_verify_attention_plan_workspace(int dtype, int B, int M_max, int Hq, int Hkv, int d, int L_cap,
+                                                int rows_per_group, int splits);
+int tmv_tree_verify_attention_plan(int dtype, int B, int M_max, int D_max, int Hq, int Hkv, int d,
+                                   const void *q, const int64_t *q_stride,
+                                   const void *k_cache, const void *v_cache,
+                                   const int64_t *kv_stride, int L_cap,
+                                   const int32_t *prefix_len, const int32_t *n_nodes,
+                                   const int32_t *anc, const int32_t *depth, int32_t *status,
+                                   float scale, void *out, const int64_t *o_stride,
+                                   int rows_per_group, int splits,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * tmv_tree_verify_attention_paged -- the same attention over a paged K/V cache.
  * Defined by the runtime-memory question of "Speculative Decoding Hierarquico: Medusa,
  * EAGLE-2 e Multi-Token Prediction" (vLLM's PagedAttention keeps the cache in pages
@@ -183,6 +207,19 @@ int tmv_tree_verify_attention_paged(int dtype, int B, int M_max, int D_max, int 
                                     const int32_t *anc, const int32_t *depth, int32_t *status,
                                     float scale, void *out, const int64_t *o_stride,
                                     void *workspace, size_t workspace_bytes, void *stream);
+/* The paged call with its launch plan pinned, as tmv_tree_verify_attention_plan. */
+size_t tmv_tree_verify_attention_paged_plan_workspace(int B, int M_max, int Hq, int Hkv, int d, int page_size,
+                                                      int max_blocks, int rows_per_group, int splits);
+int tmv_tree_verify_attention_paged_plan(int dtype, int B, int M_max, int D_max, int Hq, int Hkv, int d,
+                                         const void *q, const int64_t *q_stride,
+                                         const void *k_pages, const void *v_pages,
+                                         const int64_t *page_stride, int num_pages, int page_size,
+                                         const int32_t *block_table, int64_t table_stride, int max_blocks,
+                                         const int32_t *prefix_len, const int32_t *n_nodes,
+                                         const int32_t *anc, const int32_t *depth, int32_t *status,
+                                         float scale, void *out, const int64_t *o_stride,
+                                         int rows_per_group, int splits,
+                                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * tmv_tree_accept -- choose the accepted path and the next token.

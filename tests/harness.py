@@ -62,9 +62,9 @@ class DeviceStep:
         self.tmv.tree_build_ancestors(self.parents if parents is None else parents, self.n_nodes, self.anc,
                                       self.depth, self.status, parent_format=parent_format, valid=valid)
 
-    def attention(self, workspace=None):
+    def attention(self, workspace=None, plan=None):
         self.tmv.tree_verify_attention(self.q, self.k, self.v, self.prefix, self.n_nodes, self.anc, self.depth,
-                                       self.status, self.out, scale=self.w.scale, workspace=workspace)
+                                       self.status, self.out, scale=self.w.scale, workspace=workspace, plan=plan)
 
     def accept(self, workspace=None):
         w = self.w

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     import tree_masked_verification_amd as tmv
-    assert tmv.abi_version() == 1
+    assert tmv.abi_version() == 2
     names = {tmv.status_string(c) for c in range(8)}
     assert len(names) == 8 and tmv.status_string(99) == "unknown status"
 

@@ -28,7 +28,7 @@ def _padded(w, L):
                        w.prefix, w.tokens, w.q, pad(w.k), pad(w.v))
 
 
-def _paged_attention(w, page_size, rng, alias=(), table_edit=None):
+def _paged_attention(w, page_size, rng, alias=(), table_edit=None, plan=None):
     """Runs tree_verify_attention_paged on w's caches laid out in pages; returns the step
     (tables, status) and the output bits."""
     import tree_masked_verification_amd as tmv
@@ -41,7 +41,7 @@ def _paged_attention(w, page_size, rng, alias=(), table_edit=None):
     tab = torch.from_numpy(table).cuda()
     dev.out.fill_(float("nan"))
     tmv.tree_verify_attention_paged(dev.q, kpd, vpd, tab, dev.prefix, dev.n_nodes, dev.anc, dev.depth, dev.status,
-                                    dev.out, scale=w.scale)
+                                    dev.out, scale=w.scale, plan=plan)
     torch.cuda.synchronize()
     return dev, host_bits(dev.out)
 
@@ -57,11 +57,11 @@ def _check_against_oracle(ref, w, dev, out):
     assert not np.any(np.isnan(ti.bf16_to_f32(out)))
 
 
-def _contiguous_bits(w):
+def _contiguous_bits(w, plan=None):
     dev = DeviceStep(w)
     dev.build()
     dev.out.fill_(float("nan"))
-    dev.attention()
+    dev.attention(plan=plan)
     torch.cuda.synchronize()
     return host_bits(dev.out)
 
@@ -170,17 +170,16 @@ def test_paged_commit(ref, page_size, nl):
             assert np.array_equal(kg[:, pg, :, r], kr[:, b, :, t]) and np.array_equal(vg[:, pg, :, r], vr[:, b, :, t])
 
 
-@pytest.mark.parametrize("plan", ["2:3", "4:1", "4:2", "1:5"])
-def test_paged_attention_launch_plans(ref, plan, monkeypatch):
-    """Every row-group width of the paged kernel (the plan override), against the oracle and
+@pytest.mark.parametrize("plan", [(64, 3), (128, 1), (128, 2), (256, 5), (64, 16)])
+def test_paged_attention_launch_plans(ref, plan):
+    """Every row-group width of the paged kernel (a pinned plan), against the oracle and
     bit-identical to the contiguous kernel under the same plan."""
-    _case("paged attention: plan %s" % plan)
-    monkeypatch.setenv("TMV_ATTN_PLAN", plan)
+    _case("paged attention: plan %s" % (plan,))
     w = small_attention_workload(290, 2, 16, 2, 128, 40, [600, 70], [40, 33], q_scale=3.0)
-    dev, out = _paged_attention(w, 16, np.random.default_rng(291))
+    dev, out = _paged_attention(w, 16, np.random.default_rng(291), plan=plan)
     _check_against_oracle(ref, w, dev, out)
     L = -(-w.L_cap // 16) * 16
-    assert np.array_equal(out, _contiguous_bits(_padded(w, L)))
+    assert np.array_equal(out, _contiguous_bits(_padded(w, L), plan=plan))
 
 
 def test_paged_attention_deep_trees(ref):

@@ -44,6 +44,10 @@ _lib.tmv_tree_verify_attention_workspace.argtypes = [_I, _I, _I, _I, _I, _I, _I]
 _lib.tmv_tree_verify_attention_workspace.restype = _SZ
 _lib.tmv_tree_verify_attention.argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P,
                                            _F, _P, _P, _P, _SZ, _P]
+_lib.tmv_tree_verify_attention_plan_workspace.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _I]
+_lib.tmv_tree_verify_attention_plan_workspace.restype = _SZ
+_lib.tmv_tree_verify_attention_plan.argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P,
+                                                _F, _P, _P, _I, _I, _P, _SZ, _P]
 _lib.tmv_tree_accept_workspace.argtypes = [_I, _I, _I, _I]
 _lib.tmv_tree_accept_workspace.restype = _SZ
 _lib.tmv_tree_accept.argtypes = [_I, _I, _I, _I, _I, _P, _I, _P, _I64, _I64, _P, _I64, _I64, _U64, _U64,
@@ -53,6 +57,10 @@ _lib.tmv_tree_verify_attention_paged_workspace.argtypes = [_I, _I, _I, _I, _I, _
 _lib.tmv_tree_verify_attention_paged_workspace.restype = _SZ
 _lib.tmv_tree_verify_attention_paged.argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _I64, _I,
                                                  _P, _P, _P, _P, _P, _F, _P, _P, _P, _SZ, _P]
+_lib.tmv_tree_verify_attention_paged_plan_workspace.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _I]
+_lib.tmv_tree_verify_attention_paged_plan_workspace.restype = _SZ
+_lib.tmv_tree_verify_attention_paged_plan.argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _I64,
+                                                      _I, _P, _P, _P, _P, _P, _F, _P, _P, _I, _I, _P, _SZ, _P]
 _lib.tmv_kv_commit_path_paged.argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _I64, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,
                                           _P, _P, _P]
 _lib.tmv_tree_best_first_workspace.argtypes = [_I, _I, _I, _I]
@@ -64,7 +72,9 @@ EXPORTED = ("tmv_status_string", "tmv_abi_version", "tmv_tree_build_ancestors",
             "tmv_tree_verify_attention_workspace", "tmv_tree_verify_attention", "tmv_tree_accept_workspace",
             "tmv_tree_accept", "tmv_kv_commit_path", "tmv_tree_best_first_workspace", "tmv_tree_best_first",
             "tmv_tree_verify_attention_paged_workspace", "tmv_tree_verify_attention_paged",
-            "tmv_kv_commit_path_paged")
+            "tmv_kv_commit_path_paged", "tmv_tree_verify_attention_plan_workspace",
+            "tmv_tree_verify_attention_plan", "tmv_tree_verify_attention_paged_plan_workspace",
+            "tmv_tree_verify_attention_paged_plan")
 
 
 class TmvError(RuntimeError):
@@ -90,9 +100,32 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _torch_stream(stream):
+    return torch.cuda.current_stream() if stream is None else stream
+
+
 def _stream(stream):
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    return ctypes.c_void_p(_torch_stream(stream).cuda_stream)
+
+
+def _temp_workspace(nbytes, device, stream, zero):
+    """A workspace for one call, allocated (and zero-filled) on the call's own stream: the
+    fill is ordered before the launch, and the caching allocator does not hand the block
+    to other work until everything queued on that stream up to its release has run."""
+    with torch.cuda.stream(_torch_stream(stream)):
+        alloc = torch.zeros if zero else torch.empty
+        return alloc(max(256, int(nbytes)), dtype=torch.uint8, device=device)
+
+
+def _shape(t, shape, name):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _vec(n, name, *ts):
+    for t in ts:
+        if t is not None and t.numel() != n:
+            raise ValueError("%s: expected %d entries, got %d" % (name, n, t.numel()))
 
 
 def _strides(t, dims):
@@ -127,6 +160,10 @@ def tree_build_ancestors(parents, n_nodes, anc, depth, status, parent_format=PAR
     B, R, W = anc.shape
     if valid is not None and (valid.dtype != torch.uint8 or not valid.is_contiguous()):
         raise TypeError("valid must be contiguous uint8")
+    _shape(parents, (B, R if parent_format == PARENTS_VROOT else R - 1), "parents")
+    _shape(depth, (B, R), "depth")
+    _shape(valid, (B, R), "valid")
+    _vec(B, "n_nodes / status", n_nodes, status)
     _check(_lib.tmv_tree_build_ancestors(B, R - 1, W - 1, parent_format, _ptr(parents), _ptr(valid), _ptr(n_nodes),
                                          _ptr(anc), _ptr(depth), _ptr(status), _stream(stream)),
            "tree_build_ancestors")
@@ -137,9 +174,22 @@ def tree_verify_attention_workspace(dtype, B, M_max, Hq, Hkv, d, L_cap) -> int:
     return int(_lib.tmv_tree_verify_attention_workspace(dtype, B, M_max, Hq, Hkv, d, L_cap))
 
 
+def tree_verify_attention_plan_workspace(dtype, B, M_max, Hq, Hkv, d, L_cap, rows_per_group, splits) -> int:
+    return int(_lib.tmv_tree_verify_attention_plan_workspace(dtype, B, M_max, Hq, Hkv, d, L_cap, rows_per_group,
+                                                             splits))
+
+
+def _check_tree_tables(B, M_max, anc, depth, what):
+    if anc.dim() != 3 or anc.shape[0] != B or anc.shape[1] != M_max + 1:
+        raise ValueError("%s: anc must be [B][M_max+1][D_max+1]" % what)
+    _shape(depth, (B, M_max + 1), "depth")
+
+
 def tree_verify_attention(q, k_cache, v_cache, prefix_len, n_nodes, anc, depth, status, out, scale=None,
-                          workspace=None, stream=None):
-    """q, out [B][M_max][Hq][d]; k_cache, v_cache [B][Hkv][L_cap][d] (same dtype, d contiguous)."""
+                          workspace=None, stream=None, plan=None):
+    """q, out [B][M_max][Hq][d]; k_cache, v_cache [B][Hkv][L_cap][d] (same dtype, d contiguous).
+    plan = (rows per group, token splits) pins the launch plan (tuning and tests); None lets
+    the library choose."""
     _i32(prefix_len, n_nodes, anc, depth, status)
     dt = _dtype_code(q)
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype or out.dtype != q.dtype:
@@ -147,21 +197,28 @@ def tree_verify_attention(q, k_cache, v_cache, prefix_len, n_nodes, anc, depth, 
     if k_cache.shape != v_cache.shape or k_cache.stride() != v_cache.stride():
         raise ValueError("k_cache and v_cache must have the same shape and strides")
     B, M_max, Hq, d = q.shape
+    if k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[3] != d:
+        raise ValueError("k_cache must be [B][Hkv][L_cap][d]")
     Hkv, L_cap = k_cache.shape[1], k_cache.shape[2]
     if tuple(out.shape) != tuple(q.shape) or q.stride(3) != 1 or k_cache.stride(3) != 1 or out.stride(3) != 1:
         raise ValueError("bad q / out / cache layout")
+    _check_tree_tables(B, M_max, anc, depth, "tree_verify_attention")
+    _vec(B, "prefix_len / n_nodes / status", prefix_len, n_nodes, status)
     D_max = anc.shape[2] - 1
     if scale is None:
         scale = 1.0 / float(d) ** 0.5
+    rows, splits = (0, 0) if plan is None else (int(plan[0]), int(plan[1]))
     if workspace is None:
-        workspace = torch.zeros(tree_verify_attention_workspace(dt, B, M_max, Hq, Hkv, d, L_cap),
-                                dtype=torch.uint8, device=q.device)
-    _check(_lib.tmv_tree_verify_attention(dt, B, M_max, D_max, Hq, Hkv, d, _ptr(q), _strides(q, (0, 1, 2)),
-                                          _ptr(k_cache), _ptr(v_cache), _strides(k_cache, (0, 1, 2)), L_cap,
-                                          _ptr(prefix_len), _ptr(n_nodes), _ptr(anc), _ptr(depth), _ptr(status),
-                                          float(scale), _ptr(out), _strides(out, (0, 1, 2)), _ptr(workspace),
-                                          workspace.numel() * workspace.element_size(), _stream(stream)),
-           "tree_verify_attention")
+        workspace = _temp_workspace(tree_verify_attention_plan_workspace(dt, B, M_max, Hq, Hkv, d, L_cap, rows, splits),
+                                    q.device, stream, zero=True)
+    args = (dt, B, M_max, D_max, Hq, Hkv, d, _ptr(q), _strides(q, (0, 1, 2)), _ptr(k_cache), _ptr(v_cache),
+            _strides(k_cache, (0, 1, 2)), L_cap, _ptr(prefix_len), _ptr(n_nodes), _ptr(anc), _ptr(depth), _ptr(status),
+            float(scale), _ptr(out), _strides(out, (0, 1, 2)))
+    tail = (_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if plan is None:
+        _check(_lib.tmv_tree_verify_attention(*args, *tail), "tree_verify_attention")
+    else:
+        _check(_lib.tmv_tree_verify_attention_plan(*args, rows, splits, *tail), "tree_verify_attention_plan")
 
 
 def tree_verify_attention_paged_workspace(B, M_max, Hq, Hkv, d, page_size, max_blocks) -> int:
@@ -169,7 +226,7 @@ def tree_verify_attention_paged_workspace(B, M_max, Hq, Hkv, d, page_size, max_b
 
 
 def tree_verify_attention_paged(q, k_pages, v_pages, block_table, prefix_len, n_nodes, anc, depth, status, out,
-                                scale=None, workspace=None, stream=None):
+                                scale=None, workspace=None, stream=None, plan=None):
     """q, out [B][M_max][Hq][d] bf16; k_pages, v_pages [num_pages][Hkv][page_size][d] bf16;
     block_table int32 [B][max_blocks] (logical slot t of sequence b: page block_table[b][t //
     page_size], row t % page_size)."""
@@ -183,20 +240,27 @@ def tree_verify_attention_paged(q, k_pages, v_pages, block_table, prefix_len, n_
     max_blocks = block_table.shape[1]
     if tuple(out.shape) != tuple(q.shape) or q.stride(3) != 1 or k_pages.stride(3) != 1 or out.stride(3) != 1:
         raise ValueError("bad q / out / page layout")
+    if k_pages.dim() != 4 or k_pages.shape[3] != d or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("k_pages must be [num_pages][Hkv][page_size][d] and block_table [B][max_blocks]")
+    _check_tree_tables(B, M_max, anc, depth, "tree_verify_attention_paged")
+    _vec(B, "prefix_len / n_nodes / status", prefix_len, n_nodes, status)
     D_max = anc.shape[2] - 1
     if scale is None:
         scale = 1.0 / float(d) ** 0.5
+    rows, splits = (0, 0) if plan is None else (int(plan[0]), int(plan[1]))
     if workspace is None:
-        workspace = torch.zeros(tree_verify_attention_paged_workspace(B, M_max, Hq, Hkv, d, page_size, max_blocks),
-                                dtype=torch.uint8, device=q.device)
-    _check(_lib.tmv_tree_verify_attention_paged(_dtype_code(q), B, M_max, D_max, Hq, Hkv, d, _ptr(q),
-                                                _strides(q, (0, 1, 2)), _ptr(k_pages), _ptr(v_pages),
-                                                _strides(k_pages, (0, 1, 2)), num_pages, page_size, _ptr(block_table),
-                                                block_table.stride(0), max_blocks, _ptr(prefix_len), _ptr(n_nodes),
-                                                _ptr(anc), _ptr(depth), _ptr(status), float(scale), _ptr(out),
-                                                _strides(out, (0, 1, 2)), _ptr(workspace),
-                                                workspace.numel() * workspace.element_size(), _stream(stream)),
-           "tree_verify_attention_paged")
+        workspace = _temp_workspace(_lib.tmv_tree_verify_attention_paged_plan_workspace(
+            B, M_max, Hq, Hkv, d, page_size, max_blocks, rows, splits), q.device, stream, zero=True)
+    args = (_dtype_code(q), B, M_max, D_max, Hq, Hkv, d, _ptr(q), _strides(q, (0, 1, 2)), _ptr(k_pages),
+            _ptr(v_pages), _strides(k_pages, (0, 1, 2)), num_pages, page_size, _ptr(block_table), block_table.stride(0),
+            max_blocks, _ptr(prefix_len), _ptr(n_nodes), _ptr(anc), _ptr(depth), _ptr(status), float(scale), _ptr(out),
+            _strides(out, (0, 1, 2)))
+    tail = (_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if plan is None:
+        _check(_lib.tmv_tree_verify_attention_paged(*args, *tail), "tree_verify_attention_paged")
+    else:
+        _check(_lib.tmv_tree_verify_attention_paged_plan(*args, rows, splits, *tail),
+               "tree_verify_attention_paged_plan")
 
 
 # ------------------------------------------------------------------------ stage 3
@@ -210,7 +274,11 @@ def tree_accept(mode, tokens, teacher, n_nodes, anc, depth, status, accept_len, 
     same shape (SAMPLE).  Outputs accept_len [B], path [B][D_max], next_token [B]."""
     _i32(tokens, n_nodes, anc, depth, status, accept_len, path, next_token)
     B, R, V = teacher.shape
+    _check_tree_tables(B, R - 1, anc, depth, "tree_accept")
     D_max = anc.shape[2] - 1
+    _shape(tokens, (B, R), "tokens")
+    _shape(path, (B, D_max), "path")
+    _vec(B, "n_nodes / status / accept_len / next_token", n_nodes, status, accept_len, next_token)
     if teacher.stride(2) != 1:
         raise ValueError("teacher rows must be contiguous")
     if mode == ACCEPT_SAMPLE:
@@ -220,7 +288,8 @@ def tree_accept(mode, tokens, teacher, n_nodes, anc, depth, status, accept_len, 
     else:
         qs = (0, 0)
     if workspace is None:
-        workspace = torch.zeros(tree_accept_workspace(mode, B, R - 1, V), dtype=torch.uint8, device=teacher.device)
+        workspace = _temp_workspace(tree_accept_workspace(mode, B, R - 1, V), teacher.device, stream,
+                                    zero=(mode == ACCEPT_SAMPLE))
     _check(_lib.tmv_tree_accept(mode, B, R - 1, D_max, V, _ptr(tokens), _dtype_code(teacher), _ptr(teacher),
                                 teacher.stride(0), teacher.stride(1), _ptr(draft_q), qs[0], qs[1],
                                 ctypes.c_uint64(seed), ctypes.c_uint64(step), _ptr(n_nodes), _ptr(anc), _ptr(depth),
@@ -240,6 +309,9 @@ def kv_commit_path(k_cache, v_cache, prefix_len, n_nodes, accept_len, path, stat
     nl, B, Hkv, L_cap, d = k_cache.shape
     if k_cache.stride(4) != 1:
         raise ValueError("d must be contiguous")
+    if path.dim() != 2 or path.shape[0] != B:
+        raise ValueError("path must be [B][D_max]")
+    _vec(B, "prefix_len / n_nodes / accept_len / status / new_len", prefix_len, n_nodes, accept_len, status, new_len)
     _check(_lib.tmv_kv_commit_path(_dtype_code(k_cache), nl, B, Hkv, d, L_cap, int(M_max), path.shape[1],
                                    _ptr(k_cache), _ptr(v_cache), _strides(k_cache, (0, 1, 2, 3)), _ptr(prefix_len),
                                    _ptr(n_nodes), _ptr(accept_len), _ptr(path), _ptr(status), _ptr(new_len),
@@ -259,6 +331,10 @@ def kv_commit_path_paged(k_pages, v_pages, block_table, prefix_len, n_nodes, acc
     nl, num_pages, Hkv, page_size, d = k_pages.shape
     if k_pages.stride(4) != 1:
         raise ValueError("d must be contiguous")
+    B = prefix_len.numel()
+    if path.dim() != 2 or path.shape[0] != B or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("path must be [B][D_max] and block_table [B][max_blocks]")
+    _vec(B, "n_nodes / accept_len / status / new_len", n_nodes, accept_len, status, new_len)
     _check(_lib.tmv_kv_commit_path_paged(_dtype_code(k_pages), nl, prefix_len.shape[0], Hkv, d, num_pages, page_size,
                                          _ptr(block_table), block_table.stride(0), block_table.shape[1], int(M_max),
                                          path.shape[1], _ptr(k_pages), _ptr(v_pages), _strides(k_pages, (0, 1, 2, 3)),
@@ -288,8 +364,9 @@ def tree_best_first(q, N_max, parents, tokens, n_nodes, rho, status, cost=None, 
     if tuple(parents.shape) != (B, N_max + 1) or tuple(tokens.shape) != (B, N_max + 1) or \
             tuple(rho.shape) != (B, N_max + 1):
         raise ValueError("outputs must be [B][N_max+1]")
+    _vec(B, "n_nodes / status", n_nodes, status)
     if workspace is None:
-        workspace = torch.empty(tree_best_first_workspace(B, D, V, N_max), dtype=torch.uint8, device=q.device)
+        workspace = _temp_workspace(tree_best_first_workspace(B, D, V, N_max), q.device, stream, zero=False)
     _check(_lib.tmv_tree_best_first(B, D, V, int(N_max), _ptr(q), q.stride(0), q.stride(1), _ptr(cost),
                                     ctypes.c_double(l_ar), _ptr(parents), _ptr(tokens), _ptr(n_nodes), _ptr(rho),
                                     _ptr(status), _ptr(workspace), workspace.numel() * workspace.element_size(),

@@ -16,4 +16,4 @@ extern "C" const char *tmv_status_string(int code)
     }
 }
 
-extern "C" int tmv_abi_version(void) { return 1; }
+extern "C" int tmv_abi_version(void) { return 2; }

@@ -7,30 +7,29 @@
 // kernel; here each query row's ancestor set is a 128-bit mask built in registers from
 // the ancestor table, applied only to the <= M tree columns.
 //
-// bf16 kernel (MFMA, gfx950):
-//   * rows of one KV head = (node, query head in the GQA group), node-major; a wave owns
-//     32 rows (two 16-row MFMA tiles) and streams 32-token chunks of K and V straight
-//     from HBM into registers in MFMA operand layout -- no LDS in the main loop.
-//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 leaves each lane holding scores of ONE
-//     query row for 8 tokens; those 8 tokens are exactly the lane's slice of the B
-//     operand of O^T = V^T P^T, so probabilities never move between lanes.  The token
-//     order inside a chunk and the head-dim order inside a tile are permuted (the
-//     contraction does not care) so that every K/V load is a contiguous 16-byte read
-//     and every V load instruction covers whole 256-byte rows.
-//   * online softmax in base 2 (log2 e folded into the scale), row max across the four
-//     lanes holding a row via two xor-shuffles; the row sum is kept per lane and reduced
-//     once at the end.
-//   * a workgroup has 4 waves: either all on the same 32 rows splitting the chunks
-//     (WR = 1, combined in LDS) or on 4 different row tiles sharing the chunks through
-//     the cache (WR = 4).  Token ranges are further split across workgroups (split-KV);
-//     a small second kernel merges the split partials in a fixed order (deterministic).
-//     No workgroup ever waits on another inside a kernel: on this GPU an agent-scope
-//     fence writes back and invalidates the whole XCD L2, which costs far more than the
-//     work it would protect.
-//   * workgroup ids are laid out so that every workgroup of one (sequence, KV head)
-//     lands on the same XCD: the head's K/V goes from HBM into that XCD's L2 once and is
-//     re-read by the head's other row blocks from there.
-// fp32 kernel: one wave per (node, query head), plain FMA; used for fp32 caches.
+// bf16, head dim 128 (tree_attn_bf16_kernel):
+//   * rows of one KV head = (node, query head in the GQA group), node-major; a workgroup
+//     of 8 waves (two per SIMD) owns a row group of 64, 128 or 256 rows and one token
+//     split of the (sequence, KV head).  K/V arrive in 32-token chunks through a 128 KiB
+//     LDS ring filled by buffer-to-LDS DMA (two halves of four chunks, one half in flight
+//     while the other is computed); every wave along the rows reads each staged chunk, so
+//     a chunk load serves the whole row group.
+//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 leaves each lane holding the scores of ONE
+//     query row for 8 tokens, exactly its slice of the B operand of O^T = V^T P^T, so
+//     probabilities never move between lanes; V^T operands come from LDS through the
+//     transposing ds_read_b64_tr_b16.
+//   * softmax in base 2 (log2 e folded into the scale) against a fixed per-row reference
+//     (the first finite chunk maximum), with an exact-maximum recompute of the split in
+//     the rare case a score outgrows it by 2^32; row max and sums via permlane swaps.
+//   * token groups of waves share a row group and are combined in LDS at the end; token
+//     splits publish (m, l, bf16 rows) with agent-coherent stores and the last split of a
+//     row block to arrive merges the block in split order (deterministic).
+//   * workgroup ids are laid out so that every workgroup of one (sequence, KV head) lands
+//     on the same XCD: the head's K/V goes from HBM into that XCD's L2 once and is re-read
+//     by the head's other row groups from there.
+// bf16, head dim 64 (tree_attn_bf16_stream_kernel): 4 waves streaming their chunks straight
+//   into registers, split partials merged by tree_attn_merge_kernel.
+// fp32 (tree_attn_f32_kernel): one wave per (node, query head), plain FMA.
 #include <cstdlib>
 #include <cstdio>
 
@@ -156,7 +155,7 @@ constexpr int kRowsPerWave = 32;    // two 16-row tiles
 
 // --------------------------------------------------------------------------- plan
 struct AttnPlan {
-    int wr;        // waves along rows (1 or 4); the other 4/wr waves split tokens
+    int wr;        // waves along rows: d128 ring kernel 2, 4 or 8 of its 8 waves; d64 streaming kernel 1 or 4 of 4
     int rb;        // rows per workgroup = wr * 32
     int nb;        // row blocks per (sequence, kv head)
     int splits;    // token splits per row block
@@ -173,66 +172,85 @@ constexpr size_t kCounterBytes = kMaxSplitUnits * sizeof(int32_t);
 // L2 while the pair's row groups re-read them.
 constexpr long kL2Bytes = 4l << 20;
 
-// Launch plan.  d128 runs the LDS-ring kernel, whose ring takes 128 KB of a CU's 160 KB
-// LDS, so a CU holds one of its workgroups at a time: a grid of more than 256 workgroups
-// runs in several rounds, and the plan keeps the grid at one round where it can.
-//   * row-group width: 32-row groups when the 32-row blocks of an XCD's pairs fit one
-//     round on its 32 CUs and a pair's K/V fit an L2 (the re-reads by each row group then come from L2); 128-row
-//     groups when a pair's K/V are larger than an L2 (re-reads would come from HBM, so
-//     the rows that share a chunk load are maximised); 64-row groups otherwise;
-//   * token splits: the most that keep the grid within one round (at least 1, at most
-//     16, and at least two chunks per wave in each split).
-// d64 runs the streaming kernel (no ring) with 128-row groups from 256 rows on and
-// enough splits to reach 256 workgroups.
-AttnPlan make_plan(int B, int M_max, int Hq, int Hkv, int L_cap, int d) {
+// compute units of the current device (the plan spreads one round of workgroups over them)
+int device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < tmv::kXcds)
+        return 256;
+    return cus;
+}
+
+// Launch plan.  d128 runs the LDS-ring kernel: 8 waves, two per SIMD, whose 128 KB ring
+// keeps one workgroup per CU, so the plan aims for one round of at most `cus` workgroups.
+//   * row-group width (rows sharing every staged K/V chunk): the narrowest of 64, 128 and
+//     256 rows whose row blocks leave at least four token splits per block within the
+//     round; 256 rows when a pair's K/V are larger than an L2 (each row group then
+//     re-reads them from HBM, so the rows sharing a chunk load are maximised);
+//   * token splits: the most that keep the grid within one round (1 to 16, and at least
+//     two chunks for each token group of waves in each split).
+// d64 runs the streaming kernel (4 waves, no ring) with 128-row groups from 256 rows on
+// and enough splits to reach 256 workgroups.
+// `force_rows` / `force_splits` (0 = the rule's choice) pin the plan (tuning and tests).
+AttnPlan make_plan(int B, int M_max, int Hq, int Hkv, int L_cap, int d, int cus, int force_rows = 0,
+                   int force_splits = 0) {
     AttnPlan p;
     const int g = Hq / Hkv;
     const int rows = M_max * g;
+    p.pairs = B * Hkv;
     // pairs per XCD: workgroup i runs on XCD i % 8 and the grid gives each XCD its own pairs
-    const long xcd_pairs = (static_cast<long>(B) * Hkv + tmv::kXcds - 1) / tmv::kXcds;
-    const long cus_per_xcd = 256 / tmv::kXcds;
+    const long xcd_pairs = (static_cast<long>(p.pairs) + tmv::kXcds - 1) / tmv::kXcds;
+    const long cpx = cus / tmv::kXcds;
+    auto blocks = [&](int wr) { return rows > 0 ? (rows + wr * kRowsPerWave - 1) / (wr * kRowsPerWave) : 0; };
     if (d == 128) {
         const long kv_pair = static_cast<long>(L_cap) * d * 2 * 2;
-        const long blocks32 = xcd_pairs * ((rows + kRowsPerWave - 1) / kRowsPerWave);
-        p.wr = kv_pair > kL2Bytes ? 4 : blocks32 <= cus_per_xcd ? 1 : 2;
+        if (kv_pair > kL2Bytes) p.wr = 8;
+        else if (xcd_pairs * blocks(2) * 4 <= cpx) p.wr = 2;
+        else if (xcd_pairs * blocks(4) * 4 <= cpx) p.wr = 4;
+        else p.wr = 8;
+        if (force_rows == 64 || force_rows == 128 || force_rows == 256) p.wr = force_rows / kRowsPerWave;
     } else {
         p.wr = rows >= 256 ? 4 : 1;
+        if (force_rows == 32 || force_rows == 128) p.wr = force_rows / kRowsPerWave;
     }
-    int forced_wr = 0, forced_s = 0;
-    if (const char *e = std::getenv("TMV_ATTN_PLAN")) std::sscanf(e, "%d:%d", &forced_wr, &forced_s);
-    if (forced_wr == 1 || forced_wr == 4 || (forced_wr == 2 && d == 128)) p.wr = forced_wr;
     p.rb = p.wr * kRowsPerWave;
-    p.nb = rows > 0 ? (rows + p.rb - 1) / p.rb : 0;
-    p.pairs = B * Hkv;
-    const int wt = kWaves / p.wr;
+    p.nb = blocks(p.wr);
     const long base = static_cast<long>(p.pairs) * p.nb;
-    int s = base <= 0 ? 1
-          : d == 128 ? static_cast<int>(cus_per_xcd / (xcd_pairs * p.nb))
-                     : static_cast<int>((256 + base - 1) / base);
-    const int s_tok = L_cap / (wt * 2 * kChunk);          // >= 2 chunks per wave per split
-    if (s > s_tok) s = s_tok;
+    int s;
+    if (d == 128) {
+        const int tw = 8 / p.wr;                                     // token groups of waves
+        s = base <= 0 ? 1 : static_cast<int>(cpx / (xcd_pairs * p.nb));
+        const int s_tok = L_cap / (tw * 2 * kChunk);                 // >= 2 chunks per token group
+        if (s > s_tok) s = s_tok;
+    } else {
+        s = base <= 0 ? 1 : static_cast<int>((256 + base - 1) / base);
+        const int s_tok = L_cap / ((kWaves / p.wr) * 2 * kChunk);
+        if (s > s_tok) s = s_tok;
+    }
     if (s > 16) s = 16;
     if (s < 1) s = 1;
-    if (forced_s >= 1 && forced_s <= 16) s = forced_s;
+    if (force_splits >= 1 && force_splits <= 16) s = force_splits;
     if (base >= kMaxSplitUnits) s = 1;
     p.splits = s;
     p.per_pair = p.nb * p.splits;
-    p.slots = ((p.pairs + tmv::kXcds - 1) / tmv::kXcds) * p.per_pair;
+    p.slots = static_cast<int>(xcd_pairs) * p.per_pair;
     return p;
 }
 
 // workspace layout: [arrival counters: kMaxSplitUnits int32][stats: pairs*nb*S*rb*2 f32]
-// [partial O: pairs*nb*S*rb*d f32] (the last two only with split-KV).  The counter block
-// sits at the same place for every shape and nothing else is ever written there: it must
-// be zero before the first call, and every call leaves the counters it used at zero, so a
-// zero-filled workspace stays valid across calls of any shape it is large enough for.
-// Split-KV is only planned for fewer than kMaxSplitUnits row blocks (with that many, one
-// split per block already fills the chip).
+// [partial O: pairs*nb*S*rb*d, bf16 for d128 (normalised rows), f32 for d64 (unnormalised)]
+// (the last two only with split-KV).  The counter block sits at the same place for every
+// shape and nothing else is ever written there: it must be zero before the first call,
+// and every call leaves the counters it used at zero, so a zero-filled workspace stays
+// valid across calls of any shape it is large enough for.  Split-KV is only planned for
+// fewer than kMaxSplitUnits row blocks (with that many, one split per block already fills
+// the chip).
 size_t plan_bytes(const AttnPlan &p, int d, size_t *off_o, size_t *off_stats = nullptr) {
     const size_t units = static_cast<size_t>(p.pairs) * p.nb * p.splits * p.rb;
     size_t st = p.splits > 1 ? units * 2 * sizeof(float) : 0;
     st = (st + 255) / 256 * 256;
-    const size_t o = p.splits > 1 ? units * d * sizeof(float) : 0;
+    const size_t es = d == 128 ? 2 : 4;
+    const size_t o = p.splits > 1 ? units * d * es : 0;
     if (off_stats) *off_stats = kCounterBytes;
     if (off_o) *off_o = kCounterBytes + st;
     return kCounterBytes + st + o;
@@ -241,9 +259,6 @@ size_t plan_bytes(const AttnPlan &p, int d, size_t *off_o, size_t *off_stats = n
 __device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t *p) {
     return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(p));
 }
-
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
 
 // --------------------------------------------------------------------------- split merge
 // Row rr, dims part*8 .. +8 of split-KV unit `unit`: the S partials (m, l, unnormalised O)
@@ -327,85 +342,6 @@ tree_attn_merge_kernel(int M_max, int D_max, int Hq, int Hkv, int L_cap,
     const int b = pair / Hkv, kvh = pair % Hkv, g = Hq / Hkv;
     merge_row_part<D, RB>(unit, rr, part, splits, b, kvh, g, rbk * RB + rr, M_max, L_cap, n_nodes[b], prefix_len[b],
                           status[b], depth, out, os0, os1, os2, ws_stats, ws_o);
-}
-
-// The merging workgroup of a split-KV row block (LDS-ring kernel): IPB items (row rr,
-// dims part*8 .. +8) per thread and batch.  Every split's (m, l) and O slice of the
-// batch's items are loaded at once with agent-coherent loads (the partials were written
-// by other workgroups, on any XCD, with agent-coherent stores), then merged in split order.
-template <int D, int RB, int IPB, int SMAX>
-__device__ __forceinline__ void merge_block(int64_t unit, int splits, int b, int kvh, int g, int row0_wg, int M_max,
-                                            int L_cap, int M, int P, int st, const int32_t *__restrict__ depth,
-                                            uint16_t *__restrict__ out, int64_t os0, int64_t os1, int64_t os2,
-                                            const float *__restrict__ ws_stats, const float *__restrict__ ws_o)
-{
-    constexpr int kItems = RB * (D / 8);
-    constexpr int kThreads = kWaves * kWave;
-    const __amdgpu_buffer_rsrc_t rst = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(ws_stats + unit * splits * RB * 2), 0, splits * RB * 2 * 4, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(ws_o + unit * splits * RB * D), 0, splits * RB * D * 4, kBufferFlags);
-    const bool seq_ok = st == TMV_OK && M >= 0 && M <= M_max && P >= 0 && static_cast<int64_t>(P) + M <= L_cap;
-    for (int i0 = threadIdx.x; i0 < kItems; i0 += kThreads * IPB) {
-        u32x2_t ml[IPB][SMAX];
-        u32x4_t oa[IPB][SMAX], ob[IPB][SMAX];
-#pragma unroll
-        for (int k = 0; k < IPB; ++k) {
-            const int item = i0 + k * kThreads;
-            const int rr = item / (D / 8), part = item % (D / 8);
-#pragma unroll
-            for (int s2 = 0; s2 < SMAX; ++s2) {
-                if (s2 < splits && item < kItems) {
-                    const int row = s2 * RB + rr;
-                    ml[k][s2] = __builtin_amdgcn_raw_buffer_load_b64(rst, row * 8, 0, kCoherent);
-                    oa[k][s2] = __builtin_amdgcn_raw_buffer_load_b128(ro, (row * D + part * 8) * 4, 0, kCoherent);
-                    ob[k][s2] = __builtin_amdgcn_raw_buffer_load_b128(ro, (row * D + part * 8 + 4) * 4, 0, kCoherent);
-                }
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < IPB; ++k) {
-            const int item = i0 + k * kThreads;
-            if (item >= kItems) break;
-            const int rr = item / (D / 8), part = item % (D / 8);
-            const int r = row0_wg + rr;
-            if (r >= M_max * g) continue;
-            const int j = r / g + 1, gi = r % g;
-            const int dp = depth[static_cast<int64_t>(b) * (M_max + 1) + j];
-            const bool live = seq_ok && r < M * g && dp >= 1;
-            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            if (live) {
-                float mt = -INFINITY;
-#pragma unroll
-                for (int s2 = 0; s2 < SMAX; ++s2)
-                    if (s2 < splits) mt = fmaxf(mt, __uint_as_float(ml[k][s2][0]));
-                const float mref = mt == -INFINITY ? 0.f : mt;
-                float lt = 0.f;
-#pragma unroll
-                for (int s2 = 0; s2 < SMAX; ++s2) {
-                    if (s2 < splits) {
-                        const float sc = __builtin_amdgcn_exp2f(__uint_as_float(ml[k][s2][0]) - mref);
-                        lt += sc * __uint_as_float(ml[k][s2][1]);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            acc[e] += sc * __uint_as_float(oa[k][s2][e]);
-                            acc[4 + e] += sc * __uint_as_float(ob[k][s2][e]);
-                        }
-                    }
-                }
-                const float inv = lt > 0.f ? 1.f / lt : 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] *= inv;
-            }
-            uint32_t w4[4];
-#pragma unroll
-            for (int h2 = 0; h2 < 4; ++h2)
-                w4[h2] = static_cast<uint32_t>(tmv::f32_to_bf16(acc[2 * h2])) |
-                         (static_cast<uint32_t>(tmv::f32_to_bf16(acc[2 * h2 + 1])) << 16);
-            uint16_t *o = out + b * os0 + static_cast<int64_t>(j - 1) * os1 + static_cast<int64_t>(kvh * g + gi) * os2 + part * 8;
-            *reinterpret_cast<uint4 *>(o) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-        }
-    }
 }
 
 // ------------------------------------------------ bf16 MFMA kernel, register streaming (d64)
@@ -829,9 +765,10 @@ tree_attn_bf16_stream_kernel(int M_max, int D_max, int Hq, int Hkv,
     }
 }
 
-// --------------------------------------------------------------------------- bf16 MFMA kernel
+// --------------------------------------------------------------------------- bf16 MFMA kernel (d128)
 // LDS ring of chunk slots: 128 KiB, two halves of kRound chunks each (double buffered).
 constexpr int kRingBytes = 128 * 1024;
+constexpr int kRingWaves = 8;       // waves of the ring kernel: two per SIMD
 
 template <int D>
 struct RingShape {
@@ -839,15 +776,15 @@ struct RingShape {
     static constexpr int kPieces = D / 8;                   // 16-byte pieces per row
     static constexpr int kMatBytes = kChunk * kRowBytes;    // K (or V) part of one chunk
     static constexpr int kSlotBytes = 2 * kMatBytes;        // K then V
-    static constexpr int kSlots = kRingBytes / kSlotBytes;  // 8 (d128) or 16 (d64)
+    static constexpr int kSlots = kRingBytes / kSlotBytes;  // 8 (d128)
     static constexpr int kRound = kSlots / 2;               // chunks per half
     static constexpr int kDmaPerChunk = kSlotBytes / 1024;  // 1 KiB per DMA instruction
-    static constexpr int kDmaPerWave = kDmaPerChunk / kWaves;
-    static_assert(kDmaPerWave * kWaves == kDmaPerChunk, "chunk DMA must split evenly over the waves");
+    static constexpr int kDmaPerWave = kDmaPerChunk / kRingWaves;
+    static_assert(kDmaPerWave * kRingWaves == kDmaPerChunk, "chunk DMA must split evenly over the waves");
 };
 
-// ancestor entries of a row fetched in the prologue; deeper rows (DEEP kernels only)
-// fetch the rest in further batches
+// ancestor entries of a row fetched in the prologue (four per lane); deeper rows (DEEP
+// kernels only) fetch the rest in further batches
 constexpr int kAncBatch = 16;
 
 // paged caches: block-table entries of one sequence staged in LDS (the ring leaves 32 KB)
@@ -862,8 +799,95 @@ struct PagedArgs {
     int npages;
 };
 
-template <int D, int WR, bool DEEP, bool PAGED>
-__global__ void __launch_bounds__(kWaves * kWave)
+// The merging workgroup of a split-KV row block (LDS-ring kernel).  Split s left, per row
+// of the block, (m, l) in fp32 -- m the row's largest score in base-2 units, l the sum of
+// 2^(score - m) -- and the row's output normalised by l, rounded to bf16.  IPB items (row
+// rr, dims part*8 .. +8) per thread and batch: every split's (m, l) and 16-byte O slice of
+// the batch's items are loaded at once with agent-coherent loads (the partials were written
+// by other workgroups, on any XCD, with agent-coherent stores), then merged in split order,
+// so the result does not depend on which split arrived last.
+template <int D, int RB, int IPB, int SMAX>
+__device__ __forceinline__ void merge_block(int64_t unit, int splits, int b, int kvh, int g, int row0_wg, int M_max,
+                                            int L_cap, int M, int P, int st, const int32_t *__restrict__ depth,
+                                            uint16_t *__restrict__ out, int64_t os0, int64_t os1, int64_t os2,
+                                            const float *__restrict__ ws_stats, const uint16_t *__restrict__ ws_o)
+{
+    constexpr int kItems = RB * (D / 8);
+    constexpr int kThreads = kRingWaves * kWave;
+    const __amdgpu_buffer_rsrc_t rst = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(ws_stats + unit * splits * RB * 2), 0, splits * RB * 2 * 4, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(ws_o + unit * splits * RB * D), 0, splits * RB * D * 2, kBufferFlags);
+    const bool seq_ok = st == TMV_OK && M >= 0 && M <= M_max && P >= 0 && static_cast<int64_t>(P) + M <= L_cap;
+    for (int i0 = threadIdx.x; i0 < kItems; i0 += kThreads * IPB) {
+        u32x2_t ml[IPB][SMAX];
+        u32x4_t ov[IPB][SMAX];
+#pragma unroll
+        for (int k = 0; k < IPB; ++k) {
+            const int item = i0 + k * kThreads;
+            const int rr = item / (D / 8), part = item % (D / 8);
+#pragma unroll
+            for (int s2 = 0; s2 < SMAX; ++s2) {
+                if (s2 < splits && item < kItems) {
+                    const int row = s2 * RB + rr;
+                    ml[k][s2] = __builtin_amdgcn_raw_buffer_load_b64(rst, row * 8, 0, kCoherent);
+                    ov[k][s2] = __builtin_amdgcn_raw_buffer_load_b128(ro, (row * D + part * 8) * 2, 0, kCoherent);
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < IPB; ++k) {
+            const int item = i0 + k * kThreads;
+            if (item >= kItems) break;
+            const int rr = item / (D / 8), part = item % (D / 8);
+            const int r = row0_wg + rr;
+            if (r >= M_max * g) continue;
+            const int j = r / g + 1, gi = r % g;
+            const int dp = depth[static_cast<int64_t>(b) * (M_max + 1) + j];
+            const bool live = seq_ok && r < M * g && dp >= 1;
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            if (live) {
+                float mt = -INFINITY;
+#pragma unroll
+                for (int s2 = 0; s2 < SMAX; ++s2)
+                    if (s2 < splits) mt = fmaxf(mt, __uint_as_float(ml[k][s2][0]));
+                const float mref = mt == -INFINITY ? 0.f : mt;
+                float lt = 0.f;
+#pragma unroll
+                for (int s2 = 0; s2 < SMAX; ++s2) {
+                    if (s2 < splits) {
+                        // weight of split s2: its share of the row's softmax mass
+                        const float w = __builtin_amdgcn_exp2f(__uint_as_float(ml[k][s2][0]) - mref) *
+                                        __uint_as_float(ml[k][s2][1]);
+                        lt += w;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            acc[2 * e] += w * tmv::bf16_to_f32(static_cast<uint16_t>(ov[k][s2][e] & 0xffffu));
+                            acc[2 * e + 1] += w * tmv::bf16_to_f32(static_cast<uint16_t>(ov[k][s2][e] >> 16));
+                        }
+                    }
+                }
+                const float inv = lt > 0.f ? 1.f / lt : 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] *= inv;
+            }
+            uint32_t w4[4];
+#pragma unroll
+            for (int h2 = 0; h2 < 4; ++h2)
+                w4[h2] = static_cast<uint32_t>(tmv::f32_to_bf16(acc[2 * h2])) |
+                         (static_cast<uint32_t>(tmv::f32_to_bf16(acc[2 * h2 + 1])) << 16);
+            uint16_t *o = out + b * os0 + static_cast<int64_t>(j - 1) * os1 + static_cast<int64_t>(kvh * g + gi) * os2 + part * 8;
+            *reinterpret_cast<uint4 *>(o) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        }
+    }
+}
+
+// Tree attention of one (sequence, KV head, row block, token split).  8 waves, two per
+// SIMD (at most 256 registers per lane), so one wave's MFMAs overlap the other's softmax
+// and LDS reads.  RW waves lie along the rows (RB = 32 RW rows share every staged chunk)
+// and TW = 8 / RW token groups of waves take turns on the chunks of each ring round.
+template <int D, int RW, bool DEEP, bool PAGED>
+__global__ void __launch_bounds__(kRingWaves * kWave)
 tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
                       const int32_t *__restrict__ prefix_len, const int32_t *__restrict__ n_nodes,
                       uint32_t ks0_16, uint32_t ks1_16, uint32_t ks2_16, int L_cap, int pairs, uint32_t geom,
@@ -875,27 +899,30 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
                       const int32_t *__restrict__ anc, const int32_t *__restrict__ depth,
                       int32_t *__restrict__ status, float qk_scale_log2,
                       uint16_t *__restrict__ out, int64_t os0, int64_t os1, int64_t os2,
-                      float *__restrict__ ws_stats, float *__restrict__ ws_o, int32_t *__restrict__ ws_cnt,
+                      float *__restrict__ ws_stats, uint16_t *__restrict__ ws_o, int32_t *__restrict__ ws_cnt,
                       PagedArgs pg)
 {
     using RS = RingShape<D>;
     static_assert(D == 128, "the LDS-ring kernel is written for head dimension 128");
+    static_assert(RW == 2 || RW == 4 || RW == 8, "row groups of 64, 128 or 256 rows");
     constexpr int KS = D / 32;           // k-steps of the QK^T contraction
     constexpr int NT = D / 16;           // 16-dim output tiles
-    constexpr int WT = kWaves / WR;      // waves sharing rows (they split the chunks)
-    constexpr int RB = WR * kRowsPerWave;
-    constexpr int DG = D / 4;            // dims per lane of an output row
+    constexpr int TW = kRingWaves / RW;  // token groups of waves
+    constexpr int RB = RW * kRowsPerWave;
     constexpr int PP = RS::kPieces;
+    constexpr int kThreads = kRingWaves * kWave;
+    constexpr int kDW = RS::kDmaPerWave;
 
     // two halves of the ring as distinct objects, so LDS reads of one half need not wait
     // for DMA still landing in the other
     __shared__ __attribute__((aligned(16))) char ring0[RS::kRound * RS::kSlotBytes];
     __shared__ __attribute__((aligned(16))) char ring1[RS::kRound * RS::kSlotBytes];
+    __shared__ float s_ml[kRingWaves * kRowsPerWave * 2];
     __shared__ int s_last;
     // paged caches: this sequence's block-table entries (-1: invalid) and, per wave, the
     // first invalid entry it staged
     __shared__ int32_t pg_lds[PAGED ? kMaxPagesLds : 1];
-    __shared__ int pg_bad[kWaves];
+    __shared__ int pg_bad[kRingWaves];
 
     // ---- decode the workgroup: XCD-major so one (sequence, kv head) stays on one XCD
     // geom = splits | workgroups per pair << 5 | Hkv << 16
@@ -911,11 +938,11 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);     // wave-uniform
-    const int wr = wave / WT, wt = wave % WT;
+    const int rw = wave % RW, tw = wave / RW;
     const int c16 = lane & 15, G = lane >> 4;
     const int R = 1 + M_max, W = D_max + 1;
     const int row0_wg = rbk * RB;
-    const int row0 = row0_wg + wr * kRowsPerWave;         // first row of this wave
+    const int row0 = row0_wg + rw * kRowsPerWave;         // first row of this wave
 
     // ---- K/V copies.  Split s takes the global 32-token chunks s, s + S, s + 2S, ... (local
     // chunk k = global chunk s + k*S), so the chunks of a split are known before the
@@ -931,27 +958,26 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
 
     // DMA lane mapping: instruction i of a chunk covers LDS bytes [i*1 KiB, +1 KiB) of the
     // slot; lane l writes 16 bytes at 16*l.  Within K (or V) the LDS holds row t at
-    // t*kRowBytes with its 16-byte pieces XOR-swizzled by (t mod kPieces), so the lane
-    // that fills LDS piece (t, pp) reads global piece pp ^ (t mod kPieces) of row t.
+    // t*kRowBytes with its 16-byte pieces XOR-swizzled, so the lane that fills LDS piece
+    // (t, pp) reads global piece pp ^ swizzle(t) of row t.  Waves 0-3 move K, 4-7 move V.
     // (paged: ks0_16 is the page stride; a chunk's page is added when it is issued)
     const int64_t head_off = ((PAGED ? 0 : static_cast<int64_t>(b) * ks0_16) + static_cast<int64_t>(kvh) * ks1_16) * 16;
     const int64_t page_bytes = static_cast<int64_t>(ks0_16) * 16;
     const char *kbase = reinterpret_cast<const char *>(kc) + head_off;
     const char *vbase = reinterpret_cast<const char *>(vc) + head_off;
     const int64_t row_bytes = static_cast<int64_t>(ks2_16) * 16;
-    // each wave moves whole 1 KiB pieces of either K or V (waves 0-1 K, 2-3 V)
-    static_assert((RS::kDmaPerChunk / 2) % RS::kDmaPerWave == 0, "a wave must stay within K or V");
-    const bool wave_v = wave * RS::kDmaPerWave >= RS::kDmaPerChunk / 2;
+    static_assert((RS::kDmaPerChunk / 2) % kDW == 0, "a wave must stay within K or V");
+    const bool wave_v = wave * kDW >= RS::kDmaPerChunk / 2;
     const char *mbase = wave_v ? vbase : kbase;
-    uint32_t dma_off[RS::kDmaPerWave];
-    int dma_lds[RS::kDmaPerWave];
+    uint32_t dma_off[kDW];
+    int dma_lds[kDW];
     // 16-token pages: rows 16-31 of a chunk lie on its second page; every DMA instruction
     // covers 4 rows, all on one page (dma_hi), at offsets relative to that page
-    bool dma_hi[RS::kDmaPerWave];
+    bool dma_hi[kDW];
     const bool two_pages = PAGED && pg.shift == 4;
 #pragma unroll
-    for (int jd = 0; jd < RS::kDmaPerWave; ++jd) {
-        const int i = wave * RS::kDmaPerWave + jd;             // instruction within the chunk
+    for (int jd = 0; jd < kDW; ++jd) {
+        const int i = wave * kDW + jd;                         // instruction within the chunk
         const int ii = wave_v ? i - RS::kDmaPerChunk / 2 : i;
         const int qpos = ii * 64 + lane;                       // 16-byte LDS piece index
         const int t = qpos / PP, pp = qpos % PP;
@@ -965,8 +991,6 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         dma_off[jd] = static_cast<uint32_t>((dma_hi[jd] ? t - 16 : t) * row_bytes + ((pp ^ sw) * 16));
         dma_lds[jd] = (wave_v ? RS::kMatBytes : 0) + ii * 1024;
     }
-    // issue this wave's share of local chunk k into the slot at `slot` (records stop at
-    // t_lim, so loads past it write zeros and touch no memory; chunks past nk_lim load nothing)
     // rows of local chunk k to copy (records stop at t_lim, so loads past it write zeros and
     // touch no memory; chunks past nk_lim load nothing)
     auto chunk_recs = [&](int k) {
@@ -987,7 +1011,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     };
     // issue this wave's share of local chunk k into the slot at `slot` (paged: pa / pb are
     // its page entries, wave-uniform)
-    auto issue_chunk = [&](int k, char *slot, int pa, int pb) {
+    auto issue_chunk = [&](int k, char *slot_p, int pa, int pb) {
         const int t0 = (split + k * splits) * kChunk;
         int recs = (k < nk_lim) ? t_lim - t0 : 0;
         recs = recs < 0 ? 0 : (recs > kChunk ? kChunk : recs);
@@ -1002,22 +1026,22 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
             const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<char *>(mbase + (pa >= 0 ? pa : 0) * page_bytes + in_page), 0,
                 pa >= 0 ? static_cast<int>(recs0 * row_bytes) : 0, kBufferFlags);
-            const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            const __amdgpu_buffer_rsrc_t rbuf = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<char *>(mbase + (pb >= 0 ? pb : 0) * page_bytes), 0,
                 pb >= 0 ? static_cast<int>(recs1 * row_bytes) : 0, kBufferFlags);
             // (the page choice goes through readfirstlane as an integer: selected as a lane mask,
             // the descriptor would land in vector registers and every copy would become a
             // waterfall loop)
 #pragma unroll
-            for (int jd = 0; jd < RS::kDmaPerWave; ++jd)
-                dma_to_lds16(__builtin_amdgcn_readfirstlane(dma_hi[jd] ? 1 : 0) ? rb : ra, slot + dma_lds[jd], dma_off[jd]);
+            for (int jd = 0; jd < kDW; ++jd)
+                dma_to_lds16(__builtin_amdgcn_readfirstlane(dma_hi[jd] ? 1 : 0) ? rbuf : ra, slot_p + dma_lds[jd], dma_off[jd]);
         } else {
             const int nbytes = __builtin_amdgcn_readfirstlane(static_cast<int>(recs * row_bytes));
             const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<char *>(mbase + static_cast<int64_t>(k < nk_lim ? t0 : 0) * row_bytes), 0, nbytes, kBufferFlags);
 #pragma unroll
-            for (int jd = 0; jd < RS::kDmaPerWave; ++jd)
-                dma_to_lds16(mr, slot + dma_lds[jd], dma_off[jd]);
+            for (int jd = 0; jd < kDW; ++jd)
+                dma_to_lds16(mr, slot_p + dma_lds[jd], dma_off[jd]);
         }
     };
     // paged: page entries of the next round to issue, read from LDS a round ahead so the
@@ -1033,7 +1057,9 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         }
     };
     // round r fills half r % 2 of the ring with local chunks r*kRound .. +kRound (paged:
-    // from the prefetched entries when `prefetched`)
+    // from the prefetched entries when `prefetched`).  Every wave issues exactly kRound *
+    // kDW copies per round, empty ones included, so the count of copies issued after a
+    // round -- what the waits below rely on -- is the same on every path.
     auto issue_round = [&](int r, char *half, bool prefetched = false) {
         if constexpr (PAGED) {
 #pragma unroll
@@ -1050,34 +1076,33 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     };
     // paged caches: this thread's block-table entries are loaded first, together with the
     // prologue's loads below, and staged in LDS before the first copies (L_cap = entries x page)
-    constexpr int kPgPer = kMaxPagesLds / (kWaves * kWave);
+    constexpr int kPgPer = kMaxPagesLds / kThreads;
     int pg_reg[PAGED ? kPgPer : 1];
     if constexpr (PAGED) {
         const int n_pg = L_cap >> pg.shift;
         const int32_t *trow = pg.tab + static_cast<int64_t>(b) * pg.stride;
 #pragma unroll
         for (int u = 0; u < kPgPer; ++u) {
-            const int i = threadIdx.x + u * kWaves * kWave;
+            const int i = threadIdx.x + u * kThreads;
             pg_reg[u] = i < n_pg ? trow[i] : -1;
         }
     } else {
-        // the first two rounds go out before anything else is loaded or waited for
-        // (both are issued even when empty -- they then load nothing -- so the number of DMA
-        // operations in flight is the same on every path)
+        // the first round goes out before anything else is loaded or waited for
         issue_round(0, ring0);
-        issue_round(1, ring1);
     }
 
-    // ---- one round trip for the prologue, under the first copies: the sequence's scalars and,
-    // independently of them, this lane's query fragments, node depths and first ancestor entries (row
-    // indices are clamped into the tables, so no load waits on another)
-    // (values are wave-uniform; readfirstlane keeps the chunk descriptors in scalar registers)
+    // ---- the prologue's loads, between the first and the second round of copies (vector
+    // loads complete in issue order, so these wait for the first round only): the
+    // sequence's scalars and, independently of them, this lane's query fragments, node
+    // depths and ancestor entries.  Lane group G fetches entries 4G .. 4G+3 of its rows'
+    // ancestor lists; the four groups' mask bits are OR-ed together below.  (Row indices
+    // are clamped into the tables, so no load waits on another.)
     const int M = __builtin_amdgcn_readfirstlane(n_nodes[b]);
     const int P = __builtin_amdgcn_readfirstlane(prefix_len[b]);
     int st = __builtin_amdgcn_readfirstlane(status[b]);
     const int g = Hq / Hkv;
     bf16x8_t qf[2][KS];
-    int dep[2], anc8[2][kAncBatch];
+    int dep[2], ancq[2][4];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
         int r = row0 + rt * 16 + c16;
@@ -1089,8 +1114,12 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         dep[rt] = depth[static_cast<int64_t>(b) * R + j];
         const int32_t *arow = anc + (static_cast<int64_t>(b) * R + j) * W;
 #pragma unroll
-        for (int k = 0; k < kAncBatch; ++k) anc8[rt][k] = arow[k < W ? k : W - 1];
+        for (int k = 0; k < 4; ++k) {
+            const int kk = 4 * G + k;
+            ancq[rt][k] = arow[kk < W ? kk : W - 1];
+        }
     }
+    if constexpr (!PAGED) issue_round(1, ring1);
     if constexpr (PAGED) {
         // stage the entries (invalid ones as -1; each wave records the first invalid one),
         // then issue the first two rounds from them
@@ -1098,7 +1127,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         int bad_min = 0x7fffffff;
 #pragma unroll
         for (int u = 0; u < kPgPer; ++u) {
-            const int i = threadIdx.x + u * kWaves * kWave;
+            const int i = threadIdx.x + u * kThreads;
             if (i < n_pg) {
                 const int e = pg_reg[u];
                 const bool ok = e >= 0 && e < pg.npages;
@@ -1124,7 +1153,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         // every page holding a visible token must be a valid page
         int fb = pg_bad[0];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) fb = pg_bad[w] < fb ? pg_bad[w] : fb;
+        for (int w = 1; w < kRingWaves; ++w) fb = pg_bad[w] < fb ? pg_bad[w] : fb;
         fb = __builtin_amdgcn_readfirstlane(fb);
         if (st == TMV_OK && fb < ((P + M + (1 << pg.shift) - 1) >> pg.shift)) {
             st = TMV_ERR_INPUT;
@@ -1136,14 +1165,14 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     if (row0_wg >= Rh) {
         // no live row in this workgroup (nor in the other splits of its row block, which
         // see the same rows): split 0 clears the block's output rows
-        if (split == 0 && wt == 0) {
+        if (split == 0 && tw == 0) {
             for (int rt = 0; rt < 2; ++rt) {
                 const int r = row0 + rt * 16 + c16;
                 if (r >= M_max * g) continue;
                 const int j = r / g + 1, gi = r % g;
-                uint16_t *o = out + b * os0 + static_cast<int64_t>(j - 1) * os1 + static_cast<int64_t>(kvh * g + gi) * os2 + G * DG;
+                uint16_t *o = out + b * os0 + static_cast<int64_t>(j - 1) * os1 + static_cast<int64_t>(kvh * g + gi) * os2 + G * (D / 4);
 #pragma unroll
-                for (int e = 0; e < DG; e += 8) *reinterpret_cast<uint4 *>(o + e) = make_uint4(0, 0, 0, 0);
+                for (int e = 0; e < D / 4; e += 8) *reinterpret_cast<uint4 *>(o + e) = make_uint4(0, 0, 0, 0);
             }
         }
         __builtin_amdgcn_s_waitcnt(kVmcntZero);   // no copy may land in LDS after the exit
@@ -1163,40 +1192,53 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     const int kb_loc = (T % kChunk != 0 && cb >= split && (cb - split) % splits == 0) ? (cb - split) / splits : -1;
     const int kb_round = kb_loc >= 0 && kb_loc < 2 * RS::kRound ? kb_loc / RS::kRound : -1;
 
-
     const bool wave_live = row0 < Rh;
 
-    // ---- ancestor-or-self masks of the lane's two rows (bit a <-> tree slot P + a);
-    // rows beyond the live ones are padding whose results are never written
-    uint64_t mlo[2] = {0, 0}, mhi[2] = {0, 0};
+    // ---- ancestor-or-self masks of the lane's two rows as four 32-bit words (bit a of the
+    // mask <-> tree slot P + a); rows beyond the live ones are padding whose results are
+    // never written.  A bit index outside [0, 128) sets nothing.
+    uint32_t mw[2][4];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) mw[rt][w] = 0u;
         const int r = row0 + rt * 16 + c16;
         if (r >= Rh) continue;
         const int dp = dep[rt];
+        auto set_bit = [&](int a) {
 #pragma unroll
-        for (int k = 0; k < kAncBatch; ++k)
-            if (k < dp) {
-                const int a = anc8[rt][k] - 1;
-                if (a < 64) mlo[rt] |= 1ull << a; else mhi[rt] |= 1ull << (a - 64);
-            }
+            for (int w = 0; w < 4; ++w) mw[rt][w] |= (a >> 5) == w ? (1u << (a & 31)) : 0u;
+        };
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (4 * G + k < dp) set_bit(ancq[rt][k] - 1);
         if (DEEP && dp > kAncBatch) {
             // deep rows: the rest of the path, one batch of loads per round trip
             const int j = r / g + 1;
             const int32_t *arow = anc + (static_cast<int64_t>(b) * R + j) * W;
             for (int k0 = kAncBatch; k0 < dp; k0 += kAncBatch) {
-                int e[kAncBatch];
+                int e[4];
 #pragma unroll
-                for (int k = 0; k < kAncBatch; ++k) e[k] = arow[k0 + k < W ? k0 + k : W - 1];
+                for (int k = 0; k < 4; ++k) {
+                    const int kk = k0 + 4 * G + k;
+                    e[k] = arow[kk < W ? kk : W - 1];
+                }
 #pragma unroll
-                for (int k = 0; k < kAncBatch; ++k)
-                    if (k0 + k < dp) {
-                        const int a = e[k] - 1;
-                        if (a < 64) mlo[rt] |= 1ull << a; else mhi[rt] |= 1ull << (a - 64);
-                    }
+                for (int k = 0; k < 4; ++k)
+                    if (k0 + 4 * G + k < dp) set_bit(e[k] - 1);
             }
         }
     }
+    // OR the four lane groups' bits (lanes c16, c16 + 16, c16 + 32, c16 + 48 hold one row)
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const auto x16 = __builtin_amdgcn_permlane16_swap(mw[rt][w], mw[rt][w], false, false);
+            const uint32_t y = x16[0] | x16[1];
+            const auto x32 = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+            mw[rt][w] = x32[0] | x32[1];
+        }
 
     // LDS read offsets of the MFMA operands inside a slot (constant per lane).  K
     // fragment (tt, ks): row tt*16 + c16, logical piece ks*4 + G.  V^T: lane reads row
@@ -1242,8 +1284,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) ka[tt * KS + ks] = sp + lk[tt][ks];
-            if constexpr (NK == 8) lds_read_b128_x8(kraw, ka);
-            else lds_read_b128_x4(kraw, ka);
+            lds_read_b128_x8(kraw, ka);
         }
         bf16x8_t kf[2][KS];
 #pragma unroll
@@ -1273,8 +1314,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
             const int qw = e >> 5, sh = e & 31;                       // wave-uniform
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
-                const uint32_t w0 = static_cast<uint32_t>(mlo[rt]), w1 = static_cast<uint32_t>(mlo[rt] >> 32);
-                const uint32_t w2 = static_cast<uint32_t>(mhi[rt]), w3 = static_cast<uint32_t>(mhi[rt] >> 32);
+                const uint32_t w0 = mw[rt][0], w1 = mw[rt][1], w2 = mw[rt][2], w3 = mw[rt][3];
                 const uint32_t lo = qw == 0 ? 0xFFFFFFFFu : qw == 1 ? w0 : qw == 2 ? w1 : qw == 3 ? w2 : w3;
                 const uint32_t hi = qw == 0 ? w0 : qw == 1 ? w1 : qw == 2 ? w2 : qw == 3 ? w3 : 0u;
                 const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, sh) >> (G * 4);
@@ -1332,20 +1372,23 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
             issue_round(0, ring0);
             issue_round(1, ring1);
         }
-        // Round r: wait until this wave's DMA of round r has landed (round r + 1 may still
-        // be in flight), barrier so every wave's share is visible, compute, barrier so no
-        // wave still reads the half, then refill it with round r + 2.  The barriers carry
-        // no memory fence on purpose: a fence would wait for all DMA in flight.
+        // Round r: wait until this wave's copies of round r have landed (round r + 1 may
+        // still be in flight: vector-memory operations complete in issue order and every
+        // wave issued exactly kRound * kDW copies for round r + 1 after round r, plus
+        // only operations that are needed here anyway), barrier so every wave's share is
+        // visible, compute, barrier so no wave still reads the half, then refill it with
+        // round r + 2.  The barriers carry no memory fence on purpose: a fence would wait
+        // for all copies in flight.
         auto run_round = [&](int r, char *half) {
             if (r + 2 < nrounds) prefetch_pages(r + 2);
-            if (r + 1 < nrounds) __builtin_amdgcn_s_waitcnt(kVmcntRound<RS::kRound * RS::kDmaPerWave>());
+            if (r + 1 < nrounds) __builtin_amdgcn_s_waitcnt(kVmcntRound<RS::kRound * kDW>());
             else __builtin_amdgcn_s_waitcnt(kVmcntZero);
             __builtin_amdgcn_s_barrier();
             if (pass == 0 && r == kb_round) {
                 // the chunk holding T was copied before T was known: zero its V rows >= T
                 const int r0 = T - (split + kb_loc * splits) * kChunk;
                 const uint32_t vb = lds_addr(half) + (kb_loc % RS::kRound) * RS::kSlotBytes + RS::kMatBytes + r0 * RS::kRowBytes;
-                for (int i = threadIdx.x; i < (kChunk - r0) * PP; i += kWaves * kWave) lds_zero16(vb + i * 16);
+                for (int i = threadIdx.x; i < (kChunk - r0) * PP; i += kThreads) lds_zero16(vb + i * 16);
                 __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
                 __builtin_amdgcn_s_barrier();
             }
@@ -1353,7 +1396,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
 #pragma unroll
                 for (int j = 0; j < RS::kRound; ++j) {
                     const int k = r * RS::kRound + j;
-                    if (k < nk && (k % WT) == wt) compute_chunk(lds_addr(half) + j * RS::kSlotBytes, split + k * splits);
+                    if (k < nk && (j % TW) == tw) compute_chunk(lds_addr(half) + j * RS::kSlotBytes, split + k * splits);
                 }
             }
             __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
@@ -1378,16 +1421,14 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     float mrow[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-        mrow[rt] = mref[rt];
         // row sums: each of the four lanes of a row holds a partial sum
         auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(lrow[rt]), __float_as_uint(lrow[rt]), false, false);
         const float l16 = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
         auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(l16), __float_as_uint(l16), false, false);
         lrow[rt] = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+        // from here on the running maxima are in base-2 units, as the merge steps expect
+        mrow[rt] = mref[rt] == -INFINITY ? -INFINITY : mref[rt] * cs;
     }
-    // from here on the running maxima are in base-2 units, as the merge steps expect
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) mrow[rt] = mrow[rt] == -INFINITY ? -INFINITY : mrow[rt] * cs;
 
     // ---- split-KV completion: the last split of a row block to arrive merges the block.
     // Splits publish their partials with agent-coherent stores (sc1: written through to
@@ -1399,11 +1440,11 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     // this launch's split partials: [pairs * nb units][splits][RB rows] (m, l) and O rows
     const int64_t part_rows = static_cast<int64_t>(pairs) * nb * splits * RB;
     const __amdgpu_buffer_rsrc_t part_o =
-        __builtin_amdgcn_make_buffer_rsrc(ws_o, 0, static_cast<int>(part_rows * D * 4), kBufferFlags);
+        __builtin_amdgcn_make_buffer_rsrc(ws_o, 0, static_cast<int>(part_rows * D * 2), kBufferFlags);
     const __amdgpu_buffer_rsrc_t part_ml =
         __builtin_amdgcn_make_buffer_rsrc(ws_stats, 0, static_cast<int>(part_rows * 8), kBufferFlags);
+    const int64_t unit = static_cast<int64_t>(pair) * nb + rbk;
     auto finish_split = [&]() {
-        const int64_t unit = static_cast<int64_t>(pair) * nb + rbk;
         __builtin_amdgcn_s_waitcnt(kVmcntZero);
         __syncthreads();
         if (threadIdx.x == 0) {
@@ -1413,26 +1454,45 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         __syncthreads();
         if (s_last == 0) return;
         if (threadIdx.x == 0) __hip_atomic_store(ws_cnt + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // one round trip for the partials of up to 8 splits and 2 items per thread
-        if (splits <= 8)
-            merge_block<D, RB, 2, 8>(unit, splits, b, kvh, g, row0_wg, M_max, L_cap, M, P, st, depth, out, os0, os1,
-                                     os2, ws_stats, ws_o);
+        // one round trip for the partials of up to 8 splits and up to 2 items per thread
+        constexpr int kIpt = (RB * (D / 8) + kThreads - 1) / kThreads;
+        if (splits <= 4)
+            merge_block<D, RB, (kIpt < 4 ? kIpt : 4), 4>(unit, splits, b, kvh, g, row0_wg, M_max, L_cap, M, P, st,
+                                                          depth, out, os0, os1, os2, ws_stats, ws_o);
+        else if (splits <= 8)
+            merge_block<D, RB, (kIpt < 2 ? kIpt : 2), 8>(unit, splits, b, kvh, g, row0_wg, M_max, L_cap, M, P, st,
+                                                          depth, out, os0, os1, os2, ws_stats, ws_o);
         else
-            merge_block<D, RB, 1, 16>(unit, splits, b, kvh, g, row0_wg, M_max, L_cap, M, P, st, depth, out, os0, os1,
-                                      os2, ws_stats, ws_o);
+            merge_block<D, RB, 1, 16>(unit, splits, b, kvh, g, row0_wg, M_max, L_cap, M, P, st, depth, out, os0,
+                                      os1, os2, ws_stats, ws_o);
+    };
+    // row `rr` of the workgroup's block, dims d0 .. d0 + n - 1 (n a multiple of 8) of the
+    // final output (splits == 1) from x / l, or zeros for inert rows
+    auto write_row = [&](int rr, int d0, const float *x, int n, float l) {
+        const int r = row0_wg + rr;
+        if (r >= M_max * g) return;
+        const int j = r / g + 1, gi = r % g;
+        const bool live = r < Rh && depth[static_cast<int64_t>(b) * R + j] >= 1;
+        const float inv = live && l > 0.f ? 1.f / l : 0.f;
+        uint16_t *o = out + b * os0 + static_cast<int64_t>(j - 1) * os1 + static_cast<int64_t>(kvh * g + gi) * os2 + d0;
+        for (int e = 0; e < n; e += 8) {
+            uint32_t w4[4];
+#pragma unroll
+            for (int h2 = 0; h2 < 4; ++h2) {
+                const float x0 = live ? x[e + 2 * h2] * inv : 0.f, x1 = live ? x[e + 2 * h2 + 1] * inv : 0.f;
+                w4[h2] = static_cast<uint32_t>(tmv::f32_to_bf16(x0)) | (static_cast<uint32_t>(tmv::f32_to_bf16(x1)) << 16);
+            }
+            *reinterpret_cast<uint4 *>(o + e) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        }
     };
 
-    if constexpr (WT > 1) {
-        // ---- the WT waves of a row group share its 32 rows: every wave parks its (m, l, O)
-        // in the idle ring, then each wave combines its share of its group's rows over the
-        // group's WT waves in a fixed order and writes them.  O rows sit kOS floats apart so
-        // the parked writes are free of bank conflicts.
-        static_assert(WR * WT == kWaves && (WR == 1 || WR == 2), "row groups of 32 rows shared by WT waves");
-        constexpr int kOS = D + 4;
-        constexpr int kPark = kRowsPerWave * kOS;                  // floats per parked wave
-        static_assert(2 * kPark * 4 + kWaves * kRowsPerWave * 2 * 4 <= (int)sizeof(ring1), "park area");
-        auto parked = [&](int w) { return reinterpret_cast<float *>(w < 2 ? ring0 : ring1) + (w & 1) * kPark; };
-        float *ml = reinterpret_cast<float *>(ring1) + 2 * kPark;    // [wave][32 rows][m, l]
+    if constexpr (TW > 1) {
+        // ---- the TW token groups share each row group: every wave parks its (m, l, O) in
+        // the idle ring (16 KB per wave; 4-float groups XOR-swizzled by row so the parked
+        // writes are free of bank conflicts), then each wave combines its share of its row
+        // group's rows over the group's TW waves in a fixed order.
+        static_assert(kRingWaves * kRowsPerWave * D * 4 == 2 * sizeof(ring0), "park area = ring");
+        auto parked = [&](int w) { return reinterpret_cast<float *>((w < 4 ? ring0 : ring1) + (w & 3) * kRowsPerWave * D * 4); };
         {
             float *o = parked(wave);
 #pragma unroll
@@ -1440,49 +1500,51 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
                 const int rr = rt * 16 + c16;
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt)
-                    *reinterpret_cast<f32x4_t *>(o + rr * kOS + nt * 16 + 4 * G) = oacc[rt][nt];
-                if (G == 0) *reinterpret_cast<float2 *>(ml + (wave * kRowsPerWave + rr) * 2) = make_float2(mrow[rt], lrow[rt]);
+                    *reinterpret_cast<f32x4_t *>(o + rr * D + (((nt * 4 + G) ^ (rr & 31)) << 2)) = oacc[rt][nt];
+                if (G == 0) *reinterpret_cast<float2 *>(s_ml + (wave * kRowsPerWave + rr) * 2) = make_float2(mrow[rt], lrow[rt]);
             }
         }
         __syncthreads();
-        // wave (wr, wt) combines rows wt*RPW .. +RPW of its row group; LPR lanes per row,
+        // wave (rw, tw) combines rows tw*RPW .. +RPW of row group rw; LPR lanes per row,
         // DL dims per lane
-        constexpr int RPW = kRowsPerWave / WT, LPR = kWave / RPW, DL = D / LPR;
-        const int rg = wt * RPW + lane / LPR, d0 = (lane % LPR) * DL;
-        const int rr = wr * kRowsPerWave + rg;                      // row within the workgroup
-        float mw[WT], lw[WT], mt = -INFINITY;
+        constexpr int RPW = kRowsPerWave / TW, LPR = kWave / RPW, DL = D / LPR;
+        const int rg = tw * RPW + lane / LPR, d0 = (lane % LPR) * DL;
+        const int rr = rw * kRowsPerWave + rg;                      // row within the workgroup
+        float mw_[TW], lw_[TW], mt = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < WT; ++w) {
-            const float2 x = *reinterpret_cast<const float2 *>(ml + ((wr * WT + w) * kRowsPerWave + rg) * 2);
-            mw[w] = x.x; lw[w] = x.y;
+        for (int w = 0; w < TW; ++w) {
+            const float2 x = *reinterpret_cast<const float2 *>(s_ml + ((w * RW + rw) * kRowsPerWave + rg) * 2);
+            mw_[w] = x.x; lw_[w] = x.y;
             mt = fmaxf(mt, x.x);
         }
         const float mref2 = mt == -INFINITY ? 0.f : mt;
-        float sc[WT], lt = 0.f;
+        float sc[TW], lt = 0.f;
 #pragma unroll
-        for (int w = 0; w < WT; ++w) { sc[w] = __builtin_amdgcn_exp2f(mw[w] - mref2); lt += sc[w] * lw[w]; }
+        for (int w = 0; w < TW; ++w) { sc[w] = __builtin_amdgcn_exp2f(mw_[w] - mref2); lt += sc[w] * lw_[w]; }
         float acc[DL];
 #pragma unroll
         for (int e = 0; e < DL; ++e) acc[e] = 0.f;
 #pragma unroll
-        for (int w = 0; w < WT; ++w) {
-            const float *src = parked(wr * WT + w) + rg * kOS + d0;
+        for (int w = 0; w < TW; ++w) {
+            const float *src = parked(w * RW + rw) + rg * D;
 #pragma unroll
             for (int e = 0; e < DL; e += 4) {
-                const float4 x = *reinterpret_cast<const float4 *>(src + e);
+                const float4 x = *reinterpret_cast<const float4 *>(src + ((((d0 + e) >> 2) ^ (rg & 31)) << 2));
                 acc[e] += sc[w] * x.x; acc[e + 1] += sc[w] * x.y; acc[e + 2] += sc[w] * x.z; acc[e + 3] += sc[w] * x.w;
             }
         }
         if (splits > 1) {
-            // ---- split-KV: publish this split's partial (m, l, unnormalised O); the last
-            // split of the row block to arrive merges them (finish_split)
-            const int64_t unit = static_cast<int64_t>(pair) * nb + rbk;
+            // ---- publish this split's partial: (m, l) and the row normalised by l in bf16
             const int base = static_cast<int>((unit * splits + split) * RB);
+            const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
-            for (int e = 0; e < DL; e += 4) {
-                const u32x4_t x = {__float_as_uint(acc[e]), __float_as_uint(acc[e + 1]), __float_as_uint(acc[e + 2]),
-                                   __float_as_uint(acc[e + 3])};
-                __builtin_amdgcn_raw_buffer_store_b128(x, part_o, ((base + rr) * D + d0 + e) * 4, 0, kCoherent);
+            for (int e = 0; e < DL; e += 8) {
+                u32x4_t x;
+#pragma unroll
+                for (int h2 = 0; h2 < 4; ++h2)
+                    x[h2] = static_cast<uint32_t>(tmv::f32_to_bf16(acc[e + 2 * h2] * inv)) |
+                            (static_cast<uint32_t>(tmv::f32_to_bf16(acc[e + 2 * h2 + 1] * inv)) << 16);
+                __builtin_amdgcn_raw_buffer_store_b128(x, part_o, ((base + rr) * D + d0 + e) * 2, 0, kCoherent);
             }
             if ((lane % LPR) == 0) {
                 const u32x2_t x = {__float_as_uint(mt), __float_as_uint(lt)};
@@ -1491,64 +1553,48 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
             finish_split();
             return;
         }
-        const int r = row0_wg + rr;
-        if (r >= M_max * g) return;
-        const int j = r / g + 1, gi = r % g;
-        const bool live = r < Rh && depth[static_cast<int64_t>(b) * R + j] >= 1;
-        const float inv = live && lt > 0.f ? 1.f / lt : 0.f;
-        uint16_t *o = out + b * os0 + static_cast<int64_t>(j - 1) * os1 + static_cast<int64_t>(kvh * g + gi) * os2 + d0;
-#pragma unroll
-        for (int e = 0; e < DL; e += 8) {
-            uint32_t w4[4];
-#pragma unroll
-            for (int h2 = 0; h2 < 4; ++h2) {
-                const float x0 = live ? acc[e + 2 * h2] * inv : 0.f, x1 = live ? acc[e + 2 * h2 + 1] * inv : 0.f;
-                w4[h2] = static_cast<uint32_t>(tmv::f32_to_bf16(x0)) | (static_cast<uint32_t>(tmv::f32_to_bf16(x1)) << 16);
-            }
-            *reinterpret_cast<uint4 *>(o + e) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-        }
-        return;
+        write_row(rr, d0, acc, DL, lt);
     } else {
-    // ---- split-KV: publish this split's partial (m, l, unnormalised O); the last split
-    // of the row block to arrive merges them (finish_split)
-    if (splits > 1) {
-        const int64_t unit = static_cast<int64_t>(pair) * nb + rbk;          // (pair, row block)
-        const int base = static_cast<int>((unit * splits + split) * RB + wr * kRowsPerWave);
+        // ---- one token group: every wave holds whole rows (lane: dims nt*16 + 4G .. +3)
+        if (splits > 1) {
+            const int base = static_cast<int>((unit * splits + split) * RB + rw * kRowsPerWave);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                const int rr = rt * 16 + c16;
+                const float inv = lrow[rt] > 0.f ? 1.f / lrow[rt] : 0.f;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const u32x2_t x = {static_cast<uint32_t>(tmv::f32_to_bf16(oacc[rt][nt][0] * inv)) |
+                                           (static_cast<uint32_t>(tmv::f32_to_bf16(oacc[rt][nt][1] * inv)) << 16),
+                                       static_cast<uint32_t>(tmv::f32_to_bf16(oacc[rt][nt][2] * inv)) |
+                                           (static_cast<uint32_t>(tmv::f32_to_bf16(oacc[rt][nt][3] * inv)) << 16)};
+                    __builtin_amdgcn_raw_buffer_store_b64(x, part_o, ((base + rr) * D + nt * 16 + 4 * G) * 2, 0, kCoherent);
+                }
+                if (G == 0) {
+                    const u32x2_t x = {__float_as_uint(mrow[rt]), __float_as_uint(lrow[rt])};
+                    __builtin_amdgcn_raw_buffer_store_b64(x, part_ml, (base + rr) * 8, 0, kCoherent);
+                }
+            }
+            finish_split();
+            return;
+        }
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-            const int rr = rt * 16 + c16;
+            const int r = row0 + rt * 16 + c16;
+            if (r >= M_max * g) continue;
+            const int j = r / g + 1, gi = r % g;
+            const bool live = r < Rh && depth[static_cast<int64_t>(b) * R + j] >= 1;
+            const float inv = live && lrow[rt] > 0.f ? 1.f / lrow[rt] : 0.f;
+            uint16_t *o = out + b * os0 + static_cast<int64_t>(j - 1) * os1 + static_cast<int64_t>(kvh * g + gi) * os2 + 4 * G;
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, oacc[rt][nt]), part_o,
-                                                       ((base + rr) * D + nt * 16 + 4 * G) * 4, 0, kCoherent);
-            if (G == 0) {
-                const u32x2_t x = {__float_as_uint(mrow[rt]), __float_as_uint(lrow[rt])};
-                __builtin_amdgcn_raw_buffer_store_b64(x, part_ml, (base + rr) * 8, 0, kCoherent);
+            for (int nt = 0; nt < NT; ++nt) {
+                const float x0 = live ? oacc[rt][nt][0] * inv : 0.f, x1 = live ? oacc[rt][nt][1] * inv : 0.f;
+                const float x2 = live ? oacc[rt][nt][2] * inv : 0.f, x3 = live ? oacc[rt][nt][3] * inv : 0.f;
+                *reinterpret_cast<uint2 *>(o + nt * 16) =
+                    make_uint2(static_cast<uint32_t>(tmv::f32_to_bf16(x0)) | (static_cast<uint32_t>(tmv::f32_to_bf16(x1)) << 16),
+                               static_cast<uint32_t>(tmv::f32_to_bf16(x2)) | (static_cast<uint32_t>(tmv::f32_to_bf16(x3)) << 16));
             }
         }
-        finish_split();
-        return;
-    }
-    if (wt != 0) return;
-
-    // ---- write the final rows: lane writes dims nt*16 + 4G .. +3 of its row in each tile
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-        const int r = row0 + rt * 16 + c16;
-        if (r >= M_max * g) continue;
-        const int j = r / g + 1, gi = r % g;
-        const bool live = r < Rh && depth[static_cast<int64_t>(b) * R + j] >= 1;
-        const float inv = live && lrow[rt] > 0.f ? 1.f / lrow[rt] : 0.f;
-        uint16_t *o = out + b * os0 + static_cast<int64_t>(j - 1) * os1 + static_cast<int64_t>(kvh * g + gi) * os2 + 4 * G;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const float x0 = live ? oacc[rt][nt][0] * inv : 0.f, x1 = live ? oacc[rt][nt][1] * inv : 0.f;
-            const float x2 = live ? oacc[rt][nt][2] * inv : 0.f, x3 = live ? oacc[rt][nt][3] * inv : 0.f;
-            *reinterpret_cast<uint2 *>(o + nt * 16) =
-                make_uint2(static_cast<uint32_t>(tmv::f32_to_bf16(x0)) | (static_cast<uint32_t>(tmv::f32_to_bf16(x1)) << 16),
-                           static_cast<uint32_t>(tmv::f32_to_bf16(x2)) | (static_cast<uint32_t>(tmv::f32_to_bf16(x3)) << 16));
-        }
-    }
     }
 }
 
@@ -1680,24 +1726,36 @@ void launch_bf16(const AttnPlan &p, hipStream_t s, int M_max, int D_max, int Hq,
 {
     char *w = static_cast<char *>(ws);
     int32_t *cnt = reinterpret_cast<int32_t *>(w);
-    float *stats = reinterpret_cast<float *>(w + off_stats), *part = reinterpret_cast<float *>(w + off_o);
-    const uint32_t geom = static_cast<uint32_t>(p.splits) | (static_cast<uint32_t>(p.per_pair) << 5) |
-                          (static_cast<uint32_t>(Hkv) << 16);
-#define TMV_LAUNCH_ATTN(DEEP, PAGED)                                                                       \
-    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, WR, DEEP, PAGED>), dim3(p.slots * tmv::kXcds), dim3(kWaves * kWave), 0, s, \
-                       static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), P, n,                 \
-                       static_cast<uint32_t>(kvs[0] / 8), static_cast<uint32_t>(kvs[1] / 8),                    \
-                       static_cast<uint32_t>(kvs[2] / 8), L_cap, p.pairs, geom, M_max, D_max, Hq, p.nb,         \
-                       static_cast<const uint16_t *>(q), qs[0], qs[1], qs[2], anc, dep, status, scale * kLog2e,  \
-                       static_cast<uint16_t *>(out), os[0], os[1], os[2], stats, part, cnt, pgv)
+    float *stats = reinterpret_cast<float *>(w + off_stats);
     if constexpr (D == 64) {
+        float *part = reinterpret_cast<float *>(w + off_o);
         hipLaunchKernelGGL((tree_attn_bf16_stream_kernel<D, WR>), dim3(p.slots * tmv::kXcds), dim3(kWaves * kWave), 0,
                            s, M_max, D_max, Hq, Hkv, static_cast<const uint16_t *>(q), qs[0], qs[1], qs[2],
                            static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), kvs[0], kvs[1],
                            kvs[2], L_cap, P, n, anc, dep, status, scale * kLog2e, static_cast<uint16_t *>(out),
                            os[0], os[1], os[2], stats, part, p.pairs, p.nb, p.splits, p.per_pair);
+        // the streaming kernel leaves its split partials to the merge kernel
+        if (p.splits > 1) {
+            constexpr int RB = WR * kRowsPerWave;
+            const int64_t threads = static_cast<int64_t>(p.pairs) * p.nb * RB * (D / 8);
+            hipLaunchKernelGGL((tree_attn_merge_kernel<D, RB>), dim3(static_cast<unsigned>((threads + 255) / 256)),
+                               dim3(256), 0, s, M_max, D_max, Hq, Hkv, L_cap, P, n, dep, status,
+                               static_cast<uint16_t *>(out), os[0], os[1], os[2], stats, part, p.pairs, p.nb, p.splits);
+        }
     } else {
+        // the ring kernel merges its splits itself (the last split of a row block to arrive)
+        uint16_t *part = reinterpret_cast<uint16_t *>(w + off_o);
+        const uint32_t geom = static_cast<uint32_t>(p.splits) | (static_cast<uint32_t>(p.per_pair) << 5) |
+                              (static_cast<uint32_t>(Hkv) << 16);
         const PagedArgs pgv = pg ? *pg : PagedArgs{nullptr, 0, 0, 0};
+#define TMV_LAUNCH_ATTN(DEEP, PAGED)                                                                       \
+        hipLaunchKernelGGL((tree_attn_bf16_kernel<D, WR, DEEP, PAGED>), dim3(p.slots * tmv::kXcds),      \
+                           dim3(kRingWaves * kWave), 0, s, static_cast<const uint16_t *>(k),              \
+                           static_cast<const uint16_t *>(v), P, n, static_cast<uint32_t>(kvs[0] / 8),     \
+                           static_cast<uint32_t>(kvs[1] / 8), static_cast<uint32_t>(kvs[2] / 8), L_cap,   \
+                           p.pairs, geom, M_max, D_max, Hq, p.nb, static_cast<const uint16_t *>(q), qs[0], \
+                           qs[1], qs[2], anc, dep, status, scale * kLog2e, static_cast<uint16_t *>(out),   \
+                           os[0], os[1], os[2], stats, part, cnt, pgv)
         if (pg) {
             if (D_max + 1 > kAncBatch) TMV_LAUNCH_ATTN(true, true);
             else TMV_LAUNCH_ATTN(false, true);
@@ -1705,16 +1763,7 @@ void launch_bf16(const AttnPlan &p, hipStream_t s, int M_max, int D_max, int Hq,
             if (D_max + 1 > kAncBatch) TMV_LAUNCH_ATTN(true, false);
             else TMV_LAUNCH_ATTN(false, false);
         }
-    }
 #undef TMV_LAUNCH_ATTN
-    // the LDS-ring kernel (d128) merges its splits itself; the streaming kernel needs the
-    // merge kernel after it
-    if (D == 64 && p.splits > 1) {
-        constexpr int RB = WR * kRowsPerWave;
-        const int64_t threads = static_cast<int64_t>(p.pairs) * p.nb * RB * (D / 8);
-        hipLaunchKernelGGL((tree_attn_merge_kernel<D, RB>), dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256),
-                           0, s, M_max, D_max, Hq, Hkv, L_cap, P, n, dep, status, static_cast<uint16_t *>(out),
-                           os[0], os[1], os[2], stats, part, p.pairs, p.nb, p.splits);
     }
 }
 
@@ -1726,44 +1775,41 @@ void dispatch_bf16(const AttnPlan &p, int d, hipStream_t s, int M_max, int D_max
                    const int32_t *n, const int32_t *anc, const int32_t *dep, int32_t *status, float scale, void *out,
                    const int64_t *os, void *ws, size_t off_o, size_t off_stats, const PagedArgs *pg)
 {
+#define TMV_DISPATCH(DD, WRR) \
+    launch_bf16<DD, WRR>(p, s, M_max, D_max, Hq, Hkv, q, qs, k, v, kvs, L_cap, P, n, anc, dep, status, scale, out, os, \
+                         ws, off_o, off_stats, pg)
     if (d == 128) {
-        if (p.wr == 4)
-            launch_bf16<128, 4>(p, s, M_max, D_max, Hq, Hkv, q, qs, k, v, kvs, L_cap, P, n, anc, dep, status, scale, out,
-                                os, ws, off_o, off_stats, pg);
-        else if (p.wr == 2)
-            launch_bf16<128, 2>(p, s, M_max, D_max, Hq, Hkv, q, qs, k, v, kvs, L_cap, P, n, anc, dep, status, scale, out,
-                                os, ws, off_o, off_stats, pg);
-        else
-            launch_bf16<128, 1>(p, s, M_max, D_max, Hq, Hkv, q, qs, k, v, kvs, L_cap, P, n, anc, dep, status, scale, out,
-                                os, ws, off_o, off_stats, pg);
+        if (p.wr == 8) TMV_DISPATCH(128, 8);
+        else if (p.wr == 4) TMV_DISPATCH(128, 4);
+        else TMV_DISPATCH(128, 2);
     } else {
-        if (p.wr == 4)
-            launch_bf16<64, 4>(p, s, M_max, D_max, Hq, Hkv, q, qs, k, v, kvs, L_cap, P, n, anc, dep, status, scale, out,
-                               os, ws, off_o, off_stats, nullptr);
-        else
-            launch_bf16<64, 1>(p, s, M_max, D_max, Hq, Hkv, q, qs, k, v, kvs, L_cap, P, n, anc, dep, status, scale, out,
-                               os, ws, off_o, off_stats, nullptr);
+        if (p.wr == 4) TMV_DISPATCH(64, 4);
+        else TMV_DISPATCH(64, 1);
     }
+#undef TMV_DISPATCH
 }
 
-}  // namespace
+// the plan's workspace and grid fit the kernels' 32-bit offsets
+bool plan_fits(const AttnPlan &p, int d) {
+    const int64_t part_rows = static_cast<int64_t>(p.pairs) * p.nb * p.splits * p.rb;
+    return part_rows * d * 4 < (int64_t(1) << 31) && static_cast<int64_t>(p.slots) * tmv::kXcds <= 0x7fffffff &&
+           p.per_pair <= 2047;
+}
 
-extern "C" size_t tmv_tree_verify_attention_workspace(int dtype, int B, int M_max, int Hq, int Hkv, int d,
-                                                      int L_cap)
+size_t attention_workspace(int dtype, int B, int M_max, int Hq, int Hkv, int d, int L_cap, int force_rows,
+                           int force_splits)
 {
-    if (dtype != TMV_BF16 || B <= 0 || Hkv <= 0 || Hq <= 0 || Hq % Hkv) return 256;
-    const AttnPlan p = make_plan(B, M_max, Hq, Hkv, L_cap, d);
+    if (dtype != TMV_BF16 || B <= 0 || Hkv <= 0 || Hq <= 0 || Hq % Hkv || L_cap < 1 || (d != 64 && d != 128))
+        return 256;
+    const AttnPlan p = make_plan(B, M_max, Hq, Hkv, L_cap, d, device_cus(), force_rows, force_splits);
     return plan_bytes(p, d, nullptr);
 }
 
-extern "C" int tmv_tree_verify_attention(int dtype, int B, int M_max, int D_max, int Hq, int Hkv, int d,
-                                         const void *q, const int64_t *q_stride,
-                                         const void *k_cache, const void *v_cache,
-                                         const int64_t *kv_stride, int L_cap,
-                                         const int32_t *prefix_len, const int32_t *n_nodes,
-                                         const int32_t *anc, const int32_t *depth, int32_t *status,
-                                         float scale, void *out, const int64_t *o_stride,
-                                         void *workspace, size_t workspace_bytes, void *stream)
+int attention(int dtype, int B, int M_max, int D_max, int Hq, int Hkv, int d, const void *q, const int64_t *q_stride,
+              const void *k_cache, const void *v_cache, const int64_t *kv_stride, int L_cap,
+              const int32_t *prefix_len, const int32_t *n_nodes, const int32_t *anc, const int32_t *depth,
+              int32_t *status, float scale, void *out, const int64_t *o_stride, int force_rows, int force_splits,
+              void *workspace, size_t workspace_bytes, void *stream)
 {
     if (dtype != TMV_F32 && dtype != TMV_BF16) return TMV_ERR_ARG;
     if (B < 0 || M_max < 0 || M_max > 128 || D_max < 0 || D_max > 128) return TMV_ERR_ARG;
@@ -1777,7 +1823,6 @@ extern "C" int tmv_tree_verify_attention(int dtype, int B, int M_max, int D_max,
     for (int i = 0; i < 3; ++i)
         if (q_stride[i] < 0 || kv_stride[i] < 0 || o_stride[i] < 0) return TMV_ERR_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
-
     if (dtype == TMV_F32) {
         const int64_t items = static_cast<int64_t>(B) * M_max * Hq;
         const int64_t blocks = (items + 3) / 4;
@@ -1799,7 +1844,6 @@ extern "C" int tmv_tree_verify_attention(int dtype, int B, int M_max, int D_max,
 #undef TMV_LAUNCH_F32
         return tmv_host::launch_status(hipGetLastError());
     }
-
     // bf16: 16-byte vector loads need 16-byte aligned rows and head slices
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return TMV_ERR_ARG;
     for (int i = 0; i < 3; ++i)
@@ -1809,35 +1853,76 @@ extern "C" int tmv_tree_verify_attention(int dtype, int B, int M_max, int D_max,
     for (int i = 0; i < 3; ++i)
         if (kv_stride[i] / 8 > 0xffffffffll) return TMV_ERR_ARG;
     if (Hkv > 0xffff) return TMV_ERR_ARG;
-    const AttnPlan p = make_plan(B, M_max, Hq, Hkv, L_cap, d);
+    const AttnPlan p = make_plan(B, M_max, Hq, Hkv, L_cap, d, device_cus(), force_rows, force_splits);
     size_t off_o = 0, off_stats = 0;
     const size_t need = plan_bytes(p, d, &off_o, &off_stats);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return TMV_ERR_ARG;
-    if (static_cast<int64_t>(p.slots) * tmv::kXcds > 0x7fffffff) return TMV_ERR_ARG;
-
+    if (!plan_fits(p, d)) return TMV_ERR_ARG;
     dispatch_bf16(p, d, s, M_max, D_max, Hq, Hkv, q, q_stride, k_cache, v_cache, kv_stride, L_cap, prefix_len, n_nodes,
                   anc, depth, status, scale, out, o_stride, workspace, off_o, off_stats, nullptr);
     return tmv_host::launch_status(hipGetLastError());
 }
 
-extern "C" size_t tmv_tree_verify_attention_paged_workspace(int B, int M_max, int Hq, int Hkv, int d, int page_size,
-                                                            int max_blocks)
+}  // namespace
+
+extern "C" size_t tmv_tree_verify_attention_workspace(int dtype, int B, int M_max, int Hq, int Hkv, int d,
+                                                      int L_cap)
+{
+    return attention_workspace(dtype, B, M_max, Hq, Hkv, d, L_cap, 0, 0);
+}
+
+extern "C" int tmv_tree_verify_attention(int dtype, int B, int M_max, int D_max, int Hq, int Hkv, int d,
+                                         const void *q, const int64_t *q_stride,
+                                         const void *k_cache, const void *v_cache,
+                                         const int64_t *kv_stride, int L_cap,
+                                         const int32_t *prefix_len, const int32_t *n_nodes,
+                                         const int32_t *anc, const int32_t *depth, int32_t *status,
+                                         float scale, void *out, const int64_t *o_stride,
+                                         void *workspace, size_t workspace_bytes, void *stream)
+{
+    return attention(dtype, B, M_max, D_max, Hq, Hkv, d, q, q_stride, k_cache, v_cache, kv_stride, L_cap, prefix_len,
+                     n_nodes, anc, depth, status, scale, out, o_stride, 0, 0, workspace, workspace_bytes, stream);
+}
+
+extern "C" size_t tmv_tree_verify_attention_plan_workspace(int dtype, int B, int M_max, int Hq, int Hkv, int d,
+                                                           int L_cap, int rows_per_group, int splits)
+{
+    return attention_workspace(dtype, B, M_max, Hq, Hkv, d, L_cap, rows_per_group, splits);
+}
+
+extern "C" int tmv_tree_verify_attention_plan(int dtype, int B, int M_max, int D_max, int Hq, int Hkv, int d,
+                                              const void *q, const int64_t *q_stride,
+                                              const void *k_cache, const void *v_cache,
+                                              const int64_t *kv_stride, int L_cap,
+                                              const int32_t *prefix_len, const int32_t *n_nodes,
+                                              const int32_t *anc, const int32_t *depth, int32_t *status,
+                                              float scale, void *out, const int64_t *o_stride,
+                                              int rows_per_group, int splits,
+                                              void *workspace, size_t workspace_bytes, void *stream)
+{
+    return attention(dtype, B, M_max, D_max, Hq, Hkv, d, q, q_stride, k_cache, v_cache, kv_stride, L_cap, prefix_len,
+                     n_nodes, anc, depth, status, scale, out, o_stride, rows_per_group, splits, workspace,
+                     workspace_bytes, stream);
+}
+
+namespace {
+
+size_t paged_workspace(int B, int M_max, int Hq, int Hkv, int d, int page_size, int max_blocks, int force_rows,
+                       int force_splits)
 {
     if (B <= 0 || Hkv <= 0 || Hq <= 0 || Hq % Hkv || page_size <= 0 || max_blocks <= 0) return 256;
     const int64_t L_cap = static_cast<int64_t>(page_size) * max_blocks;
     if (L_cap > 0x7fffffff) return 256;
-    return plan_bytes(make_plan(B, M_max, Hq, Hkv, static_cast<int>(L_cap), d), d, nullptr);
+    return plan_bytes(make_plan(B, M_max, Hq, Hkv, static_cast<int>(L_cap), d, device_cus(), force_rows, force_splits),
+                      d, nullptr);
 }
 
-extern "C" int tmv_tree_verify_attention_paged(int dtype, int B, int M_max, int D_max, int Hq, int Hkv, int d,
-                                               const void *q, const int64_t *q_stride,
-                                               const void *k_pages, const void *v_pages,
-                                               const int64_t *page_stride, int num_pages, int page_size,
-                                               const int32_t *block_table, int64_t table_stride, int max_blocks,
-                                               const int32_t *prefix_len, const int32_t *n_nodes,
-                                               const int32_t *anc, const int32_t *depth, int32_t *status,
-                                               float scale, void *out, const int64_t *o_stride,
-                                               void *workspace, size_t workspace_bytes, void *stream)
+int paged_attention(int dtype, int B, int M_max, int D_max, int Hq, int Hkv, int d, const void *q,
+                    const int64_t *q_stride, const void *k_pages, const void *v_pages, const int64_t *page_stride,
+                    int num_pages, int page_size, const int32_t *block_table, int64_t table_stride, int max_blocks,
+                    const int32_t *prefix_len, const int32_t *n_nodes, const int32_t *anc, const int32_t *depth,
+                    int32_t *status, float scale, void *out, const int64_t *o_stride, int force_rows,
+                    int force_splits, void *workspace, size_t workspace_bytes, void *stream)
 {
     if (dtype != TMV_BF16 || d != 128) return TMV_ERR_ARG;
     if (B < 0 || M_max < 0 || M_max > 128 || D_max < 0 || D_max > 128) return TMV_ERR_ARG;
@@ -1858,11 +1943,11 @@ extern "C" int tmv_tree_verify_attention_paged(int dtype, int B, int M_max, int 
     }
     // a chunk's rows are addressed by 32-bit offsets from their page's first row
     if (static_cast<int64_t>(page_size) * page_stride[2] * 2 >= (int64_t(1) << 31)) return TMV_ERR_ARG;
-    const AttnPlan p = make_plan(B, M_max, Hq, Hkv, static_cast<int>(L_cap), d);
+    const AttnPlan p = make_plan(B, M_max, Hq, Hkv, static_cast<int>(L_cap), d, device_cus(), force_rows, force_splits);
     size_t off_o = 0, off_stats = 0;
     const size_t need = plan_bytes(p, d, &off_o, &off_stats);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return TMV_ERR_ARG;
-    if (static_cast<int64_t>(p.slots) * tmv::kXcds > 0x7fffffff) return TMV_ERR_ARG;
+    if (!plan_fits(p, d)) return TMV_ERR_ARG;
     int shift = 0;
     while ((1 << shift) < page_size) ++shift;
     const PagedArgs pg{block_table, table_stride, shift, num_pages};
@@ -1870,4 +1955,50 @@ extern "C" int tmv_tree_verify_attention_paged(int dtype, int B, int M_max, int 
                   page_stride, static_cast<int>(L_cap), prefix_len, n_nodes, anc, depth, status, scale, out, o_stride,
                   workspace, off_o, off_stats, &pg);
     return tmv_host::launch_status(hipGetLastError());
+}
+
+}  // namespace
+
+extern "C" size_t tmv_tree_verify_attention_paged_workspace(int B, int M_max, int Hq, int Hkv, int d, int page_size,
+                                                            int max_blocks)
+{
+    return paged_workspace(B, M_max, Hq, Hkv, d, page_size, max_blocks, 0, 0);
+}
+
+extern "C" int tmv_tree_verify_attention_paged(int dtype, int B, int M_max, int D_max, int Hq, int Hkv, int d,
+                                               const void *q, const int64_t *q_stride,
+                                               const void *k_pages, const void *v_pages,
+                                               const int64_t *page_stride, int num_pages, int page_size,
+                                               const int32_t *block_table, int64_t table_stride, int max_blocks,
+                                               const int32_t *prefix_len, const int32_t *n_nodes,
+                                               const int32_t *anc, const int32_t *depth, int32_t *status,
+                                               float scale, void *out, const int64_t *o_stride,
+                                               void *workspace, size_t workspace_bytes, void *stream)
+{
+    return paged_attention(dtype, B, M_max, D_max, Hq, Hkv, d, q, q_stride, k_pages, v_pages, page_stride, num_pages,
+                           page_size, block_table, table_stride, max_blocks, prefix_len, n_nodes, anc, depth, status,
+                           scale, out, o_stride, 0, 0, workspace, workspace_bytes, stream);
+}
+
+extern "C" size_t tmv_tree_verify_attention_paged_plan_workspace(int B, int M_max, int Hq, int Hkv, int d,
+                                                                 int page_size, int max_blocks, int rows_per_group,
+                                                                 int splits)
+{
+    return paged_workspace(B, M_max, Hq, Hkv, d, page_size, max_blocks, rows_per_group, splits);
+}
+
+extern "C" int tmv_tree_verify_attention_paged_plan(int dtype, int B, int M_max, int D_max, int Hq, int Hkv, int d,
+                                                    const void *q, const int64_t *q_stride,
+                                                    const void *k_pages, const void *v_pages,
+                                                    const int64_t *page_stride, int num_pages, int page_size,
+                                                    const int32_t *block_table, int64_t table_stride, int max_blocks,
+                                                    const int32_t *prefix_len, const int32_t *n_nodes,
+                                                    const int32_t *anc, const int32_t *depth, int32_t *status,
+                                                    float scale, void *out, const int64_t *o_stride,
+                                                    int rows_per_group, int splits,
+                                                    void *workspace, size_t workspace_bytes, void *stream)
+{
+    return paged_attention(dtype, B, M_max, D_max, Hq, Hkv, d, q, q_stride, k_pages, v_pages, page_stride, num_pages,
+                           page_size, block_table, table_stride, max_blocks, prefix_len, n_nodes, anc, depth, status,
+                           scale, out, o_stride, rows_per_group, splits, workspace, workspace_bytes, stream);
 }

@@ -139,7 +139,10 @@ __device__ __forceinline__ void lds_zero16(uint32_t addr) {
     const u32x4_t z = {0u, 0u, 0u, 0u};
     asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(z) : "memory");
 }
-// the XCD (accelerator complex die) this wave runs on
+// store 16 bytes to LDS (inline assembly, for the same reason)
+__device__ __forceinline__ void lds_write16(uint32_t addr, u32x4_t v) {
+    asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
 
 // buffer -> LDS copy of 16 bytes per lane: lane l's bytes land at lds + 16*l; a voffset
 // past the descriptor's records writes zeros and reads nothing
@@ -807,7 +810,7 @@ struct PagedArgs {
 // by other workgroups, on any XCD, with agent-coherent stores), then merged in split order,
 // so the result does not depend on which split arrived last.
 template <int D, int RB, int IPB, int SMAX>
-__device__ __forceinline__ void merge_block(int64_t unit, int splits, int b, int kvh, int g, int row0_wg, int M_max,
+__device__ __forceinline__ void merge_block(int64_t unit, int splits, int b, int kvh, int g, int g_magic, int row0_wg, int M_max,
                                             int L_cap, int M, int P, int st, const int32_t *__restrict__ depth,
                                             uint16_t *__restrict__ out, int64_t os0, int64_t os1, int64_t os2,
                                             const float *__restrict__ ws_stats, const uint16_t *__restrict__ ws_o)
@@ -842,7 +845,7 @@ __device__ __forceinline__ void merge_block(int64_t unit, int splits, int b, int
             const int rr = item / (D / 8), part = item % (D / 8);
             const int r = row0_wg + rr;
             if (r >= M_max * g) continue;
-            const int j = r / g + 1, gi = r % g;
+            const int j = ((r * g_magic) >> 16) + 1, gi = r - (j - 1) * g;
             const int dp = depth[static_cast<int64_t>(b) * (M_max + 1) + j];
             const bool live = seq_ok && r < M * g && dp >= 1;
             float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -894,7 +897,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
                       // (the arguments above fill the 14 SGPRs the hardware preloads: everything
                       // the first K/V copies need, cache strides in 16-byte units; the rest
                       // arrive through the kernel-argument segment)
-                      int M_max, int D_max, int Hq, int nb,
+                      int M_max, int D_max, int nb,
                       const uint16_t *__restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
                       const int32_t *__restrict__ anc, const int32_t *__restrict__ depth,
                       int32_t *__restrict__ status, float qk_scale_log2,
@@ -913,28 +916,34 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     constexpr int kThreads = kRingWaves * kWave;
     constexpr int kDW = RS::kDmaPerWave;
 
-    // two halves of the ring as distinct objects, so LDS reads of one half need not wait
-    // for DMA still landing in the other
-    __shared__ __attribute__((aligned(16))) char ring0[RS::kRound * RS::kSlotBytes];
-    __shared__ __attribute__((aligned(16))) char ring1[RS::kRound * RS::kSlotBytes];
+    // the ring: two halves of kRound slots (all its reads are inline assembly, so the
+    // compiler never waits for copies in flight before touching it)
+    constexpr int kHalfBytes = RS::kRound * RS::kSlotBytes;
+    __shared__ __attribute__((aligned(16))) char ring[2 * kHalfBytes];
     __shared__ float s_ml[kRingWaves * kRowsPerWave * 2];
+    // 64-row groups (contiguous caches): the four token groups of a row group share one
+    // copy of its query fragments, each loading one k-step (16 KB for the workgroup)
+    constexpr bool kShareQ = RW == 2 && TW == KS && !PAGED;
+    __shared__ __attribute__((aligned(16))) u32x4_t q_x[kShareQ ? RW * 2 * KS * kWave : 1];
     __shared__ int s_last;
     // paged caches: this sequence's block-table entries (-1: invalid) and, per wave, the
     // first invalid entry it staged
     __shared__ int32_t pg_lds[PAGED ? kMaxPagesLds : 1];
     __shared__ int pg_bad[kRingWaves];
 
-    // ---- decode the workgroup: XCD-major so one (sequence, kv head) stays on one XCD
-    // geom = splits | workgroups per pair << 5 | Hkv << 16
-    const int splits = static_cast<int>(geom & 31u), per_pair = static_cast<int>((geom >> 5) & 2047u);
-    const int Hkv = static_cast<int>(geom >> 16);
-    const int wg = blockIdx.x;
-    const int xcd = wg % tmv::kXcds, slot = wg / tmv::kXcds;
-    const int pair = (slot / per_pair) * tmv::kXcds + xcd;
+    // ---- decode the workgroup.  grid = (8 * nb, splits, ceil(pairs / 8)) with x = XCD slot +
+    // 8 * row block: the linear workgroup id is x + 8 nb (split + splits z), so every
+    // workgroup of one (sequence, kv head) pair has the same id mod 8 and the hardware deals
+    // them all to the same XCD.  geom = Hkv | g << 16.
+    const int Hkv = static_cast<int>(geom & 0xffffu), g = static_cast<int>(geom >> 16);
+    const int xcd = blockIdx.x & (tmv::kXcds - 1), rbk = blockIdx.x >> 3;
+    const int split = blockIdx.y, splits = gridDim.y;
+    const int pair = blockIdx.z * tmv::kXcds + xcd;
     if (pair >= pairs) return;
-    const int within = slot % per_pair;
-    const int rbk = within / splits, split = within % splits;
-    const int b = pair / Hkv, kvh = pair % Hkv;
+    const int b = pair / Hkv, kvh = pair - b * Hkv;
+    // row r -> node r / g + 1 by a multiply: exact for r < 4096 and g <= 16
+    const int g_magic = (65536 + g - 1) / g;
+    auto node_of = [&](int r) { return ((r * g_magic) >> 16) + 1; };
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);     // wave-uniform
@@ -1088,7 +1097,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         }
     } else {
         // the first round goes out before anything else is loaded or waited for
-        issue_round(0, ring0);
+        issue_round(0, ring);
     }
 
     // ---- the prologue's loads, between the first and the second round of copies (vector
@@ -1100,17 +1109,18 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     const int M = __builtin_amdgcn_readfirstlane(n_nodes[b]);
     const int P = __builtin_amdgcn_readfirstlane(prefix_len[b]);
     int st = __builtin_amdgcn_readfirstlane(status[b]);
-    const int g = Hq / Hkv;
     bf16x8_t qf[2][KS];
     int dep[2], ancq[2][4];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
         int r = row0 + rt * 16 + c16;
         if (r > M_max * g - 1) r = M_max * g - 1;
-        const int j = r / g + 1, gi = r % g;
+        const int j = node_of(r), gi = r - (j - 1) * g;
         const uint16_t *qp = q + b * qs0 + static_cast<int64_t>(j - 1) * qs1 + static_cast<int64_t>(kvh * g + gi) * qs2 + G * 8;
+        // (with a shared query tile each token group loads one k-step: see below)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = load_bf16x8(qp + ks * 32);
+        for (int ks = 0; ks < KS; ++ks)
+            if (!kShareQ || ks == tw) qf[rt][ks] = load_bf16x8(qp + ks * 32);
         dep[rt] = depth[static_cast<int64_t>(b) * R + j];
         const int32_t *arow = anc + (static_cast<int64_t>(b) * R + j) * W;
 #pragma unroll
@@ -1119,7 +1129,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
             ancq[rt][k] = arow[kk < W ? kk : W - 1];
         }
     }
-    if constexpr (!PAGED) issue_round(1, ring1);
+    if constexpr (!PAGED) issue_round(1, ring + kHalfBytes);
     if constexpr (PAGED) {
         // stage the entries (invalid ones as -1; each wave records the first invalid one),
         // then issue the first two rounds from them
@@ -1141,8 +1151,8 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         }
         if (lane == 0) pg_bad[wave] = bad_min;
         __syncthreads();
-        issue_round(0, ring0);
-        issue_round(1, ring1);
+        issue_round(0, ring);
+        issue_round(1, ring + kHalfBytes);
     }
 
     if (st == TMV_OK && (M < 0 || M > M_max || P < 0 || static_cast<int64_t>(P) + M > L_cap)) {
@@ -1169,7 +1179,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
             for (int rt = 0; rt < 2; ++rt) {
                 const int r = row0 + rt * 16 + c16;
                 if (r >= M_max * g) continue;
-                const int j = r / g + 1, gi = r % g;
+                const int j = node_of(r), gi = r - (j - 1) * g;
                 uint16_t *o = out + b * os0 + static_cast<int64_t>(j - 1) * os1 + static_cast<int64_t>(kvh * g + gi) * os2 + G * (D / 4);
 #pragma unroll
                 for (int e = 0; e < D / 4; e += 8) *reinterpret_cast<uint4 *>(o + e) = make_uint4(0, 0, 0, 0);
@@ -1214,7 +1224,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
             if (4 * G + k < dp) set_bit(ancq[rt][k] - 1);
         if (DEEP && dp > kAncBatch) {
             // deep rows: the rest of the path, one batch of loads per round trip
-            const int j = r / g + 1;
+            const int j = node_of(r);
             const int32_t *arow = anc + (static_cast<int64_t>(b) * R + j) * W;
             for (int k0 = kAncBatch; k0 < dp; k0 += kAncBatch) {
                 int e[4];
@@ -1239,6 +1249,30 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
             const auto x32 = __builtin_amdgcn_permlane32_swap(y, y, false, false);
             mw[rt][w] = x32[0] | x32[1];
         }
+
+    if constexpr (kShareQ) {
+        // exchange the query k-steps: write this wave's, barrier, read all (LDS operations
+        // in inline assembly: a compiler-written one would first wait for every copy in flight)
+        const uint32_t qb = lds_addr(reinterpret_cast<const char *>(q_x));
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                if (ks == tw) lds_write16(qb + (((rw * 2 + rt) * KS + ks) * kWave + lane) * 16, __builtin_bit_cast(u32x4_t, qf[rt][ks]));
+        __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
+        __builtin_amdgcn_s_barrier();
+        uint32_t qa[2 * KS];
+        u32x4_t qv[2 * KS];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qa[rt * KS + ks] = qb + (((rw * 2 + rt) * KS + ks) * kWave + lane) * 16;
+        lds_read_b128_x8(qv, qa);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = __builtin_bit_cast(bf16x8_t, qv[rt * KS + ks]);
+    }
 
     // LDS read offsets of the MFMA operands inside a slot (constant per lane).  K
     // fragment (tt, ks): row tt*16 + c16, logical piece ks*4 + G.  V^T: lane reads row
@@ -1361,6 +1395,9 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
 
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) { mref[rt] = -INFINITY; mtrue[rt] = -INFINITY; }
+    // (the pass, round and slot loops stay rolled: one copy of the chunk code keeps the
+    // kernel small enough for the instruction cache)
+#pragma unroll 1
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
@@ -1369,17 +1406,19 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
             for (int nt = 0; nt < NT; ++nt) oacc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
         if (pass > 0) {
-            issue_round(0, ring0);
-            issue_round(1, ring1);
+            issue_round(0, ring);
+            issue_round(1, ring + kHalfBytes);
         }
-        // Round r: wait until this wave's copies of round r have landed (round r + 1 may
-        // still be in flight: vector-memory operations complete in issue order and every
-        // wave issued exactly kRound * kDW copies for round r + 1 after round r, plus
-        // only operations that are needed here anyway), barrier so every wave's share is
-        // visible, compute, barrier so no wave still reads the half, then refill it with
-        // round r + 2.  The barriers carry no memory fence on purpose: a fence would wait
-        // for all copies in flight.
-        auto run_round = [&](int r, char *half) {
+        // Round r (ring half r % 2): wait until this wave's copies of round r have landed
+        // (round r + 1 may still be in flight: vector-memory operations complete in issue
+        // order and every wave issued exactly kRound * kDW copies for round r + 1 after
+        // round r, plus only operations that are needed here anyway), barrier so every
+        // wave's share is visible, compute, barrier so no wave still reads the half, then
+        // refill it with round r + 2.  The barriers carry no memory fence on purpose: a
+        // fence would wait for all copies in flight.
+#pragma unroll 1
+        for (int r = 0; r < nrounds; ++r) {
+            char *half = ring + (r & 1) * kHalfBytes;
             if (r + 2 < nrounds) prefetch_pages(r + 2);
             if (r + 1 < nrounds) __builtin_amdgcn_s_waitcnt(kVmcntRound<RS::kRound * kDW>());
             else __builtin_amdgcn_s_waitcnt(kVmcntZero);
@@ -1393,19 +1432,15 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
                 __builtin_amdgcn_s_barrier();
             }
             if (wave_live) {
-#pragma unroll
-                for (int j = 0; j < RS::kRound; ++j) {
+#pragma unroll 1
+                for (int j = tw; j < RS::kRound; j += TW) {
                     const int k = r * RS::kRound + j;
-                    if (k < nk && (j % TW) == tw) compute_chunk(lds_addr(half) + j * RS::kSlotBytes, split + k * splits);
+                    if (k < nk) compute_chunk(lds_addr(half) + j * RS::kSlotBytes, split + k * splits);
                 }
             }
             __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
             __builtin_amdgcn_s_barrier();
             if (r + 2 < nrounds) issue_round(r + 2, half, true);
-        };
-        for (int r = 0; r < nrounds; r += 2) {
-            run_round(r, ring0);
-            if (r + 1 < nrounds) run_round(r + 1, ring1);
         }
         __builtin_amdgcn_s_waitcnt(kVmcntZero);   // nothing may land in LDS after this
         // the decision is the workgroup's: every wave must take the same number of passes,
@@ -1456,14 +1491,11 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         if (threadIdx.x == 0) __hip_atomic_store(ws_cnt + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // one round trip for the partials of up to 8 splits and up to 2 items per thread
         constexpr int kIpt = (RB * (D / 8) + kThreads - 1) / kThreads;
-        if (splits <= 4)
-            merge_block<D, RB, (kIpt < 4 ? kIpt : 4), 4>(unit, splits, b, kvh, g, row0_wg, M_max, L_cap, M, P, st,
-                                                          depth, out, os0, os1, os2, ws_stats, ws_o);
-        else if (splits <= 8)
-            merge_block<D, RB, (kIpt < 2 ? kIpt : 2), 8>(unit, splits, b, kvh, g, row0_wg, M_max, L_cap, M, P, st,
+        if (splits <= 8)
+            merge_block<D, RB, (kIpt < 2 ? kIpt : 2), 8>(unit, splits, b, kvh, g, g_magic, row0_wg, M_max, L_cap, M, P, st,
                                                           depth, out, os0, os1, os2, ws_stats, ws_o);
         else
-            merge_block<D, RB, 1, 16>(unit, splits, b, kvh, g, row0_wg, M_max, L_cap, M, P, st, depth, out, os0,
+            merge_block<D, RB, 1, 16>(unit, splits, b, kvh, g, g_magic, row0_wg, M_max, L_cap, M, P, st, depth, out, os0,
                                       os1, os2, ws_stats, ws_o);
     };
     // row `rr` of the workgroup's block, dims d0 .. d0 + n - 1 (n a multiple of 8) of the
@@ -1471,7 +1503,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     auto write_row = [&](int rr, int d0, const float *x, int n, float l) {
         const int r = row0_wg + rr;
         if (r >= M_max * g) return;
-        const int j = r / g + 1, gi = r % g;
+        const int j = node_of(r), gi = r - (j - 1) * g;
         const bool live = r < Rh && depth[static_cast<int64_t>(b) * R + j] >= 1;
         const float inv = live && l > 0.f ? 1.f / l : 0.f;
         uint16_t *o = out + b * os0 + static_cast<int64_t>(j - 1) * os1 + static_cast<int64_t>(kvh * g + gi) * os2 + d0;
@@ -1491,8 +1523,8 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         // the idle ring (16 KB per wave; 4-float groups XOR-swizzled by row so the parked
         // writes are free of bank conflicts), then each wave combines its share of its row
         // group's rows over the group's TW waves in a fixed order.
-        static_assert(kRingWaves * kRowsPerWave * D * 4 == 2 * sizeof(ring0), "park area = ring");
-        auto parked = [&](int w) { return reinterpret_cast<float *>((w < 4 ? ring0 : ring1) + (w & 3) * kRowsPerWave * D * 4); };
+        static_assert(kRingWaves * kRowsPerWave * D * 4 == sizeof(ring), "park area = ring");
+        auto parked = [&](int w) { return reinterpret_cast<float *>(ring + w * kRowsPerWave * D * 4); };
         {
             float *o = parked(wave);
 #pragma unroll
@@ -1582,7 +1614,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         for (int rt = 0; rt < 2; ++rt) {
             const int r = row0 + rt * 16 + c16;
             if (r >= M_max * g) continue;
-            const int j = r / g + 1, gi = r % g;
+            const int j = node_of(r), gi = r - (j - 1) * g;
             const bool live = r < Rh && depth[static_cast<int64_t>(b) * R + j] >= 1;
             const float inv = live && lrow[rt] > 0.f ? 1.f / lrow[rt] : 0.f;
             uint16_t *o = out + b * os0 + static_cast<int64_t>(j - 1) * os1 + static_cast<int64_t>(kvh * g + gi) * os2 + 4 * G;
@@ -1745,15 +1777,15 @@ void launch_bf16(const AttnPlan &p, hipStream_t s, int M_max, int D_max, int Hq,
     } else {
         // the ring kernel merges its splits itself (the last split of a row block to arrive)
         uint16_t *part = reinterpret_cast<uint16_t *>(w + off_o);
-        const uint32_t geom = static_cast<uint32_t>(p.splits) | (static_cast<uint32_t>(p.per_pair) << 5) |
-                              (static_cast<uint32_t>(Hkv) << 16);
+        const uint32_t geom = static_cast<uint32_t>(Hkv) | (static_cast<uint32_t>(Hq / Hkv) << 16);
+        const dim3 grid(tmv::kXcds * p.nb, p.splits, (p.pairs + tmv::kXcds - 1) / tmv::kXcds);
         const PagedArgs pgv = pg ? *pg : PagedArgs{nullptr, 0, 0, 0};
 #define TMV_LAUNCH_ATTN(DEEP, PAGED)                                                                       \
-        hipLaunchKernelGGL((tree_attn_bf16_kernel<D, WR, DEEP, PAGED>), dim3(p.slots * tmv::kXcds),      \
+        hipLaunchKernelGGL((tree_attn_bf16_kernel<D, WR, DEEP, PAGED>), grid,                             \
                            dim3(kRingWaves * kWave), 0, s, static_cast<const uint16_t *>(k),              \
                            static_cast<const uint16_t *>(v), P, n, static_cast<uint32_t>(kvs[0] / 8),     \
                            static_cast<uint32_t>(kvs[1] / 8), static_cast<uint32_t>(kvs[2] / 8), L_cap,   \
-                           p.pairs, geom, M_max, D_max, Hq, p.nb, static_cast<const uint16_t *>(q), qs[0], \
+                           p.pairs, geom, M_max, D_max, p.nb, static_cast<const uint16_t *>(q), qs[0],    \
                            qs[1], qs[2], anc, dep, status, scale * kLog2e, static_cast<uint16_t *>(out),   \
                            os[0], os[1], os[2], stats, part, cnt, pgv)
         if (pg) {
@@ -1792,8 +1824,9 @@ void dispatch_bf16(const AttnPlan &p, int d, hipStream_t s, int M_max, int D_max
 // the plan's workspace and grid fit the kernels' 32-bit offsets
 bool plan_fits(const AttnPlan &p, int d) {
     const int64_t part_rows = static_cast<int64_t>(p.pairs) * p.nb * p.splits * p.rb;
+    // (ring kernel grid: (8 nb, splits, ceil(pairs / 8)); streaming kernel: 8 slots)
     return part_rows * d * 4 < (int64_t(1) << 31) && static_cast<int64_t>(p.slots) * tmv::kXcds <= 0x7fffffff &&
-           p.per_pair <= 2047;
+           (p.pairs + tmv::kXcds - 1) / tmv::kXcds <= 65535;
 }
 
 size_t attention_workspace(int dtype, int B, int M_max, int Hq, int Hkv, int d, int L_cap, int force_rows,

@@ -207,6 +207,27 @@ int tmv_tree_verify_attention_paged(int dtype, int B, int M_max, int D_max, int 
                                     const int32_t *anc, const int32_t *depth, int32_t *status,
                                     float scale, void *out, const int64_t *o_stride,
                                     void *workspace, size_t workspace_bytes, void *stream);
+/*
+ * tmv_tree_verify_attention_noalloc -- tmv_tree_verify_attention without a workspace, for
+ * callers that cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and per-sequence errors;
+ * the call allocates nothing.  Its scratch (arrival counters and split partials) is a
+ * fixed 32 MiB array on every device the library runs on, held until the process ends
+ * and cleared by a small kernel on the device's first call.
+ *   - A call whose workspace (tmv_tree_verify_attention_workspace) exceeds 32 MiB returns
+ *     TMV_ERR_ARG and launches nothing.
+ *   - Every call on one device shares that device's array: calls that may overlap on one
+ *     device (different streams, or host threads) race and must be serialised by the
+ *     caller.  A completed call leaves the array ready for the next one.
+ */
+int tmv_tree_verify_attention_noalloc(int dtype, int B, int M_max, int D_max, int Hq, int Hkv, int d,
+                                      const void *q, const int64_t *q_stride,
+                                      const void *k_cache, const void *v_cache,
+                                      const int64_t *kv_stride, int L_cap,
+                                      const int32_t *prefix_len, const int32_t *n_nodes,
+                                      const int32_t *anc, const int32_t *depth, int32_t *status,
+                                      float scale, void *out, const int64_t *o_stride, void *stream);
+
 /* The paged call with its launch plan pinned, as tmv_tree_verify_attention_plan. */
 size_t tmv_tree_verify_attention_paged_plan_workspace(int B, int M_max, int Hq, int Hkv, int d, int page_size,
                                                       int max_blocks, int rows_per_group, int splits);

@@ -48,6 +48,8 @@ _lib.tmv_tree_verify_attention_plan_workspace.argtypes = [_I, _I, _I, _I, _I, _I
 _lib.tmv_tree_verify_attention_plan_workspace.restype = _SZ
 _lib.tmv_tree_verify_attention_plan.argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P,
                                                 _F, _P, _P, _I, _I, _P, _SZ, _P]
+_lib.tmv_tree_verify_attention_noalloc.argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P,
+                                                   _P, _F, _P, _P, _P]
 _lib.tmv_tree_accept_workspace.argtypes = [_I, _I, _I, _I]
 _lib.tmv_tree_accept_workspace.restype = _SZ
 _lib.tmv_tree_accept.argtypes = [_I, _I, _I, _I, _I, _P, _I, _P, _I64, _I64, _P, _I64, _I64, _U64, _U64,
@@ -74,7 +76,7 @@ EXPORTED = ("tmv_status_string", "tmv_abi_version", "tmv_tree_build_ancestors",
             "tmv_tree_verify_attention_paged_workspace", "tmv_tree_verify_attention_paged",
             "tmv_kv_commit_path_paged", "tmv_tree_verify_attention_plan_workspace",
             "tmv_tree_verify_attention_plan", "tmv_tree_verify_attention_paged_plan_workspace",
-            "tmv_tree_verify_attention_paged_plan")
+            "tmv_tree_verify_attention_paged_plan", "tmv_tree_verify_attention_noalloc")
 
 
 class TmvError(RuntimeError):

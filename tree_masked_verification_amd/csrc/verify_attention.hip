@@ -32,6 +32,7 @@
 // fp32 (tree_attn_f32_kernel): one wave per (node, query head), plain FMA.
 #include <cstdlib>
 #include <cstdio>
+#include <mutex>
 
 #include "tmv_device.hpp"
 
@@ -2034,4 +2035,65 @@ extern "C" int tmv_tree_verify_attention_paged_plan(int dtype, int B, int M_max,
     return paged_attention(dtype, B, M_max, D_max, Hq, Hkv, d, q, q_stride, k_pages, v_pages, page_stride, num_pages,
                            page_size, block_table, table_stride, max_blocks, prefix_len, n_nodes, anc, depth, status,
                            scale, out, o_stride, rows_per_group, splits, workspace, workspace_bytes, stream);
+}
+
+// --------------------------------------------------------------------------- allocation-free call
+// Scratch memory of tmv_tree_verify_attention_noalloc: a fixed array on every device the
+// library runs on, held until the process ends.  Host code never uses this name as an
+// address (on the host it is only a stand-in): the device address comes from
+// hipGetSymbolAddress, once per device, and is what the kernels receive.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// zeroes n 32-bit words (the arrival counters; a kernel rather than a memset, so a caller
+// may capture the first call in a graph)
+__global__ void __launch_bounds__(256) scratch_clear_kernel(uint32_t *p, int n) {
+    for (int i = threadIdx.x; i < n; i += 256) p[i] = 0u;
+}
+
+// the current device's scratch address; on the device's first call also queues the
+// clearing of the counter block on `s` (the array is zero when loaded; the clear makes
+// that explicit and costs one tiny launch per device)
+int noalloc_scratch(hipStream_t s, void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TMV_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return TMV_ERR_DEVICE;
+        hipLaunchKernelGGL(scratch_clear_kernel, dim3(1), dim3(256), 0, s, static_cast<uint32_t *>(ptr),
+                           static_cast<int>(kCounterBytes / 4));
+        if (hipGetLastError() != hipSuccess) return TMV_ERR_DEVICE;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return TMV_OK;
+}
+
+}  // namespace
+
+extern "C" int tmv_tree_verify_attention_noalloc(int dtype, int B, int M_max, int D_max, int Hq, int Hkv, int d,
+                                                 const void *q, const int64_t *q_stride,
+                                                 const void *k_cache, const void *v_cache,
+                                                 const int64_t *kv_stride, int L_cap,
+                                                 const int32_t *prefix_len, const int32_t *n_nodes,
+                                                 const int32_t *anc, const int32_t *depth, int32_t *status,
+                                                 float scale, void *out, const int64_t *o_stride, void *stream)
+{
+    // the workspace this call needs must fit the fixed scratch (nothing is launched otherwise)
+    if (dtype == TMV_BF16 && B > 0 && M_max > 0 &&
+        attention_workspace(dtype, B, M_max, Hq, Hkv, d, L_cap, 0, 0) > kNoAllocScratchBytes)
+        return TMV_ERR_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void *ws = nullptr;
+    const int rc = noalloc_scratch(s, &ws);
+    if (rc != TMV_OK) return rc;
+    return attention(dtype, B, M_max, D_max, Hq, Hkv, d, q, q_stride, k_cache, v_cache, kv_stride, L_cap, prefix_len,
+                     n_nodes, anc, depth, status, scale, out, o_stride, 0, 0, ws, kNoAllocScratchBytes, stream);
 }

@@ -63,6 +63,7 @@ def _load():
         lib.tmvref_accept_greedy.argtypes = [I, I, I, I, P, I, P, I64, I64, P, P, P, P, P, P, P]
         lib.tmvref_accept_sample.argtypes = [I, I, I, I, P, P, P, U64, U64, P, P, P, P, P, P, P]
         lib.tmvref_commit.argtypes = [I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
+        lib.tmvref_lm_head_logits.argtypes = [I, I, I, P, P, I64, P, P]
         lib.tmvref_philox_words.argtypes = [U64, U64, I64, P]
         lib.tmvref_philox_words.restype = None
         lib.tmvref_sample_accept_test.argtypes = [U64, U64, U64, U64, U64, U64, U64]
@@ -145,6 +146,20 @@ def accept_greedy(tokens, logits, n_nodes, anc, depth, status, row_dtype=F32):
                                         R * V, V, _p(_c(n_nodes, np.int32)), _p(_c(anc, np.int32)),
                                         _p(_c(depth, np.int32)), _p(st), _p(A), _p(path), _p(nxt)))
     return A, path, nxt, st
+
+
+def lm_head_logits(h_bits, w_bits, with_bound=True):
+    """fp64 logits of the rows h_bits [n][K] (bf16 bit patterns) against the LM head
+    w_bits [V][K]: (logits [n][V], bound [n][V] = sum_k |h w| or None)."""
+    h = _c(h_bits, np.uint16)
+    w = _c(w_bits, np.uint16)
+    n, K = h.shape
+    V = w.shape[0]
+    assert w.shape[1] == K
+    logits = np.zeros((n, V), np.float64)
+    bound = np.zeros((n, V), np.float64) if with_bound else None
+    _check(_load().tmvref_lm_head_logits(n, K, V, _p(h), _p(w), K, _p(logits), _p(bound) if with_bound else None))
+    return logits, bound
 
 
 def accept_sample(tokens, p, q, seed, step, n_nodes, anc, depth, status):

@@ -282,6 +282,35 @@ int tmvref_accept_greedy(int B, int M_max, int D_max, int V, const int32_t *toke
 }
 
 /* ------------------------------------------------------------------------------------
+ * LM-head logits in fp64 (the teacher's projection whose argmax the greedy rule takes)
+ * [SDH roofline section: decode reads the LM-head weights once per step; the argmax of
+ * each verified row's logits is the teacher's greedy choice of the Medusa section].
+ *   logits[i][x] = sum_k h[i][k] * w[x][k], h and w bf16 bit patterns widened exactly;
+ *   bound[i][x]  = sum_k |h[i][k] * w[x][k]| (the scale of the rounding error any fp32
+ *                  accumulation order can make: at most K * 2^-24 * bound), or NULL.
+ *   h [n][K] contiguous, w row x at x * w_stride.
+ * ---------------------------------------------------------------------------------- */
+int tmvref_lm_head_logits(int n, int K, int V, const uint16_t *h, const uint16_t *w, int64_t w_stride,
+                          double *logits, double *bound)
+{
+    if (n < 0 || K < 0 || V < 0 || w_stride < K) return REF_ERR_ARG;
+    for (int i = 0; i < n; ++i) {
+        for (int x = 0; x < V; ++x) {
+            double acc = 0.0, mag = 0.0;
+            for (int k = 0; k < K; ++k) {
+                const double pr = load_elem(h, REF_BF16, (int64_t)i * K + k) *
+                                  load_elem(w, REF_BF16, (int64_t)x * w_stride + k);
+                acc += pr;
+                mag += fabs(pr);
+            }
+            logits[(int64_t)i * V + x] = acc;
+            if (bound) bound[(int64_t)i * V + x] = mag;
+        }
+    }
+    return REF_OK;
+}
+
+/* ------------------------------------------------------------------------------------
  * Philox4x64-10 (Salmon et al., "Parallel random numbers: as easy as 1, 2, 3", SC'11):
  * 10 rounds of two 64x64->128 multiplies with the published multipliers and Weyl key
  * increments.

@@ -306,6 +306,39 @@ int tmv_tree_accept(int mode, int B, int M_max, int D_max, int V,
                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * tmv_tree_accept_lm_head -- greedy acceptance straight from the teacher's LM head: the
+ * logits of row u are hidden_u . W^T, and only their argmax t(u) is needed, so the logits
+ * are reduced to t(u) as an MFMA GEMM produces them and are never written (roofline
+ * section of "Speculative Decoding Hierarquico: Medusa, EAGLE-2 e Multi-Token Prediction":
+ * decode is bound by reading weights; the LM head is read once per step).  The path rule
+ * is exactly tmv_tree_accept's GREEDY rule on those logits.
+ *   K          hidden size, a multiple of 32.
+ *   hidden     bf16 [B][M_max+1][K], element strides {h_stride_b, h_stride_row}, K
+ *              contiguous: row u holds the teacher's final hidden state after node u (row 0:
+ *              after the committed prefix).
+ *   lm_head    bf16 [V][K], row x at x * w_stride_row (>= K), K contiguous.
+ *   Arithmetic: bf16 products accumulated in fp32 (v_mfma_f32_16x16x32_bf16), so t(u) is
+ *              the argmax of fp32 sums; it agrees with the exact argmax wherever the top two
+ *              logits differ by more than the fp32 accumulation error (K * 2^-24 *
+ *              sum_k |h_k w_k| for each of them).  Ties: smallest token.  A NaN logit in a
+ *              live row sets TMV_ERR_INPUT.
+ *   row_argmax int32 [B][M_max+1] or NULL: t(u) of every live row, -1 elsewhere.
+ *   Other arguments and outputs as tmv_tree_accept (GREEDY).
+ *   Requires hidden, lm_head and the workspace 16-byte aligned, strides multiples of 8
+ *   elements, and both tensors spanning less than 2 GiB (TMV_ERR_ARG otherwise).
+ *   workspace: tmv_tree_accept_lm_head_workspace() bytes, 16-byte aligned: one 64-bit key
+ *   per row, merged with atomics.  Zero-fill it once before its first use; every completed
+ *   call leaves it zero.
+ */
+size_t tmv_tree_accept_lm_head_workspace(int B, int M_max);
+int tmv_tree_accept_lm_head(int B, int M_max, int D_max, int K, int V, const int32_t *tokens,
+                            const void *hidden, int64_t h_stride_b, int64_t h_stride_row,
+                            const void *lm_head, int64_t w_stride_row,
+                            const int32_t *n_nodes, const int32_t *anc, const int32_t *depth,
+                            int32_t *status, int32_t *accept_len, int32_t *path, int32_t *next_token,
+                            int32_t *row_argmax, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * tmv_kv_commit_path -- prefix-sharing path-index commit, in place.
  * Defined by section 2.1 of the Chinese EAGLE-Pangu technical summary (commit by
  * accepted length or by path index; a prefix-sharing fast reorder moves only the newly

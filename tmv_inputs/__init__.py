@@ -394,6 +394,32 @@ def small_sampling_case(rng, B, M, V, max_depth, overlap=None, dist_sigma=2.0, t
     return _pad_parents(trees, M), np.full(B, M, np.int32), tokens, p, q
 
 
+def lm_head_weights(rng, V: int, K: int, sigma: float, chunk: int = 8192) -> np.ndarray:
+    """Synthetic LM-head weights [V][K] as bf16 bits: N(0, sigma) drawn in fp32, in chunks
+    of rows (the full 8B-shaped head is 1 GiB of bf16)."""
+    out = np.empty((V, K), np.uint16)
+    for v0 in range(0, V, chunk):
+        v1 = min(V, v0 + chunk)
+        out[v0:v1] = bf16_bits(rng.standard_normal((v1 - v0, K), dtype=np.float32) * np.float32(sigma))
+    return out
+
+
+def plant_from_argmax(rng, parents, M, V, t_row, tokens_b, alpha=0.7):
+    """Draft tokens of one tree given the teacher's choices t_row[u]: at each node with
+    children, with probability alpha one child gets t_row[u]; the other children get
+    distinct tokens different from it."""
+    kids = children_lists(parents, M)
+    for u in range(M + 1):
+        ch = kids[u]
+        if not ch:
+            continue
+        x = int(t_row[u])
+        star = int(rng.integers(0, len(ch))) if rng.random() < alpha else -1
+        others = [y for y in rng.choice(V, size=min(V, len(ch) + 2), replace=False).tolist() if y != x]
+        for ci, c in enumerate(ch):
+            tokens_b[c] = x if ci == star else others[ci % len(others)]
+
+
 def cache_pattern_value(layer, b, head, slot, dim):
     """Deterministic cache contents for the multi-layer commit workload: every row is
     tagged by its coordinates, so a row moved to the wrong place is visible.  Values are

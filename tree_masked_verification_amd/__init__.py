@@ -54,6 +54,10 @@ _lib.tmv_tree_accept_workspace.argtypes = [_I, _I, _I, _I]
 _lib.tmv_tree_accept_workspace.restype = _SZ
 _lib.tmv_tree_accept.argtypes = [_I, _I, _I, _I, _I, _P, _I, _P, _I64, _I64, _P, _I64, _I64, _U64, _U64,
                                  _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+_lib.tmv_tree_accept_lm_head_workspace.argtypes = [_I, _I]
+_lib.tmv_tree_accept_lm_head_workspace.restype = _SZ
+_lib.tmv_tree_accept_lm_head.argtypes = [_I, _I, _I, _I, _I, _P, _P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P,
+                                         _P, _P, _SZ, _P]
 _lib.tmv_kv_commit_path.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.tmv_tree_verify_attention_paged_workspace.argtypes = [_I, _I, _I, _I, _I, _I, _I]
 _lib.tmv_tree_verify_attention_paged_workspace.restype = _SZ
@@ -76,7 +80,8 @@ EXPORTED = ("tmv_status_string", "tmv_abi_version", "tmv_tree_build_ancestors",
             "tmv_tree_verify_attention_paged_workspace", "tmv_tree_verify_attention_paged",
             "tmv_kv_commit_path_paged", "tmv_tree_verify_attention_plan_workspace",
             "tmv_tree_verify_attention_plan", "tmv_tree_verify_attention_paged_plan_workspace",
-            "tmv_tree_verify_attention_paged_plan", "tmv_tree_verify_attention_noalloc")
+            "tmv_tree_verify_attention_paged_plan", "tmv_tree_verify_attention_noalloc",
+            "tmv_tree_accept_lm_head_workspace", "tmv_tree_accept_lm_head")
 
 
 class TmvError(RuntimeError):
@@ -298,6 +303,39 @@ def tree_accept(mode, tokens, teacher, n_nodes, anc, depth, status, accept_len, 
                                 _ptr(status), _ptr(accept_len), _ptr(path), _ptr(next_token), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(stream)),
            "tree_accept")
+
+
+def tree_accept_lm_head_workspace(B, M_max) -> int:
+    return int(_lib.tmv_tree_accept_lm_head_workspace(B, M_max))
+
+
+def tree_accept_lm_head(tokens, hidden, lm_head, n_nodes, anc, depth, status, accept_len, path, next_token,
+                        row_argmax=None, workspace=None, stream=None):
+    """Greedy acceptance from the LM head: hidden bf16 [B][M_max+1][K], lm_head bf16 [V][K]
+    (K contiguous).  Outputs as tree_accept; row_argmax int32 [B][M_max+1] (optional)."""
+    _i32(tokens, n_nodes, anc, depth, status, accept_len, path, next_token, row_argmax)
+    if hidden.dtype != torch.bfloat16 or lm_head.dtype != torch.bfloat16:
+        raise TypeError("hidden and lm_head must be bfloat16")
+    if hidden.dim() != 3 or lm_head.dim() != 2 or hidden.stride(2) != 1 or lm_head.stride(1) != 1:
+        raise ValueError("hidden [B][M_max+1][K] and lm_head [V][K] with K contiguous")
+    B, R, K = hidden.shape
+    V = lm_head.shape[0]
+    if lm_head.shape[1] != K:
+        raise ValueError("lm_head must be [V][K]")
+    _check_tree_tables(B, R - 1, anc, depth, "tree_accept_lm_head")
+    D_max = anc.shape[2] - 1
+    _shape(tokens, (B, R), "tokens")
+    _shape(path, (B, D_max), "path")
+    _shape(row_argmax, (B, R), "row_argmax")
+    _vec(B, "n_nodes / status / accept_len / next_token", n_nodes, status, accept_len, next_token)
+    if workspace is None:
+        workspace = _temp_workspace(tree_accept_lm_head_workspace(B, R - 1), hidden.device, stream, zero=True)
+    _check(_lib.tmv_tree_accept_lm_head(B, R - 1, D_max, K, V, _ptr(tokens), _ptr(hidden), hidden.stride(0),
+                                        hidden.stride(1), _ptr(lm_head), lm_head.stride(0), _ptr(n_nodes), _ptr(anc),
+                                        _ptr(depth), _ptr(status), _ptr(accept_len), _ptr(path), _ptr(next_token),
+                                        _ptr(row_argmax), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                        _stream(stream)),
+           "tree_accept_lm_head")
 
 
 # ------------------------------------------------------------------------ stage 4

@@ -118,12 +118,16 @@ greedy_scan_kernel(int M_max, int V, int nchunk, const void *__restrict__ teache
 
 // One workgroup per sequence, after the scan: merge the chunk keys of every live row into
 // t(u), check the draft tokens, mark matching nodes and pick the deepest (smallest id).
+// (clear_keys: every key read is set back to zero -- the LM-head path accumulates its keys
+// with atomics into a zeroed workspace; row_argmax, if not null, receives t(u) of every live
+// row and -1 elsewhere)
 __global__ void __launch_bounds__(kScanThreads)
 greedy_select_kernel(int M_max, int D_max, int V, int nchunk, const int32_t *__restrict__ tokens,
                      const int32_t *__restrict__ n_nodes, const int32_t *__restrict__ anc,
                      const int32_t *__restrict__ depth, int32_t *__restrict__ status,
                      int32_t *__restrict__ accept_len, int32_t *__restrict__ path,
-                     int32_t *__restrict__ next_token, const uint64_t *__restrict__ keys)
+                     int32_t *__restrict__ next_token, uint64_t *__restrict__ keys, int clear_keys,
+                     int32_t *__restrict__ row_argmax)
 {
     constexpr int kKeyBatch = 32;                  // chunk keys per row fetched at once
     constexpr int kAncBatch = 8;                   // ancestor entries per node fetched at once
@@ -170,11 +174,14 @@ greedy_select_kernel(int M_max, int D_max, int V, int nchunk, const int32_t *__r
             const uint64_t kc = keys[rb * nchunk + c];
             k = kc > k ? kc : k;
         }
+        if (clear_keys)
+            for (int c = 0; c < nchunk; ++c) keys[rb * nchunk + c] = 0;
         if (k == kNanKey) bad = 1;
         tsel[tid] = static_cast<int32_t>(0xffffffffu - static_cast<uint32_t>(k & 0xffffffffu));
         if (tid > 0 && (tok < 0 || tok >= V)) bad = 1;
     }
     __syncthreads();
+    if (row_argmax && tid < R) row_argmax[rb] = (bad || !row_live) ? -1 : tsel[tid];
     if (bad) {
         for (int j = tid; j < D_max; j += kScanThreads) pth[j] = 0;
         if (tid == 0) {
@@ -219,6 +226,156 @@ greedy_select_kernel(int M_max, int D_max, int V, int nchunk, const int32_t *__r
     for (int j = tid; j < D_max; j += kScanThreads) {
         const int e = dstar - 1 - j;
         pth[j] = j >= dstar ? 0 : e < kAncBatch ? anc_sh[star][e] : anc[(static_cast<int64_t>(b) * R + star) * W + e];
+    }
+}
+
+// ============================================================== greedy on LM-head logits
+// The teacher's logits of row u are h_u W^T: its final hidden state h_u (K entries) against
+// the LM head W [V][K] (roofline section of "Speculative Decoding Hierarquico": decode
+// streams the LM-head weights once per step).  Only each row's argmax is needed, so the
+// logits are reduced to the greedy keys as the MFMA tiles produce them and never written:
+// per step that saves writing and re-reading rows x V fp32 logits, and the weights -- the
+// whole cost at a few dozen rows -- are read once.
+//   * a workgroup of 8 waves computes 256-entry vocabulary tiles for one block of 64 rows:
+//     wave w owns entries 32w .. +32 (two 16-entry MFMA row tiles) against the block's 64
+//     rows (four 16-row column tiles), v_mfma_f32_16x16x32_bf16 over K in 32-wide steps;
+//   * weights stream from HBM straight into registers, kLmDepth k-steps ahead; the rows'
+//     fragments are the same for all 8 waves, so after the first wave they come from L1;
+//   * each lane keeps, per row, the best (value, ~index) key over the tiles it computed;
+//     the keys are reduced over the lanes and waves of the workgroup and merged into the
+//     row's key in the workspace with one device-scope 64-bit atomic max per row, which the
+//     select kernel reads (and clears).  A NaN logit makes the row's key all ones.
+constexpr int kLmWaves = 8;
+constexpr int kLmThreads = kLmWaves * kWave;
+constexpr int kLmRows = 64;                            // rows per row block
+constexpr int kLmVocabPerWave = 32;
+constexpr int kLmTile = kLmWaves * kLmVocabPerWave;    // vocabulary entries per tile
+constexpr int kLmDepth = 4;                            // k-steps of loads in flight per wave
+constexpr int kLmBufferFlags = 0x00020000;             // raw buffer descriptor word 3 (gfx9 family)
+
+typedef __bf16 lm_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float lm_f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned lm_u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bool lm_row_live(int gr, int R, int M_max, const int32_t *__restrict__ n_nodes,
+                                            const int32_t *__restrict__ depth, const int32_t *__restrict__ status)
+{
+    const int b = gr / R, u = gr - b * R;
+    const int M = n_nodes[b];
+    return status[b] == TMV_OK && M >= 0 && M <= M_max && u <= M && (u == 0 || depth[gr] >= 1);
+}
+
+__global__ void __launch_bounds__(kLmThreads)
+lm_head_argmax_kernel(int B, int M_max, int K, int V, const uint16_t *__restrict__ hidden, int64_t hsb,
+                      int64_t hsr, uint32_t h_bytes, const uint16_t *__restrict__ w, int64_t wsr, uint32_t w_bytes,
+                      const int32_t *__restrict__ n_nodes, const int32_t *__restrict__ depth,
+                      const int32_t *__restrict__ status, uint64_t *__restrict__ row_keys, int ntiles)
+{
+    __shared__ uint64_t s_key[kLmWaves][kLmRows];
+    __shared__ int s_any;
+    const int R = M_max + 1, nrows = B * R;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int c16 = lane & 15, G = lane >> 4;
+    const int rb0 = blockIdx.y * kLmRows;
+
+    // a row block without a live row does nothing
+    if (threadIdx.x == 0) s_any = 0;
+    __syncthreads();
+    if (threadIdx.x < kLmRows && rb0 + static_cast<int>(threadIdx.x) < nrows &&
+        lm_row_live(rb0 + threadIdx.x, R, M_max, n_nodes, depth, status))
+        s_any = 1;
+    __syncthreads();
+    if (!s_any) return;
+
+    // B operands: row rb0 + rt*16 + c16 (clamped into the tensor; padding rows are never
+    // merged), k entries G*8 .. +8 of each 32-wide step
+    const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(hidden), 0,
+                                                                        static_cast<int>(h_bytes), kLmBufferFlags);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(w), 0,
+                                                                        static_cast<int>(w_bytes), kLmBufferFlags);
+    uint32_t hoff[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        int gr = rb0 + rt * 16 + c16;
+        if (gr > nrows - 1) gr = nrows - 1;
+        const int b = gr / R, u = gr - b * R;
+        hoff[rt] = static_cast<uint32_t>((b * hsb + u * hsr + G * 8) * 2);
+    }
+    const int nks = K / 32;
+    uint64_t best[4] = {0, 0, 0, 0};
+    bool nan[4] = {false, false, false, false};
+
+    for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int vbase = t * kLmTile + wave * kLmVocabPerWave;
+        uint32_t woff[2];
+#pragma unroll
+        for (int vt = 0; vt < 2; ++vt) {
+            int v = vbase + vt * 16 + c16;
+            if (v > V - 1) v = V - 1;
+            woff[vt] = static_cast<uint32_t>((v * wsr + G * 8) * 2);
+        }
+        lm_f32x4 acc[2][4];
+#pragma unroll
+        for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) acc[vt][rt] = lm_f32x4{0.f, 0.f, 0.f, 0.f};
+        lm_u32x4 wa[kLmDepth][2], hb[kLmDepth][4];
+        auto load_step = [&](int d, int ks) {
+#pragma unroll
+            for (int vt = 0; vt < 2; ++vt) wa[d][vt] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff[vt] + ks * 64, 0, 0);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) hb[d][rt] = __builtin_amdgcn_raw_buffer_load_b128(hr, hoff[rt] + ks * 64, 0, 0);
+        };
+#pragma unroll
+        for (int d = 0; d < kLmDepth; ++d)
+            if (d < nks) load_step(d, d);
+        for (int ks0 = 0; ks0 < nks; ks0 += kLmDepth) {
+#pragma unroll
+            for (int d = 0; d < kLmDepth; ++d) {
+                const int ks = ks0 + d;
+                if (ks < nks) {
+#pragma unroll
+                    for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+                        for (int rt = 0; rt < 4; ++rt)
+                            acc[vt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(lm_bf16x8, wa[d][vt]), __builtin_bit_cast(lm_bf16x8, hb[d][rt]),
+                                acc[vt][rt], 0, 0, 0);
+                    if (ks + kLmDepth < nks) load_step(d, ks + kLmDepth);
+                }
+            }
+        }
+        // lane holds row rt*16 + c16 at entries vbase + vt*16 + G*4 + i
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int v = vbase + vt * 16 + G * 4 + i;
+                    if (v < V) scan_one(acc[vt][rt][i], v, best[rt], nan[rt]);
+                }
+    }
+    // reduce over the four lanes of a row, then over the waves, and merge into the row's key
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        uint64_t k = nan[rt] ? kNanKey : best[rt];
+        uint64_t o = tmv::shfl_xor_u64(k, 16);
+        k = o > k ? o : k;
+        o = tmv::shfl_xor_u64(k, 32);
+        k = o > k ? o : k;
+        if (G == 0) s_key[wave][rt * 16 + c16] = k;
+    }
+    __syncthreads();
+    if (threadIdx.x < kLmRows) {
+        const int gr = rb0 + threadIdx.x;
+        uint64_t k = s_key[0][threadIdx.x];
+#pragma unroll
+        for (int w2 = 1; w2 < kLmWaves; ++w2) k = s_key[w2][threadIdx.x] > k ? s_key[w2][threadIdx.x] : k;
+        if (gr < nrows && lm_row_live(gr, R, M_max, n_nodes, depth, status))
+            __hip_atomic_fetch_max(reinterpret_cast<unsigned long long *>(row_keys + gr),
+                                   static_cast<unsigned long long>(k), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -922,7 +1079,8 @@ extern "C" int tmv_tree_accept(int mode, int B, int M_max, int D_max, int V,
             hipLaunchKernelGGL(greedy_scan_kernel<TMV_BF16>, dim3(static_cast<unsigned>(blocks)), dim3(kScanThreads), 0, s,
                                M_max, V, nchunk, teacher, t_stride_b, t_stride_row, n_nodes, depth, status, keys);
         hipLaunchKernelGGL(greedy_select_kernel, dim3(B), dim3(kScanThreads), 0, s, M_max, D_max, V, nchunk, tokens,
-                           n_nodes, anc, depth, status, accept_len, path, next_token, keys);
+                           n_nodes, anc, depth, status, accept_len, path, next_token, keys, 0,
+                           static_cast<int32_t *>(nullptr));
         return tmv_host::launch_status(hipGetLastError());
     }
     if (row_dtype != TMV_F32 || !draft_q || q_stride_b < 0 || q_stride_row < 0) return TMV_ERR_ARG;
@@ -932,5 +1090,54 @@ extern "C" int tmv_tree_accept(int mode, int B, int M_max, int D_max, int V,
                        D_max, V, K, tokens, static_cast<const float *>(teacher), t_stride_b, t_stride_row, draft_q,
                        q_stride_b, q_stride_row, seed, step, n_nodes, anc, depth, status, accept_len, path,
                        next_token, reinterpret_cast<SeqSync *>(ws));
+    return tmv_host::launch_status(hipGetLastError());
+}
+
+extern "C" size_t tmv_tree_accept_lm_head_workspace(int B, int M_max)
+{
+    if (B <= 0 || M_max < 0) return 256;
+    return static_cast<size_t>(B) * (M_max + 1) * sizeof(uint64_t) + 256;
+}
+
+extern "C" int tmv_tree_accept_lm_head(int B, int M_max, int D_max, int K, int V, const int32_t *tokens,
+                                       const void *hidden, int64_t h_stride_b, int64_t h_stride_row,
+                                       const void *lm_head, int64_t w_stride_row,
+                                       const int32_t *n_nodes, const int32_t *anc, const int32_t *depth,
+                                       int32_t *status, int32_t *accept_len, int32_t *path, int32_t *next_token,
+                                       int32_t *row_argmax, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (B < 0 || M_max < 0 || M_max > 128 || D_max < 0 || D_max > 128 || V < 1) return TMV_ERR_ARG;
+    if (K < 32 || K % 32 != 0 || h_stride_b < 0 || h_stride_row < 0 || w_stride_row < K) return TMV_ERR_ARG;
+    if (B == 0) return TMV_OK;
+    if (!tokens || !hidden || !lm_head || !n_nodes || !anc || !depth || !status || !accept_len || !next_token)
+        return TMV_ERR_ARG;
+    if (D_max > 0 && !path) return TMV_ERR_ARG;
+    if (!workspace || workspace_bytes < tmv_tree_accept_lm_head_workspace(B, M_max)) return TMV_ERR_ARG;
+    // 16-byte operand loads: aligned bases and strides in whole 8-element groups; byte
+    // offsets of every row fit the 32-bit buffer offsets
+    if (((reinterpret_cast<uintptr_t>(hidden) | reinterpret_cast<uintptr_t>(lm_head) |
+          reinterpret_cast<uintptr_t>(workspace)) & 15u) != 0)
+        return TMV_ERR_ARG;
+    if (((h_stride_b | h_stride_row | w_stride_row) & 7) != 0) return TMV_ERR_ARG;
+    const int64_t h_bytes = ((B - 1) * h_stride_b + static_cast<int64_t>(M_max) * h_stride_row + K) * 2;
+    const int64_t w_bytes = (static_cast<int64_t>(V - 1) * w_stride_row + K) * 2;
+    if (h_bytes >= (int64_t(1) << 31) || w_bytes >= (int64_t(1) << 31)) return TMV_ERR_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint64_t *keys = static_cast<uint64_t *>(workspace);
+    const int nrows = B * (M_max + 1);
+    const int nrb = (nrows + kLmRows - 1) / kLmRows;
+    const int ntiles = (V + kLmTile - 1) / kLmTile;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    int gx = cus / nrb;
+    if (gx < 1) gx = 1;
+    if (gx > ntiles) gx = ntiles;
+    hipLaunchKernelGGL(lm_head_argmax_kernel, dim3(gx, nrb), dim3(kLmThreads), 0, s, B, M_max, K, V,
+                       static_cast<const uint16_t *>(hidden), h_stride_b, h_stride_row, static_cast<uint32_t>(h_bytes),
+                       static_cast<const uint16_t *>(lm_head), w_stride_row, static_cast<uint32_t>(w_bytes), n_nodes,
+                       depth, status, keys, ntiles);
+    hipLaunchKernelGGL(greedy_select_kernel, dim3(B), dim3(kScanThreads), 0, s, M_max, D_max, V, 1, tokens, n_nodes,
+                       anc, depth, status, accept_len, path, next_token, keys, 1, row_argmax);
     return tmv_host::launch_status(hipGetLastError());
 }

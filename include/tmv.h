@@ -312,7 +312,7 @@ int tmv_tree_accept(int mode, int B, int M_max, int D_max, int V,
  * section of "Speculative Decoding Hierarquico: Medusa, EAGLE-2 e Multi-Token Prediction":
  * decode is bound by reading weights; the LM head is read once per step).  The path rule
  * is exactly tmv_tree_accept's GREEDY rule on those logits.
- *   K          hidden size, a multiple of 32.
+ *   K          hidden size: 512, 1024, 2048, 4096 or 8192.
  *   hidden     bf16 [B][M_max+1][K], element strides {h_stride_b, h_stride_row}, K
  *              contiguous: row u holds the teacher's final hidden state after node u (row 0:
  *              after the committed prefix).

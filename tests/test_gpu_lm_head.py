@@ -95,7 +95,7 @@ def _small_case(seed, B, M_max, D_max, K, V, sigma_w, alpha=0.8):
     return parents, n_nodes, hidden, w, tokens
 
 
-@pytest.mark.parametrize("B,M_max,D_max,K,V", [(2, 6, 3, 256, 3000), (3, 20, 5, 128, 1000), (1, 1, 1, 64, 257)])
+@pytest.mark.parametrize("B,M_max,D_max,K,V", [(2, 6, 3, 512, 3000), (3, 20, 5, 1024, 1000), (1, 1, 1, 512, 257)])
 def test_lm_head_accept_small(B, M_max, D_max, K, V):
     _case("lm-head accept: B%d M%d K%d V%d" % (B, M_max, K, V))
     parents, n_nodes, hidden, w, tokens = _small_case(300 + V, B, M_max, D_max, K, V, 0.05)
@@ -111,7 +111,8 @@ def test_lm_head_accept_small(B, M_max, D_max, K, V):
     # the path rule on the device's choices, bit-exact
     rA, rpath, rnxt, rst = _one_hot_accept(targ, tokens, parents, n_nodes, M_max, D_max, V)
     assert np.array_equal(A, rA) and np.array_equal(path, rpath) and np.array_equal(nxt, rnxt)
-    assert A.max() > 0
+    if M_max > 1:
+        assert A.max() > 0
     if all_clear:
         # every choice unambiguous: the whole result equals the oracle's on its own fp64 logits
         oA = []
@@ -126,7 +127,7 @@ def test_lm_head_accept_small(B, M_max, D_max, K, V):
 def test_lm_head_nan_and_workspace_reuse():
     _case("lm-head accept: NaN row rejects its sequence; the workspace is left zero")
     import tree_masked_verification_amd as tmv
-    B, M_max, D_max, K, V = 3, 6, 3, 128, 700
+    B, M_max, D_max, K, V = 3, 6, 3, 512, 700
     parents, n_nodes, hidden, w, tokens = _small_case(311, B, M_max, D_max, K, V, 0.05)
     ws = torch.zeros(tmv.tree_accept_lm_head_workspace(B, M_max), dtype=torch.uint8, device="cuda")
     first = _run(hidden, w, parents, n_nodes, tokens, M_max, D_max, ws=ws)

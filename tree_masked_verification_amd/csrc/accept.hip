@@ -236,21 +236,28 @@ greedy_select_kernel(int M_max, int D_max, int V, int nchunk, const int32_t *__r
 // logits are reduced to the greedy keys as the MFMA tiles produce them and never written:
 // per step that saves writing and re-reading rows x V fp32 logits, and the weights -- the
 // whole cost at a few dozen rows -- are read once.
-//   * a workgroup of 8 waves computes 256-entry vocabulary tiles for one block of 64 rows:
-//     wave w owns entries 32w .. +32 (two 16-entry MFMA row tiles) against the block's 64
-//     rows (four 16-row column tiles), v_mfma_f32_16x16x32_bf16 over K in 32-wide steps;
-//   * weights stream from HBM straight into registers, kLmDepth k-steps ahead; the rows'
-//     fragments are the same for all 8 waves, so after the first wave they come from L1;
-//   * each lane keeps, per row, the best (value, ~index) key over the tiles it computed;
-//     the keys are reduced over the lanes and waves of the workgroup and merged into the
-//     row's key in the workspace with one device-scope 64-bit atomic max per row, which the
-//     select kernel reads (and clears).  A NaN logit makes the row's key all ones.
+//   * a workgroup of 8 waves owns a block of 64 rows and kLmTpw vocabulary tiles of 256
+//     entries; wave w computes entries 32w .. +32 of each tile (two 16-entry MFMA row tiles)
+//     against the 64 rows (four 16-row column tiles), v_mfma_f32_16x16x32_bf16 over K in
+//     32-wide steps;
+//   * the rows' hidden states are staged in LDS one 512-wide k-block at a time (16-byte
+//     pieces XOR-swizzled by row, so the operand reads of a wave hit distinct banks) and
+//     shared by the waves and the tiles; the weights stream from HBM straight into
+//     registers, kLmDepth steps ahead, through a fully unrolled step sequence so that every
+//     step waits for exactly its own loads;
+//   * each lane keeps, per row, the best (value, ~index) key; the keys are reduced over
+//     the lanes and waves of the workgroup and merged into the row's key in the workspace
+//     with one device-scope 64-bit atomic max per row, which the select kernel reads (and
+//     clears).  A NaN logit makes the row's key all ones.
 constexpr int kLmWaves = 8;
 constexpr int kLmThreads = kLmWaves * kWave;
 constexpr int kLmRows = 64;                            // rows per row block
 constexpr int kLmVocabPerWave = 32;
 constexpr int kLmTile = kLmWaves * kLmVocabPerWave;    // vocabulary entries per tile
-constexpr int kLmDepth = 4;                            // k-steps of loads in flight per wave
+constexpr int kLmTpw = 2;                              // tiles per workgroup
+constexpr int kLmKB = 512;                             // k entries per staged block
+constexpr int kLmPieces = kLmKB / 8;                   // 16-byte pieces per staged row
+constexpr int kLmDepth = 8;                            // weight steps in flight per wave
 constexpr int kLmBufferFlags = 0x00020000;             // raw buffer descriptor word 3 (gfx9 family)
 
 typedef __bf16 lm_bf16x8 __attribute__((ext_vector_type(8)));
@@ -265,12 +272,18 @@ __device__ __forceinline__ bool lm_row_live(int gr, int R, int M_max, const int3
     return status[b] == TMV_OK && M >= 0 && M <= M_max && u <= M && (u == 0 || depth[gr] >= 1);
 }
 
+// NKS = K / 32 steps (K a multiple of kLmKB), unrolled completely
+template <int NKS>
 __global__ void __launch_bounds__(kLmThreads)
-lm_head_argmax_kernel(int B, int M_max, int K, int V, const uint16_t *__restrict__ hidden, int64_t hsb,
-                      int64_t hsr, uint32_t h_bytes, const uint16_t *__restrict__ w, int64_t wsr, uint32_t w_bytes,
+lm_head_argmax_kernel(int B, int M_max, int V, const uint16_t *__restrict__ hidden, int64_t hsb, int64_t hsr,
+                      uint32_t h_bytes, const uint16_t *__restrict__ w, int64_t wsr, uint32_t w_bytes,
                       const int32_t *__restrict__ n_nodes, const int32_t *__restrict__ depth,
                       const int32_t *__restrict__ status, uint64_t *__restrict__ row_keys, int ntiles)
 {
+    static_assert(NKS % (kLmKB / 32) == 0, "whole staged blocks");
+    constexpr int kStepsPerBlock = kLmKB / 32;
+    constexpr int kSteps = kLmTpw * NKS;                       // (block, tile, step) sequence
+    __shared__ lm_u32x4 h_lds[kLmRows][kLmPieces];
     __shared__ uint64_t s_key[kLmWaves][kLmRows];
     __shared__ int s_any;
     const int R = M_max + 1, nrows = B * R;
@@ -288,73 +301,118 @@ lm_head_argmax_kernel(int B, int M_max, int K, int V, const uint16_t *__restrict
     __syncthreads();
     if (!s_any) return;
 
-    // B operands: row rb0 + rt*16 + c16 (clamped into the tensor; padding rows are never
-    // merged), k entries G*8 .. +8 of each 32-wide step
     const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(hidden), 0,
                                                                         static_cast<int>(h_bytes), kLmBufferFlags);
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(w), 0,
                                                                         static_cast<int>(w_bytes), kLmBufferFlags);
-    uint32_t hoff[4];
+    // staging of a k-block: thread t moves pieces t + 512 i (row q / kLmPieces, piece
+    // q % kLmPieces) of the block; rows past the tensor are clamped (never merged)
+    constexpr int kStage = kLmRows * kLmPieces / kLmThreads;
+    uint32_t soff[kStage];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        int gr = rb0 + rt * 16 + c16;
+    for (int i = 0; i < kStage; ++i) {
+        const int q = threadIdx.x + i * kLmThreads, r = q / kLmPieces, pc = q % kLmPieces;
+        int gr = rb0 + r;
         if (gr > nrows - 1) gr = nrows - 1;
         const int b = gr / R, u = gr - b * R;
-        hoff[rt] = static_cast<uint32_t>((b * hsb + u * hsr + G * 8) * 2);
+        soff[i] = static_cast<uint32_t>((b * hsb + u * hsr) * 2 + pc * 16);
     }
-    const int nks = K / 32;
-    uint64_t best[4] = {0, 0, 0, 0};
-    bool nan[4] = {false, false, false, false};
-
-    for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const int vbase = t * kLmTile + wave * kLmVocabPerWave;
-        uint32_t woff[2];
+    // tiles of this workgroup; a missing second tile computes on clamped rows and is ignored
+    int vbase[kLmTpw];
+    bool tile_ok[kLmTpw];
+    uint32_t woff[kLmTpw][2];
+#pragma unroll
+    for (int tp = 0; tp < kLmTpw; ++tp) {
+        const int t = blockIdx.x + tp * gridDim.x;
+        tile_ok[tp] = t < ntiles;
+        vbase[tp] = t * kLmTile + wave * kLmVocabPerWave;
 #pragma unroll
         for (int vt = 0; vt < 2; ++vt) {
-            int v = vbase + vt * 16 + c16;
+            int v = vbase[tp] + vt * 16 + c16;
             if (v > V - 1) v = V - 1;
-            woff[vt] = static_cast<uint32_t>((v * wsr + G * 8) * 2);
+            woff[tp][vt] = static_cast<uint32_t>(v * wsr * 2 + G * 16);
         }
-        lm_f32x4 acc[2][4];
+    }
+    lm_f32x4 acc[kLmTpw][2][4];
+#pragma unroll
+    for (int tp = 0; tp < kLmTpw; ++tp)
 #pragma unroll
         for (int vt = 0; vt < 2; ++vt)
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) acc[vt][rt] = lm_f32x4{0.f, 0.f, 0.f, 0.f};
-        lm_u32x4 wa[kLmDepth][2], hb[kLmDepth][4];
-        auto load_step = [&](int d, int ks) {
+            for (int rt = 0; rt < 4; ++rt) acc[tp][vt][rt] = lm_f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // step i of the sequence: block i / (kLmTpw * kStepsPerBlock), tile (i / kStepsPerBlock)
+    // % kLmTpw, k-step within the block i % kStepsPerBlock
+    // (k offsets go in the scalar offset operand: uniform, and no per-step address registers)
+    lm_u32x4 wa[kLmDepth][2];
+    auto load_w = [&](int i) {
+        const int blk = i / (kLmTpw * kStepsPerBlock), tp = (i / kStepsPerBlock) % kLmTpw;
+        const int ks = blk * kStepsPerBlock + i % kStepsPerBlock;
 #pragma unroll
-            for (int vt = 0; vt < 2; ++vt) wa[d][vt] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff[vt] + ks * 64, 0, 0);
+        for (int vt = 0; vt < 2; ++vt)
+            wa[i % kLmDepth][vt] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff[tp][vt], ks * 64, 0);
+    };
+    // the hidden states of block 0 go out first; each block's arrive a block ahead of use
+    constexpr int kBlocks = NKS / kStepsPerBlock;
+    lm_u32x4 hv[kStage];
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) hb[d][rt] = __builtin_amdgcn_raw_buffer_load_b128(hr, hoff[rt] + ks * 64, 0, 0);
-        };
+    for (int j = 0; j < kStage; ++j) hv[j] = __builtin_amdgcn_raw_buffer_load_b128(hr, soff[j], 0, 0);
 #pragma unroll
-        for (int d = 0; d < kLmDepth; ++d)
-            if (d < nks) load_step(d, d);
-        for (int ks0 = 0; ks0 < nks; ks0 += kLmDepth) {
+    for (int i = 0; i < kLmDepth; ++i) load_w(i);
+    // B operand of row rt*16 + c16 at k-step ks of the staged block: piece 4 ks + G
+    auto h_frag = [&](int rt, int ks) {
+        const int r = rt * 16 + c16;
+        return h_lds[r][(ks * 4 + G) ^ (r & 15)];
+    };
 #pragma unroll
-            for (int d = 0; d < kLmDepth; ++d) {
-                const int ks = ks0 + d;
-                if (ks < nks) {
+    for (int i = 0; i < kSteps; ++i) {
+        const int blk = i / (kLmTpw * kStepsPerBlock), tp = (i / kStepsPerBlock) % kLmTpw;
+        const int ks = i % kStepsPerBlock;
+        if (i % (kLmTpw * kStepsPerBlock) == 0) {
+            // stage block blk of the rows' hidden states (after every wave is done with the
+            // last), then send for block blk + 1
+            __syncthreads();
 #pragma unroll
-                    for (int vt = 0; vt < 2; ++vt)
+            for (int j = 0; j < kStage; ++j) {
+                const int q = threadIdx.x + j * kLmThreads, r = q / kLmPieces, pc = q % kLmPieces;
+                h_lds[r][pc ^ (r & 15)] = hv[j];
+            }
+            __syncthreads();
+            if (blk + 1 < kBlocks) {
 #pragma unroll
-                        for (int rt = 0; rt < 4; ++rt)
-                            acc[vt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                __builtin_bit_cast(lm_bf16x8, wa[d][vt]), __builtin_bit_cast(lm_bf16x8, hb[d][rt]),
-                                acc[vt][rt], 0, 0, 0);
-                    if (ks + kLmDepth < nks) load_step(d, ks + kLmDepth);
-                }
+                for (int j = 0; j < kStage; ++j)
+                    hv[j] = __builtin_amdgcn_raw_buffer_load_b128(hr, soff[j], (blk + 1) * kLmKB * 2, 0);
             }
         }
-        // lane holds row rt*16 + c16 at entries vbase + vt*16 + G*4 + i
+        lm_u32x4 hb[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) hb[rt] = h_frag(rt, ks);
+#pragma unroll
+        for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+                acc[tp][vt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(lm_bf16x8, wa[i % kLmDepth][vt]), __builtin_bit_cast(lm_bf16x8, hb[rt]),
+                    acc[tp][vt][rt], 0, 0, 0);
+        if (i + kLmDepth < kSteps) load_w(i + kLmDepth);
+        // pin the schedule: without this the scheduler sinks every load next to its use
+        // (to save registers) and the steps wait for their loads one by one
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // lane holds row rt*16 + c16 at entries vbase + vt*16 + G*4 + i
+    uint64_t best[4] = {0, 0, 0, 0};
+    bool nan[4] = {false, false, false, false};
+#pragma unroll
+    for (int tp = 0; tp < kLmTpw; ++tp) {
+        if (!tile_ok[tp]) continue;
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
             for (int vt = 0; vt < 2; ++vt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int v = vbase + vt * 16 + G * 4 + i;
-                    if (v < V) scan_one(acc[vt][rt][i], v, best[rt], nan[rt]);
+                    const int v = vbase[tp] + vt * 16 + G * 4 + i;
+                    if (v < V) scan_one(acc[tp][vt][rt][i], v, best[rt], nan[rt]);
                 }
     }
     // reduce over the four lanes of a row, then over the waves, and merge into the row's key
@@ -1107,7 +1165,9 @@ extern "C" int tmv_tree_accept_lm_head(int B, int M_max, int D_max, int K, int V
                                        int32_t *row_argmax, void *workspace, size_t workspace_bytes, void *stream)
 {
     if (B < 0 || M_max < 0 || M_max > 128 || D_max < 0 || D_max > 128 || V < 1) return TMV_ERR_ARG;
-    if (K < 32 || K % 32 != 0 || h_stride_b < 0 || h_stride_row < 0 || w_stride_row < K) return TMV_ERR_ARG;
+    if ((K != 512 && K != 1024 && K != 2048 && K != 4096 && K != 8192) || h_stride_b < 0 ||
+        h_stride_row < 0 || w_stride_row < K)
+        return TMV_ERR_ARG;
     if (B == 0) return TMV_OK;
     if (!tokens || !hidden || !lm_head || !n_nodes || !anc || !depth || !status || !accept_len || !next_token)
         return TMV_ERR_ARG;
@@ -1127,16 +1187,22 @@ extern "C" int tmv_tree_accept_lm_head(int B, int M_max, int D_max, int K, int V
     const int nrows = B * (M_max + 1);
     const int nrb = (nrows + kLmRows - 1) / kLmRows;
     const int ntiles = (V + kLmTile - 1) / kLmTile;
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 256;
-    int gx = cus / nrb;
-    if (gx < 1) gx = 1;
-    if (gx > ntiles) gx = ntiles;
-    hipLaunchKernelGGL(lm_head_argmax_kernel, dim3(gx, nrb), dim3(kLmThreads), 0, s, B, M_max, K, V,
-                       static_cast<const uint16_t *>(hidden), h_stride_b, h_stride_row, static_cast<uint32_t>(h_bytes),
-                       static_cast<const uint16_t *>(lm_head), w_stride_row, static_cast<uint32_t>(w_bytes), n_nodes,
-                       depth, status, keys, ntiles);
+    // every workgroup takes kLmTpw tiles (ceil(tiles / kLmTpw) workgroups per row block)
+    const int gx = (ntiles + kLmTpw - 1) / kLmTpw;
+#define TMV_LAUNCH_LM(NKS)                                                                                     \
+    hipLaunchKernelGGL(lm_head_argmax_kernel<NKS>, dim3(gx, nrb), dim3(kLmThreads), 0, s, B, M_max, V,             \
+                       static_cast<const uint16_t *>(hidden), h_stride_b, h_stride_row, static_cast<uint32_t>(h_bytes), \
+                       static_cast<const uint16_t *>(lm_head), w_stride_row, static_cast<uint32_t>(w_bytes), n_nodes,  \
+                       depth, status, keys, ntiles)
+    switch (K) {
+    case 512: TMV_LAUNCH_LM(16); break;
+    case 1024: TMV_LAUNCH_LM(32); break;
+    case 2048: TMV_LAUNCH_LM(64); break;
+    case 4096: TMV_LAUNCH_LM(128); break;
+    case 8192: TMV_LAUNCH_LM(256); break;
+    default: return TMV_ERR_ARG;
+    }
+#undef TMV_LAUNCH_LM
     hipLaunchKernelGGL(greedy_select_kernel, dim3(B), dim3(kScanThreads), 0, s, M_max, D_max, V, 1, tokens, n_nodes,
                        anc, depth, status, accept_len, path, next_token, keys, 1, row_argmax);
     return tmv_host::launch_status(hipGetLastError());

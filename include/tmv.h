@@ -389,6 +389,31 @@ int tmv_kv_commit_path_paged(int dtype, int n_layers, int B, int Hkv, int d, int
                              int32_t *status, int32_t *new_len, void *stream);
 
 /*
+ * tmv_kv_commit_path_paged_evict -- the paged commit, then block eviction: the block table
+ * is rewritten so that only the accepted path stays in the sequence.  Defined by the same
+ * runtime-memory question (pages of the tree allocated for the step; after the parallel
+ * step the blocks of discarded branches are evicted; only the accepted path is kept).
+ *   Rows move exactly as tmv_kv_commit_path_paged moves them; only blocks holding slots of
+ *   [P_b, P_b + A_b) are written (partial blocks).  Then, for every sequence whose status
+ *   is TMV_OK, each block i of the tree's slots [P_b, P_b + M_b) with i * page_size >=
+ *   new_len[b] -- nothing in it is still part of the sequence -- has a valid page entry
+ *   (in [0, num_pages)) cleared to -1 in block_table, and that page number is appended to
+ *   freed_pages at index atomicAdd(freed_count, 1) (caller-owned device int32 array and
+ *   counter, in any order).  An entry whose index would reach freed_capacity is left in
+ *   the table instead.  Blocks of a failed sequence and blocks past the tree are never
+ *   touched.  The pages of evicted blocks must belong to their sequence alone (pages of
+ *   the prefix, which a sequence may share, are never evicted).  At most ceil(M_b /
+ *   page_size) + 1 blocks per sequence are evicted.
+ */
+int tmv_kv_commit_path_paged_evict(int dtype, int n_layers, int B, int Hkv, int d, int num_pages, int page_size,
+                                   int32_t *block_table, int64_t table_stride, int max_blocks,
+                                   int M_max, int D_max, void *k_pages, void *v_pages,
+                                   const int64_t *page_stride, const int32_t *prefix_len,
+                                   const int32_t *n_nodes, const int32_t *accept_len, const int32_t *path,
+                                   int32_t *status, int32_t *new_len, int32_t *freed_pages, int32_t *freed_count,
+                                   int freed_capacity, void *stream);
+
+/*
  * tmv_tree_best_first -- a best-first prefix tree from per-position draft marginals, and
  * the hardware-aware budget controller that chooses its size.
  * Defined by sections 1-3 of the BASTION technical summary:

@@ -148,6 +148,28 @@ def accept_greedy(tokens, logits, n_nodes, anc, depth, status, row_dtype=F32):
     return A, path, nxt, st
 
 
+def commit_paged_table(table, page_size, num_pages, prefix_len, n_nodes, new_len, status):
+    """Block eviction after a paged commit (the runtime-memory question of the hierarchical
+    speculative decoding blog: discarded branches' blocks are evicted, only the accepted
+    path is kept).  For every sequence with status OK, the blocks of its tree slots
+    [P, P + M) that start at or beyond new_len and hold a valid page are cleared to -1 and
+    their pages freed.  Returns (new table, sorted list of freed pages)."""
+    table = np.array(table, np.int32, copy=True)
+    freed = []
+    for b in range(table.shape[0]):
+        if int(status[b]) != OK:
+            continue
+        P, M, nl = int(prefix_len[b]), int(n_nodes[b]), int(new_len[b])
+        first = -(-nl // page_size)                   # first block starting at or after new_len
+        last = -(-(P + M) // page_size)               # one past the tree's last block
+        for i in range(first, min(last, table.shape[1])):
+            pg = int(table[b, i])
+            if 0 <= pg < num_pages:
+                freed.append(pg)
+                table[b, i] = -1
+    return table, sorted(freed)
+
+
 def lm_head_logits(h_bits, w_bits, with_bound=True):
     """fp64 logits of the rows h_bits [n][K] (bf16 bit patterns) against the LM head
     w_bits [V][K]: (logits [n][V], bound [n][V] = sum_k |h w| or None)."""

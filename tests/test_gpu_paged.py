@@ -170,6 +170,65 @@ def test_paged_commit(ref, page_size, nl):
             assert np.array_equal(kg[:, pg, :, r], kr[:, b, :, t]) and np.array_equal(vg[:, pg, :, r], vr[:, b, :, t])
 
 
+@pytest.mark.parametrize("page_size,capacity", [(16, 1000), (4, 1000), (1, 1000), (4, 3)])
+def test_paged_commit_evict(ref, page_size, capacity):
+    """The commit with block eviction: rows as the oracle's commit through the kept entries,
+    the rewritten table and the freed pages as the oracle's eviction rule (or, with a short
+    free list, exactly the entries that fit)."""
+    _case("paged commit with eviction: page %d, free-list capacity %d" % (page_size, capacity))
+    import tree_masked_verification_amd as tmv
+    rng = np.random.default_rng(330 + page_size + capacity)
+    B, Hkv, M_max, D_max, d, nl = 6, 2, 24, 10, 128, 2
+    n = rng.integers(1, M_max + 1, size=B).astype(np.int32)
+    P = rng.integers(0, 70, size=B).astype(np.int32)
+    L_cap = int((P + n).max()) + 3
+    parents = np.zeros((B, M_max + 1), np.int32)
+    A = np.zeros(B, np.int32)
+    path = np.zeros((B, D_max), np.int32)
+    for b in range(B):
+        parents[b, : n[b] + 1] = random_labelled_tree(rng, int(n[b]), D_max)
+        pn = _path_of(parents[b], int(rng.integers(0, n[b] + 1)))
+        A[b], path[b, : len(pn)] = len(pn), pn
+    kh = rng.integers(0, 65536, size=(nl, B, Hkv, L_cap, d)).astype(np.uint16)
+    vh = rng.integers(0, 65536, size=(nl, B, Hkv, L_cap, d)).astype(np.uint16)
+    (kp, vp), table = ti.paged_layout(rng, [kh, vh], page_size)
+    w = ti.Workload("commit", ti.BF16, B, 0, Hkv, d, M_max, D_max, L_cap, 1, "greedy", parents, n, P,
+                    np.zeros((B, M_max + 1), np.int32))
+    dev = DeviceStep(w)
+    dev.build()
+    dev.accept_len.copy_(torch.from_numpy(A).cuda())
+    dev.path.copy_(torch.from_numpy(path).cuda())
+    kpd, vpd = dev_tensor(kp, True), dev_tensor(vp, True)
+    tab = torch.from_numpy(table.copy()).cuda()
+    freed = torch.full((capacity,), -5, dtype=torch.int32, device="cuda")
+    count = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    tmv.kv_commit_path_paged_evict(kpd, vpd, tab, dev.prefix, dev.n_nodes, dev.accept_len, dev.path, dev.status,
+                                   dev.new_len, M_max, freed, count)
+    torch.cuda.synchronize()
+    ra, rd, rs = oracle_tables(ref, w)
+    kr, vr = kh.copy(), vh.copy()
+    new_len, st = ref.commit(kr, vr, P, n, A, path, rs, M_max)
+    assert np.array_equal(host_bits(dev.new_len), new_len) and np.array_equal(host_bits(dev.status), st)
+    rtab, rfreed = ref.commit_paged_table(table, page_size, kp.shape[1], P, n, new_len, st)
+    t2, fr, cnt = host_bits(tab), host_bits(freed), int(host_bits(count)[0])
+    assert cnt == len(rfreed)
+    if capacity >= len(rfreed):
+        assert np.array_equal(t2, rtab) and sorted(fr[:cnt].tolist()) == rfreed
+    else:
+        # the first `capacity` evictions happened, the rest kept their entries
+        cleared = (t2 == -1) & (table != -1)
+        assert int(cleared.sum()) == capacity
+        assert sorted(table[cleared].tolist()) == sorted(fr.tolist())
+        assert np.all((t2 == table) | cleared) and np.all(rtab[cleared] == -1)
+    # every kept slot below the new length holds the committed rows
+    kg, vg = host_bits(kpd), host_bits(vpd)
+    for b in range(B):
+        for t in range(int(new_len[b])):
+            pg, r = t2[b, t // page_size], t % page_size
+            assert pg >= 0
+            assert np.array_equal(kg[:, pg, :, r], kr[:, b, :, t]) and np.array_equal(vg[:, pg, :, r], vr[:, b, :, t])
+
+
 @pytest.mark.parametrize("plan", [(64, 3), (128, 1), (128, 2), (256, 5), (64, 16)])
 def test_paged_attention_launch_plans(ref, plan):
     """Every row-group width of the paged kernel (a pinned plan), against the oracle and

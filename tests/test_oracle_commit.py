@@ -8,6 +8,7 @@ over the committed length equals causal attention over prefix + path (torch SDPA
 import numpy as np
 import torch
 
+import oracle
 import tmv_inputs as ti
 from tests.test_oracle_build import random_labelled_tree
 
@@ -111,3 +112,44 @@ def test_attention_over_committed_length(ref):
     slots = list(range(P)) + [P + j - 1 for j in pn]
     before = torch.nn.functional.scaled_dot_product_attention(qv, t64(k0[0, 0, 0][slots]), t64(v0[0, 0, 0][slots]))
     assert torch.equal(after, before)
+
+
+def test_block_eviction_hand_cases():
+    """Block eviction after a paged commit (runtime-memory question of the hierarchical
+    speculative decoding blog): blocks of the tree wholly past the new length are freed."""
+    table = np.array([[10, 11, 12, 13, 14]], np.int32)
+    # page 4, prefix 6, 7 tree slots (6..12), 2 accepted -> new length 8: blocks 2 and 3 go
+    t2, freed = oracle.commit_paged_table(table, 4, 100, [6], [7], [8], [0])
+    assert t2.tolist() == [[10, 11, -1, -1, 14]] and freed == [12, 13]
+    # one accepted: block 1 (slots 4..7) still holds slot 6, so it stays
+    t2, freed = oracle.commit_paged_table(table, 4, 100, [6], [7], [7], [0])
+    assert t2.tolist() == [[10, 11, -1, -1, 14]] and freed == [12, 13]
+    # none accepted: block 1 also holds prefix slots 4 and 5, so it stays
+    t2, freed = oracle.commit_paged_table(table, 4, 100, [6], [7], [6], [0])
+    assert t2.tolist() == [[10, 11, -1, -1, 14]] and freed == [12, 13]
+    # a fully accepted chain keeps everything; a failed sequence is left alone
+    t2, freed = oracle.commit_paged_table(table, 4, 100, [6], [7], [13], [0])
+    assert t2.tolist() == table.tolist() and freed == []
+    t2, freed = oracle.commit_paged_table(table, 4, 100, [6], [7], [6], [oracle.ERR_INPUT])
+    assert t2.tolist() == table.tolist() and freed == []
+    # invalid entries are skipped, page-aligned new length frees the following block
+    t2, freed = oracle.commit_paged_table(np.array([[1, 2, -1, 300, 5]], np.int32), 4, 100, [4], [12], [8], [0])
+    assert t2.tolist() == [[1, 2, -1, 300, -1]] and freed == [5]
+
+
+def test_block_eviction_invariants():
+    rng = np.random.default_rng(91)
+    for _ in range(300):
+        ps = int(rng.choice([1, 2, 4, 8, 16]))
+        P = int(rng.integers(0, 40))
+        M = int(rng.integers(0, 30))
+        A = int(rng.integers(0, M + 1))
+        nb = (P + M + ps - 1) // ps + 2
+        table = rng.permutation(1000)[:nb].astype(np.int32)[None]
+        t2, freed = oracle.commit_paged_table(table, ps, 1000, [P], [M], [P + A], [0])
+        for i in range(nb):
+            evicted = t2[0, i] == -1
+            start = i * ps
+            # evicted exactly when the block starts at or past the new length inside the tree
+            assert evicted == (start >= P + A and start < P + M)
+        assert sorted(table[0][t2[0] == -1].tolist()) == freed

@@ -69,6 +69,8 @@ _lib.tmv_tree_verify_attention_paged_plan.argtypes = [_I, _I, _I, _I, _I, _I, _I
                                                       _I, _P, _P, _P, _P, _P, _F, _P, _P, _I, _I, _P, _SZ, _P]
 _lib.tmv_kv_commit_path_paged.argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _I64, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,
                                           _P, _P, _P]
+_lib.tmv_kv_commit_path_paged_evict.argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _I64, _I, _I, _I, _P, _P, _P, _P, _P,
+                                                _P, _P, _P, _P, _P, _P, _I, _P]
 _lib.tmv_tree_best_first_workspace.argtypes = [_I, _I, _I, _I]
 _lib.tmv_tree_best_first_workspace.restype = _SZ
 _lib.tmv_tree_best_first.argtypes = [_I, _I, _I, _I, _P, _I64, _I64, _P, ctypes.c_double, _P, _P, _P, _P, _P, _P,
@@ -81,7 +83,7 @@ EXPORTED = ("tmv_status_string", "tmv_abi_version", "tmv_tree_build_ancestors",
             "tmv_kv_commit_path_paged", "tmv_tree_verify_attention_plan_workspace",
             "tmv_tree_verify_attention_plan", "tmv_tree_verify_attention_paged_plan_workspace",
             "tmv_tree_verify_attention_paged_plan", "tmv_tree_verify_attention_noalloc",
-            "tmv_tree_accept_lm_head_workspace", "tmv_tree_accept_lm_head")
+            "tmv_tree_accept_lm_head_workspace", "tmv_tree_accept_lm_head", "tmv_kv_commit_path_paged_evict")
 
 
 class TmvError(RuntimeError):
@@ -381,6 +383,34 @@ def kv_commit_path_paged(k_pages, v_pages, block_table, prefix_len, n_nodes, acc
                                          _ptr(prefix_len), _ptr(n_nodes), _ptr(accept_len), _ptr(path), _ptr(status),
                                          _ptr(new_len), _stream(stream)),
            "kv_commit_path_paged")
+
+
+def kv_commit_path_paged_evict(k_pages, v_pages, block_table, prefix_len, n_nodes, accept_len, path, status, new_len,
+                               M_max, freed_pages, freed_count, stream=None):
+    """kv_commit_path_paged, then block eviction: block_table (int32 [B][max_blocks], in/out)
+    loses the tree blocks wholly past new_len, whose pages are appended to freed_pages
+    (int32 device array) at indices counted by freed_count (int32 [1], in/out)."""
+    _i32(block_table, prefix_len, n_nodes, accept_len, path, status, new_len, freed_pages, freed_count)
+    if k_pages.dim() == 4:
+        k_pages, v_pages = k_pages.unsqueeze(0), v_pages.unsqueeze(0)
+    if k_pages.shape != v_pages.shape or k_pages.stride() != v_pages.stride() or k_pages.dtype != v_pages.dtype:
+        raise ValueError("k_pages and v_pages must match")
+    nl, num_pages, Hkv, page_size, d = k_pages.shape
+    if k_pages.stride(4) != 1:
+        raise ValueError("d must be contiguous")
+    B = prefix_len.numel()
+    if path.dim() != 2 or path.shape[0] != B or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("path must be [B][D_max] and block_table [B][max_blocks]")
+    _vec(B, "n_nodes / accept_len / status / new_len", n_nodes, accept_len, status, new_len)
+    _vec(1, "freed_count", freed_count)
+    _check(_lib.tmv_kv_commit_path_paged_evict(_dtype_code(k_pages), nl, B, Hkv, d, num_pages, page_size,
+                                               _ptr(block_table), block_table.stride(0), block_table.shape[1],
+                                               int(M_max), path.shape[1], _ptr(k_pages), _ptr(v_pages),
+                                               _strides(k_pages, (0, 1, 2, 3)), _ptr(prefix_len), _ptr(n_nodes),
+                                               _ptr(accept_len), _ptr(path), _ptr(status), _ptr(new_len),
+                                               _ptr(freed_pages), _ptr(freed_count), freed_pages.numel(),
+                                               _stream(stream)),
+           "kv_commit_path_paged_evict")
 
 
 # ------------------------------------------------------------------------ tree construction

@@ -14,10 +14,12 @@
 //
 // Paged caches (vLLM-style blocks, the PagedAttention-for-trees notes of the
 // speculative-decoding survey page): logical slot t of sequence b lives in page
-// table[b][t / page] at row t % page.  The same moves go through the block table; the
-// table itself is not rewritten (a commit moves at most D_max rows per layer and head,
-// which a page copy could only match for whole pages of an in-order path), and pages past
-// the new length hold nothing the sequence still needs, so the caller may free them.
+// table[b][t / page] at row t % page.  The same moves go through the block table.  Only
+// the blocks that hold slots of [P, P + A) are ever written, a partial block at a time (a
+// commit moves at most D_max rows per layer and head).  The evicting variant then
+// rewrites the table: every block of the tree that now lies wholly at or beyond the new
+// length -- a discarded branch's block -- is cleared and its page handed back to the
+// caller's free list (the page's block eviction).
 #include "tmv_device.hpp"
 
 namespace {
@@ -124,6 +126,35 @@ commit_kernel(int n_layers, int B, int Hkv, int row_bytes, int L_cap, int D_max,
     }
 }
 
+// Block eviction after a paged commit (ordered after it on the stream, so every layer's
+// row moves, which may read rows of these blocks, are done): one workgroup per sequence;
+// the blocks of the tree's slots [P, P + M) that start at or beyond new_len are cleared
+// in the table and their pages appended to the free list.  A full list keeps the block.
+__global__ void __launch_bounds__(64)
+evict_kernel(int M_max, int page_shift, int max_blocks, int npages, int32_t *__restrict__ tab, int64_t stride,
+             const int32_t *__restrict__ prefix_len, const int32_t *__restrict__ n_nodes,
+             const int32_t *__restrict__ status, const int32_t *__restrict__ new_len,
+             int32_t *__restrict__ freed, int32_t *__restrict__ freed_count, int capacity)
+{
+    const int b = blockIdx.x;
+    if (status[b] != TMV_OK) return;
+    const int P = prefix_len[b], M = n_nodes[b], nl = new_len[b];
+    if (P < 0 || M < 0 || M > M_max || nl < P) return;
+    const int ps = 1 << page_shift;
+    const int64_t end = static_cast<int64_t>(P) + M;          // first slot past the tree
+    const int first = (nl + ps - 1) >> page_shift;            // first block wholly >= new_len
+    const int64_t last = (end + ps - 1) >> page_shift;        // one past the tree's last block
+    int32_t *trow = tab + static_cast<int64_t>(b) * stride;
+    for (int64_t i = first + threadIdx.x; i < last && i < max_blocks; i += 64) {
+        const int pg = trow[i];
+        if (pg < 0 || pg >= npages) continue;
+        const int slot = atomicAdd(freed_count, 1);
+        if (slot >= capacity) continue;                        // no room: the block stays
+        freed[slot] = pg;
+        trow[i] = -1;
+    }
+}
+
 }  // namespace
 
 extern "C" int tmv_kv_commit_path(int dtype, int n_layers, int B, int Hkv, int d, int L_cap,
@@ -195,5 +226,26 @@ extern "C" int tmv_kv_commit_path_paged(int dtype, int n_layers, int B, int Hkv,
                        page_stride[0] * es, page_stride[1] * es, page_stride[2] * es, page_stride[3] * es,
                        prefix_len, n_nodes, accept_len, path, status, new_len,
                        CommitPages{block_table, table_stride, shift, num_pages});
+    return tmv_host::launch_status(hipGetLastError());
+}
+
+extern "C" int tmv_kv_commit_path_paged_evict(int dtype, int n_layers, int B, int Hkv, int d, int num_pages,
+                                              int page_size, int32_t *block_table, int64_t table_stride,
+                                              int max_blocks, int M_max, int D_max, void *k_pages, void *v_pages,
+                                              const int64_t *page_stride, const int32_t *prefix_len,
+                                              const int32_t *n_nodes, const int32_t *accept_len, const int32_t *path,
+                                              int32_t *status, int32_t *new_len, int32_t *freed_pages,
+                                              int32_t *freed_count, int freed_capacity, void *stream)
+{
+    if (freed_capacity < 0 || (B > 0 && (!freed_pages || !freed_count))) return TMV_ERR_ARG;
+    const int rc = tmv_kv_commit_path_paged(dtype, n_layers, B, Hkv, d, num_pages, page_size, block_table,
+                                            table_stride, max_blocks, M_max, D_max, k_pages, v_pages, page_stride,
+                                            prefix_len, n_nodes, accept_len, path, status, new_len, stream);
+    if (rc != TMV_OK || B == 0) return rc;
+    int shift = 0;
+    while ((1 << shift) < page_size) ++shift;
+    hipLaunchKernelGGL(evict_kernel, dim3(B), dim3(64), 0, static_cast<hipStream_t>(stream), M_max, shift, max_blocks,
+                       num_pages, block_table, table_stride, prefix_len, n_nodes, status, new_len, freed_pages,
+                       freed_count, freed_capacity);
     return tmv_host::launch_status(hipGetLastError());
 }

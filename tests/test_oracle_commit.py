@@ -133,7 +133,7 @@ def test_block_eviction_hand_cases():
     t2, freed = oracle.commit_paged_table(table, 4, 100, [6], [7], [6], [oracle.ERR_INPUT])
     assert t2.tolist() == table.tolist() and freed == []
     # invalid entries are skipped, page-aligned new length frees the following block
-    t2, freed = oracle.commit_paged_table(np.array([[1, 2, -1, 300, 5]], np.int32), 4, 100, [4], [12], [8], [0])
+    t2, freed = oracle.commit_paged_table(np.array([[1, 2, -1, 300, 5]], np.int32), 4, 100, [4], [16], [8], [0])
     assert t2.tolist() == [[1, 2, -1, 300, -1]] and freed == [5]
 
 

@@ -83,3 +83,20 @@ def test_errors_and_failed_sequences(ref):
     st_in = np.array([0, 0, 0, 5, 0], np.int32)
     parents, tokens, n, rho, st = _parity(ref, q, 32, status=st_in)
     assert st.tolist() == [6, 6, 6, 5, 0] and n.tolist() == [0, 0, 0, 0, 32]
+
+
+def test_negative_zero_marginals(ref):
+    """-0.0 is a valid probability equal to 0: it ranks with the zeros, ties broken by
+    token, exactly as the oracle's comparisons do."""
+    _case("best-first: marginals with -0.0 entries")
+    rng = np.random.default_rng(1400)
+    q = ti.draft_marginals(rng, 3, 3, 300, sigma=2.0, levels=4)
+    # most entries are zero, half of them -0.0, so the tree needs zero-scored nodes and
+    # their order (by token) mixes both signs
+    zeros = rng.random(q.shape) < 0.99
+    neg = rng.random(q.shape) < 0.5
+    q[zeros & neg] = -0.0
+    q[zeros & ~neg] = 0.0
+    assert np.signbit(q).any()
+    parents, tokens, n, rho, st = _parity(ref, q, 96)
+    assert np.all(st == 0)

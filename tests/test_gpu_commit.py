@@ -73,6 +73,62 @@ def test_commit_small_caches(ref, dtype, d, nl):
     assert np.array_equal(kr[:, 0], kh[:, 0])        # full chain accept moved nothing
 
 
+@pytest.mark.parametrize("dtype,A_len", [(ti.BF16, 17), (ti.BF16, 40), (ti.F32, 9), (ti.F32, 30)])
+def test_commit_long_paths_take_several_passes(ref, dtype, A_len):
+    """Paths long enough that a (layer, sequence)'s moving rows over its 8 KV heads and both
+    caches do not fit one LDS snapshot: more than 16 rows of bf16 d128 or 8 rows of fp32
+    d128 are snapshotted and written in several passes."""
+    _case("commit: %d-row path, dtype=%d, 8 KV heads, d128" % (A_len, dtype))
+    rng = np.random.default_rng(600 + A_len + dtype)
+    B, Hkv, d, nl = 3, 8, 128, 2
+    M_max, D_max = 64, 48
+    n = np.array([M_max, 50, A_len], np.int32)
+    P = np.array([5, 0, 33], np.int32)
+    L_cap = int((P + n).max()) + 4
+    parents = np.zeros((B, M_max + 1), np.int32)
+    A = np.zeros(B, np.int32)
+    path = np.zeros((B, D_max), np.int32)
+    for b in range(B):
+        # a chain of A_len nodes under random labels (so almost every row moves), the rest
+        # hanging off it
+        labels = rng.permutation(np.arange(1, n[b] + 1))
+        chain = labels[:A_len]
+        par = np.zeros(n[b] + 1, np.int32)
+        for i, c in enumerate(chain):
+            par[c] = 0 if i == 0 else chain[i - 1]
+        for c in labels[A_len:]:
+            par[c] = chain[int(rng.integers(0, min(A_len, D_max - 1)))]
+        parents[b, : n[b] + 1] = par
+        A[b] = A_len
+        path[b, :A_len] = chain
+    edt = np.float32 if dtype == ti.F32 else np.uint16
+    shape = (nl, B, Hkv, L_cap, d)
+    if dtype == ti.F32:
+        kh = rng.standard_normal(shape).astype(np.float32)
+        vh = rng.standard_normal(shape).astype(np.float32)
+    else:
+        kh = rng.integers(0, 65536, size=shape).astype(np.uint16)
+        vh = rng.integers(0, 65536, size=shape).astype(np.uint16)
+    w = ti.Workload("commit", dtype, B, 0, Hkv, d, M_max, D_max, L_cap, 1, "greedy", parents, n, P,
+                    np.zeros((B, M_max + 1), np.int32))
+    dev = DeviceStep(w)
+    dev.build()
+    dev.accept_len.copy_(torch.from_numpy(A).cuda())
+    dev.path.copy_(torch.from_numpy(path).cuda())
+    kd, vd = dev_tensor(kh, dtype == ti.BF16), dev_tensor(vh, dtype == ti.BF16)
+    dev.commit(kd, vd)
+    torch.cuda.synchronize()
+    ra, rd, rs = oracle_tables(ref, w)
+    assert np.all(rs == 0) and np.all(rd.max(axis=1) >= A_len)
+    kr, vr = kh.copy(), vh.copy()
+    new_len, st = ref.commit(kr, vr, P, n, A, path, rs, M_max)
+    moving = [int(np.sum(path[b, :A_len] - 1 != np.arange(A_len))) for b in range(B)]
+    row_bytes = d * (4 if dtype == ti.F32 else 2)
+    assert max(moving) * row_bytes * 2 * Hkv > 64 * 1024      # several snapshot passes
+    assert np.array_equal(host_bits(dev.new_len), new_len) and np.array_equal(host_bits(dev.status), st)
+    assert np.array_equal(host_bits(kd), kr) and np.array_equal(host_bits(vd), vr)
+
+
 def test_commit_no_layers_publishes_lengths(ref):
     _case("commit: zero layers")
     import tree_masked_verification_amd as tmv

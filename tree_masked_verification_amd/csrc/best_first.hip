@@ -156,7 +156,8 @@ bf_segment_kernel(int D, int V, int K, int nseg, const float *__restrict__ q, in
         const float v = __uint_as_float(vb[e]);
         const bool ok = v >= 0.f && v <= 1.f;         // (false for NaN)
         bad = bad || (x < V && !ok);
-        vb[e] = x < V && ok ? vb[e] : kNoEntry;
+        // -0.0 equals 0 and ranks as +0.0 (its raw bits would outrank every positive value)
+        vb[e] = x < V && ok ? (vb[e] & 0x7fffffffu) : kNoEntry;
     }
     // the thread's largest key: largest value, then smallest token -- the first entry
     // holding the largest value bits (entries are in token order)

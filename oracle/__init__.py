@@ -31,6 +31,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "tmv_oracle.c")
 _LIB = os.path.join(_HERE, "libtmv_oracle.so")
+# a sanitizer build of the same source (tests/test_oracle_sanitized.py) is loaded instead
+# when TMV_ORACLE_LIB names it
+_LIB_OVERRIDE = os.environ.get("TMV_ORACLE_LIB")
 
 OK, ERR_ARG, ERR_RANGE, ERR_CYCLE, ERR_DEPTH, ERR_CLOSURE, ERR_INPUT = range(7)
 PARENTS_VROOT, PARENTS_NEG1 = 0, 1
@@ -53,8 +56,11 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            build()
+            lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         I, I64, U64, D = ctypes.c_int, ctypes.c_int64, ctypes.c_uint64, ctypes.c_double
         lib.tmvref_build_ancestors.argtypes = [I, I, I, I, P, P, P, P, P, P]

@@ -30,8 +30,12 @@ Timed regions (both after --warmup untimed steps):
   5. a streaming ceiling of the device (the better of torch.amax over 4 GiB and a 2 GiB
      device copy), reported as "stream_read_ceiling"; every kernel's GB/s is also given as
      a fraction of it.
-The oracle (tests-only CPU implementation) is timed on a bounded sample of the default
-workload for the cpu_baseline field.
+  6. workloads 2 and 4: greedy acceptance straight from the LM head (hidden 4096 / 8192,
+     vocabulary 128256, synthetic bf16 weights): the fused product + argmax against a
+     library GEMM that writes the logits followed by tree_accept, reported as "lm_head".
+The oracle (tests-only CPU implementation) is timed on a bounded sample of the same
+workload for the cpu_baseline field: once on one thread, then as one process per host
+thread (at most 16) running the sample concurrently.
 
 Prints one JSON line.
 """
@@ -177,27 +181,109 @@ def set_bytes(w):
 
 
 # ---------------------------------------------------------------- counters from profiles/
-def kernel_source_digest():
+# the sources each timed stage is compiled from (its kernels plus the shared device header
+# and the C ABI header)
+STAGE_SOURCES = {
+    "build": ["build_ancestors.hip"],
+    "attention": ["verify_attention.hip"],
+    "accept": ["accept.hip"],
+    "commit": ["commit.hip"],
+    "lm_head": ["accept.hip"],
+}
+
+
+def stage_source_digest(stage):
     h = hashlib.sha256()
     src = os.path.join(ROOT, "tree_masked_verification_amd", "csrc")
-    for name in sorted(os.listdir(src)):
+    for name in STAGE_SOURCES[stage] + ["tmv_device.hpp"]:
         with open(os.path.join(src, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.join(ROOT, "include", "tmv.h"), "rb") as f:
+        h.update(b"tmv.h\0" + f.read())
     return h.hexdigest()
 
 
-def traffic_from_profiles(kernel_key, workload):
-    """HBM bytes per launch from committed rocprofv3 counter runs of this workload, or
-    None when the kernels changed since the counters were taken."""
+def traffic_from_profiles(stage, workload):
+    """HBM bytes per launch of `stage` from the committed rocprofv3 counter runs of this
+    workload, or None when none was taken or the stage's sources changed since."""
     path = os.path.join(ROOT, "profiles", "hbm_counters.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_sha256") != kernel_source_digest() or rec.get("workload", 2) != workload:
+    k = rec.get("workloads", {}).get(str(workload), {}).get(stage)
+    if k is None or k.get("source_sha256") != stage_source_digest(stage):
         return None
-    k = rec.get("kernels", {}).get(kernel_key)
-    return None if k is None else k.get("hbm_bytes_per_launch")
+    return k.get("hbm_bytes_per_launch")
+
+
+STAGE_KERNELS = {
+    "build": ("build_ancestors_kernel",),
+    "attention": ("tree_attn_bf16_kernel", "tree_attn_bf16_stream_kernel", "tree_attn_merge_kernel",
+                  "tree_attn_f32_kernel"),
+    "accept": ("greedy_scan_kernel", "greedy_select_kernel", "sample_walk_kernel"),
+    "commit": ("commit_kernel",),
+}
+
+
+def stage_of(kernel_name):
+    """The timed stage a dispatched kernel belongs to; None for the paged-cache variants
+    (block-table template argument true), library kernels and everything else."""
+    import re
+    if re.search(r"tree_attn_bf16_kernel<\d+, \d+, (true|false), true>", kernel_name) or "commit_kernel<true>" in kernel_name:
+        return None
+    for stage, names in STAGE_KERNELS.items():
+        if any(re.search(r"\b%s\b" % n, kernel_name) for n in names):
+            return stage
+    return None
+
+
+def ingest_counters(workload, fetch_csv, write_csv, command):
+    """HBM bytes per launch of each stage from two rocprofv3 --pmc runs of this script with
+    --copy-probe (FETCH_SIZE, then WRITE_SIZE; per-dispatch KiB), each counter scaled by the
+    factor that makes it read the copy probe's known 256 MiB, into profiles/hbm_counters.json
+    under this workload, with each stage's source digest."""
+    import csv
+    import collections
+
+    def per_kernel(path):
+        agg = collections.defaultdict(list)
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in agg.items()}
+
+    fe, wr = per_kernel(fetch_csv), per_kernel(write_csv)
+    probe_kib = (256 << 20) / 1024
+    probe = [k for k in fe if "AUnaryFunctor" in k or "BUnaryFunctor" in k]
+    if len(probe) != 1:
+        raise RuntimeError("copy probe kernel not found once in the counter run: %s" % probe)
+    fscale, wscale = probe_kib / fe[probe[0]], probe_kib / wr[probe[0]]
+    stages = {}
+    for k in fe:
+        st = stage_of(k)
+        if st is None:
+            continue
+        e = stages.setdefault(st, {"fetch_kib": 0.0, "write_kib": 0.0, "kernels": []})
+        e["fetch_kib"] += fe[k]
+        e["write_kib"] += wr.get(k, 0.0)
+        e["kernels"].append(k.split("(")[0].replace("void ", ""))
+    for st, e in stages.items():
+        e["hbm_bytes_per_launch"] = (e["fetch_kib"] * fscale + e["write_kib"] * wscale) * 1024
+        e["source_sha256"] = stage_source_digest(st)
+    path = os.path.join(ROOT, "profiles", "hbm_counters.json")
+    rec = {"workloads": {}}
+    if os.path.exists(path):
+        with open(path) as f:
+            rec = json.load(f)
+        rec.setdefault("workloads", {})
+    rec["copy_probe_bytes"] = 256 << 20
+    rec["how"] = ("rocprofv3 FETCH_SIZE and WRITE_SIZE per dispatch (KiB), each scaled by the copy probe's "
+                  "known size, summed over the stage's kernels (one dispatch each per launch)")
+    rec["workloads"][str(workload)] = {"fetch_scale": fscale, "write_scale": wscale, "command": command, **stages}
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    return rec["workloads"][str(workload)]
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -205,35 +291,183 @@ def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
             if line.startswith("model name"):
-                return "%s (%d logical CPUs)" % (line.split(":", 1)[1].strip(), os.cpu_count() or 0)
+                return line.split(":", 1)[1].strip()
     except OSError:
         pass
     return None
 
 
-def cpu_baseline(w, budget_s):
-    """The oracle, as it stands, on whole verify steps of the same workload."""
+def host_threads():
+    """CPU threads this process may use, at most 16 (one GPU's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def slice_workload(w, seqs):
+    """The sequences `seqs` of workload w as a workload of their own (same layer)."""
+    import dataclasses
+    sl = lambda a: None if a is None else np.ascontiguousarray(a[seqs])
+    return dataclasses.replace(w, B=len(seqs), parents=sl(w.parents), n_nodes=sl(w.n_nodes), prefix=sl(w.prefix),
+                               tokens=sl(w.tokens), q=sl(w.q), k=sl(w.k), v=sl(w.v), logits=sl(w.logits),
+                               p=sl(w.p), qd=sl(w.qd))
+
+
+def cpu_sample(c, w):
+    """The bounded sample of workload c the oracle is timed on: (sample workload, attention
+    rows to compute or None for all, the factor from sampled to whole-step attention time,
+    layers of cache the commit sample moves, the factor to the workload's layers, words)."""
+    if c in (1, 2):
+        return w, None, 1.0, 1, 1.0, "whole verify steps of the workload"
+    if c == 3:
+        s = slice_workload(w, [0])
+        return s, None, 1.0, 1, 1.0, ("verify steps of sequence 0 of the batch (prefix %d, %d nodes)"
+                                      % (int(s.prefix[0]), int(s.n_nodes[0])))
+    if c == 4:
+        s = slice_workload(w, [0])
+        rows = np.zeros((1, s.M_max), np.uint8)
+        rows[0, ::8] = 1
+        return s, rows, s.M_max / int(rows.sum()), 1, 1.0, (
+            "verify steps of sequence 0 of the batch with the attention over every 8th tree node (%d of %d, its "
+            "time scaled by %d)" % (int(rows.sum()), s.M_max, s.M_max // int(rows.sum())))
+    s = slice_workload(w, [0, 1, 2, 3])
+    return s, None, 1.0, 1, float(w.n_layers), ("sampling acceptance of sequences 0-3 of the batch and their "
+                                                "commit over 1 of the %d layers (its time scaled by %d)"
+                                                % (w.n_layers, w.n_layers))
+
+
+def oracle_worker(args):
+    """Oracle verify steps on a sample for about budget_s seconds; returns (steps, seconds
+    per stage).  Runs in a worker process of its own (the oracle is single-threaded)."""
+    w, rows, layers, budget_s = args
+    import oracle
+    t = {"build": 0.0, "attention": 0.0, "accept": 0.0, "commit": 0.0}
+    if w.mode == "greedy":
+        k, v = w.k.copy()[None], w.v.copy()[None]
+    else:
+        shape = (layers, w.B, w.Hkv, w.L_cap, w.d)
+        k, v = np.zeros(shape, np.uint16), np.ones(shape, np.uint16)
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        a = time.perf_counter()
+        anc, depth, st = oracle.build_ancestors(w.parents, w.n_nodes, w.M_max, w.D_max)
+        b = time.perf_counter()
+        t["build"] += b - a
+        if w.mode == "greedy":
+            out, st = oracle.tree_attention(w.q, k[0], v[0], w.prefix, w.n_nodes, anc, depth, st, w.scale, w.dtype,
+                                            w.Hkv, row_select=rows)
+            a = time.perf_counter()
+            t["attention"] += a - b
+            A, path, nxt, st = oracle.accept_greedy(w.tokens, w.logits, w.n_nodes, anc, depth, st)
+        else:
+            a = time.perf_counter()
+            A, path, nxt, st = oracle.accept_sample(w.tokens, w.p, w.qd, w.seed, w.step, w.n_nodes, anc, depth, st)
+        b = time.perf_counter()
+        t["accept"] += b - a
+        oracle.commit(k, v, w.prefix, w.n_nodes, A, path, st, w.M_max)
+        t["commit"] += time.perf_counter() - b
+        steps += 1
+        if time.perf_counter() - t0 >= budget_s or steps >= 1000:
+            break
+    return steps, t
+
+
+def cpu_baseline(c, w, budget_s):
+    """The oracle, as it stands, on a bounded sample of workload c: once on one thread, then
+    as one process per host thread (up to 16) running the same sample concurrently; the
+    value is the concurrent aggregate in node-tokens/s of the whole workload."""
+    import multiprocessing as mp
     import oracle
     oracle.build()
-    k = w.k.copy()
-    v = w.v.copy()
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
-        anc, depth, st = oracle.build_ancestors(w.parents, w.n_nodes, w.M_max, w.D_max)
-        out, st = oracle.tree_attention(w.q, k, v, w.prefix, w.n_nodes, anc, depth, st, w.scale, w.dtype, w.Hkv)
-        A, path, nxt, st = oracle.accept_greedy(w.tokens, w.logits, w.n_nodes, anc, depth, st)
-        oracle.commit(k[None], v[None], w.prefix, w.n_nodes, A, path, st, w.M_max)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or steps >= 1000:
-            break
-    node_tokens = steps * int(w.n_nodes.sum())
-    return {"value": node_tokens / el, "unit": "node-tokens/s", "cores": 1, "kind": "oracle", "cpu": cpu_model(),
-            "sample": "%d full verify steps of the same workload (build, attention over all %d query rows, "
-                      "greedy accept over %d x %d logits, commit), single thread, %.1f s"
-                      % (steps, int(w.n_nodes.sum()) * w.Hq, int(w.n_nodes.sum()) + w.B, w.V, el),
-            "ms_per_step": 1e3 * el / steps}
+    s, rows, attn_scale, layers, commit_scale, words = cpu_sample(c, w)
+    nodes = int(s.n_nodes.sum())
+
+    def rate(steps, t):
+        step_s = (t["build"] + t["attention"] * attn_scale + t["accept"] + t["commit"] * commit_scale) / steps
+        return nodes / step_s, step_s
+
+    steps1, t1 = oracle_worker((s, rows, layers, budget_s))
+    v1, step1 = rate(steps1, t1)
+    n = host_threads()
+    with mp.get_context("spawn").Pool(n) as pool:
+        res = pool.map(oracle_worker, [(s, rows, layers, budget_s)] * n)
+    vn = sum(rate(st, t)[0] for st, t in res)
+    return {"value": round(vn, 2), "unit": "node-tokens/s", "cores": n, "kind": "oracle", "cpu": cpu_model(),
+            "sample": "%s; the oracle on %d processes at once (one per host thread), each about %.0f s; the "
+                      "single-thread leg ran %d step(s) at %.3g s per step" % (words, n, budget_s, steps1, step1),
+            "single_thread": {"value": round(v1, 2), "cores": 1, "s_per_step": float("%.4g" % step1)}}
+
+
+# ---------------------------------------------------------------- LM head with fused argmax
+def time_lm_head(torch, tmv, s, stream, K, reps=20):
+    """Greedy acceptance straight from the LM head on the first input set's trees: the fused
+    bf16 product + argmax (logits never written) against a library bf16 GEMM that writes the
+    logits followed by the greedy accept on them.  Hidden states N(0,1) and weights
+    N(0, 0.03^2) bf16 from a seeded device generator; the weight matrix (K x vocabulary,
+    1 GB at K 4096) is larger than the Infinity Cache, so every launch streams it from HBM."""
+    w = s.w
+    g = torch.Generator(device="cuda")
+    g.manual_seed(777)
+    W = (torch.randn((w.V, K), generator=g, device="cuda") * 0.03).to(torch.bfloat16)
+    H = torch.randn((w.B, w.M_max + 1, K), generator=g, device="cuda").to(torch.bfloat16)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    A, path, nxt = torch.zeros((w.B,), **i32), torch.zeros((w.B, w.D_max), **i32), torch.zeros((w.B,), **i32)
+    A2, path2, nxt2 = torch.zeros_like(A), torch.zeros_like(path), torch.zeros_like(nxt)
+    ws = torch.zeros(tmv.tree_accept_lm_head_workspace(w.B, w.M_max), dtype=torch.uint8, device="cuda")
+    ws2 = torch.zeros(tmv.tree_accept_workspace(tmv.ACCEPT_GREEDY, w.B, w.M_max, w.V), dtype=torch.uint8,
+                      device="cuda")
+    logits = torch.empty((w.B, w.M_max + 1, w.V), dtype=torch.bfloat16, device="cuda")
+    st = s.status
+    torch.cuda.synchronize()            # weights and zeroed workspaces were made on torch's stream
+
+    def fused():
+        tmv.tree_accept_lm_head(s.tokens, H, W, s.n_nodes, s.anc, s.depth, st, A, path, nxt, workspace=ws,
+                                stream=stream)
+
+    def gemm():
+        torch.matmul(H.view(-1, K), W.t(), out=logits.view(-1, w.V))
+
+    def scan():
+        tmv.tree_accept(tmv.ACCEPT_GREEDY, s.tokens, logits, s.n_nodes, s.anc, s.depth, st, A2, path2, nxt2,
+                        workspace=ws2, stream=stream)
+
+    def timed(fn):
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                fn()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=stream):
+                for _ in range(reps):
+                    fn()
+            gr.replay()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            gr.replay()
+            e1.record(stream)
+            e1.synchronize()
+        del gr
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    us_f, us_g, us_s = timed(fused), timed(gemm), timed(scan)
+    torch.cuda.synchronize()
+    if int(st.abs().sum()) != 0:
+        raise RuntimeError("tree_accept_lm_head reported a non-OK status")
+    nb = w.V * K * 2 + H.numel() * 2
+    fl = 2.0 * w.V * K * H.shape[0] * H.shape[1]
+    gbs = nb / (us_f * 1e-6) / 1e9
+    del W, H, logits
+    torch.cuda.empty_cache()
+    return {"hidden": K, "rows": w.B * (w.M_max + 1), "vocab": w.V,
+            "fused_argmax": {"avg_us": round(us_f, 3), "bytes": int(nb), "GB/s": round(gbs, 1),
+                             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                             "TFLOP/s": round(fl / (us_f * 1e-6) / 1e12, 1)},
+            "library_gemm_then_accept": {"avg_us": round(us_g + us_s, 3), "gemm_us": round(us_g, 3),
+                                         "accept_us": round(us_s, 3),
+                                         "how": "torch.matmul bf16 into bf16 logits, then tree_accept greedy"},
+            "speedup": round((us_g + us_s) / us_f, 3)}
 
 
 # ---------------------------------------------------------------- main
@@ -254,6 +488,7 @@ def time_best_first(torch, tmv, ti, stream, B=16, D=8, V=128256, N=128):
     ws = torch.empty(tmv.tree_best_first_workspace(B, D, V, N), dtype=torch.uint8, device="cuda")
     run = lambda q: tmv.tree_best_first(q, N, parents, tokens, n_nodes, rho, status, workspace=ws, stream=stream)
     reps = 40
+    torch.cuda.synchronize()            # inputs were made on torch's stream
     with torch.cuda.stream(stream):
         for q in qs:
             run(q)
@@ -349,6 +584,7 @@ def time_paged(torch, tmv, sets, stream, durations, page_size=16, reps=None):
 
     reps = reps or (40 if w0.B * w0.L_cap > 100000 else 400)
     out = {}
+    torch.cuda.synchronize()            # the pools were filled on torch's stream
     with torch.cuda.stream(stream):
         for name, fn in (("attention", attn), ("commit", commit)):
             for e in paged:
@@ -536,9 +772,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-lm-head", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain copy kernel of known size (for counter scaling)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/hbm_counters.json for --workload from two rocprofv3 --pmc runs "
+                         "(FETCH_SIZE, WRITE_SIZE) of this script with --copy-probe, and exit")
+    ap.add_argument("--counter-command", default="", help="the profiled command, recorded with --ingest-counters")
     args = ap.parse_args()
+    if args.ingest_counters:
+        print(json.dumps(ingest_counters(args.workload, args.ingest_counters[0], args.ingest_counters[1],
+                                         args.counter_command), indent=1))
+        return
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only; --gpus %d is not supported "
               "(the multi-GPU sharding is described in the design notes, not run)" % args.gpus, file=sys.stderr)
@@ -667,9 +912,18 @@ def main():
         print("bench: copy probe %d bytes read, %d bytes written per launch (3 launches)" % (n, n),
               file=sys.stderr, flush=True)
 
+    lm_head = None
+    if c in (2, 4) and not args.no_lm_head:
+        lm_head = time_lm_head(torch, tmv, sets[0], stream, 4096 if c == 2 else 8192)
+        print("bench: LM head + greedy accept: fused %.2f us, library GEMM + accept %.2f us"
+              % (lm_head["fused_argmax"]["avg_us"], lm_head["library_gemm_then_accept"]["avg_us"]),
+              file=sys.stderr, flush=True)
+
     cpu = None
-    if not args.no_cpu and c in (1, 2):
-        cpu = cpu_baseline(w0, args.cpu_budget)
+    if not args.no_cpu:
+        cpu = cpu_baseline(c, w0, args.cpu_budget)
+        print("bench: oracle %.4g node-tokens/s on %d processes (%.4g on one)"
+              % (cpu["value"], cpu["cores"], cpu["single_thread"]["value"]), file=sys.stderr, flush=True)
 
     config = {"workload": w0.name, "batch": w0.B,
               "prefix": int(w0.prefix[0]) if w0.B == 1 else [int(x) for x in w0.prefix],
@@ -687,6 +941,7 @@ def main():
         "kernels": kernels,
         "drafting": drafting,
         "paged": paged,
+        "lm_head": lm_head,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -8,6 +8,36 @@ import torch
 import tmv_inputs as ti
 
 
+GUARD_BYTES = 4096          # canary band on each side of a guarded device buffer
+GUARD_FILL = 0xA5
+
+
+class Guards:
+    """Device buffers with canary bands: each lives in the middle of a larger allocation
+    whose first and last GUARD_BYTES hold GUARD_FILL, and check() fails if any band changed
+    -- a write past either end of an output or a cache."""
+
+    def __init__(self):
+        self.bufs = []
+
+    def alloc(self, shape, dtype, fill=None, like=None):
+        n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        raw = torch.full((n + 2 * GUARD_BYTES,), GUARD_FILL, dtype=torch.uint8, device="cuda")
+        t = raw[GUARD_BYTES:GUARD_BYTES + n].view(dtype).view(tuple(shape))
+        if like is not None:
+            t.copy_(like)
+        elif fill is not None:
+            t.fill_(fill)
+        self.bufs.append((raw, n))
+        return t
+
+    def check(self):
+        for raw, n in self.bufs:
+            lo = raw[:GUARD_BYTES].cpu().numpy()
+            hi = raw[GUARD_BYTES + n:].cpu().numpy()
+            assert np.all(lo == GUARD_FILL) and np.all(hi == GUARD_FILL), "a canary band was overwritten"
+
+
 def dev_tensor(a, bf16=False):
     t = torch.from_numpy(np.ascontiguousarray(a))
     if bf16:
@@ -36,35 +66,41 @@ class DeviceStep:
         self.w = w
         B, M, D = w.B, w.M_max, w.D_max
         bf = w.dtype == ti.BF16
+        self.guards = Guards()
+        g = self.guards
         self.parents = dev_tensor(w.parents.astype(np.int32))
         self.n_nodes = dev_tensor(w.n_nodes.astype(np.int32))
         self.prefix = dev_tensor(w.prefix.astype(np.int32))
         self.tokens = dev_tensor(w.tokens.astype(np.int32))
-        self.anc = torch.full((B, M + 1, D + 1), -7, dtype=torch.int32, device="cuda")
-        self.depth = torch.full((B, M + 1), -7, dtype=torch.int32, device="cuda")
-        self.status = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+        i32 = torch.int32
+        self.anc = g.alloc((B, M + 1, D + 1), i32, fill=-7)
+        self.depth = g.alloc((B, M + 1), i32, fill=-7)
+        self.status = g.alloc((B,), i32, fill=-7)
         if w.q is not None:
             self.q = dev_tensor(w.q, bf)
-            self.k = dev_tensor(w.k, bf)
-            self.v = dev_tensor(w.v, bf)
-            self.out = torch.full_like(self.q, float("nan"))
+            # the caches are written by the commit: guarded too
+            self.k = g.alloc(w.k.shape, torch.bfloat16 if bf else torch.float32, like=dev_tensor(w.k, bf))
+            self.v = g.alloc(w.v.shape, torch.bfloat16 if bf else torch.float32, like=dev_tensor(w.v, bf))
+            self.out = g.alloc(w.q.shape, torch.bfloat16 if bf else torch.float32, fill=float("nan"))
         if w.logits is not None:
             self.logits = dev_tensor(w.logits)
         if w.p is not None:
             self.p = dev_tensor(w.p)
             self.qd = dev_tensor(w.qd)
-        self.accept_len = torch.full((B,), -7, dtype=torch.int32, device="cuda")
-        self.path = torch.full((B, D), -7, dtype=torch.int32, device="cuda")
-        self.next_token = torch.full((B,), -7, dtype=torch.int32, device="cuda")
-        self.new_len = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+        self.accept_len = g.alloc((B,), i32, fill=-7)
+        self.path = g.alloc((B, D), i32, fill=-7)
+        self.next_token = g.alloc((B,), i32, fill=-7)
+        self.new_len = g.alloc((B,), i32, fill=-7)
 
     def build(self, valid=None, parent_format=0, parents=None):
         self.tmv.tree_build_ancestors(self.parents if parents is None else parents, self.n_nodes, self.anc,
                                       self.depth, self.status, parent_format=parent_format, valid=valid)
+        self.guards.check()
 
     def attention(self, workspace=None, plan=None):
         self.tmv.tree_verify_attention(self.q, self.k, self.v, self.prefix, self.n_nodes, self.anc, self.depth,
                                        self.status, self.out, scale=self.w.scale, workspace=workspace, plan=plan)
+        self.guards.check()
 
     def accept(self, workspace=None):
         w = self.w
@@ -76,12 +112,14 @@ class DeviceStep:
             self.tmv.tree_accept(self.tmv.ACCEPT_SAMPLE, self.tokens, self.p, self.n_nodes, self.anc, self.depth,
                                  self.status, self.accept_len, self.path, self.next_token, draft_q=self.qd,
                                  seed=w.seed, step=w.step, workspace=workspace)
+        self.guards.check()
 
     def commit(self, k_cache=None, v_cache=None):
         kc = self.k if k_cache is None else k_cache
         vc = self.v if v_cache is None else v_cache
         self.tmv.kv_commit_path(kc, vc, self.prefix, self.n_nodes, self.accept_len, self.path, self.status,
                                 self.new_len, self.w.M_max)
+        self.guards.check()
 
     def tables(self):
         torch.cuda.synchronize()

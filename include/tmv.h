@@ -248,7 +248,8 @@ int tmv_tree_verify_attention_paged_plan(int dtype, int B, int M_max, int D_max,
  * GREEDY (Medusa section of the hierarchical speculative decoding blog: the longest
  * valid branch is kept; teacher-greedy decoding is the baseline of section 4 of the
  * Portuguese EAGLE-Pangu summary):
- *   t(u) = argmax_x teacher[b][u][x] (smallest x on ties) for u = 0 and every live node;
+ *   t(u) = argmax_x teacher[b][u][x] (smallest x on ties; -0 and +0 are equal) for u = 0
+ *   and every live node;
  *   node i matches iff every node c on its path has tokens[c] == t(parent(c));
  *   the deepest matching node a* (smallest id on ties; 0 if none) gives
  *   accept_len = depth(a*), path = its ancestors root->leaf, next_token = t(a*).

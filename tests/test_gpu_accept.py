@@ -100,6 +100,24 @@ def test_greedy_errors_and_degenerate(ref):
     _greedy_parity(ref, w0)
 
 
+@pytest.mark.parametrize("V", [300, 9000])
+def test_greedy_signed_zero_ties(ref, V):
+    """Rows whose maximum is a -0.0 and a +0.0: the two compare equal, so the first of them
+    is the argmax (in one chunk, or in different chunks of the scan); fp32 and bf16 rows."""
+    _case("greedy: -0.0 / +0.0 maxima, V=%d" % V)
+    from tests.test_oracle_greedy import signed_zero_rows
+    rng = np.random.default_rng(330 + V)
+    B, M_max = 6, 8
+    parents, tokens, logits, first = signed_zero_rows(rng, B, M_max, V)
+    w = ti.Workload("signed-zeros", ti.F32, B, 0, 1, 64, M_max, M_max, 1, V, "greedy", parents,
+                    np.full(B, M_max, np.int32), np.zeros(B, np.int32), tokens, logits=logits)
+    A, st = _greedy_parity(ref, w)
+    assert np.all(st == 0) and np.any(A > 1)
+    lb = ti.bf16_bits(logits)
+    assert np.array_equal(np.argmax(ti.bf16_to_f32(lb), axis=2), first)
+    _greedy_parity(ref, w, logits_dev=dev_tensor(lb, bf16=True), row_dtype=1, logits_host=lb)
+
+
 @pytest.mark.parametrize("c", [1, 2, 4])
 def test_greedy_workloads(ref, c):
     _case("greedy: workload %d" % c)

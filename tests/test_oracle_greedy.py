@@ -127,3 +127,36 @@ def test_empty_tree_emits_root_choice(ref):
     anc, depth, st = ref.build_ancestors(np.zeros((1, 1), np.int32), np.array([0]), 0, 0)
     A, path, nxt, st2 = ref.accept_greedy(np.zeros((1, 1), np.int32), logits, np.array([0]), anc, depth, st)
     assert A[0] == 0 and nxt[0] == 1 and st2[0] == 0 and path.shape == (1, 0)
+
+
+def signed_zero_rows(rng, B, M_max, V):
+    """Chains whose rows are all negative except a -0.0 and a +0.0 at random places (either
+    order): the row maximum is zero twice, and -0 == +0 makes the first of the two the
+    argmax.  Each child carries that first position with probability 0.8."""
+    logits = -rng.uniform(0.5, 2.0, size=(B, M_max + 1, V)).astype(np.float32)
+    parents = np.zeros((B, M_max + 1), np.int32)
+    parents[:, 1:] = np.arange(M_max)[None, :]
+    tokens = np.zeros((B, M_max + 1), np.int32)
+    first = np.zeros((B, M_max + 1), np.int64)
+    for b in range(B):
+        for u in range(M_max + 1):
+            p1, p2 = rng.choice(V, size=2, replace=False)
+            logits[b, u, p1], logits[b, u, p2] = (-0.0, 0.0) if rng.random() < 0.5 else (0.0, -0.0)
+            first[b, u] = min(p1, p2)
+        for c in range(1, M_max + 1):
+            tokens[b, c] = first[b, c - 1] if rng.random() < 0.8 else (first[b, c - 1] + 1) % V
+    return parents, tokens, logits, first
+
+
+def test_signed_zeros_tie_to_first_index(ref):
+    rng = np.random.default_rng(23)
+    B, M_max, V = 12, 8, 300
+    parents, tokens, logits, first = signed_zero_rows(rng, B, M_max, V)
+    assert np.array_equal(np.argmax(logits, axis=2), first)          # numpy: -0 == +0
+    n = np.full(B, M_max, np.int32)
+    anc, depth, st = ref.build_ancestors(parents, n, M_max, M_max)
+    A, path, nxt, st2 = ref.accept_greedy(tokens, logits, n, anc, depth, st)
+    assert np.all(st2 == 0)
+    for b in range(B):
+        assert (A[b], path[b].tolist(), nxt[b]) == brute_force(parents[b], M_max, tokens[b], logits[b], M_max)
+    assert np.any(A > 1)

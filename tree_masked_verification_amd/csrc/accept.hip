@@ -4,10 +4,10 @@
 //   path matches those choices (Medusa section of "Speculative Decoding Hierarquico":
 //   the longest valid branch is kept).  The row scans are the HBM-bound part: one
 //   workgroup per (sequence, row, vocabulary chunk) reads its chunk with 16-byte loads
-//   and reduces a 64-bit key (order-preserving value bits << 32 | ~index), so max() gives
-//   the largest value and, on ties, the smallest index.  A second kernel (one
-//   workgroup per sequence, ordered after the scan on the stream) merges the chunk keys
-//   and picks the path -- no cross-workgroup synchronisation inside a kernel.
+//   and reduces it to a 64-bit key (order-preserving value bits << 32 | ~index, -0 keyed
+//   as +0), so max() gives the largest value and, on ties, the smallest index.  A second
+//   kernel (one workgroup per sequence, ordered after the scan on the stream) merges the
+//   chunk keys and picks the path -- no cross-workgroup synchronisation inside a kernel.
 // SAMPLE: modified rejection sampling (same page, its rejection-sampling section and
 //   FAQ), children of the current node tried in ascending id against the running
 //   residual, which against one draft row keeps the form (p - c q)+.  Exact integer fixed
@@ -23,136 +23,78 @@ using tmv::u128;
 
 // ============================================================== greedy
 constexpr int kScanThreads = 256;
-constexpr int kScanChunk = 4096;          // vocabulary entries per workgroup (four 16-byte loads per thread)
+constexpr int kScanChunk = 4096;          // vocabulary entries per workgroup (four 16-byte fp32 loads per thread)
 constexpr uint64_t kNanKey = ~0ull;       // a chunk with a NaN reports the all-ones key
+constexpr int kSelectBatch = 8;           // chunk keys per thread in flight in the path choice
 
 __device__ __forceinline__ uint32_t order_bits(float v) {
     const uint32_t u = __float_as_uint(v);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// key of value v at index idx: order-preserving value bits << 32 | ~idx, with -0 keyed as
+// +0 (the two compare equal, so the smaller index wins between them)
+__device__ __forceinline__ uint64_t value_key(float v, int idx) {
+    if (__float_as_uint(v) == 0x80000000u) v = 0.0f;
+    return (static_cast<uint64_t>(order_bits(v)) << 32) | (0xffffffffu - static_cast<uint32_t>(idx));
+}
+
 __device__ __forceinline__ void scan_one(float v, int idx, uint64_t &best, bool &nan) {
     if (v != v) nan = true;
-    const uint64_t key = (static_cast<uint64_t>(order_bits(v)) << 32) | (0xffffffffu - static_cast<uint32_t>(idx));
+    const uint64_t key = value_key(v, idx);
     best = key > best ? key : best;
 }
 
-template <int DT>
-__global__ void __launch_bounds__(kScanThreads)
-greedy_scan_kernel(int M_max, int V, int nchunk, const void *__restrict__ teacher, int64_t sb, int64_t sr,
-                   const int32_t *__restrict__ n_nodes, const int32_t *__restrict__ depth,
-                   const int32_t *__restrict__ status, uint64_t *__restrict__ keys)
-{
-    __shared__ uint64_t red[kScanThreads / kWave];
-    const int R = M_max + 1;
-    const int chunk = blockIdx.x % nchunk;
-    const int u = (blockIdx.x / nchunk) % R;
-    const int b = blockIdx.x / (nchunk * R);
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
-    // The row's loads go out before the words that decide whether the row is live have
-    // returned: every (b, u, chunk) of the grid addresses the teacher tensor in bounds, so
-    // a dead row only costs bandwidth, and a live one saves a round trip.
-    const int M = n_nodes[b];
-    const int st = status[b];
-    const int dp = u > 0 ? depth[static_cast<int64_t>(b) * R + u] : 1;
+// The path choice of sequence b (one workgroup of kScanThreads threads, rows on threads):
+// t(u) of every live row from its merged key, the draft tokens checked against them, the
+// deepest matching node (smallest id on ties) and its path.  load_path_inputs issues the
+// per-row reads (token, depth, first ancestor entries; indices clamped into the tables) so
+// that they travel together with the caller's key reads; choose_path_from takes this
+// thread's row key (all ones after a NaN) and does the rest.  row_argmax, if not null,
+// receives t(u) of every live row and -1 elsewhere.
+constexpr int kAncBatch = 8;                       // ancestor entries per node fetched at once
 
-    const int x0 = chunk * kScanChunk;
-    const int x1 = min(V, x0 + kScanChunk);
-    uint64_t best = 0;
-    bool nan = false;
-    if constexpr (DT == TMV_F32) {
-        const float *row = static_cast<const float *>(teacher) + b * sb + static_cast<int64_t>(u) * sr;
-        constexpr int kPer = kScanChunk / (4 * kScanThreads);        // float4 per thread
-        if (x1 - x0 == kScanChunk && ((reinterpret_cast<uintptr_t>(row + x0) & 15u) == 0)) {
-            const float4 *r4 = reinterpret_cast<const float4 *>(row + x0);
-            float4 f[kPer];
+struct PathInputs {
+    int M, st_in, tok, dep;
+    int a8[kAncBatch];
+    const int32_t *arow;
+};
+
+__device__ __forceinline__ PathInputs load_path_inputs(int b, int M_max, int D_max, const int32_t *__restrict__ tokens,
+                                                       const int32_t *__restrict__ n_nodes,
+                                                       const int32_t *__restrict__ anc,
+                                                       const int32_t *__restrict__ depth,
+                                                       const int32_t *__restrict__ status)
+{
+    PathInputs in;
+    const int R = M_max + 1, W = D_max + 1, tid = threadIdx.x;
+    const int row = tid < R ? tid : R - 1;
+    const int64_t rb = static_cast<int64_t>(b) * R + row;
+    in.M = n_nodes[b];
+    in.st_in = status[b];
+    in.tok = tokens[rb];
+    in.dep = row > 0 ? depth[rb] : 0;
+    in.arow = anc + rb * W;
 #pragma unroll
-            for (int i = 0; i < kPer; ++i) f[i] = r4[tid + i * kScanThreads];
-            if (st != TMV_OK || M < 0 || M > M_max || u > M || dp < 1) return;
-#pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-                const int x = x0 + 4 * (tid + i * kScanThreads);
-                scan_one(f[i].x, x, best, nan);
-                scan_one(f[i].y, x + 1, best, nan);
-                scan_one(f[i].z, x + 2, best, nan);
-                scan_one(f[i].w, x + 3, best, nan);
-            }
-        } else {
-            if (st != TMV_OK || M < 0 || M > M_max || u > M || dp < 1) return;
-            for (int x = x0 + tid; x < x1; x += kScanThreads) scan_one(row[x], x, best, nan);
-        }
-    } else {
-        const uint16_t *row = static_cast<const uint16_t *>(teacher) + b * sb + static_cast<int64_t>(u) * sr;
-        constexpr int kPer = kScanChunk / (8 * kScanThreads);        // 8 bf16 per thread and load
-        if (x1 - x0 == kScanChunk && ((reinterpret_cast<uintptr_t>(row + x0) & 15u) == 0)) {
-            const uint4 *r8 = reinterpret_cast<const uint4 *>(row + x0);
-            uint4 h[kPer];
-#pragma unroll
-            for (int i = 0; i < kPer; ++i) h[i] = r8[tid + i * kScanThreads];
-            if (st != TMV_OK || M < 0 || M > M_max || u > M || dp < 1) return;
-#pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-                const int x = x0 + 8 * (tid + i * kScanThreads);
-                const uint32_t w[4] = {h[i].x, h[i].y, h[i].z, h[i].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    scan_one(__uint_as_float(w[e] << 16), x + 2 * e, best, nan);
-                    scan_one(__uint_as_float(w[e] & 0xffff0000u), x + 2 * e + 1, best, nan);
-                }
-            }
-        } else {
-            if (st != TMV_OK || M < 0 || M > M_max || u > M || dp < 1) return;
-            for (int x = x0 + tid; x < x1; x += kScanThreads) scan_one(tmv::bf16_to_f32(row[x]), x, best, nan);
-        }
-    }
-    if (nan) best = kNanKey;
-    best = tmv::wave_max_u64(best);
-    if (lane == 0) red[wv] = best;
-    __syncthreads();
-    if (tid == 0) {
-        uint64_t k = red[0];
-        for (int w = 1; w < kScanThreads / kWave; ++w) k = red[w] > k ? red[w] : k;
-        keys[(static_cast<int64_t>(b) * R + u) * nchunk + chunk] = k;
-    }
+    for (int k = 0; k < kAncBatch; ++k) in.a8[k] = in.arow[k < W ? k : W - 1];
+    return in;
 }
 
-// One workgroup per sequence, after the scan: merge the chunk keys of every live row into
-// t(u), check the draft tokens, mark matching nodes and pick the deepest (smallest id).
-// (clear_keys: every key read is set back to zero -- the LM-head path accumulates its keys
-// with atomics into a zeroed workspace; row_argmax, if not null, receives t(u) of every live
-// row and -1 elsewhere)
-__global__ void __launch_bounds__(kScanThreads)
-greedy_select_kernel(int M_max, int D_max, int V, int nchunk, const int32_t *__restrict__ tokens,
-                     const int32_t *__restrict__ n_nodes, const int32_t *__restrict__ anc,
-                     const int32_t *__restrict__ depth, int32_t *__restrict__ status,
-                     int32_t *__restrict__ accept_len, int32_t *__restrict__ path,
-                     int32_t *__restrict__ next_token, uint64_t *__restrict__ keys, int clear_keys,
-                     int32_t *__restrict__ row_argmax)
+__device__ __forceinline__ void choose_path_from(const PathInputs &in, int b, int M_max, int D_max, int V,
+                                                 uint64_t krow, int32_t *__restrict__ status,
+                                                 int32_t *__restrict__ accept_len, int32_t *__restrict__ path,
+                                                 int32_t *__restrict__ next_token, const int32_t *__restrict__ anc,
+                                                 int32_t *__restrict__ row_argmax)
 {
-    constexpr int kKeyBatch = 32;                  // chunk keys per row fetched at once
-    constexpr int kAncBatch = 8;                   // ancestor entries per node fetched at once
     __shared__ int32_t tsel[129], tok_sh[129];
     __shared__ int32_t anc_sh[129][kAncBatch];     // every row's first ancestor entries
     __shared__ int bad;
     __shared__ uint64_t best_node[kScanThreads / kWave];
     const int R = M_max + 1, W = D_max + 1;
-    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
-
-    // one round trip: sequence scalars, this thread's row of keys, token, depth and
-    // first ancestor entries (indices clamped into the tables)
-    const int M = n_nodes[b];
-    const int st_in = status[b];
-    const int row = tid < R ? tid : R - 1;
-    const int64_t rb = static_cast<int64_t>(b) * R + row;
-    uint64_t kb[kKeyBatch];
-#pragma unroll
-    for (int c = 0; c < kKeyBatch; ++c) kb[c] = c < nchunk ? keys[rb * nchunk + c] : 0;
-    const int tok = tokens[rb];
-    const int dep = row > 0 ? depth[rb] : 0;
-    int a8[kAncBatch];
-    const int32_t *arow = anc + rb * W;
-#pragma unroll
-    for (int k = 0; k < kAncBatch; ++k) a8[k] = arow[k < W ? k : W - 1];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+    const int M = in.M, st_in = in.st_in, tok = in.tok, dep = in.dep;
+    const int32_t *arow = in.arow;
+    const int64_t rb = static_cast<int64_t>(b) * R + (tid < R ? tid : R - 1);
 
     // a node count outside [0, M_max] cannot come with an OK status from the build stage;
     // it is rejected here so that no row beyond the tables is ever addressed
@@ -162,22 +104,13 @@ greedy_select_kernel(int M_max, int D_max, int V, int nchunk, const int32_t *__r
     if (tid < R) {
         tok_sh[tid] = tok;
 #pragma unroll
-        for (int k = 0; k < kAncBatch; ++k) anc_sh[tid][k] = a8[k];
+        for (int k = 0; k < kAncBatch; ++k) anc_sh[tid][k] = in.a8[k];
     }
     __syncthreads();
     const bool row_live = st == TMV_OK && tid < R && tid <= M && (tid == 0 || dep >= 1);
     if (row_live) {
-        uint64_t k = 0;
-#pragma unroll
-        for (int c = 0; c < kKeyBatch; ++c) k = kb[c] > k ? kb[c] : k;
-        for (int c = kKeyBatch; c < nchunk; ++c) {
-            const uint64_t kc = keys[rb * nchunk + c];
-            k = kc > k ? kc : k;
-        }
-        if (clear_keys)
-            for (int c = 0; c < nchunk; ++c) keys[rb * nchunk + c] = 0;
-        if (k == kNanKey) bad = 1;
-        tsel[tid] = static_cast<int32_t>(0xffffffffu - static_cast<uint32_t>(k & 0xffffffffu));
+        if (krow == kNanKey) bad = 1;
+        tsel[tid] = static_cast<int32_t>(0xffffffffu - static_cast<uint32_t>(krow & 0xffffffffu));
         if (tid > 0 && (tok < 0 || tok >= V)) bad = 1;
     }
     __syncthreads();
@@ -199,8 +132,8 @@ greedy_select_kernel(int M_max, int D_max, int V, int nchunk, const int32_t *__r
 #pragma unroll
         for (int k = 0; k < kAncBatch; ++k) {
             if (k < dep) {
-                const int parent = k + 1 < kAncBatch ? a8[k + 1] : arow[k + 1];
-                ok = ok && tok_sh[a8[k]] == tsel[k + 1 < dep ? parent : 0];
+                const int parent = k + 1 < kAncBatch ? in.a8[k + 1] : arow[k + 1];
+                ok = ok && tok_sh[in.a8[k]] == tsel[k + 1 < dep ? parent : 0];
             }
         }
         for (int k = kAncBatch; k < dep && ok; ++k)
@@ -227,6 +160,144 @@ greedy_select_kernel(int M_max, int D_max, int V, int nchunk, const int32_t *__r
         const int e = dstar - 1 - j;
         pth[j] = j >= dstar ? 0 : e < kAncBatch ? anc_sh[star][e] : anc[(static_cast<int64_t>(b) * R + star) * W + e];
     }
+}
+
+// One workgroup per (sequence, row, chunk of kScanChunk entries): the chunk's key.  The
+// liveness words (status, n_nodes, the row's depth) are read first and a dead row loads
+// nothing of its logits.  In a whole, aligned chunk each thread's values are reduced in
+// ascending index order by a running maximum under a strict comparison (the first of
+// equal values is kept, -0 equals +0, NaN fails every comparison and is flagged on its
+// own) and the 64-bit key is formed once per thread.
+template <int DT>
+__global__ void __launch_bounds__(kScanThreads)
+greedy_scan_kernel(int M_max, int V, int nchunk, const void *__restrict__ teacher, int64_t sb, int64_t sr,
+                   const int32_t *__restrict__ n_nodes, const int32_t *__restrict__ depth,
+                   const int32_t *__restrict__ status, uint64_t *__restrict__ keys)
+{
+    __shared__ uint64_t red[kScanThreads / kWave];
+    const int R = M_max + 1;
+    const int chunk = blockIdx.x % nchunk;
+    const int u = (blockIdx.x / nchunk) % R;
+    const int b = blockIdx.x / (nchunk * R);
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+    const int M = n_nodes[b];
+    const int st = status[b];
+    const int dp = u > 0 ? depth[static_cast<int64_t>(b) * R + u] : 1;
+    if (st != TMV_OK || M < 0 || M > M_max || u > M || dp < 1) return;
+
+    constexpr int kElem = DT == TMV_F32 ? 4 : 2;
+    const int x0 = chunk * kScanChunk;
+    const int x1 = min(V, x0 + kScanChunk);
+    const char *row = static_cast<const char *>(teacher) + (b * sb + static_cast<int64_t>(u) * sr) * kElem;
+    uint64_t best = 0;
+    bool nan = false;
+    if (x1 - x0 == kScanChunk && ((reinterpret_cast<uintptr_t>(row + x0 * kElem) & 15u) == 0)) {
+        constexpr int kPer = kScanChunk * kElem / (16 * kScanThreads);      // 16-byte loads per thread
+        constexpr int kPerLoad = 16 / kElem;                                 // values per load
+        const uint4 *r16 = reinterpret_cast<const uint4 *>(row + x0 * kElem);
+        uint4 h[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) h[i] = r16[tid + i * kScanThreads];
+        auto val = [&](int k) -> float {
+            const uint4 &q = h[k / kPerLoad];
+            const int e = k % kPerLoad, wi = e / (kPerLoad / 4);
+            const uint32_t w = wi == 0 ? q.x : wi == 1 ? q.y : wi == 2 ? q.z : q.w;
+            if constexpr (DT == TMV_F32) return __uint_as_float(w);
+            else return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+        };
+        float m = val(0);
+        int g = 0;
+        nan = m != m;
+#pragma unroll
+        for (int k = 1; k < kPer * kPerLoad; ++k) {
+            const float v = val(k);
+            nan = nan || v != v;
+            const bool c = v > m;
+            m = c ? v : m;
+            g = c ? k : g;
+        }
+        best = value_key(m, x0 + kPerLoad * (tid + (g / kPerLoad) * kScanThreads) + g % kPerLoad);
+    } else if constexpr (DT == TMV_F32) {
+        const float *r = reinterpret_cast<const float *>(row);
+        for (int x = x0 + tid; x < x1; x += kScanThreads) scan_one(r[x], x, best, nan);
+    } else {
+        const uint16_t *r = reinterpret_cast<const uint16_t *>(row);
+        for (int x = x0 + tid; x < x1; x += kScanThreads) scan_one(tmv::bf16_to_f32(r[x]), x, best, nan);
+    }
+    if (nan) best = kNanKey;
+    best = tmv::wave_max_u64(best);
+    if (lane == 0) red[wv] = best;
+    __syncthreads();
+    if (tid == 0) {
+        uint64_t k = red[0];
+        for (int w = 1; w < kScanThreads / kWave; ++w) k = red[w] > k ? red[w] : k;
+        keys[(static_cast<int64_t>(b) * R + u) * nchunk + chunk] = k;
+    }
+}
+
+// One workgroup per sequence, after the scan: the chunk keys of the sequence ([row][chunk],
+// contiguous) are read by all threads in coalesced batches, issued together with the
+// per-row reads of the path choice, and merged per row with LDS atomics; then the path is
+// chosen.  Keys of rows beyond n_nodes were not written in this call and are not read;
+// those of other dead rows may be stale and are never used.
+__global__ void __launch_bounds__(kScanThreads)
+greedy_select_kernel(int M_max, int D_max, int V, int nchunk, const int32_t *__restrict__ tokens,
+                     const int32_t *__restrict__ n_nodes, const int32_t *__restrict__ anc,
+                     const int32_t *__restrict__ depth, int32_t *__restrict__ status,
+                     int32_t *__restrict__ accept_len, int32_t *__restrict__ path,
+                     int32_t *__restrict__ next_token, const uint64_t *__restrict__ keys)
+{
+    __shared__ unsigned long long rowkey[129];
+    const int R = M_max + 1, b = blockIdx.x, tid = threadIdx.x;
+    const int n = R * nchunk;                          // < 2^27: R <= 129, nchunk < 2^19
+    const uint64_t *kb = keys + static_cast<int64_t>(b) * n;
+    if (tid < R) rowkey[tid] = 0;
+    const PathInputs in = load_path_inputs(b, M_max, D_max, tokens, n_nodes, anc, depth, status);
+    const int M = in.M;
+    __syncthreads();
+    // key k = row * nchunk + chunk; this thread visits k = tid, tid + 256, ... and carries
+    // (row, chunk) along instead of dividing
+    int row = tid / nchunk, c = tid - row * nchunk;
+    const int drow = kScanThreads / nchunk, dc = kScanThreads - drow * nchunk;
+    for (int k0 = 0; k0 < n; k0 += kScanThreads * kSelectBatch) {
+        uint64_t kv[kSelectBatch];
+        int rw[kSelectBatch];
+#pragma unroll
+        for (int j = 0; j < kSelectBatch; ++j) {
+            const int k = k0 + tid + j * kScanThreads;
+            rw[j] = row;
+            kv[j] = k < n && row <= M ? kb[k] : 0;
+            row += drow;
+            c += dc;
+            if (c >= nchunk) {
+                c -= nchunk;
+                ++row;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kSelectBatch; ++j)
+            if (kv[j] != 0) atomicMax(&rowkey[rw[j]], static_cast<unsigned long long>(kv[j]));
+    }
+    __syncthreads();
+    choose_path_from(in, b, M_max, D_max, V, rowkey[tid < R ? tid : 0], status, accept_len, path, next_token, anc,
+                     static_cast<int32_t *>(nullptr));
+}
+
+// The LM-head path's choice (one workgroup per sequence, ordered after the LM-head kernel
+// on the stream, which merged one key per row with atomics): each row's key is read once
+// and set back to zero for the next call.
+__global__ void __launch_bounds__(kScanThreads)
+lm_select_kernel(int M_max, int D_max, int V, const int32_t *__restrict__ tokens, const int32_t *__restrict__ n_nodes,
+                 const int32_t *__restrict__ anc, const int32_t *__restrict__ depth, int32_t *__restrict__ status,
+                 int32_t *__restrict__ accept_len, int32_t *__restrict__ path, int32_t *__restrict__ next_token,
+                 uint64_t *__restrict__ keys, int32_t *__restrict__ row_argmax)
+{
+    const int b = blockIdx.x, R = M_max + 1, tid = threadIdx.x;
+    const int64_t rb = static_cast<int64_t>(b) * R + (tid < R ? tid : R - 1);
+    const PathInputs in = load_path_inputs(b, M_max, D_max, tokens, n_nodes, anc, depth, status);
+    const uint64_t krow = keys[rb];
+    if (tid < R) keys[rb] = 0;
+    choose_path_from(in, b, M_max, D_max, V, krow, status, accept_len, path, next_token, anc, row_argmax);
 }
 
 // ============================================================== greedy on LM-head logits
@@ -1137,8 +1208,7 @@ extern "C" int tmv_tree_accept(int mode, int B, int M_max, int D_max, int V,
             hipLaunchKernelGGL(greedy_scan_kernel<TMV_BF16>, dim3(static_cast<unsigned>(blocks)), dim3(kScanThreads), 0, s,
                                M_max, V, nchunk, teacher, t_stride_b, t_stride_row, n_nodes, depth, status, keys);
         hipLaunchKernelGGL(greedy_select_kernel, dim3(B), dim3(kScanThreads), 0, s, M_max, D_max, V, nchunk, tokens,
-                           n_nodes, anc, depth, status, accept_len, path, next_token, keys, 0,
-                           static_cast<int32_t *>(nullptr));
+                           n_nodes, anc, depth, status, accept_len, path, next_token, keys);
         return tmv_host::launch_status(hipGetLastError());
     }
     if (row_dtype != TMV_F32 || !draft_q || q_stride_b < 0 || q_stride_row < 0) return TMV_ERR_ARG;
@@ -1203,7 +1273,7 @@ extern "C" int tmv_tree_accept_lm_head(int B, int M_max, int D_max, int K, int V
     default: return TMV_ERR_ARG;
     }
 #undef TMV_LAUNCH_LM
-    hipLaunchKernelGGL(greedy_select_kernel, dim3(B), dim3(kScanThreads), 0, s, M_max, D_max, V, 1, tokens, n_nodes,
-                       anc, depth, status, accept_len, path, next_token, keys, 1, row_argmax);
+    hipLaunchKernelGGL(lm_select_kernel, dim3(B), dim3(kScanThreads), 0, s, M_max, D_max, V, tokens, n_nodes, anc,
+                       depth, status, accept_len, path, next_token, keys, row_argmax);
     return tmv_host::launch_status(hipGetLastError());
 }

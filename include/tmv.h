@@ -287,14 +287,13 @@ int tmv_tree_verify_attention_paged_plan(int dtype, int B, int M_max, int D_max,
  *   next_token out int32 [B].  All 0 for a failed sequence.
  *   workspace: tmv_tree_accept_workspace() bytes, 16-byte aligned.
  *     SAMPLE: one synchronisation block per sequence.  K workgroups walk a sequence
- *     together, one per vocabulary slice (K = compute units / B, at most 64), and meet
- *     after every row pass.
- *     - Every completed call leaves the workspace zero; zero-fill it once before first use,
- *       and again after a GREEDY call has used it.
- *     - A wait for the other slices that exceeds 2 ms ends the walk with status
- *       TMV_ERR_DEVICE (never a hang).  Zero-fill the workspace again after that status.
- *     - All K workgroups of a sequence must be resident at once, which holds when no other
- *       kernel occupies the device's compute units.
+ *     together, one per vocabulary slice, and meet after every row pass; K = (the walk
+ *     kernel's resident workgroups per compute unit x compute units) / B, at most 64, so the
+ *     whole launch is resident on an otherwise idle device (the results do not depend on K).
+ *     - Every completed call leaves the workspace zero; zero-fill it once before first use.
+ *     - A workgroup that waits more than 2 ms for the other slices (kernels on other streams
+ *       can hold compute units) gives up: the sequence ends with status TMV_ERR_DEVICE and
+ *       zero outputs, every workgroup still exits, and the workspace is again left zero.
  */
 size_t tmv_tree_accept_workspace(int mode, int B, int M_max, int V);
 int tmv_tree_accept(int mode, int B, int M_max, int D_max, int V,
@@ -305,6 +304,22 @@ int tmv_tree_accept(int mode, int B, int M_max, int D_max, int V,
                     const int32_t *n_nodes, const int32_t *anc, const int32_t *depth,
                     int32_t *status, int32_t *accept_len, int32_t *path, int32_t *next_token,
                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * tmv_tree_accept_wait -- tmv_tree_accept with the sampling walk's wait bound given in
+ * microseconds (tmv_tree_accept uses 2000): how long a workgroup waits for the other slices
+ * of its sequence before the sequence ends with TMV_ERR_DEVICE.  For callers that share the
+ * device with long-running kernels on other streams (a larger bound), or that prefer to
+ * fail fast; 0 gives up at the first wait that is not already met.  GREEDY ignores it.
+ */
+int tmv_tree_accept_wait(int mode, int B, int M_max, int D_max, int V,
+                         const int32_t *tokens, int row_dtype, const void *teacher,
+                         int64_t t_stride_b, int64_t t_stride_row,
+                         const float *draft_q, int64_t q_stride_b, int64_t q_stride_row,
+                         uint64_t seed, uint64_t step,
+                         const int32_t *n_nodes, const int32_t *anc, const int32_t *depth,
+                         int32_t *status, int32_t *accept_len, int32_t *path, int32_t *next_token,
+                         void *workspace, size_t workspace_bytes, uint32_t wait_us, void *stream);
 
 /*
  * tmv_tree_accept_lm_head -- greedy acceptance straight from the teacher's LM head: the

@@ -174,6 +174,93 @@ def test_sampling_small(ref, V, overlap):
         assert np.any(A >= 2)
 
 
+def test_sampling_beside_a_busy_device(ref):
+    """Long fp32 GEMMs on a second stream hold compute units while the walk runs, so the
+    K workgroups of a sequence may not all be resident at once.  Every sequence then either
+    matches the oracle bit for bit or fails with TMV_ERR_DEVICE and zero outputs; every
+    kernel exits; the workspace is left zero, and the next call on it (not zero-filled
+    again) is bit-exact."""
+    _case("sampling: walk beside GEMMs on another stream")
+    import tree_masked_verification_amd as tmv
+    rng = np.random.default_rng(450)
+    B, M, V, D = 16, 12, 50000, 5
+    parents, n, tokens, p, q = ti.small_sampling_case(rng, B, M, V, D, overlap=0.95)
+    w = ti.Workload("sample", ti.F32, B, 0, 1, 64, M, D, 1, V, "sample", parents, n, np.zeros(B, np.int32), tokens,
+                    p=p, qd=q, seed=91, step=3)
+    ra, rd, rs = oracle_tables(ref, w)
+    want = ref.accept_sample(tokens, p, q, w.seed, w.step, n, ra, rd, rs)
+    dev = DeviceStep(w)
+    ws = torch.zeros(tmv.tree_accept_workspace(tmv.ACCEPT_SAMPLE, B, M, V), dtype=torch.uint8, device="cuda")
+    big = torch.randn((6144, 6144), device="cuda")
+    prod = torch.empty_like(big)
+    side = torch.cuda.Stream()
+    dev.build()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        for _ in range(4):
+            torch.mm(big, big, out=prod)
+    dev.accept(workspace=ws)
+    torch.cuda.synchronize()
+    got = [host_bits(t) for t in (dev.accept_len, dev.path, dev.next_token, dev.status)]
+    failed = 0
+    for b in range(B):
+        if got[3][b] == tmv.ERR_DEVICE:
+            failed += 1
+            assert got[0][b] == 0 and got[2][b] == 0 and not got[1][b].any(), b
+        else:
+            assert all(np.array_equal(g[b], e[b]) for g, e in zip(got, want)), b
+    print("    sequences that gave up waiting: %d of %d" % (failed, B), flush=True)
+    assert int(ws.count_nonzero()) == 0
+    dev.build()
+    dev.accept(workspace=ws)
+    torch.cuda.synchronize()
+    got = [host_bits(t) for t in (dev.accept_len, dev.path, dev.next_token, dev.status)]
+    assert all(np.array_equal(g, e) for g, e in zip(got, want))
+
+
+@pytest.mark.parametrize("wait_us", [0, 5])
+def test_sampling_gives_up_cleanly(ref, wait_us):
+    """The walk's wait bound forced from the host (tmv_tree_accept_wait) down to nothing or
+    a few microseconds: workgroups give up waiting for slices not yet resident.  Each
+    sequence then matches the oracle bit for bit or ends with TMV_ERR_DEVICE and zero
+    outputs, every kernel exits, the workspace is left zero, and a call with the default
+    bound on that same workspace is bit-exact."""
+    _case("sampling: wait bound %d us" % wait_us)
+    import tree_masked_verification_amd as tmv
+    rng = np.random.default_rng(460 + wait_us)
+    B, M, V, D = 24, 12, 60000, 5
+    parents, n, tokens, p, q = ti.small_sampling_case(rng, B, M, V, D, overlap=0.95)
+    w = ti.Workload("sample", ti.F32, B, 0, 1, 64, M, D, 1, V, "sample", parents, n, np.zeros(B, np.int32), tokens,
+                    p=p, qd=q, seed=92, step=4)
+    ra, rd, rs = oracle_tables(ref, w)
+    want = ref.accept_sample(tokens, p, q, w.seed, w.step, n, ra, rd, rs)
+    dev = DeviceStep(w)
+    ws = torch.zeros(tmv.tree_accept_workspace(tmv.ACCEPT_SAMPLE, B, M, V), dtype=torch.uint8, device="cuda")
+    failed = 0
+    for rep in range(3):
+        dev.build()
+        tmv.tree_accept(tmv.ACCEPT_SAMPLE, dev.tokens, dev.p, dev.n_nodes, dev.anc, dev.depth, dev.status,
+                        dev.accept_len, dev.path, dev.next_token, draft_q=dev.qd, seed=w.seed, step=w.step,
+                        workspace=ws, wait_us=wait_us)
+        torch.cuda.synchronize()
+        got = [host_bits(t) for t in (dev.accept_len, dev.path, dev.next_token, dev.status)]
+        for b in range(B):
+            if got[3][b] == tmv.ERR_DEVICE:
+                failed += 1
+                assert got[0][b] == 0 and got[2][b] == 0 and not got[1][b].any(), b
+            else:
+                assert all(np.array_equal(g[b], e[b]) for g, e in zip(got, want)), b
+        assert int(ws.count_nonzero()) == 0
+    print("    sequences that gave up waiting: %d of %d" % (failed, 3 * B), flush=True)
+    if wait_us == 0:
+        assert failed > 0
+    dev.build()
+    dev.accept(workspace=ws)
+    torch.cuda.synchronize()
+    got = [host_bits(t) for t in (dev.accept_len, dev.path, dev.next_token, dev.status)]
+    assert all(np.array_equal(g, e) for g, e in zip(got, want))
+
+
 def test_sampling_unnormalised_and_edge_rows(ref):
     """Rows that do not sum to 1 (the integer rule renormalises), rows with zeros,
     a p row equal to q (empty residual), exact 0/1 probabilities."""

@@ -54,6 +54,8 @@ _lib.tmv_tree_accept_workspace.argtypes = [_I, _I, _I, _I]
 _lib.tmv_tree_accept_workspace.restype = _SZ
 _lib.tmv_tree_accept.argtypes = [_I, _I, _I, _I, _I, _P, _I, _P, _I64, _I64, _P, _I64, _I64, _U64, _U64,
                                  _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+_lib.tmv_tree_accept_wait.argtypes = [_I, _I, _I, _I, _I, _P, _I, _P, _I64, _I64, _P, _I64, _I64, _U64, _U64,
+                                      _P, _P, _P, _P, _P, _P, _P, _P, _SZ, ctypes.c_uint32, _P]
 _lib.tmv_tree_accept_lm_head_workspace.argtypes = [_I, _I]
 _lib.tmv_tree_accept_lm_head_workspace.restype = _SZ
 _lib.tmv_tree_accept_lm_head.argtypes = [_I, _I, _I, _I, _I, _P, _P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P,
@@ -83,7 +85,8 @@ EXPORTED = ("tmv_status_string", "tmv_abi_version", "tmv_tree_build_ancestors",
             "tmv_kv_commit_path_paged", "tmv_tree_verify_attention_plan_workspace",
             "tmv_tree_verify_attention_plan", "tmv_tree_verify_attention_paged_plan_workspace",
             "tmv_tree_verify_attention_paged_plan", "tmv_tree_verify_attention_noalloc",
-            "tmv_tree_accept_lm_head_workspace", "tmv_tree_accept_lm_head", "tmv_kv_commit_path_paged_evict")
+            "tmv_tree_accept_lm_head_workspace", "tmv_tree_accept_lm_head", "tmv_kv_commit_path_paged_evict",
+            "tmv_tree_accept_wait")
 
 
 class TmvError(RuntimeError):
@@ -278,9 +281,10 @@ def tree_accept_workspace(mode, B, M_max, V) -> int:
 
 
 def tree_accept(mode, tokens, teacher, n_nodes, anc, depth, status, accept_len, path, next_token, draft_q=None,
-                seed=0, step=0, workspace=None, stream=None):
+                seed=0, step=0, workspace=None, stream=None, wait_us=None):
     """teacher [B][M_max+1][V]: logits (GREEDY, f32/bf16) or p (SAMPLE, f32); draft_q the
-    same shape (SAMPLE).  Outputs accept_len [B], path [B][D_max], next_token [B]."""
+    same shape (SAMPLE).  Outputs accept_len [B], path [B][D_max], next_token [B].
+    wait_us: the sampling walk's wait bound (tmv_tree_accept_wait); None = the default."""
     _i32(tokens, n_nodes, anc, depth, status, accept_len, path, next_token)
     B, R, V = teacher.shape
     _check_tree_tables(B, R - 1, anc, depth, "tree_accept")
@@ -299,12 +303,16 @@ def tree_accept(mode, tokens, teacher, n_nodes, anc, depth, status, accept_len, 
     if workspace is None:
         workspace = _temp_workspace(tree_accept_workspace(mode, B, R - 1, V), teacher.device, stream,
                                     zero=(mode == ACCEPT_SAMPLE))
-    _check(_lib.tmv_tree_accept(mode, B, R - 1, D_max, V, _ptr(tokens), _dtype_code(teacher), _ptr(teacher),
-                                teacher.stride(0), teacher.stride(1), _ptr(draft_q), qs[0], qs[1],
-                                ctypes.c_uint64(seed), ctypes.c_uint64(step), _ptr(n_nodes), _ptr(anc), _ptr(depth),
-                                _ptr(status), _ptr(accept_len), _ptr(path), _ptr(next_token), _ptr(workspace),
-                                workspace.numel() * workspace.element_size(), _stream(stream)),
-           "tree_accept")
+    args = (mode, B, R - 1, D_max, V, _ptr(tokens), _dtype_code(teacher), _ptr(teacher), teacher.stride(0),
+            teacher.stride(1), _ptr(draft_q), qs[0], qs[1], ctypes.c_uint64(seed), ctypes.c_uint64(step), _ptr(n_nodes),
+            _ptr(anc), _ptr(depth), _ptr(status), _ptr(accept_len), _ptr(path), _ptr(next_token), _ptr(workspace),
+            workspace.numel() * workspace.element_size())
+    if wait_us is None:
+        _check(_lib.tmv_tree_accept(*args, _stream(stream)), "tree_accept")
+    else:
+        if not 0 <= int(wait_us) < 1 << 32:
+            raise ValueError("wait_us out of range")
+        _check(_lib.tmv_tree_accept_wait(*args, int(wait_us), _stream(stream)), "tree_accept")
 
 
 def tree_accept_lm_head_workspace(B, M_max) -> int:

@@ -14,6 +14,8 @@
 //   point, so the result is bit-identical to any correct implementation.  K workgroups
 //   walk a sequence, one per vocabulary slice, holding their slices of the node's two rows
 //   in registers; every refusal is one exact sum over them, met at a bounded barrier.
+#include <mutex>
+
 #include "tmv_device.hpp"
 
 namespace {
@@ -526,7 +528,8 @@ constexpr int kMaxSlices = 64;                 // workgroups per sequence: one l
 constexpr int kMaxWords = 4 * ((kMaxNodes + 1 + 3) / 4);   // one per tried child, one draw
 constexpr int kSeg = 16;                       // segment entries a thread keeps in registers
 constexpr int kTailBatch = 4;                  // loads in flight per thread beyond them
-constexpr uint64_t kSyncSpinTicks = 200000;    // 2 ms at the 100 MHz s_memrealtime clock
+constexpr uint64_t kTicksPerUs = 100;          // s_memrealtime runs at 100 MHz
+constexpr uint32_t kDefaultWaitUs = 2000;       // tmv_tree_accept's wait bound
 constexpr int kFlagBad = 1;                    // an entry outside [0, 1] in a scanned row
 constexpr int kFlagTimeout = 2;                // a workgroup stopped waiting for the others
 constexpr int kTagShift = 48;                  // record words: 48-bit piece | phase << 48
@@ -549,7 +552,8 @@ __device__ __forceinline__ float row_load(__amdgpu_buffer_rsrc_t r, int x) {
 // everything is zero: the last workgroup to leave clears the records and the count.
 struct SeqSync {
     uint64_t leave;                          // workgroups done with this call
-    uint64_t pad[15];
+    uint64_t failed;                         // set by a workgroup that stopped waiting
+    uint64_t pad[14];
     uint64_t rec[2][kMaxSlices][4];          // [phase parity][slice]: sum bits 0-47, 48-95, 96-143; flags
 };
 
@@ -681,7 +685,8 @@ __device__ bool block_any(bool v, int *sh) {
 // which gathers the slices' sums, then runs post(view) -- the walk's scalar decisions are
 // taken there once, instead of in every wave -- before the block reads the results.
 template <class Post>
-__device__ SeqView seq_reduce(SeqSync *ss, int K, int k, int &phase, u128 local, int flags, SyncLds &L, Post post) {
+__device__ SeqView seq_reduce(SeqSync *ss, int K, int k, int &phase, u128 local, int flags, SyncLds &L,
+                             uint64_t wait_ticks, Post post) {
     const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
     const bool any_bad = __ballot(flags != 0) != 0;
     __syncthreads();                                  // the previous call's results are read
@@ -719,7 +724,7 @@ __device__ SeqView seq_reduce(SeqSync *ss, int K, int k, int &phase, u128 local,
                      (w3 >> kTagShift) == tag;
             }
             if (__ballot(!ok) == 0) break;
-            if (__builtin_amdgcn_s_memrealtime() - t0 > kSyncSpinTicks) { timed_out = 1; break; }
+            if (__builtin_amdgcn_s_memrealtime() - t0 > wait_ticks) { timed_out = 1; break; }
             __builtin_amdgcn_s_sleep(1);
         }
         // the slices' sums in scalar registers, slice by slice (K is at most 64)
@@ -761,9 +766,19 @@ __device__ SeqView seq_reduce(SeqSync *ss, int K, int k, int &phase, u128 local,
     return r;
 }
 
-// The workgroup is done with the call.  Its record stores are complete before it counts
-// itself out, so the last of the K can clear every record for the next call.
-__device__ void seq_leave(SeqSync *ss, int K) {
+// The workgroup is done with the call.  Its record and output stores (all written through
+// to memory) are complete before it counts itself out, so the last of the K sees every
+// other workgroup's effects: it clears every record for the next call, and when any
+// workgroup gave up waiting it writes the sequence's failed state last -- status
+// TMV_ERR_DEVICE and zero outputs, whatever a slice that did finish the walk wrote.
+__device__ __forceinline__ void store_out(int32_t *p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ void seq_leave(SeqSync *ss, int K, int b, int D_max, int32_t *__restrict__ status,
+                          int32_t *__restrict__ accept_len, int32_t *__restrict__ path,
+                          int32_t *__restrict__ next_token) {
+    __builtin_amdgcn_s_waitcnt(0);                    // every wave's stores are complete
     __syncthreads();
     if (threadIdx.x < kWave) {
         const int lane = threadIdx.x;
@@ -774,6 +789,16 @@ __device__ void seq_leave(SeqSync *ss, int K) {
         }
         l = __shfl(l, 0, kWave);
         if (l == static_cast<uint64_t>(K) - 1) {
+            const bool failed = __hip_atomic_load(&ss->failed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+            if (failed) {
+                for (int j = lane; j < D_max; j += kWave) store_out(path + static_cast<int64_t>(b) * D_max + j, 0);
+                if (lane == 0) {
+                    store_out(accept_len + b, 0);
+                    store_out(next_token + b, 0);
+                    store_out(status + b, TMV_ERR_DEVICE);
+                    __hip_atomic_store(&ss->failed, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
             for (int i = lane; i < 2 * K * 4; i += kWave) {
                 const int slot = i / (4 * K), j = i % (4 * K);
                 __hip_atomic_store(&ss->rec[slot][j / 4][j % 4], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -852,7 +877,7 @@ sample_walk_kernel(int M_max, int D_max, int V, int K,
                    const int32_t *__restrict__ n_nodes, const int32_t *__restrict__ anc,
                    const int32_t *__restrict__ depth, int32_t *__restrict__ status,
                    int32_t *__restrict__ accept_len, int32_t *__restrict__ path,
-                   int32_t *__restrict__ next_token, SeqSync *__restrict__ sync)
+                   int32_t *__restrict__ next_token, SeqSync *__restrict__ sync, uint64_t wait_ticks)
 {
     __shared__ SyncLds L;
     __shared__ int par[kMaxNodes + 1];         // parent of a live node, -1 otherwise
@@ -882,26 +907,30 @@ sample_walk_kernel(int M_max, int D_max, int V, int K,
     const uint64_t stream = (step << 32) | static_cast<uint32_t>(b);
 
     // outputs: slice 0 writes the path, the length and a data error; the slice holding the
-    // final draw writes the token
+    // final draw writes the token.  A workgroup that gave up waiting (TMV_ERR_DEVICE) only
+    // marks the sequence failed; the last workgroup to leave writes the failed state.  All
+    // output stores are written through, so that the last one to leave writes last.
     auto finish = [&](int code, int acc, int tk, bool mine) {
         __syncthreads();
-        if (code != TMV_OK) { acc = 0; tk = 0; }
-        if (k == 0)
-            for (int j = tid; j < D_max; j += kSampleThreads)
-                if (code != TMV_OK || j >= acc) pth[j] = 0;
-        if (tid == 0) {
-            if (code == TMV_ERR_DEVICE) {
-                status[b] = TMV_ERR_DEVICE;
-            } else if (k == 0) {
-                accept_len[b] = acc;
-                if (code != TMV_OK) {
-                    next_token[b] = 0;
-                    if (st_in == TMV_OK) status[b] = code;
+        if (code == TMV_ERR_DEVICE) {
+            if (tid == 0) __hip_atomic_store(&ss->failed, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            if (code != TMV_OK) { acc = 0; tk = 0; }
+            if (k == 0)
+                for (int j = tid; j < D_max; j += kSampleThreads)
+                    if (code != TMV_OK || j >= acc) store_out(pth + j, 0);
+            if (tid == 0) {
+                if (k == 0) {
+                    store_out(accept_len + b, acc);
+                    if (code != TMV_OK) {
+                        store_out(next_token + b, 0);
+                        if (st_in == TMV_OK) store_out(status + b, code);
+                    }
                 }
+                if (code == TMV_OK && mine) store_out(next_token + b, tk);
             }
-            if (code == TMV_OK && mine) next_token[b] = tk;
         }
-        seq_leave(ss, K);
+        seq_leave(ss, K, b, D_max, status, accept_len, path, next_token);
     };
     if (st != TMV_OK) { finish(st, 0, 0, false); return; }
 
@@ -1019,7 +1048,7 @@ sample_walk_kernel(int M_max, int D_max, int V, int K,
         };
         // (slice sums of WP and WQ stay below 2^55, so they share one 128-bit sum)
         const SeqView va = seq_reduce(ss, K, k, phase, static_cast<u128>(sp) | (static_cast<u128>(sq) << 64),
-                                      bd ? kFlagBad : 0, L, [&](const SeqView &w) {
+                                      bd ? kFlagBad : 0, L, wait_ticks, [&](const SeqView &w) {
             const uint64_t sp_w = static_cast<uint64_t>(w.total), sq_w = static_cast<uint64_t>(w.total >> 64);
             if (!(w.flags & (kFlagBad | kFlagTimeout)) && sp_w != 0 && (!have_q || sq_w != 0)) {
                 const uint64_t sq1 = have_q ? sq_w : 1;
@@ -1039,7 +1068,7 @@ sample_walk_kernel(int M_max, int D_max, int V, int K,
         bool moved = false;
         for (int ci = 0; ci < nk; ++ci) {
             if (__builtin_amdgcn_readfirstlane(L.dec_accept)) {
-                if (k == 0 && tid == 0) pth[acc] = kids[ci];
+                if (k == 0 && tid == 0) store_out(pth + acc, kids[ci]);
                 ++acc;
                 u = kids[ci];
                 n += ci + 1;
@@ -1053,7 +1082,7 @@ sample_walk_kernel(int M_max, int D_max, int V, int K,
             uint64_t SQp = SQ;
             asm volatile("" : "+s"(SQp));
             const u128 s = thread_sum(rp, rq, x_lo, x_hi, ncol, prs, qrs, SQp, Mn);
-            const SeqView vr = seq_reduce(ss, K, k, phase, s, 0, L, [&](const SeqView &w) {
+            const SeqView vr = seq_reduce(ss, K, k, phase, s, 0, L, wait_ticks, [&](const SeqView &w) {
                 if (!(w.flags & kFlagTimeout)) {
                     if (w.total != 0) decide(ci + 1, Mn, w.total, SQ);
                     else decide(ci + 1, Mc, T, SQ);      // empty residual: the state is kept
@@ -1152,13 +1181,28 @@ static size_t sample_ws_bytes(int B) {
     return static_cast<size_t>(B) * sizeof(SeqSync) + 256;
 }
 
-// workgroups per sequence: at most one workgroup per compute unit in all (so every workgroup
-// a barrier waits for is resident), at most kMaxSlices, slices of >= 2048 entries
+// workgroups per sequence: all B * K of the launch resident at once on an otherwise idle
+// device (the walk kernel's occupancy per compute unit times the compute units), at most
+// kMaxSlices, slices of >= 2048 entries.  The walk's results do not depend on K.
+static int walk_capacity() {
+    static std::mutex mu;
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cached[dev] == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&sample_walk_kernel),
+                                                         kSampleThreads, 0) != hipSuccess || per_cu < 1)
+            per_cu = 1;
+        cached[dev] = cus * per_cu;
+    }
+    return cached[dev];
+}
+
 static int sample_slices(int B, int V) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 1;
-    int K = cus / (B > 0 ? B : 1);
+    int K = walk_capacity() / (B > 0 ? B : 1);
     if (K > kMaxSlices) K = kMaxSlices;
     if (K > V / 2048) K = V / 2048;
     return K < 1 ? 1 : K;
@@ -1174,14 +1218,14 @@ extern "C" size_t tmv_tree_accept_workspace(int mode, int B, int M_max, int V)
     return sample_ws_bytes(B);
 }
 
-extern "C" int tmv_tree_accept(int mode, int B, int M_max, int D_max, int V,
-                               const int32_t *tokens, int row_dtype, const void *teacher,
-                               int64_t t_stride_b, int64_t t_stride_row,
-                               const float *draft_q, int64_t q_stride_b, int64_t q_stride_row,
-                               uint64_t seed, uint64_t step,
-                               const int32_t *n_nodes, const int32_t *anc, const int32_t *depth,
-                               int32_t *status, int32_t *accept_len, int32_t *path, int32_t *next_token,
-                               void *workspace, size_t workspace_bytes, void *stream)
+extern "C" int tmv_tree_accept_wait(int mode, int B, int M_max, int D_max, int V,
+                                    const int32_t *tokens, int row_dtype, const void *teacher,
+                                    int64_t t_stride_b, int64_t t_stride_row,
+                                    const float *draft_q, int64_t q_stride_b, int64_t q_stride_row,
+                                    uint64_t seed, uint64_t step,
+                                    const int32_t *n_nodes, const int32_t *anc, const int32_t *depth,
+                                    int32_t *status, int32_t *accept_len, int32_t *path, int32_t *next_token,
+                                    void *workspace, size_t workspace_bytes, uint32_t wait_us, void *stream)
 {
     if (mode != TMV_ACCEPT_GREEDY && mode != TMV_ACCEPT_SAMPLE) return TMV_ERR_ARG;
     if (B < 0 || M_max < 0 || M_max > 128 || D_max < 0 || D_max > 128 || V < 1) return TMV_ERR_ARG;
@@ -1217,8 +1261,22 @@ extern "C" int tmv_tree_accept(int mode, int B, int M_max, int D_max, int V,
     hipLaunchKernelGGL(sample_walk_kernel, dim3(static_cast<unsigned>(B) * K), dim3(kSampleThreads), 0, s, M_max,
                        D_max, V, K, tokens, static_cast<const float *>(teacher), t_stride_b, t_stride_row, draft_q,
                        q_stride_b, q_stride_row, seed, step, n_nodes, anc, depth, status, accept_len, path,
-                       next_token, reinterpret_cast<SeqSync *>(ws));
+                       next_token, reinterpret_cast<SeqSync *>(ws), static_cast<uint64_t>(wait_us) * kTicksPerUs);
     return tmv_host::launch_status(hipGetLastError());
+}
+
+extern "C" int tmv_tree_accept(int mode, int B, int M_max, int D_max, int V,
+                               const int32_t *tokens, int row_dtype, const void *teacher,
+                               int64_t t_stride_b, int64_t t_stride_row,
+                               const float *draft_q, int64_t q_stride_b, int64_t q_stride_row,
+                               uint64_t seed, uint64_t step,
+                               const int32_t *n_nodes, const int32_t *anc, const int32_t *depth,
+                               int32_t *status, int32_t *accept_len, int32_t *path, int32_t *next_token,
+                               void *workspace, size_t workspace_bytes, void *stream)
+{
+    return tmv_tree_accept_wait(mode, B, M_max, D_max, V, tokens, row_dtype, teacher, t_stride_b, t_stride_row, draft_q,
+                                q_stride_b, q_stride_row, seed, step, n_nodes, anc, depth, status, accept_len, path,
+                                next_token, workspace, workspace_bytes, kDefaultWaitUs, stream);
 }
 
 extern "C" size_t tmv_tree_accept_lm_head_workspace(int B, int M_max)

@@ -132,7 +132,7 @@ int tmv_tree_build_ancestors(int B, int M_max, int D_max, int parent_format,
  *        Hq/Hkv <= 16, 1 <= L_cap, q and the caches 16-byte aligned with strides that
  *        are multiples of 16 bytes (bf16: out too; TMV_ERR_ARG otherwise).
  *   workspace: tmv_tree_verify_attention_workspace() bytes, 16-byte aligned.  It opens
- *        with a fixed 1 KiB block of arrival counters (one per split row block; the last
+ *        with a fixed 16 KiB block of arrival counters (one per split row block; the last
  *        split of a block to finish merges it) followed by the split-KV partials, which
  *        every call rewrites.  The counter block must be zero before the first call and
  *        every completed call leaves it zero, so zero-fill a new workspace once; it then

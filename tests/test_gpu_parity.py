@@ -142,6 +142,32 @@ def test_attention_bf16_small_ragged(ref, variant):
 
 
 @pytest.mark.parametrize("d", [128, 64])
+def test_attention_bf16_late_outlier_scores(ref, d):
+    """Keys planted late in the prefix and in the tree so that some rows' scores there exceed
+    everything in the first chunks by far more than 2^32 in base 2: the kernels' first pass
+    detects it and redoes the split against the exact row maxima.  Rows that never see a
+    planted key are unaffected; the planted ones must come out as the planted tokens' V."""
+    _case("attention: bf16 late outlier scores d=%d" % d)
+    B, Hq, Hkv, M_max = 2, 8, 2, 20
+    prefixes, n_nodes = [600, 130], [20, 12]
+    w = small_attention_workload(230 + d, B, Hq, Hkv, d, M_max, prefixes, n_nodes)
+    qf = ti.bf16_to_f32(w.q)
+    kf = ti.bf16_to_f32(w.k)
+    g = Hq // Hkv
+    rng = np.random.default_rng(231)
+    for b in range(B):
+        for kvh in range(Hkv):
+            # a prefix slot in the last chunks gets 40 x a query row of node 1 (head kvh*g):
+            # that row's score there is ~ 40 |q|^2 / sqrt(d) above its others
+            t = prefixes[b] - 1 - int(rng.integers(0, 20))
+            kf[b, kvh, t] = 40.0 * qf[b, 0, kvh * g]
+            # and the tree slot of the last node, for the rows that see it
+            kf[b, kvh, prefixes[b] + n_nodes[b] - 1] = 30.0 * qf[b, n_nodes[b] - 1, kvh * g + 1]
+    w.k = ti.bf16_bits(kf)
+    _attention_parity(ref, w, 2e-2, 1e-2)
+
+
+@pytest.mark.parametrize("d", [128, 64])
 def test_attention_bf16_deep_paths(ref, d):
     # ancestor paths longer than the entries a row fetches up front (the kernels' deep-row
     # branch): chains and deep random trees, with and without a prefix

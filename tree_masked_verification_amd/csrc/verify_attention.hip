@@ -169,7 +169,7 @@ struct AttnPlan {
 };
 
 // split-KV row blocks (pairs x row blocks) are limited to the counter block's size
-constexpr int kMaxSplitUnits = 256;
+constexpr int kMaxSplitUnits = 4096;
 constexpr size_t kCounterBytes = kMaxSplitUnits * sizeof(int32_t);
 
 // An XCD's L2 (4 MB): a (sequence, kv head) pair's K and V rows up to this size stay in
@@ -1292,7 +1292,14 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     }
 
     f32x4_t oacc[2][NT];
-    float mref[2], mtrue[2], lrow[2];
+    // row sums of p come out of the PV product itself: an extra dim tile whose A operand is
+    // 1 at tile dim 0 and 0 elsewhere accumulates, at dim 0, the sum of the bf16 p of each
+    // row (exactly the weights the rows of O receive); lane (c16, G = 0) holds row c16's sum
+    f32x4_t lacc[2];
+    const uint32_t one2 = c16 == 0 ? 0x3F803F80u : 0u;                 // two bf16 ones
+    const bf16x8_t ones_a = __builtin_bit_cast(bf16x8_t, make_uint4(one2, one2, one2, one2));
+    float mref[2], mlane[2], lrow[2];
+    float mrs[2];                      // mref * cs (0 while the reference is unset)
     const float cs = qk_scale_log2;
     auto xor16_max = [](float x) {
         const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -1304,10 +1311,56 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     };
     // first pass: each row's reference is the first finite chunk maximum (O and l are
     // still exactly zero then, so adopting it rescales nothing); later maxima are only
-    // tracked.  p = 2^(s*cs - ref) stays finite unless a score exceeds the reference by
-    // more than kOverflow in base 2, in which case the whole split is recomputed against
+    // tracked, per lane (a row's maximum is the maximum over its four lanes, taken only
+    // when needed).  p = 2^(s*cs - ref) stays finite unless a score exceeds the reference
+    // by more than kOverflow in base 2, in which case the whole split is recomputed against
     // the exact maximum -- the accumulators never need rescaling inside the loop.
     bool first_pass = true, overflow = false;
+    // softmax weights of a chunk's scores (cm: this lane's maxima of them) and the PV product
+    auto lane_max = [](const f32x4_t (&s)[2]) {
+        return fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    };
+    auto finish_chunk = [&](f32x4_t (&s)[2][2], const u32x2_t (&vt)[16], const float (&cm)[2]) {
+        if (first_pass) {
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) mlane[rt] = fmaxf(mlane[rt], cm[rt]);
+            // a row without a reference takes this chunk's row maximum (a wave-uniform test,
+            // false after the first chunk with finite scores)
+            if (__builtin_amdgcn_ballot_w64(mref[0] == -INFINITY || mref[1] == -INFINITY) != 0) {
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    const float rm = xor32_max(xor16_max(cm[rt]));
+                    if (mref[rt] == -INFINITY) mref[rt] = rm;
+                    mrs[rt] = mref[rt] == -INFINITY ? 0.f : mref[rt] * cs;
+                }
+            }
+            // (a row whose reference is still unset has no finite score in this lane)
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) overflow |= __builtin_fmaf(cm[rt], cs, -mrs[rt]) > kOverflow;
+        }
+        bf16x8_t pb[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const float mr = mrs[rt];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    pb[rt][tt * 4 + i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[rt][tt][i], cs, -mr)));
+        }
+        // O^T += V^T P^T over dim tiles of 16: A operand of tile nt = (tokens pi(8G + j)) at
+        // dim nt*16 + c16; the accumulator lane holds dims nt*16 + 4G + i of row c16
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(vt[2 * nt].x, vt[2 * nt].y, vt[2 * nt + 1].x, vt[2 * nt + 1].y));
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+                oacc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rt], oacc[rt][nt], 0, 0, 0);
+        }
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) lacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_a, pb[rt], lacc[rt], 0, 0, 0);
+    };
     auto compute_chunk = [&](uint32_t sp, int c) {
         const int t0 = c * kChunk;
         // S^T tiles: [token][row]; lane holds row c16 of tile rt, tokens t0 + tt*16 + G*4 + i
@@ -1337,6 +1390,9 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[tt][ks], qf[rt][ks], acc, 0, 0, 0);
                 s[rt][tt] = acc;
             }
+        // this lane's score maxima (a chunk reaching the tree slots takes them again over
+        // its visible scores below)
+        float cm[2] = {lane_max(s[0]), lane_max(s[1])};
         // V^T fragments go out while the score MFMAs run
         u32x2_t vt[16];
         lds_read_vt(vt, sp + zv[0], sp + zv[1]);
@@ -1358,51 +1414,21 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         s[rt][tt][i] = ((win >> (tt * 16 + i)) & 1u) ? s[rt][tt][i] : -INFINITY;
+                cm[rt] = lane_max(s[rt]);
             }
         }
-        bf16x8_t pb[2];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            if (first_pass) {
-                float cm = fmaxf(fmaxf(fmaxf(s[rt][0][0], s[rt][0][1]), fmaxf(s[rt][0][2], s[rt][0][3])),
-                                 fmaxf(fmaxf(s[rt][1][0], s[rt][1][1]), fmaxf(s[rt][1][2], s[rt][1][3])));
-                cm = xor32_max(xor16_max(cm));
-                mtrue[rt] = fmaxf(mtrue[rt], cm);
-                if (mref[rt] == -INFINITY) mref[rt] = cm;
-                overflow |= (cm - mref[rt]) * cs > kOverflow;
-            }
-            const float mr = mref[rt] == -INFINITY ? 0.f : mref[rt] * cs;
-            float lsum = 0.f;
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rt][tt][i], cs, -mr));
-                    pb[rt][tt * 4 + i] = static_cast<__bf16>(pe);
-                    lsum += pe;
-                }
-            lrow[rt] += lsum;
-        }
-        // O^T += V^T P^T over dim tiles of 16: A operand of tile nt = (tokens pi(8G + j)) at
-        // dim nt*16 + c16; the accumulator lane holds dims nt*16 + 4G + i of row c16
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(vt[2 * nt].x, vt[2 * nt].y, vt[2 * nt + 1].x, vt[2 * nt + 1].y));
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-                oacc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rt], oacc[rt][nt], 0, 0, 0);
-        }
+        finish_chunk(s, vt, cm);
     };
 
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) { mref[rt] = -INFINITY; mtrue[rt] = -INFINITY; }
+    for (int rt = 0; rt < 2; ++rt) { mref[rt] = -INFINITY; mlane[rt] = -INFINITY; mrs[rt] = 0.f; }
     // (the pass, round and slot loops stay rolled: one copy of the chunk code keeps the
     // kernel small enough for the instruction cache)
 #pragma unroll 1
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-            lrow[rt] = 0.f;
+            lacc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) oacc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
@@ -1451,12 +1477,16 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         first_pass = false;
         overflow = false;
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) mref[rt] = mtrue[rt];
+        for (int rt = 0; rt < 2; ++rt) {
+            mref[rt] = xor32_max(xor16_max(mlane[rt]));
+            mrs[rt] = mref[rt] == -INFINITY ? 0.f : mref[rt] * cs;
+        }
     }
     __syncthreads();
     float mrow[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
+        lrow[rt] = lacc[rt][0];       // the ones tile: lanes with G > 0 hold exact zeros
         // row sums: each of the four lanes of a row holds a partial sum
         auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(lrow[rt]), __float_as_uint(lrow[rt]), false, false);
         const float l16 = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);

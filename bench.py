@@ -245,6 +245,7 @@ def ingest_counters(workload, fetch_csv, write_csv, command):
     under this workload, with each stage's source digest."""
     import csv
     import collections
+    import re
 
     def per_kernel(path):
         agg = collections.defaultdict(list)
@@ -267,7 +268,8 @@ def ingest_counters(workload, fetch_csv, write_csv, command):
         e = stages.setdefault(st, {"fetch_kib": 0.0, "write_kib": 0.0, "kernels": []})
         e["fetch_kib"] += fe[k]
         e["write_kib"] += wr.get(k, 0.0)
-        e["kernels"].append(k.split("(")[0].replace("void ", ""))
+        m = re.search(r"(\w+_kernel(<[^>]*>)?)", k)
+        e["kernels"].append(m.group(1) if m else k[:80])
     for st, e in stages.items():
         e["hbm_bytes_per_launch"] = (e["fetch_kib"] * fscale + e["write_kib"] * wscale) * 1024
         e["source_sha256"] = stage_source_digest(st)

@@ -29,7 +29,8 @@
 //     by the head's other row groups from there.
 // bf16, head dim 64 (tree_attn_bf16_stream_kernel): 4 waves streaming their chunks straight
 //   into registers, split partials merged by tree_attn_merge_kernel.
-// fp32 (tree_attn_f32_kernel): one wave per (node, query head), plain FMA.
+// fp32 (tree_attn_f32_kernel): one workgroup of 4 waves per (node, query head), the row's
+//   64-token chunks dealt to the waves, plain FMA, waves merged in LDS.
 #include <cstdlib>
 #include <cstdio>
 #include <mutex>
@@ -1662,13 +1663,15 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
 }
 
 // --------------------------------------------------------------------------- fp32 kernel
-// One wave per (sequence, node, query head).  Tokens are visited in chunks of 64, one per
-// lane for the scores: the lane's K row arrives as D/4 independent 16-byte loads against
-// the query held in registers, and the next chunk's rows are requested before this
-// chunk's V rows are consumed.  For P V the visible rows of the chunk are taken in
-// batches of 64 / (D/64), their addresses made wave-uniform with readlane, so every V load
-// is one coalesced row and a batch's loads are all in flight together; lanes hold dims
-// lane and lane + 64.
+// One workgroup of 4 waves per (sequence, node, query head); wave w takes the 64-token
+// chunks w, w + 4, w + 8, ... of the row's visible tokens (prefix, then its path), so a
+// short row's chunks are all in flight at once instead of one after another.  Within a
+// chunk each lane scores one token: its K row arrives as D/4 independent 16-byte loads
+// against the query held in registers.  The chunk's V rows go out together with the K
+// rows, each one coalesced row at a wave-uniform address (readlane of the token's slot),
+// lanes holding dims lane and lane + 64; prefix tokens need no ancestor-table read, so a
+// prefix chunk's loads leave as soon as the prefix length is known.  Each wave keeps a
+// running (max, sum, weighted V) and the four are combined in LDS at the end.
 template <int D>
 __global__ void __launch_bounds__(256)
 tree_attn_f32_kernel(int B, int M_max, int D_max, int Hq, int Hkv,
@@ -1681,11 +1684,13 @@ tree_attn_f32_kernel(int B, int M_max, int D_max, int Hq, int Hkv,
                      float *__restrict__ out, int64_t os0, int64_t os1, int64_t os2)
 {
     constexpr int DV = D / 64;                 // output dims per lane
-    constexpr int kBatch = 64 / DV;            // V rows in flight per batch
+    constexpr int kBatch = 64 / DV;            // V rows per batch (a chunk is 64 tokens)
+    constexpr int kFw = 4;                     // waves per row
+    __shared__ float red_ml[kFw][2];
+    __shared__ float red_acc[kFw][D];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + wv;
-    if (item >= static_cast<int64_t>(B) * M_max * Hq) return;
+    const int64_t item = blockIdx.x;
     const int h = static_cast<int>(item % Hq);
     const int j = static_cast<int>((item / Hq) % M_max) + 1;
     const int b = static_cast<int>(item / (static_cast<int64_t>(Hq) * M_max));
@@ -1697,12 +1702,13 @@ tree_attn_f32_kernel(int B, int M_max, int D_max, int Hq, int Hkv,
     int st = status[b];
     if (st == TMV_OK && (M < 0 || M > M_max || P < 0 || static_cast<int64_t>(P) + M > L_cap)) {
         st = TMV_ERR_INPUT;
-        if (lane == 0 && j == 1 && h == 0) status[b] = TMV_ERR_INPUT;
+        if (threadIdx.x == 0 && j == 1 && h == 0) status[b] = TMV_ERR_INPUT;
     }
     const int dep = (st == TMV_OK && j <= M) ? depth[static_cast<int64_t>(b) * R + j] : 0;
     if (dep < 1) {
+        if (wv == 0)
 #pragma unroll
-        for (int e = 0; e < DV; ++e) o[lane + 64 * e] = 0.f;
+            for (int e = 0; e < DV; ++e) o[lane + 64 * e] = 0.f;
         return;
     }
     const float *qp = q + b * qs0 + static_cast<int64_t>(j - 1) * qs1 + h * qs2;
@@ -1715,25 +1721,39 @@ tree_attn_f32_kernel(int B, int M_max, int D_max, int Hq, int Hkv,
     const int32_t *arow = anc + (static_cast<int64_t>(b) * R + j) * W;
     const int total = P + dep;            // visible tokens: prefix then the path
     const int ks2_32 = static_cast<int>(ks2);
-    // slot of the lane's token in chunk t0 (-1 past the visible tokens) and its K row
+    // slot of the lane's token in chunk t0 (-1 past the visible tokens)
     auto slot_of = [&](int t0) {
         const int idx = t0 + lane;
         return idx < P ? idx : (idx < total ? P + arow[idx - P] - 1 : -1);
     };
-    auto load_k = [&](int slot, float4 (&kv)[D / 4]) {
-        const float4 *kr = reinterpret_cast<const float4 *>(kb + static_cast<int64_t>(slot < 0 ? 0 : slot) * ks2);
-#pragma unroll
-        for (int e = 0; e < D / 4; ++e) kv[e] = kr[e];
-    };
     float m = -INFINITY, l = 0.f, acc[DV];
 #pragma unroll
     for (int e = 0; e < DV; ++e) acc[e] = 0.f;
-    int slot = slot_of(0);
-    float4 kv[D / 4];
-    load_k(slot, kv);
-    for (int t0 = 0; t0 < total; t0 += 64) {
+    for (int t0 = wv * 64; t0 < total; t0 += kFw * 64) {
+        const int cur = slot_of(t0);
+        const int n = min(64, total - t0);
+        // this chunk's K row (one token per lane) and its first batch of V rows, all issued
+        // before any is used
+        float4 kv[D / 4];
+        {
+            const float4 *kr = reinterpret_cast<const float4 *>(kb + static_cast<int64_t>(cur < 0 ? 0 : cur) * ks2);
+#pragma unroll
+            for (int e = 0; e < D / 4; ++e) kv[e] = kr[e];
+        }
+        float vv[kBatch][DV];
+        auto load_v = [&](int u0) {
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int t = u0 + u < n ? u0 + u : n - 1;         // padding lanes repeat a row, weight 0
+                const int sl = __builtin_amdgcn_readlane(cur, t);
+                const float *vr = vb + static_cast<uint32_t>(sl * ks2_32);     // slot * stride < 2^31 (host-checked)
+#pragma unroll
+                for (int e = 0; e < DV; ++e) vv[u][e] = vr[lane + 64 * e];
+            }
+        };
+        load_v(0);
         float s = -INFINITY;
-        if (slot >= 0) {
+        if (cur >= 0) {
             float dot = 0.f;
 #pragma unroll
             for (int e = 0; e < D / 4; ++e) {
@@ -1744,40 +1764,49 @@ tree_attn_f32_kernel(int B, int M_max, int D_max, int Hq, int Hkv,
             }
             s = dot * scale;
         }
-        // the next chunk's K rows go out before this chunk's V rows are waited for
-        const int cur = slot;
-        if (t0 + 64 < total) {
-            slot = slot_of(t0 + 64);
-            load_k(slot, kv);
-        }
         const float mnew = fmaxf(m, tmv::wave_max(s));
         const float alpha = expf(m - mnew);
         const float p = cur >= 0 ? expf(s - mnew) : 0.f;
         l = l * alpha + tmv::wave_sum(p);
 #pragma unroll
         for (int e = 0; e < DV; ++e) acc[e] *= alpha;
-        const int n = min(64, total - t0);
         for (int u0 = 0; u0 < n; u0 += kBatch) {
-            float vv[kBatch][DV], pv[kBatch];
+            if (u0 > 0) load_v(u0);
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
-                const int t = u0 + u < n ? u0 + u : n - 1;         // padding lanes repeat a row, weight 0
-                const int sl = __builtin_amdgcn_readlane(cur, t);
-                pv[u] = u0 + u < n ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), t)) : 0.f;
-                const float *vr = vb + static_cast<uint32_t>(sl * ks2_32);     // slot * stride < 2^31 (host-checked)
+                const float pu = u0 + u < n ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), u0 + u)) : 0.f;
 #pragma unroll
-                for (int e = 0; e < DV; ++e) vv[u][e] = vr[lane + 64 * e];
+                for (int e = 0; e < DV; ++e) acc[e] = fmaf(pu, vv[u][e], acc[e]);
             }
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u)
-#pragma unroll
-                for (int e = 0; e < DV; ++e) acc[e] = fmaf(pv[u], vv[u][e], acc[e]);
         }
         m = mnew;
     }
-    const float inv = 1.f / l;
+    // the four waves' (max, sum, weighted V) merged in LDS; a wave without a chunk holds
+    // (-inf, 0, 0) and contributes nothing
+    if (lane == 0) {
+        red_ml[wv][0] = m;
+        red_ml[wv][1] = l;
+    }
 #pragma unroll
-    for (int e = 0; e < DV; ++e) o[lane + 64 * e] = acc[e] * inv;
+    for (int e = 0; e < DV; ++e) red_acc[wv][lane + 64 * e] = acc[e];
+    __syncthreads();
+    if (wv != 0) return;
+    float mt = red_ml[0][0];
+#pragma unroll
+    for (int w = 1; w < kFw; ++w) mt = fmaxf(mt, red_ml[w][0]);
+    float lt = 0.f, at[DV];
+#pragma unroll
+    for (int e = 0; e < DV; ++e) at[e] = 0.f;
+#pragma unroll
+    for (int w = 0; w < kFw; ++w) {
+        const float c = red_ml[w][0] == -INFINITY ? 0.f : expf(red_ml[w][0] - mt);
+        lt += c * red_ml[w][1];
+#pragma unroll
+        for (int e = 0; e < DV; ++e) at[e] += c * red_acc[w][lane + 64 * e];
+    }
+    const float inv = 1.f / lt;
+#pragma unroll
+    for (int e = 0; e < DV; ++e) o[lane + 64 * e] = at[e] * inv;
 }
 
 template <int D, int WR>
@@ -1888,8 +1917,7 @@ int attention(int dtype, int B, int M_max, int D_max, int Hq, int Hkv, int d, co
         if (q_stride[i] < 0 || kv_stride[i] < 0 || o_stride[i] < 0) return TMV_ERR_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == TMV_F32) {
-        const int64_t items = static_cast<int64_t>(B) * M_max * Hq;
-        const int64_t blocks = (items + 3) / 4;
+        const int64_t blocks = static_cast<int64_t>(B) * M_max * Hq;       // one workgroup per row
         if (blocks > 0x7fffffff) return TMV_ERR_ARG;
         // 16-byte loads of q and K rows need 16-byte aligned rows; slot offsets within a
         // (sequence, head) are 32-bit

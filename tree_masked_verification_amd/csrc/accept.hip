@@ -351,7 +351,8 @@ __global__ void __launch_bounds__(kLmThreads)
 lm_head_argmax_kernel(int B, int M_max, int V, const uint16_t *__restrict__ hidden, int64_t hsb, int64_t hsr,
                       uint32_t h_bytes, const uint16_t *__restrict__ w, int64_t wsr, uint32_t w_bytes,
                       const int32_t *__restrict__ n_nodes, const int32_t *__restrict__ depth,
-                      const int32_t *__restrict__ status, uint64_t *__restrict__ row_keys, int ntiles)
+                      const int32_t *__restrict__ status, uint64_t *__restrict__ row_keys, int ntiles, int ntp,
+                      int nrb)
 {
     static_assert(NKS % (kLmKB / 32) == 0, "whole staged blocks");
     constexpr int kStepsPerBlock = kLmKB / 32;
@@ -363,7 +364,14 @@ lm_head_argmax_kernel(int B, int M_max, int V, const uint16_t *__restrict__ hidd
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int c16 = lane & 15, G = lane >> 4;
-    const int rb0 = blockIdx.y * kLmRows;
+    // workgroup id = XCD slot + 8 (row block + nrb * s), covering tile pair s * 8 + slot: the
+    // row blocks of one tile pair share an id mod 8, hence one XCD, and are dispatched one
+    // after another, so they stream the same weight rows at about the same time -- the
+    // weights come from HBM once and the other row blocks read them from that XCD's L2
+    const int xslot = blockIdx.x & 7, rest = blockIdx.x >> 3;
+    const int tpi = (rest / nrb) * 8 + xslot;
+    if (tpi >= ntp) return;
+    const int rb0 = (rest % nrb) * kLmRows;
 
     // a row block without a live row does nothing
     if (threadIdx.x == 0) s_any = 0;
@@ -396,7 +404,7 @@ lm_head_argmax_kernel(int B, int M_max, int V, const uint16_t *__restrict__ hidd
     uint32_t woff[kLmTpw][2];
 #pragma unroll
     for (int tp = 0; tp < kLmTpw; ++tp) {
-        const int t = blockIdx.x + tp * gridDim.x;
+        const int t = tpi + tp * ntp;
         tile_ok[tp] = t < ntiles;
         vbase[tp] = t * kLmTile + wave * kLmVocabPerWave;
 #pragma unroll
@@ -1315,13 +1323,16 @@ extern "C" int tmv_tree_accept_lm_head(int B, int M_max, int D_max, int K, int V
     const int nrows = B * (M_max + 1);
     const int nrb = (nrows + kLmRows - 1) / kLmRows;
     const int ntiles = (V + kLmTile - 1) / kLmTile;
-    // every workgroup takes kLmTpw tiles (ceil(tiles / kLmTpw) workgroups per row block)
-    const int gx = (ntiles + kLmTpw - 1) / kLmTpw;
+    // every workgroup takes kLmTpw tiles of one row block: ntp tile pairs x nrb row blocks,
+    // laid out in groups of 8 tile pairs (see the kernel)
+    const int ntp = (ntiles + kLmTpw - 1) / kLmTpw;
+    const int64_t groups = 8ll * nrb * ((ntp + 7) / 8);
+    if (groups > 0x7fffffff) return TMV_ERR_ARG;
 #define TMV_LAUNCH_LM(NKS)                                                                                     \
-    hipLaunchKernelGGL(lm_head_argmax_kernel<NKS>, dim3(gx, nrb), dim3(kLmThreads), 0, s, B, M_max, V,             \
-                       static_cast<const uint16_t *>(hidden), h_stride_b, h_stride_row, static_cast<uint32_t>(h_bytes), \
-                       static_cast<const uint16_t *>(lm_head), w_stride_row, static_cast<uint32_t>(w_bytes), n_nodes,  \
-                       depth, status, keys, ntiles)
+    hipLaunchKernelGGL(lm_head_argmax_kernel<NKS>, dim3(static_cast<unsigned>(groups)), dim3(kLmThreads), 0, s, B,  \
+                       M_max, V, static_cast<const uint16_t *>(hidden), h_stride_b, h_stride_row,                  \
+                       static_cast<uint32_t>(h_bytes), static_cast<const uint16_t *>(lm_head), w_stride_row,       \
+                       static_cast<uint32_t>(w_bytes), n_nodes, depth, status, keys, ntiles, ntp, nrb)
     switch (K) {
     case 512: TMV_LAUNCH_LM(16); break;
     case 1024: TMV_LAUNCH_LM(32); break;

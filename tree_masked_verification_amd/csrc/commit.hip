@@ -49,30 +49,34 @@ commit_kernel(int n_layers, int B, int Hkv, int row_bytes, int L_cap, int D_max,
     __shared__ uint4 snap[kCommitLds / 16];
     __shared__ int src_row[128], path_sh[128];
     __shared__ int64_t src_off[128], dst_off[128];   // byte offsets of the moving rows' slots
-    __shared__ int nmove, fits;
+    __shared__ int wcount[kCommitThreads / 64];
 
     const int layer = blockIdx.x / B, b = blockIdx.x % B;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int P = prefix_len[b], M = n_nodes[b], A = accept_len[b];
     const int st = status[b];
     const int32_t *pth = path + static_cast<int64_t>(b) * D_max;
     if (tid < D_max) path_sh[tid] = pth[tid];            // the whole path in one round trip
     __syncthreads();
 
-    if (tid == 0) {
-        int ok = st == TMV_OK && P >= 0 && static_cast<int64_t>(P) + M <= L_cap && A >= 0 && A <= D_max && A <= M;
-        for (int j = 0; ok && j < A; ++j) {
-            const int node = path_sh[j];
-            if (node < 1 || node > M) ok = 0;
-        }
-        fits = ok;
-        // rows that actually move: destination P + j, source P + path[j] - 1
-        int k = 0;
-        if (ok)
-            for (int j = 0; j < A; ++j)
-                if (path_sh[j] - 1 != j) src_row[k++] = j;
-        nmove = k;
+    // which path entries move (destination P + j, source P + path[j] - 1, j < A), compacted
+    // in path order by a block scan: a ballot per wave, then the waves' counts
+    const bool base_ok = st == TMV_OK && P >= 0 && static_cast<int64_t>(P) + M <= L_cap && A >= 0 && A <= D_max &&
+                         A <= M;
+    const int node = base_ok && tid < A ? path_sh[tid] : 1;
+    const bool bad = base_ok && tid < A && (node < 1 || node > M);
+    const bool mv = base_ok && tid < A && !bad && node - 1 != tid;
+    const uint64_t bal = __ballot(mv);
+    if (lane == 0) wcount[wv] = __popcll(bal);
+    const bool fits = base_ok && __syncthreads_or(bad ? 1 : 0) == 0;
+    int before = __popcll(bal & ((1ull << lane) - 1)), nmove = 0;
+#pragma unroll
+    for (int w = 0; w < kCommitThreads / 64; ++w) {
+        before += w < wv ? wcount[w] : 0;
+        nmove += wcount[w];
     }
+    if (mv) src_row[before] = tid;
+    if (!fits) nmove = 0;
     __syncthreads();
     // byte offsets of the moving rows' slots, one thread per row (paged: through the
     // block table; every page involved must be valid)

@@ -11,16 +11,18 @@
 //   * rows of one KV head = (node, query head in the GQA group), node-major; a workgroup
 //     of 8 waves (two per SIMD) owns a row group of 64, 128 or 256 rows and one token
 //     split of the (sequence, KV head).  K/V arrive in 32-token chunks through a 128 KiB
-//     LDS ring filled by buffer-to-LDS DMA (two halves of four chunks, one half in flight
-//     while the other is computed); every wave along the rows reads each staged chunk, so
-//     a chunk load serves the whole row group.
+//     LDS ring filled by buffer-to-LDS DMA: rounds of 2 (or 4) chunks, up to 3 (or 1)
+//     rounds in flight while one is computed, one barrier per round (ring_schedule.hpp);
+//     every wave along the rows reads each staged chunk, so a chunk load serves the
+//     whole row group.
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 leaves each lane holding the scores of ONE
 //     query row for 8 tokens, exactly its slice of the B operand of O^T = V^T P^T, so
 //     probabilities never move between lanes; V^T operands come from LDS through the
 //     transposing ds_read_b64_tr_b16.
-//   * softmax in base 2 (log2 e folded into the scale) against a fixed per-row reference
-//     (the first finite chunk maximum), with an exact-maximum recompute of the split in
-//     the rare case a score outgrows it by 2^32; row max and sums via permlane swaps.
+//   * softmax in base 2: the query tile carries scale * log2 e and the score MFMAs start
+//     from minus a fixed per-row reference (the first finite chunk maximum), so they yield
+//     the exponents directly; the split is recomputed against the exact maxima in the rare
+//     case a score outgrows the reference by 2^32; row sums come out of the PV product.
 //   * token groups of waves share a row group and are combined in LDS at the end; token
 //     splits publish (m, l, bf16 rows) with agent-coherent stores and the last split of a
 //     row block to arrive merges the block in split order (deterministic).
@@ -36,6 +38,7 @@
 #include <mutex>
 
 #include "tmv_device.hpp"
+#include "ring_schedule.hpp"
 
 namespace {
 
@@ -782,7 +785,6 @@ struct RingShape {
     static constexpr int kMatBytes = kChunk * kRowBytes;    // K (or V) part of one chunk
     static constexpr int kSlotBytes = 2 * kMatBytes;        // K then V
     static constexpr int kSlots = kRingBytes / kSlotBytes;  // 8 (d128)
-    static constexpr int kRound = kSlots / 2;               // chunks per half
     static constexpr int kDmaPerChunk = kSlotBytes / 1024;  // 1 KiB per DMA instruction
     static constexpr int kDmaPerWave = kDmaPerChunk / kRingWaves;
     static_assert(kDmaPerWave * kRingWaves == kDmaPerChunk, "chunk DMA must split evenly over the waves");
@@ -918,10 +920,15 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     constexpr int kThreads = kRingWaves * kWave;
     constexpr int kDW = RS::kDmaPerWave;
 
-    // the ring: two halves of kRound slots (all its reads are inline assembly, so the
-    // compiler never waits for copies in flight before touching it)
-    constexpr int kHalfBytes = RS::kRound * RS::kSlotBytes;
-    __shared__ __attribute__((aligned(16))) char ring[2 * kHalfBytes];
+    // the ring: kNR groups of kR chunk slots, one round of copies each (all its reads are
+    // inline assembly, so the compiler never waits for copies in flight before touching
+    // it).  A round holds a chunk for every token group (rounds of 2 chunks when the waves
+    // form at most 2 token groups, so that up to 3 rounds are in flight while one is computed).
+    constexpr int kR = TW > 2 ? TW : 2;
+    constexpr int kNR = RS::kSlots / kR;
+    static_assert(kNR * kR == RS::kSlots && kNR >= 2 && kNR <= 4, "ring groups");
+    constexpr int kGroupBytes = kR * RS::kSlotBytes;
+    __shared__ __attribute__((aligned(16))) char ring[kNR * kGroupBytes];
     __shared__ float s_ml[kRingWaves * kRowsPerWave * 2];
     // 64-row groups (contiguous caches): the four token groups of a row group share one
     // copy of its query fragments, each loading one k-step (16 KB for the workgroup)
@@ -962,7 +969,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     // visible length T.  Rows in [T, L_cap) of a speculatively copied chunk are never
     // visible (their mask bits are clear); V rows among them are zeroed in LDS before use
     // (0 * garbage could be NaN), and chunks entirely beyond T are never computed.
-    // Local chunk k sits in slot k % kSlots (half (k / kRound) % 2).
+    // Local chunk k sits in slot k % kSlots (group (k / kR) % kNR).
     const int ncap = (L_cap + kChunk - 1) / kChunk;
     const int nk_cap = ncap > split ? (ncap - split + splits - 1) / splits : 0;
     int t_lim = L_cap, nk_lim = nk_cap;       // copy bounds: capacity until T is known
@@ -1004,7 +1011,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     }
     // rows of local chunk k to copy (records stop at t_lim, so loads past it write zeros and
     // touch no memory; chunks past nk_lim load nothing)
-    auto chunk_recs = [&](int k) {
+    auto chunk_recs = [&](int k) __attribute__((always_inline)) {
         const int t0 = (split + k * splits) * kChunk;
         const int recs = (k < nk_lim) ? t_lim - t0 : 0;
         return recs < 0 ? 0 : (recs > kChunk ? kChunk : recs);
@@ -1012,7 +1019,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     // paged: the staged table entry of local chunk k's first (which = 0) or second page,
     // -1 when the chunk copies no rows there (indices clamped into the staged entries: a
     // chunk with rows has them there)
-    auto page_of = [&](int k, int which) {
+    auto page_of = [&](int k, int which) __attribute__((always_inline)) {
         const int t0 = (split + k * splits) * kChunk;
         const int recs = chunk_recs(k);
         const int rows = which == 0 ? (two_pages ? (recs < 16 ? recs : 16) : recs) : (two_pages ? recs - 16 : 0);
@@ -1022,7 +1029,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     };
     // issue this wave's share of local chunk k into the slot at `slot` (paged: pa / pb are
     // its page entries, wave-uniform)
-    auto issue_chunk = [&](int k, char *slot_p, int pa, int pb) {
+    auto issue_chunk = [&](int k, char *slot_p, int pa, int pb) __attribute__((always_inline)) {
         const int t0 = (split + k * splits) * kChunk;
         int recs = (k < nk_lim) ? t_lim - t0 : 0;
         recs = recs < 0 ? 0 : (recs > kChunk ? kChunk : recs);
@@ -1057,33 +1064,39 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     };
     // paged: page entries of the next round to issue, read from LDS a round ahead so the
     // read's latency hides behind that round's wait and compute
-    int pf_a[RS::kRound], pf_b[RS::kRound];
-    auto prefetch_pages = [&](int r) {
+    int pf_a[kR], pf_b[kR];
+    auto prefetch_pages = [&](int r) __attribute__((always_inline)) {
         if constexpr (PAGED) {
 #pragma unroll
-            for (int j = 0; j < RS::kRound; ++j) {
-                pf_a[j] = page_of(r * RS::kRound + j, 0);
-                pf_b[j] = page_of(r * RS::kRound + j, 1);
+            for (int j = 0; j < kR; ++j) {
+                pf_a[j] = page_of(r * kR + j, 0);
+                pf_b[j] = page_of(r * kR + j, 1);
             }
         }
     };
-    // round r fills half r % 2 of the ring with local chunks r*kRound .. +kRound (paged:
-    // from the prefetched entries when `prefetched`).  Every wave issues exactly kRound *
-    // kDW copies per round, empty ones included, so the count of copies issued after a
-    // round -- what the waits below rely on -- is the same on every path.
-    auto issue_round = [&](int r, char *half, bool prefetched = false) {
+    // round r fills group r % kNR of the ring with local chunks r*kR .. +kR (paged: from
+    // the prefetched entries when `prefetched`).  Every wave issues exactly kR * kDW copies
+    // per round, empty ones included, so the count of copies issued after a round -- what
+    // the waits below rely on -- is the same on every path.
+    auto issue_round = [&](int r, bool prefetched = false) __attribute__((always_inline)) {
+        char *grp = ring + (r % kNR) * kGroupBytes;
         if constexpr (PAGED) {
 #pragma unroll
-            for (int j = 0; j < RS::kRound; ++j) {
-                const int k = r * RS::kRound + j;
+            for (int j = 0; j < kR; ++j) {
+                const int k = r * kR + j;
                 const int pa = __builtin_amdgcn_readfirstlane(prefetched ? pf_a[j] : page_of(k, 0));
                 const int pb = __builtin_amdgcn_readfirstlane(prefetched ? pf_b[j] : page_of(k, 1));
-                issue_chunk(k, half + j * RS::kSlotBytes, pa, pb);
+                issue_chunk(k, grp + j * RS::kSlotBytes, pa, pb);
             }
         } else {
 #pragma unroll
-            for (int j = 0; j < RS::kRound; ++j) issue_chunk(r * RS::kRound + j, half + j * RS::kSlotBytes, -1, -1);
+            for (int j = 0; j < kR; ++j) issue_chunk(r * kR + j, grp + j * RS::kSlotBytes, -1, -1);
         }
+    };
+    // the first kNR rounds, before the chunk loop (every slot of the ring)
+    auto issue_prologue = [&](int from) __attribute__((always_inline)) {
+#pragma unroll 1
+        for (int r = from; r < kNR; ++r) issue_round(r);
     };
     // paged caches: this thread's block-table entries are loaded first, together with the
     // prologue's loads below, and staged in LDS before the first copies (L_cap = entries x page)
@@ -1099,7 +1112,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         }
     } else {
         // the first round goes out before anything else is loaded or waited for
-        issue_round(0, ring);
+        issue_round(0);
     }
 
     // ---- the prologue's loads, between the first and the second round of copies (vector
@@ -1131,7 +1144,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
             ancq[rt][k] = arow[kk < W ? kk : W - 1];
         }
     }
-    if constexpr (!PAGED) issue_round(1, ring + kHalfBytes);
+    if constexpr (!PAGED) issue_prologue(1);
     if constexpr (PAGED) {
         // stage the entries (invalid ones as -1; each wave records the first invalid one),
         // then issue the first two rounds from them
@@ -1153,8 +1166,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         }
         if (lane == 0) pg_bad[wave] = bad_min;
         __syncthreads();
-        issue_round(0, ring);
-        issue_round(1, ring + kHalfBytes);
+        issue_prologue(0);
     }
 
     if (st == TMV_OK && (M < 0 || M > M_max || P < 0 || static_cast<int64_t>(P) + M > L_cap)) {
@@ -1195,14 +1207,14 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     const int T = P + M;                                  // tokens visible to someone
     const int nchunks = (T + kChunk - 1) / kChunk;
     const int nk = __builtin_amdgcn_readfirstlane(nchunks > split ? (nchunks - split + splits - 1) / splits : 0);
-    const int nrounds = (nk + RS::kRound - 1) / RS::kRound;
+    const int nrounds = (nk + kR - 1) / kR;
     t_lim = T;
     nk_lim = nk;
     // the chunk holding T when T is not a chunk boundary: its rows >= T may hold anything
-    // if it was copied before T was known (first two rounds of the first pass)
+    // if it was copied before T was known (the first kNR rounds of the first pass)
     const int cb = T / kChunk;
     const int kb_loc = (T % kChunk != 0 && cb >= split && (cb - split) % splits == 0) ? (cb - split) / splits : -1;
-    const int kb_round = kb_loc >= 0 && kb_loc < 2 * RS::kRound ? kb_loc / RS::kRound : -1;
+    const int kb_round = kb_loc >= 0 && kb_loc < RS::kSlots ? kb_loc / kR : -1;
 
     const bool wave_live = row0 < Rh;
 
@@ -1252,6 +1264,14 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
             mw[rt][w] = x32[0] | x32[1];
         }
 
+    // the query fragments carry the score scale (scale * log2 e, rounded to bf16 once), so
+    // the score MFMAs yield base-2 exponents directly (with a shared query tile each wave
+    // scales the k-step it loaded)
+    auto scale_q = [&](bf16x8_t x) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = static_cast<__bf16>(static_cast<float>(x[e]) * qk_scale_log2);
+        return x;
+    };
     if constexpr (kShareQ) {
         // exchange the query k-steps: write this wave's, barrier, read all (LDS operations
         // in inline assembly: a compiler-written one would first wait for every copy in flight)
@@ -1260,7 +1280,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                if (ks == tw) lds_write16(qb + (((rw * 2 + rt) * KS + ks) * kWave + lane) * 16, __builtin_bit_cast(u32x4_t, qf[rt][ks]));
+                if (ks == tw) lds_write16(qb + (((rw * 2 + rt) * KS + ks) * kWave + lane) * 16, __builtin_bit_cast(u32x4_t, scale_q(qf[rt][ks])));
         __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
         __builtin_amdgcn_s_barrier();
         uint32_t qa[2 * KS];
@@ -1276,6 +1296,12 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
             for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = __builtin_bit_cast(bf16x8_t, qv[rt * KS + ks]);
     }
 
+    if constexpr (!kShareQ) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = scale_q(qf[rt][ks]);
+    }
     // LDS read offsets of the MFMA operands inside a slot (constant per lane).  K
     // fragment (tt, ks): row tt*16 + c16, logical piece ks*4 + G.  V^T: lane reads row
     // h*16 + 4G + c16/4 at dims 4*(c16%4) of each 16-dim tile (base zv[h], see lds_read_vt).
@@ -1300,56 +1326,66 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     const uint32_t one2 = c16 == 0 ? 0x3F803F80u : 0u;                 // two bf16 ones
     const bf16x8_t ones_a = __builtin_bit_cast(bf16x8_t, make_uint4(one2, one2, one2, one2));
     float mref[2], mlane[2], lrow[2];
-    float mrs[2];                      // mref * cs (0 while the reference is unset)
-    const float cs = qk_scale_log2;
-    auto xor16_max = [](float x) {
+    // minit[rt]: the score MFMAs' initial accumulator, minus the row's reference (0 while it
+    // is unset), so that they yield each score's exponent relative to the reference
+    f32x4_t minit[2];
+    // maxima of scores in IEEE maximum form (a NaN score propagates; -0 and +0 need no
+    // care here): unlike fmaxf it needs no quieting of MFMA results first
+    auto vmax = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
+    auto xor16_max = [&](float x) {
         const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-        return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
     };
-    auto xor32_max = [](float x) {
+    auto xor32_max = [&](float x) {
         const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-        return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
     };
     // first pass: each row's reference is the first finite chunk maximum (O and l are
     // still exactly zero then, so adopting it rescales nothing); later maxima are only
-    // tracked, per lane (a row's maximum is the maximum over its four lanes, taken only
-    // when needed).  p = 2^(s*cs - ref) stays finite unless a score exceeds the reference
-    // by more than kOverflow in base 2, in which case the whole split is recomputed against
-    // the exact maximum -- the accumulators never need rescaling inside the loop.
-    bool first_pass = true, overflow = false;
+    // tracked, per lane, relative to the reference (a row's maximum is the maximum over its
+    // four lanes, taken only when needed).  p = 2^(score exponent - ref) stays finite
+    // unless an exponent exceeds the reference by more than kOverflow, in which case the
+    // whole split is recomputed against the exact maximum -- the accumulators never need
+    // rescaling inside the loop.
+    bool first_pass = true;
+    // every row of the wave has its reference (wave-uniform; first pass only)
+    bool ref_ready = false;
     // softmax weights of a chunk's scores (cm: this lane's maxima of them) and the PV product
-    auto lane_max = [](const f32x4_t (&s)[2]) {
-        return fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    auto lane_max = [&](const f32x4_t (&s)[2]) {
+        return vmax(vmax(vmax(s[0][0], s[0][1]), vmax(s[0][2], s[0][3])),
+                    vmax(vmax(s[1][0], s[1][1]), vmax(s[1][2], s[1][3])));
     };
-    auto finish_chunk = [&](f32x4_t (&s)[2][2], const u32x2_t (&vt)[16], const float (&cm)[2]) {
-        if (first_pass) {
+    auto finish_chunk = [&](f32x4_t (&s)[2][2], const u32x2_t (&vt)[16], float (&cm)[2]) {
+        if (first_pass && !ref_ready) {
+            // a row without a reference takes this chunk's row maximum (scores of such a row
+            // are absolute; they become relative here)
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) mlane[rt] = fmaxf(mlane[rt], cm[rt]);
-            // a row without a reference takes this chunk's row maximum (a wave-uniform test,
-            // false after the first chunk with finite scores)
-            if (__builtin_amdgcn_ballot_w64(mref[0] == -INFINITY || mref[1] == -INFINITY) != 0) {
+            for (int rt = 0; rt < 2; ++rt) {
+                if (__builtin_amdgcn_ballot_w64(mref[rt] == -INFINITY) == 0) continue;
+                const float rm = xor32_max(xor16_max(cm[rt]));
+                if (mref[rt] == -INFINITY && rm != -INFINITY) {
+                    mref[rt] = rm;
+                    cm[rt] -= rm;
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
-                    const float rm = xor32_max(xor16_max(cm[rt]));
-                    if (mref[rt] == -INFINITY) mref[rt] = rm;
-                    mrs[rt] = mref[rt] == -INFINITY ? 0.f : mref[rt] * cs;
+                    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) s[rt][tt][i] -= rm;
+                    minit[rt] = f32x4_t{-rm, -rm, -rm, -rm};
                 }
             }
-            // (a row whose reference is still unset has no finite score in this lane)
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) overflow |= __builtin_fmaf(cm[rt], cs, -mrs[rt]) > kOverflow;
+            ref_ready = __builtin_amdgcn_ballot_w64(mref[0] == -INFINITY || mref[1] == -INFINITY) == 0;
         }
+        // each lane's largest exponent relative to its row's reference (a row whose reference
+        // is still unset has no finite score in this lane)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) mlane[rt] = vmax(mlane[rt], cm[rt]);
         bf16x8_t pb[2];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            const float mr = mrs[rt];
+        for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    pb[rt][tt * 4 + i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[rt][tt][i], cs, -mr)));
-        }
+                for (int i = 0; i < 4; ++i) pb[rt][tt * 4 + i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(s[rt][tt][i]));
         // O^T += V^T P^T over dim tiles of 16: A operand of tile nt = (tokens pi(8G + j)) at
         // dim nt*16 + c16; the accumulator lane holds dims nt*16 + 4G + i of row c16
 #pragma unroll
@@ -1385,7 +1421,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                f32x4_t acc = minit[rt];
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[tt][ks], qf[rt][ks], acc, 0, 0, 0);
@@ -1422,7 +1458,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     };
 
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) { mref[rt] = -INFINITY; mlane[rt] = -INFINITY; mrs[rt] = 0.f; }
+    for (int rt = 0; rt < 2; ++rt) { mref[rt] = -INFINITY; mlane[rt] = -INFINITY; minit[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f}; }
     // (the pass, round and slot loops stay rolled: one copy of the chunk code keeps the
     // kernel small enough for the instruction cache)
 #pragma unroll 1
@@ -1433,54 +1469,59 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) oacc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-        if (pass > 0) {
-            issue_round(0, ring);
-            issue_round(1, ring + kHalfBytes);
-        }
-        // Round r (ring half r % 2): wait until this wave's copies of round r have landed
-        // (round r + 1 may still be in flight: vector-memory operations complete in issue
-        // order and every wave issued exactly kRound * kDW copies for round r + 1 after
-        // round r, plus only operations that are needed here anyway), barrier so every
-        // wave's share is visible, compute, barrier so no wave still reads the half, then
-        // refill it with round r + 2.  The barriers carry no memory fence on purpose: a
-        // fence would wait for all copies in flight.
+        if (pass > 0) issue_prologue(0);
+        // Round r (ring group r % kNR): wait until this wave's copies of round r have landed
+        // (later rounds may still be in flight: vector-memory operations complete in issue
+        // order and every wave issues exactly kR * kDW copies per round), barrier -- every
+        // wave's share of round r is then visible and every wave has finished reading round
+        // r - 1 -- then refill round r - 1's group with the next round and compute round r.
+        // (tmv_ring defines and checks the schedule.)  The barriers carry no memory fence on
+        // purpose: a fence would wait for all copies in flight.
 #pragma unroll 1
         for (int r = 0; r < nrounds; ++r) {
-            char *half = ring + (r & 1) * kHalfBytes;
-            if (r + 2 < nrounds) prefetch_pages(r + 2);
-            if (r + 1 < nrounds) __builtin_amdgcn_s_waitcnt(kVmcntRound<RS::kRound * kDW>());
-            else __builtin_amdgcn_s_waitcnt(kVmcntZero);
+            char *grp = ring + (r % kNR) * kGroupBytes;
+            switch (tmv_ring::inflight(r, kNR, nrounds)) {
+            case 0: __builtin_amdgcn_s_waitcnt(kVmcntZero); break;
+            case 1: __builtin_amdgcn_s_waitcnt(kVmcntRound<kR * kDW>()); break;
+            case 2: __builtin_amdgcn_s_waitcnt(kVmcntRound<2 * kR * kDW>()); break;
+            default: __builtin_amdgcn_s_waitcnt(kVmcntRound<3 * kR * kDW>()); break;
+            }
+            __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
             __builtin_amdgcn_s_barrier();
             if (pass == 0 && r == kb_round) {
                 // the chunk holding T was copied before T was known: zero its V rows >= T
                 const int r0 = T - (split + kb_loc * splits) * kChunk;
-                const uint32_t vb = lds_addr(half) + (kb_loc % RS::kRound) * RS::kSlotBytes + RS::kMatBytes + r0 * RS::kRowBytes;
+                const uint32_t vb = lds_addr(grp) + (kb_loc % kR) * RS::kSlotBytes + RS::kMatBytes + r0 * RS::kRowBytes;
                 for (int i = threadIdx.x; i < (kChunk - r0) * PP; i += kThreads) lds_zero16(vb + i * 16);
                 __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
                 __builtin_amdgcn_s_barrier();
             }
+            const int x = tmv_ring::issue_at(r, kNR, nrounds);
+            if (x >= 0) issue_round(x, true);
+            // (paged: the next issue's table entries, read from LDS a round ahead)
+            const int xn = tmv_ring::issue_at(r + 1, kNR, nrounds);
+            if (xn >= 0) prefetch_pages(xn);
             if (wave_live) {
 #pragma unroll 1
-                for (int j = tw; j < RS::kRound; j += TW) {
-                    const int k = r * RS::kRound + j;
-                    if (k < nk) compute_chunk(lds_addr(half) + j * RS::kSlotBytes, split + k * splits);
+                for (int j = tw; j < kR; j += TW) {
+                    const int k = r * kR + j;
+                    if (k < nk) compute_chunk(lds_addr(grp) + j * RS::kSlotBytes, split + k * splits);
                 }
             }
-            __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
-            __builtin_amdgcn_s_barrier();
-            if (r + 2 < nrounds) issue_round(r + 2, half, true);
         }
         __builtin_amdgcn_s_waitcnt(kVmcntZero);   // nothing may land in LDS after this
         // the decision is the workgroup's: every wave must take the same number of passes,
         // since the passes contain barriers
+        const bool overflow = first_pass && (mlane[0] > kOverflow || mlane[1] > kOverflow);
         if (!__syncthreads_or(overflow ? 1 : 0)) break;
         // rare: some score outgrew its reference; redo the split against the exact maxima
         first_pass = false;
-        overflow = false;
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-            mref[rt] = xor32_max(xor16_max(mlane[rt]));
-            mrs[rt] = mref[rt] == -INFINITY ? 0.f : mref[rt] * cs;
+            const float mx = xor32_max(xor16_max(mlane[rt]));
+            if (mref[rt] != -INFINITY) mref[rt] += mx;
+            minit[rt] = mref[rt] == -INFINITY ? f32x4_t{0.f, 0.f, 0.f, 0.f}
+                                              : f32x4_t{-mref[rt], -mref[rt], -mref[rt], -mref[rt]};
         }
     }
     __syncthreads();
@@ -1494,7 +1535,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(l16), __float_as_uint(l16), false, false);
         lrow[rt] = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
         // from here on the running maxima are in base-2 units, as the merge steps expect
-        mrow[rt] = mref[rt] == -INFINITY ? -INFINITY : mref[rt] * cs;
+        mrow[rt] = mref[rt];
     }
 
     // ---- split-KV completion: the last split of a row block to arrive merges the block.

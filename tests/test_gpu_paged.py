@@ -11,7 +11,7 @@ import torch
 import tmv_inputs as ti
 from tests.harness import DeviceStep, attention_error, dev_tensor, host_bits, oracle_attention, oracle_tables
 from tests.test_gpu_commit import _path_of
-from tests.test_gpu_parity import small_attention_workload
+from tests.test_gpu_parity import adaptive_workload, small_attention_workload
 from tests.test_oracle_build import random_labelled_tree
 
 pytestmark = pytest.mark.gpu
@@ -249,3 +249,16 @@ def test_paged_attention_deep_trees(ref):
     dev, out = _paged_attention(w, 32, np.random.default_rng(296))
     _check_against_oracle(ref, w, dev, out)
     assert int(dev.tables()[1].max()) > 16
+
+
+@pytest.mark.parametrize("page_size", [16, 128])
+def test_paged_attention_adaptive_splits(ref, page_size):
+    """The ragged batch of the adaptive plan (per-sequence splits) through the block table:
+    against the oracle and bit-identical to the contiguous kernel."""
+    _case("paged attention: ragged batch with per-sequence splits, page %d" % page_size)
+    w = adaptive_workload(300 + page_size)
+    L = -(-w.L_cap // page_size) * page_size
+    wp = _padded(w, L)
+    dev, out = _paged_attention(wp, page_size, np.random.default_rng(310 + page_size))
+    _check_against_oracle(ref, wp, dev, out)
+    assert np.array_equal(out, _contiguous_bits(wp))

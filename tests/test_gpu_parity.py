@@ -269,6 +269,34 @@ def test_attention_after_kernels_of_odd_grid_sizes(ref):
         assert np.array_equal(host_bits(dev.out), first), n
 
 
+# a ragged batch shaped for the adaptive plan (16 sequences, 8 KV heads, two 256-row groups
+# per head at M_max 96 fill one workgroup per CU): the sequences with the most chunks have
+# few nodes, so the row groups they leave free go to second splits; node counts 0 and 1, an
+# empty prefix and a sequence failed by a cycle (status set by the build) ride along
+ADAPTIVE_PREFIX = [200, 100, 300, 50, 0, 150, 250, 100, 1400, 1300, 1200, 1100, 1000, 0, 900, 800]
+ADAPTIVE_NODES = [96, 90, 80, 70, 65, 96, 66, 75, 40, 30, 20, 10, 1, 0, 64, 50]
+
+
+def adaptive_workload(seed, q_scale=1.0):
+    w = small_attention_workload(seed, 16, 32, 8, 128, 96, ADAPTIVE_PREFIX, ADAPTIVE_NODES, q_scale=q_scale)
+    w.parents[6, 3], w.parents[6, 4] = 4, 3       # sequence 6 fails the build (a cycle)
+    return w
+
+
+@pytest.mark.parametrize("q_scale", [1.0, 6.0])
+def test_attention_adaptive_splits_ragged_batch(ref, q_scale):
+    """Every row of a ragged batch under the default (adaptive) plan: split and unsplit
+    sequences, row groups past a sequence's last node, a failed and an empty sequence."""
+    _case("attention: ragged batch with per-sequence splits, q x%g" % q_scale)
+    w = adaptive_workload(290, q_scale)
+    dev = _attention_parity(ref, w, 2e-2, 1e-2)
+    first = host_bits(dev.out).copy()
+    for _ in range(2):
+        dev.out.fill_(float("nan"))
+        dev.attention()
+        assert np.array_equal(host_bits(dev.out), first)
+
+
 @pytest.mark.parametrize("plan", [(64, 1), (64, 3), (64, 8), (128, 1), (128, 4), (128, 16), (256, 1), (256, 6),
                                   (32, 1), (128, 5)])
 def test_attention_launch_plans(ref, plan):

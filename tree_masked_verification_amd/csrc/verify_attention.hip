@@ -58,7 +58,6 @@ constexpr int kVmcntRound() {
     return (N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14);
 }
 constexpr int kVmcntZero = kVmcntRound<0>();
-// s_getreg operand for bits 3:0 of HW_REG_XCC_ID (register 20): the XCD running the wave
 // buffer cache policy sc1: agent-scope coherent access (the form of a relaxed agent-scope
 // atomic load or store): stores write through to memory, loads are not served stale lines
 constexpr int kCoherent = 16;
@@ -170,7 +169,14 @@ struct AttnPlan {
     int pairs;     // B * Hkv
     int per_pair;  // workgroups per pair = nb * splits
     int slots;     // workgroups per XCD (ceil(pairs / 8) * per_pair)
+    int adapt;     // ring kernel, ragged batches: one round of this many workgroups (one per CU),
+                   // each taking a work item with split counts chosen per sequence on the device
+                   // (up to `splits`); 0: off
 };
+
+// split bound of adaptive splitting, and the batch sizes it is used for
+constexpr int kAdaptSplits = 2;
+constexpr int kAdaptMaxB = 64;
 
 // split-KV row blocks (pairs x row blocks) are limited to the counter block's size
 constexpr int kMaxSplitUnits = 4096;
@@ -239,6 +245,14 @@ AttnPlan make_plan(int B, int M_max, int Hq, int Hkv, int L_cap, int d, int cus,
     if (s < 1) s = 1;
     if (force_splits >= 1 && force_splits <= 16) s = force_splits;
     if (base >= kMaxSplitUnits) s = 1;
+    // a ragged batch whose row blocks fit one workgroup per CU but leave no room for uniform
+    // splits: the device gives the sequences with the most chunks a second split
+    p.adapt = 0;
+    if (d == 128 && force_rows == 0 && force_splits == 0 && s == 1 && B >= 2 && B <= kAdaptMaxB &&
+        Hkv % tmv::kXcds == 0 && base <= cpx * tmv::kXcds && base < kMaxSplitUnits && L_cap >= 4 * kChunk) {
+        p.adapt = static_cast<int>(cpx) * tmv::kXcds;           // one workgroup per CU
+        s = kAdaptSplits;
+    }
     p.splits = s;
     p.per_pair = p.nb * p.splits;
     p.slots = static_cast<int>(xcd_pairs) * p.per_pair;
@@ -814,7 +828,7 @@ struct PagedArgs {
 // by other workgroups, on any XCD, with agent-coherent stores), then merged in split order,
 // so the result does not depend on which split arrived last.
 template <int D, int RB, int IPB, int SMAX>
-__device__ __forceinline__ void merge_block(int64_t unit, int splits, int b, int kvh, int g, int g_magic, int row0_wg, int M_max,
+__device__ __forceinline__ void merge_block(int64_t unit, int splits, int stride, int b, int kvh, int g, int g_magic, int row0_wg, int M_max,
                                             int L_cap, int M, int P, int st, const int32_t *__restrict__ depth,
                                             uint16_t *__restrict__ out, int64_t os0, int64_t os1, int64_t os2,
                                             const float *__restrict__ ws_stats, const uint16_t *__restrict__ ws_o)
@@ -822,9 +836,9 @@ __device__ __forceinline__ void merge_block(int64_t unit, int splits, int b, int
     constexpr int kItems = RB * (D / 8);
     constexpr int kThreads = kRingWaves * kWave;
     const __amdgpu_buffer_rsrc_t rst = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(ws_stats + unit * splits * RB * 2), 0, splits * RB * 2 * 4, kBufferFlags);
+        const_cast<float *>(ws_stats + unit * stride * RB * 2), 0, splits * RB * 2 * 4, kBufferFlags);
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(ws_o + unit * splits * RB * D), 0, splits * RB * D * 2, kBufferFlags);
+        const_cast<uint16_t *>(ws_o + unit * stride * RB * D), 0, splits * RB * D * 2, kBufferFlags);
     const bool seq_ok = st == TMV_OK && M >= 0 && M <= M_max && P >= 0 && static_cast<int64_t>(P) + M <= L_cap;
     for (int i0 = threadIdx.x; i0 < kItems; i0 += kThreads * IPB) {
         u32x2_t ml[IPB][SMAX];
@@ -893,6 +907,75 @@ __device__ __forceinline__ void merge_block(int64_t unit, int splits, int b, int
 // SIMD (at most 256 registers per lane), so one wave's MFMAs overlap the other's softmax
 // and LDS reads.  RW waves lie along the rows (RB = 32 RW rows share every staged chunk)
 // and TW = 8 / RW token groups of waves take turns on the chunks of each ring round.
+// Work item of workgroup w when the splits adapt to a ragged batch (B <= 64 sequences, Hkv a
+// multiple of 8; one workgroup per CU, all in one round).  Workgroup w serves XCD slot
+// x = w % 8 (KV heads x, x + 8, ...) and takes item w / 8 of that slot.  Each sequence c has
+// n_c = max(1, live row groups) row groups per head and s_c = min(smax, ceil(chunks_c / T))
+// splits, with the smallest bound T (of 64 candidates, at least two chunks per token group of
+// a split) for which every slot's items -- (head, row group, split) of every sequence, in
+// sequence order -- fit its gridDim.x / 8 workgroups.  Every workgroup derives the same items
+// from the same inputs: the prefix lengths and node counts, which the kernel never writes.
+struct AdaptItem {
+    int pair, rbk, split, splits;   // pair < 0: no item
+    int tail_from;                  // the item that clears the sequence's rows from this row on (-1: none)
+};
+__device__ __forceinline__ AdaptItem adaptive_item(const int32_t *__restrict__ prefix_len,
+                                                   const int32_t *__restrict__ n_nodes, int B, int Hkv, int g, int RB,
+                                                   int TW, int M_max, int L_cap, int smax) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int ch = 0, nbl = 0;                   // lane c: sequence c's chunks and row groups
+    if (lane < B) {
+        nbl = 1;
+        const int P = prefix_len[lane], M = n_nodes[lane];
+        if (M >= 0 && M <= M_max && P >= 0 && static_cast<int64_t>(P) + M <= L_cap) {
+            ch = (P + M + kChunk - 1) / kChunk;
+            const int n = (M * g + RB - 1) / RB;
+            nbl = n > 1 ? n : 1;
+        }
+    }
+    int maxc = 0;
+    for (int c = 0; c < B; ++c) {
+        const int x = __builtin_amdgcn_readlane(ch, c);
+        maxc = x > maxc ? x : maxc;
+    }
+    // candidate bound of this lane; ceil(x / T) for x <= 4T by comparisons (smax <= 4)
+    int T = maxc * (lane + 1) / kWave + 1;
+    T = T < 2 * TW ? 2 * TW : T;
+    auto nsplit = [&](int x, int t) {
+        const int s = 1 + (x > t) + (x > 2 * t) + (x > 3 * t);
+        return s < smax ? s : smax;
+    };
+    const int hpl = Hkv / tmv::kXcds;     // heads per XCD slot
+    int need = 0;
+    for (int c = 0; c < B; ++c)
+        need += hpl * __builtin_amdgcn_readlane(nbl, c) * nsplit(__builtin_amdgcn_readlane(ch, c), T);
+    const uint64_t ok = __builtin_amdgcn_ballot_w64(need <= static_cast<int>(gridDim.x / tmv::kXcds));
+    const int sel = ok ? __builtin_ctzll(ok) : kWave - 1;
+    const int Ts = __builtin_amdgcn_readlane(T, sel);
+    // item j of slot x
+    const int x = blockIdx.x & (tmv::kXcds - 1), j = blockIdx.x / tmv::kXcds;
+    AdaptItem it = {-1, 0, 0, 1, -1};
+    int acc = 0;
+    for (int c = 0; c < B; ++c) {
+        const int n = __builtin_amdgcn_readlane(nbl, c);
+        const int s = nsplit(__builtin_amdgcn_readlane(ch, c), Ts);
+        const int cnt = hpl * n * s;
+        if (j < acc + cnt) {
+            const int loc = j - acc, per_head = n * s;
+            const int h = loc / per_head, rem = loc - h * per_head;
+            it.pair = c * Hkv + x + tmv::kXcds * h;
+            it.rbk = rem / s;
+            it.split = rem - it.rbk * s;
+            it.splits = s;
+            // the sequence's last row group (split 0) also clears the rows no item covers
+            it.tail_from = (it.rbk == n - 1 && it.split == 0) ? n * RB : -1;
+            break;
+        }
+        acc += cnt;
+    }
+    return it;
+}
+
 template <int D, int RW, bool DEEP, bool PAGED>
 __global__ void __launch_bounds__(kRingWaves * kWave)
 tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
@@ -907,7 +990,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
                       int32_t *__restrict__ status, float qk_scale_log2,
                       uint16_t *__restrict__ out, int64_t os0, int64_t os1, int64_t os2,
                       float *__restrict__ ws_stats, uint16_t *__restrict__ ws_o, int32_t *__restrict__ ws_cnt,
-                      PagedArgs pg)
+                      PagedArgs pg, int adapt)
 {
     using RS = RingShape<D>;
     static_assert(D == 128, "the LDS-ring kernel is written for head dimension 128");
@@ -943,12 +1026,27 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     // ---- decode the workgroup.  grid = (8 * nb, splits, ceil(pairs / 8)) with x = XCD slot +
     // 8 * row block: the linear workgroup id is x + 8 nb (split + splits z), so every
     // workgroup of one (sequence, kv head) pair has the same id mod 8 and the hardware deals
-    // them all to the same XCD.  geom = Hkv | g << 16.
+    // them all to the same XCD.  geom = Hkv | g << 16.  With adapt > 0 (ragged batches: the
+    // split bound) the grid is one workgroup per CU and each takes its work item from
+    // adaptive_item (the same XCD slot for all items of a pair).
     const int Hkv = static_cast<int>(geom & 0xffffu), g = static_cast<int>(geom >> 16);
-    const int xcd = blockIdx.x & (tmv::kXcds - 1), rbk = blockIdx.x >> 3;
-    const int split = blockIdx.y, splits = gridDim.y;
-    const int pair = blockIdx.z * tmv::kXcds + xcd;
-    if (pair >= pairs) return;
+    int rbk, split, splits, pair, smax, tail_from = -1;
+    if (adapt > 0) {
+        const AdaptItem it = adaptive_item(prefix_len, n_nodes, pairs / Hkv, Hkv, g, RB, TW, M_max, L_cap, adapt);
+        pair = __builtin_amdgcn_readfirstlane(it.pair);
+        if (pair < 0) return;
+        rbk = __builtin_amdgcn_readfirstlane(it.rbk);
+        split = __builtin_amdgcn_readfirstlane(it.split);
+        splits = __builtin_amdgcn_readfirstlane(it.splits);
+        tail_from = __builtin_amdgcn_readfirstlane(it.tail_from);
+        smax = adapt;
+    } else {
+        rbk = blockIdx.x >> 3;
+        split = blockIdx.y;
+        splits = smax = gridDim.y;
+        pair = blockIdx.z * tmv::kXcds + (blockIdx.x & (tmv::kXcds - 1));
+        if (pair >= pairs) return;
+    }
     const int b = pair / Hkv, kvh = pair - b * Hkv;
     // row r -> node r / g + 1 by a multiply: exact for r < 4096 and g <= 16
     const int g_magic = (65536 + g - 1) / g;
@@ -1186,7 +1284,20 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     }
     const int Rh = (st == TMV_OK) ? M * g : 0;           // live rows of this kv head
 
+    // adaptive items: the last row group of a sequence also clears its output rows from
+    // tail_from on, which no item covers (zeros, as for any inert row)
+    auto clear_tail = [&]() {
+        if (tail_from < 0) return;
+        const int rows = M_max * g - tail_from;
+        for (int i = threadIdx.x; i < rows * (D / 8); i += kThreads) {
+            const int r = tail_from + i / (D / 8), e = (i % (D / 8)) * 8;
+            const int j = node_of(r), gi = r - (j - 1) * g;
+            *reinterpret_cast<uint4 *>(out + b * os0 + static_cast<int64_t>(j - 1) * os1 +
+                                       static_cast<int64_t>(kvh * g + gi) * os2 + e) = make_uint4(0, 0, 0, 0);
+        }
+    };
     if (row0_wg >= Rh) {
+        clear_tail();
         // no live row in this workgroup (nor in the other splits of its row block, which
         // see the same rows): split 0 clears the block's output rows
         if (split == 0 && tw == 0) {
@@ -1525,6 +1636,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         }
     }
     __syncthreads();
+    clear_tail();
     float mrow[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
@@ -1545,8 +1657,8 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     // any XCDs: no L2 write-back or invalidation is needed.  A split's stores are complete
     // once its vector-memory count drains, after which it counts itself in with a
     // device-scope atomic; the last arrival clears the counter and merges.
-    // this launch's split partials: [pairs * nb units][splits][RB rows] (m, l) and O rows
-    const int64_t part_rows = static_cast<int64_t>(pairs) * nb * splits * RB;
+    // this launch's split partials: [pairs * nb units][smax][RB rows] (m, l) and O rows
+    const int64_t part_rows = static_cast<int64_t>(pairs) * nb * smax * RB;
     const __amdgpu_buffer_rsrc_t part_o =
         __builtin_amdgcn_make_buffer_rsrc(ws_o, 0, static_cast<int>(part_rows * D * 2), kBufferFlags);
     const __amdgpu_buffer_rsrc_t part_ml =
@@ -1565,10 +1677,10 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         // one round trip for the partials of up to 8 splits and up to 2 items per thread
         constexpr int kIpt = (RB * (D / 8) + kThreads - 1) / kThreads;
         if (splits <= 8)
-            merge_block<D, RB, (kIpt < 2 ? kIpt : 2), 8>(unit, splits, b, kvh, g, g_magic, row0_wg, M_max, L_cap, M, P, st,
+            merge_block<D, RB, (kIpt < 2 ? kIpt : 2), 8>(unit, splits, smax, b, kvh, g, g_magic, row0_wg, M_max, L_cap, M, P, st,
                                                           depth, out, os0, os1, os2, ws_stats, ws_o);
         else
-            merge_block<D, RB, 1, 16>(unit, splits, b, kvh, g, g_magic, row0_wg, M_max, L_cap, M, P, st, depth, out, os0,
+            merge_block<D, RB, 1, 16>(unit, splits, smax, b, kvh, g, g_magic, row0_wg, M_max, L_cap, M, P, st, depth, out, os0,
                                       os1, os2, ws_stats, ws_o);
     };
     // row `rr` of the workgroup's block, dims d0 .. d0 + n - 1 (n a multiple of 8) of the
@@ -1640,7 +1752,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         }
         if (splits > 1) {
             // ---- publish this split's partial: (m, l) and the row normalised by l in bf16
-            const int base = static_cast<int>((unit * splits + split) * RB);
+            const int base = static_cast<int>((unit * smax + split) * RB);
             const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
             for (int e = 0; e < DL; e += 8) {
@@ -1662,7 +1774,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     } else {
         // ---- one token group: every wave holds whole rows (lane: dims nt*16 + 4G .. +3)
         if (splits > 1) {
-            const int base = static_cast<int>((unit * splits + split) * RB + rw * kRowsPerWave);
+            const int base = static_cast<int>((unit * smax + split) * RB + rw * kRowsPerWave);
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
                 const int rr = rt * 16 + c16;
@@ -1879,7 +1991,8 @@ void launch_bf16(const AttnPlan &p, hipStream_t s, int M_max, int D_max, int Hq,
         // the ring kernel merges its splits itself (the last split of a row block to arrive)
         uint16_t *part = reinterpret_cast<uint16_t *>(w + off_o);
         const uint32_t geom = static_cast<uint32_t>(Hkv) | (static_cast<uint32_t>(Hq / Hkv) << 16);
-        const dim3 grid(tmv::kXcds * p.nb, p.splits, (p.pairs + tmv::kXcds - 1) / tmv::kXcds);
+        const unsigned pgroups = static_cast<unsigned>((p.pairs + tmv::kXcds - 1) / tmv::kXcds);
+        const dim3 grid = p.adapt ? dim3(static_cast<unsigned>(p.adapt)) : dim3(tmv::kXcds * p.nb, p.splits, pgroups);
         const PagedArgs pgv = pg ? *pg : PagedArgs{nullptr, 0, 0, 0};
 #define TMV_LAUNCH_ATTN(DEEP, PAGED)                                                                       \
         hipLaunchKernelGGL((tree_attn_bf16_kernel<D, WR, DEEP, PAGED>), grid,                             \
@@ -1888,7 +2001,7 @@ void launch_bf16(const AttnPlan &p, hipStream_t s, int M_max, int D_max, int Hq,
                            static_cast<uint32_t>(kvs[1] / 8), static_cast<uint32_t>(kvs[2] / 8), L_cap,   \
                            p.pairs, geom, M_max, D_max, p.nb, static_cast<const uint16_t *>(q), qs[0],    \
                            qs[1], qs[2], anc, dep, status, scale * kLog2e, static_cast<uint16_t *>(out),   \
-                           os[0], os[1], os[2], stats, part, cnt, pgv)
+                           os[0], os[1], os[2], stats, part, cnt, pgv, p.adapt ? p.splits : 0)
         if (pg) {
             if (D_max + 1 > kAncBatch) TMV_LAUNCH_ATTN(true, true);
             else TMV_LAUNCH_ATTN(false, true);

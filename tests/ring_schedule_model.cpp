@@ -30,7 +30,7 @@ bool run(int NR, int nrounds, int waves) {
         for (int x = 0; x < NR; ++x) issue(w, x);
     std::vector<double> read_end(nrounds, 0.0);   // when the last wave finished reading round r
     for (int r = 0; r < nrounds; ++r) {
-        const int n = tmv_ring::inflight(r, NR, nrounds);
+        const int n = tmv_ring::inflight(r, NR);
         // the wait: all but the n most recent rounds of this wave's copies have landed
         for (int w = 0; w < waves; ++w) {
             const int done = static_cast<int>(issued[w].size()) - n;
@@ -45,7 +45,7 @@ bool run(int NR, int nrounds, int waves) {
                     std::printf("round %d read before it landed (NR %d, rounds %d)\n", r, NR, nrounds);
                     return false;
                 }
-        const int x = tmv_ring::issue_at(r, NR, nrounds);
+        const int x = tmv_ring::issue_at(r, NR);
         if (x >= 0) {
             const int prev = x - NR;                 // the group's previous round
             if (prev >= 0 && (prev >= r || read_end[prev] > bar)) {
@@ -60,7 +60,7 @@ bool run(int NR, int nrounds, int waves) {
     }
     for (int r = 0; r < nrounds; ++r) {
         int cnt = 0;
-        for (const Copy &c : issued[0]) cnt += c.round == r;
+        for (const Copy &c : issued[0]) cnt += c.round == r;   // (rounds past the last are empty copies)
         if (cnt != 1) { std::printf("round %d issued %d times\n", r, cnt); return false; }
     }
     return true;

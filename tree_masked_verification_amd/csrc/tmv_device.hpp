@@ -8,6 +8,12 @@
 
 namespace tmv {
 
+// a compile-time integer passed as a value (to generic lambdas)
+template <int N>
+struct Const {
+    static constexpr int value = N;
+};
+
 constexpr int kWave = 64;       // CDNA wavefront width
 constexpr int kXcds = 8;        // MI355X: workgroups are dealt round-robin to 8 XCDs
 

@@ -64,24 +64,20 @@ constexpr int kCoherent = 16;
 // s_waitcnt immediate that waits for LDS / scalar-memory count 0 only
 constexpr int kLgkmcntZero = 0xF | (0x7 << 4) | (0x3 << 14);
 
-// LDS operand reads of the attention loop.  The compiler cannot tell the two halves of
-// the DMA ring apart inside the loop, so for any LDS load it writes itself it would first
-// wait for all buffer->LDS DMA in flight, including the next round's.  These reads are
-// therefore inline assembly, each block self-contained: it issues its reads and waits for
-// them before its outputs exist, so no register is ever seen before its data has landed
-// (outputs are early-clobber: a returning read must not overwrite a later read's address).
-// The loop's own waits and barriers order the blocks against the DMA (the memory clobber
-// keeps the compiler from moving them across those).
+// LDS accesses outside the ring's chunk loop that run while buffer->LDS copies are in
+// flight (the query-tile exchange, the zeroing of V rows past the visible range): the
+// compiler cannot tell which LDS bytes a copy in flight writes there, so for an LDS access
+// it writes itself it would first wait for every copy.  These are therefore inline
+// assembly, each block self-contained: it issues its accesses and waits for them before
+// its outputs exist, so no register is ever seen before its data has landed (outputs are
+// early-clobber: a returning read must not overwrite a later read's address).  The loop's
+// own waits and barriers order the blocks against the copies (the memory clobber keeps the
+// compiler from moving them across those).  The chunk loop's operand reads are ordinary
+// loads: there every ring group is a separate LDS array named statically.
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void lds_read_b128_x4(u32x4_t (&v)[4], const uint32_t (&a)[4]) {
-    asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
-                 "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
-                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
-                 : "memory");
-}
 __device__ __forceinline__ void lds_read_b128_x8(u32x4_t (&v)[8], const uint32_t (&a)[8]) {
     asm volatile("ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\tds_read_b128 %3, %11\n\t"
                  "ds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\tds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\t"
@@ -91,13 +87,8 @@ __device__ __forceinline__ void lds_read_b128_x8(u32x4_t (&v)[8], const uint32_t
                  : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
                  : "memory");
 }
-// V^T operand reads with the gfx950 transposing LDS load: within each 16-lane group, lane
-// s supplies 4 consecutive bf16 at its address and receives element s%4 of the groups
-// supplied by lanes s/4, s/4 + 4, s/4 + 8, s/4 + 12.  With lane s reading row T[s/4] at
-// dims 4*(s%4) .. +3 of a 16-dim tile, lane s ends up with dim s of rows T[0..3] -- one
-// column of V, as the MFMA A operand wants.  v[2*nt + h]: dim tile nt, token half h; the
-// tile's address is the lane's half base z_h with 32*nt XORed in (the swizzle of the V
-// rows only permutes 32-byte dim groups, so tiles stay XOR-addressable).
+// V^T operand reads in inline assembly (see the note above): ds_read_b64_tr_b16 at the
+// lane's half offsets z0, z1 with 32*nt XORed in, v[2*nt + h] as in compute_chunk.
 __device__ __forceinline__ void lds_read_vt(u32x2_t (&v)[16], uint32_t z0, uint32_t z1) {
     uint32_t t0, t1;
     asm volatile("ds_read_b64_tr_b16 %0, %18\n\t"
@@ -1003,15 +994,27 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     constexpr int kThreads = kRingWaves * kWave;
     constexpr int kDW = RS::kDmaPerWave;
 
-    // the ring: kNR groups of kR chunk slots, one round of copies each (all its reads are
-    // inline assembly, so the compiler never waits for copies in flight before touching
-    // it).  A round holds a chunk for every token group (rounds of 2 chunks when the waves
-    // form at most 2 token groups, so that up to 3 rounds are in flight while one is computed).
+    // the ring: kNR groups of kR chunk slots, one round of copies each.  A round holds a
+    // chunk for every token group (rounds of 2 chunks when the waves form at most 2 token
+    // groups, so that up to 3 rounds are in flight while one is computed).  The groups are
+    // separate LDS arrays, and the chunk loop names each group it touches statically: the
+    // compiler then tells them apart, so a read of one group never waits for the copies
+    // still in flight into another (it waits for the group's own copies, which the loop's
+    // schedule has already waited for).
     constexpr int kR = TW > 2 ? TW : 2;
     constexpr int kNR = RS::kSlots / kR;
     static_assert(kNR * kR == RS::kSlots && kNR >= 2 && kNR <= 4, "ring groups");
     constexpr int kGroupBytes = kR * RS::kSlotBytes;
-    __shared__ __attribute__((aligned(16))) char ring[kNR * kGroupBytes];
+    __shared__ __attribute__((aligned(256))) char ring0[kGroupBytes];
+    __shared__ __attribute__((aligned(256))) char ring1[kGroupBytes];
+    __shared__ __attribute__((aligned(256))) char ring2[kNR > 2 ? kGroupBytes : 16];
+    __shared__ __attribute__((aligned(256))) char ring3[kNR > 3 ? kGroupBytes : 16];
+    auto group = [&](int gi) -> char * { return gi == 0 ? ring0 : gi == 1 ? ring1 : gi == 2 ? ring2 : ring3; };
+    // 64- and 128-row groups read their chunk operands with the inline-assembly blocks (each
+    // waits for its own reads) in a rolled loop: the compiler's freedom to hoist ordinary
+    // loads, and the unrolled loop they need, cost these kernels more registers than they
+    // save time
+    constexpr bool kAsmReads = RW <= 4;
     __shared__ float s_ml[kRingWaves * kRowsPerWave * 2];
     // 64-row groups (contiguous caches): the four token groups of a row group share one
     // copy of its query fragments, each loading one k-step (16 KB for the workgroup)
@@ -1098,7 +1101,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         const int qpos = ii * 64 + lane;                       // 16-byte LDS piece index
         const int t = qpos / PP, pp = qpos % PP;
         // K rows swizzle their 16-byte pieces by t mod 16, V rows by 2t mod 16 (the V^T reads
-        // take four consecutive rows at once; see lds_read_vt)
+        // take four consecutive rows at once; see the V^T reads in compute_chunk)
         const int sw = wave_v ? (2 * t) % PP : t % PP;
         // (from the wave-uniform instruction index: instruction ii covers rows 64*ii/PP ..
         // +64/PP - 1, all on one side of row 16, so the page choice stays scalar)
@@ -1176,8 +1179,9 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     // the prefetched entries when `prefetched`).  Every wave issues exactly kR * kDW copies
     // per round, empty ones included, so the count of copies issued after a round -- what
     // the waits below rely on -- is the same on every path.
-    auto issue_round = [&](int r, bool prefetched = false) __attribute__((always_inline)) {
-        char *grp = ring + (r % kNR) * kGroupBytes;
+    // (gi: the group, r % kNR -- a constant in the unrolled chunk loop)
+    auto issue_round = [&](int gi, int r, bool prefetched = false) __attribute__((always_inline)) {
+        char *grp = group(gi);
         if constexpr (PAGED) {
 #pragma unroll
             for (int j = 0; j < kR; ++j) {
@@ -1192,9 +1196,18 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         }
     };
     // the first kNR rounds, before the chunk loop (every slot of the ring)
-    auto issue_prologue = [&](int from) __attribute__((always_inline)) {
+    auto issue_prologue = [&](bool from_first) __attribute__((always_inline)) {
+        if constexpr (kAsmReads) {
 #pragma unroll 1
-        for (int r = from; r < kNR; ++r) issue_round(r);
+            for (int r = from_first ? 0 : 1; r < kNR; ++r) issue_round(r, r);
+            return;
+        }
+        if (from_first) issue_round(0, 0);
+        issue_round(1, 1);
+        if constexpr (kNR > 2) {
+            issue_round(2, 2);
+            issue_round(3 % kNR, 3);
+        }
     };
     // paged caches: this thread's block-table entries are loaded first, together with the
     // prologue's loads below, and staged in LDS before the first copies (L_cap = entries x page)
@@ -1210,7 +1223,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         }
     } else {
         // the first round goes out before anything else is loaded or waited for
-        issue_round(0);
+        issue_round(0, 0);
     }
 
     // ---- the prologue's loads, between the first and the second round of copies (vector
@@ -1242,7 +1255,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
             ancq[rt][k] = arow[kk < W ? kk : W - 1];
         }
     }
-    if constexpr (!PAGED) issue_prologue(1);
+    if constexpr (!PAGED) issue_prologue(false);
     if constexpr (PAGED) {
         // stage the entries (invalid ones as -1; each wave records the first invalid one),
         // then issue the first two rounds from them
@@ -1264,7 +1277,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         }
         if (lane == 0) pg_bad[wave] = bad_min;
         __syncthreads();
-        issue_prologue(0);
+        issue_prologue(true);
     }
 
     if (st == TMV_OK && (M < 0 || M > M_max || P < 0 || static_cast<int64_t>(P) + M > L_cap)) {
@@ -1415,7 +1428,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     }
     // LDS read offsets of the MFMA operands inside a slot (constant per lane).  K
     // fragment (tt, ks): row tt*16 + c16, logical piece ks*4 + G.  V^T: lane reads row
-    // h*16 + 4G + c16/4 at dims 4*(c16%4) of each 16-dim tile (base zv[h], see lds_read_vt).
+    // h*16 + 4G + c16/4 at dims 4*(c16%4) of each 16-dim tile (offset zv[h]; see compute_chunk).
     uint32_t lk[2][KS], zv[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -1509,7 +1522,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) lacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_a, pb[rt], lacc[rt], 0, 0, 0);
     };
-    auto compute_chunk = [&](uint32_t sp, int c) {
+    auto compute_chunk = [&](const char *slot, int c) {
         const int t0 = c * kChunk;
         // S^T tiles: [token][row]; lane holds row c16 of tile rt, tokens t0 + tt*16 + G*4 + i
         constexpr int NK = 2 * KS;                   // K fragments of the chunk per lane
@@ -1519,8 +1532,16 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) ka[tt * KS + ks] = sp + lk[tt][ks];
-            lds_read_b128_x8(kraw, ka);
+                for (int ks = 0; ks < KS; ++ks) ka[tt * KS + ks] = lk[tt][ks];
+            if constexpr (kAsmReads) {
+                const uint32_t sp = lds_addr(slot);
+#pragma unroll
+                for (int i = 0; i < NK; ++i) ka[i] += sp;
+                lds_read_b128_x8(kraw, ka);
+            } else {
+#pragma unroll
+                for (int i = 0; i < NK; ++i) kraw[i] = *reinterpret_cast<const u32x4_t *>(slot + ka[i]);
+            }
         }
         bf16x8_t kf[2][KS];
 #pragma unroll
@@ -1543,7 +1564,22 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         float cm[2] = {lane_max(s[0]), lane_max(s[1])};
         // V^T fragments go out while the score MFMAs run
         u32x2_t vt[16];
-        lds_read_vt(vt, sp + zv[0], sp + zv[1]);
+        // V^T operand reads with the gfx950 transposing LDS load: within each 16-lane group,
+        // lane s supplies 4 consecutive bf16 at its address and receives element s%4 of the
+        // groups supplied by lanes s/4, s/4 + 4, s/4 + 8, s/4 + 12.  With lane s reading row
+        // T[s/4] at dims 4*(s%4) .. +3 of a 16-dim tile, lane s ends up with dim s of rows
+        // T[0..3] -- one column of V, as the MFMA A operand wants.  vt[2*nt + h]: dim tile
+        // nt, token half h; the tile's offset is the lane's half offset zv[h] with 32*nt
+        // XORed in (the swizzle of the V rows only permutes 32-byte dim groups).
+        if constexpr (kAsmReads) {
+            // (the XOR touches bits 5-7 only: a slot starts at a multiple of 256 bytes)
+            lds_read_vt(vt, lds_addr(slot) + zv[0], lds_addr(slot) + zv[1]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                vt[i] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) s16x4_t *)(slot + (zv[i & 1] ^ (32u * (i >> 1))))));
+        }
         if (t0 + kChunk > P) {
             // chunk reaches the tree slots: a token is visible if it is in the prefix or is
             // an ancestor-or-self of the row's node.  Over the sequence of 32-bit words
@@ -1580,23 +1616,20 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) oacc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-        if (pass > 0) issue_prologue(0);
+        if (pass > 0) issue_prologue(true);
         // Round r (ring group r % kNR): wait until this wave's copies of round r have landed
         // (later rounds may still be in flight: vector-memory operations complete in issue
         // order and every wave issues exactly kR * kDW copies per round), barrier -- every
         // wave's share of round r is then visible and every wave has finished reading round
-        // r - 1 -- then refill round r - 1's group with the next round and compute round r.
+        // r - 1 -- then refill round r - 1's group with round r + kNR - 1 and compute round r.
         // (tmv_ring defines and checks the schedule.)  The barriers carry no memory fence on
-        // purpose: a fence would wait for all copies in flight.
-#pragma unroll 1
-        for (int r = 0; r < nrounds; ++r) {
-            char *grp = ring + (r % kNR) * kGroupBytes;
-            switch (tmv_ring::inflight(r, kNR, nrounds)) {
-            case 0: __builtin_amdgcn_s_waitcnt(kVmcntZero); break;
-            case 1: __builtin_amdgcn_s_waitcnt(kVmcntRound<kR * kDW>()); break;
-            case 2: __builtin_amdgcn_s_waitcnt(kVmcntRound<2 * kR * kDW>()); break;
-            default: __builtin_amdgcn_s_waitcnt(kVmcntRound<3 * kR * kDW>()); break;
-            }
+        // purpose: a fence would wait for all copies in flight.  The loop is unrolled over
+        // the groups so that each group is named statically.
+        auto round_body = [&](auto G, int r, auto refill) __attribute__((always_inline)) {
+            constexpr int gi = decltype(G)::value;
+            char *grp = group(gi);
+            if (r == 0) __builtin_amdgcn_s_waitcnt(kVmcntRound<(kNR - 1) * kR * kDW>());
+            else __builtin_amdgcn_s_waitcnt(kVmcntRound<(kNR - 2) * kR * kDW>());
             __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
             __builtin_amdgcn_s_barrier();
             if (pass == 0 && r == kb_round) {
@@ -1607,18 +1640,61 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
                 __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
                 __builtin_amdgcn_s_barrier();
             }
-            const int x = tmv_ring::issue_at(r, kNR, nrounds);
-            if (x >= 0) issue_round(x, true);
-            // (paged: the next issue's table entries, read from LDS a round ahead)
-            const int xn = tmv_ring::issue_at(r + 1, kNR, nrounds);
-            if (xn >= 0) prefetch_pages(xn);
+            if constexpr (decltype(refill)::value) issue_round((gi + kNR - 1) % kNR, r + kNR - 1, true);
+            // (paged: the next refill's table entries, read from LDS a round ahead)
+            prefetch_pages(r + kNR);
             if (wave_live) {
 #pragma unroll 1
                 for (int j = tw; j < kR; j += TW) {
                     const int k = r * kR + j;
-                    if (k < nk) compute_chunk(lds_addr(grp) + j * RS::kSlotBytes, split + k * splits);
+                    if (k < nk) compute_chunk(grp + j * RS::kSlotBytes, split + k * splits);
                 }
             }
+        };
+        static_assert(tmv_ring::inflight(0, kNR) == kNR - 1 && tmv_ring::inflight(1, kNR) == kNR - 2 &&
+                      tmv_ring::issue_at(1, kNR) == kNR, "the loop below follows tmv_ring");
+        if constexpr (kAsmReads) {
+            // (operands read by the inline-assembly blocks: one copy of the loop, the group
+            // chosen at run time, keeps these kernels small.  With two groups every wait is
+            // for all copies in flight, so rounds past the last need not be issued.)
+#pragma unroll 1
+            for (int r = 0; r < nrounds; ++r) {
+                char *grp = group(r % kNR);
+                if (r == 0) __builtin_amdgcn_s_waitcnt(kVmcntRound<(kNR - 1) * kR * kDW>());
+                else __builtin_amdgcn_s_waitcnt(kVmcntRound<(kNR - 2) * kR * kDW>());
+                __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
+                __builtin_amdgcn_s_barrier();
+                if (pass == 0 && r == kb_round) {
+                    const int r0 = T - (split + kb_loc * splits) * kChunk;
+                    const uint32_t vb = lds_addr(grp) + (kb_loc % kR) * RS::kSlotBytes + RS::kMatBytes + r0 * RS::kRowBytes;
+                    for (int i = threadIdx.x; i < (kChunk - r0) * PP; i += kThreads) lds_zero16(vb + i * 16);
+                    __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
+                    __builtin_amdgcn_s_barrier();
+                }
+                if (r >= 1 && (kNR > 2 || r + kNR - 1 < nrounds)) issue_round((r + kNR - 1) % kNR, r + kNR - 1, true);
+                prefetch_pages(r + kNR);
+                if (wave_live) {
+#pragma unroll 1
+                    for (int j = tw; j < kR; j += TW) {
+                        const int k = r * kR + j;
+                        if (k < nk) compute_chunk(grp + j * RS::kSlotBytes, split + k * splits);
+                    }
+                }
+            }
+        } else {
+        if (nrounds > 0) round_body(tmv::Const<0>{}, 0, tmv::Const<0>{});
+#pragma unroll 1
+        for (int r0 = 1; r0 < nrounds; r0 += kNR) {
+            round_body(tmv::Const<1>{}, r0, tmv::Const<1>{});
+            if (r0 + 1 >= nrounds) break;
+            if constexpr (kNR > 2) {
+                round_body(tmv::Const<2 % kNR>{}, r0 + 1, tmv::Const<1>{});
+                if (r0 + 2 >= nrounds) break;
+                round_body(tmv::Const<3 % kNR>{}, r0 + 2, tmv::Const<1>{});
+                if (r0 + 3 >= nrounds) break;
+            }
+            round_body(tmv::Const<0>{}, r0 + kNR - 1, tmv::Const<1>{});
+        }
         }
         __builtin_amdgcn_s_waitcnt(kVmcntZero);   // nothing may land in LDS after this
         // the decision is the workgroup's: every wave must take the same number of passes,
@@ -1708,8 +1784,12 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         // the idle ring (16 KB per wave; 4-float groups XOR-swizzled by row so the parked
         // writes are free of bank conflicts), then each wave combines its share of its row
         // group's rows over the group's TW waves in a fixed order.
-        static_assert(kRingWaves * kRowsPerWave * D * 4 == sizeof(ring), "park area = ring");
-        auto parked = [&](int w) { return reinterpret_cast<float *>(ring + w * kRowsPerWave * D * 4); };
+        constexpr int kParkBytes = kRowsPerWave * D * 4;
+        static_assert(kRingWaves * kParkBytes == kNR * kGroupBytes && kGroupBytes % kParkBytes == 0, "park area = ring");
+        auto parked = [&](int w) {
+            constexpr int per = kGroupBytes / kParkBytes;
+            return reinterpret_cast<float *>(group(w / per) + (w % per) * kParkBytes);
+        };
         {
             float *o = parked(wave);
 #pragma unroll

@@ -6,6 +6,8 @@ The oracle cannot afford every attention row of the long-prefix workloads, so:
     are compared on every row;
   * properties that hold at any size are checked on every row: inert rows are exactly
     zero, live rows are finite."""
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -33,6 +35,26 @@ def _sampled_rows(w, anc, depth, per_seq, seed):
     return sel
 
 
+def _oracle_rows(ref, w, ra, rd, rs, sel, threads=8):
+    """The oracle on the selected rows, the sequences dealt to threads (the oracle's C
+    routine runs without the interpreter lock)."""
+    parts = np.array_split(np.arange(w.B), min(threads, w.B))
+
+    def one(bs):
+        s = np.zeros_like(sel)
+        s[bs] = sel[bs]
+        return bs, oracle_attention(ref, w, ra, rd, rs, row_select=s)[0]
+
+    out = None
+    with ThreadPoolExecutor(len(parts)) as ex:
+        for bs, o in ex.map(one, parts):
+            if out is None:
+                out = o
+            else:
+                out[bs] = o[bs]
+    return out
+
+
 def _run(ref, w, per_seq, seed, all_rows=False):
     dev = DeviceStep(w)
     dev.build()
@@ -48,7 +70,7 @@ def _run(ref, w, per_seq, seed, all_rows=False):
             live[b, j - 1] = j <= w.n_nodes[b] and rd[b, j] >= 1
     assert np.all(outf[~live] == 0) and np.all(np.isfinite(outf[live]))
     sel = np.ones((w.B, w.M_max), np.uint8) * live if all_rows else _sampled_rows(w, ra, rd, per_seq, seed)
-    ref_out, _ = oracle_attention(ref, w, ra, rd, rs, row_select=sel)
+    ref_out = _oracle_rows(ref, w, ra, rd, rs, sel)
     mask = np.zeros(out.shape, bool)
     mask[sel.astype(bool)] = True
     err, rel = attention_error(out, ref_out, w.dtype, mask)
@@ -59,7 +81,15 @@ def _run(ref, w, per_seq, seed, all_rows=False):
 def test_batched_dynamic_trees_sampled(ref):
     _case("attention: batched dynamic trees (config 3), sampled nodes")
     w = ti.workload(3, with_rows=False)
-    _run(ref, w, per_seq=2, seed=31)
+    _run(ref, w, per_seq=6, seed=31)
+
+
+def test_batched_dynamic_trees_all_rows(ref):
+    """Every row of the batched workload with its prefixes: the ragged plan's per-sequence
+    splits and split merges at full size."""
+    _case("attention: batched dynamic trees (config 3), every row")
+    w = ti.workload(3, with_rows=False)
+    _run(ref, w, 0, 0, all_rows=True)
 
 
 def test_batched_dynamic_trees_empty_prefix_all_rows(ref):
@@ -73,7 +103,7 @@ def test_batched_dynamic_trees_empty_prefix_all_rows(ref):
 def test_long_context_70b_sampled(ref):
     _case("attention: 70B-shaped layer, prefix 32768 (config 4), sampled nodes")
     w = ti.workload(4, with_rows=False)
-    _run(ref, w, per_seq=1, seed=41)
+    _run(ref, w, per_seq=4, seed=41)
 
 
 def test_long_context_70b_empty_prefix_all_rows(ref):

@@ -72,8 +72,10 @@ constexpr int kLgkmcntZero = 0xF | (0x7 << 4) | (0x3 << 14);
 // its outputs exist, so no register is ever seen before its data has landed (outputs are
 // early-clobber: a returning read must not overwrite a later read's address).  The loop's
 // own waits and barriers order the blocks against the copies (the memory clobber keeps the
-// compiler from moving them across those).  The chunk loop's operand reads are ordinary
-// loads: there every ring group is a separate LDS array named statically.
+// compiler from moving them across those).  The chunk operands of 64- and 128-row groups
+// are read by such blocks too; 256-row groups read them with ordinary loads, in a loop
+// unrolled over the ring groups, each a separate LDS array named statically (the compiler
+// then waits only for the copies into the group it reads).
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -967,7 +969,7 @@ __device__ __forceinline__ AdaptItem adaptive_item(const int32_t *__restrict__ p
     return it;
 }
 
-template <int D, int RW, bool DEEP, bool PAGED>
+template <int D, int RW, bool DEEP, bool PAGED, bool ADAPT>
 __global__ void __launch_bounds__(kRingWaves * kWave)
 tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
                       const int32_t *__restrict__ prefix_len, const int32_t *__restrict__ n_nodes,
@@ -981,7 +983,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
                       int32_t *__restrict__ status, float qk_scale_log2,
                       uint16_t *__restrict__ out, int64_t os0, int64_t os1, int64_t os2,
                       float *__restrict__ ws_stats, uint16_t *__restrict__ ws_o, int32_t *__restrict__ ws_cnt,
-                      PagedArgs pg, int adapt)
+                      PagedArgs pg)
 {
     using RS = RingShape<D>;
     static_assert(D == 128, "the LDS-ring kernel is written for head dimension 128");
@@ -1029,24 +1031,27 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     // ---- decode the workgroup.  grid = (8 * nb, splits, ceil(pairs / 8)) with x = XCD slot +
     // 8 * row block: the linear workgroup id is x + 8 nb (split + splits z), so every
     // workgroup of one (sequence, kv head) pair has the same id mod 8 and the hardware deals
-    // them all to the same XCD.  geom = Hkv | g << 16.  With adapt > 0 (ragged batches: the
-    // split bound) the grid is one workgroup per CU and each takes its work item from
-    // adaptive_item (the same XCD slot for all items of a pair).
-    const int Hkv = static_cast<int>(geom & 0xffffu), g = static_cast<int>(geom >> 16);
+    // them all to the same XCD.  geom = Hkv | g << 16 | S << 21 (S: the splits, or with
+    // adaptive items their bound), a preloaded argument, so the first copies of a
+    // non-adaptive kernel wait for no kernel-argument load.  ADAPT kernels (ragged batches)
+    // run one workgroup per CU, each taking its work item from adaptive_item (the same XCD
+    // slot for all items of a pair).
+    const int Hkv = static_cast<int>(geom & 0xffffu), g = static_cast<int>((geom >> 16) & 31u);
+    const int S = static_cast<int>((geom >> 21) & 31u);
     int rbk, split, splits, pair, smax, tail_from = -1;
-    if (adapt > 0) {
-        const AdaptItem it = adaptive_item(prefix_len, n_nodes, pairs / Hkv, Hkv, g, RB, TW, M_max, L_cap, adapt);
+    if constexpr (ADAPT) {
+        const AdaptItem it = adaptive_item(prefix_len, n_nodes, pairs / Hkv, Hkv, g, RB, TW, M_max, L_cap, S);
         pair = __builtin_amdgcn_readfirstlane(it.pair);
         if (pair < 0) return;
         rbk = __builtin_amdgcn_readfirstlane(it.rbk);
         split = __builtin_amdgcn_readfirstlane(it.split);
         splits = __builtin_amdgcn_readfirstlane(it.splits);
         tail_from = __builtin_amdgcn_readfirstlane(it.tail_from);
-        smax = adapt;
+        smax = S;
     } else {
         rbk = blockIdx.x >> 3;
         split = blockIdx.y;
-        splits = smax = gridDim.y;
+        splits = smax = S;
         pair = blockIdx.z * tmv::kXcds + (blockIdx.x & (tmv::kXcds - 1));
         if (pair >= pairs) return;
     }
@@ -2070,18 +2075,25 @@ void launch_bf16(const AttnPlan &p, hipStream_t s, int M_max, int D_max, int Hq,
     } else {
         // the ring kernel merges its splits itself (the last split of a row block to arrive)
         uint16_t *part = reinterpret_cast<uint16_t *>(w + off_o);
-        const uint32_t geom = static_cast<uint32_t>(Hkv) | (static_cast<uint32_t>(Hq / Hkv) << 16);
+        // (Hkv <= 0xffff, Hq / Hkv <= 16 and splits <= 16 are checked or planned)
+        const uint32_t geom = static_cast<uint32_t>(Hkv) | (static_cast<uint32_t>(Hq / Hkv) << 16) |
+                              (static_cast<uint32_t>(p.splits) << 21);
         const unsigned pgroups = static_cast<unsigned>((p.pairs + tmv::kXcds - 1) / tmv::kXcds);
         const dim3 grid = p.adapt ? dim3(static_cast<unsigned>(p.adapt)) : dim3(tmv::kXcds * p.nb, p.splits, pgroups);
         const PagedArgs pgv = pg ? *pg : PagedArgs{nullptr, 0, 0, 0};
-#define TMV_LAUNCH_ATTN(DEEP, PAGED)                                                                       \
-        hipLaunchKernelGGL((tree_attn_bf16_kernel<D, WR, DEEP, PAGED>), grid,                             \
+#define TMV_LAUNCH_ATTN1(DEEP, PAGED, ADAPT)                                                               \
+        hipLaunchKernelGGL((tree_attn_bf16_kernel<D, WR, DEEP, PAGED, ADAPT>), grid,                      \
                            dim3(kRingWaves * kWave), 0, s, static_cast<const uint16_t *>(k),              \
                            static_cast<const uint16_t *>(v), P, n, static_cast<uint32_t>(kvs[0] / 8),     \
                            static_cast<uint32_t>(kvs[1] / 8), static_cast<uint32_t>(kvs[2] / 8), L_cap,   \
                            p.pairs, geom, M_max, D_max, p.nb, static_cast<const uint16_t *>(q), qs[0],    \
                            qs[1], qs[2], anc, dep, status, scale * kLog2e, static_cast<uint16_t *>(out),   \
-                           os[0], os[1], os[2], stats, part, cnt, pgv, p.adapt ? p.splits : 0)
+                           os[0], os[1], os[2], stats, part, cnt, pgv)
+#define TMV_LAUNCH_ATTN(DEEP, PAGED)                                                                       \
+        do {                                                                                               \
+            if (p.adapt) TMV_LAUNCH_ATTN1(DEEP, PAGED, true);                                              \
+            else TMV_LAUNCH_ATTN1(DEEP, PAGED, false);                                                     \
+        } while (0)
         if (pg) {
             if (D_max + 1 > kAncBatch) TMV_LAUNCH_ATTN(true, true);
             else TMV_LAUNCH_ATTN(false, true);
@@ -2090,6 +2102,7 @@ void launch_bf16(const AttnPlan &p, hipStream_t s, int M_max, int D_max, int Hq,
             else TMV_LAUNCH_ATTN(false, false);
         }
 #undef TMV_LAUNCH_ATTN
+#undef TMV_LAUNCH_ATTN1
     }
 }
 

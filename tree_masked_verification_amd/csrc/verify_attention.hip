@@ -815,81 +815,87 @@ struct PagedArgs {
 
 // The merging workgroup of a split-KV row block (LDS-ring kernel).  Split s left, per row
 // of the block, (m, l) in fp32 -- m the row's largest score in base-2 units, l the sum of
-// 2^(score - m) -- and the row's output normalised by l, rounded to bf16.  IPB items (row
-// rr, dims part*8 .. +8) per thread and batch: every split's (m, l) and 16-byte O slice of
-// the batch's items are loaded at once with agent-coherent loads (the partials were written
-// by other workgroups, on any XCD, with agent-coherent stores), then merged in split order,
-// so the result does not depend on which split arrived last.
-template <int D, int RB, int IPB, int SMAX>
+// 2^(score - m) -- and the row's output normalised by l, rounded to bf16.  A thread merges
+// items (row rr, dims part*8 .. +8), IPB at a time: every split's (m, l) and 16-byte O slice
+// of those items, and the rows' depths, are loaded in one straight batch with
+// agent-coherent loads (the partials were written by other workgroups, on any XCD, with
+// agent-coherent stores), then merged in split order, so the result does not depend on
+// which split arrived last.  The buffer descriptors end at the `splits`-th partial: loads of
+// splits past it return zeros without touching memory and are left out of the merge.
+template <int D, int RB, int SMAX>
 __device__ __forceinline__ void merge_block(int64_t unit, int splits, int stride, int b, int kvh, int g, int g_magic, int row0_wg, int M_max,
                                             int L_cap, int M, int P, int st, const int32_t *__restrict__ depth,
                                             uint16_t *__restrict__ out, int64_t os0, int64_t os1, int64_t os2,
                                             const float *__restrict__ ws_stats, const uint16_t *__restrict__ ws_o)
 {
-    constexpr int kItems = RB * (D / 8);
     constexpr int kThreads = kRingWaves * kWave;
+    constexpr int kItems = RB * (D / 8);
+    static_assert(kItems % kThreads == 0, "whole items per thread");
+    constexpr int kIpt = kItems / kThreads;            // items per thread
+    constexpr int IPB = kIpt < 2 ? kIpt : 2;           // items per batch of loads
     const __amdgpu_buffer_rsrc_t rst = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float *>(ws_stats + unit * stride * RB * 2), 0, splits * RB * 2 * 4, kBufferFlags);
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(ws_o + unit * stride * RB * D), 0, splits * RB * D * 2, kBufferFlags);
     const bool seq_ok = st == TMV_OK && M >= 0 && M <= M_max && P >= 0 && static_cast<int64_t>(P) + M <= L_cap;
-    for (int i0 = threadIdx.x; i0 < kItems; i0 += kThreads * IPB) {
+    const int rows_max = M_max * g;
+#pragma unroll 1
+    for (int i0 = 0; i0 < kIpt; i0 += IPB) {
         u32x2_t ml[IPB][SMAX];
         u32x4_t ov[IPB][SMAX];
+        int dp[IPB];
 #pragma unroll
         for (int k = 0; k < IPB; ++k) {
-            const int item = i0 + k * kThreads;
+            const int item = (i0 + k) * kThreads + static_cast<int>(threadIdx.x);
             const int rr = item / (D / 8), part = item % (D / 8);
 #pragma unroll
             for (int s2 = 0; s2 < SMAX; ++s2) {
-                if (s2 < splits && item < kItems) {
-                    const int row = s2 * RB + rr;
-                    ml[k][s2] = __builtin_amdgcn_raw_buffer_load_b64(rst, row * 8, 0, kCoherent);
-                    ov[k][s2] = __builtin_amdgcn_raw_buffer_load_b128(ro, (row * D + part * 8) * 2, 0, kCoherent);
-                }
+                const int row = s2 * RB + rr;
+                ml[k][s2] = __builtin_amdgcn_raw_buffer_load_b64(rst, row * 8, 0, kCoherent);
+                ov[k][s2] = __builtin_amdgcn_raw_buffer_load_b128(ro, (row * D + part * 8) * 2, 0, kCoherent);
             }
+            int r = row0_wg + rr;
+            r = r < rows_max ? r : rows_max - 1;
+            dp[k] = depth[static_cast<int64_t>(b) * (M_max + 1) + ((r * g_magic) >> 16) + 1];
         }
 #pragma unroll
         for (int k = 0; k < IPB; ++k) {
-            const int item = i0 + k * kThreads;
-            if (item >= kItems) break;
+            const int item = (i0 + k) * kThreads + static_cast<int>(threadIdx.x);
             const int rr = item / (D / 8), part = item % (D / 8);
             const int r = row0_wg + rr;
-            if (r >= M_max * g) continue;
-            const int j = ((r * g_magic) >> 16) + 1, gi = r - (j - 1) * g;
-            const int dp = depth[static_cast<int64_t>(b) * (M_max + 1) + j];
-            const bool live = seq_ok && r < M * g && dp >= 1;
+            // (computed for every item, live or not, and selected at the end: a branch on
+            // liveness would let the compiler sink the partial loads behind the depth load)
+            float mt = -INFINITY;
+#pragma unroll
+            for (int s2 = 0; s2 < SMAX; ++s2)
+                if (s2 < splits) mt = fmaxf(mt, __uint_as_float(ml[k][s2][0]));
+            const float mref = mt == -INFINITY ? 0.f : mt;
             float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            if (live) {
-                float mt = -INFINITY;
+            float lt = 0.f;
 #pragma unroll
-                for (int s2 = 0; s2 < SMAX; ++s2)
-                    if (s2 < splits) mt = fmaxf(mt, __uint_as_float(ml[k][s2][0]));
-                const float mref = mt == -INFINITY ? 0.f : mt;
-                float lt = 0.f;
+            for (int s2 = 0; s2 < SMAX; ++s2) {
+                // weight of split s2: its share of the row's softmax mass (0 past the splits)
+                const float w = s2 < splits ? __builtin_amdgcn_exp2f(__uint_as_float(ml[k][s2][0]) - mref) *
+                                                  __uint_as_float(ml[k][s2][1])
+                                            : 0.f;
+                lt += w;
 #pragma unroll
-                for (int s2 = 0; s2 < SMAX; ++s2) {
-                    if (s2 < splits) {
-                        // weight of split s2: its share of the row's softmax mass
-                        const float w = __builtin_amdgcn_exp2f(__uint_as_float(ml[k][s2][0]) - mref) *
-                                        __uint_as_float(ml[k][s2][1]);
-                        lt += w;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            acc[2 * e] += w * tmv::bf16_to_f32(static_cast<uint16_t>(ov[k][s2][e] & 0xffffu));
-                            acc[2 * e + 1] += w * tmv::bf16_to_f32(static_cast<uint16_t>(ov[k][s2][e] >> 16));
-                        }
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    acc[2 * e] += w * tmv::bf16_to_f32(static_cast<uint16_t>(ov[k][s2][e] & 0xffffu));
+                    acc[2 * e + 1] += w * tmv::bf16_to_f32(static_cast<uint16_t>(ov[k][s2][e] >> 16));
                 }
-                const float inv = lt > 0.f ? 1.f / lt : 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] *= inv;
             }
+            // inert rows are zeros whatever their partials hold
+            const bool live = seq_ok && r < M * g && dp[k] >= 1;
+            const float inv = lt > 0.f ? 1.f / lt : 0.f;
             uint32_t w4[4];
 #pragma unroll
             for (int h2 = 0; h2 < 4; ++h2)
-                w4[h2] = static_cast<uint32_t>(tmv::f32_to_bf16(acc[2 * h2])) |
-                         (static_cast<uint32_t>(tmv::f32_to_bf16(acc[2 * h2 + 1])) << 16);
+                w4[h2] = live ? static_cast<uint32_t>(tmv::f32_to_bf16(acc[2 * h2] * inv)) |
+                                    (static_cast<uint32_t>(tmv::f32_to_bf16(acc[2 * h2 + 1] * inv)) << 16)
+                              : 0u;
+            if (r >= rows_max) continue;
+            const int j = ((r * g_magic) >> 16) + 1, gi = r - (j - 1) * g;
             uint16_t *o = out + b * os0 + static_cast<int64_t>(j - 1) * os1 + static_cast<int64_t>(kvh * g + gi) * os2 + part * 8;
             *reinterpret_cast<uint4 *>(o) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
         }
@@ -1755,14 +1761,12 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         __syncthreads();
         if (s_last == 0) return;
         if (threadIdx.x == 0) __hip_atomic_store(ws_cnt + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // one round trip for the partials of up to 8 splits and up to 2 items per thread
-        constexpr int kIpt = (RB * (D / 8) + kThreads - 1) / kThreads;
         if (splits <= 8)
-            merge_block<D, RB, (kIpt < 2 ? kIpt : 2), 8>(unit, splits, smax, b, kvh, g, g_magic, row0_wg, M_max, L_cap, M, P, st,
-                                                          depth, out, os0, os1, os2, ws_stats, ws_o);
+            merge_block<D, RB, 8>(unit, splits, smax, b, kvh, g, g_magic, row0_wg, M_max, L_cap, M, P, st, depth, out, os0,
+                                  os1, os2, ws_stats, ws_o);
         else
-            merge_block<D, RB, 1, 16>(unit, splits, smax, b, kvh, g, g_magic, row0_wg, M_max, L_cap, M, P, st, depth, out, os0,
-                                      os1, os2, ws_stats, ws_o);
+            merge_block<D, RB, 16>(unit, splits, smax, b, kvh, g, g_magic, row0_wg, M_max, L_cap, M, P, st, depth, out, os0,
+                                   os1, os2, ws_stats, ws_o);
     };
     // row `rr` of the workgroup's block, dims d0 .. d0 + n - 1 (n a multiple of 8) of the
     // final output (splits == 1) from x / l, or zeros for inert rows

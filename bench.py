@@ -221,7 +221,7 @@ STAGE_KERNELS = {
     "build": ("build_ancestors_kernel",),
     "attention": ("tree_attn_bf16_kernel", "tree_attn_bf16_stream_kernel", "tree_attn_merge_kernel",
                   "tree_attn_f32_kernel"),
-    "accept": ("greedy_scan_kernel", "greedy_select_kernel", "sample_walk_kernel"),
+    "accept": ("greedy_accept_kernel", "sample_walk_kernel"),
     "commit": ("commit_kernel",),
 }
 

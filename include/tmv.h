@@ -19,11 +19,10 @@
  *     tensor's data_ptr), except the small int64 stride arrays, which are HOST arrays read
  *     during the call.  The library keeps no global state and allocates nothing; scratch
  *     memory comes from a caller workspace whose size the *_workspace call returns.  The
- *     attention and sampling workspaces hold counters: zero-fill them once before their
+ *     attention and accept workspaces hold counters: zero-fill them once before their
  *     first use; every completed call leaves them ready for the next call of any shape
- *     they are large enough for (after a TMV_ERR_DEVICE status, zero-fill again).  The
- *     greedy-accept workspace needs no initialisation.  Calls that may run at the same
- *     time (different streams) must not share a workspace.
+ *     they are large enough for (after a TMV_ERR_DEVICE status, zero-fill again).  Calls
+ *     that may run at the same time (different streams) must not share a workspace.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are asynchronous; none
  *     synchronises the host.
  *   - The return value reports problems the host can see (TMV_ERR_ARG: bad sizes, null
@@ -285,12 +284,20 @@ int tmv_tree_verify_attention_paged_plan(int dtype, int B, int M_max, int D_max,
  *              GREEDY.
  *   accept_len out int32 [B]; path out int32 [B][D_max] (node ids root->leaf, then 0);
  *   next_token out int32 [B].  All 0 for a failed sequence.
- *   workspace: tmv_tree_accept_workspace() bytes, 16-byte aligned.
+ *   workspace: tmv_tree_accept_workspace() bytes, 16-byte aligned.  Every completed call
+ *     leaves it zero; zero-fill it once before first use.
+ *     GREEDY: one workgroup per (sequence, row, 4096-entry chunk).  When they are all
+ *     resident at once (the kernel's occupancy times the compute units), one launch: per
+ *     (sequence, row) a key and an arrival counter, per sequence an arrival counter; a
+ *     row's chunks merge their argmax keys with a device-scope atomic maximum, the last
+ *     chunk of a row to arrive counts the row in, the last row of a sequence chooses its
+ *     path, and each counter and key is reset by whoever completes it.  Otherwise two
+ *     launches: the chunk keys are written to the workspace and a second kernel merges
+ *     them and chooses the paths.
  *     SAMPLE: one synchronisation block per sequence.  K workgroups walk a sequence
  *     together, one per vocabulary slice, and meet after every row pass; K = (the walk
  *     kernel's resident workgroups per compute unit x compute units) / B, at most 64, so the
  *     whole launch is resident on an otherwise idle device (the results do not depend on K).
- *     - Every completed call leaves the workspace zero; zero-fill it once before first use.
  *     - A workgroup that waits more than 2 ms for the other slices (kernels on other streams
  *       can hold compute units) gives up: the sequence ends with status TMV_ERR_DEVICE and
  *       zero outputs, every workgroup still exits, and the workspace is again left zero.

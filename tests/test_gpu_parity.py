@@ -217,7 +217,7 @@ def test_attention_determinism():
 
 
 def test_workspace_reuse_across_calls_and_shapes():
-    _case("attention: zero-filled workspace reused across shapes; greedy: garbage workspace")
+    _case("attention and greedy accept: zero-filled workspaces reused across calls and shapes")
     import tree_masked_verification_amd as tmv
     w = ti.workload(2)
     dev = DeviceStep(w)
@@ -235,21 +235,38 @@ def test_workspace_reuse_across_calls_and_shapes():
     # arrival counters must have come back to zero after every call
     ds = DeviceStep(small)
     ds.build()
+    # logits for the small shape: two vocabulary chunks, the second one partial
+    g = torch.Generator(device="cpu").manual_seed(208)
+    ds.logits = torch.randn((small.B, small.M_max + 1, 5000), generator=g).cuda()
+    ds.tokens = torch.randint(0, 5000, (small.B, small.M_max + 1), generator=g, dtype=torch.int32).cuda()
     for _ in range(2):
         ds.attention(workspace=wa)
+    ds.accept()
     torch.cuda.synchronize()
     s1 = host_bits(ds.out).copy()
-    n_acc = tmv.tree_accept_workspace(tmv.ACCEPT_GREEDY, w.B, w.M_max, w.V)
-    for fill in (0xFF, 0x7F, 0x00):
-        wc = torch.full((n_acc,), fill, dtype=torch.uint8, device="cuda")
+    s1_acc = [host_bits(t).copy() for t in (ds.accept_len, ds.path, ds.next_token)]
+    # the greedy accept's keys and counters: one zero-filled workspace for both shapes,
+    # left zero by every call
+    n_acc = max(tmv.tree_accept_workspace(tmv.ACCEPT_GREEDY, w.B, w.M_max, w.V),
+                tmv.tree_accept_workspace(tmv.ACCEPT_GREEDY, small.B, small.M_max, 5000))
+    wc = torch.zeros(n_acc, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
         dev.out.fill_(float("nan"))
+        dev.accept_len.fill_(-7)
         dev.attention(workspace=wa)
         dev.accept(workspace=wc)
+        torch.cuda.synchronize()
         assert np.array_equal(host_bits(dev.out), ref_out)
         assert all(np.array_equal(host_bits(t), r) for t, r in zip((dev.accept_len, dev.path, dev.next_token), ref_acc))
+        assert int(wc.count_nonzero()) == 0
         ds.out.fill_(float("nan"))
+        ds.accept_len.fill_(-7)
         ds.attention(workspace=wa)
+        ds.accept(workspace=wc)
+        torch.cuda.synchronize()
         assert np.array_equal(host_bits(ds.out), s1)
+        assert all(np.array_equal(host_bits(t), r) for t, r in zip((ds.accept_len, ds.path, ds.next_token), s1_acc))
+        assert int(wc.count_nonzero()) == 0
 
 
 def test_attention_after_kernels_of_odd_grid_sizes(ref):

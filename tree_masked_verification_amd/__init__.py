@@ -301,8 +301,7 @@ def tree_accept(mode, tokens, teacher, n_nodes, anc, depth, status, accept_len, 
     else:
         qs = (0, 0)
     if workspace is None:
-        workspace = _temp_workspace(tree_accept_workspace(mode, B, R - 1, V), teacher.device, stream,
-                                    zero=(mode == ACCEPT_SAMPLE))
+        workspace = _temp_workspace(tree_accept_workspace(mode, B, R - 1, V), teacher.device, stream, zero=True)
     args = (mode, B, R - 1, D_max, V, _ptr(tokens), _dtype_code(teacher), _ptr(teacher), teacher.stride(0),
             teacher.stride(1), _ptr(draft_q), qs[0], qs[1], ctypes.c_uint64(seed), ctypes.c_uint64(step), _ptr(n_nodes),
             _ptr(anc), _ptr(depth), _ptr(status), _ptr(accept_len), _ptr(path), _ptr(next_token), _ptr(workspace),

@@ -5,9 +5,14 @@
 //   the longest valid branch is kept).  The row scans are the HBM-bound part: one
 //   workgroup per (sequence, row, vocabulary chunk) reads its chunk with 16-byte loads
 //   and reduces it to a 64-bit key (order-preserving value bits << 32 | ~index, -0 keyed
-//   as +0), so max() gives the largest value and, on ties, the smallest index.  A second
-//   kernel (one workgroup per sequence, ordered after the scan on the stream) merges the
-//   chunk keys and picks the path -- no cross-workgroup synchronisation inside a kernel.
+//   as +0), so max() gives the largest value and, on ties, the smallest index.  When the
+//   whole scan is resident on the device at once, the keys meet in one 64-bit device-scope
+//   atomic maximum per row, the last chunk of a row to arrive counts the row in for its
+//   sequence, and the last row of a sequence chooses the path in the same launch (counters
+//   only: no workgroup ever waits for another).  Larger scans write one key per chunk and
+//   a second kernel (one workgroup per sequence, ordered after the scan on the stream)
+//   merges them and picks the path: there the per-workgroup atomics would lengthen every
+//   round of resident workgroups.
 // SAMPLE: modified rejection sampling (same page, its rejection-sampling section and
 //   FAQ), children of the current node tried in ascending id against the running
 //   residual, which against one draft row keeps the form (p - c q)+.  Exact integer fixed
@@ -28,6 +33,10 @@ constexpr int kScanThreads = 256;
 constexpr int kScanChunk = 4096;          // vocabulary entries per workgroup (four 16-byte fp32 loads per thread)
 constexpr uint64_t kNanKey = ~0ull;       // a chunk with a NaN reports the all-ones key
 constexpr int kSelectBatch = 8;           // chunk keys per thread in flight in the path choice
+// greedy workspace: [one-launch part: per (sequence, row) a 64-bit key and an arrival
+// counter, per sequence an arrival counter, each on a 128-byte line of its own (atomics
+// on one line serialise); zero between calls] [two-launch part: the chunk keys]
+constexpr int kSlot = 128;
 
 __device__ __forceinline__ uint32_t order_bits(float v) {
     const uint32_t u = __float_as_uint(v);
@@ -164,29 +173,17 @@ __device__ __forceinline__ void choose_path_from(const PathInputs &in, int b, in
     }
 }
 
-// One workgroup per (sequence, row, chunk of kScanChunk entries): the chunk's key.  The
-// liveness words (status, n_nodes, the row's depth) are read first and a dead row loads
-// nothing of its logits.  In a whole, aligned chunk each thread's values are reduced in
-// ascending index order by a running maximum under a strict comparison (the first of
-// equal values is kept, -0 equals +0, NaN fails every comparison and is flagged on its
-// own) and the 64-bit key is formed once per thread.
+// The 64-bit key of chunk `chunk` of row u of sequence b (kScanChunk entries), returned to
+// thread 0.  In a whole, aligned chunk each thread's values are reduced in ascending index
+// order by a running maximum under a strict comparison (the first of equal values is kept,
+// -0 equals +0, NaN fails every comparison and is flagged on its own) and the key is formed
+// once per thread; the all-ones key reports a NaN.
 template <int DT>
-__global__ void __launch_bounds__(kScanThreads)
-greedy_scan_kernel(int M_max, int V, int nchunk, const void *__restrict__ teacher, int64_t sb, int64_t sr,
-                   const int32_t *__restrict__ n_nodes, const int32_t *__restrict__ depth,
-                   const int32_t *__restrict__ status, uint64_t *__restrict__ keys)
+__device__ __forceinline__ uint64_t chunk_key(int V, const void *__restrict__ teacher, int64_t sb, int64_t sr, int b,
+                                              int u, int chunk)
 {
     __shared__ uint64_t red[kScanThreads / kWave];
-    const int R = M_max + 1;
-    const int chunk = blockIdx.x % nchunk;
-    const int u = (blockIdx.x / nchunk) % R;
-    const int b = blockIdx.x / (nchunk * R);
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
-    const int M = n_nodes[b];
-    const int st = status[b];
-    const int dp = u > 0 ? depth[static_cast<int64_t>(b) * R + u] : 1;
-    if (st != TMV_OK || M < 0 || M > M_max || u > M || dp < 1) return;
-
     constexpr int kElem = DT == TMV_F32 ? 4 : 2;
     const int x0 = chunk * kScanChunk;
     const int x1 = min(V, x0 + kScanChunk);
@@ -230,14 +227,33 @@ greedy_scan_kernel(int M_max, int V, int nchunk, const void *__restrict__ teache
     best = tmv::wave_max_u64(best);
     if (lane == 0) red[wv] = best;
     __syncthreads();
-    if (tid == 0) {
-        uint64_t k = red[0];
-        for (int w = 1; w < kScanThreads / kWave; ++w) k = red[w] > k ? red[w] : k;
-        keys[(static_cast<int64_t>(b) * R + u) * nchunk + chunk] = k;
-    }
+    uint64_t k = red[0];
+    for (int w = 1; w < kScanThreads / kWave; ++w) k = red[w] > k ? red[w] : k;
+    return k;
 }
 
-// One workgroup per sequence, after the scan: the chunk keys of the sequence ([row][chunk],
+// Two launches, first: one workgroup per (sequence, row, chunk of kScanChunk entries) writes
+// the chunk's key.  The liveness words (status, n_nodes, the row's depth) are read first and
+// a dead row loads nothing of its logits.
+template <int DT>
+__global__ void __launch_bounds__(kScanThreads)
+greedy_scan_kernel(int M_max, int V, int nchunk, const void *__restrict__ teacher, int64_t sb, int64_t sr,
+                   const int32_t *__restrict__ n_nodes, const int32_t *__restrict__ depth,
+                   const int32_t *__restrict__ status, uint64_t *__restrict__ keys)
+{
+    const int R = M_max + 1;
+    const int chunk = blockIdx.x % nchunk;
+    const int u = (blockIdx.x / nchunk) % R;
+    const int b = blockIdx.x / (nchunk * R);
+    const int M = n_nodes[b];
+    const int st = status[b];
+    const int dp = u > 0 ? depth[static_cast<int64_t>(b) * R + u] : 1;
+    if (st != TMV_OK || M < 0 || M > M_max || u > M || dp < 1) return;
+    const uint64_t k = chunk_key<DT>(V, teacher, sb, sr, b, u, chunk);
+    if (threadIdx.x == 0) keys[(static_cast<int64_t>(b) * R + u) * nchunk + chunk] = k;
+}
+
+// Two launches, second: one workgroup per sequence, after the scan: the chunk keys of the sequence ([row][chunk],
 // contiguous) are read by all threads in coalesced batches, issued together with the
 // per-row reads of the path choice, and merged per row with LDS atomics; then the path is
 // chosen.  Keys of rows beyond n_nodes were not written in this call and are not read;
@@ -282,6 +298,80 @@ greedy_select_kernel(int M_max, int D_max, int V, int nchunk, const int32_t *__r
     }
     __syncthreads();
     choose_path_from(in, b, M_max, D_max, V, rowkey[tid < R ? tid : 0], status, accept_len, path, next_token, anc,
+                     static_cast<int32_t *>(nullptr));
+}
+
+// The greedy accept in one launch (the whole grid resident at once): one workgroup per
+// (sequence, row, chunk), liveness as in greedy_scan_kernel.  Then:
+//   * the chunk's key goes into the row's key by a device-scope atomic maximum, and once
+//     that has completed the workgroup counts itself in on the row's counter;
+//   * the last chunk of a live row to arrive (and chunk 0 of a dead row, at once) counts
+//     the row in on the sequence's counter;
+//   * the last row of the sequence to arrive reads every row key with agent-coherent loads
+//     and chooses the path.
+// Every counter is reset by the workgroup that completes it and every row key by the
+// chooser, so a zero-filled workspace is left zero by each call.
+template <int DT>
+__global__ void __launch_bounds__(kScanThreads)
+greedy_accept_kernel(int M_max, int D_max, int V, int nchunk, const void *__restrict__ teacher, int64_t sb,
+                     int64_t sr, const int32_t *__restrict__ tokens, const int32_t *__restrict__ n_nodes,
+                     const int32_t *__restrict__ anc, const int32_t *__restrict__ depth,
+                     int32_t *__restrict__ status, int32_t *__restrict__ accept_len, int32_t *__restrict__ path,
+                     int32_t *__restrict__ next_token, char *__restrict__ ws)
+{
+    __shared__ int s_flag;
+    const int R = M_max + 1;
+    const int chunk = blockIdx.x % nchunk;
+    const int u = (blockIdx.x / nchunk) % R;
+    const int b = blockIdx.x / (nchunk * R);
+    const int tid = threadIdx.x;
+    const int B = gridDim.x / (nchunk * R);
+    unsigned long long *row_key = reinterpret_cast<unsigned long long *>(ws + (static_cast<int64_t>(b) * R + u) * kSlot);
+    int32_t *row_cnt = reinterpret_cast<int32_t *>(ws + (static_cast<int64_t>(B) * R + static_cast<int64_t>(b) * R + u) * kSlot);
+    int32_t *seq_cnt = reinterpret_cast<int32_t *>(ws + (2 * static_cast<int64_t>(B) * R + b) * kSlot);
+    const int M = n_nodes[b];
+    const int st = status[b];
+    const int dp = u > 0 ? depth[static_cast<int64_t>(b) * R + u] : 1;
+    const bool live = st == TMV_OK && M >= 0 && M <= M_max && u <= M && dp >= 1;
+    if (!live && chunk != 0) return;
+
+    if (live) {
+        const uint64_t k = chunk_key<DT>(V, teacher, sb, sr, b, u, chunk);
+        if (tid == 0) {
+            // the maximum has been performed (its old value has returned, the returning form)
+            // before the arrival is counted, so the row's last arrival finds every chunk's key
+            // in the row key
+            const unsigned long long old_k = __hip_atomic_fetch_max(row_key, static_cast<unsigned long long>(k),
+                                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            asm volatile("" ::"v"(old_k));
+            const int old = __hip_atomic_fetch_add(row_cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const bool last = old == nchunk - 1;
+            if (last) __hip_atomic_store(row_cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_flag = last ? 1 : 0;
+        }
+        __syncthreads();
+        if (s_flag == 0) return;
+    }
+    // this row is complete (or dead): count it in for the sequence; the last row chooses.
+    // (The path inputs are read first, so their loads travel with the arrival.)
+    const PathInputs in = load_path_inputs(b, M_max, D_max, tokens, n_nodes, anc, depth, status);
+    if (tid == 0) {
+        const int old = __hip_atomic_fetch_add(seq_cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = old == R - 1;
+        if (last) __hip_atomic_store(seq_cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_flag = last ? 2 : 0;
+    }
+    __syncthreads();
+    if (s_flag != 2) return;
+    // every row of the sequence has arrived: its keys are final (dead rows' stay zero)
+    uint64_t krow = 0;
+    if (tid < R) {
+        unsigned long long *rk = reinterpret_cast<unsigned long long *>(ws + (static_cast<int64_t>(b) * R + tid) * kSlot);
+        krow = __hip_atomic_load(rk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(rk, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    choose_path_from(in, b, M_max, D_max, V, krow, status, accept_len, path, next_token, anc,
                      static_cast<int32_t *>(nullptr));
 }
 
@@ -1184,6 +1274,31 @@ sample_walk_kernel(int M_max, int D_max, int V, int K,
 
 }  // namespace
 
+// greedy workspace, one-launch part: keys and counters (all zero between calls)
+static size_t greedy_fused_bytes(int B, int M_max) {
+    return (2 * static_cast<size_t>(B) * (M_max + 1) + B) * kSlot;
+}
+
+// workgroups of the one-launch greedy kernel resident at once on an otherwise idle device
+// (its occupancy per compute unit times the compute units); larger scans take two launches
+static int64_t greedy_resident() {
+    static std::mutex mu;
+    static int64_t cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cached[dev] == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, reinterpret_cast<const void *>(&greedy_accept_kernel<TMV_F32>), kScanThreads, 0) != hipSuccess ||
+            per_cu < 1)
+            per_cu = 1;
+        cached[dev] = static_cast<int64_t>(cus) * per_cu;
+    }
+    return cached[dev];
+}
+
 // sampling workspace: one synchronisation block per sequence (all zero between calls)
 static size_t sample_ws_bytes(int B) {
     return static_cast<size_t>(B) * sizeof(SeqSync) + 256;
@@ -1221,7 +1336,7 @@ extern "C" size_t tmv_tree_accept_workspace(int mode, int B, int M_max, int V)
     if (B <= 0 || M_max < 0 || V <= 0) return 256;
     if (mode == TMV_ACCEPT_GREEDY) {
         const int nchunk = (V + kScanChunk - 1) / kScanChunk;
-        return static_cast<size_t>(B) * (M_max + 1) * nchunk * sizeof(uint64_t) + 256;
+        return greedy_fused_bytes(B, M_max) + static_cast<size_t>(B) * (M_max + 1) * nchunk * sizeof(uint64_t) + 256;
     }
     return sample_ws_bytes(B);
 }
@@ -1252,7 +1367,18 @@ extern "C" int tmv_tree_accept_wait(int mode, int B, int M_max, int D_max, int V
         const int nchunk = (V + kScanChunk - 1) / kScanChunk;
         const int64_t blocks = static_cast<int64_t>(B) * (M_max + 1) * nchunk;
         if (blocks > 0x7fffffff) return TMV_ERR_ARG;
-        uint64_t *keys = reinterpret_cast<uint64_t *>(ws);
+        if (blocks <= greedy_resident()) {
+            if (row_dtype == TMV_F32)
+                hipLaunchKernelGGL(greedy_accept_kernel<TMV_F32>, dim3(static_cast<unsigned>(blocks)), dim3(kScanThreads),
+                                   0, s, M_max, D_max, V, nchunk, teacher, t_stride_b, t_stride_row, tokens, n_nodes, anc,
+                                   depth, status, accept_len, path, next_token, ws);
+            else
+                hipLaunchKernelGGL(greedy_accept_kernel<TMV_BF16>, dim3(static_cast<unsigned>(blocks)), dim3(kScanThreads),
+                                   0, s, M_max, D_max, V, nchunk, teacher, t_stride_b, t_stride_row, tokens, n_nodes, anc,
+                                   depth, status, accept_len, path, next_token, ws);
+            return tmv_host::launch_status(hipGetLastError());
+        }
+        uint64_t *keys = reinterpret_cast<uint64_t *>(ws + greedy_fused_bytes(B, M_max));
         if (row_dtype == TMV_F32)
             hipLaunchKernelGGL(greedy_scan_kernel<TMV_F32>, dim3(static_cast<unsigned>(blocks)), dim3(kScanThreads), 0, s,
                                M_max, V, nchunk, teacher, t_stride_b, t_stride_row, n_nodes, depth, status, keys);

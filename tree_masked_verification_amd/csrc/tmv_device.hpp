@@ -30,6 +30,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return static_cast<uint16_t>(u >> 16);
 }
 
+// two floats to a packed bf16 pair (low half first), round to nearest even, by the hardware
+// conversion (v_cvt_pk_bf16_f32): equal to f32_to_bf16 for every non-NaN value
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 // ---------------------------------------------------------------- wave reductions
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

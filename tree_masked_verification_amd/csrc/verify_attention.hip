@@ -773,7 +773,7 @@ tree_attn_bf16_stream_kernel(int M_max, int D_max, int Hq, int Hkv,
                 const int d0 = e + 2 * h2, d1 = d0 + 1;
                 const float x0 = live ? oacc[rt][d0 % NT][d0 / NT] * inv : 0.f;
                 const float x1 = live ? oacc[rt][d1 % NT][d1 / NT] * inv : 0.f;
-                w4[h2] = static_cast<uint32_t>(tmv::f32_to_bf16(x0)) | (static_cast<uint32_t>(tmv::f32_to_bf16(x1)) << 16);
+                w4[h2] = tmv::pack_bf16x2(x0, x1);
             }
             *reinterpret_cast<uint4 *>(o + e) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
         }
@@ -815,85 +815,106 @@ struct PagedArgs {
 
 // The merging workgroup of a split-KV row block (LDS-ring kernel).  Split s left, per row
 // of the block, (m, l) in fp32 -- m the row's largest score in base-2 units, l the sum of
-// 2^(score - m) -- and the row's output normalised by l, rounded to bf16.  A thread merges
-// items (row rr, dims part*8 .. +8), IPB at a time: every split's (m, l) and 16-byte O slice
-// of those items, and the rows' depths, are loaded in one straight batch with
-// agent-coherent loads (the partials were written by other workgroups, on any XCD, with
-// agent-coherent stores), then merged in split order, so the result does not depend on
-// which split arrived last.  The buffer descriptors end at the `splits`-th partial: loads of
+// 2^(score - m) -- and the row's output normalised by l, rounded to bf16.  Every (split,
+// row) statistic is loaded once and shared through LDS (lds_ml, RB * SMAX pairs); a thread
+// merges items (row rr, dims part*8 .. +8), two at a time: the rows' depths and every
+// split's 16-byte O slice of those items are loaded in one straight batch (the first batch
+// right after the statistics, so these are staged while it travels), then merged in split
+// order, so the result does not depend on which split arrived last.  All loads are
+// agent-coherent (the partials were written by other workgroups, on any XCD, with
+// agent-coherent stores).  The buffer descriptors end at the `splits`-th partial: loads of
 // splits past it return zeros without touching memory and are left out of the merge.
 template <int D, int RB, int SMAX>
-__device__ __forceinline__ void merge_block(int64_t unit, int splits, int stride, int b, int kvh, int g, int g_magic, int row0_wg, int M_max,
-                                            int L_cap, int M, int P, int st, const int32_t *__restrict__ depth,
-                                            uint16_t *__restrict__ out, int64_t os0, int64_t os1, int64_t os2,
-                                            const float *__restrict__ ws_stats, const uint16_t *__restrict__ ws_o)
+__device__ __forceinline__ void merge_block(int64_t unit, int splits, int stride, int b, int kvh, int g, int g_magic,
+                                            int row0_wg, int M_max, int L_cap, int M, int P, int st,
+                                            const int32_t *__restrict__ depth, uint16_t *__restrict__ out,
+                                            int64_t os0, int64_t os1, int64_t os2, const float *__restrict__ ws_stats,
+                                            const uint16_t *__restrict__ ws_o, float *__restrict__ lds_ml)
 {
     constexpr int kThreads = kRingWaves * kWave;
     constexpr int kItems = RB * (D / 8);
     static_assert(kItems % kThreads == 0, "whole items per thread");
     constexpr int kIpt = kItems / kThreads;            // items per thread
-    constexpr int IPB = kIpt < 2 ? kIpt : 2;           // items per batch of loads
+    constexpr int kPairs = RB * SMAX;                  // (split, row) statistics of the block
+    static_assert(kPairs % kThreads == 0, "whole statistics per thread");
+    constexpr int kPpt = kPairs / kThreads;
     const __amdgpu_buffer_rsrc_t rst = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float *>(ws_stats + unit * stride * RB * 2), 0, splits * RB * 2 * 4, kBufferFlags);
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(ws_o + unit * stride * RB * D), 0, splits * RB * D * 2, kBufferFlags);
     const bool seq_ok = st == TMV_OK && M >= 0 && M <= M_max && P >= 0 && static_cast<int64_t>(P) + M <= L_cap;
     const int rows_max = M_max * g;
-#pragma unroll 1
-    for (int i0 = 0; i0 < kIpt; i0 += IPB) {
-        u32x2_t ml[IPB][SMAX];
-        u32x4_t ov[IPB][SMAX];
-        int dp[IPB];
+    const int tid = static_cast<int>(threadIdx.x);
+    // pair i*kThreads + tid is (split, row) = (pidx / RB, pidx % RB): the partials' own order
+    u32x2_t mlp[kPpt];
+#pragma unroll
+    for (int i = 0; i < kPpt; ++i) mlp[i] = __builtin_amdgcn_raw_buffer_load_b64(rst, (i * kThreads + tid) * 8, 0, kCoherent);
+    // items in batches of IPB per thread: the rows' depths and every split's O slices
+    constexpr int IPB = kIpt < 2 ? kIpt : 2;
+    u32x4_t ov[IPB][SMAX];
+    int dp[IPB];
+    auto load_batch = [&](int i0) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < IPB; ++k) {
-            const int item = (i0 + k) * kThreads + static_cast<int>(threadIdx.x);
+            const int item = (i0 + k) * kThreads + tid;
             const int rr = item / (D / 8), part = item % (D / 8);
-#pragma unroll
-            for (int s2 = 0; s2 < SMAX; ++s2) {
-                const int row = s2 * RB + rr;
-                ml[k][s2] = __builtin_amdgcn_raw_buffer_load_b64(rst, row * 8, 0, kCoherent);
-                ov[k][s2] = __builtin_amdgcn_raw_buffer_load_b128(ro, (row * D + part * 8) * 2, 0, kCoherent);
-            }
             int r = row0_wg + rr;
             r = r < rows_max ? r : rows_max - 1;
             dp[k] = depth[static_cast<int64_t>(b) * (M_max + 1) + ((r * g_magic) >> 16) + 1];
+#pragma unroll
+            for (int s2 = 0; s2 < SMAX; ++s2)
+                ov[k][s2] = __builtin_amdgcn_raw_buffer_load_b128(ro, ((s2 * RB + rr) * D + part * 8) * 2, 0, kCoherent);
         }
+    };
+    load_batch(0);
+    // the statistics, row-major ([row][split]) in LDS, while the first batch travels
+#pragma unroll
+    for (int i = 0; i < kPpt; ++i) {
+        const int pidx = i * kThreads + tid, s2 = pidx / RB, rr = pidx % RB;
+        *reinterpret_cast<u32x2_t *>(lds_ml + (rr * SMAX + s2) * 2) = mlp[i];
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int i0 = 0; i0 < kIpt; i0 += IPB) {
+        if (i0 > 0) load_batch(i0);
 #pragma unroll
         for (int k = 0; k < IPB; ++k) {
-            const int item = (i0 + k) * kThreads + static_cast<int>(threadIdx.x);
+            const int item = (i0 + k) * kThreads + tid;
             const int rr = item / (D / 8), part = item % (D / 8);
             const int r = row0_wg + rr;
-            // (computed for every item, live or not, and selected at the end: a branch on
-            // liveness would let the compiler sink the partial loads behind the depth load)
+            float2 ml[SMAX];
+#pragma unroll
+            for (int s2 = 0; s2 < SMAX; s2 += 2) {
+                const float4 x = *reinterpret_cast<const float4 *>(lds_ml + (rr * SMAX + s2) * 2);
+                ml[s2] = make_float2(x.x, x.y);
+                ml[s2 + 1] = make_float2(x.z, x.w);
+            }
             float mt = -INFINITY;
 #pragma unroll
             for (int s2 = 0; s2 < SMAX; ++s2)
-                if (s2 < splits) mt = fmaxf(mt, __uint_as_float(ml[k][s2][0]));
+                if (s2 < splits) mt = fmaxf(mt, ml[s2].x);
             const float mref = mt == -INFINITY ? 0.f : mt;
             float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             float lt = 0.f;
 #pragma unroll
             for (int s2 = 0; s2 < SMAX; ++s2) {
                 // weight of split s2: its share of the row's softmax mass (0 past the splits)
-                const float w = s2 < splits ? __builtin_amdgcn_exp2f(__uint_as_float(ml[k][s2][0]) - mref) *
-                                                  __uint_as_float(ml[k][s2][1])
-                                            : 0.f;
+                const float w = s2 < splits ? __builtin_amdgcn_exp2f(ml[s2].x - mref) * ml[s2].y : 0.f;
                 lt += w;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    acc[2 * e] += w * tmv::bf16_to_f32(static_cast<uint16_t>(ov[k][s2][e] & 0xffffu));
-                    acc[2 * e + 1] += w * tmv::bf16_to_f32(static_cast<uint16_t>(ov[k][s2][e] >> 16));
+                    acc[2 * e] += w * __uint_as_float(ov[k][s2][e] << 16);
+                    acc[2 * e + 1] += w * __uint_as_float(ov[k][s2][e] & 0xffff0000u);
                 }
             }
-            // inert rows are zeros whatever their partials hold
+            // inert rows are zeros whatever their partials hold (computed for every item, live
+            // or not, and selected at the end: a branch on liveness would let the compiler sink
+            // the partial loads behind the depth load)
             const bool live = seq_ok && r < M * g && dp[k] >= 1;
             const float inv = lt > 0.f ? 1.f / lt : 0.f;
             uint32_t w4[4];
 #pragma unroll
-            for (int h2 = 0; h2 < 4; ++h2)
-                w4[h2] = live ? static_cast<uint32_t>(tmv::f32_to_bf16(acc[2 * h2] * inv)) |
-                                    (static_cast<uint32_t>(tmv::f32_to_bf16(acc[2 * h2 + 1] * inv)) << 16)
-                              : 0u;
+            for (int h2 = 0; h2 < 4; ++h2) w4[h2] = live ? tmv::pack_bf16x2(acc[2 * h2] * inv, acc[2 * h2 + 1] * inv) : 0u;
             if (r >= rows_max) continue;
             const int j = ((r * g_magic) >> 16) + 1, gi = r - (j - 1) * g;
             uint16_t *o = out + b * os0 + static_cast<int64_t>(j - 1) * os1 + static_cast<int64_t>(kvh * g + gi) * os2 + part * 8;
@@ -1722,7 +1743,8 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
                                               : f32x4_t{-mref[rt], -mref[rt], -mref[rt], -mref[rt]};
         }
     }
-    __syncthreads();
+    // (the pass loop is only left through the block-wide __syncthreads_or above: every wave
+    // has finished reading the ring, so no further barrier is needed before it is reused)
     clear_tail();
     float mrow[2];
 #pragma unroll
@@ -1761,12 +1783,13 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         __syncthreads();
         if (s_last == 0) return;
         if (threadIdx.x == 0) __hip_atomic_store(ws_cnt + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // (the ring is idle: the merge stages the statistics in its first group)
         if (splits <= 8)
             merge_block<D, RB, 8>(unit, splits, smax, b, kvh, g, g_magic, row0_wg, M_max, L_cap, M, P, st, depth, out, os0,
-                                  os1, os2, ws_stats, ws_o);
+                                  os1, os2, ws_stats, ws_o, reinterpret_cast<float *>(ring0));
         else
             merge_block<D, RB, 16>(unit, splits, smax, b, kvh, g, g_magic, row0_wg, M_max, L_cap, M, P, st, depth, out, os0,
-                                   os1, os2, ws_stats, ws_o);
+                                   os1, os2, ws_stats, ws_o, reinterpret_cast<float *>(ring0));
     };
     // row `rr` of the workgroup's block, dims d0 .. d0 + n - 1 (n a multiple of 8) of the
     // final output (splits == 1) from x / l, or zeros for inert rows
@@ -1782,7 +1805,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
 #pragma unroll
             for (int h2 = 0; h2 < 4; ++h2) {
                 const float x0 = live ? x[e + 2 * h2] * inv : 0.f, x1 = live ? x[e + 2 * h2 + 1] * inv : 0.f;
-                w4[h2] = static_cast<uint32_t>(tmv::f32_to_bf16(x0)) | (static_cast<uint32_t>(tmv::f32_to_bf16(x1)) << 16);
+                w4[h2] = tmv::pack_bf16x2(x0, x1);
             }
             *reinterpret_cast<uint4 *>(o + e) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
         }
@@ -1848,8 +1871,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
                 u32x4_t x;
 #pragma unroll
                 for (int h2 = 0; h2 < 4; ++h2)
-                    x[h2] = static_cast<uint32_t>(tmv::f32_to_bf16(acc[e + 2 * h2] * inv)) |
-                            (static_cast<uint32_t>(tmv::f32_to_bf16(acc[e + 2 * h2 + 1] * inv)) << 16);
+                    x[h2] = tmv::pack_bf16x2(acc[e + 2 * h2] * inv, acc[e + 2 * h2 + 1] * inv);
                 __builtin_amdgcn_raw_buffer_store_b128(x, part_o, ((base + rr) * D + d0 + e) * 2, 0, kCoherent);
             }
             if ((lane % LPR) == 0) {
@@ -1870,10 +1892,8 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
                 const float inv = lrow[rt] > 0.f ? 1.f / lrow[rt] : 0.f;
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
-                    const u32x2_t x = {static_cast<uint32_t>(tmv::f32_to_bf16(oacc[rt][nt][0] * inv)) |
-                                           (static_cast<uint32_t>(tmv::f32_to_bf16(oacc[rt][nt][1] * inv)) << 16),
-                                       static_cast<uint32_t>(tmv::f32_to_bf16(oacc[rt][nt][2] * inv)) |
-                                           (static_cast<uint32_t>(tmv::f32_to_bf16(oacc[rt][nt][3] * inv)) << 16)};
+                    const u32x2_t x = {tmv::pack_bf16x2(oacc[rt][nt][0] * inv, oacc[rt][nt][1] * inv),
+                                       tmv::pack_bf16x2(oacc[rt][nt][2] * inv, oacc[rt][nt][3] * inv)};
                     __builtin_amdgcn_raw_buffer_store_b64(x, part_o, ((base + rr) * D + nt * 16 + 4 * G) * 2, 0, kCoherent);
                 }
                 if (G == 0) {
@@ -1896,9 +1916,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
             for (int nt = 0; nt < NT; ++nt) {
                 const float x0 = live ? oacc[rt][nt][0] * inv : 0.f, x1 = live ? oacc[rt][nt][1] * inv : 0.f;
                 const float x2 = live ? oacc[rt][nt][2] * inv : 0.f, x3 = live ? oacc[rt][nt][3] * inv : 0.f;
-                *reinterpret_cast<uint2 *>(o + nt * 16) =
-                    make_uint2(static_cast<uint32_t>(tmv::f32_to_bf16(x0)) | (static_cast<uint32_t>(tmv::f32_to_bf16(x1)) << 16),
-                               static_cast<uint32_t>(tmv::f32_to_bf16(x2)) | (static_cast<uint32_t>(tmv::f32_to_bf16(x3)) << 16));
+                *reinterpret_cast<uint2 *>(o + nt * 16) = make_uint2(tmv::pack_bf16x2(x0, x1), tmv::pack_bf16x2(x2, x3));
             }
         }
     }

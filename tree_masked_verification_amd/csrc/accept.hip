@@ -97,10 +97,11 @@ __device__ __forceinline__ void choose_path_from(const PathInputs &in, int b, in
                                                  int32_t *__restrict__ next_token, const int32_t *__restrict__ anc,
                                                  int32_t *__restrict__ row_argmax)
 {
-    __shared__ int32_t tsel[129], tok_sh[129];
+    __shared__ int32_t tsel[129];
     __shared__ int32_t anc_sh[129][kAncBatch];     // every row's first ancestor entries
+    __shared__ uint64_t match_w[3];                // bit u: node u's token is its parent row's choice
     __shared__ int bad;
-    __shared__ uint64_t best_node[kScanThreads / kWave];
+    __shared__ uint32_t best;
     const int R = M_max + 1, W = D_max + 1;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
     const int M = in.M, st_in = in.st_in, tok = in.tok, dep = in.dep;
@@ -111,9 +112,11 @@ __device__ __forceinline__ void choose_path_from(const PathInputs &in, int b, in
     // it is rejected here so that no row beyond the tables is ever addressed
     const int st = (st_in == TMV_OK && (M < 0 || M > M_max)) ? TMV_ERR_INPUT : st_in;
     int32_t *pth = path + static_cast<int64_t>(b) * D_max;
-    if (tid == 0) bad = st != TMV_OK;
+    if (tid == 0) {
+        bad = st != TMV_OK;
+        best = 0u;
+    }
     if (tid < R) {
-        tok_sh[tid] = tok;
 #pragma unroll
         for (int k = 0; k < kAncBatch; ++k) anc_sh[tid][k] = in.a8[k];
     }
@@ -135,36 +138,36 @@ __device__ __forceinline__ void choose_path_from(const PathInputs &in, int b, in
         }
         return;
     }
-    // node i matches iff every node c on its path has token == t(parent(c)); the chosen
-    // node maximises (depth, -id): key = depth << 8 | (255 - id)
-    uint64_t key = 0;
-    if (tid >= 1 && tid <= M && dep >= 1) {
+    // node u (live, depth >= 1) matches its parent row when its token is that row's choice;
+    // anc[u][1] is the parent (0: the root).  One ballot word per wave of rows.
+    const bool node = tid >= 1 && tid <= M && dep >= 1;
+    const bool m = node && tok == tsel[node ? in.a8[1] : 0];
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(m);
+    if (lane == 0 && wv < 3) match_w[wv] = bal;
+    __syncthreads();
+    // node u is accepted iff every node on its path matches (the path is u's ancestor-or-self
+    // row up to its depth); the chosen node maximises (depth, -id): key = depth << 8 | (255 - id)
+    if (node) {
+        const uint64_t w0 = match_w[0], w1 = match_w[1], w2 = match_w[2];
+        auto bit = [&](int a) {
+            const uint64_t w = a < 64 ? w0 : a < 128 ? w1 : w2;
+            return ((w >> (a & 63)) & 1ull) != 0;
+        };
         bool ok = true;
 #pragma unroll
-        for (int k = 0; k < kAncBatch; ++k) {
-            if (k < dep) {
-                const int parent = k + 1 < kAncBatch ? in.a8[k + 1] : arow[k + 1];
-                ok = ok && tok_sh[in.a8[k]] == tsel[k + 1 < dep ? parent : 0];
-            }
-        }
-        for (int k = kAncBatch; k < dep && ok; ++k)
-            ok = tok_sh[arow[k]] == tsel[arow[k + 1]];
-        if (ok) key = (static_cast<uint64_t>(dep) << 8) | static_cast<uint64_t>(255 - tid);
+        for (int k = 0; k < kAncBatch; ++k)
+            if (k < dep) ok = ok & bit(in.a8[k]);
+        for (int k = kAncBatch; k < dep && ok; ++k) ok = bit(arow[k]);
+        if (ok) atomicMax(&best, (static_cast<uint32_t>(dep) << 8) | static_cast<uint32_t>(255 - tid));
     }
-    key = tmv::wave_max_u64(key);
-    if (lane == 0) best_node[wv] = key;
     __syncthreads();
+    const uint32_t kb = best;
+    const int star = kb ? 255 - static_cast<int>(kb & 255u) : 0;
+    const int dstar = static_cast<int>(kb >> 8);
     if (tid == 0) {
-        uint64_t k = best_node[0];
-        for (int w = 1; w < kScanThreads / kWave; ++w) k = best_node[w] > k ? best_node[w] : k;
-        const int star = k ? 255 - static_cast<int>(k & 255u) : 0;
-        const int dstar = static_cast<int>(k >> 8);
-        best_node[0] = (static_cast<uint64_t>(dstar) << 32) | static_cast<uint32_t>(star);
         accept_len[b] = dstar;
         next_token[b] = tsel[star];
     }
-    __syncthreads();
-    const int dstar = static_cast<int>(best_node[0] >> 32), star = static_cast<int>(best_node[0] & 0xffffffffu);
     // the path root -> leaf is the chosen node's ancestor row read backwards; its first
     // kAncBatch entries are already in LDS
     for (int j = tid; j < D_max; j += kScanThreads) {

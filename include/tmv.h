@@ -62,7 +62,9 @@ enum {
     TMV_ERR_CLOSURE = 5,  /* a valid node under an invalid one                          */
     TMV_ERR_INPUT = 6,    /* malformed data: NaN / out-of-range probabilities, a token
                              outside [0,V), a prefix or path that does not fit the cache */
-    TMV_ERR_DEVICE = 7    /* a kernel launch failed                                     */
+    TMV_ERR_DEVICE = 7    /* a kernel launch failed, or per sequence: the device could
+                             not complete it (the sampling walk's bounded wait, an
+                             attention row block spread over XCDs)                      */
 };
 
 enum { TMV_F32 = 0, TMV_BF16 = 1 };                       /* element types           */
@@ -131,11 +133,15 @@ int tmv_tree_build_ancestors(int B, int M_max, int D_max, int parent_format,
  *        Hq/Hkv <= 16, 1 <= L_cap, q and the caches 16-byte aligned with strides that
  *        are multiples of 16 bytes (bf16: out too; TMV_ERR_ARG otherwise).
  *   workspace: tmv_tree_verify_attention_workspace() bytes, 16-byte aligned.  It opens
- *        with a fixed 16 KiB block of arrival counters (one per split row block; the last
- *        split of a block to finish merges it) followed by the split-KV partials, which
+ *        with a fixed 32 KiB block of 64-bit arrival words (one per split row block; the
+ *        last split of a block to finish merges it) followed by the split-KV partials, which
  *        every call rewrites.  The counter block must be zero before the first call and
  *        every completed call leaves it zero, so zero-fill a new workspace once; it then
  *        stays valid for calls of any shape whose size it covers.
+ *   The splits of a row block exchange their partials through the L2 of the XCD they share
+ *   (the workgroups of a block have equal ids mod 8, which the hardware deals round-robin
+ *   to the 8 XCDs).  A block whose splits are found on several XCDs is not merged: its rows
+ *   are written as 0 and the sequence gets TMV_ERR_DEVICE.
  */
 size_t tmv_tree_verify_attention_workspace(int dtype, int B, int M_max, int Hq, int Hkv,
                                            int d, int L_cap);
@@ -156,10 +162,15 @@ int tmv_tree_verify_attention(int dtype, int B, int M_max, int D_max, int Hq, in
  * chunk, token splits per row block):
  *   rows_per_group  d = 128: 64, 128 or 256; d = 64: 32 or 128; 0 = the library's choice.
  *   splits          1 .. 16; 0 = the library's choice.  (Split-KV is dropped when the
- *                   call has 256 or more row blocks.)
+ *                   call has 256 or more row blocks.)  ORed with TMV_PLAN_SCATTER_XCD
+ *                   (d = 128, 2 .. 16 splits, B * Hkv a multiple of 8): split s of each row
+ *                   block goes to a different XCD, a placement the partial exchange rejects
+ *                   (rows 0, TMV_ERR_DEVICE) -- for tests of that path; TMV_ERR_ARG when the
+ *                   shape does not allow it.
  * Other values are ignored (the library's choice).  fp32 calls have no plan.  The
  * workspace must hold tmv_tree_verify_attention_plan_workspace() bytes for the same plan.
  */
+#define TMV_PLAN_SCATTER_XCD 0x100
 size_t tmv_tree_verify_attention_plan_workspace(int dtype, int B, int M_max, int Hq, int Hkv, int d, int L_cap,
                                                 int rows_per_group, int splits);
 int tmv_tree_verify_attention_plan(int dtype, int B, int M_max, int D_max, int Hq, int Hkv, int d,

@@ -270,9 +270,9 @@ def test_workspace_reuse_across_calls_and_shapes():
 
 
 def test_attention_after_kernels_of_odd_grid_sizes(ref):
-    """The hardware deals a launch's workgroups to the XCDs round-robin, starting where the
-    previous launch stopped, so the XCD of a split-KV row block's splits depends on what ran
-    before.  After kernels of assorted grid sizes the rows must stay bit-identical."""
+    """The splits of a row block (equal workgroup ids mod 8) exchange their partials through
+    the L2 of the XCD the hardware deals them to, whatever ran before: after kernels of
+    assorted grid sizes the rows must stay bit-identical (and no block may be rejected)."""
     _case("attention: 8B-shaped layer after kernels of odd grid sizes")
     w = ti.workload(2)
     dev = _attention_parity(ref, w, 2e-2, 1e-2)
@@ -284,6 +284,43 @@ def test_attention_after_kernels_of_odd_grid_sizes(ref):
         dev.attention()
         torch.cuda.synchronize()
         assert np.array_equal(host_bits(dev.out), first), n
+
+
+def test_attention_splits_spread_over_xcds_rejected(ref):
+    """A test-only placement deals each row block's splits to different XCDs, whose L2s do not
+    see each other's partials: the merge must refuse (every row 0, status ERR_DEVICE), never
+    merge stale data, and leave the workspace ready -- the next call on it is bit-identical
+    to one on a fresh workspace."""
+    _case("attention: row blocks spread over XCDs are rejected")
+    import tree_masked_verification_amd as tmv
+    w = ti.workload(2)
+    dev = DeviceStep(w)
+    dev.build()
+    n = tmv.tree_verify_attention_plan_workspace(tmv.BF16, w.B, w.M_max, w.Hq, w.Hkv, w.d, w.L_cap, 64, 8)
+    wa = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        dev.out.fill_(float("nan"))
+        dev.attention(workspace=wa, plan=(64, 8 | tmv.PLAN_SCATTER_XCD))
+        torch.cuda.synchronize()
+        assert host_bits(dev.status).tolist() == [tmv.ERR_DEVICE]
+        assert not np.any(host_bits(dev.out))
+        assert int(wa[:32768].count_nonzero()) == 0          # arrival words left zero
+        dev.build()                                           # status back to OK
+    dev.out.fill_(float("nan"))
+    dev.attention(workspace=wa, plan=(64, 8))
+    torch.cuda.synchronize()
+    after = host_bits(dev.out).copy()
+    dev.out.fill_(float("nan"))
+    dev.attention(workspace=torch.zeros(n, dtype=torch.uint8, device="cuda"), plan=(64, 8))
+    torch.cuda.synchronize()
+    assert host_bits(dev.status).tolist() == [tmv.OK]
+    assert np.array_equal(host_bits(dev.out), after)
+    # a shape whose pairs do not fill whole XCD groups cannot be scattered
+    small = small_attention_workload(207, 3, 8, 2, 128, 37, [700, 33, 5], [37, 20, 1])
+    ds = DeviceStep(small)
+    ds.build()
+    with pytest.raises(tmv.TmvError):
+        ds.attention(plan=(64, 4 | tmv.PLAN_SCATTER_XCD))
 
 
 # a ragged batch shaped for the adaptive plan (16 sequences, 8 KV heads, two 256-row groups

@@ -28,6 +28,9 @@ OK, ERR_ARG, ERR_RANGE, ERR_CYCLE, ERR_DEPTH, ERR_CLOSURE, ERR_INPUT, ERR_DEVICE
 F32, BF16 = 0, 1
 PARENTS_VROOT, PARENTS_NEG1 = 0, 1
 ACCEPT_GREEDY, ACCEPT_SAMPLE = 0, 1
+# ORed into the pinned split count of a plan: each row block's splits on different XCDs
+# (a placement the attention's partial exchange rejects: zero rows, ERR_DEVICE; tests)
+PLAN_SCATTER_XCD = 0x100
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libtmv.so is not built (run `python tree_masked_verification_amd/build.py`); "

@@ -24,11 +24,13 @@
 //     the exponents directly; the split is recomputed against the exact maxima in the rare
 //     case a score outgrows the reference by 2^32; row sums come out of the PV product.
 //   * token groups of waves share a row group and are combined in LDS at the end; token
-//     splits publish (m, l, bf16 rows) with agent-coherent stores and the last split of a
-//     row block to arrive merges the block in split order (deterministic).
+//     splits publish (m, l, bf16 rows) and the last split of a row block to arrive merges
+//     the block in split order (deterministic).
 //   * workgroup ids are laid out so that every workgroup of one (sequence, KV head) lands
 //     on the same XCD: the head's K/V goes from HBM into that XCD's L2 once and is re-read
-//     by the head's other row groups from there.
+//     by the head's other row groups from there, and the split partials are exchanged
+//     through that L2 (plain stores, L1-bypassing loads; a block found spread over several
+//     XCDs is rejected, never merged from stale data).
 // bf16, head dim 64 (tree_attn_bf16_stream_kernel): 4 waves streaming their chunks straight
 //   into registers, split partials merged by tree_attn_merge_kernel.
 // fp32 (tree_attn_f32_kernel): one workgroup of 4 waves per (node, query head), the row's
@@ -58,9 +60,9 @@ constexpr int kVmcntRound() {
     return (N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14);
 }
 constexpr int kVmcntZero = kVmcntRound<0>();
-// buffer cache policy sc1: agent-scope coherent access (the form of a relaxed agent-scope
-// atomic load or store): stores write through to memory, loads are not served stale lines
-constexpr int kCoherent = 16;
+// buffer cache policy sc0: the load misses the CU's own L1 and reads the XCD's L2, where
+// every other CU of the XCD has written (L1s write through to the L2)
+constexpr int kXcdCoherent = 1;
 // s_waitcnt immediate that waits for LDS / scalar-memory count 0 only
 constexpr int kLgkmcntZero = 0xF | (0x7 << 4) | (0x3 << 14);
 
@@ -165,15 +167,20 @@ struct AttnPlan {
     int adapt;     // ring kernel, ragged batches: one round of this many workgroups (one per CU),
                    // each taking a work item with split counts chosen per sequence on the device
                    // (up to `splits`); 0: off
+    int scatter;   // ring kernel: split s of a row block goes to XCD slot (pair + s) % 8 (tests)
 };
 
 // split bound of adaptive splitting, and the batch sizes it is used for
 constexpr int kAdaptSplits = 2;
 constexpr int kAdaptMaxB = 64;
 
-// split-KV row blocks (pairs x row blocks) are limited to the counter block's size
+// split-KV row blocks (pairs x row blocks) are limited to the counter block's size (one
+// 64-bit arrival word per row block: eight 8-bit counts, one per XCD)
 constexpr int kMaxSplitUnits = 4096;
-constexpr size_t kCounterBytes = kMaxSplitUnits * sizeof(int32_t);
+constexpr size_t kCounterBytes = kMaxSplitUnits * sizeof(uint64_t);
+// plan flag (ORed into the pinned split count): deal the splits of each row block to
+// different XCDs, a placement the L2 partial exchange detects and rejects (tests)
+constexpr int kPlanScatter = 0x100;
 
 // An XCD's L2 (4 MB): a (sequence, kv head) pair's K and V rows up to this size stay in
 // L2 while the pair's row groups re-read them.
@@ -202,6 +209,8 @@ int device_cus() {
 AttnPlan make_plan(int B, int M_max, int Hq, int Hkv, int L_cap, int d, int cus, int force_rows = 0,
                    int force_splits = 0) {
     AttnPlan p;
+    p.scatter = (force_splits & kPlanScatter) ? 1 : 0;
+    force_splits &= ~kPlanScatter;
     const int g = Hq / Hkv;
     const int rows = M_max * g;
     p.pairs = B * Hkv;
@@ -820,10 +829,11 @@ struct PagedArgs {
 // merges items (row rr, dims part*8 .. +8), two at a time: the rows' depths and every
 // split's 16-byte O slice of those items are loaded in one straight batch (the first batch
 // right after the statistics, so these are staged while it travels), then merged in split
-// order, so the result does not depend on which split arrived last.  All loads are
-// agent-coherent (the partials were written by other workgroups, on any XCD, with
-// agent-coherent stores).  The buffer descriptors end at the `splits`-th partial: loads of
-// splits past it return zeros without touching memory and are left out of the merge.
+// order, so the result does not depend on which split arrived last.  The partials were
+// written by the block's other workgroups on this XCD with plain stores, so they sit in its
+// L2: the loads skip the L1 and read them there.  The buffer descriptors end at the
+// `splits`-th partial: loads of splits past it return zeros without touching memory and are
+// left out of the merge.
 template <int D, int RB, int SMAX>
 __device__ __forceinline__ void merge_block(int64_t unit, int splits, int stride, int b, int kvh, int g, int g_magic,
                                             int row0_wg, int M_max, int L_cap, int M, int P, int st,
@@ -848,7 +858,7 @@ __device__ __forceinline__ void merge_block(int64_t unit, int splits, int stride
     // pair i*kThreads + tid is (split, row) = (pidx / RB, pidx % RB): the partials' own order
     u32x2_t mlp[kPpt];
 #pragma unroll
-    for (int i = 0; i < kPpt; ++i) mlp[i] = __builtin_amdgcn_raw_buffer_load_b64(rst, (i * kThreads + tid) * 8, 0, kCoherent);
+    for (int i = 0; i < kPpt; ++i) mlp[i] = __builtin_amdgcn_raw_buffer_load_b64(rst, (i * kThreads + tid) * 8, 0, kXcdCoherent);
     // items in batches of IPB per thread: the rows' depths and every split's O slices
     constexpr int IPB = kIpt < 2 ? kIpt : 2;
     u32x4_t ov[IPB][SMAX];
@@ -863,7 +873,7 @@ __device__ __forceinline__ void merge_block(int64_t unit, int splits, int stride
             dp[k] = depth[static_cast<int64_t>(b) * (M_max + 1) + ((r * g_magic) >> 16) + 1];
 #pragma unroll
             for (int s2 = 0; s2 < SMAX; ++s2)
-                ov[k][s2] = __builtin_amdgcn_raw_buffer_load_b128(ro, ((s2 * RB + rr) * D + part * 8) * 2, 0, kCoherent);
+                ov[k][s2] = __builtin_amdgcn_raw_buffer_load_b128(ro, ((s2 * RB + rr) * D + part * 8) * 2, 0, kXcdCoherent);
         }
     };
     load_batch(0);
@@ -1009,7 +1019,7 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
                       const int32_t *__restrict__ anc, const int32_t *__restrict__ depth,
                       int32_t *__restrict__ status, float qk_scale_log2,
                       uint16_t *__restrict__ out, int64_t os0, int64_t os1, int64_t os2,
-                      float *__restrict__ ws_stats, uint16_t *__restrict__ ws_o, int32_t *__restrict__ ws_cnt,
+                      float *__restrict__ ws_stats, uint16_t *__restrict__ ws_o, uint64_t *__restrict__ ws_cnt,
                       PagedArgs pg)
 {
     using RS = RingShape<D>;
@@ -1079,7 +1089,9 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         rbk = blockIdx.x >> 3;
         split = blockIdx.y;
         splits = smax = S;
-        pair = blockIdx.z * tmv::kXcds + (blockIdx.x & (tmv::kXcds - 1));
+        // (scattered plans, for tests: split s of a pair sits in XCD slot (pair + s) % 8)
+        const int shift = (geom >> 26) & 1 ? split : 0;
+        pair = blockIdx.z * tmv::kXcds + ((static_cast<int>(blockIdx.x) - shift) & (tmv::kXcds - 1));
         if (pair >= pairs) return;
     }
     const int b = pair / Hkv, kvh = pair - b * Hkv;
@@ -1760,12 +1772,16 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
     }
 
     // ---- split-KV completion: the last split of a row block to arrive merges the block.
-    // Splits publish their partials with agent-coherent stores (sc1: written through to
-    // memory, as the compiler writes a relaxed agent-scope atomic store) and the merging
-    // workgroup reads them with agent-coherent loads, so the splits of a block may run on
-    // any XCDs: no L2 write-back or invalidation is needed.  A split's stores are complete
-    // once its vector-memory count drains, after which it counts itself in with a
-    // device-scope atomic; the last arrival clears the counter and merges.
+    // Every workgroup of a row block has the same id mod 8, and the hardware deals a launch's
+    // workgroups round-robin to the 8 XCDs, so the block's splits share one XCD and its L2:
+    // they publish their partials with plain stores (the L1s write through to that L2) and
+    // the merging workgroup reads them from the L2 -- the partials need not travel to memory
+    // and back.  A split's stores are complete once its vector-memory count drains, after
+    // which it counts itself in with a device-scope atomic on the block's 64-bit arrival
+    // word, adding 1 to the 8-bit count of its own XCD (HW_REG_XCC_ID).  The last arrival
+    // clears the word; if every other arrival came from its XCD it merges, otherwise (a
+    // dispatch that split the block over several XCDs, whose L2s do not see each other's
+    // stores) it writes the block's rows as zeros and marks the sequence TMV_ERR_DEVICE.
     // this launch's split partials: [pairs * nb units][smax][RB rows] (m, l) and O rows
     const int64_t part_rows = static_cast<int64_t>(pairs) * nb * smax * RB;
     const __amdgpu_buffer_rsrc_t part_o =
@@ -1777,19 +1793,31 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
         __builtin_amdgcn_s_waitcnt(kVmcntZero);
         __syncthreads();
         if (threadIdx.x == 0) {
-            const int old = __hip_atomic_fetch_add(ws_cnt + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            s_last = old == splits - 1 ? 1 : 0;
+            unsigned xcc;
+            asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+            const int sh = 8 * static_cast<int>(xcc & 7u);
+            const uint64_t old = __hip_atomic_fetch_add(ws_cnt + unit, uint64_t(1) << sh, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
+            int arrived = 0;
+#pragma unroll
+            for (int x = 0; x < tmv::kXcds; ++x) arrived += static_cast<int>((old >> (8 * x)) & 0xffu);
+            s_last = arrived != splits - 1 ? 0 : old == (static_cast<uint64_t>(splits - 1) << sh) ? 1 : 2;
         }
         __syncthreads();
         if (s_last == 0) return;
-        if (threadIdx.x == 0) __hip_atomic_store(ws_cnt + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int mst = st;
+        if (threadIdx.x == 0) {
+            __hip_atomic_store(ws_cnt + unit, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (s_last == 2 && st == TMV_OK) status[b] = TMV_ERR_DEVICE;
+        }
+        if (s_last == 2) mst = TMV_ERR_DEVICE;       // the block's rows are written as zeros
         // (the ring is idle: the merge stages the statistics in its first group)
         if (splits <= 8)
-            merge_block<D, RB, 8>(unit, splits, smax, b, kvh, g, g_magic, row0_wg, M_max, L_cap, M, P, st, depth, out, os0,
-                                  os1, os2, ws_stats, ws_o, reinterpret_cast<float *>(ring0));
+            merge_block<D, RB, 8>(unit, splits, smax, b, kvh, g, g_magic, row0_wg, M_max, L_cap, M, P, mst, depth, out,
+                                  os0, os1, os2, ws_stats, ws_o, reinterpret_cast<float *>(ring0));
         else
-            merge_block<D, RB, 16>(unit, splits, smax, b, kvh, g, g_magic, row0_wg, M_max, L_cap, M, P, st, depth, out, os0,
-                                   os1, os2, ws_stats, ws_o, reinterpret_cast<float *>(ring0));
+            merge_block<D, RB, 16>(unit, splits, smax, b, kvh, g, g_magic, row0_wg, M_max, L_cap, M, P, mst, depth, out,
+                                   os0, os1, os2, ws_stats, ws_o, reinterpret_cast<float *>(ring0));
     };
     // row `rr` of the workgroup's block, dims d0 .. d0 + n - 1 (n a multiple of 8) of the
     // final output (splits == 1) from x / l, or zeros for inert rows
@@ -1872,11 +1900,11 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
 #pragma unroll
                 for (int h2 = 0; h2 < 4; ++h2)
                     x[h2] = tmv::pack_bf16x2(acc[e + 2 * h2] * inv, acc[e + 2 * h2 + 1] * inv);
-                __builtin_amdgcn_raw_buffer_store_b128(x, part_o, ((base + rr) * D + d0 + e) * 2, 0, kCoherent);
+                __builtin_amdgcn_raw_buffer_store_b128(x, part_o, ((base + rr) * D + d0 + e) * 2, 0, 0);
             }
             if ((lane % LPR) == 0) {
                 const u32x2_t x = {__float_as_uint(mt), __float_as_uint(lt)};
-                __builtin_amdgcn_raw_buffer_store_b64(x, part_ml, (base + rr) * 8, 0, kCoherent);
+                __builtin_amdgcn_raw_buffer_store_b64(x, part_ml, (base + rr) * 8, 0, 0);
             }
             finish_split();
             return;
@@ -1894,11 +1922,11 @@ tree_attn_bf16_kernel(const uint16_t *__restrict__ kc, const uint16_t *__restric
                 for (int nt = 0; nt < NT; ++nt) {
                     const u32x2_t x = {tmv::pack_bf16x2(oacc[rt][nt][0] * inv, oacc[rt][nt][1] * inv),
                                        tmv::pack_bf16x2(oacc[rt][nt][2] * inv, oacc[rt][nt][3] * inv)};
-                    __builtin_amdgcn_raw_buffer_store_b64(x, part_o, ((base + rr) * D + nt * 16 + 4 * G) * 2, 0, kCoherent);
+                    __builtin_amdgcn_raw_buffer_store_b64(x, part_o, ((base + rr) * D + nt * 16 + 4 * G) * 2, 0, 0);
                 }
                 if (G == 0) {
                     const u32x2_t x = {__float_as_uint(mrow[rt]), __float_as_uint(lrow[rt])};
-                    __builtin_amdgcn_raw_buffer_store_b64(x, part_ml, (base + rr) * 8, 0, kCoherent);
+                    __builtin_amdgcn_raw_buffer_store_b64(x, part_ml, (base + rr) * 8, 0, 0);
                 }
             }
             finish_split();
@@ -2077,7 +2105,7 @@ void launch_bf16(const AttnPlan &p, hipStream_t s, int M_max, int D_max, int Hq,
                  const PagedArgs *pg)
 {
     char *w = static_cast<char *>(ws);
-    int32_t *cnt = reinterpret_cast<int32_t *>(w);
+    uint64_t *cnt = reinterpret_cast<uint64_t *>(w);
     float *stats = reinterpret_cast<float *>(w + off_stats);
     if constexpr (D == 64) {
         float *part = reinterpret_cast<float *>(w + off_o);
@@ -2099,7 +2127,7 @@ void launch_bf16(const AttnPlan &p, hipStream_t s, int M_max, int D_max, int Hq,
         uint16_t *part = reinterpret_cast<uint16_t *>(w + off_o);
         // (Hkv <= 0xffff, Hq / Hkv <= 16 and splits <= 16 are checked or planned)
         const uint32_t geom = static_cast<uint32_t>(Hkv) | (static_cast<uint32_t>(Hq / Hkv) << 16) |
-                              (static_cast<uint32_t>(p.splits) << 21);
+                              (static_cast<uint32_t>(p.splits) << 21) | (static_cast<uint32_t>(p.scatter) << 26);
         const unsigned pgroups = static_cast<unsigned>((p.pairs + tmv::kXcds - 1) / tmv::kXcds);
         const dim3 grid = p.adapt ? dim3(static_cast<unsigned>(p.adapt)) : dim3(tmv::kXcds * p.nb, p.splits, pgroups);
         const PagedArgs pgv = pg ? *pg : PagedArgs{nullptr, 0, 0, 0};
@@ -2154,6 +2182,8 @@ void dispatch_bf16(const AttnPlan &p, int d, hipStream_t s, int M_max, int D_max
 bool plan_fits(const AttnPlan &p, int d) {
     const int64_t part_rows = static_cast<int64_t>(p.pairs) * p.nb * p.splits * p.rb;
     // (ring kernel grid: (8 nb, splits, ceil(pairs / 8)); streaming kernel: 8 slots)
+    // (a scattered plan needs whole XCD groups of pairs and split row blocks of the ring kernel)
+    if (p.scatter && (d != 128 || p.adapt || p.splits < 2 || p.pairs % tmv::kXcds != 0)) return false;
     return part_rows * d * 4 < (int64_t(1) << 31) && static_cast<int64_t>(p.slots) * tmv::kXcds <= 0x7fffffff &&
            (p.pairs + tmv::kXcds - 1) / tmv::kXcds <= 65535;
 }

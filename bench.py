@@ -221,7 +221,7 @@ STAGE_KERNELS = {
     "build": ("build_ancestors_kernel",),
     "attention": ("tree_attn_bf16_kernel", "tree_attn_bf16_stream_kernel", "tree_attn_merge_kernel",
                   "tree_attn_f32_kernel"),
-    "accept": ("greedy_accept_kernel", "sample_walk_kernel"),
+    "accept": ("greedy_accept_kernel", "greedy_scan_kernel", "greedy_select_kernel", "sample_walk_kernel"),
     "commit": ("commit_kernel",),
 }
 
@@ -230,7 +230,7 @@ def stage_of(kernel_name):
     """The timed stage a dispatched kernel belongs to; None for the paged-cache variants
     (block-table template argument true), library kernels and everything else."""
     import re
-    if re.search(r"tree_attn_bf16_kernel<\d+, \d+, (true|false), true>", kernel_name) or "commit_kernel<true>" in kernel_name:
+    if re.search(r"tree_attn_bf16_kernel<\d+, \d+, (true|false), true\b", kernel_name) or "commit_kernel<true>" in kernel_name:
         return None
     for stage, names in STAGE_KERNELS.items():
         if any(re.search(r"\b%s\b" % n, kernel_name) for n in names):

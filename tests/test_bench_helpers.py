@@ -81,3 +81,24 @@ def test_paged_layout_places_every_slot():
     assert np.array_equal(table[2, :2], table[0, :2])
     rest = np.concatenate([table[0], table[1], table[2, 2:]])
     assert len(set(rest.tolist())) == rest.size and rest.max() < kp.shape[1]
+
+
+def test_counter_kernels_map_to_stages():
+    """Counter ingestion attributes each dispatched kernel to its stage: the paged-cache
+    attention (block-table template argument true) and paged commit belong to none."""
+    import bench
+    ns = "void (anonymous namespace)::"
+    assert bench.stage_of(ns + "tree_attn_bf16_kernel<128, 2, false, false, false>(unsigned short const*)") == "attention"
+    assert bench.stage_of(ns + "tree_attn_bf16_kernel<128, 8, true, false, true>(unsigned short const*)") == "attention"
+    assert bench.stage_of(ns + "tree_attn_bf16_kernel<128, 2, false, true, false>(unsigned short const*)") is None
+    assert bench.stage_of(ns + "tree_attn_bf16_kernel<128, 8, true, true, true>(unsigned short const*)") is None
+    assert bench.stage_of(ns + "tree_attn_f32_kernel<64>(int, int)") == "attention"
+    assert bench.stage_of(ns + "greedy_accept_kernel<0>(int, int)") == "accept"
+    assert bench.stage_of(ns + "greedy_scan_kernel<0>(int, int)") == "accept"
+    assert bench.stage_of(ns + "greedy_select_kernel(int, int)") == "accept"
+    assert bench.stage_of(ns + "sample_walk_kernel(int, int)") == "accept"
+    assert bench.stage_of(ns + "lm_select_kernel(int, int)") is None
+    assert bench.stage_of(ns + "commit_kernel<false>(int, int)") == "commit"
+    assert bench.stage_of(ns + "commit_kernel<true>(int, int)") is None
+    assert bench.stage_of(ns + "build_ancestors_kernel(int, int)") == "build"
+    assert bench.stage_of("Cijk_Alik_Bljk_BBS_BH_MT128x128x64") is None

@@ -196,10 +196,16 @@ __device__ __forceinline__ uint64_t chunk_key(int V, const void *__restrict__ te
     if (x1 - x0 == kScanChunk && ((reinterpret_cast<uintptr_t>(row + x0 * kElem) & 15u) == 0)) {
         constexpr int kPer = kScanChunk * kElem / (16 * kScanThreads);      // 16-byte loads per thread
         constexpr int kPerLoad = 16 / kElem;                                 // values per load
-        const uint4 *r16 = reinterpret_cast<const uint4 *>(row + x0 * kElem);
+        // (the logits are read once: non-temporal loads stream them past the caches -- workload
+        // 3's scan 116 -> 99 us, workload 2's 12.2 -> 11.2 us)
+        typedef unsigned u32x4_nt __attribute__((ext_vector_type(4)));
+        const u32x4_nt *r16 = reinterpret_cast<const u32x4_nt *>(row + x0 * kElem);
         uint4 h[kPer];
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) h[i] = r16[tid + i * kScanThreads];
+        for (int i = 0; i < kPer; ++i) {
+            const u32x4_nt v = __builtin_nontemporal_load(r16 + tid + i * kScanThreads);
+            h[i] = make_uint4(v.x, v.y, v.z, v.w);
+        }
         auto val = [&](int k) -> float {
             const uint4 &q = h[k / kPerLoad];
             const int e = k % kPerLoad, wi = e / (kPerLoad / 4);

@@ -363,8 +363,8 @@ greedy_accept_kernel(int M_max, int D_max, int V, int nchunk, const void *__rest
         if (s_flag == 0) return;
     }
     // this row is complete (or dead): count it in for the sequence; the last row chooses.
-    // (The path inputs are read first, so their loads travel with the arrival.)
-    const PathInputs in = load_path_inputs(b, M_max, D_max, tokens, n_nodes, anc, depth, status);
+    // (Only the chooser reads the path inputs, together with the row keys: issued before the
+    // arrival they would hold its result back, loads completing in issue order.)
     if (tid == 0) {
         const int old = __hip_atomic_fetch_add(seq_cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const bool last = old == R - 1;
@@ -374,6 +374,7 @@ greedy_accept_kernel(int M_max, int D_max, int V, int nchunk, const void *__rest
     __syncthreads();
     if (s_flag != 2) return;
     // every row of the sequence has arrived: its keys are final (dead rows' stay zero)
+    const PathInputs in = load_path_inputs(b, M_max, D_max, tokens, n_nodes, anc, depth, status);
     uint64_t krow = 0;
     if (tid < R) {
         unsigned long long *rk = reinterpret_cast<unsigned long long *>(ws + (static_cast<int64_t>(b) * R + tid) * kSlot);

@@ -158,10 +158,8 @@ __device__ __forceinline__ void lds_write16(uint32_t addr, u32x4_t v) {
 
 // buffer -> LDS copy of 16 bytes per lane: lane l's bytes land at lds + 16*l; a voffset
 // past the descriptor's records writes zeros and reads nothing
-// (cache policy nt: the K/V stream is read about once from memory; the hint measured 1-2 %
-// faster at workloads 2-4, the head's re-reads still hitting the L2)
 __device__ __forceinline__ void dma_to_lds16(__amdgpu_buffer_rsrc_t r, char *lds, uint32_t voffset) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voffset, 0, 0, 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voffset, 0, 0, 0);
 }
 __device__ __forceinline__ uint32_t lds_addr(const char *p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char *)p));

@@ -781,6 +781,9 @@ def main():
                     help="write profiles/hbm_counters.json for --workload from two rocprofv3 --pmc runs "
                          "(FETCH_SIZE, WRITE_SIZE) of this script with --copy-probe, and exit")
     ap.add_argument("--counter-command", default="", help="the profiled command, recorded with --ingest-counters")
+    ap.add_argument("--record", default="", metavar="JSONL",
+                    help="also append this run's record (the JSON line, the command, host and device, the input "
+                         "seeds and sizes) to this JSON-lines file")
     args = ap.parse_args()
     if args.ingest_counters:
         print(json.dumps(ingest_counters(args.workload, args.ingest_counters[0], args.ingest_counters[1],
@@ -947,6 +950,36 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+    if args.record:
+        append_record(args.record, line, run_record(w0, c, torch.cuda.get_device_name(0)))
+
+
+def run_record(w0, c, gpu_name):
+    """What a JSON-lines run record holds beside the bench line: the command, when, where
+    (host CPU, its thread count, the device), the code (the git commit when the tree has one)
+    and the workload's seeds and sizes."""
+    head = None
+    try:
+        with open(os.path.join(ROOT, ".git", "HEAD")) as f:
+            ref = f.read().strip()
+        if ref.startswith("ref: "):
+            with open(os.path.join(ROOT, ".git", ref[5:])) as f:
+                head = f.read().strip()
+        else:
+            head = ref
+    except OSError:
+        pass
+    return {"time_utc": time.strftime("%Y-%m-%dT%H:%M:%SZ", time.gmtime()), "argv": sys.argv[1:],
+            "git_head": head, "host_cpu": cpu_model(), "host_threads": host_threads(), "gpu": gpu_name,
+            "workload": c, "seed": 1000 + c, "extra_set_seeds": "20000 + 100 * workload + i",
+            "sizes": {"B": w0.B, "M_max": w0.M_max, "D_max": w0.D_max, "Hq": w0.Hq, "Hkv": w0.Hkv, "d": w0.d,
+                      "L_cap": w0.L_cap, "V": w0.V, "layers": w0.n_layers}}
+
+
+def append_record(path, line, meta):
+    """Append one JSON line {..meta, "result": line} to `path`."""
+    with open(path, "a") as f:
+        f.write(json.dumps(dict(meta, result=line)) + "\n")
 
 
 if __name__ == "__main__":

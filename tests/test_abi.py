@@ -127,3 +127,19 @@ def test_package_fails_loudly_without_library(tmp_path):
     r = subprocess.run([sys.executable, "-c", "import tree_masked_verification_amd"], cwd=tmp_path,
                        capture_output=True, text=True)
     assert r.returncode != 0 and "ImportError" in r.stderr and "no CPU fallback" in r.stderr
+
+
+def test_debug_mode_reports_failed_sequences(capsys, monkeypatch):
+    """TMV_DEBUG=1 makes the binding report, after a call, every sequence whose status is not
+    OK (here on a host status array: no GPU call is made)."""
+    import torch
+    import tree_masked_verification_amd as tmv
+    st = torch.tensor([tmv.OK, tmv.ERR_CYCLE, tmv.OK, tmv.ERR_DEVICE], dtype=torch.int32)
+    monkeypatch.setattr(tmv, "DEBUG", False)
+    assert tmv._debug("tree_verify_attention", st) == []
+    assert capsys.readouterr().err == ""
+    monkeypatch.setattr(tmv, "DEBUG", True)
+    bad = tmv._debug("tree_verify_attention", st)
+    assert [i for i, _ in bad] == [1, 3]
+    err = capsys.readouterr().err
+    assert "tree_verify_attention: 2 of 4 sequences not OK" in err and tmv.status_string(tmv.ERR_CYCLE) in err

@@ -102,3 +102,20 @@ def test_counter_kernels_map_to_stages():
     assert bench.stage_of(ns + "commit_kernel<true>(int, int)") is None
     assert bench.stage_of(ns + "build_ancestors_kernel(int, int)") == "build"
     assert bench.stage_of("Cijk_Alik_Bljk_BBS_BH_MT128x128x64") is None
+
+
+def test_run_record_appends_json_lines(tmp_path):
+    """--record appends one self-contained JSON line per run: the bench line under "result"
+    beside the command, host, device and the workload's seeds and sizes."""
+    import json
+    w = ti.workload(1)
+    meta = bench.run_record(w, 1, "test-device")
+    path = tmp_path / "runs.jsonl"
+    for v in (1.0, 2.0):
+        bench.append_record(str(path), {"metric": "m", "value": v}, meta)
+    recs = [json.loads(l) for l in open(path)]
+    assert [r["result"]["value"] for r in recs] == [1.0, 2.0]
+    r = recs[0]
+    assert r["gpu"] == "test-device" and r["workload"] == 1 and r["seed"] == 1001
+    assert r["sizes"]["B"] == 1 and r["sizes"]["d"] == 64 and r["sizes"]["V"] == 32
+    assert r["host_threads"] >= 1 and "time_utc" in r

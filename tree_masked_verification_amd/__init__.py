@@ -160,6 +160,26 @@ def _check(rc, what):
         raise TmvError(rc, what)
 
 
+# TMV_DEBUG=1: after every call, synchronise its stream and report on stderr each sequence
+# whose status is not OK (debugging only: it adds a host synchronisation to every call, so it
+# must stay off under graph capture and in timed runs; the computation is the same)
+DEBUG = os.environ.get("TMV_DEBUG", "") not in ("", "0")
+
+
+def _debug(what, status, stream=None):
+    if not DEBUG:
+        return []
+    if status.is_cuda:
+        _torch_stream(stream).synchronize()
+    codes = status.cpu().tolist()
+    bad = [(i, status_string(int(c))) for i, c in enumerate(codes) if c != OK]
+    if bad:
+        import sys
+        print("tmv debug: %s: %d of %d sequences not OK: %s" % (what, len(bad), len(codes), bad[:16]),
+              file=sys.stderr, flush=True)
+    return bad
+
+
 def _i32(*ts):
     for t in ts:
         if t is not None and (t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous()):
@@ -182,6 +202,7 @@ def tree_build_ancestors(parents, n_nodes, anc, depth, status, parent_format=PAR
     _check(_lib.tmv_tree_build_ancestors(B, R - 1, W - 1, parent_format, _ptr(parents), _ptr(valid), _ptr(n_nodes),
                                          _ptr(anc), _ptr(depth), _ptr(status), _stream(stream)),
            "tree_build_ancestors")
+    _debug("tree_build_ancestors", status, stream)
 
 
 # ------------------------------------------------------------------------ stage 2
@@ -234,6 +255,7 @@ def tree_verify_attention(q, k_cache, v_cache, prefix_len, n_nodes, anc, depth, 
         _check(_lib.tmv_tree_verify_attention(*args, *tail), "tree_verify_attention")
     else:
         _check(_lib.tmv_tree_verify_attention_plan(*args, rows, splits, *tail), "tree_verify_attention_plan")
+    _debug("tree_verify_attention", status, stream)
 
 
 def tree_verify_attention_paged_workspace(B, M_max, Hq, Hkv, d, page_size, max_blocks) -> int:
@@ -276,6 +298,7 @@ def tree_verify_attention_paged(q, k_pages, v_pages, block_table, prefix_len, n_
     else:
         _check(_lib.tmv_tree_verify_attention_paged_plan(*args, rows, splits, *tail),
                "tree_verify_attention_paged_plan")
+    _debug("tree_verify_attention_paged", status, stream)
 
 
 # ------------------------------------------------------------------------ stage 3
@@ -315,6 +338,7 @@ def tree_accept(mode, tokens, teacher, n_nodes, anc, depth, status, accept_len, 
         if not 0 <= int(wait_us) < 1 << 32:
             raise ValueError("wait_us out of range")
         _check(_lib.tmv_tree_accept_wait(*args, int(wait_us), _stream(stream)), "tree_accept")
+    _debug("tree_accept", status, stream)
 
 
 def tree_accept_lm_head_workspace(B, M_max) -> int:
@@ -348,6 +372,7 @@ def tree_accept_lm_head(tokens, hidden, lm_head, n_nodes, anc, depth, status, ac
                                         _ptr(row_argmax), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                         _stream(stream)),
            "tree_accept_lm_head")
+    _debug("tree_accept_lm_head", status, stream)
 
 
 # ------------------------------------------------------------------------ stage 4
@@ -369,6 +394,7 @@ def kv_commit_path(k_cache, v_cache, prefix_len, n_nodes, accept_len, path, stat
                                    _ptr(n_nodes), _ptr(accept_len), _ptr(path), _ptr(status), _ptr(new_len),
                                    _stream(stream)),
            "kv_commit_path")
+    _debug("kv_commit_path", status, stream)
 
 
 def kv_commit_path_paged(k_pages, v_pages, block_table, prefix_len, n_nodes, accept_len, path, status, new_len, M_max,
@@ -393,6 +419,7 @@ def kv_commit_path_paged(k_pages, v_pages, block_table, prefix_len, n_nodes, acc
                                          _ptr(prefix_len), _ptr(n_nodes), _ptr(accept_len), _ptr(path), _ptr(status),
                                          _ptr(new_len), _stream(stream)),
            "kv_commit_path_paged")
+    _debug("kv_commit_path_paged", status, stream)
 
 
 def kv_commit_path_paged_evict(k_pages, v_pages, block_table, prefix_len, n_nodes, accept_len, path, status, new_len,
@@ -421,6 +448,7 @@ def kv_commit_path_paged_evict(k_pages, v_pages, block_table, prefix_len, n_node
                                                _ptr(freed_pages), _ptr(freed_count), freed_pages.numel(),
                                                _stream(stream)),
            "kv_commit_path_paged_evict")
+    _debug("kv_commit_path_paged_evict", status, stream)
 
 
 # ------------------------------------------------------------------------ tree construction
@@ -452,6 +480,7 @@ def tree_best_first(q, N_max, parents, tokens, n_nodes, rho, status, cost=None, 
                                     _ptr(status), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream(stream)),
            "tree_best_first")
+    _debug("tree_best_first", status, stream)
 
 
 class Workspaces:

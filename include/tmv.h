@@ -357,6 +357,8 @@ int tmv_tree_accept_wait(int mode, int B, int M_max, int D_max, int V,
  *              sum_k |h_k w_k| for each of them).  Ties: smallest token.  A NaN logit in a
  *              live row sets TMV_ERR_INPUT.
  *   row_argmax int32 [B][M_max+1] or NULL: t(u) of every live row, -1 elsewhere.
+ *   Rows: up to 64 rows (B * (M_max+1)) stream the weights once; more rows go in blocks of
+ *              272, each streaming them once.
  *   Other arguments and outputs as tmv_tree_accept (GREEDY).
  *   Requires hidden, lm_head and the workspace 16-byte aligned, strides multiples of 8
  *   elements, and both tensors spanning less than 2 GiB (TMV_ERR_ARG otherwise).

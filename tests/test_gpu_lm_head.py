@@ -95,7 +95,9 @@ def _small_case(seed, B, M_max, D_max, K, V, sigma_w, alpha=0.8):
     return parents, n_nodes, hidden, w, tokens
 
 
-@pytest.mark.parametrize("B,M_max,D_max,K,V", [(2, 6, 3, 512, 3000), (3, 20, 5, 1024, 1000), (1, 1, 1, 512, 257)])
+@pytest.mark.parametrize("B,M_max,D_max,K,V", [(2, 6, 3, 512, 3000), (3, 20, 5, 1024, 1000), (1, 1, 1, 512, 257),
+                                               # more than 64 rows: 272-row blocks (one, one, two)
+                                               (2, 40, 5, 1024, 900), (4, 64, 6, 512, 2000), (3, 100, 8, 512, 700)])
 def test_lm_head_accept_small(B, M_max, D_max, K, V):
     _case("lm-head accept: B%d M%d K%d V%d" % (B, M_max, K, V))
     parents, n_nodes, hidden, w, tokens = _small_case(300 + V, B, M_max, D_max, K, V, 0.05)
@@ -124,10 +126,11 @@ def test_lm_head_accept_small(B, M_max, D_max, K, V):
         assert np.array_equal(A, oA) and np.array_equal(path, opath) and np.array_equal(nxt, onxt)
 
 
-def test_lm_head_nan_and_workspace_reuse():
-    _case("lm-head accept: NaN row rejects its sequence; the workspace is left zero")
+@pytest.mark.parametrize("M_max", [6, 40])
+def test_lm_head_nan_and_workspace_reuse(M_max):
+    _case("lm-head accept: NaN row rejects its sequence; the workspace is left zero (M_max %d)" % M_max)
     import tree_masked_verification_amd as tmv
-    B, M_max, D_max, K, V = 3, 6, 3, 512, 700
+    B, D_max, K, V = 3, 3, 512, 700
     parents, n_nodes, hidden, w, tokens = _small_case(311, B, M_max, D_max, K, V, 0.05)
     ws = torch.zeros(tmv.tree_accept_lm_head_workspace(B, M_max), dtype=torch.uint8, device="cuda")
     first = _run(hidden, w, parents, n_nodes, tokens, M_max, D_max, ws=ws)

@@ -26,6 +26,15 @@ def flags():
             "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
 
 
+# per-source flags on top of flags()
+EXTRA = {
+    # MFMA accumulators in VGPRs: with 136 of them in AGPRs the register allocator copies the
+    # wide LM-head kernel's accumulators between registers on every k-step (the other
+    # kernels of the file keep theirs in VGPRs either way)
+    "accept.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def build(verbose: bool = False) -> str:
     """Compile every HIP source into one shared library (always recompiles)."""
     objs = []
@@ -33,7 +42,8 @@ def build(verbose: bool = False) -> str:
     os.makedirs(os.path.join(HERE, "_build"), exist_ok=True)
     for src in sources():
         obj = os.path.join(HERE, "_build", os.path.basename(src) + ".o")
-        cmd = [HIPCC] + [f for f in flags() if f != "-shared"] + ["-c", src, "-o", obj]
+        cmd = [HIPCC] + [f for f in flags() if f != "-shared"] + EXTRA.get(os.path.basename(src), []) + \
+            ["-c", src, "-o", obj]
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
         objs.append(obj)
     failed = False

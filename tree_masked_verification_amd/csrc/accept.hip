@@ -618,6 +618,197 @@ lm_head_argmax_kernel(int B, int M_max, int V, const uint16_t *__restrict__ hidd
     }
 }
 
+// The LM-head product for more rows than one 64-row block (several sequences' trees, or
+// deep trees): a block of up to 272 rows (17 row tiles of 16) against one vocabulary tile
+// of 128 entries per workgroup, so that the weights are read once for all those rows (the
+// 64-row kernel would stream them once per row block).  4 waves, one per SIMD (the 17 x 2
+// accumulator tiles take 136 registers per lane); wave w computes entries 32w .. +32 of the
+// tile, v_mfma_f32_16x16x32_bf16 over K in 32-wide steps.
+//   * the rows' hidden states are staged in LDS one 128-wide k-block at a time (16-byte
+//     pieces XOR-swizzled by row), the next block travelling in registers meanwhile;
+//   * the weights stream from HBM straight into registers kLwDepth steps ahead, in a loop
+//     whose body covers two k-blocks (kLwDepth steps, so every ring slot is a constant);
+//   * the keys are formed and merged as in the 64-row kernel: per lane and row the best
+//     (value, ~index), reduced over lanes and waves, one device-scope atomic max per row.
+constexpr int kLwWaves = 8;
+constexpr int kLwThreads = kLwWaves * kWave;
+constexpr int kLwRT = 17;                              // row tiles of 16 per row block
+constexpr int kLwRows = kLwRT * 16;                    // 272 rows per row block
+constexpr int kLwTile = kLwWaves * kLmVocabPerWave;    // 128 vocabulary entries per workgroup
+constexpr int kLwKB = 128;                             // k entries per staged block
+constexpr int kLwPieces = kLwKB / 8;                   // 16-byte pieces per staged row (16)
+constexpr int kLwSteps = kLwKB / 32;                   // MFMA k-steps per staged block
+constexpr int kLwBody = 1;                             // staged blocks per loop iteration
+constexpr int kLwDepth = kLwBody * kLwSteps;           // weight steps in flight per wave
+constexpr int kLwPre = 4;                              // B-operand LDS reads in flight per wave
+constexpr int kLwPiecesAll = kLwRows * kLwPieces;
+constexpr int kLwStage = (kLwPiecesAll + kLwThreads - 1) / kLwThreads;   // staged pieces per thread (9)
+static_assert(kLwPieces == 16, "the row swizzle spans 16 pieces");
+
+__global__ void __launch_bounds__(kLwThreads)
+lm_head_argmax_wide_kernel(int B, int M_max, int K, int V, const uint16_t *__restrict__ hidden, int64_t hsb,
+                           int64_t hsr, uint32_t h_bytes, const uint16_t *__restrict__ w, int64_t wsr,
+                           uint32_t w_bytes, const int32_t *__restrict__ n_nodes, const int32_t *__restrict__ depth,
+                           const int32_t *__restrict__ status, uint64_t *__restrict__ row_keys, int ntiles, int nrb)
+{
+    __shared__ lm_u32x4 h_lds[kLwRows][kLwPieces];
+    __shared__ uint64_t s_key[kLwWaves][kLwRows];
+    __shared__ int s_any;
+    const int R = M_max + 1, nrows = B * R;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int c16 = lane & 15, G = lane >> 4;
+    // workgroup id = XCD slot + 8 (row block + nrb * s), covering tile s * 8 + slot: the row
+    // blocks of one tile share an XCD and are dispatched one after another (as in the
+    // 64-row kernel)
+    const int xslot = blockIdx.x & 7, rest = blockIdx.x >> 3;
+    const int tile = (rest / nrb) * 8 + xslot;
+    if (tile >= ntiles) return;
+    const int rb0 = (rest % nrb) * kLwRows;
+
+    // a row block without a live row does nothing
+    if (threadIdx.x == 0) s_any = 0;
+    __syncthreads();
+    for (int r = threadIdx.x; r < kLwRows; r += kLwThreads)
+        if (rb0 + r < nrows && lm_row_live(rb0 + r, R, M_max, n_nodes, depth, status)) s_any = 1;
+    __syncthreads();
+    if (!s_any) return;
+
+    const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(hidden), 0,
+                                                                        static_cast<int>(h_bytes), kLmBufferFlags);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(w), 0,
+                                                                        static_cast<int>(w_bytes), kLmBufferFlags);
+    // staging: thread t moves pieces q = t + 256 j of a block (row q / 16, piece q % 16);
+    // rows past the tensor are clamped (computed, never merged)
+    uint32_t soff[kLwStage];
+#pragma unroll
+    for (int j = 0; j < kLwStage; ++j) {
+        int q = threadIdx.x + j * kLwThreads;
+        q = q < kLwPiecesAll ? q : q - kLwPiecesAll;
+        const int r = q / kLwPieces, pc = q % kLwPieces;
+        int gr = rb0 + r;
+        if (gr > nrows - 1) gr = nrows - 1;
+        const int b = gr / R, u = gr - b * R;
+        soff[j] = static_cast<uint32_t>((b * hsb + u * hsr) * 2 + pc * 16);
+    }
+    const int vbase = tile * kLwTile + wave * kLmVocabPerWave;
+    uint32_t woff[2];
+#pragma unroll
+    for (int vt = 0; vt < 2; ++vt) {
+        int v = vbase + vt * 16 + c16;
+        if (v > V - 1) v = V - 1;
+        woff[vt] = static_cast<uint32_t>(v * wsr * 2 + G * 16);
+    }
+    lm_f32x4 acc[2][kLwRT];
+#pragma unroll
+    for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+        for (int rt = 0; rt < kLwRT; ++rt) acc[vt][rt] = lm_f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nblk = K / kLwKB, nsteps = K / 32;       // K a multiple of kLwBody kLwKB
+    lm_u32x4 wa[kLwDepth][2];
+    lm_u32x4 hv[kLwStage];
+#pragma unroll
+    for (int j = 0; j < kLwStage; ++j) hv[j] = __builtin_amdgcn_raw_buffer_load_b128(hr, soff[j], 0, 0);
+    // the hidden states go out before the weights, as in the loop: then the loop's first
+    // wait for them leaves the weights in flight
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kLwDepth; ++i)
+#pragma unroll
+        for (int vt = 0; vt < 2; ++vt) wa[i][vt] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff[vt], i * 64, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll 1
+    for (int blk2 = 0; blk2 < nblk; blk2 += kLwBody) {
+#pragma unroll
+        for (int h = 0; h < kLwBody; ++h) {
+            const int blk = blk2 + h;
+            // stage block blk (after every wave is done with the last), then send for blk + 1
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < kLwStage; ++j) {
+                int q = threadIdx.x + j * kLwThreads;
+                q = q < kLwPiecesAll ? q : q - kLwPiecesAll;
+                const int r = q / kLwPieces, pc = q % kLwPieces;
+                h_lds[r][pc ^ (r & 15)] = hv[j];
+            }
+            __syncthreads();
+            // (the loads are unconditional -- the last block loads itself again -- so that the
+            // compiler counts every load in flight exactly and never waits for the whole ring)
+            const int nb = blk + 1 < nblk ? blk + 1 : nblk - 1;
+#pragma unroll
+            for (int j = 0; j < kLwStage; ++j)
+                hv[j] = __builtin_amdgcn_raw_buffer_load_b128(hr, soff[j], nb * kLwKB * 2, 0);
+#pragma unroll
+            for (int ks = 0; ks < kLwSteps; ++ks) {
+                const int slot = h * kLwSteps + ks;          // ring slot of step blk * 4 + ks
+                // B operands read kLwPre row tiles ahead of their MFMAs (one wave's LDS reads
+                // would otherwise wait one by one); the order is pinned below
+                auto h_frag = [&](int rt) {
+                    const int r = rt * 16 + c16;
+                    return h_lds[r][(ks * 4 + G) ^ (r & 15)];
+                };
+                lm_u32x4 hq[kLwPre];
+#pragma unroll
+                for (int p = 0; p < kLwPre; ++p) hq[p] = h_frag(p);
+#pragma unroll
+                for (int rt = 0; rt < kLwRT; ++rt) {
+                    const lm_u32x4 hb = hq[rt % kLwPre];
+                    if (rt + kLwPre < kLwRT) hq[rt % kLwPre] = h_frag(rt + kLwPre);
+#pragma unroll
+                    for (int vt = 0; vt < 2; ++vt)
+                        acc[vt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(lm_bf16x8, wa[slot][vt]), __builtin_bit_cast(lm_bf16x8, hb),
+                            acc[vt][rt], 0, 0, 0);
+                }
+#pragma unroll
+                for (int p = 0; p < kLwPre; ++p) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+#pragma unroll
+                for (int rt = 0; rt < kLwRT; ++rt) {
+                    if (rt + kLwPre < kLwRT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                          // MFMA
+                }
+                int nxt = blk * kLwSteps + ks + kLwDepth;
+                nxt = nxt < nsteps ? nxt : nsteps - 1;
+#pragma unroll
+                for (int vt = 0; vt < 2; ++vt)
+                    wa[slot][vt] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff[vt], nxt * 64, 0);
+                // keep the loads where they are (the scheduler would sink them to their use)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    // lane holds row rt*16 + c16 at entries vbase + vt*16 + G*4 + i
+#pragma unroll
+    for (int rt = 0; rt < kLwRT; ++rt) {
+        uint64_t best = 0;
+        bool nan = false;
+#pragma unroll
+        for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int v = vbase + vt * 16 + G * 4 + i;
+                if (v < V) scan_one(acc[vt][rt][i], v, best, nan);
+            }
+        uint64_t k = nan ? kNanKey : best;
+        uint64_t o = tmv::shfl_xor_u64(k, 16);
+        k = o > k ? o : k;
+        o = tmv::shfl_xor_u64(k, 32);
+        k = o > k ? o : k;
+        if (G == 0) s_key[wave][rt * 16 + c16] = k;
+    }
+    __syncthreads();
+    for (int r = threadIdx.x; r < kLwRows; r += kLwThreads) {
+        const int gr = rb0 + r;
+        uint64_t k = s_key[0][r];
+#pragma unroll
+        for (int w2 = 1; w2 < kLwWaves; ++w2) k = s_key[w2][r] > k ? s_key[w2][r] : k;
+        if (gr < nrows && lm_row_live(gr, R, M_max, n_nodes, depth, status))
+            __hip_atomic_fetch_max(reinterpret_cast<unsigned long long *>(row_keys + gr),
+                                   static_cast<unsigned long long>(k), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 // ============================================================== sampling
 // K workgroups walk each sequence together, each owning a contiguous slice of the
 // vocabulary.  At node u the teacher
@@ -1457,6 +1648,20 @@ extern "C" int tmv_tree_accept_lm_head(int B, int M_max, int D_max, int K, int V
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint64_t *keys = static_cast<uint64_t *>(workspace);
     const int nrows = B * (M_max + 1);
+    if (nrows > kLmRows) {
+        // more rows than one 64-row block: 272-row blocks against 128-entry tiles
+        const int nrb = (nrows + kLwRows - 1) / kLwRows;
+        const int ntiles = (V + kLwTile - 1) / kLwTile;
+        const int64_t groups = 8ll * nrb * ((ntiles + 7) / 8);
+        if (groups > 0x7fffffff) return TMV_ERR_ARG;
+        hipLaunchKernelGGL(lm_head_argmax_wide_kernel, dim3(static_cast<unsigned>(groups)), dim3(kLwThreads), 0, s, B,
+                           M_max, K, V, static_cast<const uint16_t *>(hidden), h_stride_b, h_stride_row,
+                           static_cast<uint32_t>(h_bytes), static_cast<const uint16_t *>(lm_head), w_stride_row,
+                           static_cast<uint32_t>(w_bytes), n_nodes, depth, status, keys, ntiles, nrb);
+        hipLaunchKernelGGL(lm_select_kernel, dim3(B), dim3(kScanThreads), 0, s, M_max, D_max, V, tokens, n_nodes, anc,
+                           depth, status, accept_len, path, next_token, keys, row_argmax);
+        return tmv_host::launch_status(hipGetLastError());
+    }
     const int nrb = (nrows + kLmRows - 1) / kLmRows;
     const int ntiles = (V + kLmTile - 1) / kLmTile;
     // every workgroup takes kLmTpw tiles of one row block: ntp tile pairs x nrb row blocks,

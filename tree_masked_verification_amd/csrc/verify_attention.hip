@@ -2003,33 +2003,47 @@ tree_attn_f32_kernel(int B, int M_max, int D_max, int Hq, int Hkv,
     const int R = M_max + 1, W = D_max + 1;
     float *o = out + b * os0 + static_cast<int64_t>(j - 1) * os1 + h * os2;
 
+    // every load that does not depend on another goes out at once: the sequence's counts,
+    // the node's depth, its ancestor row (lane k holds entries k, 64 + k, 128 + k) and its
+    // query row -- all inside their tables whatever they hold -- so the launch waits for one
+    // round trip before the K/V loads instead of one per dependent step
+    const int32_t *arow = anc + (static_cast<int64_t>(b) * R + j) * W;
     const int M = n_nodes[b], P = prefix_len[b];
     int st = status[b];
+    const int dep_in = depth[static_cast<int64_t>(b) * R + j];
+    int a3[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) a3[k] = arow[min(64 * k + lane, W - 1)];
+    const float *qp = q + b * qs0 + static_cast<int64_t>(j - 1) * qs1 + h * qs2;
+    float4 qv[D / 4];
+#pragma unroll
+    for (int e = 0; e < D / 4; ++e) qv[e] = reinterpret_cast<const float4 *>(qp)[e];
     if (st == TMV_OK && (M < 0 || M > M_max || P < 0 || static_cast<int64_t>(P) + M > L_cap)) {
         st = TMV_ERR_INPUT;
         if (threadIdx.x == 0 && j == 1 && h == 0) status[b] = TMV_ERR_INPUT;
     }
-    const int dep = (st == TMV_OK && j <= M) ? depth[static_cast<int64_t>(b) * R + j] : 0;
+    const int dep = (st == TMV_OK && j <= M) ? dep_in : 0;
     if (dep < 1) {
         if (wv == 0)
 #pragma unroll
             for (int e = 0; e < DV; ++e) o[lane + 64 * e] = 0.f;
         return;
     }
-    const float *qp = q + b * qs0 + static_cast<int64_t>(j - 1) * qs1 + h * qs2;
-    float4 qv[D / 4];
-#pragma unroll
-    for (int e = 0; e < D / 4; ++e) qv[e] = reinterpret_cast<const float4 *>(qp)[e];
 
     const float *kb = kc + b * ks0 + kvh * ks1;
     const float *vb = vc + b * ks0 + kvh * ks1;
-    const int32_t *arow = anc + (static_cast<int64_t>(b) * R + j) * W;
-    const int total = P + dep;            // visible tokens: prefix then the path
+    const int total = P + dep;            // visible tokens: prefix then the path (dep <= D_max < W)
     const int ks2_32 = static_cast<int>(ks2);
-    // slot of the lane's token in chunk t0 (-1 past the visible tokens)
+    // slot of the lane's token in chunk t0 (-1 past the visible tokens); path entry i is
+    // a3[i / 64] of lane i % 64
     auto slot_of = [&](int t0) {
         const int idx = t0 + lane;
-        return idx < P ? idx : (idx < total ? P + arow[idx - P] - 1 : -1);
+        const int i = min(max(idx - P, 0), 191), src = (i & 63) << 2;
+        const int a0 = __builtin_amdgcn_ds_bpermute(src, a3[0]);
+        const int a1 = __builtin_amdgcn_ds_bpermute(src, a3[1]);
+        const int a2 = __builtin_amdgcn_ds_bpermute(src, a3[2]);
+        const int a = i < 64 ? a0 : i < 128 ? a1 : a2;
+        return idx < P ? idx : (idx < total ? P + a - 1 : -1);
     };
     float m = -INFINITY, l = 0.f, acc[DV];
 #pragma unroll

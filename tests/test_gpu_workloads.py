@@ -36,26 +36,31 @@ def _sampled_rows(w, anc, depth, per_seq, seed):
 
 
 def _oracle_rows(ref, w, ra, rd, rs, sel, threads=8):
-    """The oracle on the selected rows, the sequences dealt to threads (the oracle's C
+    """The oracle on the selected rows, dealt round-robin to threads (the oracle's C
     routine runs without the interpreter lock)."""
-    parts = np.array_split(np.arange(w.B), min(threads, w.B))
-
-    def one(bs):
+    rows = np.argwhere(sel)
+    n = max(1, min(threads, len(rows)))
+    parts = []
+    for t in range(n):
         s = np.zeros_like(sel)
-        s[bs] = sel[bs]
-        return bs, oracle_attention(ref, w, ra, rd, rs, row_select=s)[0]
+        for b, j in rows[t::n]:
+            s[b, j] = 1
+        parts.append(s)
+
+    def one(s):
+        return s, oracle_attention(ref, w, ra, rd, rs, row_select=s)[0]
 
     out = None
     with ThreadPoolExecutor(len(parts)) as ex:
-        for bs, o in ex.map(one, parts):
+        for s, o in ex.map(one, parts):
             if out is None:
                 out = o
             else:
-                out[bs] = o[bs]
+                out[s.astype(bool)] = o[s.astype(bool)]
     return out
 
 
-def _run(ref, w, per_seq, seed, all_rows=False):
+def _run(ref, w, per_seq, seed, all_rows=False, only_seq=None, threads=8):
     dev = DeviceStep(w)
     dev.build()
     dev.attention()
@@ -70,7 +75,9 @@ def _run(ref, w, per_seq, seed, all_rows=False):
             live[b, j - 1] = j <= w.n_nodes[b] and rd[b, j] >= 1
     assert np.all(outf[~live] == 0) and np.all(np.isfinite(outf[live]))
     sel = np.ones((w.B, w.M_max), np.uint8) * live if all_rows else _sampled_rows(w, ra, rd, per_seq, seed)
-    ref_out = _oracle_rows(ref, w, ra, rd, rs, sel)
+    if only_seq is not None:
+        sel[np.arange(w.B) != only_seq] = 0
+    ref_out = _oracle_rows(ref, w, ra, rd, rs, sel, threads)
     mask = np.zeros(out.shape, bool)
     mask[sel.astype(bool)] = True
     err, rel = attention_error(out, ref_out, w.dtype, mask)
@@ -104,6 +111,14 @@ def test_long_context_70b_sampled(ref):
     _case("attention: 70B-shaped layer, prefix 32768 (config 4), sampled nodes")
     w = ti.workload(4, with_rows=False)
     _run(ref, w, per_seq=4, seed=41)
+
+
+def test_long_context_70b_one_sequence_all_rows(ref):
+    """Every row of one sequence (64 nodes x 64 query heads) with its whole 32768-token
+    prefix, the oracle's rows dealt over 16 threads."""
+    _case("attention: 70B-shaped layer, prefix 32768 (config 4), every row of sequence 1")
+    w = ti.workload(4, with_rows=False)
+    _run(ref, w, 0, 0, all_rows=True, only_seq=1, threads=16)
 
 
 def test_long_context_70b_empty_prefix_all_rows(ref):
